@@ -1,0 +1,463 @@
+"""Pins of the CPU oracle to facts fixed by the method's description and by mathematics.
+
+The method: "Level of Detail Attention" (featherless.ai blog), section "How It Works".
+Each test names the fact it checks.  None re-types the oracle's own formula: they use
+closed forms, a hand-worked example (tests/golden), an independent library (torch's
+bfloat16 cast, scikit-learn's Lloyd k-means, numpy dense softmax), invariants, or brute
+force over tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _dense_np(K, V, q, p, scale):
+    lam = scale * (K[: p + 1].astype(np.float64) @ q.astype(np.float64))
+    w = np.exp(lam - lam.max())
+    return (w[:, None] * V[: p + 1].astype(np.float64)).sum(0) / w.sum(), lam.max() + math.log(w.sum())
+
+
+def _softmax_terms(terms):
+    lam = np.array([t[0] for t in terms], np.float64)
+    val = np.array([t[1] for t in terms], np.float64)
+    w = np.exp(lam - lam.max())
+    return (w[:, None] * val).sum(0) / w.sum(), lam.max() + math.log(w.sum())
+
+
+def _mixture(T, d, seed, n_centres=8, sigma=0.3, round_bf16=False):
+    rng = np.random.default_rng(seed)
+    cen = rng.standard_normal((n_centres, d))
+    z = rng.integers(0, n_centres, T)
+    K = (cen[z] + sigma * rng.standard_normal((T, d))).astype(np.float32)
+    V = rng.standard_normal((T, d)).astype(np.float32)
+    if round_bf16:
+        K = torch.from_numpy(K).to(torch.bfloat16).float().numpy()
+        V = torch.from_numpy(V).to(torch.bfloat16).float().numpy()
+    return K, V, cen, z
+
+
+# --------------------------------------------------------------------------- rounding, dots
+
+def test_round_bf16_matches_torch_cast():
+    """Summaries are rounded to the storage type (bf16 KV): compare with torch's RNE cast."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(4096).astype(np.float32) * 10.0
+    # exact halfway cases: low 16 bits = 0x8000 with even and odd kept lsb
+    u = rng.integers(0, 2**31, 512, dtype=np.int64).astype(np.uint32)
+    halfway = ((u & 0xFFFF0000) | 0x8000).view(np.float32)
+    halfway = halfway[np.isfinite(halfway)]
+    x = np.concatenate([x, halfway, np.array([0.0, -0.0, 1.0, -1.0, 3.0e38], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    got = orc.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_canonical_dot_exact_on_integers():
+    """Closed form: small-integer dot products are exact in fp32 whatever the order."""
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        a = rng.integers(-8, 9, 128).astype(np.float32)
+        b = rng.integers(-8, 9, 128).astype(np.float32)
+        assert orc.canonical_dot(a, b) == np.float32(int(a.astype(np.int64) @ b.astype(np.int64)))
+
+
+def test_canonical_dot_is_a_fused_sequential_chain():
+    """The ranking score is an fp32 fma chain in index order (fixed rounding order).
+
+    (1) fma keeps the low bits of a product: with x = 1 + 2^-12, x*x - 1 is 2^-11 + 2^-24
+        under a fused step and 2^-11 when the product is rounded first.
+    (2) order: 2^24 + 1 - 2^24 is 0 left to right in fp32 (the +1 is lost), 1 exactly."""
+    x = np.float32(1.0 + 2.0**-12)
+    assert orc.canonical_dot(np.array([1.0, x], np.float32), np.array([-1.0, x], np.float32)) == \
+        np.float32(2.0**-11 + 2.0**-24)
+    assert orc.canonical_dot(np.array([1, 1, 1], np.float32),
+                             np.array([2.0**24, 1.0, -(2.0**24)], np.float32)) == 0.0
+    assert orc.canonical_dot(np.array([1, 1, 1], np.float32),
+                             np.array([2.0**24, -(2.0**24), 1.0], np.float32)) == 1.0
+
+
+def test_canonical_dot_error_bound():
+    """|fp32 chain - exact| <= gamma_d * sum |a_t b_t| with gamma_d = d u / (1 - d u)."""
+    rng = np.random.default_rng(2)
+    u = 2.0**-24
+    g = 128 * u / (1 - 128 * u)
+    for _ in range(200):
+        a = rng.standard_normal(128).astype(np.float32)
+        b = rng.standard_normal(128).astype(np.float32)
+        ex = float(a.astype(np.float64) @ b.astype(np.float64))
+        bound = g * float(np.abs(a.astype(np.float64) * b).sum())
+        assert abs(float(orc.canonical_dot(a, b)) - ex) <= bound
+
+
+# --------------------------------------------------------------------------- k-means
+
+def test_kmeans_objective_never_increases():
+    """Lloyd's iteration: the assignment and the mean update can only lower the objective."""
+    for seed in range(6):
+        K, _, _, _ = _mixture(256, 128, seed, n_centres=32, sigma=0.3 + 0.2 * seed)
+        _, obj = orc.kmeans(K, 8, 10)
+        assert np.all(np.diff(obj) <= 1e-9 * obj[0]), obj
+
+
+def test_kmeans_recovers_well_separated_clusters():
+    """Well separated clusters with seeds in each of them: the generating partition."""
+    rng = np.random.default_rng(3)
+    cen = rng.standard_normal((4, 128)) * 10
+    z = np.repeat(np.arange(4), 64)  # contiguous runs: strided seeds land in each cluster
+    K = (cen[z] + 0.05 * rng.standard_normal((256, 128))).astype(np.float32)
+    a, _ = orc.kmeans(K, 4, 10)
+    assert np.array_equal(a, z)
+
+
+def test_kmeans_agrees_with_scikit_learn_lloyd():
+    """Independent Lloyd implementation with the same strided seeds, one start, no tolerance."""
+    from sklearn.cluster import KMeans
+    agree = 0
+    for seed in range(8):
+        K, _, _, _ = _mixture(256, 128, 10 + seed, n_centres=32, sigma=0.3)
+        G = 8
+        a, _ = orc.kmeans(K, G, 10)
+        init = K[[(j * 256) // G for j in range(G)]].astype(np.float64)
+        km = KMeans(n_clusters=G, init=init, n_init=1, max_iter=10, tol=0.0,
+                    algorithm="lloyd").fit(K.astype(np.float64))
+        # scikit-learn relabels nothing with an explicit init: labels are comparable.
+        # It relocates empty clusters (this oracle keeps them), so compare only when none
+        # became empty on either side.
+        if len(np.unique(a)) == G and len(np.unique(km.labels_)) == G:
+            assert np.mean(a == km.labels_) >= 0.99, seed
+            agree += 1
+    assert agree >= 4
+
+
+def test_kmeans_ties_go_low_and_empty_groups_stay_empty():
+    """Two points, four groups: seeds x[0], x[0], x[1], x[1].  Equal distances go to the
+    lower group, so groups 1 and 3 stay empty and keep their (duplicate) centroids."""
+    x = np.array([[0.0, 0.0], [1.0, 1.0]], np.float32)
+    a, _ = orc.kmeans(x, 4, 10)
+    assert a.tolist() == [0, 2]
+
+
+# --------------------------------------------------------------------------- layout and summaries
+
+def test_build_layout_invariants():
+    """Groups partition the chunk's non-sink keys; pages are runs of 16 in position order."""
+    cfg = orc.Config(d=128, groups=8, n_sink=4, window=512)
+    K, V, _, _ = _mixture(4 * 256, 128, 4, n_centres=32)
+    idx = orc.build_stream(cfg, K, V, 4)
+    for c in range(4):
+        members = [p for p in range(c * 256, (c + 1) * 256) if p >= cfg.n_sink]
+        assert idx["gcount"][c].sum() == len(members)
+        for off in range(256):
+            pos = c * 256 + off
+            assert (idx["assign"][c, off] == -1) == (pos < cfg.n_sink)
+        seen = []
+        last_group = -1
+        for sl in range(cfg.page_slots):
+            j = idx["pgroup"][c, sl]
+            if j < 0:
+                assert idx["pcount"][c, sl] == 0
+                continue
+            assert j >= last_group
+            last_group = j
+            mem = idx["pmem"][c, sl, : idx["pcount"][c, sl]]
+            assert all(idx["assign"][c, m - c * 256] == j for m in mem)
+            assert list(mem) == sorted(mem)
+            seen.extend(mem.tolist())
+        # concatenated pages of a group = its members in ascending order; only last page short
+        assert sorted(seen) == members
+        for j in range(8):
+            sls = [sl for sl in range(cfg.page_slots) if idx["pgroup"][c, sl] == j]
+            cnts = [idx["pcount"][c, sl] for sl in sls]
+            assert all(n == 16 for n in cnts[:-1])
+            mem = np.concatenate([idx["pmem"][c, sl, : idx["pcount"][c, sl]] for sl in sls]) if sls else []
+            assert list(mem) == sorted(mem)
+
+
+def test_summaries_are_means_within_fp32_bounds_and_exact_for_identical_rows():
+    """Mean of a group: within the fp32 summation bound of the exact mean; identical
+    bf16-valued rows give that row exactly (their sums are exact in fp32)."""
+    cfg = orc.Config(d=128, groups=4, n_sink=1, window=256)
+    K, V, _, _ = _mixture(512, 128, 5, n_centres=16)
+    idx = orc.build_stream(cfg, K, V, 2)
+    u = 2.0**-24
+    for c in range(2):
+        for j in range(4):
+            mem = [c * 256 + o for o in range(256) if idx["assign"][c, o] == j]
+            if not mem:
+                continue
+            n = len(mem)
+            ex = K[mem].astype(np.float64).mean(0)
+            bound = (n * u / (1 - n * u)) * np.abs(K[mem]).astype(np.float64).sum(0) / n + u * np.abs(ex) * 2
+            assert np.all(np.abs(idx["gk"][c, j] - ex) <= bound + 1e-30)
+    row = torch.randn(128).to(torch.bfloat16).float().numpy()
+    Kc = np.tile(row, (256, 1)).astype(np.float32)
+    idx = orc.build_stream(orc.Config(d=128, groups=4, n_sink=0, window=256, bf16=True), Kc, Kc, 1)
+    for j in range(4):
+        if idx["gcount"][0, j]:
+            assert np.array_equal(idx["gk"][0, j], row)
+
+
+# --------------------------------------------------------------------------- the worked example
+
+def _golden_case(two_tier: bool):
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    pr = dict(g["params"])
+    if two_tier:
+        pr["top_pages"] = 0
+    cfg = orc.Config(**pr)
+    K = np.array(g["keys"], np.float32)
+    V = np.array(g["values"], np.float32)
+    q = np.array(g["query"], np.float32)
+    idx = orc.build_stream(cfg, K, V, 2, assign_in=np.array(g["assign"], np.int32))
+    r = orc.attend(cfg, idx, K, V, q, g["position"])
+    return g, r
+
+
+@pytest.mark.parametrize("two_tier", [False, True])
+def test_worked_example_by_hand(two_tier):
+    """Hand-derived case (tests/golden/worked_example.json): selection and every term."""
+    g, r = _golden_case(two_tier)
+    case = g["two_tier" if two_tier else "three_tier"]
+    assert r["sel_groups"].tolist() == case["sel_groups"]
+    if not two_tier:
+        assert r["sel_pages"].tolist() == case["sel_pages"]
+    terms = [((1.0 + math.log(2.0)) if t["logit"] == "1 + ln 2" else float(t["logit"]), t["value"])
+             for t in case["terms"]]
+    out, lm = _softmax_terms(terms)
+    assert np.allclose(r["out"], out, rtol=0, atol=1e-14)
+    assert abs(r["log_mass"] - lm) < 1e-12
+
+
+# --------------------------------------------------------------------------- identities
+
+def _expanded_dense(cfg, idx, K, V, q, p, r):
+    """Dense softmax over the exact keys plus n copies of each coarse (kbar, vbar)."""
+    C, G, PS, d = cfg.chunk, cfg.groups, cfg.page_slots, cfg.d
+    nb = cfg.built_chunks(p)
+    sel = [g for g in r["sel_groups"].tolist() if g >= 0]
+    keys, vals = [], []
+    exact = set(range(min(cfg.n_sink, p + 1))) | set(range(nb * C, p + 1))
+    opened_pages = set()
+    for i, g in enumerate(sel):
+        c, j = divmod(g, G)
+        slots = [sl for sl in range(PS) if idx["pgroup"][c, sl] == j]
+        chosen = slots if cfg.top_pages == 0 else [s for s in r["sel_pages"][i].tolist() if s >= 0]
+        for sl in chosen:
+            opened_pages.add((c, sl))
+            exact |= set(idx["pmem"][c, sl, : idx["pcount"][c, sl]].tolist())
+    for x in sorted(exact):
+        keys.append(K[x].astype(np.float64)); vals.append(V[x].astype(np.float64))
+    counted = len(exact)
+    for c in range(nb):
+        for j in range(G):
+            n = int(idx["gcount"][c, j])
+            if n == 0:
+                continue
+            if c * G + j not in sel:
+                keys += [idx["gk"][c, j].astype(np.float64)] * n
+                vals += [idx["gv"][c, j].astype(np.float64)] * n
+                counted += n
+            else:
+                for sl in range(PS):
+                    if idx["pgroup"][c, sl] == j and (c, sl) not in opened_pages:
+                        m = int(idx["pcount"][c, sl])
+                        keys += [idx["pk"][c, sl].astype(np.float64)] * m
+                        vals += [idx["pv"][c, sl].astype(np.float64)] * m
+                        counted += m
+    Kx, Vx = np.array(keys), np.array(vals)
+    lam = cfg.params().scale * (Kx @ q.astype(np.float64))
+    w = np.exp(lam - lam.max())
+    return (w[:, None] * Vx).sum(0) / w.sum(), counted
+
+
+@pytest.mark.parametrize("top_pages", [2, 0])
+def test_expanded_dense_identity_and_every_key_counted_once(top_pages):
+    """One softmax with coarse terms 'repeated by the number of keys' is dense softmax over
+    an expanded key list; and every position in [0, p] is represented exactly once."""
+    cfg = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=3, top_pages=top_pages,
+                     window=128, n_sink=2)
+    K, V, cen, _ = _mixture(1024, 16, 6, n_centres=8, sigma=0.5)
+    idx = orc.build_stream(cfg, K, V, 16)
+    rng = np.random.default_rng(7)
+    for p in [0, 5, 63, 64, 127, 128, 200, 511, 777, 1023]:
+        q = (cen[rng.integers(0, 8)] + 0.3 * rng.standard_normal(16)).astype(np.float32)
+        r = orc.attend(cfg, idx, K, V, q, p)
+        ref, counted = _expanded_dense(cfg, idx, K, V, q, p, r)
+        assert counted == p + 1
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_selection_is_brute_force_top_k():
+    """Top groups = full sort by (score desc, id asc); top pages likewise inside each group."""
+    cfg = orc.Config(d=32, chunk=64, page=4, groups=4, top_groups=5, top_pages=2, window=64,
+                     n_sink=1)
+    K, V, cen, _ = _mixture(1024, 32, 8, n_centres=6, sigma=0.4, round_bf16=True)
+    idx = orc.build_stream(cfg, K, V, 16)
+    rng = np.random.default_rng(9)
+    for p in [64, 300, 1023]:
+        for _ in range(4):
+            q = torch.from_numpy(rng.standard_normal(32).astype(np.float32)).to(torch.bfloat16).float().numpy()
+            r = orc.attend(cfg, idx, K, V, q, p)
+            nb = cfg.built_chunks(p)
+            cand = [(-float(orc.canonical_dot(q, idx["gk"][c, j])), c * 4 + j)
+                    for c in range(nb) for j in range(4) if idx["gcount"][c, j] > 0]
+            want = [g for _, g in sorted(cand)[: cfg.top_groups]]
+            assert r["sel_groups"].tolist()[: len(want)] == want
+            for i, g in enumerate(want):
+                c, j = divmod(g, 4)
+                pc = [(-float(orc.canonical_dot(q, idx["pk"][c, sl])), sl)
+                      for sl in range(cfg.page_slots) if idx["pgroup"][c, sl] == j]
+                wp = [sl for _, sl in sorted(pc)[:2]]
+                assert r["sel_pages"][i].tolist()[: len(wp)] == wp
+
+
+def test_ties_break_to_lower_id():
+    """Identical centroids tie exactly: the lower group id opens first."""
+    cfg = orc.Config(d=8, chunk=16, page=4, groups=2, top_groups=1, top_pages=1, window=16,
+                     n_sink=0)
+    K = np.zeros((48, 8), np.float32)
+    K[:, 0] = 1.0
+    V = np.arange(48 * 8, dtype=np.float32).reshape(48, 8)
+    idx = orc.build_stream(cfg, K, V, 2, assign_in=np.array([[0] * 8 + [1] * 8] * 2, np.int32))
+    r = orc.attend(cfg, idx, K, V, np.ones(8, np.float32), 47)
+    assert r["sel_groups"].tolist() == [0]
+    assert r["sel_pages"].tolist() == [[0]]
+
+
+def test_open_everything_equals_dense():
+    """Opening every group and every page leaves nothing coarse: dense causal attention."""
+    cfg = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=10**6, top_pages=0,
+                     window=64, n_sink=3)
+    K, V, cen, _ = _mixture(1000, 16, 11)
+    idx = orc.build_stream(cfg, K, V, 15)
+    rng = np.random.default_rng(12)
+    for p in [0, 2, 3, 63, 64, 500, 999]:
+        q = rng.standard_normal(16).astype(np.float32)
+        r = orc.attend(cfg, idx, K, V, q, p)
+        ref, lm = _dense_np(K, V, q, p, cfg.params().scale)
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12)
+        assert abs(r["log_mass"] - lm) < 1e-10
+
+
+def test_no_summarised_chunks_gives_dense_causal():
+    """While the query is inside the first W tokens nothing is summarised: dense causal."""
+    cfg = orc.Config(d=128, groups=8, window=512, n_sink=4)
+    K, V, cen, _ = _mixture(512, 128, 13)
+    idx = orc.build_stream(cfg, K, V, 0)
+    q = cen[0].astype(np.float32)
+    for p in [0, 3, 4, 255, 256, 511]:
+        r = orc.attend(cfg, idx, K, V, q, p)
+        assert r["sel_groups"].tolist() == [-1] * 8
+        assert np.allclose(r["out"], _dense_np(K, V, q, p, cfg.params().scale)[0], atol=1e-12)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_zero_variance_groups_give_full_attention(bf16):
+    """'When the groups have zero variance, this ends up being equivalent to full
+    attention': chunks of four identical-key runs, strided seeds land on each run."""
+    from hierarchical_kv_approximation_amd import synth
+    K, V, cen, _ = synth.clustered_kv(1, 4096, 1, 128, seed=14, zero_variance=True,
+                                      dtype=torch.bfloat16 if bf16 else torch.float32)
+    K, V = K[0, :, 0].float().numpy(), V[0, :, 0].float().numpy()
+    cfg = orc.Config(d=128, groups=4, top_groups=8, top_pages=2, window=256, n_sink=1, bf16=bf16)
+    idx = orc.build_stream(cfg, K, V, 15)
+    for c in range(15):  # k-means reached zero variance: every group holds one key value
+        for j in range(4):
+            mem = [o for o in range(256) if idx["assign"][c, o] == j]
+            assert len(mem) > 0 and np.all(K[c * 256 + np.array(mem)] == K[c * 256 + mem[0]])
+    rng = np.random.default_rng(15)
+    for p in [4095, 3000, 700]:
+        q = (cen[0, 0, rng.integers(0, 32)] + 0.3 * rng.standard_normal(128)).numpy().astype(np.float32)
+        if bf16:
+            q = torch.from_numpy(q).to(torch.bfloat16).float().numpy()
+        r = orc.attend(cfg, idx, K, V, q, p)
+        ref, lm = _dense_np(K, V, q, p, cfg.params().scale)
+        # keys are exact; only the rounding of the value means remains
+        tol = 1e-6 if not bf16 else 2.0**-8 * float(np.abs(V[: p + 1]).max())
+        assert np.max(np.abs(r["out"] - ref)) <= tol
+        assert abs(r["log_mass"] - lm) < 1e-9
+
+
+def test_coarse_mass_is_conservative_jensen():
+    """'As variance increases, it becomes a conservative estimate of attention mass':
+    n exp(q.kbar) <= sum exp(q.k_i) for every group and page, and the total mass of the
+    LoD softmax never exceeds the dense one (fp32 summaries; a small rounding slack)."""
+    cfg = orc.Config(d=128, groups=8, window=512, n_sink=4)
+    K, V, cen, _ = _mixture(8192, 128, 16, n_centres=32, sigma=0.6)
+    idx = orc.build_stream(cfg, K, V, 31)
+    sc = cfg.params().scale
+    rng = np.random.default_rng(17)
+    for _ in range(4):
+        q = (cen[rng.integers(0, 32)] + 0.3 * rng.standard_normal(128)).astype(np.float32)
+        for c in range(31):
+            for j in range(8):
+                mem = [c * 256 + o for o in range(256) if idx["assign"][c, o] == j]
+                if not mem:
+                    continue
+                lhs = math.log(len(mem)) + sc * float(idx["gk"][c, j].astype(np.float64) @ q)
+                lam = sc * (K[mem].astype(np.float64) @ q)
+                rhs = lam.max() + math.log(np.exp(lam - lam.max()).sum())
+                assert lhs <= rhs + 1e-5
+        r = orc.attend(cfg, idx, K, V, q, 8191)
+        _, lm = _dense_np(K, V, q, 8191, sc)
+        assert r["log_mass"] <= lm + 1e-5
+
+
+def test_singleton_groups_make_coarse_terms_exact():
+    """A group (and page) of one key: its mean is the key, so LoD equals dense attention."""
+    cfg = orc.Config(d=8, chunk=8, page=2, groups=8, top_groups=2, top_pages=1, window=8,
+                     n_sink=0)
+    rng = np.random.default_rng(18)
+    K = rng.standard_normal((64, 8)).astype(np.float32)
+    V = rng.standard_normal((64, 8)).astype(np.float32)
+    idx = orc.build_stream(cfg, K, V, 7)
+    assert np.all(idx["gcount"] == 1)
+    q = rng.standard_normal(8).astype(np.float32)
+    r = orc.attend(cfg, idx, K, V, q, 63)
+    assert np.allclose(r["out"], _dense_np(K, V, q, 63, cfg.params().scale)[0], atol=1e-12)
+
+
+def test_batched_helpers_match_single_calls():
+    """The threaded helpers only fan out single-stream calls (same results)."""
+    cfg = orc.Config(d=128, groups=8, window=512, n_sink=4, bf16=True)
+    from hierarchical_kv_approximation_amd import synth
+    K, V, cen, _ = synth.clustered_kv(2, 1024, 2, 128, seed=19)
+    Q = synth.queries(2, 4, cen, seed=20)
+    st = orc.streams(K.float().numpy(), V.float().numpy())
+    idx = orc.build_all(cfg, st, 2)
+    seq = [1024, 900]
+    out, out64, sg, sp = orc.decode(cfg, st, idx, Q.float().numpy(), seq)
+    for b in range(2):
+        for h in range(4):
+            r = orc.attend(cfg, idx[(b, h // 2)], *st[(b, h // 2)], Q[b, h].float().numpy(), seq[b] - 1)
+            assert np.array_equal(r["out"], out64[b, h])
+            assert np.array_equal(r["sel_groups"], sg[b, h])
+
+
+def test_bf16_summaries_are_rounded_means():
+    """bf16 KV: every stored mean is a bfloat16 value, within half a bf16 ulp (2^-8 relative, plus the
+    fp32 summation bound) of the exact mean."""
+    cfg = orc.Config(d=128, groups=8, window=512, n_sink=4, bf16=True)
+    K, V, _, _ = _mixture(1024, 128, 21, n_centres=32, round_bf16=True)
+    idx = orc.build_stream(cfg, K, V, 4)
+    for name in ("gk", "gv", "pk", "pv"):
+        assert np.all((idx[name].view(np.uint32) & 0xFFFF) == 0), name
+    for c in range(4):
+        for j in range(8):
+            mem = [c * 256 + o for o in range(256) if idx["assign"][c, o] == j]
+            if not mem:
+                continue
+            ex = V[mem].astype(np.float64).mean(0)
+            n = len(mem)
+            tol = 2.0**-8 * np.abs(ex) * 1.01 + (n * 2.0**-24 / (1 - n * 2.0**-24)) * \
+                np.abs(V[mem]).astype(np.float64).sum(0) / n + 1e-30
+            assert np.all(np.abs(idx["gv"][c, j] - ex) <= tol)
