@@ -1,0 +1,91 @@
+// lod_device.h -- device helpers shared by the LoD kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lod_internal.h"
+
+namespace lodi {
+
+typedef uint16_t bf16_t;  // bfloat16 bits
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even fp32 -> bfloat16 bits (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) {
+        if (u & 0x007fffffu) u |= 0x00400000u;
+        return (bf16_t)(u >> 16);
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+    static constexpr int kPer16 = 4;  // elements per 16-byte load
+    __device__ static __forceinline__ float to_f32(float x) { return x; }
+    __device__ static __forceinline__ float store_round(float x) { return x; }
+    // Unpack one 16-byte chunk into kPer16 floats.
+    __device__ static __forceinline__ void unpack(const uint4& u, float* o) {
+        o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+        o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+    }
+};
+template <> struct Elt<bf16_t> {
+    static constexpr int kPer16 = 8;
+    __device__ static __forceinline__ float to_f32(bf16_t x) { return bf16_bits_to_f32(x); }
+    __device__ static __forceinline__ bf16_t store_round(float x) { return f32_to_bf16_rne(x); }
+    __device__ static __forceinline__ void unpack(const uint4& u, float* o) {
+        o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+        o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+        o[4] = __uint_as_float(u.z << 16); o[5] = __uint_as_float(u.z & 0xffff0000u);
+        o[6] = __uint_as_float(u.w << 16); o[7] = __uint_as_float(u.w & 0xffff0000u);
+    }
+};
+
+// Storage conversion of an fp32 mean to the element type.
+__device__ __forceinline__ void store_elt(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store_elt(bf16_t* p, float x) { *p = f32_to_bf16_rne(x); }
+
+// Ranking key: larger key = higher score, then lower id.  -0 and +0 rank equal.
+__device__ __forceinline__ uint64_t rank_key(float r, uint32_t id) {
+    uint32_t u = __float_as_uint(r == 0.0f ? 0.0f : r);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - id);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
+__device__ __forceinline__ float key_score(uint64_t k) {
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v, int width) {
+    for (int m = width >> 1; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v, int width) {
+    for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// exp(x) for x <= 0 (softmax weights); exp(-inf) = 0.
+__device__ __forceinline__ float softmax_exp(float x) { return __expf(x); }
+
+}  // namespace lodi

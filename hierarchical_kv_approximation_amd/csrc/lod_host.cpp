@@ -1,0 +1,139 @@
+// lod_host.cpp -- host-only parts of the LoD C ABI: status strings, argument checks,
+// index layout and workspace sizing.  Nothing here touches the GPU.
+#include <math.h>
+
+#include "lod_internal.h"
+
+namespace lodi {
+
+int check_params(const lod_params* p) {
+    if (!p) return LOD_ERR_ARG;
+    if (p->head_dim <= 0 || p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->chunk_size <= 0 ||
+        p->page_size <= 0 || p->groups_per_chunk <= 0 || p->top_groups <= 0 ||
+        p->top_pages < 0 || p->window <= 0 || p->n_sink < 0 || p->kmeans_iters <= 0)
+        return LOD_ERR_ARG;
+    if (p->n_q_heads % p->n_kv_heads != 0) return LOD_ERR_ARG;
+    if (p->window % p->chunk_size != 0) return LOD_ERR_ARG;
+    if (p->n_sink >= p->chunk_size) return LOD_ERR_ARG;
+    if (!(p->scale > 0.0f) || !isfinite(p->scale)) return LOD_ERR_ARG;
+    if (p->kv_dtype != LOD_F32 && p->kv_dtype != LOD_BF16) return LOD_ERR_UNSUPPORTED;
+    if (p->head_dim != kD || p->chunk_size != kChunk || p->page_size != kPage)
+        return LOD_ERR_UNSUPPORTED;
+    if (p->groups_per_chunk > kMaxG || p->top_groups > kMaxTG || p->top_pages > kPage)
+        return LOD_ERR_UNSUPPORTED;
+    const int g = p->n_q_heads / p->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return LOD_ERR_UNSUPPORTED;
+    return LOD_OK;
+}
+
+lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_chunks) {
+    lod_index_layout_t L{};
+    const size_t U = (size_t)batch * p->n_kv_heads;
+    const size_t NC = (size_t)max_chunks;
+    const size_t G = p->groups_per_chunk, PS = page_slots(p), d = p->head_dim;
+    const size_t E = elt_bytes(p);
+    size_t o = 0;
+    L.gk = o;     o = align256(o + U * NC * G * d * E);
+    L.gv = o;     o = align256(o + U * NC * G * d * E);
+    L.gln = o;    o = align256(o + U * NC * G * 4);
+    L.pk = o;     o = align256(o + U * NC * PS * d * E);
+    L.pv = o;     o = align256(o + U * NC * PS * d * E);
+    L.pln = o;    o = align256(o + U * NC * PS * 4);
+    L.meta = o;   o = align256(o + U * NC * meta_stride(p) * 2);
+    L.assign = o; o = align256(o + U * NC * p->chunk_size);
+    L.total = o;
+    L.page_slots = (int32_t)PS;
+    L.meta_stride = meta_stride(p);
+    return L;
+}
+
+DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len) {
+    DecodePlan P{};
+    const int nb = built_chunks(p, (int64_t)max_seq_len - 1);
+    const int64_t ng = (int64_t)nb * p->groups_per_chunk;
+    const int64_t units = (int64_t)batch * p->n_kv_heads;
+    // Aim for about 512 slice workgroups (two per CU) over the whole batch.
+    int64_t want = ceil_div(512, units);
+    int64_t slice = ceil_div(ng > 0 ? ng : 1, want);
+    slice = ceil_div(slice, kTile) * kTile;
+    if (slice < kTile) slice = kTile;
+    if (slice > 4 * kTile) slice = 4 * kTile;
+    P.slice = (int)slice;
+    P.nslice = ng > 0 ? (int)ceil_div(ng, slice) : 0;
+    P.nwin = 1 + (int)ceil_div(p->window, kTile);  // sinks, then window tiles
+    P.nslot = P.nslice + P.nwin + p->top_groups;
+    const size_t heads = (size_t)batch * p->n_q_heads;
+    P.off_part = 0;
+    P.off_cand = align256(heads * P.nslot * kPartStride * sizeof(float));
+    P.bytes = align256(P.off_cand + heads * (size_t)(P.nslice > 0 ? P.nslice : 1) *
+                                        p->top_groups * sizeof(uint64_t));
+    return P;
+}
+
+DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len) {
+    DensePlan P{};
+    const int64_t units = (int64_t)batch * p->n_kv_heads;
+    // About 1024 workgroups, at least 4 tiles each so partials stay a small fraction.
+    int64_t want = ceil_div(1024, units);
+    int64_t rows = ceil_div(max_seq_len, want);
+    rows = ceil_div(rows, kTile) * kTile;
+    if (rows < 4 * kTile) rows = 4 * kTile;
+    P.rows_per_wg = (int)rows;
+    P.nsplit = (int)ceil_div(max_seq_len, rows);
+    P.bytes = align256((size_t)batch * p->n_q_heads * P.nsplit * kPartStride * sizeof(float));
+    return P;
+}
+
+}  // namespace lodi
+
+using namespace lodi;
+
+extern "C" {
+
+const char* lod_status_string(int status) {
+    switch (status) {
+        case LOD_OK: return "LOD_OK";
+        case LOD_ERR_ARG: return "LOD_ERR_ARG: invalid argument";
+        case LOD_ERR_UNSUPPORTED: return "LOD_ERR_UNSUPPORTED: parameters not supported";
+        case LOD_ERR_WORKSPACE: return "LOD_ERR_WORKSPACE: buffer too small";
+        case LOD_ERR_HIP: return "LOD_ERR_HIP: HIP runtime or launch failure";
+        default: return "unknown status";
+    }
+}
+
+int lod_index_layout(const lod_params* params, int32_t batch, int32_t max_chunks,
+                     lod_index_layout_t* layout) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!layout || batch <= 0 || max_chunks < 0) return LOD_ERR_ARG;
+    *layout = make_layout(params, batch, max_chunks);
+    return LOD_OK;
+}
+
+int lod_index_bytes(const lod_params* params, int32_t batch, int32_t max_tokens, size_t* bytes) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!bytes || batch <= 0 || max_tokens < 0) return LOD_ERR_ARG;
+    *bytes = make_layout(params, batch, max_tokens / params->chunk_size).total;
+    return LOD_OK;
+}
+
+int lod_decode_ws_bytes(const lod_params* params, int32_t batch, int32_t max_seq_len,
+                        size_t* bytes) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!bytes || batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
+    *bytes = plan_decode(params, batch, max_seq_len).bytes;
+    return LOD_OK;
+}
+
+int lod_dense_decode_ws_bytes(const lod_params* params, int32_t batch, int32_t max_seq_len,
+                              size_t* bytes) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!bytes || batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
+    *bytes = plan_dense(params, batch, max_seq_len).bytes;
+    return LOD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// lod_internal.h -- layout, launch planning and argument checks shared by the host
+// entry points of the LoD library.  Pure host C++ (no HIP types), so it also builds
+// for CPU-only checks.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lod.h"
+
+namespace lodi {
+
+constexpr int kD = 128;        // supported head dimension
+constexpr int kChunk = 256;    // supported chunk size
+constexpr int kPage = 16;      // supported page size
+constexpr int kMaxG = 16;      // groups per chunk
+constexpr int kMaxTG = 16;     // opened groups per query
+constexpr int kThreads = 256;  // threads per workgroup of every kernel
+constexpr int kTile = 64;      // rows per LDS tile in the decode kernels
+constexpr int kPartStride = kD + 4;  // floats per partial softmax state: o[d], m, l, pad
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validate the parameter block (host).  Returns LOD_OK or an error status.
+int check_params(const lod_params* p);
+
+inline int elt_bytes(const lod_params* p) { return p->kv_dtype == LOD_BF16 ? 2 : 4; }
+inline int page_slots(const lod_params* p) { return p->chunk_size / p->page_size + p->groups_per_chunk; }
+inline int meta_stride(const lod_params* p) {
+    int n = (p->groups_per_chunk + 1) + (page_slots(p) + 1) + p->chunk_size;
+    return (n + 31) & ~31;  // 64-byte multiple of int16 entries
+}
+// Chunks summarised for a query at position pos (block-granular window).
+inline int built_chunks(const lod_params* p, int64_t pos) {
+    int64_t nb = pos / p->chunk_size - p->window / p->chunk_size + 1;
+    return nb < 0 ? 0 : (int)nb;
+}
+
+lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_chunks);
+
+// Decode launch plan, a pure function of (params, batch, max_seq_len).
+struct DecodePlan {
+    int slice;      // groups per slice workgroup (multiple of kTile)
+    int nslice;     // slice workgroups per (sequence, KV head)
+    int nwin;       // window workgroups per (sequence, KV head): sinks + window tiles
+    int nslot;      // partial softmax states per (sequence, query head)
+    size_t off_part, off_cand, bytes;
+};
+DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len);
+
+struct DensePlan {
+    int rows_per_wg;  // rows of one split workgroup (multiple of kTile)
+    int nsplit;
+    size_t bytes;
+};
+DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len);
+
+}  // namespace lodi

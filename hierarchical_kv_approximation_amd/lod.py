@@ -1,0 +1,294 @@
+"""ctypes binding of the LoD HIP library (liblod.so).
+
+Argument marshalling only: every step of the method runs in the library's kernels.
+torch provides device memory and the current HIP stream, nothing else.  The library
+must be built (``__graft_entry__.build()`` or ``python -m
+hierarchical_kv_approximation_amd._build``); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from dataclasses import dataclass, field
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblod.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "lod.h")
+
+LOD_OK, LOD_ERR_ARG, LOD_ERR_UNSUPPORTED, LOD_ERR_WORKSPACE, LOD_ERR_HIP = 0, -1, -2, -3, -4
+LOD_F32, LOD_BF16 = 0, 1
+
+
+class Params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "head_dim", "n_q_heads", "n_kv_heads", "chunk_size", "page_size", "groups_per_chunk",
+        "top_groups", "top_pages", "window", "n_sink", "kmeans_iters", "kv_dtype")] + \
+        [("scale", ctypes.c_float)]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class Index(ctypes.Structure):
+    _fields_ = [("mem", ctypes.c_void_p), ("bytes", ctypes.c_size_t), ("batch", ctypes.c_int32),
+                ("max_chunks", ctypes.c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("gk", "gv", "gln", "pk", "pv", "pln", "meta", "assign", "total")] + \
+        [("page_slots", ctypes.c_int32), ("meta_stride", ctypes.c_int32)]
+
+
+class LodError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {lib().lod_status_string(status).decode()}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load liblod.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -m hierarchical_kv_approximation_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, vp, i32, i64, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        pp = P(Params)
+        L.lod_status_string.restype = ctypes.c_char_p
+        L.lod_status_string.argtypes = [ctypes.c_int]
+        L.lod_index_bytes.argtypes = [pp, i32, i32, P(sz)]
+        L.lod_index_layout.argtypes = [pp, i32, i32, P(Layout)]
+        L.lod_build_chunk.argtypes = [pp, P(Index), KV, i32, i32, i32, vp, vp, vp]
+        L.lod_decode_ws_bytes.argtypes = [pp, i32, i32, P(sz)]
+        L.lod_attend_decode.argtypes = [pp, P(Index), KV, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.lod_prefill_ws_bytes.argtypes = [pp, i32, i32, i32, P(sz)]
+        L.lod_attend_prefill.argtypes = [pp, P(Index), KV, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.lod_dense_decode_ws_bytes.argtypes = [pp, i32, i32, P(sz)]
+        L.lod_dense_decode.argtypes = [pp, KV, vp, vp, i32, i32, vp, vp, sz, vp]
+        L.lod_dense_prefill.argtypes = [pp, KV, vp, i32, i32, i32, vp, vp]
+        for fn in ("lod_index_bytes", "lod_index_layout", "lod_build_chunk", "lod_decode_ws_bytes",
+                   "lod_attend_decode", "lod_prefill_ws_bytes", "lod_attend_prefill",
+                   "lod_dense_decode_ws_bytes", "lod_dense_decode", "lod_dense_prefill"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/lod.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(lod_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn, status):
+    if status != LOD_OK:
+        raise LodError(fn, status)
+
+
+@dataclass
+class Config:
+    """LoD parameters (chunk 256, pages of 16, top 8 groups / top 2 pages by default)."""
+    n_q_heads: int = 64
+    n_kv_heads: int = 8
+    groups: int = 8
+    top_groups: int = 8
+    top_pages: int = 2
+    window: int = 512
+    n_sink: int = 4
+    kmeans_iters: int = 10
+    dtype: torch.dtype = torch.bfloat16
+    head_dim: int = 128
+    chunk_size: int = 256
+    page_size: int = 16
+    scale: float | None = None
+
+    def params(self) -> Params:
+        sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+        dt = {torch.float32: LOD_F32, torch.bfloat16: LOD_BF16}.get(self.dtype, 99)
+        return Params(self.head_dim, self.n_q_heads, self.n_kv_heads, self.chunk_size,
+                      self.page_size, self.groups, self.top_groups, self.top_pages, self.window,
+                      self.n_sink, self.kmeans_iters, dt, sc)
+
+    @property
+    def page_slots(self) -> int:
+        return self.chunk_size // self.page_size + self.groups
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def kv_view(K: torch.Tensor, V: torch.Tensor) -> KV:
+    """[B][T][Hkv][d] (any strides, last dim contiguous) -> the library's KV view."""
+    assert K.shape == V.shape and K.stride() == V.stride() and K.dtype == V.dtype
+    assert K.stride(3) == 1
+    return KV(K.data_ptr(), V.data_ptr(), K.stride(0), K.stride(1), K.stride(2))
+
+
+@dataclass
+class LodIndex:
+    """Caller-owned multi-resolution view (a device byte tensor)."""
+    cfg: Config
+    batch: int
+    max_chunks: int
+    mem: torch.Tensor = field(repr=False)
+
+    @classmethod
+    def allocate(cls, cfg: Config, batch: int, max_tokens: int, device="cuda"):
+        n = ctypes.c_size_t()
+        _check("lod_index_bytes", lib().lod_index_bytes(ctypes.byref(cfg.params()), batch, max_tokens,
+                                                        ctypes.byref(n)))
+        mem = torch.zeros(n.value, dtype=torch.uint8, device=device)
+        return cls(cfg, batch, max_tokens // cfg.chunk_size, mem)
+
+    def c(self) -> Index:
+        return Index(self.mem.data_ptr(), self.mem.numel(), self.batch, self.max_chunks)
+
+    def layout(self) -> Layout:
+        L = Layout()
+        _check("lod_index_layout", lib().lod_index_layout(ctypes.byref(self.cfg.params()), self.batch,
+                                                          self.max_chunks, ctypes.byref(L)))
+        return L
+
+    def arrays(self) -> dict:
+        """Typed views of the index arrays (for inspection and tests)."""
+        L, cfg = self.layout(), self.cfg
+        U = self.batch * cfg.n_kv_heads
+        NC, G, PS, d = self.max_chunks, cfg.groups, L.page_slots, cfg.head_dim
+        es = 2 if cfg.dtype == torch.bfloat16 else 4
+
+        def view(off, count, dt, shape):
+            nbytes = count * torch.tensor([], dtype=dt).element_size()
+            return self.mem[off:off + nbytes].view(dt).view(*shape)
+
+        return {
+            "gk": view(L.gk, U * NC * G * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, G, d)),
+            "gv": view(L.gv, U * NC * G * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, G, d)),
+            "gln": view(L.gln, U * NC * G, torch.float32, (self.batch, cfg.n_kv_heads, NC, G)),
+            "pk": view(L.pk, U * NC * PS * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, PS, d)),
+            "pv": view(L.pv, U * NC * PS * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, PS, d)),
+            "pln": view(L.pln, U * NC * PS, torch.float32, (self.batch, cfg.n_kv_heads, NC, PS)),
+            "meta": view(L.meta, U * NC * L.meta_stride, torch.int16,
+                         (self.batch, cfg.n_kv_heads, NC, L.meta_stride)),
+            "assign": view(L.assign, U * NC * cfg.chunk_size, torch.int8,
+                           (self.batch, cfg.n_kv_heads, NC, cfg.chunk_size)),
+        } if es else None
+
+
+def build_chunk(cfg: Config, index: LodIndex, K, V, chunk_begin: int, n_chunks: int,
+                assign_in: torch.Tensor | None = None, want_assign: bool = False):
+    """lod_build_chunk over chunks [chunk_begin, chunk_begin + n_chunks) of every sequence."""
+    B = K.shape[0]
+    aout = None
+    if want_assign:
+        aout = torch.empty(B, cfg.n_kv_heads, n_chunks, cfg.chunk_size, dtype=torch.int32, device=K.device)
+    if assign_in is not None:
+        assign_in = assign_in.to(device=K.device, dtype=torch.int32).contiguous()
+    idx = index.c()
+    _check("lod_build_chunk", lib().lod_build_chunk(ctypes.byref(cfg.params()), ctypes.byref(idx),
+                                                    kv_view(K, V), B, chunk_begin, n_chunks,
+                                                    _ptr(assign_in), _ptr(aout), _stream()))
+    return aout
+
+
+def decode_ws_bytes(cfg: Config, batch: int, max_seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check("lod_decode_ws_bytes", lib().lod_decode_ws_bytes(ctypes.byref(cfg.params()), batch,
+                                                            max_seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def attend_decode(cfg: Config, index: LodIndex, K, V, q, seq_lens: torch.Tensor, max_seq_len: int,
+                  want_selection: bool = False, ws: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None):
+    """lod_attend_decode; q [B][Hq][d]; seq_lens device int32 [B].  Returns out (fp32) or
+    (out, sel_groups, sel_pages)."""
+    B = q.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+    sg = sp = None
+    if want_selection:
+        sg = torch.empty(B, cfg.n_q_heads, cfg.top_groups, dtype=torch.int32, device=dev)
+        sp = torch.empty(B, cfg.n_q_heads, cfg.top_groups, max(cfg.top_pages, 1), dtype=torch.int32,
+                         device=dev)
+    if ws is None:
+        ws = torch.empty(decode_ws_bytes(cfg, B, max_seq_len), dtype=torch.uint8, device=dev)
+    idx = index.c()
+    _check("lod_attend_decode", lib().lod_attend_decode(
+        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V), _ptr(q), _ptr(seq_lens), B,
+        max_seq_len, _ptr(out), _ptr(sg), _ptr(sp), _ptr(ws), ws.numel(), _stream()))
+    return (out, sg, sp) if want_selection else out
+
+
+def prefill_ws_bytes(cfg: Config, batch: int, n_q: int, max_tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check("lod_prefill_ws_bytes", lib().lod_prefill_ws_bytes(ctypes.byref(cfg.params()), batch, n_q,
+                                                              max_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def attend_prefill(cfg: Config, index: LodIndex, K, V, q, q_start: int, want_selection: bool = False,
+                   ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """lod_attend_prefill; q [B][n_q][Hq][d] holds rows q_start .. q_start+n_q-1."""
+    B, nq = q.shape[0], q.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, nq, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+    sg = sp = None
+    if want_selection:
+        sg = torch.empty(B, nq, cfg.n_q_heads, cfg.top_groups, dtype=torch.int32, device=dev)
+        sp = torch.empty(B, nq, cfg.n_q_heads, cfg.top_groups, max(cfg.top_pages, 1),
+                         dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, prefill_ws_bytes(cfg, B, nq, q_start + nq)), dtype=torch.uint8, device=dev)
+    idx = index.c()
+    _check("lod_attend_prefill", lib().lod_attend_prefill(
+        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V), _ptr(q), q_start, nq, B,
+        _ptr(out), _ptr(sg), _ptr(sp), _ptr(ws), ws.numel(), _stream()))
+    return (out, sg, sp) if want_selection else out
+
+
+def dense_decode_ws_bytes(cfg: Config, batch: int, max_seq_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check("lod_dense_decode_ws_bytes", lib().lod_dense_decode_ws_bytes(
+        ctypes.byref(cfg.params()), batch, max_seq_len, ctypes.byref(n)))
+    return n.value
+
+
+def dense_decode(cfg: Config, K, V, q, seq_lens: torch.Tensor, max_seq_len: int,
+                 ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty(B, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(dense_decode_ws_bytes(cfg, B, max_seq_len), dtype=torch.uint8, device=q.device)
+    _check("lod_dense_decode", lib().lod_dense_decode(
+        ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), _ptr(seq_lens), B, max_seq_len,
+        _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def dense_prefill(cfg: Config, K, V, q, q_start: int, out: torch.Tensor | None = None):
+    B, nq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty(B, nq, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+    _check("lod_dense_prefill", lib().lod_dense_prefill(
+        ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), q_start, nq, B, _ptr(out), _stream()))
+    return out

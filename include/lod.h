@@ -1,0 +1,219 @@
+/*
+ * lod.h -- C ABI of the Level-of-Detail (LoD) attention library for AMD MI355X (gfx950).
+ *
+ * The method is the one described in "Level of Detail Attention: allocating
+ * resolution instead of sparsity" (featherless.ai blog), section "How It Works":
+ *   - after every chunk of 256 tokens the chunk's keys are clustered into centroid
+ *     groups; each group is cut into pages of 16 keys; every group and page keeps a
+ *     mean key, a mean value and its key count;
+ *   - a query scores the group centroids and opens the top groups (8), scores the page
+ *     summaries inside them and opens the top pages (2) of each opened group;
+ *   - one softmax covers the exact keys (opened pages, the recent block window, the
+ *     sink tokens) and a coarse remainder in which every unopened group and every
+ *     unopened page of an opened group enters as its mean key/value repeated by its
+ *     key count, i.e. with logit scale*q.kbar + ln(n) and value vbar.
+ * Readings for what the post leaves open (k-means details, rounding, tie-breaks,
+ * window granularity) are stated at each call below.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *     buffer; the library never allocates device memory and keeps no state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work;
+ *     they return before the GPU finishes.  Device faults surface at the caller's next
+ *     synchronisation of that stream.
+ *   - Arguments are validated on the host before anything is enqueued: a bad argument
+ *     returns LOD_ERR_ARG (or LOD_ERR_UNSUPPORTED / LOD_ERR_WORKSPACE) and enqueues
+ *     nothing.  A failed launch returns LOD_ERR_HIP.  No exception crosses the ABI.
+ *   - Calls are reentrant.  Calls that share output, index or workspace buffers must
+ *     be ordered by the caller (same stream or events).
+ *   - KV cache: element (b, t, h, i) of K is at k[b*stride_b + t*stride_t + h*stride_h + i]
+ *     (strides in elements, last dimension contiguous, 16-byte aligned rows).
+ *     Queries have the cache's element type; outputs are fp32.
+ */
+#ifndef LOD_H
+#define LOD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    LOD_OK = 0,
+    LOD_ERR_ARG = -1,         /* null pointer, inconsistent sizes, out-of-range value */
+    LOD_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim != 128) */
+    LOD_ERR_WORKSPACE = -3,   /* workspace or index buffer smaller than required */
+    LOD_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Element types of K, V and q. */
+enum { LOD_F32 = 0, LOD_BF16 = 1 };
+
+/*
+ * LoD parameters.  Supported: head_dim 128; chunk_size 256; page_size 16;
+ * 1 <= groups_per_chunk <= 16; 1 <= top_groups <= 16; 0 <= top_pages <= 16
+ * (0 = two-tier: every page of an opened group is exact); window a positive multiple
+ * of chunk_size; 0 <= n_sink < chunk_size; kmeans_iters >= 1;
+ * n_q_heads = g * n_kv_heads with g in {1, 2, 4, 8}.
+ */
+typedef struct {
+    int32_t head_dim;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t chunk_size;       /* C: tokens per clustered chunk (256) */
+    int32_t page_size;        /* P: keys per page (16) */
+    int32_t groups_per_chunk; /* G: k-means groups per chunk */
+    int32_t top_groups;       /* groups a query opens (8) */
+    int32_t top_pages;        /* pages opened per opened group (2); 0 = two-tier */
+    int32_t window;           /* W: exact block window in tokens */
+    int32_t n_sink;           /* s: leading positions that are always exact */
+    int32_t kmeans_iters;     /* Lloyd rounds per chunk (10) */
+    int32_t kv_dtype;         /* LOD_F32 or LOD_BF16 */
+    float scale;              /* softmax scale, normally 1/sqrt(head_dim) */
+} lod_params;
+
+/* Strided view of the caller's KV cache (see the conventions above). */
+typedef struct {
+    const void* k;
+    const void* v;
+    int64_t stride_b, stride_t, stride_h;
+} lod_kv;
+
+/* The multi-resolution view: one caller-allocated device buffer of `bytes` bytes,
+ * sized by lod_index_bytes for (batch, max_chunks).  Its layout is given by
+ * lod_index_layout; it holds absolute positions and summaries only, so it can be
+ * copied as plain memory. */
+typedef struct {
+    void* mem;
+    size_t bytes;
+    int32_t batch;
+    int32_t max_chunks;
+} lod_index;
+
+/*
+ * Byte offsets of the arrays inside lod_index.mem (U = batch * n_kv_heads units,
+ * NC = max_chunks, G = groups_per_chunk, PS = page_slots = C/P + G, d = head_dim,
+ * E = element size of kv_dtype).  Every array is 256-byte aligned.
+ *   gk, gv   [U][NC*G][d]  E     group mean key / value (storage-rounded)
+ *   gln      [U][NC*G]     f32   ln(key count), -inf for an empty group
+ *   pk, pv   [U][NC*PS][d] E     page mean key / value
+ *   pln      [U][NC*PS]    f32   ln(key count), -inf for an unused page slot
+ *   meta     [U][NC][meta_stride] int16: gpg[G+1] first page slot of each group,
+ *            pst[PS+1] first perm entry of each page slot, perm[C] chunk-local offsets
+ *            of the clustered keys ordered by (group, position)
+ *   assign   [U][NC][C]    int8  group of every chunk-local position, -1 for sinks
+ */
+typedef struct {
+    size_t gk, gv, gln, pk, pv, pln, meta, assign, total;
+    int32_t page_slots;
+    int32_t meta_stride; /* int16 entries per chunk in `meta` */
+} lod_index_layout_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* lod_status_string(int status);
+
+/* Host-only: bytes of an index that holds max_tokens/chunk_size chunks per sequence. */
+int lod_index_bytes(const lod_params* params, int32_t batch, int32_t max_tokens, size_t* bytes);
+
+/* Host-only: array offsets for (batch, max_chunks); see lod_index_layout_t. */
+int lod_index_layout(const lod_params* params, int32_t batch, int32_t max_chunks,
+                     lod_index_layout_t* layout);
+
+/*
+ * Build chunks [chunk_begin, chunk_begin + n_chunks) of every sequence and KV head
+ * ("after every chunk of 256 tokens, similar keys are grouped into centroid clusters.
+ * Within each cluster, keys are divided into pages of 16 keys" -- How It Works).
+ * Clustering: Lloyd's k-means on the chunk's non-sink keys (positions >= n_sink) in
+ * fp32, seeds mu_j = x[floor(j*m/G)] for m members, kmeans_iters rounds of (assign to
+ * the nearest centroid by the fp32 fma chain of squared differences in index order,
+ * ties to the lower group; update to the fp32 mean in position order, correctly
+ * rounded divide; an empty group keeps its centroid).  Sinks are never clustered.
+ * Summaries: the same fp32 means of keys and values of each group and of each page
+ * (runs of page_size members in position order inside a group), rounded to nearest
+ * even to kv_dtype.  Chunks are independent, so one call over many chunks equals
+ * one call per chunk.
+ *   kv          the cache; K and V rows of the chunks must be written
+ *   assign_in   nullable [batch][n_kv_heads][n_chunks][chunk_size] int32: groups to use
+ *               instead of k-means (sinks: -1); values outside [0, G) for a non-sink
+ *               position are clamped to that range on the device
+ *   assign_out  nullable, same shape: the groups used
+ * Errors: LOD_ERR_ARG if the range exceeds index->max_chunks or batch != index->batch.
+ */
+int lod_build_chunk(const lod_params* params, const lod_index* index, lod_kv kv, int32_t batch,
+                    int32_t chunk_begin, int32_t n_chunks, const int32_t* assign_in,
+                    int32_t* assign_out, void* stream);
+
+/* Host-only: workspace bytes for lod_attend_decode at (batch, max_seq_len). */
+int lod_decode_ws_bytes(const lod_params* params, int32_t batch, int32_t max_seq_len,
+                        size_t* bytes);
+
+/*
+ * LoD decode: one query token per sequence (How It Works, all three paragraphs).
+ * Sequence b's query sits at position p = seq_lens[b] - 1 and its own K/V row is
+ * already in the cache.  Chunks c < n_b = max(0, p/C - W/C + 1) are summarised; the
+ * block window [n_b*C, p] and the sinks [0, min(n_sink, p+1)) are exact.  Groups are
+ * ranked by the unscaled fp32 fma chain q.kbar in index order, ties to the lower group
+ * id c*G + j; pages of an opened group likewise, ties to the lower page slot.
+ *   q           [batch][n_q_heads][head_dim], kv_dtype
+ *   seq_lens    DEVICE [batch] int32; values are clamped to [1, max_seq_len]
+ *   max_seq_len host bound on seq_lens (sizes the launch; chunks 0..n_b(max_seq_len-1)-1
+ *               must be built for every sequence that reaches it)
+ *   out         [batch][n_q_heads][head_dim] fp32
+ *   sel_groups  nullable [batch][n_q_heads][top_groups] int32: opened group ids in rank
+ *               order, -1 padding
+ *   sel_pages   nullable [batch][n_q_heads][top_groups][max(top_pages,1)] int32: opened
+ *               chunk-local page slots in rank order, -1 padding (all -1 in two-tier)
+ *   ws          workspace of at least lod_decode_ws_bytes bytes (contents not kept)
+ */
+int lod_attend_decode(const lod_params* params, const lod_index* index, lod_kv kv,
+                      const void* q, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_seq_len, float* out, int32_t* sel_groups,
+                      int32_t* sel_pages, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-only: workspace bytes for lod_attend_prefill. */
+int lod_prefill_ws_bytes(const lod_params* params, int32_t batch, int32_t n_q,
+                         int32_t max_tokens, size_t* bytes);
+
+/*
+ * LoD prefill (causal): rows q_start .. q_start+n_q-1 of every sequence, each row p
+ * computed exactly as lod_attend_decode computes a query at p (same selection, same
+ * terms).  K/V rows [0, q_start+n_q) must be in the cache and chunks
+ * 0 .. n_b(q_start+n_q-1)-1 built.  q_start must be a multiple of chunk_size.
+ *   q           [batch][n_q][n_q_heads][head_dim], kv_dtype
+ *   out         [batch][n_q][n_q_heads][head_dim] fp32
+ *   sel_groups  nullable [batch][n_q][n_q_heads][top_groups]
+ *   sel_pages   nullable [batch][n_q][n_q_heads][top_groups][max(top_pages,1)]
+ */
+int lod_attend_prefill(const lod_params* params, const lod_index* index, lod_kv kv,
+                       const void* q, int32_t q_start, int32_t n_q, int32_t batch, float* out,
+                       int32_t* sel_groups, int32_t* sel_pages, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Host-only: workspace bytes for lod_dense_decode. */
+int lod_dense_decode_ws_bytes(const lod_params* params, int32_t batch, int32_t max_seq_len,
+                              size_t* bytes);
+
+/*
+ * Dense causal softmax attention of one query per sequence over rows [0, seq_lens[b]-1]
+ * (no LoD): the baseline the method is measured against.  Same q/out/seq_lens layout
+ * as lod_attend_decode; uses only params' head counts, head_dim, kv_dtype and scale.
+ */
+int lod_dense_decode(const lod_params* params, lod_kv kv, const void* q,
+                     const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float* out,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense causal prefill: rows q_start .. q_start+n_q-1, row p attends to [0, p].
+ * Same q/out layout as lod_attend_prefill.  No workspace.
+ */
+int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_t q_start,
+                      int32_t n_q, int32_t batch, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOD_H */

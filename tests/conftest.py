@@ -19,3 +19,13 @@ def _oracle_built():
     if not os.path.exists(orc._LIB_PATH):
         orc.build_library(force=False)
     yield
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Compile the HIP library in-tree if it is not there (hipcc cross-compiles on CPU)."""
+    from hierarchical_kv_approximation_amd import lod
+    if not os.path.exists(lod.LIB_PATH):
+        from hierarchical_kv_approximation_amd import _build
+        _build.build()
+    yield

@@ -1,0 +1,100 @@
+"""Shared helpers of the GPU parity tests: build one case on both sides and compare.
+
+Inputs come from the seeded generator only; the oracle sees the very same arrays as
+the GPU (bf16 values converted exactly to fp32)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from hierarchical_kv_approximation_amd import lod, synth
+from oracle import oracle as orc
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-3}
+
+
+def configs(dtype, Hq, Hkv, G, TG=8, TP=2, W=512, S=4, iters=10):
+    gcfg = lod.Config(n_q_heads=Hq, n_kv_heads=Hkv, groups=G, top_groups=TG, top_pages=TP,
+                      window=W, n_sink=S, kmeans_iters=iters, dtype=dtype)
+    ocfg = orc.Config(d=128, groups=G, top_groups=TG, top_pages=TP, window=W, n_sink=S, iters=iters,
+                      bf16=(dtype == torch.bfloat16))
+    return gcfg, ocfg
+
+
+class Case:
+    """Inputs on host and device, GPU index built by k-means (or injected assignments)."""
+
+    def __init__(self, gcfg, ocfg, B, T, seed=0, sigma=0.3, zero_variance=False, device="cuda",
+                 gen_device="cpu"):
+        self.gcfg, self.ocfg, self.B, self.T = gcfg, ocfg, B, T
+        Hkv = gcfg.n_kv_heads
+        K, V, cen, _ = synth.clustered_kv(B, T, Hkv, 128, seed=seed, sigma=sigma, dtype=gcfg.dtype,
+                                          zero_variance=zero_variance, device=gen_device)
+        self.cen = cen
+        self.Kd, self.Vd = K.to(device), V.to(device)
+        self.K, self.V = K, V  # generator-side copies (host or device)
+        self.nchunks = T // 256
+        self.index = lod.LodIndex.allocate(gcfg, B, T, device=device)
+        self._streams = {}
+
+    def build_gpu(self, n_chunks=None, assign_in=None):
+        n = self.nchunks if n_chunks is None else n_chunks
+        a = lod.build_chunk(self.gcfg, self.index, self.Kd, self.Vd, 0, n, assign_in=assign_in,
+                            want_assign=True)
+        torch.cuda.synchronize()
+        return a
+
+    def stream(self, b, h):
+        if (b, h) not in self._streams:
+            self._streams[(b, h)] = (self.K[b, :, h, :].float().cpu().numpy().copy(),
+                                     self.V[b, :, h, :].float().cpu().numpy().copy())
+        return self._streams[(b, h)]
+
+    def oracle_index(self, keys, n_chunks=None, assign_in=None):
+        n = self.nchunks if n_chunks is None else n_chunks
+        st = {k: self.stream(*k) for k in keys}
+        ain = None
+        if assign_in is not None:
+            ain = assign_in.cpu().numpy()
+        return st, orc.build_all(self.ocfg, st, n, assign_in=ain)
+
+    def queries(self, seed=1, kind="matched", n_rows=None):
+        return synth.queries(self.B, self.gcfg.n_q_heads, self.cen, seed=seed, kind=kind,
+                             n_rows=n_rows, dtype=self.gcfg.dtype)
+
+
+def gpu_pages(index: lod.LodIndex, b, h, n_chunks):
+    """Per-chunk page lists from the GPU index: (counts [n][PS], members [n][PS][16])."""
+    a = index.arrays()
+    G, PS = index.cfg.groups, index.cfg.page_slots
+    meta = a["meta"][b, h, :n_chunks].cpu().numpy().astype(np.int64)
+    gpg, pst, perm = meta[:, : G + 1], meta[:, G + 1: G + 1 + PS + 1], meta[:, G + 1 + PS + 1:]
+    counts = pst[:, 1:] - pst[:, :-1]
+    mem = -np.ones((n_chunks, PS, 16), np.int64)
+    for c in range(n_chunks):
+        for sl in range(PS):
+            for k in range(counts[c, sl]):
+                mem[c, sl, k] = c * 256 + perm[c, pst[c, sl] + k]
+    return gpg, counts, mem
+
+
+def compare_index(index: lod.LodIndex, oidx: dict, b, h, n_chunks):
+    """Bit-exact comparison of one stream's summaries and layout with the oracle's."""
+    a = index.arrays()
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    assert np.array_equal(a["assign"][b, h, :n_chunks].cpu().numpy().astype(np.int32), oidx["assign"]), \
+        "k-means assignments differ"
+    gpg, counts, mem = gpu_pages(index, b, h, n_chunks)
+    G = index.cfg.groups
+    gcount = np.array([[counts[c, gpg[c, j]:gpg[c, j + 1]].sum() for j in range(G)]
+                       for c in range(n_chunks)], dtype=np.int64).reshape(n_chunks, G)
+    assert np.array_equal(gcount, oidx["gcount"])
+    assert np.array_equal(counts, oidx["pcount"])
+    assert np.array_equal(mem, oidx["pmem"])
+    for name in ("gk", "gv", "pk", "pv"):
+        g = f(a[name][b, h, :n_chunks])
+        assert np.array_equal(g.view(np.uint32), oidx[name].view(np.uint32)), f"{name} differs"
+    gln = a["gln"][b, h, :n_chunks].cpu().numpy()
+    assert np.array_equal(np.isfinite(gln), oidx["gcount"] > 0)
+    ok = oidx["gcount"] > 0
+    assert np.allclose(gln[ok], np.log(oidx["gcount"][ok]), rtol=0, atol=1e-6)

@@ -1,0 +1,206 @@
+"""GPU parity of the LoD build and decode path against the CPU oracle (through the C ABI).
+
+Bar: k-means assignments, summaries, group and page selections bit-exact; outputs within
+1e-5 max-abs (fp32 KV) and 2e-3 (bf16 KV)."""
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_kv_approximation_amd import lod
+from oracle import oracle as orc
+
+from lodcase import TOL, Case, compare_index, configs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _decode_and_compare(case, keys_oidx, seq, q, check_heads=None):
+    """GPU decode at seq_lens=seq vs the oracle on every (b, h) (or check_heads)."""
+    g, o = case.gcfg, case.ocfg
+    st, oidx = keys_oidx
+    dev = case.Kd.device
+    sl = torch.tensor(seq, dtype=torch.int32, device=dev)
+    out, sg, sp = lod.attend_decode(g, case.index, case.Kd, case.Vd, q.to(dev), sl, max(seq),
+                                    want_selection=True)
+    torch.cuda.synchronize()
+    out, sg, sp = out.cpu().numpy(), sg.cpu().numpy(), sp.cpu().numpy()
+    qf = q.float().cpu().numpy()
+    hpg = g.n_q_heads // g.n_kv_heads
+    heads = check_heads or [(b, h) for b in range(case.B) for h in range(g.n_q_heads)]
+    worst = 0.0
+    for b, h in heads:
+        kv = (b, h // hpg)
+        r = orc.attend(o, oidx[kv], *st[kv], qf[b, h], seq[b] - 1)
+        assert np.array_equal(sg[b, h], r["sel_groups"]), (b, h, sg[b, h], r["sel_groups"])
+        assert np.array_equal(sp[b, h], r["sel_pages"]), (b, h)
+        worst = max(worst, float(np.max(np.abs(out[b, h] - r["out"]))))
+    assert worst <= TOL[g.dtype], worst
+    return worst
+
+
+# ------------------------------------------------------------------ fp32, one head, 4096 keys
+
+@pytest.fixture(scope="module")
+def c1():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g, o = configs(torch.float32, 1, 1, G=4, W=256, S=1)
+    case = Case(g, o, 1, 4096, seed=0)
+    case.assign = case.build_gpu()
+    case.oracle = case.oracle_index([(0, 0)])
+    return case
+
+
+def test_c1_build_bit_exact(c1):
+    compare_index(c1.index, c1.oracle[1][(0, 0)], 0, 0, c1.nchunks)
+    assert np.array_equal(c1.assign[0, 0].cpu().numpy(), c1.oracle[1][(0, 0)]["assign"])
+
+
+@pytest.mark.parametrize("kind", ["matched", "diffuse"])
+def test_c1_decode_parity(c1, kind):
+    for i, T in enumerate([4096, 4000, 3001, 700, 513, 512, 511, 257, 256, 255, 2, 1]):
+        q = c1.queries(seed=10 + i, kind=kind)
+        _decode_and_compare(c1, c1.oracle, [T], q)
+
+
+def test_c1_zero_variance_equals_dense():
+    g, o = configs(torch.float32, 1, 1, G=4, W=256, S=1)
+    case = Case(g, o, 1, 4096, seed=5, zero_variance=True)
+    case.build_gpu()
+    st, oidx = case.oracle_index([(0, 0)])
+    compare_index(case.index, oidx[(0, 0)], 0, 0, case.nchunks)
+    for i in range(4):
+        q = case.queries(seed=20 + i)
+        sl = torch.tensor([4096], dtype=torch.int32, device="cuda")
+        out = lod.attend_decode(g, case.index, case.Kd, case.Vd, q.cuda(), sl, 4096)
+        dense = lod.dense_decode(g, case.Kd, case.Vd, q.cuda(), sl, 4096)
+        ref, _ = orc.dense(o, *st[(0, 0)], q[0, 0].float().numpy(), 4095)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(out[0, 0].cpu().numpy() - ref)) <= 1e-5
+        assert np.max(np.abs(dense[0, 0].cpu().numpy() - ref)) <= 1e-5
+
+
+# ------------------------------------------------------------------ bf16 GQA 64/8, batch 4, 32K
+
+@pytest.fixture(scope="module")
+def c2():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g, o = configs(torch.bfloat16, 64, 8, G=8, W=512, S=4)
+    case = Case(g, o, 4, 32768, seed=1)
+    case.assign = case.build_gpu()
+    keys = [(b, h) for b in range(4) for h in range(8)]
+    case.oracle = case.oracle_index(keys)
+    return case
+
+
+def test_c2_kmeans_assignments_bit_exact(c2):
+    a = c2.assign.cpu().numpy()
+    for (b, h), idx in c2.oracle[1].items():
+        assert np.array_equal(a[b, h], idx["assign"]), (b, h)
+
+
+@pytest.mark.parametrize("bh", [(0, 0), (3, 7), (2, 5)])
+def test_c2_summaries_bit_exact(c2, bh):
+    compare_index(c2.index, c2.oracle[1][bh], bh[0], bh[1], c2.nchunks)
+
+
+@pytest.mark.parametrize("seq", [[32768, 32768, 32768, 32768], [32768, 30001, 1000, 257],
+                                 [513, 512, 1, 4097]])
+def test_c2_decode_parity(c2, seq):
+    q = c2.queries(seed=sum(seq) % 1000)
+    _decode_and_compare(c2, c2.oracle, seq, q)
+
+
+def test_c2_decode_diffuse_queries(c2):
+    q = c2.queries(seed=7, kind="diffuse")
+    _decode_and_compare(c2, c2.oracle, [32768, 20000, 9000, 4000], q)
+
+
+def test_c2_decode_is_deterministic(c2):
+    q = c2.queries(seed=8).cuda()
+    sl = torch.full((4,), 32768, dtype=torch.int32, device="cuda")
+    a = lod.attend_decode(c2.gcfg, c2.index, c2.Kd, c2.Vd, q, sl, 32768)
+    b = lod.attend_decode(c2.gcfg, c2.index, c2.Kd, c2.Vd, q, sl, 32768)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_c2_dense_decode_parity(c2):
+    q = c2.queries(seed=9)
+    seq = [32768, 30001, 1000, 1]
+    sl = torch.tensor(seq, dtype=torch.int32, device="cuda")
+    out = lod.dense_decode(c2.gcfg, c2.Kd, c2.Vd, q.cuda(), sl, 32768).cpu().numpy()
+    st = c2.oracle[0]
+    qf = q.float().numpy()
+    for b in range(4):
+        for h in (0, 13, 63):
+            ref, _ = orc.dense(c2.ocfg, *st[(b, h // 8)], qf[b, h], seq[b] - 1)
+            assert np.max(np.abs(out[b, h] - ref)) <= 2e-3
+
+
+# ------------------------------------------------------------------ variants
+
+@pytest.mark.parametrize("top_pages", [0, 1, 3])
+def test_pages_variants_two_tier_and_others(top_pages):
+    g, o = configs(torch.bfloat16, 16, 2, G=8, TP=top_pages, W=512, S=4)
+    case = Case(g, o, 2, 8192, seed=11)
+    case.build_gpu()
+    orc_ = case.oracle_index([(b, h) for b in range(2) for h in range(2)])
+    _decode_and_compare(case, orc_, [8192, 5000], case.queries(seed=12))
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 2), (8, 2), (16, 4)])
+def test_head_ratios(hq, hkv):
+    g, o = configs(torch.bfloat16, hq, hkv, G=8, W=512, S=4)
+    case = Case(g, o, 2, 4096, seed=13)
+    case.build_gpu()
+    orc_ = case.oracle_index([(b, h) for b in range(2) for h in range(hkv)])
+    _decode_and_compare(case, orc_, [4096, 3333], case.queries(seed=14))
+
+
+@pytest.mark.parametrize("G,TG", [(4, 16), (16, 8), (2, 3)])
+def test_group_counts_and_top_groups(G, TG):
+    g, o = configs(torch.bfloat16, 8, 1, G=G, TG=TG, W=256, S=2)
+    case = Case(g, o, 1, 4096, seed=15)
+    case.build_gpu()
+    orc_ = case.oracle_index([(0, 0)])
+    compare_index(case.index, orc_[1][(0, 0)], 0, 0, case.nchunks)
+    _decode_and_compare(case, orc_, [4096], case.queries(seed=16))
+
+
+def test_injected_assignments():
+    """Parity mode: the GPU takes the oracle's k-means assignments (oracle -> GPU only)."""
+    g, o = configs(torch.bfloat16, 8, 2, G=8, W=512, S=4)
+    case = Case(g, o, 1, 4096, seed=17, sigma=0.8)
+    keys = [(0, 0), (0, 1)]
+    st, oidx = case.oracle_index(keys)
+    ain = np.stack([np.stack([oidx[(0, h)]["assign"] for h in range(2)])])  # [1][2][n][C]
+    case.build_gpu(assign_in=torch.from_numpy(ain))
+    for h in range(2):
+        compare_index(case.index, oidx[(0, h)], 0, h, case.nchunks)
+    _decode_and_compare(case, (st, oidx), [4096], case.queries(seed=18))
+
+
+# ------------------------------------------------------------------ full size, sampled
+
+def test_c3_full_size_128k_batch8_sampled():
+    """128K context, batch 8, GQA 64/8: build and decode at full size; two sampled
+    (sequence, KV head) streams checked against the oracle (16 query heads)."""
+    g, o = configs(torch.bfloat16, 64, 8, G=8, W=512, S=4)
+    case = Case(g, o, 8, 131072, seed=21, gen_device="cuda")
+    a = case.build_gpu()
+    keys = [(0, 0), (7, 5)]
+    st, oidx = case.oracle_index(keys)
+    for b, h in keys:
+        assert np.array_equal(a[b, h].cpu().numpy(), oidx[(b, h)]["assign"])
+        compare_index(case.index, oidx[(b, h)], b, h, case.nchunks)
+    q = case.queries(seed=22)
+    heads = [(b, kvh * 8 + i) for b, kvh in keys for i in range(8)]
+    _decode_and_compare(case, (st, oidx), [131072] * 8, q, check_heads=heads)
