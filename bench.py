@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of LoD attention on one MI355X: decode at 128K context (the headline), with
+the dense-decode time on the same inputs, the dominant kernel's roofline, and the CPU
+oracle timed on a bounded sample.  Prints ONE JSON line.
+
+Workload (defaults): bf16 KV, GQA 64 query / 8 KV heads, head_dim 128, batch 8,
+context 131072; groups of a 256-token chunk = 8, pages of 16, top 8 groups, top 2
+pages, block window 512, 4 sinks.  Keys from a 32-centre Gaussian mixture (sigma 0.3),
+values N(0, 1), queries matched to the mixture (all seeded, synthetic).
+
+A step is one lod_attend_decode call: one decode token for every sequence of the batch
+through one attention layer.  Steps rotate over `--layers` independent layer copies
+(cache + index) so the 256 MB Infinity Cache cannot serve a layer's reads from the
+previous step.  Positions advance by one every `--layers` steps and the timed steps
+cross a chunk boundary, so the timed region includes the lod_build_chunk call that the
+boundary requires for each layer (the build-during-decode step of the method).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LoD attention decode tok/s & prefill tok/s at 128K ctx; % HBM / MFMA peak"
+HBM_PEAK_GBS = 8000.0
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the call's stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return float(t.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch measured by rocprofv3 (profiles/<name>.json), or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def algorithmic_decode_bytes(cfg, index, sel_g, sel_p, seq_lens, elt):
+    """Bytes the method itself must move for one decode call (per the design notes):
+    group summaries (k, v, ln n) of every summarised chunk; page summaries of opened
+    groups; K/V rows of the union of opened pages over the query heads of a KV head; the
+    exact window and sinks; q and the fp32 output."""
+    import numpy as np
+    d, G, C, W, S = cfg.head_dim, cfg.groups, cfg.chunk_size, cfg.window, cfg.n_sink
+    Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
+    g = Hq // Hkv
+    row = 2 * d * elt
+    meta = index.arrays()["meta"].cpu().numpy().astype(np.int64)
+    sg, sp = sel_g.cpu().numpy(), sel_p.cpu().numpy()
+    PS = cfg.page_slots
+    total = scan = 0
+    for b, T in enumerate(seq_lens):
+        p = T - 1
+        nb = max(0, p // C - W // C + 1)
+        tail = p - nb * C + 1
+        sinks = min(S, nb * C)
+        for kvh in range(Hkv):
+            grp = nb * G * (row + 4)
+            exact = (tail + sinks) * row
+            opened, rows = set(), set()
+            for h in range(kvh * g, (kvh + 1) * g):
+                for i, gid in enumerate(sg[b, h]):
+                    if gid < 0:
+                        continue
+                    c, j = divmod(int(gid), G)
+                    opened.add((c, j))
+                    m = meta[b, kvh, c]
+                    gpg, pst, perm = m[: G + 1], m[G + 1: G + 1 + PS + 1], m[G + 1 + PS + 1:]
+                    slots = range(gpg[j], gpg[j + 1]) if cfg.top_pages == 0 else \
+                        [s for s in sp[b, h, i] if s >= 0]
+                    for s in slots:
+                        rows.update(c * C + int(x) for x in perm[pst[s]:pst[s + 1]])
+            pages = 0
+            for c, j in opened:
+                gpg = meta[b, kvh, c][: G + 1]
+                pages += int(gpg[j + 1] - gpg[j])
+            total += grp + exact + pages * (row + 4) + len(rows) * (row + 4)
+            scan += grp + exact
+        total += Hq * d * (elt + 4)
+        scan += Hq * d * elt
+    return int(total), int(scan)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--ctx", type=int, default=131072)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-decode comparison")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this LoD "
+              "attention build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from hierarchical_kv_approximation_amd import lod, synth
+
+    dev = torch.device("cuda:0")
+    B, T, L = args.batch, args.ctx, args.layers
+    K, W = max(2, args.steps), max(0, args.warmup)
+    cfg = lod.Config(n_q_heads=64, n_kv_heads=8, groups=8, top_groups=8, top_pages=2, window=512,
+                     n_sink=4, dtype=torch.bfloat16)
+    C = cfg.chunk_size
+    elt = 2
+    assert T % C == 0
+    npos = (K + L - 1) // L
+    # first query position sits just below a chunk boundary so the timed steps cross it
+    boundary = T  # first query position of chunk T/C
+    s0 = boundary + 1 - max(1, npos // 2)  # seq_len of the first timed position
+    cap = T + C
+    nb0 = max(0, (s0 - 1) // C - cfg.window // C + 1)  # chunks built before the run
+    build_chunk = boundary // C - cfg.window // C  # chunk that the boundary requires
+    max_len = s0 + npos - 1
+
+    t_setup = time.time()
+    layers = []
+    for li in range(L):
+        Kc, Vc, cen, _ = synth.clustered_kv(B, cap, 8, 128, seed=args.seed + 101 * li, device=dev)
+        q = synth.queries(B, 64, cen, seed=args.seed + 7 + 101 * li)
+        index = lod.LodIndex.allocate(cfg, B, cap, device=dev)
+        lod.build_chunk(cfg, index, Kc, Vc, 0, nb0)
+        layers.append({"K": Kc, "V": Vc, "q": q, "index": index, "built": False})
+        del cen
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    log(f"setup done: {L} layers of B={B} x {cap} tokens, {nb0} chunks built ({setup_s:.1f} s)")
+
+    seq = torch.tensor([[s0 + k] * B for k in range(npos)], dtype=torch.int32, device=dev)
+    ws = torch.empty(lod.decode_ws_bytes(cfg, B, max_len), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, 64, 128, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+
+    # warm-up: below the boundary, no build
+    for k in range(W):
+        Ly = layers[k % L]
+        lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[0], max_len, ws=ws, out=out)
+    torch.cuda.synchronize()
+
+    # timed region
+    ev = hip.create(3 * K)
+    bev = hip.create(2 * L)
+    t0, t1 = hip.create(2)
+    nbuilt = 0
+    hip.record(t0, stream)
+    for k in range(K):
+        li, pi = k % L, k // L
+        Ly = layers[li]
+        if s0 + pi - 1 >= boundary and not Ly["built"]:
+            hip.record(bev[2 * nbuilt], stream)
+            lod.build_chunk(cfg, Ly["index"], Ly["K"], Ly["V"], build_chunk, 1)
+            hip.record(bev[2 * nbuilt + 1], stream)
+            Ly["built"] = True
+            nbuilt += 1
+        keep = lod.trace_events(ev[3 * k: 3 * k + 3])
+        lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[pi], max_len, ws=ws, out=out)
+        lod.trace_events(None)
+        del keep
+    hip.record(t1, stream)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(t0, t1)
+    scan_ms = [hip.ms(ev[3 * k], ev[3 * k + 1]) for k in range(K)]
+    open_ms = [hip.ms(ev[3 * k + 1], ev[3 * k + 2]) for k in range(K)]
+    call_ms = [hip.ms(ev[3 * k], ev[3 * k + 2]) for k in range(K)]
+    build_ms = [hip.ms(bev[2 * i], bev[2 * i + 1]) for i in range(nbuilt)]
+    hip.destroy(ev + bev + [t0, t1])
+    ms_per_step = total_ms / K
+    log(f"timed {K} steps: {ms_per_step * 1000:.1f} us/step")
+
+    # algorithmic bytes at the last timed position (selection from one extra call)
+    Ly = layers[(K - 1) % L]
+    last = seq[(K - 1) // L]
+    o2, sg, sp = lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], last, max_len,
+                                   want_selection=True)
+    torch.cuda.synchronize()
+    lens = [int(x) for x in last.cpu()]
+    bytes_call, bytes_scan = algorithmic_decode_bytes(cfg, Ly["index"], sg, sp, lens, elt)
+    scan_avg = sum(scan_ms) / K
+    call_avg = sum(call_ms) / K
+
+    # dense decode on the same inputs (same rotation, same positions)
+    dense = None
+    if not args.no_dense:
+        dws = torch.empty(lod.dense_decode_ws_bytes(cfg, B, max_len), dtype=torch.uint8, device=dev)
+        for k in range(min(W, 4)):
+            Ly = layers[k % L]
+            lod.dense_decode(cfg, Ly["K"], Ly["V"], Ly["q"], seq[0], max_len, ws=dws, out=out)
+        torch.cuda.synchronize()
+        d0, d1 = hip.create(2)
+        KD = max(L, min(K, 16))
+        hip.record(d0, stream)
+        for k in range(KD):
+            Ly = layers[k % L]
+            lod.dense_decode(cfg, Ly["K"], Ly["V"], Ly["q"], seq[min(k // L, npos - 1)], max_len, ws=dws, out=out)
+        hip.record(d1, stream)
+        torch.cuda.synchronize()
+        dms = hip.ms(d0, d1) / KD
+        hip.destroy([d0, d1])
+        dense_bytes = sum(lens) * 8 * 2 * 128 * elt
+        log(f"dense decode: {dms * 1000:.1f} us/call")
+        dense = {"ms_per_call": round(dms, 4), "tok_per_s": round(B * 1000.0 / dms, 1),
+                 "achieved_GBs": round(dense_bytes / dms / 1e6, 1),
+                 "lod_speedup_vs_dense": round(dms / ms_per_step, 2)}
+
+    # CPU oracle on a bounded sample: sequence 0 of layer 0, all 64 heads, one token
+    cpu = None
+    if not args.no_cpu:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline(cfg, layers[0], s0, args.cpu_seconds)
+        log(f"CPU oracle: {cpu['value']} tok/s on {cpu['cores']} threads")
+
+    for Ly in layers:
+        del Ly["K"], Ly["V"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(B * 1000.0 / ms_per_step, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "LoD decode, one attention layer per step: context 131072, batch 8, "
+                        "GQA 64/8, head_dim 128, bf16 KV, 8 groups per 256-token chunk, pages of 16, "
+                        "top 8 groups / top 2 pages, block window 512, 4 sinks",
+            "batch": B, "context": T, "layers_rotated": L,
+            "positions": [s0 - 1, max_len - 1], "chunk_builds_in_timed_region": nbuilt,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_scan_kernel (group-summary stream + window tiles)",
+            "achieved": round(bytes_scan / (scan_avg * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bytes_scan / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": profiled_traffic("decode_scan_traffic"),
+            "algorithmic_bytes_per_launch": bytes_scan,
+            "avg_launch_us": round(scan_avg * 1000, 2),
+        },
+        "cpu_baseline": cpu,
+        "extra": {
+            "lod_call_us": round(call_avg * 1000, 2),
+            "scan_us": round(scan_avg * 1000, 2),
+            "open_combine_us": round(sum(open_ms) / K * 1000, 2),
+            "build_one_chunk_batch_us": [round(x * 1000, 1) for x in build_ms],
+            "algorithmic_bytes_per_call": bytes_call,
+            "call_achieved_GBs": round(bytes_call / (call_avg * 1e-3) / 1e9, 1),
+            "call_frac_hbm": round(bytes_call / (call_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "dense_decode": dense,
+            "setup_s": round(setup_s, 1),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, Ly, seq_len, seconds):
+    """The oracle, as it stands, on one sequence's decode token (all 64 query heads)."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    threads = cpu_threads()
+    ocfg = orc.Config(d=128, groups=cfg.groups, top_groups=cfg.top_groups, top_pages=cfg.top_pages,
+                      window=cfg.window, n_sink=cfg.n_sink, bf16=True)
+    p = seq_len - 1
+    K = Ly["K"][0:1, :seq_len].float().cpu().numpy()
+    V = Ly["V"][0:1, :seq_len].float().cpu().numpy()
+    st = orc.streams(K, V)
+    nb = ocfg.built_chunks(p)
+    idx = orc.build_all(ocfg, st, nb, threads=threads)  # index build: not timed
+    Q = Ly["q"][0:1].float().cpu().numpy()
+    t = time.time()
+    n = 0
+    while True:
+        orc.decode(ocfg, st, idx, Q, [seq_len], threads=threads)
+        n += 1
+        el = time.time() - t
+        if el >= seconds or n >= 64:
+            break
+    return {"value": round(n / el, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} decode token(s) of one sequence (all 64 query heads) at position {p}, "
+                      f"index prebuilt (not timed); {el:.1f} s wall on {threads} threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -198,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     T* gk = reinterpret_cast<T*>(A.index + A.L.gk) + gbase * kD;
     T* gv = reinterpret_cast<T*>(A.index + A.L.gv) + gbase * kD;
     float* gln = reinterpret_cast<float*>(A.index + A.L.gln) + gbase;
+    float* gkn = reinterpret_cast<float*>(A.index + A.L.gkn) + gbase;
     T* pk = reinterpret_cast<T*>(A.index + A.L.pk) + pbase * kD;
     T* pv = reinterpret_cast<T*>(A.index + A.L.pv) + pbase * kD;
     float* pln = reinterpret_cast<float*>(A.index + A.L.pln) + pbase;
@@ -219,7 +220,18 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
         store_elt(&gk[e], s.cnt[j] > 0 ? gmean[e] : 0.0f);
     }
     if (tid < G) gln[tid] = s.cnt[tid] > 0 ? logf((float)s.cnt[tid]) : -INFINITY;
-
+    // Norm bound of every stored mean key (the storage-rounded value), rounded up
+    // generously; it only widens the error bound that MFMA ranking scores are checked
+    // against.
+    if (tid < G) {
+        float ss = 0.0f;
+        if (s.cnt[tid] > 0)
+            for (int t = 0; t < kD; ++t) {
+                const float x = Elt<T>::to_f32(Elt<T>::store_round(gmean[tid * kD + t]));
+                ss = __builtin_fmaf(x, x, ss);
+            }
+        gkn[tid] = sqrtf(ss) * 1.0001f + 1e-30f;
+    }
     // Page means of keys: thread (slot, t) sums <= 16 members in position order.
     for (int e = tid; e < PS * kD; e += kThreads) {
         const int sl = e / kD, t = e % kD;

@@ -55,6 +55,20 @@ struct DecodeArgs {
 
 __device__ __forceinline__ void row_info(const DecodeArgs& A, int row, int& seq, int& p);
 
+struct DenseArgs {
+    const void* k;
+    const void* v;
+    int64_t sb, st, sh;
+    const void* q;
+    const int32_t* seq_lens;
+    int max_seq_len;
+    float* part;
+    float* out;  // non-null: nsplit == 1 and rows write normalised outputs here
+    int Hq, Hkv, rows_per_wg, nsplit;
+    float scale;
+    int seq0, rows_per_seq, pos0;  // row mapping when seq_lens is null (as DecodeArgs)
+};
+
 __device__ __forceinline__ int query_pos(const int32_t* seq_lens, int b, int max_seq_len) {
     int s = seq_lens[b];
     s = s < 1 ? 1 : (s > max_seq_len ? max_seq_len : s);
@@ -387,27 +401,14 @@ __global__ __launch_bounds__(kThreads) void decode_scan_kernel(DecodeArgs A) {
     write_partial<HG>(s, R, o, m_run, l_run, part0, head_stride);
 }
 
-// ---------------------------------------------------------------------------- open
+// ---------------------------------------------------------------------------- open + combine
 
-constexpr int kBatch = 64;  // items per online-softmax batch in the open kernel
-
-template <typename T>
-struct OpenSmem {
-    float qs[kD];
-    uint64_t sel[kMaxTG];
-    int nsel;
-    int npg, ps0, c, nex;
-    float pr[kPage];
-    int prank[kPage];  // rank of each page of the group (-1: not opened)
-    int pst[kPage + 1];
-    int ipos[kChunk];  // exact positions of opened pages
-    int bpos[kBatch];  // batch items: position (exact) or -1 (coarse)
-    float blam[kBatch];
-    float bw[kBatch];
-    const T* bv[kBatch];
-    int bn;
-    float ored[16][kD];
-};
+// Wave-local ordering of LDS traffic between lanes of one wave.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // 8 consecutive elements of a row starting at element 8*l16, as fp32.
 template <typename T>
@@ -425,76 +426,113 @@ __device__ __forceinline__ void load8<float>(const float* row, int l16, float* f
     Elt<float>::unpack(u1, f + 4);
 }
 
-// Online-softmax step over the current batch (s.bn items in s.bpos / s.blam / s.bv).
-template <typename T>
-__device__ void open_batch(OpenSmem<T>& s, const float* q8, const T* kb, const T* vb, int64_t st,
-                           float scale, float& m_run, float& l_run, float* o8) {
-    const int sg = threadIdx.x >> 4, l16 = threadIdx.x & 15;
-    const int n = s.bn;
-    for (int it = sg; it < n; it += 16) {
-        const int pos = s.bpos[it];
-        if (pos >= 0) {
-            float kf[8];
-            load8<T>(kb + (int64_t)pos * st, l16, kf);
-            float a = 0.0f;
+// Online-softmax state of one 16-lane subgroup: lane holds o for dims 8*l16 .. 8*l16+7.
+struct Online {
+    float m, l, o[8];
+    __device__ void init() {
+        m = -INFINITY;
+        l = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-            if (l16 == 0) s.blam[it] = scale * a;
-        }
+        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
     }
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int it = 0; it < n; ++it) mx = fmaxf(mx, s.blam[it]);
-    const float m_new = fmaxf(m_run, mx);
-    if (threadIdx.x < n) s.bw[threadIdx.x] = softmax_exp(s.blam[threadIdx.x] - m_new);
-    __syncthreads();
-    float ls = 0.0f;
-    for (int it = 0; it < n; ++it) ls += s.bw[it];
-    const float alpha = m_run == -INFINITY ? 0.0f : softmax_exp(m_run - m_new);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+    __device__ __forceinline__ void add(float lam, const float* v) {
+        if (lam == -INFINITY) return;
+        const float mn = fmaxf(m, lam);
+        const float a = softmax_exp(m - mn);  // m = -inf -> 0
+        const float w = softmax_exp(lam - mn);
+        l = __builtin_fmaf(l, a, w);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o8[e] *= alpha;
-    for (int it = sg; it < n; it += 16) {
-        const int pos = s.bpos[it];
-        const T* vr = pos >= 0 ? vb + (int64_t)pos * st : s.bv[it];
-        float vf[8];
-        load8<T>(vr, l16, vf);
-        const float w = s.bw[it];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] = __builtin_fmaf(w, vf[e], o8[e]);
+        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(w, v[e], o[e] * a);
+        m = mn;
     }
-    __syncthreads();
-}
+};
 
+constexpr int kOpenBatch = 4;   // items per subgroup whose loads are issued together
+constexpr int kMetaMax = 320;   // int16 entries of one chunk's meta row (>= meta_stride)
+constexpr int kGPW = kMaxTG / 4;             // opened groups per wave (at most)
+constexpr int kItemsPerWave = kGPW * kChunk; // exact rows of a wave's groups (two-tier bound)
+
+template <typename T>
+struct OpenSmem {
+    alignas(16) int16_t meta[kMaxTG][kMetaMax];  // meta row of each opened group's chunk
+    float qs[kD];
+    uint64_t sel[kMaxTG];
+    int nsel;
+    int ex[4][kItemsPerWave];  // per wave: exact positions of the opened pages
+    int nex[4];
+    int cp[4][kGPW * kPage];   // per wave: unopened pages as (group slot k << 8 | page e)
+    float cl[4][kGPW * kPage]; // and their logits
+    int ncp[4];
+    float sm[16], sl[16];      // subgroup states
+    float so[16][kD];
+    float scan_m, scan_l;      // merged state of the scan workgroups' partials
+    float scan_o[kD];
+};
+
+// One workgroup per (query row, query head).  Wave w handles opened groups w, w+4, ...:
+// all of its groups' meta rows, then all of their page rankings (one lane per (group,
+// page), 16-lane segmented top-k), then the item lists, so the dependent global round
+// trips are few.  Every 16-lane subgroup then streams items with its loads batched.
+// Losing candidates of the slices are added back as coarse terms, and the state is
+// merged with the scan workgroups' partial states into the final output.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
     __shared__ OpenSmem<T> s;
-    const int i = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+    const int hq = blockIdx.x, b = blockIdx.y;
     const int HG = A.Hq / A.Hkv;
     const int kvh = hq / HG;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = tid & 15;
+    const int l16 = lane & 15, sgw = lane >> 4;  // subgroup within the wave
     int seq, p;
-    row_info(A, b, seq, p);  // b: query row
+    row_info(A, b, seq, p);
     const int nb = nbuilt(p, A.W);
     const int ng = nb * A.G;
     const int64_t unit = (int64_t)seq * A.Hkv + kvh;
     const int PS = A.L.page_slots;
     const int TPW = A.TP > 0 ? A.TP : 1;
-    const T* qp = reinterpret_cast<const T*>(A.q) + ((int64_t)b * A.Hq + hq) * kD;
+    const int64_t head = (int64_t)b * A.Hq + hq;
+    const T* qp = reinterpret_cast<const T*>(A.q) + head * kD;
     if (tid < kD) s.qs[tid] = Elt<T>::to_f32(qp[tid]);
     float q8[8];
+    load8<T>(qp, l16, q8);
+    const int nscan = A.nslice + A.nwin;
+    const float* part = A.part + head * A.nslot * kPartStride;
+    if (tid >= 2 * 64) {
+        // waves 2-3: merge the scan partial states (one dimension per thread), loads
+        // issued 16 slots at a time, while wave 0 merges the candidates
+        const int d = tid - 128;
+        float M = -INFINITY, L = 0.0f, O = 0.0f;
+        for (int k0 = 0; k0 < nscan; k0 += 16) {
+            float mm[16], ll[16], oo[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q8[e] = Elt<T>::to_f32(qp[8 * l16 + e]);
+            for (int x = 0; x < 16; ++x) {
+                const int k = k0 + x;
+                mm[x] = -INFINITY;
+                if (k < nscan) {
+                    const float* pp = part + (int64_t)k * kPartStride;
+                    mm[x] = pp[kD];
+                    ll[x] = pp[kD + 1];
+                    oo[x] = pp[d];
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                if (mm[x] == -INFINITY) continue;
+                const float mn = fmaxf(M, mm[x]);
+                const float a = softmax_exp(M - mn), e = softmax_exp(mm[x] - mn);
+                L = __builtin_fmaf(ll[x], e, L * a);
+                O = __builtin_fmaf(oo[x], e, O * a);
+                M = mn;
+            }
+        }
+        s.scan_o[d] = O;
+        if (d == 0) { s.scan_m = M; s.scan_l = L; }
+    }
 
-    // 1. global top-k over the slices' candidates (wave 0): per-lane sorted top-16,
-    //    then k rounds of a wave-wide max.
+    // 1. global top-k over the slices' candidates (wave 0)
     const int nsl_used = ng > 0 ? (ng + A.slice - 1) / A.slice : 0;
     const int ncand = nsl_used * A.TG;
-    const uint64_t* cand = A.cand + (int64_t)(b * A.Hq + hq) * A.nslice * A.TG;
+    const uint64_t* cand = A.cand + head * A.nslice * A.TG;
     if (wave == 0) {
         uint64_t lst[kMaxTG];
 #pragma unroll
@@ -525,162 +563,660 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
     __syncthreads();
     const int nsel = s.nsel;
     const uint64_t kth = nsel == A.TG ? s.sel[A.TG - 1] : 0;
-    const bool have = i < nsel;
-    const uint32_t gid = have ? key_id(s.sel[i]) : 0;
-    if (A.sel_groups && tid == 0) A.sel_groups[((int64_t)b * A.Hq + hq) * A.TG + i] = have ? (int)gid : -1;
+    if (A.sel_groups && tid < A.TG) A.sel_groups[head * A.TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
 
     const T* kb = reinterpret_cast<const T*>(A.k) + seq * A.sb + kvh * A.sh;
     const T* vb = reinterpret_cast<const T*>(A.v) + seq * A.sb + kvh * A.sh;
-    float o8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o8[e] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
+    const T* pk_u = reinterpret_cast<const T*>(A.index + A.L.pk) + unit * A.max_chunks * PS * kD;
+    const T* pv_u = reinterpret_cast<const T*>(A.index + A.L.pv) + unit * A.max_chunks * PS * kD;
+    const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + unit * A.max_chunks * PS;
+    const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + unit * A.max_chunks * A.L.meta_stride;
 
-    // 2. opened group i: page ranking, exact rows of opened pages, unopened pages coarse
-    if (have) {
-        const int c = gid / A.G, j = gid % A.G;
-        const int16_t* meta = reinterpret_cast<const int16_t*>(A.index + A.L.meta) +
-                              (unit * A.max_chunks + c) * A.L.meta_stride;
-        const int16_t* gpg = meta;
-        const int16_t* pst = meta + (A.G + 1);
-        const int16_t* perm = meta + (A.G + 1) + (PS + 1);
-        if (tid == 0) {
-            s.ps0 = gpg[j];
-            s.npg = gpg[j + 1] - gpg[j];
-            s.c = c;
+    // 2a. meta rows of this wave's groups (all loads in flight together)
+    const int ngw = (A.TG - wave + 3) / 4;  // group slots of this wave (k: group i = wave + 4k)
+    const int ms16 = A.L.meta_stride / 8;   // 16-byte pieces per meta row
+    for (int x = lane; x < ngw * ms16; x += 64) {
+        const int k = x / ms16, e = x % ms16, i = wave + 4 * k;
+        if (i < nsel) {
+            const int c = key_id(s.sel[i]) / A.G;
+            *reinterpret_cast<uint4*>(&s.meta[i][e * 8]) =
+                *reinterpret_cast<const uint4*>(meta_u + (int64_t)c * A.L.meta_stride + e * 8);
         }
-        __syncthreads();
-        const int npg = s.npg, ps0 = s.ps0;
-        if (tid <= npg) s.pst[tid] = pst[ps0 + tid];
-        const T* pk = reinterpret_cast<const T*>(A.index + A.L.pk) + (unit * A.max_chunks + c) * PS * kD;
-        const T* pv = reinterpret_cast<const T*>(A.index + A.L.pv) + (unit * A.max_chunks + c) * PS * kD;
-        const float* pln = reinterpret_cast<const float*>(A.index + A.L.pln) + (unit * A.max_chunks + c) * PS;
-        if (wave == 0) {
-            float r = 0.0f;
-            if (A.TP > 0 && lane < npg) {
-                const T* row = pk + (int64_t)(ps0 + lane) * kD;
-                for (int t = 0; t < kD; t += Elt<T>::kPer16) {
-                    float f[Elt<T>::kPer16];
-                    Elt<T>::unpack(*reinterpret_cast<const uint4*>(row + t), f);
+    }
+    wave_sync();
+    // 2b. page ranking: lane (k = lane/16, e = lane%16) scores page e of group i = wave+4k
+    {
+        const int k = lane >> 4, e = lane & 15, i = wave + 4 * k;
+        int c = 0, j = 0, ps0 = 0, npg = 0;
+        if (k < ngw && i < nsel) {
+            const uint32_t gid = key_id(s.sel[i]);
+            c = gid / A.G;
+            j = gid % A.G;
+            ps0 = s.meta[i][j];
+            npg = s.meta[i][j + 1] - ps0;
+        }
+        float r = 0.0f;
+        if (A.TP > 0 && e < npg) {
+            const T* row = pk_u + ((int64_t)c * PS + ps0 + e) * kD;
+            constexpr int P16 = Elt<T>::kPer16;
+            uint4 u[kD / P16];
 #pragma unroll
-                    for (int e = 0; e < Elt<T>::kPer16; ++e) r = __builtin_fmaf(s.qs[t + e], f[e], r);
+            for (int x = 0; x < kD / P16; ++x) u[x] = *reinterpret_cast<const uint4*>(row + x * P16);
+#pragma unroll
+            for (int x = 0; x < kD / P16; ++x) {
+                float f[P16];
+                Elt<T>::unpack(u[x], f);
+#pragma unroll
+                for (int t = 0; t < P16; ++t) r = __builtin_fmaf(s.qs[x * P16 + t], f[t], r);
+            }
+        }
+        const float lnp = e < npg ? pln_u[(int64_t)c * PS + ps0 + e] : -INFINITY;
+        int rank = (A.TP == 0 && e < npg) ? 0 : -1;
+        if (A.TP > 0) {
+            uint64_t key = e < npg ? rank_key(r, (uint32_t)e) : 0;
+            const int nopen = npg < A.TP ? npg : A.TP;  // uniform within the 16-lane segment
+            for (int t = 0; t < A.TP; ++t) {          // uniform trip count for the shuffles
+                uint64_t m = key;
+#pragma unroll
+                for (int sh = 8; sh >= 1; sh >>= 1) {
+                    const uint64_t o = shfl_xor_u64(m, sh);
+                    m = o > m ? o : m;
                 }
-            }
-            if (lane < kPage) s.prank[lane] = (A.TP == 0 && lane < npg) ? 0 : -1;
-            if (lane < npg) s.pr[lane] = r;
-            if (A.TP > 0) {
-                uint64_t key = lane < npg ? rank_key(r, (uint32_t)lane) : 0;
-                const int nopen = npg < A.TP ? npg : A.TP;
-                for (int k = 0; k < nopen; ++k) {
-                    const uint64_t wb = wave_max_u64(key);
-                    if (key == wb) { s.prank[lane] = k; key = 0; }
-                }
+                if (t < nopen && key == m && m != 0) { rank = t; key = 0; }
             }
         }
-        __syncthreads();
-        if (A.sel_pages && tid < TPW) {
-            int slot = -1;
-            if (A.TP > 0)
-                for (int e = 0; e < npg; ++e)
-                    if (s.prank[e] == tid) slot = ps0 + e;
-            A.sel_pages[(((int64_t)b * A.Hq + hq) * A.TG + i) * TPW + tid] = slot;
+        // sel_pages: lane t of the segment writes the slot of rank t
+        const int seg0 = lane & ~15;
+        int slot_of_rank = -1;
+        for (int x = 0; x < 16; ++x) {
+            const int rk = __shfl(rank, seg0 + x, 64);
+            if (A.TP > 0 && rk == e) slot_of_rank = ps0 + x;
         }
-        // exact positions of the opened pages (in page order)
-        if (tid == 0) {
-            int n = 0;
-            for (int e = 0; e < npg; ++e) {
-                if (s.prank[e] < 0) continue;
-                for (int qq = s.pst[e]; qq < s.pst[e + 1]; ++qq) s.ipos[n++] = c * kChunk + perm[qq];
+        if (A.sel_pages && k < ngw && i < A.TG && e < TPW)
+            A.sel_pages[(head * A.TG + i) * TPW + e] = i < nsel ? slot_of_rank : -1;
+        // 2c. item lists: unopened pages (coarse) and exact rows of opened pages
+        const bool coarse = e < npg && rank < 0;
+        const uint64_t cm = __ballot(coarse);
+        if (coarse) {
+            const int at = __popcll(cm & ((1ull << lane) - 1ull));
+            s.cp[wave][at] = (k << 8) | e;
+            s.cl[wave][at] = A.scale * r + lnp;
+        }
+        if (lane == 0) s.ncp[wave] = __popcll(cm);
+        // exact rows: page e of group slot k contributes pst[e+1]-pst[e] rows
+        const int16_t* pst = s.meta[i < kMaxTG ? i : 0] + (A.G + 1);
+        const int16_t* perm = pst + (PS + 1);
+        const int cnt = (e < npg && rank >= 0) ? pst[ps0 + e + 1] - pst[ps0 + e] : 0;
+        int off = cnt;  // inclusive prefix over the wave's lanes
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) {
+            const int o = __shfl_up(off, sh, 64);
+            if (lane >= sh) off += o;
+        }
+        const int total = __shfl(off, 63, 64);
+        off -= cnt;
+        for (int x = 0; x < cnt; ++x) s.ex[wave][off + x] = c * kChunk + perm[pst[ps0 + e] + x];
+        if (lane == 0) s.nex[wave] = total;
+    }
+    wave_sync();
+
+    Online st;
+    st.init();
+    // 3. exact rows of the wave's groups, then its coarse pages (subgroup sgw takes sgw, sgw+4, ...)
+    const int nex = s.nex[wave];
+    for (int base = 0; base < nex; base += 4 * kOpenBatch) {
+        float kf[kOpenBatch][8], vf[kOpenBatch][8];
+#pragma unroll
+        for (int x = 0; x < kOpenBatch; ++x) {
+            const int it = base + sgw + 4 * x;
+            if (it < nex) {
+                const int pos = s.ex[wave][it];
+                load8<T>(kb + (int64_t)pos * A.st, l16, kf[x]);
+                load8<T>(vb + (int64_t)pos * A.st, l16, vf[x]);
             }
-            s.nex = n;
         }
-        __syncthreads();
-        const int nex = s.nex;
-        for (int base = 0; base < nex; base += kBatch) {
-            const int n = min(kBatch, nex - base);
-            if (tid < n) s.bpos[tid] = s.ipos[base + tid];
-            if (tid == 0) s.bn = n;
-            __syncthreads();
-            open_batch<T>(s, q8, kb, vb, A.st, A.scale, m_run, l_run, o8);
-        }
-        // unopened pages of the opened group: coarse terms
-        if (tid == 0) {
-            int n = 0;
-            for (int e = 0; e < npg; ++e) {
-                if (s.prank[e] >= 0) continue;
-                s.bpos[n] = -1;
-                s.blam[n] = A.scale * s.pr[e] + pln[ps0 + e];
-                s.bv[n] = pv + (int64_t)(ps0 + e) * kD;
-                ++n;
+#pragma unroll
+        for (int x = 0; x < kOpenBatch; ++x) {
+            const int it = base + sgw + 4 * x;
+            if (it < nex) {
+                float a = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[x][e], a);
+#pragma unroll
+                for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
+                st.add(A.scale * a, vf[x]);
             }
-            s.bn = n;
         }
-        __syncthreads();
-        if (s.bn > 0) open_batch<T>(s, q8, kb, vb, A.st, A.scale, m_run, l_run, o8);
-    } else {
-        if (A.sel_pages && tid < TPW)
-            A.sel_pages[(((int64_t)b * A.Hq + hq) * A.TG + i) * TPW + tid] = -1;
+    }
+    const int ncp = s.ncp[wave];
+    for (int base = 0; base < ncp; base += 4 * kOpenBatch) {
+        float vf[kOpenBatch][8];
+#pragma unroll
+        for (int x = 0; x < kOpenBatch; ++x) {
+            const int it = base + sgw + 4 * x;
+            if (it < ncp) {
+                const int k = s.cp[wave][it] >> 8, e = s.cp[wave][it] & 255, i = wave + 4 * k;
+                const uint32_t gid = key_id(s.sel[i]);
+                const int c = gid / A.G, ps0 = s.meta[i][gid % A.G];
+                load8<T>(pv_u + ((int64_t)c * PS + ps0 + e) * kD, l16, vf[x]);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < kOpenBatch; ++x) {
+            const int it = base + sgw + 4 * x;
+            if (it < ncp) st.add(s.cl[wave][it], vf[x]);
+        }
     }
 
-    // 3. add back the coarse terms of candidates that lost the global ranking
+    // 4. add back the coarse terms of candidates that lost the global ranking
     if (kth != 0) {
         const T* gv = reinterpret_cast<const T*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
         const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
-        for (int base = i; base < ncand; base += A.TG * kBatch) {
-            // candidates base, base+TG, ... (up to kBatch of them) -> compact the losers
-            __syncthreads();
-            if (tid == 0) s.bn = 0;
-            __syncthreads();
-            if (tid < kBatch) {
-                const int k = base + tid * A.TG;
-                const uint64_t key = k < ncand ? cand[k] : 0;
-                if (key != 0 && key < kth) {
-                    const int slot = atomicAdd(&s.bn, 1);
-                    const uint32_t g = key_id(key);
-                    s.bpos[slot] = -1;
-                    s.blam[slot] = A.scale * key_score(key) + gln[g];
-                    s.bv[slot] = gv + (int64_t)g * kD;
-                }
-            }
-            __syncthreads();
-            if (s.bn > 0) {
-                // canonical order of terms inside the batch does not matter for the
-                // result beyond rounding; sort nothing, but make it deterministic:
-                if (tid == 0) {
-                    // insertion sort by group id (small batches)
-                    const int n = s.bn;
-                    for (int x = 1; x < n; ++x) {
-                        const float lv = s.blam[x];
-                        const T* vv = s.bv[x];
-                        int y = x - 1;
-                        while (y >= 0 && s.bv[y] > vv) {
-                            s.blam[y + 1] = s.blam[y];
-                            s.bv[y + 1] = s.bv[y];
-                            --y;
-                        }
-                        s.blam[y + 1] = lv;
-                        s.bv[y + 1] = vv;
+        constexpr int AB = 2 * kOpenBatch;
+        for (int k0 = wave * 4 + sgw; k0 < ncand; k0 += 16 * AB) {
+            float vf[AB][8], lam[AB];
+#pragma unroll
+            for (int x = 0; x < AB; ++x) {
+                const int k = k0 + 16 * x;
+                lam[x] = -INFINITY;
+                if (k < ncand) {
+                    const uint64_t key = cand[k];
+                    if (key != 0 && key < kth) {
+                        const uint32_t g = key_id(key);
+                        lam[x] = A.scale * key_score(key) + gln[g];
+                        load8<T>(gv + (int64_t)g * kD, l16, vf[x]);
                     }
                 }
-                __syncthreads();
-                open_batch<T>(s, q8, kb, vb, A.st, A.scale, m_run, l_run, o8);
             }
+#pragma unroll
+            for (int x = 0; x < AB; ++x)
+                if (lam[x] != -INFINITY) st.add(lam[x], vf[x]);
         }
     }
 
-    // 4. partial state of slot nslice + nwin + i
+    // 5. merge the 16 subgroup states with the merged scan state, normalise
     const int sg = tid >> 4;
+    if (l16 == 0) { s.sm[sg] = st.m; s.sl[sg] = st.l; }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s.ored[sg][8 * l16 + e] = o8[e];
+    for (int e = 0; e < 8; ++e) s.so[sg][8 * l16 + e] = st.o[e];
     __syncthreads();
-    float* dst = A.part + ((int64_t)(b * A.Hq + hq) * A.nslot + A.nslice + A.nwin + i) * kPartStride;
     if (tid < kD) {
-        float a = 0.0f;
-        for (int k = 0; k < 16; ++k) a += s.ored[k][tid];
-        dst[tid] = a;
+        float M = s.scan_m;
+        for (int k = 0; k < 16; ++k) M = fmaxf(M, s.sm[k]);
+        float L = 0.0f, O = 0.0f;
+        if (s.scan_m != -INFINITY) {
+            const float e = softmax_exp(s.scan_m - M);
+            L = s.scan_l * e;
+            O = s.scan_o[tid] * e;
+        }
+        for (int k = 0; k < 16; ++k) {
+            if (s.sm[k] == -INFINITY) continue;
+            const float e = softmax_exp(s.sm[k] - M);
+            L = __builtin_fmaf(s.sl[k], e, L);
+            O = __builtin_fmaf(s.so[k][tid], e, O);
+        }
+        A.out[head * kD + tid] = O / L;
     }
-    if (tid == 0) { dst[kD] = m_run; dst[kD + 1] = l_run; }
 }
+
+// ---------------------------------------------------------------------------- MFMA scan (bf16)
+//
+// Ranking scores and logits of a 16-row block come from v_mfma_f32_16x16x32_bf16 with
+// the g query heads as the rows of A (padded to 16) and 16 key rows as the columns of
+// B; every lane loads its 16-byte operand slices straight from HBM, so each key byte is
+// read once and shared by all heads.  bf16 x bf16 products are exact in fp32, so an
+// MFMA score S differs from the exact dot product, and so does the canonical fp32 fma
+// chain r, by at most gamma_128 * sum|q_t k_t| <= gamma_128 * |q| |kbar|; hence
+// |S - r| <= E = kErrC * |q| |kbar| with kErrC = 8 * 128 * 2^-24 (four times the
+// two-sided bound).  A slice's exact local top-k by r is therefore inside
+// {g : S_g + E_g >= T}, T being the k-th largest S_g - E_g, and only those candidates
+// are re-scored with the canonical chain.  Selection stays bit-exact; logits of the
+// coarse terms use S.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMRows = 128;     // rows per chunk of the MFMA kernels
+constexpr int kWinRows = 128;   // window rows per window workgroup (MFMA path)
+constexpr float kErrC = 8.0f * 128.0f / 16777216.0f;
+
+template <int HG>
+struct MSmem {
+    union {
+        struct {
+            float sc[HG][kMRows];   // MFMA scores, then logits (-inf: excluded / empty)
+            float csc[HG][kMRows];  // canonical scores of candidates (NaN: not a candidate)
+        } a;
+        float ored[8 / ((HG + 3) / 4)][4 * ((HG + 3) / 4)][kD];  // PV row-phase sums
+    } u;
+    alignas(16) bf16_t vl[kMRows][kD];  // value rows of the chunk, loaded straight into LDS
+    alignas(16) float wT[kMRows][8];  // softmax weights, [row][head] (heads >= HG: 0)
+    alignas(16) float qs[HG][kD];
+    float qn[HG];
+    float kn[kMRows];
+    float lnn[kMRows];
+    float mrun[HG], lrun[HG], alpha[HG];
+    uint64_t ckey[HG][kMaxTG];
+    uint64_t ckl[HG][kMRows];  // per head: ranking keys of the candidates
+    int ncl;
+    uint16_t cl[HG * kMRows];  // canonical work list: head << 8 | row
+};
+
+// q of the g heads of this KV head: fp32 copy in LDS, |q| per head, MFMA A operand.
+template <int HG>
+__device__ __forceinline__ void mfma_load_q(MSmem<HG>& s, const bf16_t* q0, bf16x8_t* qa) {
+    const int tid = threadIdx.x, l = tid & 63;
+    float ss = 0.0f;  // |q|^2 share: 16 threads per head, 8 values each
+    if (tid < HG * 16) {
+        const int h = tid >> 4, c = tid & 15;
+        float f[8];
+        Elt<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0 + h * kD + 8 * c), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s.qs[h][8 * c + e] = f[e];
+            ss = __builtin_fmaf(f[e], f[e], ss);
+        }
+    }
+    const int h = l & 15;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        if (h < HG) {
+            qa[kk] = *reinterpret_cast<const bf16x8_t*>(q0 + h * kD + 32 * kk + 8 * (l >> 4));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qa[kk][e] = (__bf16)0.0f;
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    if (tid < HG * 16 && (tid & 15) == 0) s.qn[tid >> 4] = sqrtf(ss) * 1.0001f;
+    __syncthreads();
+}
+
+// Issue global->LDS loads of value rows r < n (n <= kMRows) into s.vl; completion is
+// awaited by mfma_wait_lds.  One instruction moves 4 rows (64 lanes x 16 bytes).
+template <int HG, typename RowPtr>
+__device__ __forceinline__ void mfma_issue_v(MSmem<HG>& s, RowPtr vrow, int n) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    for (int i = w; 4 * i < n; i += 4) {
+        int r = 4 * i + (l >> 4);
+        r = r < n ? r : n - 1;
+        __builtin_amdgcn_global_load_lds(vrow(r) + 8 * (l & 15), &s.vl[4 * i][0], 16, 0, 0);
+    }
+}
+__device__ __forceinline__ void mfma_wait_lds() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+// S[h][r] for rows r < n (n <= kMRows) whose key rows are krow(r).
+template <int HG, typename RowPtr>
+__device__ __forceinline__ void mfma_scores(float (*sc)[kMRows], const bf16x8_t* qa, RowPtr krow, int n) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int nblk = (n + 15) >> 4;
+    constexpr int NB = kMRows / 64;
+    bf16x8_t kb[NB][4];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int blk = w + 4 * i;
+        if (blk < nblk) {
+            int rr = blk * 16 + (l & 15);
+            rr = rr < n ? rr : n - 1;
+            const bf16_t* row = krow(rr);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kb[i][kk] = *reinterpret_cast<const bf16x8_t*>(row + 32 * kk + 8 * (l >> 4));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int blk = w + 4 * i;
+        if (blk < nblk) {
+            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kb[i][kk], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = 4 * (l >> 4) + r;
+                if (h < HG) sc[h][blk * 16 + (l & 15)] = acc[r];
+            }
+        }
+    }
+}
+
+// PV over rows r < n with weights s.wT[r][.] and value rows s.vl[r]: thread (head quad
+// hq, row phase rp, dims 4*db..4*db+3) accumulates o[i][e] for heads 4*hq+i.
+template <int HG>
+__device__ __forceinline__ void mfma_pv(MSmem<HG>& s, int n, float (*o)[4]) {
+    constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
+    const int tid = threadIdx.x;
+    const int hq = tid / (32 * RPH), rp = (tid / 32) % RPH, db = tid & 31;
+    for (int r = rp; r < n; r += RPH) {
+        const uint2 u = *reinterpret_cast<const uint2*>(&s.vl[r][4 * db]);
+        const float4 w4 = *reinterpret_cast<const float4*>(&s.wT[r][4 * hq]);
+        const float v[4] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+        const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[i][e] = __builtin_fmaf(w[i], v[e], o[i][e]);
+    }
+}
+
+// Sum the row phases of o and write the partial state (o, m, l) of every head.
+template <int HG>
+__device__ void mfma_write_partial(MSmem<HG>& s, float (*o)[4], float* dst_head0, int64_t head_stride,
+                                   bool normalise = false) {
+    constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
+    const int tid = threadIdx.x;
+    const int hq = tid / (32 * RPH), rp = (tid / 32) % RPH, db = tid & 31;
+    __syncthreads();  // s.u is reused
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s.u.ored[rp][4 * hq + i][4 * db + e] = o[i][e];
+    __syncthreads();
+    for (int x = tid; x < HG * kD; x += kThreads) {
+        const int h = x / kD, d = x % kD;
+        float a = s.u.ored[0][h][d];
+        for (int k = 1; k < RPH; ++k) a += s.u.ored[k][h][d];
+        dst_head0[(int64_t)h * head_stride + d] = normalise ? a / s.lrun[h] : a;
+    }
+    if (!normalise && tid < HG) {
+        dst_head0[(int64_t)tid * head_stride + kD] = s.mrun[tid];
+        dst_head0[(int64_t)tid * head_stride + kD + 1] = s.lrun[tid];
+    }
+}
+
+// Exact rows (window, sinks, dense): online softmax over chunks of up to 256 rows.
+// Row r of the list is position pos(r) = r < ns ? r : base + (r - ns).
+template <int HG>
+__device__ void mfma_exact_rows(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* kb, const bf16_t* vb,
+                                int64_t st, int ns, int base, int nrows, float scale, float (*o)[4]) {
+    constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int hq = tid / (32 * RPH);
+    for (int c0 = 0; c0 < nrows; c0 += kMRows) {
+        const int n = min(kMRows, nrows - c0);
+        auto pos = [&](int r) { const int x = c0 + r; return x < ns ? x : base + (x - ns); };
+        auto krow = [&](int r) { return kb + (int64_t)pos(r) * st; };
+        auto vrow = [&](int r) { return vb + (int64_t)pos(r) * st; };
+        mfma_issue_v<HG>(s, vrow, n);
+        mfma_scores<HG>(s.u.a.sc, qa, krow, n);
+        __syncthreads();
+        for (int h = w; h < HG; h += 4) {
+            float lam[kMRows / 64], mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kMRows / 64; ++k) {
+                const int r = l + 64 * k;
+                lam[k] = r < n ? scale * s.u.a.sc[h][r] : -INFINITY;
+                mx = fmaxf(mx, lam[k]);
+            }
+            mx = wave_max_f32(mx, 64);
+            const float mold = s.mrun[h];
+            const float mn = fmaxf(mold, mx);
+            float ls = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kMRows / 64; ++k) {
+                const int r = l + 64 * k;
+                const float wgt = lam[k] == -INFINITY ? 0.0f : softmax_exp(lam[k] - mn);
+                if (r < n) s.wT[r][h] = wgt;
+                ls += wgt;
+            }
+            ls = wave_sum_f32(ls, 64);
+            if (l == 0) {
+                const float a = mold == -INFINITY ? 0.0f : softmax_exp(mold - mn);
+                s.alpha[h] = a;
+                s.lrun[h] = s.lrun[h] * a + ls;
+                s.mrun[h] = mn;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = (4 * hq + i < HG) ? s.alpha[4 * hq + i] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[i][e] *= a;
+        }
+        mfma_wait_lds();
+        mfma_pv<HG>(s, n, o);
+        __syncthreads();
+    }
+}
+
+template <int HG>
+__device__ __forceinline__ void mfma_init(MSmem<HG>& s, float (*o)[4]) {
+    const int tid = threadIdx.x;
+    if (tid < HG) { s.mrun[tid] = -INFINITY; s.lrun[tid] = 0.0f; s.alpha[tid] = 0.0f; }
+    for (int x = tid; x < kMRows * 8; x += kThreads) (&s.wT[0][0])[x] = 0.0f;
+    if (tid == 0) s.ncl = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[i][e] = 0.0f;
+}
+
+template <int HG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_scan_mfma_kernel(DecodeArgs A) {
+    __shared__ MSmem<HG> s;
+    const int kvh = blockIdx.y, b = blockIdx.z;  // b: query row
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    int seq, p;
+    row_info(A, b, seq, p);
+    const int nb = nbuilt(p, A.W);
+    const int ng = nb * A.G;
+    const int64_t unit = (int64_t)seq * A.Hkv + kvh;
+    const int hq0 = kvh * HG;
+    float* part0 = A.part + ((int64_t)(b * A.Hq + hq0) * A.nslot + blockIdx.x) * kPartStride;
+    const int64_t head_stride = (int64_t)A.nslot * kPartStride;
+    const bf16_t* q0 = reinterpret_cast<const bf16_t*>(A.q) + ((int64_t)b * A.Hq + hq0) * kD;
+
+    float o[4][4];
+    mfma_init<HG>(s, o);
+    bf16x8_t qa[4];
+    mfma_load_q<HG>(s, q0, qa);
+
+    if ((int)blockIdx.x >= A.nslice) {
+        // ---------------- window tile (block 0 also takes the sinks)
+        const int wb = blockIdx.x - A.nslice;
+        const int r0 = nb * kChunk + wb * kWinRows;
+        const int nwr = max(0, min(r0 + kWinRows, p + 1) - r0);
+        const int ns = wb == 0 ? min(A.n_sink, nb * kChunk) : 0;
+        __syncthreads();
+        if (nwr + ns > 0) {
+            const bf16_t* kb = reinterpret_cast<const bf16_t*>(A.k) + seq * A.sb + kvh * A.sh;
+            const bf16_t* vb = reinterpret_cast<const bf16_t*>(A.v) + seq * A.sb + kvh * A.sh;
+            mfma_exact_rows<HG>(s, qa, kb, vb, A.st, ns, r0, ns + nwr, A.scale, o);
+        }
+        mfma_write_partial<HG>(s, o, part0, head_stride);
+        return;
+    }
+
+    // ---------------- slice of group summaries
+    const int g0 = blockIdx.x * A.slice;
+    const int n = min(A.slice, ng - g0);
+    uint64_t* cand = A.cand + ((int64_t)(b * A.Hq + hq0) * A.nslice + blockIdx.x) * A.TG;
+    const int64_t cand_head_stride = (int64_t)A.nslice * A.TG;
+    if (n <= 0) {
+        __syncthreads();
+        for (int e = tid; e < HG * A.TG; e += kThreads) cand[(e / A.TG) * cand_head_stride + e % A.TG] = 0;
+        mfma_write_partial<HG>(s, o, part0, head_stride);
+        return;
+    }
+    const int64_t gbase = unit * A.max_chunks * A.G + g0;
+    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
+    const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
+    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
+    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + gbase;
+    if (tid < n) { s.lnn[tid] = gln[tid]; s.kn[tid] = gkn[tid]; }
+    auto krow = [&](int r) { return gk + (int64_t)r * kD; };
+    auto vrow = [&](int r) { return gv + (int64_t)r * kD; };
+    mfma_issue_v<HG>(s, vrow, n);
+    mfma_scores<HG>(s.u.a.sc, qa, krow, n);
+    __syncthreads();
+
+    // 1. candidates of the local top-k of each head (one wave per head)
+    for (int h = w; h < HG; h += 4) {
+        constexpr int RL = kMRows / 64;  // rows per lane
+        float ub[RL];
+        uint32_t okey[RL];  // orderable bits of the lower bound, 0 = not a valid group
+        const float qn = s.qn[h];
+#pragma unroll
+        for (int k = 0; k < RL; ++k) {
+            const int r = l + 64 * k;
+            const bool valid = r < n && s.lnn[r] != -INFINITY;
+            const float E = kErrC * qn * (r < n ? s.kn[r] : 0.0f);
+            const float sv = r < n ? s.u.a.sc[h][r] : 0.0f;
+            ub[k] = valid ? sv + E : -INFINITY;
+            const float lbv = sv - E;
+            const uint32_t u = __float_as_uint(lbv == 0.0f ? 0.0f : lbv);
+            okey[k] = valid ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
+        }
+        // T = TG-th largest lower bound (with multiplicity): the largest v such that at
+        // least TG keys are >= v, built bit by bit from the top; -inf if fewer than TG.
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t tryv = prefix | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int k = 0; k < RL; ++k) cnt += __popcll(__ballot(okey[k] >= tryv));
+            if (cnt >= A.TG) prefix = tryv;
+        }
+        float T = -INFINITY;
+        if (prefix != 0) {
+            const uint32_t u = (prefix & 0x80000000u) ? (prefix & 0x7fffffffu) : ~prefix;
+            T = __uint_as_float(u);
+        }
+#pragma unroll
+        for (int k = 0; k < kMRows / 64; ++k) {
+            const int r = l + 64 * k;
+            const bool c = ub[k] != -INFINITY && ub[k] >= T;
+            if (r < kMRows) s.u.a.csc[h][r] = c ? 0.0f : __builtin_nanf("");
+            const uint64_t mask = __ballot(c);
+            int basep = 0;
+            if (l == 0 && mask) basep = atomicAdd(&s.ncl, __popcll(mask));
+            basep = __shfl(basep, 0, 64);
+            if (c) {
+                const int slot = basep + __popcll(mask & ((1ull << l) - 1ull));
+                s.cl[slot] = (uint16_t)((h << 8) | r);
+            }
+        }
+    }
+    __syncthreads();
+    // 2. canonical fp32 chains for the candidates
+    const int ncl = s.ncl;
+    for (int x = tid; x < ncl; x += kThreads) {
+        const int h = s.cl[x] >> 8, r = s.cl[x] & 255;
+        const bf16_t* row = krow(r);
+        uint4 u[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) u[c] = *reinterpret_cast<const uint4*>(row + 8 * c);
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float f[8];
+            Elt<bf16_t>::unpack(u[c], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(s.qs[h][8 * c + e], f[e], acc);
+        }
+        s.u.a.csc[h][r] = acc;
+    }
+    __syncthreads();
+    // 3. exact local top-k among the candidates (rank = number of larger keys); the
+    //    winners leave the coarse sum
+    for (int h = w; h < HG; h += 4) {
+        constexpr int RL = kMRows / 64;
+        uint64_t key[RL];
+        int nc = 0;
+#pragma unroll
+        for (int k = 0; k < RL; ++k) {
+            const int r = l + 64 * k;
+            const float c = r < n ? s.u.a.csc[h][r] : __builtin_nanf("");
+            key[k] = (c == c) ? rank_key(c, (uint32_t)(g0 + r)) : 0;
+            const uint64_t mask = __ballot(key[k] != 0);
+            if (key[k] != 0) s.ckl[h][nc + __popcll(mask & ((1ull << l) - 1ull))] = key[k];
+            nc += __popcll(mask);
+        }
+        wave_sync();
+#pragma unroll
+        for (int k = 0; k < RL; ++k) {
+            if (key[k] == 0) continue;
+            int rank = 0;
+            for (int x = 0; x < nc; ++x) rank += s.ckl[h][x] > key[k];
+            if (rank < A.TG) {
+                s.ckey[h][rank] = key[k];
+                s.u.a.sc[h][l + 64 * k] = -INFINITY;
+            }
+        }
+        if (l >= nc && l < A.TG) s.ckey[h][l] = 0;
+        // coarse logits of this head: scale * S + ln n (excluded and empty groups: -inf)
+        float lam[kMRows / 64], mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kMRows / 64; ++k) {
+            const int r = l + 64 * k;
+            const float sv = r < n ? s.u.a.sc[h][r] : -INFINITY;
+            lam[k] = (r < n && sv != -INFINITY && s.lnn[r] != -INFINITY) ? A.scale * sv + s.lnn[r] : -INFINITY;
+            mx = fmaxf(mx, lam[k]);
+        }
+        mx = wave_max_f32(mx, 64);
+        float ls = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kMRows / 64; ++k) {
+            const int r = l + 64 * k;
+            const float wgt = lam[k] == -INFINITY ? 0.0f : softmax_exp(lam[k] - mx);
+            if (r < n) s.wT[r][h] = wgt;
+            ls += wgt;
+        }
+        ls = wave_sum_f32(ls, 64);
+        if (l == 0) { s.mrun[h] = mx; s.lrun[h] = ls; }
+    }
+    __syncthreads();
+    for (int e = tid; e < HG * A.TG; e += kThreads)
+        cand[(e / A.TG) * cand_head_stride + e % A.TG] = s.ckey[e / A.TG][e % A.TG];
+    // 4. PV of the coarse terms
+    mfma_wait_lds();
+    mfma_pv<HG>(s, n, o);
+    mfma_write_partial<HG>(s, o, part0, head_stride);
+}
+
+// Dense decode (bf16): split workgroups over rows, MFMA scores, online softmax.
+template <int HG>
+__global__ __launch_bounds__(kThreads) void dense_decode_mfma_kernel(DenseArgs A) {
+    __shared__ MSmem<HG> s;
+    const int kvh = blockIdx.y, b = blockIdx.z;  // b: query row
+    int seq, p;
+    if (A.seq_lens) {
+        seq = b;
+        p = query_pos(A.seq_lens, b, A.max_seq_len);
+    } else {
+        seq = A.seq0 + b / A.rows_per_seq;
+        p = A.pos0 + b % A.rows_per_seq;
+    }
+    const int hq0 = kvh * HG;
+    const bf16_t* q0 = reinterpret_cast<const bf16_t*>(A.q) + ((int64_t)b * A.Hq + hq0) * kD;
+    float o[4][4];
+    mfma_init<HG>(s, o);
+    bf16x8_t qa[4];
+    mfma_load_q<HG>(s, q0, qa);
+    __syncthreads();
+    const int r0 = blockIdx.x * A.rows_per_wg;
+    const int r1 = min(r0 + A.rows_per_wg, p + 1);
+    if (r1 > r0) {
+        const bf16_t* kb = reinterpret_cast<const bf16_t*>(A.k) + seq * A.sb + kvh * A.sh;
+        const bf16_t* vb = reinterpret_cast<const bf16_t*>(A.v) + seq * A.sb + kvh * A.sh;
+        mfma_exact_rows<HG>(s, qa, kb, vb, A.st, 0, r0, r1 - r0, A.scale, o);
+    }
+    if (A.out) {
+        mfma_write_partial<HG>(s, o, A.out + ((int64_t)b * A.Hq + hq0) * kD, kD, true);
+        return;
+    }
+    float* part0 = A.part + ((int64_t)(b * A.Hq + hq0) * A.nsplit + blockIdx.x) * kPartStride;
+    mfma_write_partial<HG>(s, o, part0, (int64_t)A.nsplit * kPartStride);
+}
+
 
 // ---------------------------------------------------------------------------- combine
 
@@ -703,19 +1239,7 @@ __global__ __launch_bounds__(kD) void combine_kernel(const float* part, int nslo
 
 // ---------------------------------------------------------------------------- dense decode
 
-struct DenseArgs {
-    const void* k;
-    const void* v;
-    int64_t sb, st, sh;
-    const void* q;
-    const int32_t* seq_lens;
-    int max_seq_len;
-    float* part;
-    float* out;  // non-null: nsplit == 1 and rows write normalised outputs here
-    int Hq, Hkv, rows_per_wg, nsplit;
-    float scale;
-    int seq0, rows_per_seq, pos0;  // row mapping when seq_lens is null (as DecodeArgs)
-};
+
 
 template <typename T, int HG>
 __global__ __launch_bounds__(kThreads) void dense_decode_kernel(DenseArgs A) {
@@ -759,27 +1283,43 @@ static int check_kv(const lod_params* p, const lod_kv& kv) {
     return LOD_OK;
 }
 
+// Record trace event k (when lod_trace_events is set on this thread).
+static inline void trace(int k, hipStream_t st) {
+    int n = 0;
+    void* const* ev = trace_events(&n);
+    if (ev && k < n) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[k]), st);
+}
+
 template <typename T, int HG>
 static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
-    if (A.nslice + A.nwin > 0)
-        hipLaunchKernelGGL((decode_scan_kernel<T, HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
-                           dim3(kThreads), 0, st, A);
-    hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.TG, A.Hq, rows), dim3(kThreads), 0, st, A);
-    hipLaunchKernelGGL(combine_kernel, dim3(A.Hq, rows), dim3(kD), 0, st, (const float*)A.part,
-                       A.nslot, A.out, A.Hq);
+    trace(0, st);
+    if (A.nslice + A.nwin > 0) {
+        if constexpr (sizeof(T) == 2)
+            hipLaunchKernelGGL((decode_scan_mfma_kernel<HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
+                               dim3(kThreads), 0, st, A);
+        else
+            hipLaunchKernelGGL((decode_scan_kernel<T, HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
+                               dim3(kThreads), 0, st, A);
+    }
+    trace(1, st);
+    hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+    trace(2, st);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
 
 template <typename T, int HG>
 static int launch_dense(const DenseArgs& A, float* out, int rows, hipStream_t st) {
-    hipLaunchKernelGGL((dense_decode_kernel<T, HG>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
-                       st, A);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((dense_decode_mfma_kernel<HG>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
+                           st, A);
+    else
+        hipLaunchKernelGGL((dense_decode_kernel<T, HG>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
+                           st, A);
     if (!A.out)
         hipLaunchKernelGGL(combine_kernel, dim3(A.Hq, rows), dim3(kD), 0, st, (const float*)A.part,
                            A.nsplit, out, A.Hq);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
-
 
 static int dispatch_decode(const lod_params* params, const DecodeArgs& A, int rows, hipStream_t st) {
     const int g = A.Hq / A.Hkv;

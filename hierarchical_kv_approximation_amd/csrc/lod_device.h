@@ -68,19 +68,22 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
     return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
-}
+
+// Full-wavefront reductions of the ROCm device library (DPP based).  Every lane of the
+// wave must execute them; the result is returned to every lane.
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(unsigned long long);
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) { return __ockl_wfred_max_u64(v); }
+// width: reduce over aligned groups of `width` lanes (64 = the whole wave).
 __device__ __forceinline__ float wave_max_f32(float v, int width) {
+    if (width == 64) return __ockl_wfred_max_f32(v);
     for (int m = width >> 1; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
     return v;
 }
 __device__ __forceinline__ float wave_sum_f32(float v, int width) {
+    if (width == 64) return __ockl_wfred_add_f32(v);
     for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }

@@ -36,6 +36,7 @@ lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_c
     L.gk = o;     o = align256(o + U * NC * G * d * E);
     L.gv = o;     o = align256(o + U * NC * G * d * E);
     L.gln = o;    o = align256(o + U * NC * G * 4);
+    L.gkn = o;    o = align256(o + U * NC * G * 4);
     L.pk = o;     o = align256(o + U * NC * PS * d * E);
     L.pv = o;     o = align256(o + U * NC * PS * d * E);
     L.pln = o;    o = align256(o + U * NC * PS * 4);
@@ -57,11 +58,15 @@ DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len) 
     int64_t slice = ceil_div(ng > 0 ? ng : 1, want);
     slice = ceil_div(slice, kTile) * kTile;
     if (slice < kTile) slice = kTile;
-    if (slice > 4 * kTile) slice = 4 * kTile;
+    // bf16 slices are one MFMA chunk (128 rows, value rows staged in LDS); fp32 up to 256
+    const int64_t cap = p->kv_dtype == LOD_BF16 ? 2 * kTile : 4 * kTile;
+    if (slice > cap) slice = cap;
     P.slice = (int)slice;
     P.nslice = ng > 0 ? (int)ceil_div(ng, slice) : 0;
-    P.nwin = 1 + (int)ceil_div(p->window, kTile);  // sinks, then window tiles
-    P.nslot = P.nslice + P.nwin + p->top_groups;
+    // window workgroups: bf16 (MFMA) takes 128-row tiles with the sinks in the first one;
+    // fp32 takes a sinks workgroup, then 64-row tiles
+    P.nwin = p->kv_dtype == LOD_BF16 ? (int)ceil_div(p->window, 128) : 1 + (int)ceil_div(p->window, kTile);
+    P.nslot = P.nslice + P.nwin;
     const size_t heads = (size_t)batch * p->n_q_heads;
     P.off_part = 0;
     P.off_cand = align256(heads * P.nslot * kPartStride * sizeof(float));
@@ -84,6 +89,14 @@ DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len) {
     return P;
 }
 
+static thread_local void* const* g_trace = nullptr;
+static thread_local int g_ntrace = 0;
+
+void* const* trace_events(int* n) {
+    *n = g_ntrace;
+    return g_trace;
+}
+
 }  // namespace lodi
 
 using namespace lodi;
@@ -99,6 +112,13 @@ const char* lod_status_string(int status) {
         case LOD_ERR_HIP: return "LOD_ERR_HIP: HIP runtime or launch failure";
         default: return "unknown status";
     }
+}
+
+int lod_trace_events(void* const* events, int32_t n_events) {
+    if (events && n_events <= 0) return LOD_ERR_ARG;
+    g_trace = events;
+    g_ntrace = events ? n_events : 0;
+    return LOD_OK;
 }
 
 int lod_index_layout(const lod_params* params, int32_t batch, int32_t max_chunks,

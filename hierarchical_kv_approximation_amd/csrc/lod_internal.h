@@ -56,4 +56,7 @@ struct DensePlan {
 };
 DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len);
 
+// Events set by lod_trace_events for the calling host thread (null when off).
+void* const* trace_events(int* n);
+
 }  // namespace lodi

@@ -42,7 +42,7 @@ class Index(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("gk", "gv", "gln", "pk", "pv", "pln", "meta", "assign", "total")] + \
+                ("gk", "gv", "gln", "gkn", "pk", "pv", "pln", "meta", "assign", "total")] + \
         [("page_slots", ctypes.c_int32), ("meta_stride", ctypes.c_int32)]
 
 
@@ -77,9 +77,11 @@ def lib():
         L.lod_dense_decode_ws_bytes.argtypes = [pp, i32, i32, P(sz)]
         L.lod_dense_decode.argtypes = [pp, KV, vp, vp, i32, i32, vp, vp, sz, vp]
         L.lod_dense_prefill.argtypes = [pp, KV, vp, i32, i32, i32, vp, vp]
+        L.lod_trace_events.argtypes = [P(vp), i32]
         for fn in ("lod_index_bytes", "lod_index_layout", "lod_build_chunk", "lod_decode_ws_bytes",
                    "lod_attend_decode", "lod_prefill_ws_bytes", "lod_attend_prefill",
-                   "lod_dense_decode_ws_bytes", "lod_dense_decode", "lod_dense_prefill"):
+                   "lod_dense_decode_ws_bytes", "lod_dense_decode", "lod_dense_prefill",
+                   "lod_trace_events"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -181,6 +183,7 @@ class LodIndex:
             "gk": view(L.gk, U * NC * G * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, G, d)),
             "gv": view(L.gv, U * NC * G * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, G, d)),
             "gln": view(L.gln, U * NC * G, torch.float32, (self.batch, cfg.n_kv_heads, NC, G)),
+            "gkn": view(L.gkn, U * NC * G, torch.float32, (self.batch, cfg.n_kv_heads, NC, G)),
             "pk": view(L.pk, U * NC * PS * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, PS, d)),
             "pv": view(L.pv, U * NC * PS * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, PS, d)),
             "pln": view(L.pln, U * NC * PS, torch.float32, (self.batch, cfg.n_kv_heads, NC, PS)),
@@ -292,3 +295,13 @@ def dense_prefill(cfg: Config, K, V, q, q_start: int, out: torch.Tensor | None =
     _check("lod_dense_prefill", lib().lod_dense_prefill(
         ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), q_start, nq, B, _ptr(out), _stream()))
     return out
+
+
+def trace_events(events):
+    """Set (list of raw hipEvent_t handles) or clear (None) the library's trace events."""
+    if events is None:
+        _check("lod_trace_events", lib().lod_trace_events(None, 0))
+        return None
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check("lod_trace_events", lib().lod_trace_events(arr, len(events)))
+    return arr  # caller keeps it alive while tracing

@@ -17,7 +17,8 @@
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
- *     buffer; the library never allocates device memory and keeps no state.
+ *     buffer; the library never allocates device memory and keeps no state apart from
+ *     the optional trace events of lod_trace_events.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work;
  *     they return before the GPU finishes.  Device faults surface at the caller's next
  *     synchronisation of that stream.
@@ -99,6 +100,7 @@ typedef struct {
  * E = element size of kv_dtype).  Every array is 256-byte aligned.
  *   gk, gv   [U][NC*G][d]  E     group mean key / value (storage-rounded)
  *   gln      [U][NC*G]     f32   ln(key count), -inf for an empty group
+ *   gkn      [U][NC*G]     f32   upper bound of the Euclidean norm of the stored mean key
  *   pk, pv   [U][NC*PS][d] E     page mean key / value
  *   pln      [U][NC*PS]    f32   ln(key count), -inf for an unused page slot
  *   meta     [U][NC][meta_stride] int16: gpg[G+1] first page slot of each group,
@@ -107,7 +109,7 @@ typedef struct {
  *   assign   [U][NC][C]    int8  group of every chunk-local position, -1 for sinks
  */
 typedef struct {
-    size_t gk, gv, gln, pk, pv, pln, meta, assign, total;
+    size_t gk, gv, gln, gkn, pk, pv, pln, meta, assign, total;
     int32_t page_slots;
     int32_t meta_stride; /* int16 entries per chunk in `meta` */
 } lod_index_layout_t;
@@ -211,6 +213,16 @@ int lod_dense_decode(const lod_params* params, lod_kv kv, const void* q,
  */
 int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_t q_start,
                       int32_t n_q, int32_t batch, float* out, void* stream);
+
+/*
+ * Instrumentation (profiling only; results are unchanged).  While `events` is non-null,
+ * every later lod_attend_decode / lod_attend_prefill call made from the same host thread
+ * records events[0] on its stream before its first kernel and events[1 + k] after its
+ * k-th kernel (decode: k = 0 scan, 1 open-and-combine).  `events` points to n_events
+ * hipEvent_t handles created by the caller, who reads them with hipEventElapsedTime;
+ * kernels beyond n_events - 1 record nothing.  Pass NULL to stop.  Not for captured graphs.
+ */
+int lod_trace_events(void* const* events, int32_t n_events);
 
 #ifdef __cplusplus
 }
