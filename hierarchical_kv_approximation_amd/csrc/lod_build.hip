@@ -38,6 +38,7 @@ struct BuildSmem {
     int32_t gpg[GMAX + 1];   // first page slot of each group
     int32_t pst[kChunk / kPage + GMAX + 1];
     int32_t perm[kChunk];    // member indices ordered by (group, position)
+    int32_t wcnt[kThreads / 64][GMAX];
 };
 
 // One Lloyd update: mu_j = fp32 mean of members with a_i == j, in member order.
@@ -53,13 +54,28 @@ __device__ void group_means(BuildSmem<T, GMAX>& s, int m, int G, bool write_mu, 
     int cnt[JP];
 #pragma unroll
     for (int k = 0; k < JP; ++k) { sum[k] = 0.0f; cnt[k] = 0; }
-    for (int i = 0; i < m; ++i) {
+    // members in position order; LDS loads are issued eight at a time
+    int i = 0;
+    for (; i + 8 <= m; i += 8) {
+        int ai[8];
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            ai[u] = s.a[i + u];
+            x[u] = Elt<T>::to_f32(s.x[i + u][t]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int k = 0; k < JP; ++k)
+                if (ai[u] == j0 + 2 * k) { sum[k] = sum[k] + x[u]; cnt[k] += 1; }
+    }
+    for (; i < m; ++i) {
         const int ai = s.a[i];
         const float x = Elt<T>::to_f32(s.x[i][t]);
 #pragma unroll
-        for (int k = 0; k < JP; ++k) {
+        for (int k = 0; k < JP; ++k)
             if (ai == j0 + 2 * k) { sum[k] = sum[k] + x; cnt[k] += 1; }
-        }
     }
 #pragma unroll
     for (int k = 0; k < JP; ++k) {
@@ -102,6 +118,25 @@ __device__ void assign_step(BuildSmem<T, GMAX>& s, const float* xr, int m, int G
             if (j < G && acc[j] < bd) { bd = acc[j]; best = j; }
         s.a[i] = best;
     }
+}
+
+// Mean over the members of page slot e / kD at dimension e % kD (position order;
+// the member indices are fetched before the values so the LDS loads overlap).
+template <typename T, int GMAX>
+__device__ __forceinline__ float page_mean(BuildSmem<T, GMAX>& s, int e) {
+    const int sl = e / kD, t = e % kD;
+    const int b0 = s.pst[sl], n = s.pst[sl + 1] - b0;
+    int idx[kPage];
+#pragma unroll
+    for (int q = 0; q < kPage; ++q) idx[q] = q < n ? s.perm[b0 + q] : 0;
+    float x[kPage];
+#pragma unroll
+    for (int q = 0; q < kPage; ++q) x[q] = Elt<T>::to_f32(s.x[idx[q]][t]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kPage; ++q)
+        if (q < n) acc = acc + x[q];
+    return n > 0 ? acc / (float)n : 0.0f;
 }
 
 // Load the chunk's members (positions >= n_sink) of K or V into LDS.
@@ -184,11 +219,22 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
         for (int q = pg; q <= PS; ++q) s.pst[q] = o;
     }
     __syncthreads();
-    if (tid < m) {
-        const int ai = s.a[tid];
+    {
+        // rank of member tid among the earlier members of its group: ballot prefix
+        // counts inside the wave plus the counts of earlier waves
+        const int ai = tid < m ? s.a[tid] : -1;
+        const int lane = tid & 63, wv = tid >> 6;
         int rank = 0;
-        for (int i = 0; i < tid; ++i) rank += (s.a[i] == ai);
-        s.perm[s.goff[ai] + rank] = tid;
+        for (int j = 0; j < G; ++j) {
+            const uint64_t mk = __ballot(ai == j);
+            if (ai == j) rank = __popcll(mk & ((1ull << lane) - 1ull));
+            if (lane == 0) s.wcnt[wv][j] = __popcll(mk);
+        }
+        __syncthreads();
+        if (ai >= 0) {
+            for (int w = 0; w < wv; ++w) rank += s.wcnt[w][ai];
+            s.perm[s.goff[ai] + rank] = tid;
+        }
     }
     __syncthreads();
 
@@ -233,13 +279,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
         gkn[tid] = sqrtf(ss) * 1.0001f + 1e-30f;
     }
     // Page means of keys: thread (slot, t) sums <= 16 members in position order.
-    for (int e = tid; e < PS * kD; e += kThreads) {
-        const int sl = e / kD, t = e % kD;
-        const int b0 = s.pst[sl], b1 = s.pst[sl + 1];
-        float acc = 0.0f;
-        for (int q = b0; q < b1; ++q) acc = acc + Elt<T>::to_f32(s.x[s.perm[q]][t]);
-        store_elt(&pk[e], b1 > b0 ? acc / (float)(b1 - b0) : 0.0f);
-    }
+    for (int e = tid; e < PS * kD; e += kThreads) store_elt(&pk[e], page_mean(s, e));
     if (tid < PS) {
         const int n = s.pst[tid + 1] - s.pst[tid];
         pln[tid] = n > 0 ? logf((float)n) : -INFINITY;
@@ -250,13 +290,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     load_members(s, vbase, A.st, first_off, m);
     __syncthreads();
     group_means(s, m, G, false, gmean, nullptr);
-    for (int e = tid; e < PS * kD; e += kThreads) {
-        const int sl = e / kD, t = e % kD;
-        const int b0 = s.pst[sl], b1 = s.pst[sl + 1];
-        float acc = 0.0f;
-        for (int q = b0; q < b1; ++q) acc = acc + Elt<T>::to_f32(s.x[s.perm[q]][t]);
-        store_elt(&pv[e], b1 > b0 ? acc / (float)(b1 - b0) : 0.0f);
-    }
+    for (int e = tid; e < PS * kD; e += kThreads) store_elt(&pv[e], page_mean(s, e));
     __syncthreads();
     for (int e = tid; e < G * kD; e += kThreads) {
         const int j = e / kD;

@@ -410,43 +410,6 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// 8 consecutive elements of a row starting at element 8*l16, as fp32.
-template <typename T>
-__device__ __forceinline__ void load8(const T* row, int l16, float* f);
-template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t* row, int l16, float* f) {
-    const uint4 u = *reinterpret_cast<const uint4*>(row + 8 * l16);
-    Elt<bf16_t>::unpack(u, f);
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* row, int l16, float* f) {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(row + 8 * l16);
-    const uint4 u1 = *reinterpret_cast<const uint4*>(row + 8 * l16 + 4);
-    Elt<float>::unpack(u0, f);
-    Elt<float>::unpack(u1, f + 4);
-}
-
-// Online-softmax state of one 16-lane subgroup: lane holds o for dims 8*l16 .. 8*l16+7.
-struct Online {
-    float m, l, o[8];
-    __device__ void init() {
-        m = -INFINITY;
-        l = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
-    }
-    __device__ __forceinline__ void add(float lam, const float* v) {
-        if (lam == -INFINITY) return;
-        const float mn = fmaxf(m, lam);
-        const float a = softmax_exp(m - mn);  // m = -inf -> 0
-        const float w = softmax_exp(lam - mn);
-        l = __builtin_fmaf(l, a, w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(w, v[e], o[e] * a);
-        m = mn;
-    }
-};
-
 constexpr int kOpenBatch = 4;   // items per subgroup whose loads are issued together
 constexpr int kMetaMax = 320;   // int16 entries of one chunk's meta row (>= meta_stride)
 constexpr int kGPW = kMaxTG / 4;             // opened groups per wave (at most)
@@ -778,7 +741,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMRows = 128;     // rows per chunk of the MFMA kernels
 constexpr int kWinRows = 128;   // window rows per window workgroup (MFMA path)
-constexpr float kErrC = 8.0f * 128.0f / 16777216.0f;
 
 template <int HG>
 struct MSmem {
@@ -1276,7 +1238,7 @@ __global__ __launch_bounds__(kThreads) void dense_decode_kernel(DenseArgs A) {
 
 // ---------------------------------------------------------------------------- host side
 
-static int check_kv(const lod_params* p, const lod_kv& kv) {
+int check_kv_view(const lod_params* p, const lod_kv& kv) {
     if (!kv.k || !kv.v || kv.stride_t <= 0 || kv.stride_h < 0 || kv.stride_b < 0) return LOD_ERR_ARG;
     const int per16 = p->kv_dtype == LOD_BF16 ? 8 : 4;
     if ((kv.stride_t | kv.stride_h | kv.stride_b) % per16 != 0) return LOD_ERR_ARG;
@@ -1389,7 +1351,7 @@ extern "C" int lod_attend_decode(const lod_params* params, const lod_index* inde
     if (rc != LOD_OK) return rc;
     if (!index || !index->mem || !q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0)
         return LOD_ERR_ARG;
-    if ((rc = check_kv(params, kv)) != LOD_OK) return rc;
+    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
     if (batch != index->batch) return LOD_ERR_ARG;
     if (built_chunks(params, (int64_t)max_seq_len - 1) > index->max_chunks) return LOD_ERR_ARG;
     const lod_index_layout_t L = make_layout(params, index->batch, index->max_chunks);
@@ -1403,29 +1365,19 @@ extern "C" int lod_attend_decode(const lod_params* params, const lod_index* inde
     return dispatch_decode(params, A, batch, reinterpret_cast<hipStream_t>(stream));
 }
 
-extern "C" int lod_prefill_ws_bytes(const lod_params* params, int32_t batch, int32_t n_q,
-                                    int32_t max_tokens, size_t* bytes) {
-    int rc = check_params(params);
-    if (rc != LOD_OK) return rc;
-    if (!bytes || batch <= 0 || n_q <= 0 || max_tokens <= 0) return LOD_ERR_ARG;
+// Row-by-row prefill (fp32 caches): each group of up to kPrefillRows rows runs as that
+// many decode queries.  Arguments are validated by the caller.
+int lodi::prefill_rows_ws_bytes(const lod_params* params, int32_t n_q, int32_t max_tokens, size_t* bytes) {
     *bytes = plan_decode(params, n_q < kPrefillRows ? n_q : kPrefillRows, max_tokens).bytes;
     return LOD_OK;
 }
 
-extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* index, lod_kv kv,
-                                  const void* q, int32_t q_start, int32_t n_q, int32_t batch,
-                                  float* out, int32_t* sel_groups, int32_t* sel_pages, void* ws,
-                                  size_t ws_bytes, void* stream) {
-    int rc = check_params(params);
-    if (rc != LOD_OK) return rc;
-    if (!index || !index->mem || !q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
-    if (q_start % params->chunk_size != 0) return LOD_ERR_ARG;
-    if ((rc = check_kv(params, kv)) != LOD_OK) return rc;
-    if (batch != index->batch) return LOD_ERR_ARG;
+int lodi::prefill_rows(const lod_params* params, const lod_index* index, lod_kv kv, const void* q,
+                       int32_t q_start, int32_t n_q, int32_t batch, float* out, int32_t* sel_groups,
+                       int32_t* sel_pages, void* ws, size_t ws_bytes, void* stream) {
+    int rc = LOD_OK;
     const int64_t end = (int64_t)q_start + n_q;
-    if (end > INT32_MAX || built_chunks(params, end - 1) > index->max_chunks) return LOD_ERR_ARG;
     const lod_index_layout_t L = make_layout(params, index->batch, index->max_chunks);
-    if (index->bytes < L.total) return LOD_ERR_WORKSPACE;
     const int rows_max = n_q < kPrefillRows ? n_q : kPrefillRows;
     const DecodePlan P = plan_decode(params, rows_max, (int32_t)end);
     if (!ws || ws_bytes < P.bytes) return LOD_ERR_WORKSPACE;
@@ -1460,7 +1412,7 @@ extern "C" int lod_dense_decode(const lod_params* params, lod_kv kv, const void*
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
-    if ((rc = check_kv(params, kv)) != LOD_OK) return rc;
+    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
     const DensePlan P = plan_dense(params, batch, max_seq_len);
     if (!ws || ws_bytes < P.bytes) return LOD_ERR_WORKSPACE;
     DenseArgs A;
@@ -1474,14 +1426,11 @@ extern "C" int lod_dense_decode(const lod_params* params, lod_kv kv, const void*
     return dispatch_dense(params, A, out, batch, reinterpret_cast<hipStream_t>(stream));
 }
 
-extern "C" int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_t q_start,
-                                 int32_t n_q, int32_t batch, float* out, void* stream) {
-    int rc = check_params(params);
-    if (rc != LOD_OK) return rc;
-    if (!q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
-    if ((rc = check_kv(params, kv)) != LOD_OK) return rc;
+// Dense causal prefill of fp32 caches: one workgroup per (row, KV head) on the VALU.
+int lodi::dense_prefill_valu(const lod_params* params, lod_kv kv, const void* q, int32_t q_start,
+                             int32_t n_q, int32_t batch, float* out, void* stream) {
+    int rc = LOD_OK;
     const int64_t end = (int64_t)q_start + n_q;
-    if (end > INT32_MAX) return LOD_ERR_ARG;
     DenseArgs A;
     A.k = kv.k; A.v = kv.v; A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
     A.seq_lens = nullptr; A.max_seq_len = (int32_t)end;

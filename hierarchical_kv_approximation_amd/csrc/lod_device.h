@@ -91,4 +91,48 @@ __device__ __forceinline__ float wave_sum_f32(float v, int width) {
 // exp(x) for x <= 0 (softmax weights); exp(-inf) = 0.
 __device__ __forceinline__ float softmax_exp(float x) { return __expf(x); }
 
+// 8 consecutive elements of a row starting at element 8*l16, as fp32.
+template <typename T>
+__device__ __forceinline__ void load8(const T* row, int l16, float* f);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* row, int l16, float* f) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + 8 * l16);
+    Elt<bf16_t>::unpack(u, f);
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* row, int l16, float* f) {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(row + 8 * l16);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(row + 8 * l16 + 4);
+    Elt<float>::unpack(u0, f);
+    Elt<float>::unpack(u1, f + 4);
+}
+
+// Online-softmax state of one 16-lane subgroup: lane holds o for dims 8*l16 .. 8*l16+7.
+struct Online {
+    float m, l, o[8];
+    __device__ void init() {
+        m = -INFINITY;
+        l = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+    }
+    __device__ __forceinline__ void add(float lam, const float* v) {
+        if (lam == -INFINITY) return;
+        const float mn = fmaxf(m, lam);
+        const float a = softmax_exp(m - mn);  // m = -inf -> 0
+        const float w = softmax_exp(lam - mn);
+        l = __builtin_fmaf(l, a, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(w, v[e], o[e] * a);
+        m = mn;
+    }
+};
+
+// Bound on |S - r| / (|q| |kbar|) between an MFMA dot product S of bf16 vectors (exact
+// products, fp32 accumulation in any order) and the canonical fp32 fma chain r: each is
+// within gamma_128 * sum|q_t k_t| <= gamma_128 |q| |kbar| of the exact value
+// (gamma_n = n u / (1 - n u), u = 2^-24), so |S - r| <= 2 gamma_128 |q| |kbar|; the
+// constant is four times that.
+constexpr float kErrC = 8.0f * 128.0f / 16777216.0f;
+
 }  // namespace lodi

@@ -56,6 +56,17 @@ struct DensePlan {
 };
 DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len);
 
+// Checks of a KV view shared by the entry points (host).
+int check_kv_view(const lod_params* p, const lod_kv& kv);
+// LoD prefill row by row through the decode kernels (fp32 caches).
+int prefill_rows_ws_bytes(const lod_params* params, int32_t n_q, int32_t max_tokens, size_t* bytes);
+int prefill_rows(const lod_params* params, const lod_index* index, lod_kv kv, const void* q,
+                 int32_t q_start, int32_t n_q, int32_t batch, float* out, int32_t* sel_groups,
+                 int32_t* sel_pages, void* ws, size_t ws_bytes, void* stream);
+// Dense causal prefill of fp32 caches (VALU path).
+int dense_prefill_valu(const lod_params* params, lod_kv kv, const void* q, int32_t q_start,
+                       int32_t n_q, int32_t batch, float* out, void* stream);
+
 // Events set by lod_trace_events for the calling host thread (null when off).
 void* const* trace_events(int* n);
 

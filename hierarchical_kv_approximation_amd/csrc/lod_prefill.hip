@@ -1,0 +1,1055 @@
+// lod_prefill.hip -- LoD prefill (causal, many query rows per call) and the dense
+// causal prefill baseline, on MFMA.
+//
+// Every query row p computes what a decode query at p computes ("Level of Detail
+// Attention", How It Works): top groups by centroid score, top pages inside them, exact
+// attention over opened pages, the block window and the sinks, and the coarse remainder,
+// all in one softmax.  The rows of a 256-token chunk share the summarised chunks, so the
+// work is organised around tiles of 128 (query row, head) pairs of one KV head:
+//
+//   select   per tile: two MFMA sweeps over the group centroids find, for every
+//            (row, head), the k-th largest lower bound of the MFMA score and the groups
+//            whose upper bound reaches it; those are re-scored with the canonical fp32
+//            chain and ranked exactly; then the pages of the opened groups are ranked.
+//   flash    per tile: one online softmax over the coarse centroids (bias ln n, the
+//            row's opened groups masked out), the sinks and the causal block window.
+//   pages    per (query chunk, KV head, group block): the opened groups' pages, shared
+//            by every (row, head) that opened them: exact rows of opened pages, mean
+//            terms of unopened pages.
+//   combine  per (row, head): log-sum-exp merge of the flash and page partial states.
+//
+// The flash kernel keeps keys as MFMA rows and (row, head) pairs as MFMA columns
+// (S^T = K Q^T), so a lane holds one column of P and the PV product O^T = V^T P^T takes
+// P straight from registers; V is staged transposed in LDS.  P enters the PV MFMA as
+// bf16 hi + lo parts (error below 2^-16 relative).
+#include <climits>
+
+#include "lod_mfma.h"
+
+namespace lodi {
+
+__device__ __forceinline__ int nbuilt_prefill(int p, int W) {
+    const int nb = p / kChunk - W / kChunk + 1;
+    return nb < 0 ? 0 : nb;
+}
+
+struct FlashArgs {
+    const bf16_t* k;
+    const bf16_t* v;
+    int64_t sb, st, sh;
+    const bf16_t* q;  // rows of this launch: [B][nq][Hq][d]
+    int seq;          // sequence of grid slice z = 0 (index and cache)
+    int nq;           // rows per sequence in this launch
+    int pos0;         // position of row 0
+    int Hq, Hkv;
+    float scale;
+    // LoD sources; index == nullptr selects the dense causal mode
+    const char* index;
+    lod_index_layout_t L;
+    int max_chunks, G, W, n_sink, TG;
+    const int32_t* selg;  // [B][nq][Hq][TG] opened groups sorted ascending, -1 padding
+    float* part;          // LoD: [B][nq][Hq] partial states (o[d], m, l)
+    float* out;           // dense: normalised output [B][nq][Hq][d]
+};
+
+template <int HG>
+struct FlashSmem {
+    alignas(16) bf16_t kt[kFlashKeys][kD];          // key tile, 16-byte chunks XOR-swizzled
+    alignas(16) bf16_t vT[kD][kFlashKeys + 4];      // value tile, transposed
+    float bias[kFlashKeys];
+    int kpos[kFlashKeys];                           // key position for the causal test
+    int32_t sel[kFlashRowHeads][kMaxTG];            // opened groups per column (LoD)
+};
+
+// One tile of nk keys: rows krow(k), vrow(k), bias bias_of(k) (-inf: not a key), causal
+// position pos_of(k) (INT_MIN: no causal test).
+template <int HG>
+struct FlashState {
+    f32x4_t O[2][8];  // O^T tiles: [column block][d block]
+    float m[2], l[2];
+};
+
+template <int HG, typename KRow, typename VRow, typename Bias, typename Pos>
+__device__ __forceinline__ void flash_tile(FlashSmem<HG>& s, FlashState<HG>& F, const bf16x8_t (*qb)[4],
+                                           int nk, KRow krow, VRow vrow, Bias bias_of, Pos pos_of,
+                                           const int* prow, const uint64_t* excl, float scale) {
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    // stage keys (direct to LDS, swizzled) and values (transposed)
+    for (int i = w; i < kFlashKeys / 4; i += 4) {
+        int row = 4 * i + (l >> 4);
+        const int cp = l & 15, c = cp ^ (row & 15);
+        const int rr = row < nk ? row : nk - 1;
+        __builtin_amdgcn_global_load_lds(krow(rr) + 8 * c, &s.kt[4 * i][0], 16, 0, 0);
+    }
+    uint4 vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + kThreads * i, key = idx & 63, ch = idx >> 6;
+        const int kr = key < nk ? key : nk - 1;
+        vv[i] = *reinterpret_cast<const uint4*>(vrow(kr) + 8 * ch);
+    }
+    if (tid < kFlashKeys) {
+        s.bias[tid] = tid < nk ? bias_of(tid) : -INFINITY;
+        s.kpos[tid] = tid < nk ? pos_of(tid) : INT_MIN;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + kThreads * i, key = idx & 63, ch = idx >> 6;
+        const uint32_t u[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s.vT[8 * ch + 2 * e][key] = (bf16_t)(u[e] & 0xffffu);
+            s.vT[8 * ch + 2 * e + 1][key] = (bf16_t)(u[e] >> 16);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // S^T = K Q^T for 4 key blocks x 2 column blocks
+    f32x4_t S[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
+        S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int row = 16 * kb + (l & 15);
+            const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
+            S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
+            S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
+        }
+    }
+    // logits, masks, online softmax (a column's 64 keys live in lanes l, l^16, l^32, l^48)
+    float P[4][2][4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 16 * kb + 4 * (l >> 4) + r;
+                const float b = s.bias[key];
+                const bool ok = b != -INFINITY && s.kpos[key] <= prow[cb] && !((excl[cb] >> key) & 1ull);
+                const float lam = ok ? __builtin_fmaf(scale, S[kb][cb][r], b) : -INFINITY;
+                P[kb][cb][r] = lam;
+                mt = fmaxf(mt, lam);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(F.m[cb], mt);
+        const float a = F.m[cb] == -INFINITY ? 0.0f : softmax_exp(F.m[cb] - mn);
+        float ls = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float lam = P[kb][cb][r];
+                const float p = lam == -INFINITY ? 0.0f : softmax_exp(lam - mn);
+                P[kb][cb][r] = p;
+                ls += p;
+            }
+        F.l[cb] = __builtin_fmaf(F.l[cb], a, ls);
+        F.m[cb] = mn;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) F.O[cb][db] *= a;
+    }
+    // O^T += V^T P^T over two 32-key steps; P as bf16 hi + lo
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        bf16x8_t ph[2], pl[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __bf16 h, lo;
+                split_bf16(P[2 * st + j / 4][cb][j % 4], h, lo);
+                ph[cb][j] = h;
+                pl[cb][j] = lo;
+            }
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const bf16_t* vr = &s.vT[16 * db + (l & 15)][32 * st + 4 * (l >> 4)];
+            const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
+            const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 16);
+            bf16x8_t a;
+            a[0] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.x & 0xffffu));
+            a[1] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.x >> 16));
+            a[2] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.y & 0xffffu));
+            a[3] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.y >> 16));
+            a[4] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.x & 0xffffu));
+            a[5] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.x >> 16));
+            a[6] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.y & 0xffffu));
+            a[7] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.y >> 16));
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                F.O[cb][db] = mfma16(a, ph[cb], F.O[cb][db]);
+                F.O[cb][db] = mfma16(a, pl[cb], F.O[cb][db]);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Workgroup: 128 (row, head) columns = (128 / HG) query rows x HG heads of one KV head.
+// Column n = row * HG + head; wave w owns column blocks 2w and 2w+1.
+template <int HG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void prefill_flash_kernel(FlashArgs A) {
+    __shared__ FlashSmem<HG> s;
+    constexpr int QT = kFlashRowHeads / HG;
+    const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int r0 = tile * QT;
+    const int nrows = min(QT, A.nq - r0);
+    const int p_first = A.pos0 + r0, p_last = A.pos0 + r0 + nrows - 1;
+    const int hq0 = kvh * HG;
+
+    // Q^T operands for this lane's two columns, row positions, per-column masks
+    bf16x8_t qb[2][4];
+    int prow[2];
+    int colrow[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n = 16 * (2 * w + cb) + (l & 15);
+        const int rl = n / HG, h = n % HG;
+        colrow[cb] = rl;
+        prow[cb] = rl < nrows ? A.pos0 + r0 + rl : INT_MIN;  // INT_MIN: no key passes
+        const bf16_t* qr = A.q + (((int64_t)b * A.nq + r0 + min(rl, nrows - 1)) * A.Hq + hq0 + h) * kD;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * (l >> 4));
+    }
+    FlashState<HG> F;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        F.m[cb] = -INFINITY;
+        F.l[cb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) F.O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const bf16_t* kc = A.k + bs * A.sb + kvh * A.sh;
+    const bf16_t* vc = A.v + bs * A.sb + kvh * A.sh;
+    uint64_t noex[2] = {0, 0};
+
+    if (A.index == nullptr) {
+        // dense causal: keys [0, p_last]
+        for (int k0 = 0; k0 <= p_last; k0 += kFlashKeys) {
+            const int nk = min(kFlashKeys, p_last + 1 - k0);
+            flash_tile<HG>(
+                s, F, qb, nk, [&](int r) { return kc + (int64_t)(k0 + r) * A.st; },
+                [&](int r) { return vc + (int64_t)(k0 + r) * A.st; }, [&](int) { return 0.0f; },
+                [&](int r) { return k0 + r; }, prow, noex, A.scale);
+        }
+    } else {
+        const int nb = nbuilt_prefill(p_first, A.W);
+        const int ng = nb * A.G;
+        // opened groups of this lane's columns (coarse exclusion)
+        for (int x = tid; x < kFlashRowHeads * A.TG; x += kThreads) {
+            const int n = x / A.TG, t = x % A.TG;
+            const int rl = n / HG, h = n % HG;
+            s.sel[n][t] = rl < nrows ? A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h) * A.TG + t] : -1;
+        }
+        __syncthreads();
+        const int64_t gbase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.G;
+        const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
+        const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
+        const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
+        // 1. coarse remainder over the group centroids
+        for (int g0 = 0; g0 < ng; g0 += kFlashKeys) {
+            const int nk = min(kFlashKeys, ng - g0);
+            uint64_t ex[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int n = 16 * (2 * w + cb) + (l & 15);
+                uint64_t msk = 0;
+                for (int t = 0; t < A.TG; ++t) {
+                    const int g = s.sel[n][t] - g0;
+                    if (g >= 0 && g < kFlashKeys) msk |= 1ull << g;
+                }
+                ex[cb] = msk;
+            }
+            flash_tile<HG>(
+                s, F, qb, nk, [&](int r) { return gk + (int64_t)(g0 + r) * kD; },
+                [&](int r) { return gv + (int64_t)(g0 + r) * kD; }, [&](int r) { return gln[g0 + r]; },
+                [&](int) { return INT_MIN; }, prow, ex, A.scale);
+        }
+        // 2. sinks not covered by the window
+        const int ns = min(A.n_sink, nb * kChunk);
+        for (int k0 = 0; k0 < ns; k0 += kFlashKeys)
+            flash_tile<HG>(
+                s, F, qb, min(kFlashKeys, ns - k0), [&](int r) { return kc + (int64_t)(k0 + r) * A.st; },
+                [&](int r) { return vc + (int64_t)(k0 + r) * A.st; }, [&](int) { return 0.0f; },
+                [&](int r) { return k0 + r; }, prow, noex, A.scale);
+        // 3. the causal block window [nb*C, p]
+        for (int k0 = nb * kChunk; k0 <= p_last; k0 += kFlashKeys) {
+            const int nk = min(kFlashKeys, p_last + 1 - k0);
+            flash_tile<HG>(
+                s, F, qb, nk, [&](int r) { return kc + (int64_t)(k0 + r) * A.st; },
+                [&](int r) { return vc + (int64_t)(k0 + r) * A.st; }, [&](int) { return 0.0f; },
+                [&](int r) { return k0 + r; }, prow, noex, A.scale);
+        }
+    }
+
+    // column totals (the 4 lanes of a column hold partial sums), then write
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        float lt = F.l[cb];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const int rl = colrow[cb];
+        if (rl >= nrows) continue;
+        const int n = 16 * (2 * w + cb) + (l & 15);
+        const int h = n % HG;
+        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h;
+        if (A.index == nullptr) {
+            float* dst = A.out + rh * kD;
+            const float inv = 1.0f / lt;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const f32x4_t o = F.O[cb][db];
+                *reinterpret_cast<float4*>(dst + 16 * db + 4 * (l >> 4)) =
+                    make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+            }
+        } else {
+            float* dst = A.part + rh * kPartStride;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const f32x4_t o = F.O[cb][db];
+                *reinterpret_cast<float4*>(dst + 16 * db + 4 * (l >> 4)) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+            if ((l >> 4) == 0) {
+                dst[kD] = F.m[cb];
+                dst[kD + 1] = lt;
+            }
+        }
+    }
+}
+
+}  // namespace lodi
+
+namespace lodi {
+
+// ---------------------------------------------------------------------------- select
+
+// Per (row, head, opened slot) record handed from select to the pages kernel.
+struct PairRec {
+    int32_t gid;       // opened group c*G + j, -1: none
+    int16_t ps0, npg;  // first page slot of the group, number of pages
+    uint32_t open;     // bit e: page ps0 + e is opened (exact)
+    float r[kPage];    // canonical ranking score of every page (coarse logits of unopened pages)
+};
+
+struct SelArgs {
+    const bf16_t* q;  // rows of this launch: [B][nq][Hq][d]
+    int seq;          // sequence of grid slice z = 0 (index and cache)
+    int nq, pos0, Hq, Hkv;
+    const char* index;
+    lod_index_layout_t L;
+    int max_chunks, G, W, TG, TP;
+    int32_t* sel_groups;  // nullable API output [B][nq][Hq][TG], rank order
+    int32_t* sel_pages;   // nullable API output [B][nq][Hq][TG][max(TP,1)]
+    int32_t* selg;        // [B][nq][Hq][TG] opened groups in ascending id order (-1 pad)
+    PairRec* rec;         // [B][nq][Hq][TG]
+};
+
+constexpr int kCandCap = 2 * kMaxTG;  // candidates kept per column; beyond: exhaustive path
+
+struct SelSmem {
+    alignas(16) bf16_t kt[kFlashKeys][kD];
+    float gkn_t[kFlashKeys], gln_t[kFlashKeys];
+    float qn[kFlashRowHeads];
+    float T[kFlashRowHeads];
+    int cnt[kFlashRowHeads];
+    int32_t cg[kFlashRowHeads][kCandCap];
+    float cs[kFlashRowHeads][kCandCap];
+    int32_t sel[kFlashRowHeads][kMaxTG];  // rank order
+    int nsel[kFlashRowHeads];
+    uint64_t red[4];
+    int any_overflow;
+};
+
+// Canonical ranking chain q . kbar (fp32 fma in index order) for bf16 rows.
+__device__ __forceinline__ float canonical_dot_bf16(const bf16_t* q, const bf16_t* k) {
+    uint4 qu[16], ku[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        qu[c] = *reinterpret_cast<const uint4*>(q + 8 * c);
+        ku[c] = *reinterpret_cast<const uint4*>(k + 8 * c);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        float qf[8], kf[8];
+        Elt<bf16_t>::unpack(qu[c], qf);
+        Elt<bf16_t>::unpack(ku[c], kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[e], kf[e], acc);
+    }
+    return acc;
+}
+
+// Stage a 64-row tile of bf16 rows (row stride kD) into LDS with XOR-swizzled chunks.
+__device__ __forceinline__ void stage_rows_swizzled(bf16_t (*kt)[kD], const bf16_t* base, int nk) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    for (int i = w; i < kFlashKeys / 4; i += 4) {
+        const int row = 4 * i + (l >> 4);
+        const int c = (l & 15) ^ (row & 15);
+        const int rr = row < nk ? row : nk - 1;
+        __builtin_amdgcn_global_load_lds(base + (int64_t)rr * kD + 8 * c, &kt[4 * i][0], 16, 0, 0);
+    }
+}
+
+template <int HG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void prefill_select_kernel(SelArgs A) {
+    __shared__ SelSmem s;
+    constexpr int QT = kFlashRowHeads / HG;
+    const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int r0 = tile * QT;
+    const int nrows = min(QT, A.nq - r0);
+    const int hq0 = kvh * HG;
+    const int nb = nbuilt_prefill(A.pos0 + r0, A.W);
+    const int ng = nb * A.G;
+    const int TG = A.TG;
+    const int TPW = A.TP > 0 ? A.TP : 1;
+    const int64_t gbase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.G;
+    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
+    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
+    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + gbase;
+    auto qrow = [&](int n) {  // column n -> its query row (clamped into the tile)
+        const int rl = min(n / HG, nrows - 1);
+        return A.q + (((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG) * kD;
+    };
+
+    // Q^T operands of this lane's two columns, |q| per column
+    bf16x8_t qb[2][4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n = 16 * (2 * w + cb) + (l & 15);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qrow(n) + 32 * kk + 8 * (l >> 4));
+    }
+    if (tid < kFlashRowHeads) {
+        const bf16_t* qr = qrow(tid);
+        float ss = 0.0f;
+        for (int c = 0; c < 16; ++c) {
+            float f[8];
+            Elt<bf16_t>::unpack(*reinterpret_cast<const uint4*>(qr + 8 * c), f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+        }
+        s.qn[tid] = sqrtf(ss) * 1.0001f;
+        s.cnt[tid] = 0;
+    }
+    if (tid == 0) s.any_overflow = 0;
+    __syncthreads();
+    const float qn[2] = {s.qn[16 * (2 * w) + (l & 15)], s.qn[16 * (2 * w + 1) + (l & 15)]};
+
+    // MFMA scores S^T of one staged tile for this lane's two columns
+    auto tile_scores = [&](f32x4_t (*S)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
+            S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int row = 16 * kb + (l & 15);
+                const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
+                S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
+                S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
+            }
+        }
+    };
+    auto stage = [&](int g0, int nk) {
+        stage_rows_swizzled(s.kt, gk + (int64_t)g0 * kD, nk);
+        if (tid < kFlashKeys) {
+            s.gln_t[tid] = tid < nk ? gln[g0 + tid] : -INFINITY;
+            s.gkn_t[tid] = tid < nk ? gkn[g0 + tid] : 0.0f;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    // pass A: per column, the k-th largest lower bound S - E (lane-local top-16 lists)
+    float lst[2][kMaxTG];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < kMaxTG; ++e) lst[cb][e] = -INFINITY;
+    for (int g0 = 0; g0 < ng; g0 += kFlashKeys) {
+        const int nk = min(kFlashKeys, ng - g0);
+        stage(g0, nk);
+        f32x4_t S[4][2];
+        tile_scores(S);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 16 * kb + 4 * (l >> 4) + r;
+                const bool valid = s.gln_t[key] != -INFINITY;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    float x = S[kb][cb][r] - kErrC * qn[cb] * s.gkn_t[key];
+                    if (valid && x > lst[cb][kMaxTG - 1]) {
+#pragma unroll
+                        for (int e = 0; e < kMaxTG; ++e) {
+                            const float hi = fmaxf(lst[cb][e], x), lo = fminf(lst[cb][e], x);
+                            lst[cb][e] = hi;
+                            x = lo;
+                        }
+                    }
+                }
+            }
+        __syncthreads();
+    }
+    // merge the four lanes of each column: T = TG-th largest with multiplicity
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        int taken = 0;
+        float T = -INFINITY;
+        for (int round = 0; round < TG; ++round) {
+            float h = lst[cb][0];
+            float m = fmaxf(h, __shfl_xor(h, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (m == -INFINITY) { T = -INFINITY; taken = TG; }
+            const int mine = (h == m && m != -INFINITY) ? 1 : 0;
+            int c = mine + __shfl_xor(mine, 16, 64);
+            c += __shfl_xor(c, 32, 64);
+            if (taken < TG) {
+                taken += c;
+                if (taken >= TG) T = m;
+                if (mine) {
+#pragma unroll
+                    for (int e = 0; e < kMaxTG - 1; ++e) lst[cb][e] = lst[cb][e + 1];
+                    lst[cb][kMaxTG - 1] = -INFINITY;
+                }
+            }
+        }
+        if ((l >> 4) == 0) s.T[16 * (2 * w + cb) + (l & 15)] = T;
+    }
+    __syncthreads();
+
+    // pass B: candidates S + E >= T
+    const float T2[2] = {s.T[16 * (2 * w) + (l & 15)], s.T[16 * (2 * w + 1) + (l & 15)]};
+    for (int g0 = 0; g0 < ng; g0 += kFlashKeys) {
+        const int nk = min(kFlashKeys, ng - g0);
+        stage(g0, nk);
+        f32x4_t S[4][2];
+        tile_scores(S);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 16 * kb + 4 * (l >> 4) + r;
+                const bool valid = s.gln_t[key] != -INFINITY;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const float ub = S[kb][cb][r] + kErrC * qn[cb] * s.gkn_t[key];
+                    if (valid && ub >= T2[cb]) {
+                        const int n = 16 * (2 * w + cb) + (l & 15);
+                        const int at = atomicAdd(&s.cnt[n], 1);
+                        if (at < kCandCap) s.cg[n][at] = g0 + key;
+                    }
+                }
+            }
+        __syncthreads();
+    }
+
+    // canonical chains for the candidates
+    for (int x = tid; x < kFlashRowHeads * kCandCap; x += kThreads) {
+        const int n = x / kCandCap, at = x % kCandCap;
+        if (at < min(s.cnt[n], kCandCap)) s.cs[n][at] = canonical_dot_bf16(qrow(n), gk + (int64_t)s.cg[n][at] * kD);
+    }
+    __syncthreads();
+    // exact top-TG per column among its candidates (columns that overflowed: below)
+    if (tid < kFlashRowHeads) {
+        const int n = tid, c = s.cnt[n];
+        if (c > kCandCap) {
+            atomicOr(&s.any_overflow, 1);
+            s.nsel[n] = -1;
+        } else {
+            uint64_t top[kMaxTG];
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) top[e] = 0;
+            for (int at = 0; at < c; ++at) {
+                uint64_t x = rank_key(s.cs[n][at], (uint32_t)s.cg[n][at]);
+#pragma unroll
+                for (int e = 0; e < kMaxTG; ++e) {
+                    const uint64_t hi = top[e] > x ? top[e] : x, lo = top[e] > x ? x : top[e];
+                    top[e] = hi;
+                    x = lo;
+                }
+            }
+            const int k = min(c, TG);
+            for (int e = 0; e < kMaxTG; ++e)
+                if (e < TG) s.sel[n][e] = e < k ? (int)key_id(top[e]) : -1;
+            s.nsel[n] = k;
+        }
+    }
+    __syncthreads();
+    // exhaustive path for columns with more candidates than kept: canonical scores of
+    // every eligible group, workgroup-wide top-TG
+    if (s.any_overflow) {
+        for (int n = 0; n < kFlashRowHeads; ++n) {
+            if (s.nsel[n] >= 0) continue;  // uniform: read from LDS after a barrier
+            uint64_t top[kMaxTG];
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) top[e] = 0;
+            for (int g = tid; g < ng; g += kThreads) {
+                if (gln[g] == -INFINITY) continue;
+                uint64_t x = rank_key(canonical_dot_bf16(qrow(n), gk + (int64_t)g * kD), (uint32_t)g);
+#pragma unroll
+                for (int e = 0; e < kMaxTG; ++e) {
+                    const uint64_t hi = top[e] > x ? top[e] : x, lo = top[e] > x ? x : top[e];
+                    top[e] = hi;
+                    x = lo;
+                }
+            }
+            int k = 0;
+            for (int round = 0; round < TG; ++round) {
+                const uint64_t wm = wave_max_u64(top[0]);
+                if (l == 0) s.red[w] = wm;
+                __syncthreads();
+                uint64_t m = s.red[0];
+                for (int x = 1; x < 4; ++x) m = s.red[x] > m ? s.red[x] : m;
+                __syncthreads();
+                if (m == 0) break;
+                if (tid == 0) s.sel[n][round] = (int)key_id(m);
+                if (top[0] == m) {
+#pragma unroll
+                    for (int e = 0; e < kMaxTG - 1; ++e) top[e] = top[e + 1];
+                    top[kMaxTG - 1] = 0;
+                }
+                ++k;
+            }
+            if (tid == 0) {
+                for (int e = k; e < TG; ++e) s.sel[n][e] = -1;
+                s.nsel[n] = k;
+            }
+            __syncthreads();
+        }
+    }
+
+    // outputs: opened groups (rank order and ascending), then the pages of each
+    for (int x = tid; x < kFlashRowHeads * TG; x += kThreads) {
+        const int n = x / TG, t = x % TG;
+        const int rl = n / HG;
+        if (rl >= nrows) continue;
+        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG;
+        if (A.sel_groups) A.sel_groups[rh * TG + t] = s.sel[n][t];
+        // ascending copy: the t-th smallest id among the selected
+        const int gt = s.sel[n][t];
+        int pos = 0;
+        for (int e = 0; e < s.nsel[n]; ++e) pos += s.sel[n][e] < gt;
+        if (gt >= 0) A.selg[rh * TG + pos] = gt;
+        if (t >= s.nsel[n]) A.selg[rh * TG + t] = -1;
+    }
+    const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) +
+                            ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.L.meta_stride;
+    const bf16_t* pk_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pk) +
+                         ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.L.page_slots * kD;
+    for (int x = tid; x < kFlashRowHeads * TG; x += kThreads) {
+        const int n = x / TG, t = x % TG;
+        const int rl = n / HG;
+        if (rl >= nrows) continue;
+        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG;
+        PairRec R;
+        R.gid = s.sel[n][t];
+        R.ps0 = R.npg = 0;
+        R.open = 0;
+        int slot_rank[kPage];
+#pragma unroll
+        for (int e = 0; e < kPage; ++e) { R.r[e] = 0.0f; slot_rank[e] = -1; }
+        if (R.gid >= 0) {
+            const int c = R.gid / A.G, j = R.gid % A.G;
+            const int16_t* gpg = meta_u + (int64_t)c * A.L.meta_stride;
+            const int ps0 = gpg[j], npg = gpg[j + 1] - ps0;
+            R.ps0 = (int16_t)ps0;
+            R.npg = (int16_t)npg;
+            if (A.TP == 0) {
+                R.open = npg >= 32 ? 0xffffffffu : ((1u << npg) - 1u);
+            } else {
+                uint64_t key[kPage];
+                for (int e = 0; e < kPage; ++e) {
+                    key[e] = 0;
+                    if (e < npg) {
+                        R.r[e] = canonical_dot_bf16(qrow(n), pk_u + ((int64_t)c * A.L.page_slots + ps0 + e) * kD);
+                        key[e] = rank_key(R.r[e], (uint32_t)e);
+                    }
+                }
+                const int nopen = min(npg, A.TP);
+                for (int k = 0; k < nopen; ++k) {
+                    int best = 0;
+                    for (int e = 1; e < kPage; ++e)
+                        if (key[e] > key[best]) best = e;
+                    slot_rank[k] = best;
+                    R.open |= 1u << best;
+                    key[best] = 0;
+                }
+            }
+        }
+        A.rec[rh * TG + t] = R;
+        if (A.sel_pages)
+            for (int k = 0; k < TPW; ++k)
+                A.sel_pages[(rh * TG + t) * TPW + k] =
+                    (A.TP > 0 && R.gid >= 0 && k < kPage && slot_rank[k] >= 0) ? R.ps0 + slot_rank[k] : -1;
+    }
+}
+// ---------------------------------------------------------------------------- bucket
+
+// A unit is (sequence, KV head, 256-row query chunk of the launch); its pairs are
+// (row, head, slot) with pair index (row_in_chunk * HG + head) * TG + slot.
+constexpr int kMaxBucketGroups = 16384;  // summarised groups per KV head a prefill supports
+
+struct PagesArgs {
+    const bf16_t* k;
+    const bf16_t* v;
+    int64_t sb, st, sh;
+    const bf16_t* q;
+    int seq;                // sequence of grid slice z = 0 (index and cache)
+    int nq, pos0, Hq, Hkv;
+    float scale;
+    const char* index;
+    lod_index_layout_t L;
+    int max_chunks, G, W, TG;
+    const PairRec* rec;     // [B][nq][Hq][TG]
+    int32_t* plist;         // [units][kChunk * HG * TG] pair indices sorted by group
+    int32_t* poff;          // [units][2]: number of pairs with a group, (unused)
+    float* part_fl;         // [B][nq][Hq] flash partial states
+    float* part_pg;         // [B][nq][Hq][TG] page partial states
+    float* out;             // [B][nq][Hq][d]
+    int units_per_seq_kv;   // query chunks in the launch
+};
+
+template <int HG>
+__global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
+    __shared__ int cnt[kMaxBucketGroups];
+    const int qc = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int r0 = qc * kChunk;
+    const int nrows = min(kChunk, A.nq - r0);
+    const int nb = nbuilt_prefill(A.pos0 + r0, A.W);
+    const int ng = nb * A.G;
+    const int npairs = nrows * HG * A.TG;
+    const int64_t unit = ((int64_t)b * A.Hkv + kvh) * A.units_per_seq_kv + qc;
+    int32_t* list = A.plist + unit * (kChunk * HG * A.TG);
+    auto pair_gid = [&](int x) {
+        const int t = x % A.TG, h = (x / A.TG) % HG, rl = x / (A.TG * HG);
+        return A.rec[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t].gid;
+    };
+    for (int g = tid; g < ng; g += kThreads) cnt[g] = 0;
+    __syncthreads();
+    for (int x = tid; x < npairs; x += kThreads) {
+        const int g = pair_gid(x);
+        if (g >= 0) atomicAdd(&cnt[g], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the counts: contiguous ranges per thread, then one thread scans
+    __shared__ int part[kThreads];
+    const int per = (ng + kThreads - 1) / kThreads;
+    const int g0 = tid * per, g1 = min(ng, g0 + per);
+    int sum = 0;
+    for (int g = g0; g < g1; ++g) sum += cnt[g];
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int x = 0; x < kThreads; ++x) { const int v = part[x]; part[x] = acc; acc += v; }
+        A.poff[unit * 2] = acc;
+    }
+    __syncthreads();
+    int acc = part[tid];
+    for (int g = g0; g < g1; ++g) { const int v = cnt[g]; cnt[g] = acc; acc += v; }
+    __syncthreads();
+    for (int x = tid; x < npairs; x += kThreads) {
+        const int g = pair_gid(x);
+        if (g >= 0) list[atomicAdd(&cnt[g], 1)] = x;
+    }
+}
+
+// ---------------------------------------------------------------------------- pages
+
+constexpr int kPairsPerWG = 64;
+
+// One workgroup per 64 consecutive pairs of a unit's group-sorted list; each 16-lane
+// subgroup runs one pair: exact rows of its opened pages and the mean terms of the
+// unopened pages of its group, one online softmax, written as the pair's partial state.
+// Pairs of the same group run side by side, so their rows come from the same cache lines.
+template <int HG>
+__global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
+    const int blk = blockIdx.x, unit_local = blockIdx.y;
+    const int qc = unit_local % A.units_per_seq_kv;
+    const int kvh = (unit_local / A.units_per_seq_kv) % A.Hkv;
+    const int b = unit_local / (A.units_per_seq_kv * A.Hkv);
+    const int tid = threadIdx.x, l16 = tid & 15, sg = tid >> 4;
+    const int64_t unit = unit_local;
+    const int npairs = A.poff[unit * 2];
+    const int r0 = qc * kChunk;
+    const int PS = A.L.page_slots;
+    const int32_t* list = A.plist + unit * (kChunk * HG * A.TG);
+    const int bs = A.seq + b;
+    const int64_t ubase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks;
+    const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + ubase * A.L.meta_stride;
+    const bf16_t* pv_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pv) + ubase * PS * kD;
+    const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + ubase * PS;
+    const bf16_t* kc = A.k + bs * A.sb + kvh * A.sh;
+    const bf16_t* vc = A.v + bs * A.sb + kvh * A.sh;
+
+    for (int x = blk * kPairsPerWG + sg; x < min(npairs, (blk + 1) * kPairsPerWG); x += 16) {
+        const int pi = list[x];
+        const int t = pi % A.TG, h = (pi / A.TG) % HG, rl = pi / (A.TG * HG);
+        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h;
+        const PairRec& R = A.rec[rh * A.TG + t];
+        const int c = R.gid / A.G;
+        const int16_t* pst = meta_u + (int64_t)c * A.L.meta_stride + (A.G + 1);
+        const int16_t* perm = pst + (PS + 1);
+        float q8[8];
+        load8<bf16_t>(A.q + rh * kD, l16, q8);
+        Online st;
+        st.init();
+        for (int e = 0; e < R.npg; ++e) {
+            const int slot = R.ps0 + e;
+            if ((R.open >> e) & 1u) {
+                const int x0 = pst[slot], x1 = pst[slot + 1];
+                for (int y0 = x0; y0 < x1; y0 += 4) {
+                    float kf[4][8], vf[4][8];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (y0 + u < x1) {
+                            const int pos = c * kChunk + perm[y0 + u];
+                            load8<bf16_t>(kc + (int64_t)pos * A.st, l16, kf[u]);
+                            load8<bf16_t>(vc + (int64_t)pos * A.st, l16, vf[u]);
+                        }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (y0 + u < x1) {
+                            float a = 0.0f;
+#pragma unroll
+                            for (int z = 0; z < 8; ++z) a = __builtin_fmaf(q8[z], kf[u][z], a);
+#pragma unroll
+                            for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
+                            st.add(A.scale * a, vf[u]);
+                        }
+                }
+            } else {
+                float vf[8];
+                load8<bf16_t>(pv_u + ((int64_t)c * PS + slot) * kD, l16, vf);
+                st.add(A.scale * R.r[e] + pln_u[(int64_t)c * PS + slot], vf);
+            }
+        }
+        float* dst = A.part_pg + (rh * A.TG + t) * kPartStride;
+        *reinterpret_cast<float4*>(dst + 8 * l16) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+        *reinterpret_cast<float4*>(dst + 8 * l16 + 4) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+        if (l16 == 0) { dst[kD] = st.m; dst[kD + 1] = st.l; }
+    }
+}
+
+// ---------------------------------------------------------------------------- combine
+
+// out = merge of the flash partial and the page partials of every opened slot.
+__global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, int64_t nrh) {
+    const int64_t rh = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+    const int d = threadIdx.x & 127;
+    if (rh >= nrh) return;
+    const float* pf = A.part_fl + rh * kPartStride;
+    float M = pf[kD];
+    for (int t = 0; t < A.TG; ++t)
+        if (A.rec[rh * A.TG + t].gid >= 0) M = fmaxf(M, A.part_pg[(rh * A.TG + t) * kPartStride + kD]);
+    float L = 0.0f, O = 0.0f;
+    if (pf[kD] != -INFINITY) {
+        const float e = softmax_exp(pf[kD] - M);
+        L = pf[kD + 1] * e;
+        O = pf[d] * e;
+    }
+    for (int t = 0; t < A.TG; ++t) {
+        if (A.rec[rh * A.TG + t].gid < 0) continue;
+        const float* pp = A.part_pg + (rh * A.TG + t) * kPartStride;
+        if (pp[kD] == -INFINITY) continue;
+        const float e = softmax_exp(pp[kD] - M);
+        L = __builtin_fmaf(pp[kD + 1], e, L);
+        O = __builtin_fmaf(pp[d], e, O);
+    }
+    A.out[rh * kD + d] = O / L;
+}
+
+}  // namespace lodi
+
+// ---------------------------------------------------------------------------- host side
+
+namespace lodi {
+
+// Rows per prefill batch (a multiple of the chunk size): bounds the workspace.
+constexpr int kPrefillBatchRows = 2048;
+
+struct PrefillPlan {
+    int rows;  // rows per batch (<= n_q, multiple of kChunk unless n_q is smaller)
+    size_t off_selg, off_rec, off_pfl, off_ppg, off_plist, off_poff, bytes;
+};
+
+// Workspace of one batch of rows of one sequence (sequences run one after another).
+static PrefillPlan plan_prefill(const lod_params* p, int n_q) {
+    PrefillPlan P{};
+    P.rows = n_q < kPrefillBatchRows ? n_q : kPrefillBatchRows;
+    const size_t rh = (size_t)P.rows * p->n_q_heads;
+    const size_t TG = p->top_groups;
+    const int HG = p->n_q_heads / p->n_kv_heads;
+    const size_t units = (size_t)p->n_kv_heads * ((P.rows + kChunk - 1) / kChunk);
+    size_t o = 0;
+    P.off_selg = o; o = align256(o + rh * TG * 4);
+    P.off_rec = o; o = align256(o + rh * TG * sizeof(PairRec));
+    P.off_pfl = o; o = align256(o + rh * kPartStride * 4);
+    P.off_ppg = o; o = align256(o + rh * TG * kPartStride * 4);
+    P.off_plist = o; o = align256(o + units * kChunk * HG * TG * 4);
+    P.off_poff = o; o = align256(o + units * 2 * 4);
+    P.bytes = o;
+    return P;
+}
+
+template <int HG>
+static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const PagesArgs& P, int batch,
+                                 int nunits_q, hipStream_t st) {
+    constexpr int QT = kFlashRowHeads / HG;
+    const int ntiles = (S.nq + QT - 1) / QT;
+    hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, S);
+    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, F);
+    hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
+    const int maxpairs = kChunk * HG * S.TG;
+    hipLaunchKernelGGL((prefill_pages_kernel<HG>), dim3((maxpairs + kPairsPerWG - 1) / kPairsPerWG,
+                       nunits_q * S.Hkv * batch), dim3(kThreads), 0, st, P);
+    const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + 1) / 2)), dim3(kThreads), 0, st, P, nrh);
+}
+
+}  // namespace lodi
+
+namespace lodi {
+
+template <int HG>
+static void launch_flash(const FlashArgs& A, int batch, hipStream_t st) {
+    constexpr int QT = kFlashRowHeads / HG;
+    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kThreads),
+                       0, st, A);
+}
+
+static int dispatch_flash(const FlashArgs& A, int batch, hipStream_t st) {
+    switch (A.Hq / A.Hkv) {
+        case 1: launch_flash<1>(A, batch, st); break;
+        case 2: launch_flash<2>(A, batch, st); break;
+        case 4: launch_flash<4>(A, batch, st); break;
+        default: launch_flash<8>(A, batch, st); break;
+    }
+    return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
+}
+
+}  // namespace lodi
+
+using namespace lodi;
+
+extern "C" int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_t q_start,
+                                 int32_t n_q, int32_t batch, float* out, void* stream) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
+    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
+    if ((int64_t)q_start + n_q > INT32_MAX) return LOD_ERR_ARG;
+    if (params->kv_dtype != LOD_BF16)
+        return dense_prefill_valu(params, kv, q, q_start, n_q, batch, out, stream);
+    FlashArgs A{};
+    A.k = reinterpret_cast<const bf16_t*>(kv.k);
+    A.v = reinterpret_cast<const bf16_t*>(kv.v);
+    A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    A.q = reinterpret_cast<const bf16_t*>(q);
+    A.nq = n_q; A.pos0 = q_start;
+    A.Hq = params->n_q_heads; A.Hkv = params->n_kv_heads; A.scale = params->scale;
+    A.index = nullptr;
+    A.out = out;
+    return dispatch_flash(A, batch, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int lod_prefill_ws_bytes(const lod_params* params, int32_t batch, int32_t n_q,
+                                    int32_t max_tokens, size_t* bytes) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!bytes || batch <= 0 || n_q <= 0 || max_tokens <= 0) return LOD_ERR_ARG;
+    if (params->kv_dtype != LOD_BF16) return prefill_rows_ws_bytes(params, n_q, max_tokens, bytes);
+    *bytes = plan_prefill(params, n_q).bytes;
+    return LOD_OK;
+}
+
+extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* index, lod_kv kv,
+                                  const void* q, int32_t q_start, int32_t n_q, int32_t batch,
+                                  float* out, int32_t* sel_groups, int32_t* sel_pages, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (!index || !index->mem || !q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
+    if (q_start % params->chunk_size != 0) return LOD_ERR_ARG;
+    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
+    if (batch != index->batch) return LOD_ERR_ARG;
+    const int64_t end = (int64_t)q_start + n_q;
+    if (end > INT32_MAX || built_chunks(params, end - 1) > index->max_chunks) return LOD_ERR_ARG;
+    const lod_index_layout_t L = make_layout(params, index->batch, index->max_chunks);
+    if (index->bytes < L.total) return LOD_ERR_WORKSPACE;
+    if (params->kv_dtype != LOD_BF16)
+        return prefill_rows(params, index, kv, q, q_start, n_q, batch, out, sel_groups, sel_pages, ws,
+                            ws_bytes, stream);
+    if ((int64_t)built_chunks(params, end - 1) * params->groups_per_chunk > kMaxBucketGroups)
+        return LOD_ERR_UNSUPPORTED;
+    const PrefillPlan P = plan_prefill(params, n_q);
+    if (!ws || ws_bytes < P.bytes) return LOD_ERR_WORKSPACE;
+    char* w = reinterpret_cast<char*>(ws);
+    const int Hq = params->n_q_heads, Hkv = params->n_kv_heads, HG = Hq / Hkv, TG = params->top_groups;
+    const int TPW = params->top_pages > 0 ? params->top_pages : 1;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    for (int r0 = 0; r0 < n_q; r0 += P.rows) {
+        const int rows = (n_q - r0) < P.rows ? (n_q - r0) : P.rows;
+        const int nunits_q = (rows + kChunk - 1) / kChunk;
+        // batch rows are taken from every sequence: q rows [r0, r0+rows) of each b
+        for (int b = 0; b < batch; ++b) {
+            const int64_t row0 = (int64_t)b * n_q + r0;
+            SelArgs S{};
+            S.q = reinterpret_cast<const bf16_t*>(q) + row0 * Hq * kD;
+            S.nq = rows; S.pos0 = q_start + r0; S.Hq = Hq; S.Hkv = Hkv;
+            S.index = reinterpret_cast<const char*>(index->mem);
+            S.L = L; S.max_chunks = index->max_chunks; S.G = params->groups_per_chunk;
+            S.W = params->window; S.TG = TG; S.TP = params->top_pages;
+            S.sel_groups = sel_groups ? sel_groups + row0 * Hq * TG : nullptr;
+            S.sel_pages = sel_pages ? sel_pages + row0 * Hq * TG * TPW : nullptr;
+            S.selg = reinterpret_cast<int32_t*>(w + P.off_selg);
+            S.rec = reinterpret_cast<PairRec*>(w + P.off_rec);
+            S.seq = b;
+            FlashArgs F{};
+            F.k = reinterpret_cast<const bf16_t*>(kv.k);
+            F.v = reinterpret_cast<const bf16_t*>(kv.v);
+            F.seq = b; F.sb = kv.stride_b; F.st = kv.stride_t; F.sh = kv.stride_h;
+            F.q = S.q; F.nq = rows; F.pos0 = S.pos0; F.Hq = Hq; F.Hkv = Hkv; F.scale = params->scale;
+            F.index = S.index; F.L = L; F.max_chunks = S.max_chunks; F.G = S.G; F.W = S.W;
+            F.n_sink = params->n_sink; F.TG = TG; F.selg = S.selg;
+            F.part = reinterpret_cast<float*>(w + P.off_pfl);
+            PagesArgs G{};
+            G.k = F.k; G.v = F.v; G.seq = b; G.sb = F.sb; G.st = F.st; G.sh = F.sh;
+            G.q = S.q; G.nq = rows; G.pos0 = S.pos0; G.Hq = Hq; G.Hkv = Hkv; G.scale = params->scale;
+            G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
+            G.rec = S.rec;
+            G.plist = reinterpret_cast<int32_t*>(w + P.off_plist);
+            G.poff = reinterpret_cast<int32_t*>(w + P.off_poff);
+            G.part_fl = F.part;
+            G.part_pg = reinterpret_cast<float*>(w + P.off_ppg);
+            G.out = out + row0 * Hq * kD;
+            G.units_per_seq_kv = nunits_q;
+            switch (HG) {
+                case 1: launch_prefill_batch<1>(S, F, G, 1, nunits_q, st); break;
+                case 2: launch_prefill_batch<2>(S, F, G, 1, nunits_q, st); break;
+                case 4: launch_prefill_batch<4>(S, F, G, 1, nunits_q, st); break;
+                default: launch_prefill_batch<8>(S, F, G, 1, nunits_q, st); break;
+            }
+        }
+        if (hipGetLastError() != hipSuccess) return LOD_ERR_HIP;
+    }
+    return LOD_OK;
+}

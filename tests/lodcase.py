@@ -25,11 +25,12 @@ class Case:
     """Inputs on host and device, GPU index built by k-means (or injected assignments)."""
 
     def __init__(self, gcfg, ocfg, B, T, seed=0, sigma=0.3, zero_variance=False, device="cuda",
-                 gen_device="cpu"):
+                 gen_device="cpu", n_centres=32):
         self.gcfg, self.ocfg, self.B, self.T = gcfg, ocfg, B, T
         Hkv = gcfg.n_kv_heads
         K, V, cen, _ = synth.clustered_kv(B, T, Hkv, 128, seed=seed, sigma=sigma, dtype=gcfg.dtype,
-                                          zero_variance=zero_variance, device=gen_device)
+                                          zero_variance=zero_variance, device=gen_device,
+                                          n_centres=n_centres)
         self.cen = cen
         self.Kd, self.Vd = K.to(device), V.to(device)
         self.K, self.V = K, V  # generator-side copies (host or device)

@@ -1,0 +1,133 @@
+"""GPU parity of prefill (LoD and the dense causal baseline) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_kv_approximation_amd import lod
+from oracle import oracle as orc
+
+from lodcase import TOL, Case, configs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _sample_rows(B, nq, Hq, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(b, i, h) for b, i, h in zip(rng.integers(0, B, n), rng.integers(0, nq, n), rng.integers(0, Hq, n))}
+    rows |= {(0, 0, 0), (B - 1, nq - 1, Hq - 1), (0, nq - 1, 0), (B - 1, 0, Hq - 1)}
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,q_start,nq", [
+    (torch.bfloat16, 64, 8, 512, 700),
+    (torch.bfloat16, 16, 4, 0, 333),
+    (torch.bfloat16, 8, 8, 256, 129),
+    (torch.float32, 4, 4, 256, 100),
+])
+def test_dense_prefill_parity(dtype, hq, hkv, q_start, nq):
+    g, o = configs(dtype, hq, hkv, G=8)
+    T = q_start + nq
+    case = Case(g, o, 2, ((T + 255) // 256) * 256, seed=31)
+    Q = case.queries(seed=32, n_rows=nq)
+    out = lod.dense_prefill(g, case.Kd, case.Vd, Q.cuda(), q_start).cpu().numpy()
+    rows = _sample_rows(2, nq, hq, 60, 33)
+    st = {kv: case.stream(*kv) for kv in {(b, h // (hq // hkv)) for b, _, h in rows}}
+    ref = orc.dense_rows(o, st, Q.float().numpy(), q_start, rows)
+    worst = max(float(np.max(np.abs(out[b, i, h] - ref[(b, i, h)]))) for b, i, h in rows)
+    assert worst <= TOL[dtype], worst
+
+
+def _prefill_and_compare(case, Q, q_start, rows, check_dense=False):
+    """GPU LoD prefill of every row of Q vs the oracle on the sampled rows: selection
+    bit-exact, outputs within tolerance.  Returns (worst error, GPU outputs)."""
+    g, o = case.gcfg, case.ocfg
+    out, sg, sp = lod.attend_prefill(g, case.index, case.Kd, case.Vd, Q.cuda(), q_start, want_selection=True)
+    torch.cuda.synchronize()
+    out, sg, sp = out.cpu().numpy(), sg.cpu().numpy(), sp.cpu().numpy()
+    hpg = g.n_q_heads // g.n_kv_heads
+    st, oidx = case.oracle_index(sorted({(b, h // hpg) for b, _, h in rows}))
+    ref = orc.prefill_rows(o, st, oidx, Q.float().numpy(), q_start, rows)
+    worst = 0.0
+    for (b, i, h), r in ref.items():
+        assert np.array_equal(sg[b, i, h], r["sel_groups"]), ((b, i, h), sg[b, i, h], r["sel_groups"])
+        assert np.array_equal(sp[b, i, h], r["sel_pages"]), ((b, i, h), sp[b, i, h], r["sel_pages"])
+        worst = max(worst, float(np.max(np.abs(out[b, i, h] - r["out"]))))
+    assert worst <= TOL[g.dtype], worst
+    if check_dense:
+        dref = orc.dense_rows(o, st, Q.float().numpy(), q_start, rows)
+        dworst = max(float(np.max(np.abs(out[r] - dref[r]))) for r in rows)
+        assert dworst <= TOL[g.dtype], dworst
+    return worst, out
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,q_start,nq,G,TG,TP", [
+    (torch.bfloat16, 64, 8, 2048, 2600, 8, 8, 2),   # two row batches, ragged last query chunk
+    (torch.bfloat16, 16, 4, 0, 700, 8, 8, 2),       # rows with no summarised chunk
+    (torch.bfloat16, 8, 8, 1024, 333, 8, 8, 2),     # one head per KV head
+    (torch.bfloat16, 8, 4, 768, 300, 8, 8, 2),      # two heads per KV head
+    (torch.bfloat16, 16, 2, 1536, 512, 8, 8, 0),    # two-tier: opened groups fully exact
+    (torch.bfloat16, 16, 2, 1536, 512, 8, 8, 1),
+    (torch.bfloat16, 16, 2, 1536, 512, 8, 8, 3),
+    (torch.bfloat16, 16, 2, 1280, 400, 4, 4, 2),
+    (torch.bfloat16, 16, 2, 1280, 400, 16, 16, 2),
+    (torch.float32, 4, 4, 1024, 300, 4, 8, 2),      # fp32 caches: row-by-row path
+])
+def test_lod_prefill_parity(dtype, hq, hkv, q_start, nq, G, TG, TP):
+    g, o = configs(dtype, hq, hkv, G=G, TG=TG, TP=TP)
+    T = q_start + nq
+    case = Case(g, o, 2, ((T + 255) // 256) * 256, seed=41)
+    case.build_gpu()
+    Q = case.queries(seed=42, n_rows=nq)
+    rows = _sample_rows(2, nq, hq, 120, 43)
+    _prefill_and_compare(case, Q, q_start, rows)
+
+
+def test_lod_prefill_diffuse_queries():
+    g, o = configs(torch.bfloat16, 16, 2, G=8)
+    case = Case(g, o, 1, 4096, seed=44)
+    case.build_gpu()
+    Q = case.queries(seed=45, n_rows=1024, kind="diffuse")
+    _prefill_and_compare(case, Q, 3072, _sample_rows(1, 1024, 16, 100, 46))
+
+
+def test_lod_prefill_ties_take_the_exhaustive_path():
+    """Four centres shared by every chunk and zero variance: dozens of groups tie at the
+    top score, more than the candidate list keeps, so selection falls back to ranking
+    every group canonically.  Zero variance also makes LoD equal dense attention."""
+    g, o = configs(torch.bfloat16, 16, 2, G=8, TG=16)
+    case = Case(g, o, 1, 12288, seed=47, zero_variance=True, n_centres=4)
+    case.build_gpu()
+    Q = case.queries(seed=48, n_rows=512)
+    _prefill_and_compare(case, Q, 11776, _sample_rows(1, 512, 16, 60, 49), check_dense=True)
+
+
+def test_lod_prefill_32k_chunked_equals_one_shot():
+    """32K-token prefill, 64/8 heads: one call over every row equals the chunked flow
+    (build the chunk that leaves the window, then attend the next 256-row query chunk),
+    bit for bit; sampled rows match the oracle."""
+    g, o = configs(torch.bfloat16, 64, 8, G=8)
+    T = 32768
+    case = Case(g, o, 1, T, seed=50)
+    case.build_gpu()
+    Q = case.queries(seed=51, n_rows=T)
+    rows = _sample_rows(1, T, 64, 150, 52)
+    _, one = _prefill_and_compare(case, Q, 0, rows)
+
+    fresh = lod.LodIndex.allocate(g, 1, T, device="cuda")
+    Qd = Q.cuda()
+    out = torch.empty(1, T, 64, 128, dtype=torch.float32, device="cuda")
+    ws = torch.empty(lod.prefill_ws_bytes(g, 1, 256, T), dtype=torch.uint8, device="cuda")
+    nwin = g.window // 256
+    for k in range(T // 256):
+        if k - nwin >= 0:
+            lod.build_chunk(g, fresh, case.Kd, case.Vd, k - nwin, 1)
+        lod.attend_prefill(g, fresh, case.Kd, case.Vd, Qd[:, 256 * k: 256 * (k + 1)], 256 * k, ws=ws,
+                           out=out[:, 256 * k: 256 * (k + 1)])
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), one)
