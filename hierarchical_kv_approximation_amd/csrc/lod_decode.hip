@@ -1,11 +1,10 @@
 // lod_decode.hip -- LoD decode (subsystems b, c, d) and the dense decode baseline.
 //
-// "Queries start by scoring themselves against the low resolution centroids. We take
-// the top eight ... score the query against those page summaries ... take the top two
-// pages ... apply exact attention to these, as well as the most recent block sliding
-// window ... and one or more sink tokens.  We combine the exactly attended KV pairs
-// with a coarse remainder in a single softmax" ("Level of Detail Attention",
-// How It Works).
+// A query first ranks the group centroids and opens the best groups, then ranks the
+// page summaries inside those groups and opens the best pages; the keys of opened pages,
+// the recent block window and the sink tokens are attended exactly, and everything else
+// enters the same softmax as count-weighted means ("Level of Detail Attention", How It
+// Works).
 //
 // Three launches per call, all on the caller's stream:
 //  1. scan    grid (slices + window tiles, KV heads, batch).  A slice workgroup streams
@@ -1245,16 +1244,9 @@ int check_kv_view(const lod_params* p, const lod_kv& kv) {
     return LOD_OK;
 }
 
-// Record trace event k (when lod_trace_events is set on this thread).
-static inline void trace(int k, hipStream_t st) {
-    int n = 0;
-    void* const* ev = trace_events(&n);
-    if (ev && k < n) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[k]), st);
-}
-
 template <typename T, int HG>
 static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
-    trace(0, st);
+    trace_point(0, st);
     if (A.nslice + A.nwin > 0) {
         if constexpr (sizeof(T) == 2)
             hipLaunchKernelGGL((decode_scan_mfma_kernel<HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
@@ -1263,9 +1255,9 @@ static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
             hipLaunchKernelGGL((decode_scan_kernel<T, HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
                                dim3(kThreads), 0, st, A);
     }
-    trace(1, st);
+    trace_point(1, st);
     hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
-    trace(2, st);
+    trace_point(2, st);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
 

@@ -97,6 +97,10 @@ void* const* trace_events(int* n) {
     return g_trace;
 }
 
+void trace_point(int k, hipStream_t st) {
+    if (g_trace && k < g_ntrace) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(g_trace[k]), st);
+}
+
 }  // namespace lodi
 
 using namespace lodi;

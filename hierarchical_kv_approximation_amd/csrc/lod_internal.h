@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime_api.h>
+
 #include "lod.h"
 
 namespace lodi {
@@ -69,5 +71,7 @@ int dense_prefill_valu(const lod_params* params, lod_kv kv, const void* q, int32
 
 // Events set by lod_trace_events for the calling host thread (null when off).
 void* const* trace_events(int* n);
+// Record trace event k on st when events are set and k is in range.
+void trace_point(int k, hipStream_t st);
 
 }  // namespace lodi

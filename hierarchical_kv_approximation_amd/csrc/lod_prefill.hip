@@ -915,14 +915,20 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
                                  int nunits_q, hipStream_t st) {
     constexpr int QT = kFlashRowHeads / HG;
     const int ntiles = (S.nq + QT - 1) / QT;
+    trace_point(0, st);
     hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, S);
+    trace_point(1, st);
     hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, F);
+    trace_point(2, st);
     hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
+    trace_point(3, st);
     const int maxpairs = kChunk * HG * S.TG;
     hipLaunchKernelGGL((prefill_pages_kernel<HG>), dim3((maxpairs + kPairsPerWG - 1) / kPairsPerWG,
                        nunits_q * S.Hkv * batch), dim3(kThreads), 0, st, P);
+    trace_point(4, st);
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + 1) / 2)), dim3(kThreads), 0, st, P, nrh);
+    trace_point(5, st);
 }
 
 }  // namespace lodi
