@@ -44,6 +44,8 @@ struct DecodeArgs {
     int32_t* sel_pages;
     float* part;
     uint64_t* cand;
+    float* score;      // bf16: MFMA ranking scores [rows][Hq][score_stride]
+    int score_stride;
     int Hq, Hkv, G, TG, TP, W, n_sink;
     float scale;
     int slice, nslice, nwin, nslot;
@@ -410,6 +412,9 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 constexpr int kOpenBatch = 4;   // items per subgroup whose loads are issued together
+constexpr int kOpenCand = 128;  // canonical re-scoring candidates kept per head
+constexpr int kPartLds = 40;    // scan partial states per head copied to LDS (bf16 path)
+constexpr int kPartLdsFloats = (kPartLds * (kPartStride / 4) + 63) / 64 * 64 * 4;
 constexpr int kMetaMax = 320;   // int16 entries of one chunk's meta row (>= meta_stride)
 constexpr int kGPW = kMaxTG / 4;             // opened groups per wave (at most)
 constexpr int kItemsPerWave = kGPW * kChunk; // exact rows of a wave's groups (two-tier bound)
@@ -429,104 +434,65 @@ struct OpenSmem {
     float so[16][kD];
     float scan_m, scan_l;      // merged state of the scan workgroups' partials
     float scan_o[kD];
+    // selection from MFMA scores (bf16 path)
+    float wl[4][kMaxTG];       // per wave: its TG largest lower bounds
+    float thr;                 // TG-th largest lower bound of the head
+    int ncand, over;
+    int32_t cg[kOpenCand];     // candidates: group id, canonical score
+    float cs[kOpenCand];
+    uint64_t red[4];
+    float sub_lam[kMaxTG];     // opened groups' coarse logits in the scan (subtracted)
+    alignas(16) float plds[kPartLdsFloats];  // the scan partial states (bf16 path), when they fit
 };
 
-// One workgroup per (query row, query head).  Wave w handles opened groups w, w+4, ...:
-// all of its groups' meta rows, then all of their page rankings (one lane per (group,
-// page), 16-lane segmented top-k), then the item lists, so the dependent global round
-// trips are few.  Every 16-lane subgroup then streams items with its loads batched.
-// Losing candidates of the slices are added back as coarse terms, and the state is
-// merged with the scan workgroups' partial states into the final output.
+// Merge of the scan workgroups' partial states of one head by waves 2-3 (one dimension
+// per thread; loads issued 16 slots at a time) into s.scan_*.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
-    __shared__ OpenSmem<T> s;
-    const int hq = blockIdx.x, b = blockIdx.y;
-    const int HG = A.Hq / A.Hkv;
-    const int kvh = hq / HG;
+__device__ __forceinline__ void open_merge_scan(OpenSmem<T>& s, const float* part, int nscan) {
+    const int tid = threadIdx.x;
+    if (tid < 2 * 64) return;
+    const int d = tid - 128;
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int k0 = 0; k0 < nscan; k0 += 16) {
+        float mm[16], ll[16], oo[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int k = k0 + x;
+            mm[x] = -INFINITY;
+            if (k < nscan) {
+                const float* pp = part + (int64_t)k * kPartStride;
+                mm[x] = pp[kD];
+                ll[x] = pp[kD + 1];
+                oo[x] = pp[d];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            if (mm[x] == -INFINITY) continue;
+            const float mn = fmaxf(M, mm[x]);
+            const float a = softmax_exp(M - mn), e = softmax_exp(mm[x] - mn);
+            L = __builtin_fmaf(ll[x], e, L * a);
+            O = __builtin_fmaf(oo[x], e, O * a);
+            M = mn;
+        }
+    }
+    s.scan_o[d] = O;
+    if (d == 0) { s.scan_m = M; s.scan_l = L; }
+}
+
+// Pages of the opened groups s.sel[0..nsel) and the exact attention over them.  Wave w
+// handles opened groups w, w+4, ...: all of its groups' meta rows, then all of their
+// page rankings (one lane per (group, page), 16-lane segmented top-k), then the item
+// lists, so the dependent global round trips are few.  Every 16-lane subgroup then
+// streams items with its loads batched into its online-softmax state st.
+template <typename T, int OB>
+__device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int seq, int kvh, int64_t head,
+                           const float* q8, Online& st) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, sgw = lane >> 4;  // subgroup within the wave
-    int seq, p;
-    row_info(A, b, seq, p);
-    const int nb = nbuilt(p, A.W);
-    const int ng = nb * A.G;
+    const int l16 = lane & 15, sgw = lane >> 4;
     const int64_t unit = (int64_t)seq * A.Hkv + kvh;
     const int PS = A.L.page_slots;
     const int TPW = A.TP > 0 ? A.TP : 1;
-    const int64_t head = (int64_t)b * A.Hq + hq;
-    const T* qp = reinterpret_cast<const T*>(A.q) + head * kD;
-    if (tid < kD) s.qs[tid] = Elt<T>::to_f32(qp[tid]);
-    float q8[8];
-    load8<T>(qp, l16, q8);
-    const int nscan = A.nslice + A.nwin;
-    const float* part = A.part + head * A.nslot * kPartStride;
-    if (tid >= 2 * 64) {
-        // waves 2-3: merge the scan partial states (one dimension per thread), loads
-        // issued 16 slots at a time, while wave 0 merges the candidates
-        const int d = tid - 128;
-        float M = -INFINITY, L = 0.0f, O = 0.0f;
-        for (int k0 = 0; k0 < nscan; k0 += 16) {
-            float mm[16], ll[16], oo[16];
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int k = k0 + x;
-                mm[x] = -INFINITY;
-                if (k < nscan) {
-                    const float* pp = part + (int64_t)k * kPartStride;
-                    mm[x] = pp[kD];
-                    ll[x] = pp[kD + 1];
-                    oo[x] = pp[d];
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                if (mm[x] == -INFINITY) continue;
-                const float mn = fmaxf(M, mm[x]);
-                const float a = softmax_exp(M - mn), e = softmax_exp(mm[x] - mn);
-                L = __builtin_fmaf(ll[x], e, L * a);
-                O = __builtin_fmaf(oo[x], e, O * a);
-                M = mn;
-            }
-        }
-        s.scan_o[d] = O;
-        if (d == 0) { s.scan_m = M; s.scan_l = L; }
-    }
-
-    // 1. global top-k over the slices' candidates (wave 0)
-    const int nsl_used = ng > 0 ? (ng + A.slice - 1) / A.slice : 0;
-    const int ncand = nsl_used * A.TG;
-    const uint64_t* cand = A.cand + head * A.nslice * A.TG;
-    if (wave == 0) {
-        uint64_t lst[kMaxTG];
-#pragma unroll
-        for (int k = 0; k < kMaxTG; ++k) lst[k] = 0;
-        for (int k = lane; k < ncand; k += 64) {
-            uint64_t x = cand[k];
-#pragma unroll
-            for (int e = 0; e < kMaxTG; ++e) {
-                const uint64_t hi = lst[e] > x ? lst[e] : x;
-                const uint64_t lo = lst[e] > x ? x : lst[e];
-                lst[e] = hi;
-                x = lo;
-            }
-        }
-        int round = 0;
-        for (; round < A.TG; ++round) {
-            const uint64_t wb = wave_max_u64(lst[0]);
-            if (wb == 0) break;
-            if (lane == 0) s.sel[round] = wb;
-            if (lst[0] == wb) {
-#pragma unroll
-                for (int e = 0; e < kMaxTG - 1; ++e) lst[e] = lst[e + 1];
-                lst[kMaxTG - 1] = 0;
-            }
-        }
-        if (lane == 0) s.nsel = round;
-    }
-    __syncthreads();
-    const int nsel = s.nsel;
-    const uint64_t kth = nsel == A.TG ? s.sel[A.TG - 1] : 0;
-    if (A.sel_groups && tid < A.TG) A.sel_groups[head * A.TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
-
     const T* kb = reinterpret_cast<const T*>(A.k) + seq * A.sb + kvh * A.sh;
     const T* vb = reinterpret_cast<const T*>(A.v) + seq * A.sb + kvh * A.sh;
     const T* pk_u = reinterpret_cast<const T*>(A.index + A.L.pk) + unit * A.max_chunks * PS * kD;
@@ -534,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
     const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + unit * A.max_chunks * PS;
     const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + unit * A.max_chunks * A.L.meta_stride;
 
-    // 2a. meta rows of this wave's groups (all loads in flight together)
+    // meta rows of this wave's groups (all loads in flight together)
     const int ngw = (A.TG - wave + 3) / 4;  // group slots of this wave (k: group i = wave + 4k)
     const int ms16 = A.L.meta_stride / 8;   // 16-byte pieces per meta row
     for (int x = lane; x < ngw * ms16; x += 64) {
@@ -546,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
         }
     }
     wave_sync();
-    // 2b. page ranking: lane (k = lane/16, e = lane%16) scores page e of group i = wave+4k
+    // page ranking: lane (k = lane/16, e = lane%16) scores page e of group i = wave+4k
     {
         const int k = lane >> 4, e = lane & 15, i = wave + 4 * k;
         int c = 0, j = 0, ps0 = 0, npg = 0;
@@ -596,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
         }
         if (A.sel_pages && k < ngw && i < A.TG && e < TPW)
             A.sel_pages[(head * A.TG + i) * TPW + e] = i < nsel ? slot_of_rank : -1;
-        // 2c. item lists: unopened pages (coarse) and exact rows of opened pages
+        // item lists: unopened pages (coarse) and exact rows of opened pages
         const bool coarse = e < npg && rank < 0;
         const uint64_t cm = __ballot(coarse);
         if (coarse) {
@@ -622,14 +588,12 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
     }
     wave_sync();
 
-    Online st;
-    st.init();
-    // 3. exact rows of the wave's groups, then its coarse pages (subgroup sgw takes sgw, sgw+4, ...)
+    // exact rows of the wave's groups, then its coarse pages (subgroup sgw takes sgw, sgw+4, ...)
     const int nex = s.nex[wave];
-    for (int base = 0; base < nex; base += 4 * kOpenBatch) {
-        float kf[kOpenBatch][8], vf[kOpenBatch][8];
+    for (int base = 0; base < nex; base += 4 * OB) {
+        float kf[OB][8], vf[OB][8];
 #pragma unroll
-        for (int x = 0; x < kOpenBatch; ++x) {
+        for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < nex) {
                 const int pos = s.ex[wave][it];
@@ -638,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
             }
         }
 #pragma unroll
-        for (int x = 0; x < kOpenBatch; ++x) {
+        for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < nex) {
                 float a = 0.0f;
@@ -651,10 +615,10 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
         }
     }
     const int ncp = s.ncp[wave];
-    for (int base = 0; base < ncp; base += 4 * kOpenBatch) {
-        float vf[kOpenBatch][8];
+    for (int base = 0; base < ncp; base += 4 * OB) {
+        float vf[OB][8];
 #pragma unroll
-        for (int x = 0; x < kOpenBatch; ++x) {
+        for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < ncp) {
                 const int k = s.cp[wave][it] >> 8, e = s.cp[wave][it] & 255, i = wave + 4 * k;
@@ -664,13 +628,87 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
             }
         }
 #pragma unroll
-        for (int x = 0; x < kOpenBatch; ++x) {
+        for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < ncp) st.add(s.cl[wave][it], vf[x]);
         }
     }
+}
 
-    // 4. add back the coarse terms of candidates that lost the global ranking
+// Write the 16 subgroup states to LDS (before a barrier).
+template <typename T>
+__device__ __forceinline__ void open_stash(OpenSmem<T>& s, const Online& st) {
+    const int tid = threadIdx.x, l16 = tid & 15, sg = tid >> 4;
+    if (l16 == 0) { s.sm[sg] = st.m; s.sl[sg] = st.l; }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s.so[sg][8 * l16 + e] = st.o[e];
+}
+
+// One workgroup per (query row, query head) (fp32 path): the slices' local top-k
+// candidates are merged into the global top-k, the opened groups are attended through
+// their pages, losing candidates are added back as coarse terms, and the state is
+// merged with the scan workgroups' partial states into the final output.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
+    __shared__ OpenSmem<T> s;
+    const int hq = blockIdx.x, b = blockIdx.y;
+    const int HG = A.Hq / A.Hkv;
+    const int kvh = hq / HG;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, sgw = lane >> 4;
+    int seq, p;
+    row_info(A, b, seq, p);
+    const int nb = nbuilt(p, A.W);
+    const int ng = nb * A.G;
+    const int64_t unit = (int64_t)seq * A.Hkv + kvh;
+    const int64_t head = (int64_t)b * A.Hq + hq;
+    const T* qp = reinterpret_cast<const T*>(A.q) + head * kD;
+    if (tid < kD) s.qs[tid] = Elt<T>::to_f32(qp[tid]);
+    float q8[8];
+    load8<T>(qp, l16, q8);
+    open_merge_scan(s, A.part + head * A.nslot * kPartStride, A.nslice + A.nwin);
+
+    // 1. global top-k over the slices' candidates (wave 0)
+    const int nsl_used = ng > 0 ? (ng + A.slice - 1) / A.slice : 0;
+    const int ncand = nsl_used * A.TG;
+    const uint64_t* cand = A.cand + head * A.nslice * A.TG;
+    if (wave == 0) {
+        uint64_t lst[kMaxTG];
+#pragma unroll
+        for (int k = 0; k < kMaxTG; ++k) lst[k] = 0;
+        for (int k = lane; k < ncand; k += 64) {
+            uint64_t x = cand[k];
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) {
+                const uint64_t hi = lst[e] > x ? lst[e] : x;
+                const uint64_t lo = lst[e] > x ? x : lst[e];
+                lst[e] = hi;
+                x = lo;
+            }
+        }
+        int round = 0;
+        for (; round < A.TG; ++round) {
+            const uint64_t wb = wave_max_u64(lst[0]);
+            if (wb == 0) break;
+            if (lane == 0) s.sel[round] = wb;
+            if (lst[0] == wb) {
+#pragma unroll
+                for (int e = 0; e < kMaxTG - 1; ++e) lst[e] = lst[e + 1];
+                lst[kMaxTG - 1] = 0;
+            }
+        }
+        if (lane == 0) s.nsel = round;
+    }
+    __syncthreads();
+    const int nsel = s.nsel;
+    const uint64_t kth = nsel == A.TG ? s.sel[A.TG - 1] : 0;
+    if (A.sel_groups && tid < A.TG) A.sel_groups[head * A.TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
+
+    Online st;
+    st.init();
+    open_pages<T, kOpenBatch>(A, s, nsel, seq, kvh, head, q8, st);
+
+    // add back the coarse terms of candidates that lost the global ranking
     if (kth != 0) {
         const T* gv = reinterpret_cast<const T*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
         const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
@@ -696,11 +734,8 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
         }
     }
 
-    // 5. merge the 16 subgroup states with the merged scan state, normalise
-    const int sg = tid >> 4;
-    if (l16 == 0) { s.sm[sg] = st.m; s.sl[sg] = st.l; }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s.so[sg][8 * l16 + e] = st.o[e];
+    // merge the 16 subgroup states with the merged scan state, normalise
+    open_stash(s, st);
     __syncthreads();
     if (tid < kD) {
         float M = s.scan_m;
@@ -744,40 +779,19 @@ constexpr int kWinRows = 128;   // window rows per window workgroup (MFMA path)
 template <int HG>
 struct MSmem {
     union {
-        struct {
-            float sc[HG][kMRows];   // MFMA scores, then logits (-inf: excluded / empty)
-            float csc[HG][kMRows];  // canonical scores of candidates (NaN: not a candidate)
-        } a;
-        float ored[8 / ((HG + 3) / 4)][4 * ((HG + 3) / 4)][kD];  // PV row-phase sums
+        alignas(16) bf16_t vl[kMRows][kD];  // value rows of the tile, loaded straight into LDS
+        float ored[8 / ((HG + 3) / 4)][4 * ((HG + 3) / 4)][kD];  // PV row-phase sums (after the last PV)
     } u;
-    alignas(16) bf16_t vl[kMRows][kD];  // value rows of the chunk, loaded straight into LDS
+    float sc[HG][kMRows];             // MFMA scores of the tile
     alignas(16) float wT[kMRows][8];  // softmax weights, [row][head] (heads >= HG: 0)
-    alignas(16) float qs[HG][kD];
-    float qn[HG];
-    float kn[kMRows];
-    float lnn[kMRows];
+    float lnn[kMRows];                // ln n of the tile's groups
     float mrun[HG], lrun[HG], alpha[HG];
-    uint64_t ckey[HG][kMaxTG];
-    uint64_t ckl[HG][kMRows];  // per head: ranking keys of the candidates
-    int ncl;
-    uint16_t cl[HG * kMRows];  // canonical work list: head << 8 | row
 };
 
-// q of the g heads of this KV head: fp32 copy in LDS, |q| per head, MFMA A operand.
+// MFMA A operand of the g query heads of this KV head (rows >= g are zero).
 template <int HG>
-__device__ __forceinline__ void mfma_load_q(MSmem<HG>& s, const bf16_t* q0, bf16x8_t* qa) {
-    const int tid = threadIdx.x, l = tid & 63;
-    float ss = 0.0f;  // |q|^2 share: 16 threads per head, 8 values each
-    if (tid < HG * 16) {
-        const int h = tid >> 4, c = tid & 15;
-        float f[8];
-        Elt<bf16_t>::unpack(*reinterpret_cast<const uint4*>(q0 + h * kD + 8 * c), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            s.qs[h][8 * c + e] = f[e];
-            ss = __builtin_fmaf(f[e], f[e], ss);
-        }
-    }
+__device__ __forceinline__ void mfma_load_q(const bf16_t* q0, bf16x8_t* qa) {
+    const int l = threadIdx.x & 63;
     const int h = l & 15;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -788,10 +802,6 @@ __device__ __forceinline__ void mfma_load_q(MSmem<HG>& s, const bf16_t* q0, bf16
             for (int e = 0; e < 8; ++e) qa[kk][e] = (__bf16)0.0f;
         }
     }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    if (tid < HG * 16 && (tid & 15) == 0) s.qn[tid >> 4] = sqrtf(ss) * 1.0001f;
-    __syncthreads();
 }
 
 // Issue global->LDS loads of value rows r < n (n <= kMRows) into s.vl; completion is
@@ -802,7 +812,7 @@ __device__ __forceinline__ void mfma_issue_v(MSmem<HG>& s, RowPtr vrow, int n) {
     for (int i = w; 4 * i < n; i += 4) {
         int r = 4 * i + (l >> 4);
         r = r < n ? r : n - 1;
-        __builtin_amdgcn_global_load_lds(vrow(r) + 8 * (l & 15), &s.vl[4 * i][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vrow(r) + 8 * (l & 15), &s.u.vl[4 * i][0], 16, 0, 0);
     }
 }
 __device__ __forceinline__ void mfma_wait_lds() {
@@ -854,7 +864,7 @@ __device__ __forceinline__ void mfma_pv(MSmem<HG>& s, int n, float (*o)[4]) {
     const int tid = threadIdx.x;
     const int hq = tid / (32 * RPH), rp = (tid / 32) % RPH, db = tid & 31;
     for (int r = rp; r < n; r += RPH) {
-        const uint2 u = *reinterpret_cast<const uint2*>(&s.vl[r][4 * db]);
+        const uint2 u = *reinterpret_cast<const uint2*>(&s.u.vl[r][4 * db]);
         const float4 w4 = *reinterpret_cast<const float4*>(&s.wT[r][4 * hq]);
         const float v[4] = {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                             __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
@@ -905,14 +915,14 @@ __device__ void mfma_exact_rows(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* 
         auto krow = [&](int r) { return kb + (int64_t)pos(r) * st; };
         auto vrow = [&](int r) { return vb + (int64_t)pos(r) * st; };
         mfma_issue_v<HG>(s, vrow, n);
-        mfma_scores<HG>(s.u.a.sc, qa, krow, n);
+        mfma_scores<HG>(s.sc, qa, krow, n);
         __syncthreads();
         for (int h = w; h < HG; h += 4) {
             float lam[kMRows / 64], mx = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kMRows / 64; ++k) {
                 const int r = l + 64 * k;
-                lam[k] = r < n ? scale * s.u.a.sc[h][r] : -INFINITY;
+                lam[k] = r < n ? scale * s.sc[h][r] : -INFINITY;
                 mx = fmaxf(mx, lam[k]);
             }
             mx = wave_max_f32(mx, 64);
@@ -947,12 +957,74 @@ __device__ void mfma_exact_rows(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* 
     }
 }
 
+// Coarse terms of n groups (tiles of kMRows): MFMA scores S (written to sdst, row h at
+// sdst + h * sstride), logits scale * S + ln n (empty groups: none), online softmax and
+// PV into o.
+template <int HG>
+__device__ void mfma_coarse_groups(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* gk, const bf16_t* gv,
+                                   const float* gln, int n, float scale, float* sdst, int64_t sstride,
+                                   float (*o)[4]) {
+    constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int hq = tid / (32 * RPH);
+    for (int c0 = 0; c0 < n; c0 += kMRows) {
+        const int nt = min(kMRows, n - c0);
+        if (tid < nt) s.lnn[tid] = gln[c0 + tid];
+        auto krow = [&](int r) { return gk + (int64_t)(c0 + r) * kD; };
+        auto vrow = [&](int r) { return gv + (int64_t)(c0 + r) * kD; };
+        mfma_issue_v<HG>(s, vrow, nt);
+        mfma_scores<HG>(s.sc, qa, krow, nt);
+        __syncthreads();
+        for (int x = tid; x < HG * nt; x += kThreads) {
+            const int h = x / nt, r = x % nt;
+            sdst[(int64_t)h * sstride + c0 + r] = s.sc[h][r];
+        }
+        for (int h = w; h < HG; h += 4) {
+            float lam[kMRows / 64], mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kMRows / 64; ++k) {
+                const int r = l + 64 * k;
+                // the same expression the open kernel uses for the opened groups it subtracts
+                lam[k] = (r < nt && s.lnn[r] != -INFINITY) ? scale * s.sc[h][r] + s.lnn[r] : -INFINITY;
+                mx = fmaxf(mx, lam[k]);
+            }
+            mx = wave_max_f32(mx, 64);
+            const float mold = s.mrun[h];
+            const float mn = fmaxf(mold, mx);
+            float ls = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kMRows / 64; ++k) {
+                const int r = l + 64 * k;
+                const float wgt = lam[k] == -INFINITY ? 0.0f : softmax_exp(lam[k] - mn);
+                if (r < nt) s.wT[r][h] = wgt;
+                ls += wgt;
+            }
+            ls = wave_sum_f32(ls, 64);
+            if (l == 0) {
+                const float a = mold == -INFINITY ? 0.0f : softmax_exp(mold - mn);
+                s.alpha[h] = a;
+                s.lrun[h] = s.lrun[h] * a + ls;
+                s.mrun[h] = mn;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = (4 * hq + i < HG) ? s.alpha[4 * hq + i] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[i][e] *= a;
+        }
+        mfma_wait_lds();
+        mfma_pv<HG>(s, nt, o);
+        __syncthreads();
+    }
+}
+
 template <int HG>
 __device__ __forceinline__ void mfma_init(MSmem<HG>& s, float (*o)[4]) {
     const int tid = threadIdx.x;
     if (tid < HG) { s.mrun[tid] = -INFINITY; s.lrun[tid] = 0.0f; s.alpha[tid] = 0.0f; }
     for (int x = tid; x < kMRows * 8; x += kThreads) (&s.wT[0][0])[x] = 0.0f;
-    if (tid == 0) s.ncl = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -978,7 +1050,8 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     float o[4][4];
     mfma_init<HG>(s, o);
     bf16x8_t qa[4];
-    mfma_load_q<HG>(s, q0, qa);
+    mfma_load_q<HG>(q0, qa);
+    __syncthreads();
 
     if ((int)blockIdx.x >= A.nslice) {
         // ---------------- window tile (block 0 also takes the sinks)
@@ -996,151 +1069,293 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
         return;
     }
 
-    // ---------------- slice of group summaries
+    // ---------------- slice of group summaries: MFMA scores (written out for the
+    // selection) and the coarse softmax over every non-empty group of the slice
     const int g0 = blockIdx.x * A.slice;
     const int n = min(A.slice, ng - g0);
-    uint64_t* cand = A.cand + ((int64_t)(b * A.Hq + hq0) * A.nslice + blockIdx.x) * A.TG;
-    const int64_t cand_head_stride = (int64_t)A.nslice * A.TG;
-    if (n <= 0) {
+    if (n > 0) {
+        const int64_t gbase = unit * A.max_chunks * A.G + g0;
+        mfma_coarse_groups<HG>(s, qa, reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD,
+                               reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD,
+                               reinterpret_cast<const float*>(A.index + A.L.gln) + gbase, n, A.scale,
+                               A.score + ((int64_t)b * A.Hq + hq0) * A.score_stride + g0, A.score_stride, o);
+    } else {
         __syncthreads();
-        for (int e = tid; e < HG * A.TG; e += kThreads) cand[(e / A.TG) * cand_head_stride + e % A.TG] = 0;
-        mfma_write_partial<HG>(s, o, part0, head_stride);
-        return;
     }
-    const int64_t gbase = unit * A.max_chunks * A.G + g0;
-    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
-    const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
-    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
-    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + gbase;
-    if (tid < n) { s.lnn[tid] = gln[tid]; s.kn[tid] = gkn[tid]; }
-    auto krow = [&](int r) { return gk + (int64_t)r * kD; };
-    auto vrow = [&](int r) { return gv + (int64_t)r * kD; };
-    mfma_issue_v<HG>(s, vrow, n);
-    mfma_scores<HG>(s.u.a.sc, qa, krow, n);
-    __syncthreads();
-
-    // 1. candidates of the local top-k of each head (one wave per head)
-    for (int h = w; h < HG; h += 4) {
-        constexpr int RL = kMRows / 64;  // rows per lane
-        float ub[RL];
-        uint32_t okey[RL];  // orderable bits of the lower bound, 0 = not a valid group
-        const float qn = s.qn[h];
-#pragma unroll
-        for (int k = 0; k < RL; ++k) {
-            const int r = l + 64 * k;
-            const bool valid = r < n && s.lnn[r] != -INFINITY;
-            const float E = kErrC * qn * (r < n ? s.kn[r] : 0.0f);
-            const float sv = r < n ? s.u.a.sc[h][r] : 0.0f;
-            ub[k] = valid ? sv + E : -INFINITY;
-            const float lbv = sv - E;
-            const uint32_t u = __float_as_uint(lbv == 0.0f ? 0.0f : lbv);
-            okey[k] = valid ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
-        }
-        // T = TG-th largest lower bound (with multiplicity): the largest v such that at
-        // least TG keys are >= v, built bit by bit from the top; -inf if fewer than TG.
-        uint32_t prefix = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t tryv = prefix | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int k = 0; k < RL; ++k) cnt += __popcll(__ballot(okey[k] >= tryv));
-            if (cnt >= A.TG) prefix = tryv;
-        }
-        float T = -INFINITY;
-        if (prefix != 0) {
-            const uint32_t u = (prefix & 0x80000000u) ? (prefix & 0x7fffffffu) : ~prefix;
-            T = __uint_as_float(u);
-        }
-#pragma unroll
-        for (int k = 0; k < kMRows / 64; ++k) {
-            const int r = l + 64 * k;
-            const bool c = ub[k] != -INFINITY && ub[k] >= T;
-            if (r < kMRows) s.u.a.csc[h][r] = c ? 0.0f : __builtin_nanf("");
-            const uint64_t mask = __ballot(c);
-            int basep = 0;
-            if (l == 0 && mask) basep = atomicAdd(&s.ncl, __popcll(mask));
-            basep = __shfl(basep, 0, 64);
-            if (c) {
-                const int slot = basep + __popcll(mask & ((1ull << l) - 1ull));
-                s.cl[slot] = (uint16_t)((h << 8) | r);
-            }
-        }
-    }
-    __syncthreads();
-    // 2. canonical fp32 chains for the candidates
-    const int ncl = s.ncl;
-    for (int x = tid; x < ncl; x += kThreads) {
-        const int h = s.cl[x] >> 8, r = s.cl[x] & 255;
-        const bf16_t* row = krow(r);
-        uint4 u[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) u[c] = *reinterpret_cast<const uint4*>(row + 8 * c);
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            float f[8];
-            Elt<bf16_t>::unpack(u[c], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(s.qs[h][8 * c + e], f[e], acc);
-        }
-        s.u.a.csc[h][r] = acc;
-    }
-    __syncthreads();
-    // 3. exact local top-k among the candidates (rank = number of larger keys); the
-    //    winners leave the coarse sum
-    for (int h = w; h < HG; h += 4) {
-        constexpr int RL = kMRows / 64;
-        uint64_t key[RL];
-        int nc = 0;
-#pragma unroll
-        for (int k = 0; k < RL; ++k) {
-            const int r = l + 64 * k;
-            const float c = r < n ? s.u.a.csc[h][r] : __builtin_nanf("");
-            key[k] = (c == c) ? rank_key(c, (uint32_t)(g0 + r)) : 0;
-            const uint64_t mask = __ballot(key[k] != 0);
-            if (key[k] != 0) s.ckl[h][nc + __popcll(mask & ((1ull << l) - 1ull))] = key[k];
-            nc += __popcll(mask);
-        }
-        wave_sync();
-#pragma unroll
-        for (int k = 0; k < RL; ++k) {
-            if (key[k] == 0) continue;
-            int rank = 0;
-            for (int x = 0; x < nc; ++x) rank += s.ckl[h][x] > key[k];
-            if (rank < A.TG) {
-                s.ckey[h][rank] = key[k];
-                s.u.a.sc[h][l + 64 * k] = -INFINITY;
-            }
-        }
-        if (l >= nc && l < A.TG) s.ckey[h][l] = 0;
-        // coarse logits of this head: scale * S + ln n (excluded and empty groups: -inf)
-        float lam[kMRows / 64], mx = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < kMRows / 64; ++k) {
-            const int r = l + 64 * k;
-            const float sv = r < n ? s.u.a.sc[h][r] : -INFINITY;
-            lam[k] = (r < n && sv != -INFINITY && s.lnn[r] != -INFINITY) ? A.scale * sv + s.lnn[r] : -INFINITY;
-            mx = fmaxf(mx, lam[k]);
-        }
-        mx = wave_max_f32(mx, 64);
-        float ls = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kMRows / 64; ++k) {
-            const int r = l + 64 * k;
-            const float wgt = lam[k] == -INFINITY ? 0.0f : softmax_exp(lam[k] - mx);
-            if (r < n) s.wT[r][h] = wgt;
-            ls += wgt;
-        }
-        ls = wave_sum_f32(ls, 64);
-        if (l == 0) { s.mrun[h] = mx; s.lrun[h] = ls; }
-    }
-    __syncthreads();
-    for (int e = tid; e < HG * A.TG; e += kThreads)
-        cand[(e / A.TG) * cand_head_stride + e % A.TG] = s.ckey[e / A.TG][e % A.TG];
-    // 4. PV of the coarse terms
-    mfma_wait_lds();
-    mfma_pv<HG>(s, n, o);
     mfma_write_partial<HG>(s, o, part0, head_stride);
+}
+
+// ---------------------------------------------------------------------------- open (bf16)
+
+// Opened groups from the stored MFMA scores S of every group of the head.  With
+// E_g = kErrC |q| |kbar_g| bounding |S_g - r_g| (r: canonical chain), the exact top-k by
+// r lies in {g : S_g + E_g >= T}, T being the k-th largest S_g - E_g; those candidates
+// are re-scored canonically and ranked exactly (score desc, id asc).  Columns with more
+// candidates than kOpenCand (massive ties) rank every group canonically.
+// Head mapping: consecutive workgroups take different KV heads, so the query heads of
+// one KV head share an XCD and its L2 (workgroups are dealt to the 8 XCDs round robin).
+// The scan included the opened groups in its coarse sums; their terms, with the very
+// same logits, are subtracted in the final merge.  The subtracted mass never exceeds
+// the scan's, and the exact terms of the opened pages carry at least the same order of
+// mass, so fp32 cancellation stays near 1e-6 of the output scale.
+__global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A) {
+    __shared__ OpenSmem<bf16_t> s;
+    const int b = blockIdx.y;
+    const int HG = A.Hq / A.Hkv;
+    const int hq = (blockIdx.x % A.Hkv) * HG + blockIdx.x / A.Hkv;
+    const int kvh = hq / HG;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15;
+    int seq, p;
+    row_info(A, b, seq, p);
+    const int nb = nbuilt(p, A.W);
+    const int ng = nb * A.G;
+    const int TG = A.TG;
+    const int64_t unit = (int64_t)seq * A.Hkv + kvh;
+    const int64_t head = (int64_t)b * A.Hq + hq;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.q) + head * kD;
+    if (tid < kD) s.qs[tid] = bf16_bits_to_f32(qp[tid]);
+    float q8[8];
+    load8<bf16_t>(qp, l16, q8);
+    // |q| (16 lanes, 8 values each), rounded up
+    float qn = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qn = __builtin_fmaf(q8[e], q8[e], qn);
+    qn = sqrtf(wave_sum_f32(qn, 16)) * 1.0001f;
+    // scan partial states: straight into LDS (awaited before the final merge), else
+    // merged from global memory by waves 2-3
+    const int nscan = A.nslice + A.nwin;
+    const float* part = A.part + head * A.nslot * kPartStride;
+    const bool part_in_lds = nscan <= kPartLds;
+    if (part_in_lds) {
+        const int npiece = nscan * (kPartStride / 4);  // 16-byte pieces
+        for (int i = wave; 64 * i < npiece; i += 4) {
+            const int pc = min(64 * i + lane, npiece - 1);
+            __builtin_amdgcn_global_load_lds(part + 4 * pc, &s.plds[256 * i], 16, 0, 0);
+        }
+    } else {
+        open_merge_scan(s, part, nscan);
+    }
+
+    const float* S = A.score + head * A.score_stride;
+    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + unit * A.max_chunks * A.G;
+    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
+    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + unit * A.max_chunks * A.G * kD;
+    const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
+    const float eq = kErrC * qn;
+
+    // 1a. every thread: its largest lower bounds S - E (sorted insertion); groups are
+    //     read SPT per thread at a time, all loads in flight together
+    constexpr int SPT = 16;
+    float sv[SPT], kn[SPT], ln[SPT];
+    auto load_scores = [&](int g0) {
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int g = g0 + tid + kThreads * u;
+            ln[u] = -INFINITY;
+            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; ln[u] = gln[g]; }
+        }
+    };
+    float lst[kMaxTG];
+#pragma unroll
+    for (int e = 0; e < kMaxTG; ++e) lst[e] = -INFINITY;
+    for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
+        load_scores(g0);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            float x = ln[u] != -INFINITY ? sv[u] - eq * kn[u] : -INFINITY;
+            if (x > lst[kMaxTG - 1]) {
+#pragma unroll
+                for (int e = 0; e < kMaxTG; ++e) {
+                    const float hi = fmaxf(lst[e], x), lo = fminf(lst[e], x);
+                    lst[e] = hi;
+                    x = lo;
+                }
+            }
+        }
+    }
+    // 1b. each wave: its TG largest (with multiplicity)
+    {
+        int taken = 0;
+        for (int round = 0; round < TG && taken < TG; ++round) {
+            const float m = wave_max_f32(lst[0], 64);
+            if (m == -INFINITY) break;
+            const bool mine = lst[0] == m;
+            const int c = __popcll(__ballot(mine));
+            if (lane == 0)
+                for (int x = 0; x < c && taken + x < TG; ++x) s.wl[wave][taken + x] = m;
+            taken += c;
+            if (mine) {
+#pragma unroll
+                for (int e = 0; e < kMaxTG - 1; ++e) lst[e] = lst[e + 1];
+                lst[kMaxTG - 1] = -INFINITY;
+            }
+        }
+        if (lane == 0)
+            for (int x = taken; x < TG; ++x) s.wl[wave][x] = -INFINITY;
+    }
+    if (tid == 0) { s.ncand = 0; s.over = 0; }
+    __syncthreads();
+    // 1c. T = the TG-th largest over the four lists (-inf if fewer than TG groups)
+    if (wave == 0) {
+        const int nv = 4 * TG;
+        const float v = lane < nv ? s.wl[lane / TG][lane % TG] : -INFINITY;
+        int cge = 0;
+        for (int x = 0; x < nv; ++x) cge += s.wl[x / TG][x % TG] >= v;
+        const float T = wave_max_f32((v != -INFINITY && cge >= TG) ? v : -INFINITY, 64);
+        if (lane == 0) s.thr = T;
+    }
+    __syncthreads();
+    // 1d. candidates: S + E >= T (a single block of groups is still in registers)
+    {
+        const float T = s.thr;
+        for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
+            if (ng > SPT * kThreads) load_scores(g0);
+#pragma unroll
+            for (int u = 0; u < SPT; ++u) {
+                const int g = g0 + tid + kThreads * u;
+                const bool c = ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T;
+                const uint64_t mk = __ballot(c);
+                int base = 0;
+                if (lane == 0 && mk) base = atomicAdd(&s.ncand, __popcll(mk));
+                base = __shfl(base, 0, 64);
+                if (c) {
+                    const int at = base + __popcll(mk & ((1ull << lane) - 1ull));
+                    if (at < kOpenCand) s.cg[at] = g;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int ncand = s.ncand;
+    if (ncand <= kOpenCand) {
+        for (int x = tid; x < ncand; x += kThreads) {
+            const bf16_t* row = gk + (int64_t)s.cg[x] * kD;
+            uint4 u[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) u[c] = *reinterpret_cast<const uint4*>(row + 8 * c);
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                float f[8];
+                Elt<bf16_t>::unpack(u[c], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(s.qs[8 * c + e], f[e], acc);
+            }
+            s.cs[x] = acc;
+        }
+        __syncthreads();
+        for (int x = tid; x < ncand; x += kThreads) {
+            const uint64_t key = rank_key(s.cs[x], (uint32_t)s.cg[x]);
+            int rank = 0;
+            for (int y = 0; y < ncand; ++y) rank += rank_key(s.cs[y], (uint32_t)s.cg[y]) > key;
+            if (rank < TG) s.sel[rank] = key;
+        }
+        if (tid == 0) s.nsel = ncand < TG ? ncand : TG;
+    } else {
+        // exhaustive: canonical score of every non-empty group, workgroup-wide top-TG
+        uint64_t top[kMaxTG];
+#pragma unroll
+        for (int e = 0; e < kMaxTG; ++e) top[e] = 0;
+        for (int g = tid; g < ng; g += kThreads) {
+            if (gln[g] == -INFINITY) continue;
+            const bf16_t* row = gk + (int64_t)g * kD;
+            float acc = 0.0f;
+            for (int c = 0; c < 16; ++c) {
+                float f[8];
+                Elt<bf16_t>::unpack(*reinterpret_cast<const uint4*>(row + 8 * c), f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(s.qs[8 * c + e], f[e], acc);
+            }
+            uint64_t x = rank_key(acc, (uint32_t)g);
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) {
+                const uint64_t hi = top[e] > x ? top[e] : x, lo = top[e] > x ? x : top[e];
+                top[e] = hi;
+                x = lo;
+            }
+        }
+        int k = 0;
+        for (int round = 0; round < TG; ++round) {
+            const uint64_t wm = wave_max_u64(top[0]);
+            if (lane == 0) s.red[wave] = wm;
+            __syncthreads();
+            uint64_t m = s.red[0];
+            for (int x = 1; x < 4; ++x) m = s.red[x] > m ? s.red[x] : m;
+            __syncthreads();
+            if (m == 0) break;
+            if (tid == 0) s.sel[round] = m;
+            if (top[0] == m) {
+#pragma unroll
+                for (int e = 0; e < kMaxTG - 1; ++e) top[e] = top[e + 1];
+                top[kMaxTG - 1] = 0;
+            }
+            ++k;
+        }
+        if (tid == 0) s.nsel = k;
+    }
+    __syncthreads();
+    const int nsel = s.nsel;
+    if (A.sel_groups && tid < TG) A.sel_groups[head * TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
+    // opened groups' logits as the scan computed them, and their mean values (loads in
+    // flight during the page work)
+    if (tid < nsel) {
+        const uint32_t g = key_id(s.sel[tid]);
+        s.sub_lam[tid] = A.scale * S[g] + gln[g];
+    }
+    float vsub[kMaxTG];
+    if (tid < kD) {
+#pragma unroll
+        for (int i = 0; i < kMaxTG; ++i)
+            vsub[i] = i < nsel ? bf16_bits_to_f32(gv[(int64_t)key_id(s.sel[i]) * kD + tid]) : 0.0f;
+    }
+
+    Online st;
+    st.init();
+    open_pages<bf16_t, 2 * kOpenBatch>(A, s, nsel, seq, kvh, head, q8, st);
+    open_stash(s, st);
+    if (part_in_lds) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (part_in_lds && tid < kD) {
+        float M = -INFINITY, L = 0.0f, O = 0.0f;
+        for (int k = 0; k < nscan; ++k) {
+            const float* pp = &s.plds[k * kPartStride];
+            const float mk = pp[kD];
+            if (mk == -INFINITY) continue;
+            const float mn = fmaxf(M, mk);
+            const float a = softmax_exp(M - mn), e = softmax_exp(mk - mn);
+            L = __builtin_fmaf(pp[kD + 1], e, L * a);
+            O = __builtin_fmaf(pp[tid], e, O * a);
+            M = mn;
+        }
+        s.scan_o[tid] = O;
+        if (tid == 0) { s.scan_m = M; s.scan_l = L; }
+    }
+    if (part_in_lds) __syncthreads();
+    if (tid < kD) {
+        float M = s.scan_m;
+        for (int k = 0; k < 16; ++k) M = fmaxf(M, s.sm[k]);
+        float L = 0.0f, O = 0.0f;
+        if (s.scan_m != -INFINITY) {
+            const float e = softmax_exp(s.scan_m - M);
+            L = s.scan_l * e;
+            O = s.scan_o[tid] * e;
+#pragma unroll
+            for (int i = 0; i < kMaxTG; ++i) {
+                if (i >= nsel) break;
+                const float w = softmax_exp(s.sub_lam[i] - M);
+                L -= w;
+                O = __builtin_fmaf(-w, vsub[i], O);
+            }
+        }
+        for (int k = 0; k < 16; ++k) {
+            if (s.sm[k] == -INFINITY) continue;
+            const float e = softmax_exp(s.sm[k] - M);
+            L = __builtin_fmaf(s.sl[k], e, L);
+            O = __builtin_fmaf(s.so[k][tid], e, O);
+        }
+        A.out[head * kD + tid] = O / L;
+    }
 }
 
 // Dense decode (bf16): split workgroups over rows, MFMA scores, online softmax.
@@ -1161,7 +1376,7 @@ __global__ __launch_bounds__(kThreads) void dense_decode_mfma_kernel(DenseArgs A
     float o[4][4];
     mfma_init<HG>(s, o);
     bf16x8_t qa[4];
-    mfma_load_q<HG>(s, q0, qa);
+    mfma_load_q<HG>(q0, qa);
     __syncthreads();
     const int r0 = blockIdx.x * A.rows_per_wg;
     const int r1 = min(r0 + A.rows_per_wg, p + 1);
@@ -1256,7 +1471,10 @@ static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
                                dim3(kThreads), 0, st, A);
     }
     trace_point(1, st);
-    hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL(decode_open_mfma_kernel, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+    else
+        hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
     trace_point(2, st);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
@@ -1321,6 +1539,8 @@ static void fill_decode_args(DecodeArgs& A, const lod_params* params, const lod_
     A.max_chunks = index->max_chunks;
     A.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + P.off_part);
     A.cand = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + P.off_cand);
+    A.score = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + P.off_score);
+    A.score_stride = P.score_stride;
     A.Hq = params->n_q_heads; A.Hkv = params->n_kv_heads; A.G = params->groups_per_chunk;
     A.TG = params->top_groups; A.TP = params->top_pages; A.W = params->window;
     A.n_sink = params->n_sink; A.scale = params->scale;

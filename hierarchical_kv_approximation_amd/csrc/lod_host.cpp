@@ -53,25 +53,37 @@ DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len) 
     const int nb = built_chunks(p, (int64_t)max_seq_len - 1);
     const int64_t ng = (int64_t)nb * p->groups_per_chunk;
     const int64_t units = (int64_t)batch * p->n_kv_heads;
-    // Aim for about 512 slice workgroups (two per CU) over the whole batch.
-    int64_t want = ceil_div(512, units);
-    int64_t slice = ceil_div(ng > 0 ? ng : 1, want);
-    slice = ceil_div(slice, kTile) * kTile;
-    if (slice < kTile) slice = kTile;
-    // bf16 slices are one MFMA chunk (128 rows, value rows staged in LDS); fp32 up to 256
-    const int64_t cap = p->kv_dtype == LOD_BF16 ? 2 * kTile : 4 * kTile;
-    if (slice > cap) slice = cap;
-    P.slice = (int)slice;
-    P.nslice = ng > 0 ? (int)ceil_div(ng, slice) : 0;
-    // window workgroups: bf16 (MFMA) takes 128-row tiles with the sinks in the first one;
-    // fp32 takes a sinks workgroup, then 64-row tiles
-    P.nwin = p->kv_dtype == LOD_BF16 ? (int)ceil_div(p->window, 128) : 1 + (int)ceil_div(p->window, kTile);
+    if (p->kv_dtype == LOD_BF16) {
+        // MFMA path: window workgroups take 128-row tiles (sinks in the first); a slice
+        // workgroup streams tiles of 128 groups.  Aim for about 768 workgroups (three per
+        // CU) over the whole batch.
+        P.nwin = (int)ceil_div(p->window, 128);
+        int64_t want = ceil_div(768, units) - P.nwin;
+        if (want < 1) want = 1;
+        int64_t slice = ceil_div(ng > 0 ? ng : 1, want);
+        slice = ceil_div(slice, 2 * kTile) * 2 * kTile;
+        P.slice = (int)slice;
+    } else {
+        // VALU path: about 512 slice workgroups of up to 256 groups, then a sinks
+        // workgroup and 64-row window tiles
+        int64_t want = ceil_div(512, units);
+        int64_t slice = ceil_div(ng > 0 ? ng : 1, want);
+        slice = ceil_div(slice, kTile) * kTile;
+        if (slice < kTile) slice = kTile;
+        if (slice > 4 * kTile) slice = 4 * kTile;
+        P.slice = (int)slice;
+        P.nwin = 1 + (int)ceil_div(p->window, kTile);
+    }
+    P.nslice = ng > 0 ? (int)ceil_div(ng, P.slice) : 0;
     P.nslot = P.nslice + P.nwin;
     const size_t heads = (size_t)batch * p->n_q_heads;
     P.off_part = 0;
     P.off_cand = align256(heads * P.nslot * kPartStride * sizeof(float));
-    P.bytes = align256(P.off_cand + heads * (size_t)(P.nslice > 0 ? P.nslice : 1) *
-                                        p->top_groups * sizeof(uint64_t));
+    P.off_score = align256(P.off_cand + heads * (size_t)(P.nslice > 0 ? P.nslice : 1) *
+                                            p->top_groups * sizeof(uint64_t));
+    // bf16: MFMA ranking score of every group for every query head
+    P.score_stride = (int)(ng > 0 ? ceil_div(ng, 64) * 64 : 64);
+    P.bytes = align256(P.off_score + (p->kv_dtype == LOD_BF16 ? heads * (size_t)P.score_stride * 4 : 0));
     return P;
 }
 

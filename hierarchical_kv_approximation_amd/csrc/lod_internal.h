@@ -47,7 +47,8 @@ struct DecodePlan {
     int nslice;     // slice workgroups per (sequence, KV head)
     int nwin;       // window workgroups per (sequence, KV head): sinks + window tiles
     int nslot;      // partial softmax states per (sequence, query head)
-    size_t off_part, off_cand, bytes;
+    int score_stride;  // bf16: stored MFMA scores per (sequence, query head)
+    size_t off_part, off_cand, off_score, bytes;
 };
 DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len);
 
