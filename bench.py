@@ -11,9 +11,10 @@ values N(0, 1), queries matched to the mixture (all seeded, synthetic).
 A step is one lod_attend_decode call: one decode token for every sequence of the batch
 through one attention layer.  Steps rotate over `--layers` independent layer copies
 (cache + index) so the 256 MB Infinity Cache cannot serve a layer's reads from the
-previous step.  Positions advance by one every `--layers` steps and the timed steps
-cross a chunk boundary, so the timed region includes the lod_build_chunk call that the
-boundary requires for each layer (the build-during-decode step of the method).
+previous step.  Positions advance by one every `--layers` steps; by default each layer
+decodes 256 positions that straddle a chunk boundary, so the timed region includes the
+one lod_build_chunk call per layer that the boundary requires (the build-during-decode
+step of the method) at its real rate of once per 256 tokens.
 """
 from __future__ import annotations
 
@@ -93,10 +94,13 @@ def cpu_threads() -> int:
 
 
 def algorithmic_decode_bytes(cfg, index, sel_g, sel_p, seq_lens, elt):
-    """Bytes the method itself must move for one decode call (per the design notes):
-    group summaries (k, v, ln n) of every summarised chunk; page summaries of opened
-    groups; K/V rows of the union of opened pages over the query heads of a KV head; the
-    exact window and sinks; q and the fp32 output."""
+    """Bytes the method itself must move for one decode call, split by launch.
+
+    scores: the mean keys of every summarised chunk (and q).
+    coarse: mean values and ln n of every summarised chunk; the exact window and sinks.
+    open:   page summaries of the opened groups; K/V rows of the union of opened pages
+            over the query heads of a KV head.
+    Returns (total, scores, coarse, open); output and workspace traffic is not counted."""
     import numpy as np
     d, G, C, W, S = cfg.head_dim, cfg.groups, cfg.chunk_size, cfg.window, cfg.n_sink
     Hq, Hkv = cfg.n_q_heads, cfg.n_kv_heads
@@ -105,15 +109,13 @@ def algorithmic_decode_bytes(cfg, index, sel_g, sel_p, seq_lens, elt):
     meta = index.arrays()["meta"].cpu().numpy().astype(np.int64)
     sg, sp = sel_g.cpu().numpy(), sel_p.cpu().numpy()
     PS = cfg.page_slots
-    total = scan = 0
+    scores = coarse = opened_b = 0
     for b, T in enumerate(seq_lens):
         p = T - 1
         nb = max(0, p // C - W // C + 1)
         tail = p - nb * C + 1
         sinks = min(S, nb * C)
         for kvh in range(Hkv):
-            grp = nb * G * (row + 4)
-            exact = (tail + sinks) * row
             opened, rows = set(), set()
             for h in range(kvh * g, (kvh + 1) * g):
                 for i, gid in enumerate(sg[b, h]):
@@ -131,18 +133,18 @@ def algorithmic_decode_bytes(cfg, index, sel_g, sel_p, seq_lens, elt):
             for c, j in opened:
                 gpg = meta[b, kvh, c][: G + 1]
                 pages += int(gpg[j + 1] - gpg[j])
-            total += grp + exact + pages * (row + 4) + len(rows) * (row + 4)
-            scan += grp + exact
-        total += Hq * d * (elt + 4)
-        scan += Hq * d * elt
-    return int(total), int(scan)
+            scores += nb * G * d * elt
+            coarse += nb * G * (d * elt + 4) + (tail + sinks) * row
+            opened_b += pages * (row + 4) + len(rows) * row
+        scores += Hq * d * elt
+    return int(scores + coarse + opened_b), int(scores), int(coarse), int(opened_b)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=131072)
     ap.add_argument("--layers", type=int, default=4)
@@ -207,7 +209,8 @@ def main():
     torch.cuda.synchronize()
 
     # timed region
-    ev = hip.create(3 * K)
+    NE = 3  # trace events per call: before the scan, after the scan, after the open step
+    ev = hip.create(NE * K)
     bev = hip.create(2 * L)
     t0, t1 = hip.create(2)
     nbuilt = 0
@@ -221,16 +224,16 @@ def main():
             hip.record(bev[2 * nbuilt + 1], stream)
             Ly["built"] = True
             nbuilt += 1
-        keep = lod.trace_events(ev[3 * k: 3 * k + 3])
+        keep = lod.trace_events(ev[NE * k: NE * k + NE])
         lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[pi], max_len, ws=ws, out=out)
         lod.trace_events(None)
         del keep
     hip.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = hip.ms(t0, t1)
-    scan_ms = [hip.ms(ev[3 * k], ev[3 * k + 1]) for k in range(K)]
-    open_ms = [hip.ms(ev[3 * k + 1], ev[3 * k + 2]) for k in range(K)]
-    call_ms = [hip.ms(ev[3 * k], ev[3 * k + 2]) for k in range(K)]
+    scan_ms = [hip.ms(ev[NE * k], ev[NE * k + 1]) for k in range(K)]
+    open_ms = [hip.ms(ev[NE * k + 1], ev[NE * k + 2]) for k in range(K)]
+    call_ms = [hip.ms(ev[NE * k], ev[NE * k + 2]) for k in range(K)]
     build_ms = [hip.ms(bev[2 * i], bev[2 * i + 1]) for i in range(nbuilt)]
     hip.destroy(ev + bev + [t0, t1])
     ms_per_step = total_ms / K
@@ -243,8 +246,13 @@ def main():
                                    want_selection=True)
     torch.cuda.synchronize()
     lens = [int(x) for x in last.cpu()]
-    bytes_call, bytes_scan = algorithmic_decode_bytes(cfg, Ly["index"], sg, sp, lens, elt)
-    scan_avg = sum(scan_ms) / K
+    bytes_call, bytes_scores, bytes_coarse, bytes_open = algorithmic_decode_bytes(cfg, Ly["index"], sg, sp,
+                                                                                 lens, elt)
+    scan_avg, open_avg = sum(scan_ms) / K, sum(open_ms) / K
+    bytes_scan = bytes_scores + bytes_coarse
+    # the dominant launch: the scan (HBM bound; the open step is latency bound)
+    dom = ("decode_scan_mfma_kernel (mean keys and values of every summarised chunk, exact window and sinks)",
+           scan_avg, bytes_scan, "decode_scan_traffic")
     call_avg = sum(call_ms) / K
 
     # dense decode on the same inputs (same rotation, same positions)
@@ -310,20 +318,21 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_scan_kernel (group-summary stream + window tiles)",
-            "achieved": round(bytes_scan / (scan_avg * 1e-3) / 1e9, 1),
+            "kernel": dom[0],
+            "achieved": round(dom[2] / (dom[1] * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(bytes_scan / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": profiled_traffic("decode_scan_traffic"),
-            "algorithmic_bytes_per_launch": bytes_scan,
-            "avg_launch_us": round(scan_avg * 1000, 2),
+            "frac": round(dom[2] / (dom[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": profiled_traffic(dom[3]),
+            "algorithmic_bytes_per_launch": dom[2],
+            "avg_launch_us": round(dom[1] * 1000, 2),
         },
         "cpu_baseline": cpu,
         "extra": {
             "lod_call_us": round(call_avg * 1000, 2),
             "scan_us": round(scan_avg * 1000, 2),
-            "open_combine_us": round(sum(open_ms) / K * 1000, 2),
+            "open_us": round(open_avg * 1000, 2),
+            "open_algorithmic_bytes": bytes_open,
             "build_one_chunk_batch_us": [round(x * 1000, 1) for x in build_ms],
             "algorithmic_bytes_per_call": bytes_call,
             "call_achieved_GBs": round(bytes_call / (call_avg * 1e-3) / 1e9, 1),

@@ -438,8 +438,11 @@ struct OpenSmem {
     float wl[4][kMaxTG];       // per wave: its TG largest lower bounds
     float thr;                 // TG-th largest lower bound of the head
     int ncand, over;
-    int32_t cg[kOpenCand];     // candidates: group id, canonical score
+    int32_t cg[kOpenCand];     // candidates: group id, canonical score, MFMA score, ln n
     float cs[kOpenCand];
+    float cS[kOpenCand], cL[kOpenCand];
+    int mrow[kMaxTG];          // meta row (in s.meta) of opened group i
+    int meta_ready;            // meta rows were prefetched (bf16 path)
     uint64_t red[4];
     float sub_lam[kMaxTG];     // opened groups' coarse logits in the scan (subtracted)
     alignas(16) float plds[kPartLdsFloats];  // the scan partial states (bf16 path), when they fit
@@ -500,18 +503,23 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
     const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + unit * A.max_chunks * PS;
     const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + unit * A.max_chunks * A.L.meta_stride;
 
-    // meta rows of this wave's groups (all loads in flight together)
+    // meta rows of this wave's groups (all loads in flight together), unless prefetched
     const int ngw = (A.TG - wave + 3) / 4;  // group slots of this wave (k: group i = wave + 4k)
     const int ms16 = A.L.meta_stride / 8;   // 16-byte pieces per meta row
-    for (int x = lane; x < ngw * ms16; x += 64) {
-        const int k = x / ms16, e = x % ms16, i = wave + 4 * k;
-        if (i < nsel) {
-            const int c = key_id(s.sel[i]) / A.G;
-            *reinterpret_cast<uint4*>(&s.meta[i][e * 8]) =
-                *reinterpret_cast<const uint4*>(meta_u + (int64_t)c * A.L.meta_stride + e * 8);
+    // meta row of opened group i: rows of meta_stride entries in the flat LDS buffer
+    int16_t* const mflat = &s.meta[0][0];
+    auto mrowp = [&](int i) { return mflat + s.mrow[i] * A.L.meta_stride; };
+    if (!s.meta_ready) {
+        for (int x = lane; x < ngw * ms16; x += 64) {
+            const int k = x / ms16, e = x % ms16, i = wave + 4 * k;
+            if (i < nsel) {
+                const int c = key_id(s.sel[i]) / A.G;
+                *reinterpret_cast<uint4*>(mrowp(i) + e * 8) =
+                    *reinterpret_cast<const uint4*>(meta_u + (int64_t)c * A.L.meta_stride + e * 8);
+            }
         }
+        wave_sync();
     }
-    wave_sync();
     // page ranking: lane (k = lane/16, e = lane%16) scores page e of group i = wave+4k
     {
         const int k = lane >> 4, e = lane & 15, i = wave + 4 * k;
@@ -520,8 +528,8 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
             const uint32_t gid = key_id(s.sel[i]);
             c = gid / A.G;
             j = gid % A.G;
-            ps0 = s.meta[i][j];
-            npg = s.meta[i][j + 1] - ps0;
+            ps0 = mrowp(i)[j];
+            npg = mrowp(i)[j + 1] - ps0;
         }
         float r = 0.0f;
         if (A.TP > 0 && e < npg) {
@@ -572,7 +580,7 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         }
         if (lane == 0) s.ncp[wave] = __popcll(cm);
         // exact rows: page e of group slot k contributes pst[e+1]-pst[e] rows
-        const int16_t* pst = s.meta[i < kMaxTG ? i : 0] + (A.G + 1);
+        const int16_t* pst = mrowp(i < kMaxTG ? i : 0) + (A.G + 1);
         const int16_t* perm = pst + (PS + 1);
         const int cnt = (e < npg && rank >= 0) ? pst[ps0 + e + 1] - pst[ps0 + e] : 0;
         int off = cnt;  // inclusive prefix over the wave's lanes
@@ -590,27 +598,37 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
 
     // exact rows of the wave's groups, then its coarse pages (subgroup sgw takes sgw, sgw+4, ...)
     const int nex = s.nex[wave];
+    constexpr int P16 = Elt<T>::kPer16, U = 8 / P16;  // 16-byte pieces per 8 elements
     for (int base = 0; base < nex; base += 4 * OB) {
-        float kf[OB][8], vf[OB][8];
+        uint4 kp[OB][U], vp[OB][U];  // rows kept packed until used
 #pragma unroll
         for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < nex) {
                 const int pos = s.ex[wave][it];
-                load8<T>(kb + (int64_t)pos * A.st, l16, kf[x]);
-                load8<T>(vb + (int64_t)pos * A.st, l16, vf[x]);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    kp[x][u] = *reinterpret_cast<const uint4*>(kb + (int64_t)pos * A.st + 8 * l16 + u * P16);
+                    vp[x][u] = *reinterpret_cast<const uint4*>(vb + (int64_t)pos * A.st + 8 * l16 + u * P16);
+                }
             }
         }
 #pragma unroll
         for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < nex) {
+                float kf[8], vf[8];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    Elt<T>::unpack(kp[x][u], kf + u * P16);
+                    Elt<T>::unpack(vp[x][u], vf + u * P16);
+                }
                 float a = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[x][e], a);
+                for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
 #pragma unroll
                 for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-                st.add(A.scale * a, vf[x]);
+                st.add(A.scale * a, vf);
             }
         }
     }
@@ -623,7 +641,7 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
             if (it < ncp) {
                 const int k = s.cp[wave][it] >> 8, e = s.cp[wave][it] & 255, i = wave + 4 * k;
                 const uint32_t gid = key_id(s.sel[i]);
-                const int c = gid / A.G, ps0 = s.meta[i][gid % A.G];
+                const int c = gid / A.G, ps0 = mrowp(i)[gid % A.G];
                 load8<T>(pv_u + ((int64_t)c * PS + ps0 + e) * kD, l16, vf[x]);
             }
         }
@@ -699,6 +717,8 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
         }
         if (lane == 0) s.nsel = round;
     }
+    if (tid < kMaxTG) s.mrow[tid] = tid;
+    if (tid == 0) s.meta_ready = 0;
     __syncthreads();
     const int nsel = s.nsel;
     const uint64_t kth = nsel == A.TG ? s.sel[A.TG - 1] : 0;
@@ -961,7 +981,7 @@ __device__ void mfma_exact_rows(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* 
 // sdst + h * sstride), logits scale * S + ln n (empty groups: none), online softmax and
 // PV into o.
 template <int HG>
-__device__ void mfma_coarse_groups(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* gk, const bf16_t* gv,
+__device__ void mfma_scan_groups(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* gk, const bf16_t* gv,
                                    const float* gln, int n, float scale, float* sdst, int64_t sstride,
                                    float (*o)[4]) {
     constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
@@ -1031,6 +1051,9 @@ __device__ __forceinline__ void mfma_init(MSmem<HG>& s, float (*o)[4]) {
         for (int e = 0; e < 4; ++e) o[i][e] = 0.0f;
 }
 
+// Decode launch 1 (bf16): per (sequence, KV head), a slice of group summaries
+// (MFMA scores written out for the selection; coarse softmax over every non-empty
+// group) or an exact window tile (tile 0 also takes the sinks).
 template <int HG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_scan_mfma_kernel(DecodeArgs A) {
@@ -1075,7 +1098,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     const int n = min(A.slice, ng - g0);
     if (n > 0) {
         const int64_t gbase = unit * A.max_chunks * A.G + g0;
-        mfma_coarse_groups<HG>(s, qa, reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD,
+        mfma_scan_groups<HG>(s, qa, reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD,
                                reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD,
                                reinterpret_cast<const float*>(A.index + A.L.gln) + gbase, n, A.scale,
                                A.score + ((int64_t)b * A.Hq + hq0) * A.score_stride + g0, A.score_stride, o);
@@ -1098,11 +1121,8 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
 // same logits, are subtracted in the final merge.  The subtracted mass never exceeds
 // the scan's, and the exact terms of the opened pages carry at least the same order of
 // mass, so fp32 cancellation stays near 1e-6 of the output scale.
-__global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A) {
-    __shared__ OpenSmem<bf16_t> s;
-    const int b = blockIdx.y;
+__device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b, int hq) {
     const int HG = A.Hq / A.Hkv;
-    const int hq = (blockIdx.x % A.Hkv) * HG + blockIdx.x / A.Hkv;
     const int kvh = hq / HG;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15;
@@ -1114,14 +1134,28 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
     const int64_t unit = (int64_t)seq * A.Hkv + kvh;
     const int64_t head = (int64_t)b * A.Hq + hq;
     const bf16_t* qp = reinterpret_cast<const bf16_t*>(A.q) + head * kD;
-    if (tid < kD) s.qs[tid] = bf16_bits_to_f32(qp[tid]);
+    const float* S = A.score + head * A.score_stride;
+    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + unit * A.max_chunks * A.G;
+    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
+    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + unit * A.max_chunks * A.G * kD;
+    const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
+    const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + unit * A.max_chunks * A.L.meta_stride;
+
+    // loads of the first round trip, issued together: q, the scores, the bounds' inputs
     float q8[8];
     load8<bf16_t>(qp, l16, q8);
-    // |q| (16 lanes, 8 values each), rounded up
-    float qn = 0.0f;
+    const float qv = tid < kD ? bf16_bits_to_f32(qp[tid]) : 0.0f;
+    constexpr int SPT = 16;  // groups per thread per round
+    float sv[SPT], kn[SPT], ln[SPT];
+    auto load_scores = [&](int g0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qn = __builtin_fmaf(q8[e], q8[e], qn);
-    qn = sqrtf(wave_sum_f32(qn, 16)) * 1.0001f;
+        for (int u = 0; u < SPT; ++u) {
+            const int g = g0 + tid + kThreads * u;
+            ln[u] = -INFINITY;
+            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; ln[u] = gln[g]; }
+        }
+    };
+    if (ng > 0) load_scores(0);
     // scan partial states: straight into LDS (awaited before the final merge), else
     // merged from global memory by waves 2-3
     const int nscan = A.nslice + A.nwin;
@@ -1133,68 +1167,43 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
             const int pc = min(64 * i + lane, npiece - 1);
             __builtin_amdgcn_global_load_lds(part + 4 * pc, &s.plds[256 * i], 16, 0, 0);
         }
-    } else {
-        open_merge_scan(s, part, nscan);
     }
-
-    const float* S = A.score + head * A.score_stride;
-    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + unit * A.max_chunks * A.G;
-    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
-    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + unit * A.max_chunks * A.G * kD;
-    const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
+    if (tid < kD) s.qs[tid] = qv;
+    // |q| (16 lanes, 8 values each), rounded up
+    float qn = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qn = __builtin_fmaf(q8[e], q8[e], qn);
+    qn = sqrtf(wave_sum_f32(qn, 16)) * 1.0001f;
     const float eq = kErrC * qn;
+    if (!part_in_lds) open_merge_scan(s, part, nscan);
 
-    // 1a. every thread: its largest lower bounds S - E (sorted insertion); groups are
-    //     read SPT per thread at a time, all loads in flight together
-    constexpr int SPT = 16;
-    float sv[SPT], kn[SPT], ln[SPT];
-    auto load_scores = [&](int g0) {
-#pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int g = g0 + tid + kThreads * u;
-            ln[u] = -INFINITY;
-            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; ln[u] = gln[g]; }
-        }
-    };
-    float lst[kMaxTG];
-#pragma unroll
-    for (int e = 0; e < kMaxTG; ++e) lst[e] = -INFINITY;
+    // 1a. every thread: the largest lower bound S - E among its groups.  The k-th
+    //     largest of these per-thread maxima is a lower bound of the k-th largest over
+    //     all groups, so it is a valid threshold.
+    float mx = -INFINITY;
     for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
-        load_scores(g0);
+        if (g0 > 0) load_scores(g0);
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            float x = ln[u] != -INFINITY ? sv[u] - eq * kn[u] : -INFINITY;
-            if (x > lst[kMaxTG - 1]) {
-#pragma unroll
-                for (int e = 0; e < kMaxTG; ++e) {
-                    const float hi = fmaxf(lst[e], x), lo = fminf(lst[e], x);
-                    lst[e] = hi;
-                    x = lo;
-                }
-            }
-        }
+        for (int u = 0; u < SPT; ++u)
+            if (ln[u] != -INFINITY) mx = fmaxf(mx, sv[u] - eq * kn[u]);
     }
-    // 1b. each wave: its TG largest (with multiplicity)
+    // 1b. each wave: its TG largest maxima (with multiplicity)
     {
         int taken = 0;
         for (int round = 0; round < TG && taken < TG; ++round) {
-            const float m = wave_max_f32(lst[0], 64);
+            const float m = wave_max_f32(mx, 64);
             if (m == -INFINITY) break;
-            const bool mine = lst[0] == m;
+            const bool mine = mx == m;
             const int c = __popcll(__ballot(mine));
             if (lane == 0)
                 for (int x = 0; x < c && taken + x < TG; ++x) s.wl[wave][taken + x] = m;
             taken += c;
-            if (mine) {
-#pragma unroll
-                for (int e = 0; e < kMaxTG - 1; ++e) lst[e] = lst[e + 1];
-                lst[kMaxTG - 1] = -INFINITY;
-            }
+            if (mine) mx = -INFINITY;
         }
         if (lane == 0)
             for (int x = taken; x < TG; ++x) s.wl[wave][x] = -INFINITY;
     }
-    if (tid == 0) { s.ncand = 0; s.over = 0; }
+    if (tid == 0) { s.ncand = 0; s.over = 0; s.meta_ready = 0; }
     __syncthreads();
     // 1c. T = the TG-th largest over the four lists (-inf if fewer than TG groups)
     if (wave == 0) {
@@ -1221,7 +1230,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
                 base = __shfl(base, 0, 64);
                 if (c) {
                     const int at = base + __popcll(mk & ((1ull << lane) - 1ull));
-                    if (at < kOpenCand) s.cg[at] = g;
+                    if (at < kOpenCand) { s.cg[at] = g; s.cS[at] = sv[u]; s.cL[at] = ln[u]; }
                 }
             }
         }
@@ -1229,6 +1238,21 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
     __syncthreads();
     const int ncand = s.ncand;
     if (ncand <= kOpenCand) {
+        // the opened groups are among the candidates: with at most kMaxTG of them, their
+        // meta rows go to LDS now, overlapping the canonical re-scoring
+        if (ncand <= kMaxTG) {
+            const int ms16 = A.L.meta_stride / 8;
+            const int npiece = ncand * ms16;
+            int16_t* mflat = &s.meta[0][0];
+            for (int i = wave; 64 * i < npiece; i += 4) {
+                // piece pc (row x, 16-byte piece e) lands at mflat + 8 * pc: candidate x's
+                // row starts at x * meta_stride entries, as the page step addresses it
+                const int pc = min(64 * i + lane, npiece - 1);
+                const int x = pc / ms16, e = pc % ms16;
+                __builtin_amdgcn_global_load_lds(meta_u + (int64_t)(s.cg[x] / A.G) * A.L.meta_stride + 8 * e,
+                                                 mflat + 512 * i, 16, 0, 0);
+            }
+        }
         for (int x = tid; x < ncand; x += kThreads) {
             const bf16_t* row = gk + (int64_t)s.cg[x] * kD;
             uint4 u[16];
@@ -1249,9 +1273,16 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
             const uint64_t key = rank_key(s.cs[x], (uint32_t)s.cg[x]);
             int rank = 0;
             for (int y = 0; y < ncand; ++y) rank += rank_key(s.cs[y], (uint32_t)s.cg[y]) > key;
-            if (rank < TG) s.sel[rank] = key;
+            if (rank < TG) {
+                s.sel[rank] = key;
+                s.mrow[rank] = x;
+                s.sub_lam[rank] = A.scale * s.cS[x] + s.cL[x];
+            }
         }
-        if (tid == 0) s.nsel = ncand < TG ? ncand : TG;
+        if (tid == 0) {
+            s.nsel = ncand < TG ? ncand : TG;
+            s.meta_ready = ncand <= kMaxTG;
+        }
     } else {
         // exhaustive: canonical score of every non-empty group, workgroup-wide top-TG
         uint64_t top[kMaxTG];
@@ -1293,16 +1324,18 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
             ++k;
         }
         if (tid == 0) s.nsel = k;
+        if (tid < kMaxTG) s.mrow[tid] = tid;
+        __syncthreads();
+        if (tid < k) {
+            const uint32_t g = key_id(s.sel[tid]);
+            s.sub_lam[tid] = A.scale * S[g] + gln[g];
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // prefetched meta rows (global -> LDS) of this wave
     __syncthreads();
     const int nsel = s.nsel;
     if (A.sel_groups && tid < TG) A.sel_groups[head * TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
-    // opened groups' logits as the scan computed them, and their mean values (loads in
-    // flight during the page work)
-    if (tid < nsel) {
-        const uint32_t g = key_id(s.sel[tid]);
-        s.sub_lam[tid] = A.scale * S[g] + gln[g];
-    }
+    // the opened groups' mean values (loads in flight during the page work)
     float vsub[kMaxTG];
     if (tid < kD) {
 #pragma unroll
@@ -1332,6 +1365,8 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
         if (tid == 0) { s.scan_m = M; s.scan_l = L; }
     }
     if (part_in_lds) __syncthreads();
+    // out = scan state - opened groups' coarse terms (the very logits the scan used) +
+    // the exact terms of the opened groups
     if (tid < kD) {
         float M = s.scan_m;
         for (int k = 0; k < 16; ++k) M = fmaxf(M, s.sm[k]);
@@ -1357,6 +1392,16 @@ __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A
         A.out[head * kD + tid] = O / L;
     }
 }
+
+// Decode launch 2 (bf16): one workgroup per (sequence, query head) runs the open step and
+// the final merge.  Consecutive workgroups take different KV heads, so the query heads
+// of one KV head share an XCD (workgroups are dealt to the 8 XCDs round robin).
+__global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A) {
+    __shared__ OpenSmem<bf16_t> s;
+    const int j = blockIdx.x;
+    decode_open_role(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
+}
+
 
 // Dense decode (bf16): split workgroups over rows, MFMA scores, online softmax.
 template <int HG>
@@ -1462,20 +1507,21 @@ int check_kv_view(const lod_params* p, const lod_kv& kv) {
 template <typename T, int HG>
 static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
     trace_point(0, st);
-    if (A.nslice + A.nwin > 0) {
-        if constexpr (sizeof(T) == 2)
+    if constexpr (sizeof(T) == 2) {
+        if (A.nslice + A.nwin > 0)
             hipLaunchKernelGGL((decode_scan_mfma_kernel<HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
                                dim3(kThreads), 0, st, A);
-        else
+        trace_point(1, st);
+        hipLaunchKernelGGL(decode_open_mfma_kernel, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+        trace_point(2, st);
+    } else {
+        if (A.nslice + A.nwin > 0)
             hipLaunchKernelGGL((decode_scan_kernel<T, HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
                                dim3(kThreads), 0, st, A);
-    }
-    trace_point(1, st);
-    if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL(decode_open_mfma_kernel, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
-    else
+        trace_point(1, st);
         hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
-    trace_point(2, st);
+        trace_point(2, st);
+    }
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
 

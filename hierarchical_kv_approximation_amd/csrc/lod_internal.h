@@ -75,4 +75,5 @@ void* const* trace_events(int* n);
 // Record trace event k on st when events are set and k is in range.
 void trace_point(int k, hipStream_t st);
 
+
 }  // namespace lodi
