@@ -48,7 +48,9 @@ struct FlashArgs {
     lod_index_layout_t L;
     int max_chunks, G, W, n_sink, TG;
     const int32_t* selg;  // [B][nq][Hq][TG] opened groups sorted ascending, -1 padding
-    float* part;          // LoD: [B][nq][Hq] partial states (o[d], m, l)
+    float* part;          // LoD: [nsplit][B][nq][Hq] partial states (o[d], m, l)
+    int nsplit;           // LoD: workgroups sharing one tile's key list
+    int64_t split_stride; // floats between the partial arrays of two splits
     float* out;           // dense: normalised output [B][nq][Hq][d]
 };
 
@@ -199,7 +201,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 void prefill_flash_kernel(FlashArgs A) {
     __shared__ FlashSmem<HG> s;
     constexpr int QT = kFlashRowHeads / HG;
-    const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
+    const int nsplit = A.index ? A.nsplit : 1;
+    const int tile = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+    const int kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int r0 = tile * QT;
     const int nrows = min(QT, A.nq - r0);
@@ -243,52 +247,55 @@ void prefill_flash_kernel(FlashArgs A) {
                 [&](int r) { return k0 + r; }, prow, noex, A.scale);
         }
     } else {
+        // key tiles: coarse centroids, then the sinks, then the causal block window
+        // [nb*C, p]; split `split` of `nsplit` takes an equal share of the list
         const int nb = nbuilt_prefill(p_first, A.W);
         const int ng = nb * A.G;
-        // opened groups of this lane's columns (coarse exclusion)
-        for (int x = tid; x < kFlashRowHeads * A.TG; x += kThreads) {
-            const int n = x / A.TG, t = x % A.TG;
-            const int rl = n / HG, h = n % HG;
-            s.sel[n][t] = rl < nrows ? A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h) * A.TG + t] : -1;
-        }
-        __syncthreads();
+        const int ns = min(A.n_sink, nb * kChunk);
+        const int w0 = nb * kChunk;
+        const int ct = (ng + kFlashKeys - 1) / kFlashKeys;
+        const int st = (ns + kFlashKeys - 1) / kFlashKeys;
+        const int wt = p_last >= w0 ? (p_last - w0) / kFlashKeys + 1 : 0;
+        const int nt = ct + st + wt;
+        const int t0 = split * nt / nsplit, t1 = (split + 1) * nt / nsplit;
         const int64_t gbase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.G;
         const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
         const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
         const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
-        // 1. coarse remainder over the group centroids
-        for (int g0 = 0; g0 < ng; g0 += kFlashKeys) {
-            const int nk = min(kFlashKeys, ng - g0);
-            uint64_t ex[2];
+        if (t0 < ct) {
+            // opened groups of the tile's columns (left out of the coarse terms)
+            for (int x = tid; x < kFlashRowHeads * A.TG; x += kThreads) {
+                const int n = x / A.TG, t = x % A.TG;
+                const int rl = n / HG, h = n % HG;
+                s.sel[n][t] = rl < nrows ? A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h) * A.TG + t] : -1;
+            }
+            __syncthreads();
+        }
+        for (int t = t0; t < t1; ++t) {
+            // one tile description for all three kinds keeps a single flash_tile body
+            const bool coarse = t < ct, sink = !coarse && t < ct + st;
+            const int k0 = coarse ? t * kFlashKeys : (sink ? (t - ct) * kFlashKeys : w0 + (t - ct - st) * kFlashKeys);
+            const int nk = coarse ? min(kFlashKeys, ng - k0) : (sink ? min(kFlashKeys, ns - k0) : min(kFlashKeys, p_last + 1 - k0));
+            const bf16_t* kt = coarse ? gk + (int64_t)k0 * kD : kc + (int64_t)k0 * A.st;
+            const bf16_t* vt = coarse ? gv + (int64_t)k0 * kD : vc + (int64_t)k0 * A.st;
+            const int64_t rs = coarse ? kD : A.st;
+            uint64_t ex[2] = {0, 0};
+            if (coarse) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const int n = 16 * (2 * w + cb) + (l & 15);
-                uint64_t msk = 0;
-                for (int t = 0; t < A.TG; ++t) {
-                    const int g = s.sel[n][t] - g0;
-                    if (g >= 0 && g < kFlashKeys) msk |= 1ull << g;
+                for (int cb = 0; cb < 2; ++cb) {
+                    const int n = 16 * (2 * w + cb) + (l & 15);
+                    uint64_t msk = 0;
+                    for (int u = 0; u < A.TG; ++u) {
+                        const int g = s.sel[n][u] - k0;
+                        if (g >= 0 && g < kFlashKeys) msk |= 1ull << g;
+                    }
+                    ex[cb] = msk;
                 }
-                ex[cb] = msk;
             }
             flash_tile<HG>(
-                s, F, qb, nk, [&](int r) { return gk + (int64_t)(g0 + r) * kD; },
-                [&](int r) { return gv + (int64_t)(g0 + r) * kD; }, [&](int r) { return gln[g0 + r]; },
-                [&](int) { return INT_MIN; }, prow, ex, A.scale);
-        }
-        // 2. sinks not covered by the window
-        const int ns = min(A.n_sink, nb * kChunk);
-        for (int k0 = 0; k0 < ns; k0 += kFlashKeys)
-            flash_tile<HG>(
-                s, F, qb, min(kFlashKeys, ns - k0), [&](int r) { return kc + (int64_t)(k0 + r) * A.st; },
-                [&](int r) { return vc + (int64_t)(k0 + r) * A.st; }, [&](int) { return 0.0f; },
-                [&](int r) { return k0 + r; }, prow, noex, A.scale);
-        // 3. the causal block window [nb*C, p]
-        for (int k0 = nb * kChunk; k0 <= p_last; k0 += kFlashKeys) {
-            const int nk = min(kFlashKeys, p_last + 1 - k0);
-            flash_tile<HG>(
-                s, F, qb, nk, [&](int r) { return kc + (int64_t)(k0 + r) * A.st; },
-                [&](int r) { return vc + (int64_t)(k0 + r) * A.st; }, [&](int) { return 0.0f; },
-                [&](int r) { return k0 + r; }, prow, noex, A.scale);
+                s, F, qb, nk, [&](int r) { return kt + (int64_t)r * rs; }, [&](int r) { return vt + (int64_t)r * rs; },
+                [&](int r) { return coarse ? gln[k0 + r] : 0.0f; }, [&](int r) { return coarse ? INT_MIN : k0 + r; },
+                prow, ex, A.scale);
         }
     }
 
@@ -313,7 +320,7 @@ void prefill_flash_kernel(FlashArgs A) {
                     make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
             }
         } else {
-            float* dst = A.part + rh * kPartStride;
+            float* dst = A.part + split * A.split_stride + rh * kPartStride;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 const f32x4_t o = F.O[cb][db];
@@ -357,8 +364,9 @@ struct SelArgs {
 constexpr int kCandCap = 2 * kMaxTG;  // candidates kept per column; beyond: exhaustive path
 
 struct SelSmem {
-    alignas(16) bf16_t kt[kFlashKeys][kD];
-    float gkn_t[kFlashKeys], gln_t[kFlashKeys];
+    alignas(16) bf16_t kt[2][kFlashKeys][kD];  // double-buffered centroid tiles
+    alignas(16) float gkn_t[2][kFlashKeys];
+    alignas(16) float gln_t[2][kFlashKeys];
     float qn[kFlashRowHeads];
     float T[kFlashRowHeads];
     int cnt[kFlashRowHeads];
@@ -450,7 +458,7 @@ void prefill_select_kernel(SelArgs A) {
     const float qn[2] = {s.qn[16 * (2 * w) + (l & 15)], s.qn[16 * (2 * w + 1) + (l & 15)]};
 
     // MFMA scores S^T of one staged tile for this lane's two columns
-    auto tile_scores = [&](f32x4_t (*S)[2]) {
+    auto tile_scores = [&](f32x4_t (*S)[2], int buf) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -459,20 +467,47 @@ void prefill_select_kernel(SelArgs A) {
             for (int kk = 0; kk < 4; ++kk) {
                 const int row = 16 * kb + (l & 15);
                 const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[buf][row][8 * chunk]);
                 S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
                 S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
             }
         }
     };
-    auto stage = [&](int g0, int nk) {
-        stage_rows_swizzled(s.kt, gk + (int64_t)g0 * kD, nk);
-        if (tid < kFlashKeys) {
-            s.gln_t[tid] = tid < nk ? gln[g0 + tid] : -INFINITY;
-            s.gkn_t[tid] = tid < nk ? gkn[g0 + tid] : 0.0f;
+    // Centroid tiles of 64 groups stream through two LDS buffers: the loads of tile t+1
+    // (keys, ln n and norm bounds, all straight to LDS) are in flight while tile t is
+    // used.  Each wave waits for its own older loads (vmcnt: the 4, or 6 in wave 0,
+    // instructions of the newer tile may stay outstanding), then a barrier publishes.
+    const int ntile = (ng + kFlashKeys - 1) / kFlashKeys;
+    auto issue = [&](int t) {
+        const int buf = t & 1, g0 = t * kFlashKeys, nk = min(kFlashKeys, ng - g0);
+        stage_rows_swizzled(s.kt[buf], gk + (int64_t)g0 * kD, nk);
+        if (w == 0) {
+            const int g = g0 + min(l, nk - 1);
+            __builtin_amdgcn_global_load_lds(gln + g, &s.gln_t[buf][0], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(gkn + g, &s.gkn_t[buf][0], 4, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+    };
+    auto await_tile = [&](int t) {
+        if (t + 1 < ntile) {
+            if (w == 0) __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt <= 6
+            else __builtin_amdgcn_s_waitcnt(0xF74);         // vmcnt <= 4
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         __syncthreads();
+    };
+    // sweep over the centroid tiles; body(t, buf, nk, S) sees the MFMA scores
+    auto sweep = [&](auto&& body) {
+        if (ntile > 0) issue(0);
+        for (int t = 0; t < ntile; ++t) {
+            if (t + 1 < ntile) issue(t + 1);
+            await_tile(t);
+            const int buf = t & 1;
+            f32x4_t S[4][2];
+            tile_scores(S, buf);
+            body(t, buf, min(kFlashKeys, ng - t * kFlashKeys), S);
+            __syncthreads();
+        }
     };
 
     // pass A: per column, the k-th largest lower bound S - E (lane-local top-16 lists)
@@ -481,20 +516,16 @@ void prefill_select_kernel(SelArgs A) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < kMaxTG; ++e) lst[cb][e] = -INFINITY;
-    for (int g0 = 0; g0 < ng; g0 += kFlashKeys) {
-        const int nk = min(kFlashKeys, ng - g0);
-        stage(g0, nk);
-        f32x4_t S[4][2];
-        tile_scores(S);
+    sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = 16 * kb + 4 * (l >> 4) + r;
-                const bool valid = s.gln_t[key] != -INFINITY;
+                const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    float x = S[kb][cb][r] - kErrC * qn[cb] * s.gkn_t[key];
+                    float x = S[kb][cb][r] - kErrC * qn[cb] * s.gkn_t[buf][key];
                     if (valid && x > lst[cb][kMaxTG - 1]) {
 #pragma unroll
                         for (int e = 0; e < kMaxTG; ++e) {
@@ -505,8 +536,7 @@ void prefill_select_kernel(SelArgs A) {
                     }
                 }
             }
-        __syncthreads();
-    }
+    });
     // merge the four lanes of each column: T = TG-th largest with multiplicity
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -536,20 +566,17 @@ void prefill_select_kernel(SelArgs A) {
 
     // pass B: candidates S + E >= T
     const float T2[2] = {s.T[16 * (2 * w) + (l & 15)], s.T[16 * (2 * w + 1) + (l & 15)]};
-    for (int g0 = 0; g0 < ng; g0 += kFlashKeys) {
-        const int nk = min(kFlashKeys, ng - g0);
-        stage(g0, nk);
-        f32x4_t S[4][2];
-        tile_scores(S);
+    sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
+        const int g0 = t * kFlashKeys;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = 16 * kb + 4 * (l >> 4) + r;
-                const bool valid = s.gln_t[key] != -INFINITY;
+                const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    const float ub = S[kb][cb][r] + kErrC * qn[cb] * s.gkn_t[key];
+                    const float ub = S[kb][cb][r] + kErrC * qn[cb] * s.gkn_t[buf][key];
                     if (valid && ub >= T2[cb]) {
                         const int n = 16 * (2 * w + cb) + (l & 15);
                         const int at = atomicAdd(&s.cnt[n], 1);
@@ -557,8 +584,7 @@ void prefill_select_kernel(SelArgs A) {
                     }
                 }
             }
-        __syncthreads();
-    }
+    });
 
     // canonical chains for the candidates
     for (int x = tid; x < kFlashRowHeads * kCandCap; x += kThreads) {
@@ -684,12 +710,17 @@ void prefill_select_kernel(SelArgs A) {
                 }
                 const int nopen = min(npg, A.TP);
                 for (int k = 0; k < nopen; ++k) {
+                    // largest remaining key (register-resident: static indices only)
+                    uint64_t bk = 0;
                     int best = 0;
-                    for (int e = 1; e < kPage; ++e)
-                        if (key[e] > key[best]) best = e;
+#pragma unroll
+                    for (int e = 0; e < kPage; ++e)
+                        if (key[e] > bk) { bk = key[e]; best = e; }
+#pragma unroll
+                    for (int e = 0; e < kPage; ++e)
+                        if (e == best) key[e] = 0;
                     slot_rank[k] = best;
                     R.open |= 1u << best;
-                    key[best] = 0;
                 }
             }
         }
@@ -720,7 +751,9 @@ struct PagesArgs {
     const PairRec* rec;     // [B][nq][Hq][TG]
     int32_t* plist;         // [units][kChunk * HG * TG] pair indices sorted by group
     int32_t* poff;          // [units][2]: number of pairs with a group, (unused)
-    float* part_fl;         // [B][nq][Hq] flash partial states
+    float* part_fl;         // [nsplit][B][nq][Hq] flash partial states
+    int nsplit;
+    int64_t split_stride;
     float* part_pg;         // [B][nq][Hq][TG] page partial states
     float* out;             // [B][nq][Hq][d]
     int units_per_seq_kv;   // query chunks in the launch
@@ -856,15 +889,17 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, 
     const int64_t rh = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
     const int d = threadIdx.x & 127;
     if (rh >= nrh) return;
-    const float* pf = A.part_fl + rh * kPartStride;
-    float M = pf[kD];
+    float M = -INFINITY;
+    for (int sp = 0; sp < A.nsplit; ++sp) M = fmaxf(M, A.part_fl[sp * A.split_stride + rh * kPartStride + kD]);
     for (int t = 0; t < A.TG; ++t)
         if (A.rec[rh * A.TG + t].gid >= 0) M = fmaxf(M, A.part_pg[(rh * A.TG + t) * kPartStride + kD]);
     float L = 0.0f, O = 0.0f;
-    if (pf[kD] != -INFINITY) {
+    for (int sp = 0; sp < A.nsplit; ++sp) {
+        const float* pf = A.part_fl + sp * A.split_stride + rh * kPartStride;
+        if (pf[kD] == -INFINITY) continue;
         const float e = softmax_exp(pf[kD] - M);
-        L = pf[kD + 1] * e;
-        O = pf[d] * e;
+        L = __builtin_fmaf(pf[kD + 1], e, L);
+        O = __builtin_fmaf(pf[d], e, O);
     }
     for (int t = 0; t < A.TG; ++t) {
         if (A.rec[rh * A.TG + t].gid < 0) continue;
@@ -887,7 +922,8 @@ namespace lodi {
 constexpr int kPrefillBatchRows = 2048;
 
 struct PrefillPlan {
-    int rows;  // rows per batch (<= n_q, multiple of kChunk unless n_q is smaller)
+    int rows;    // rows per batch (<= n_q, multiple of kChunk unless n_q is smaller)
+    int nsplit;  // flash workgroups per (tile, KV head): enough workgroups for small batches
     size_t off_selg, off_rec, off_pfl, off_ppg, off_plist, off_poff, bytes;
 };
 
@@ -899,10 +935,13 @@ static PrefillPlan plan_prefill(const lod_params* p, int n_q) {
     const size_t TG = p->top_groups;
     const int HG = p->n_q_heads / p->n_kv_heads;
     const size_t units = (size_t)p->n_kv_heads * ((P.rows + kChunk - 1) / kChunk);
+    const int64_t tiles = ((int64_t)P.rows * HG + kFlashRowHeads - 1) / kFlashRowHeads * p->n_kv_heads;
+    int64_t ns = (512 + tiles - 1) / tiles;
+    P.nsplit = (int)(ns < 1 ? 1 : (ns > 8 ? 8 : ns));
     size_t o = 0;
     P.off_selg = o; o = align256(o + rh * TG * 4);
     P.off_rec = o; o = align256(o + rh * TG * sizeof(PairRec));
-    P.off_pfl = o; o = align256(o + rh * kPartStride * 4);
+    P.off_pfl = o; o = align256(o + (size_t)P.nsplit * rh * kPartStride * 4);
     P.off_ppg = o; o = align256(o + rh * TG * kPartStride * 4);
     P.off_plist = o; o = align256(o + units * kChunk * HG * TG * 4);
     P.off_poff = o; o = align256(o + units * 2 * 4);
@@ -918,7 +957,7 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     trace_point(0, st);
     hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, S);
     trace_point(1, st);
-    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, F);
+    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0, st, F);
     trace_point(2, st);
     hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
     trace_point(3, st);
@@ -1037,6 +1076,8 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             F.index = S.index; F.L = L; F.max_chunks = S.max_chunks; F.G = S.G; F.W = S.W;
             F.n_sink = params->n_sink; F.TG = TG; F.selg = S.selg;
             F.part = reinterpret_cast<float*>(w + P.off_pfl);
+            F.nsplit = P.nsplit;
+            F.split_stride = (int64_t)P.rows * Hq * kPartStride;
             PagesArgs G{};
             G.k = F.k; G.v = F.v; G.seq = b; G.sb = F.sb; G.st = F.st; G.sh = F.sh;
             G.q = S.q; G.nq = rows; G.pos0 = S.pos0; G.Hq = Hq; G.Hkv = Hkv; G.scale = params->scale;
@@ -1045,6 +1086,8 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.plist = reinterpret_cast<int32_t*>(w + P.off_plist);
             G.poff = reinterpret_cast<int32_t*>(w + P.off_poff);
             G.part_fl = F.part;
+            G.nsplit = F.nsplit;
+            G.split_stride = F.split_stride;
             G.part_pg = reinterpret_cast<float*>(w + P.off_ppg);
             G.out = out + row0 * Hq * kD;
             G.units_per_seq_kv = nunits_q;

@@ -109,8 +109,10 @@ def test_lod_prefill_ties_take_the_exhaustive_path():
 
 def test_lod_prefill_32k_chunked_equals_one_shot():
     """32K-token prefill, 64/8 heads: one call over every row equals the chunked flow
-    (build the chunk that leaves the window, then attend the next 256-row query chunk),
-    bit for bit; sampled rows match the oracle."""
+    (build the chunk that leaves the window, then attend the next 256-row query chunk);
+    sampled rows match the oracle.  Selections are identical; outputs agree to fp32
+    rounding, since small calls split each tile's key list over several workgroups and
+    so sum the softmax in a different order."""
     g, o = configs(torch.bfloat16, 64, 8, G=8)
     T = 32768
     case = Case(g, o, 1, T, seed=50)
@@ -130,4 +132,4 @@ def test_lod_prefill_32k_chunked_equals_one_shot():
         lod.attend_prefill(g, fresh, case.Kd, case.Vd, Qd[:, 256 * k: 256 * (k + 1)], 256 * k, ws=ws,
                            out=out[:, 256 * k: 256 * (k + 1)])
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy(), one)
+    assert float(np.max(np.abs(out.cpu().numpy() - one))) <= 1e-5
