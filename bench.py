@@ -154,6 +154,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--prefill-ctx", type=int, default=131072)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the sigma sweep of the approximation error")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -291,6 +292,11 @@ def main():
     del layers, ws
     torch.cuda.empty_cache()
 
+    sweep = None
+    if not args.no_sweep:
+        sweep = bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, args.prefill_ctx, args.seed)
+        torch.cuda.empty_cache()
+
     prefill = None
     if not args.no_prefill:
         prefill = bench_prefill(torch, lod, synth, cfg, hip, stream, args.prefill_ctx, args.seed,
@@ -341,6 +347,7 @@ def main():
             "setup_s": round(setup_s, 1),
         },
         "prefill": prefill,
+        "sigma_sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 
@@ -466,6 +473,84 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
         "select_algorithmic_flops": int(select_flops),
         "dense_prefill": dense_rep,
     }
+
+
+def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, samples=96):
+    """After a T-token prompt, 256 decode steps of one sequence (batch 1) with one chunk
+    build at the boundary, for three-tier and two-tier LoD; keys whose 32 clusters have
+    sigma spread over 0.1 .. 1.0 and queries matched to a cluster.  Reports decode time
+    per token for both, and the error of the LoD output against the dense oracle (fp64)
+    on sampled (step, head) pairs, binned by the sigma of the query's cluster."""
+    import dataclasses
+
+    import numpy as np
+
+    from oracle import oracle as orc
+    dev = torch.device("cuda:0")
+    C = cfg.chunk_size
+    sig = torch.linspace(0.1, 1.0, 32)
+    K, V, cen, _ = synth.clustered_kv(1, T + steps, 8, 128, sigma=sig, seed=seed + 777, device=dev)
+    Q, z = synth.queries(1, 64, cen, n_rows=steps, sigma=sig, seed=seed + 778, return_centres=True)
+    idx = lod.LodIndex.allocate(cfg, 1, T + steps, device=dev)
+    nb0 = (T - 1) // C - cfg.window // C + 1  # chunks the prompt's last row sees
+    # every chunk the decode steps see; the timed region rebuilds the boundary chunk
+    lod.build_chunk(cfg, idx, K, V, 0, nb0 + 1)
+    torch.cuda.synchronize()
+    res = {}
+    outs = {}
+    for name, TP in (("three_tier", cfg.top_pages), ("two_tier", 0)):
+        c = dataclasses.replace(cfg, top_pages=TP)
+        ws = torch.empty(lod.decode_ws_bytes(c, 1, T + steps), dtype=torch.uint8, device=dev)
+        lens = torch.arange(T + 1, T + steps + 1, dtype=torch.int32, device=dev).view(steps, 1)
+        out = torch.empty(steps, 64, 128, dtype=torch.float32, device=dev)
+        # warm-up, then the timed pass; the first step needs the chunk leaving the window
+        lod.attend_decode(c, idx, K, V, Q[:, 0], lens[0], T + steps, ws=ws, out=out[0:1])
+        e0, e1 = hip.create(2)
+        hip.record(e0, stream)
+        lod.build_chunk(c, idx, K, V, nb0, 1)
+        for k in range(steps):
+            lod.attend_decode(c, idx, K, V, Q[:, k], lens[k], T + steps, ws=ws, out=out[k:k + 1])
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(e0, e1)
+        hip.destroy([e0, e1])
+        outs[name] = out.cpu().numpy()
+        res[name] = {"decode_us_per_token": round(ms * 1000 / steps, 2), "tok_per_s": round(steps * 1000 / ms, 1)}
+        del ws
+    # dense oracle on sampled (step, head) pairs
+    rng = np.random.default_rng(seed + 779)
+    pick = [(int(k), int(h)) for k, h in zip(rng.integers(0, steps, samples), rng.integers(0, 64, samples))]
+    ocfg = orc.Config(d=128, groups=cfg.groups, top_groups=cfg.top_groups, top_pages=cfg.top_pages,
+                      window=cfg.window, n_sink=cfg.n_sink, bf16=True)
+    Kh = K[0].float().cpu().numpy()
+    Vh = V[0].float().cpu().numpy()
+    Qh = Q[0].float().cpu().numpy()
+    zh = z[0].cpu().numpy()
+    streams = {h: (np.ascontiguousarray(Kh[:, h]), np.ascontiguousarray(Vh[:, h])) for h in {hq // 8 for _, hq in pick}}
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(kh):
+        k, h = kh
+        Ks, Vs = streams[h // 8]
+        return kh, orc.dense(ocfg, Ks, Vs, Qh[k, h], T + k)[0]
+    with ThreadPoolExecutor(cpu_threads()) as ex:
+        ref = dict(ex.map(one, pick))
+    edges = np.linspace(0.1, 1.0, 5)
+    sig_np = sig.numpy()
+    for name in res:
+        bins = []
+        for i in range(4):
+            errs = [float(np.max(np.abs(outs[name][k, h] - ref[(k, h)]))) for k, h in pick
+                    if edges[i] <= sig_np[zh[k, h]] < edges[i + 1] + (1e-9 if i == 3 else 0.0)]
+            bins.append({"sigma": [round(float(edges[i]), 3), round(float(edges[i + 1]), 3)], "n": len(errs),
+                         "mean_max_abs_err": round(float(np.mean(errs)), 5) if errs else None,
+                         "max_abs_err": round(float(np.max(errs)), 5) if errs else None})
+        res[name]["error_vs_dense_oracle_by_sigma"] = bins
+    del K, V, Q, idx
+    log("sigma sweep: " + ", ".join(f"{n} {r['decode_us_per_token']} us/token" for n, r in res.items()))
+    return {"workload": f"one sequence, {T}-token prompt then {steps} decode steps with one chunk build, "
+                        "GQA 64/8, bf16; 32 key clusters with sigma 0.1..1.0, matched queries",
+            **res, "samples": samples}
 
 
 def cpu_baseline(cfg, Ly, seq_len, seconds):

@@ -62,16 +62,20 @@ def clustered_kv(B: int, T: int, Hkv: int, d: int = 128, *, n_centres: int = 32,
 
 
 def queries(B: int, Hq: int, centres: torch.Tensor, *, n_rows: int | None = None,
-            sigma=0.3, kind: str = "matched", seed: int = 1, dtype=torch.bfloat16):
+            sigma=0.3, kind: str = "matched", seed: int = 1, dtype=torch.bfloat16,
+            return_centres: bool = False):
     """Queries drawn against the key mixture of each query head's KV head.
 
-    Returns [B][Hq][d] (decode) or, with n_rows, [B][n_rows][Hq][d] (prefill)."""
+    Returns [B][Hq][d] (decode) or, with n_rows, [B][n_rows][Hq][d] (prefill); with
+    return_centres also the centre index of every matched query (same shape without
+    d; -1 for diffuse queries)."""
     device = centres.device
     Bc, Hkv, nc, d = centres.shape
     assert Bc == B and Hq % Hkv == 0
     g = Hq // Hkv
     gen = _gen(seed, device)
     rows = 1 if n_rows is None else n_rows
+    z = torch.full((B, rows, Hq), -1, dtype=torch.int64, device=device)
     if kind == "diffuse":
         q = torch.randn(B, rows, Hq, d, generator=gen, device=device)
     elif kind == "matched":
@@ -87,4 +91,6 @@ def queries(B: int, Hq: int, centres: torch.Tensor, *, n_rows: int | None = None
     else:
         raise ValueError(f"unknown query kind {kind!r}")
     q = q.to(dtype)
-    return q[:, 0] if n_rows is None else q
+    if n_rows is None:
+        q, z = q[:, 0], z[:, 0]
+    return (q, z) if return_centres else q

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from hierarchical_kv_approximation_amd import synth
 from oracle import oracle as orc
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -461,3 +462,29 @@ def test_bf16_summaries_are_rounded_means():
             tol = 2.0**-8 * np.abs(ex) * 1.01 + (n * 2.0**-24 / (1 - n * 2.0**-24)) * \
                 np.abs(V[mem]).astype(np.float64).sum(0) / n + 1e-30
             assert np.all(np.abs(idx["gv"][c, j] - ex) <= tol)
+
+
+def test_error_grows_with_cluster_spread_and_two_tier_is_closer():
+    """The coarse terms replace keys by their group means, so the error against dense
+    attention grows with the spread of the key clusters (zero spread: no error, pinned
+    above), and opening every page of the top groups (two-tier) leaves fewer coarse
+    terms than opening the best two (three-tier)."""
+    mean_err = {}
+    for sigma in (0.1, 1.0):
+        K, V, cen, _ = synth.clustered_kv(1, 4096, 1, 128, sigma=sigma, seed=5, dtype=torch.float32)
+        Q = synth.queries(1, 1, cen, n_rows=24, sigma=sigma, seed=6, dtype=torch.float32)
+        st = orc.streams(K.numpy(), V.numpy())
+        for tier, TP in (("three", 2), ("two", 0)):
+            cfg = orc.Config(d=128, groups=8, top_groups=8, top_pages=TP, window=256, n_sink=1, bf16=False)
+            idx = orc.build_all(cfg, st, cfg.built_chunks(4095))
+            errs = []
+            for i in range(24):
+                q = Q[0, i, 0].numpy()
+                r = orc.attend(cfg, idx[(0, 0)], *st[(0, 0)], q, 4095)
+                d, _ = orc.dense(cfg, *st[(0, 0)], q, 4095)
+                errs.append(float(np.max(np.abs(r["out"] - d))))
+            mean_err[(sigma, tier)] = float(np.mean(errs))
+    for tier in ("three", "two"):
+        assert mean_err[(0.1, tier)] < mean_err[(1.0, tier)], mean_err
+    for sigma in (0.1, 1.0):
+        assert mean_err[(sigma, "two")] <= mean_err[(sigma, "three")], mean_err
