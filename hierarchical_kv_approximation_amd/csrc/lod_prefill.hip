@@ -358,7 +358,7 @@ struct SelArgs {
     int32_t* sel_groups;  // nullable API output [B][nq][Hq][TG], rank order
     int32_t* sel_pages;   // nullable API output [B][nq][Hq][TG][max(TP,1)]
     int32_t* selg;        // [B][nq][Hq][TG] opened groups in ascending id order (-1 pad)
-    PairRec* rec;         // [B][nq][Hq][TG]
+    PairRec* rec;         // [B][nq][Hq][TG] in ascending group order (as selg)
 };
 
 constexpr int kCandCap = 2 * kMaxTG;  // candidates kept per column; beyond: exhaustive path
@@ -724,7 +724,14 @@ void prefill_select_kernel(SelArgs A) {
                 }
             }
         }
-        A.rec[rh * TG + t] = R;
+        // records go in ascending group order (the order of selg), so later steps read
+        // the compact selg array to find a slot's group
+        int pos = t;
+        if (R.gid >= 0) {
+            pos = 0;
+            for (int e = 0; e < s.nsel[n]; ++e) pos += s.sel[n][e] < R.gid;
+        }
+        A.rec[rh * TG + pos] = R;
         if (A.sel_pages)
             for (int k = 0; k < TPW; ++k)
                 A.sel_pages[(rh * TG + t) * TPW + k] =
@@ -748,7 +755,8 @@ struct PagesArgs {
     const char* index;
     lod_index_layout_t L;
     int max_chunks, G, W, TG;
-    const PairRec* rec;     // [B][nq][Hq][TG]
+    const PairRec* rec;     // [B][nq][Hq][TG], slot t holds the group selg[t]
+    const int32_t* selg;    // [B][nq][Hq][TG] opened groups, ascending (-1 padding)
     int32_t* plist;         // [units][kChunk * HG * TG] pair indices sorted by group
     int32_t* poff;          // [units][2]: number of pairs with a group, (unused)
     float* part_fl;         // [nsplit][B][nq][Hq] flash partial states
@@ -773,7 +781,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
     int32_t* list = A.plist + unit * (kChunk * HG * A.TG);
     auto pair_gid = [&](int x) {
         const int t = x % A.TG, h = (x / A.TG) % HG, rl = x / (A.TG * HG);
-        return A.rec[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t].gid;
+        return A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t];
     };
     for (int g = tid; g < ng; g += kThreads) cnt[g] = 0;
     __syncthreads();
@@ -807,9 +815,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
 
 // ---------------------------------------------------------------------------- pages
 
-constexpr int kPairsPerWG = 64;
+constexpr int kPairsPerWG = 16;  // one (row, head, slot) pair per 16-lane subgroup
 
-// One workgroup per 64 consecutive pairs of a unit's group-sorted list; each 16-lane
+// One workgroup per 16 consecutive pairs of a unit's group-sorted list; each 16-lane
 // subgroup runs one pair: exact rows of its opened pages and the mean terms of the
 // unopened pages of its group, one online softmax, written as the pair's partial state.
 // Pairs of the same group run side by side, so their rows come from the same cache lines.
@@ -833,53 +841,99 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     const bf16_t* kc = A.k + bs * A.sb + kvh * A.sh;
     const bf16_t* vc = A.v + bs * A.sb + kvh * A.sh;
 
-    for (int x = blk * kPairsPerWG + sg; x < min(npairs, (blk + 1) * kPairsPerWG); x += 16) {
-        const int pi = list[x];
-        const int t = pi % A.TG, h = (pi / A.TG) % HG, rl = pi / (A.TG * HG);
-        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h;
-        const PairRec& R = A.rec[rh * A.TG + t];
-        const int c = R.gid / A.G;
-        const int16_t* pst = meta_u + (int64_t)c * A.L.meta_stride + (A.G + 1);
-        const int16_t* perm = pst + (PS + 1);
-        float q8[8];
-        load8<bf16_t>(A.q + rh * kD, l16, q8);
-        Online st;
-        st.init();
-        for (int e = 0; e < R.npg; ++e) {
-            const int slot = R.ps0 + e;
-            if ((R.open >> e) & 1u) {
-                const int x0 = pst[slot], x1 = pst[slot + 1];
-                for (int y0 = x0; y0 < x1; y0 += 4) {
-                    float kf[4][8], vf[4][8];
+    // one pair per 16-lane subgroup; its dependent loads are few and wide: the record,
+    // then the page starts, the opened pages' member positions and the first unopened
+    // pages' means together, then the rows in batches of 16 (kept packed)
+    const int x = blk * kPairsPerWG + sg;
+    if (x >= npairs) return;  // uniform in the subgroup
+    const int seg0 = (tid & 63) & ~15;
+    const int pi = list[x];
+    const int t = pi % A.TG, h = (pi / A.TG) % HG, rl = pi / (A.TG * HG);
+    const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h;
+    float q8[8];
+    load8<bf16_t>(A.q + rh * kD, l16, q8);
+    const PairRec* R = A.rec + rh * A.TG + t;
+    const int gid = R->gid, ps0 = R->ps0, npg = R->npg;
+    const uint32_t open = R->open;
+    const float rl16 = R->r[l16];  // lane e: score of page e
+    const int c = gid / A.G;
+    const int16_t* pst = meta_u + (int64_t)c * A.L.meta_stride + (A.G + 1);
+    const int16_t* perm = pst + (PS + 1);
+    const int pstv = l16 <= npg ? pst[ps0 + l16] : 0;  // lane e: first member of page e
+    // unopened pages: the first four means in flight now
+    constexpr int kCP = 4;
+    const uint32_t closed = ~open & ((npg >= 32 ? 0xffffffffu : (1u << npg) - 1u));
+    uint4 cpv[kCP];
+    int cslot[kCP];
+    {
+        uint32_t m = closed;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (y0 + u < x1) {
-                            const int pos = c * kChunk + perm[y0 + u];
-                            load8<bf16_t>(kc + (int64_t)pos * A.st, l16, kf[u]);
-                            load8<bf16_t>(vc + (int64_t)pos * A.st, l16, vf[u]);
-                        }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (y0 + u < x1) {
-                            float a = 0.0f;
-#pragma unroll
-                            for (int z = 0; z < 8; ++z) a = __builtin_fmaf(q8[z], kf[u][z], a);
-#pragma unroll
-                            for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-                            st.add(A.scale * a, vf[u]);
-                        }
-                }
-            } else {
-                float vf[8];
-                load8<bf16_t>(pv_u + ((int64_t)c * PS + slot) * kD, l16, vf);
-                st.add(A.scale * R.r[e] + pln_u[(int64_t)c * PS + slot], vf);
+        for (int u = 0; u < kCP; ++u) {
+            cslot[u] = m ? __builtin_ctz(m) : -1;
+            if (m) {
+                m &= m - 1;
+                cpv[u] = *reinterpret_cast<const uint4*>(pv_u + ((int64_t)c * PS + ps0 + cslot[u]) * kD + 8 * l16);
             }
         }
-        float* dst = A.part_pg + (rh * A.TG + t) * kPartStride;
-        *reinterpret_cast<float4*>(dst + 8 * l16) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-        *reinterpret_cast<float4*>(dst + 8 * l16 + 4) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-        if (l16 == 0) { dst[kD] = st.m; dst[kD + 1] = st.l; }
     }
+    Online st;
+    st.init();
+    // opened pages, one at a time: lane u < n holds the position of the page's row u
+    for (uint32_t m = open & ((npg >= 32 ? 0xffffffffu : (1u << npg) - 1u)); m; m &= m - 1) {
+        const int e = __builtin_ctz(m);
+        const int x0 = __shfl(pstv, seg0 + e, 64), x1 = __shfl(pstv, seg0 + e + 1, 64);
+        const int n = x1 - x0;
+        const int pos = l16 < n ? c * kChunk + perm[x0 + l16] : 0;
+        constexpr int RB = 8;  // rows in flight per batch (kept packed)
+        for (int u0 = 0; u0 < n; u0 += RB) {
+            uint4 kp[RB], vp[RB];
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                const int pu = __shfl(pos, seg0 + ((u0 + u) & 15), 64);
+                if (u0 + u < n) {
+                    kp[u] = *reinterpret_cast<const uint4*>(kc + (int64_t)pu * A.st + 8 * l16);
+                    vp[u] = *reinterpret_cast<const uint4*>(vc + (int64_t)pu * A.st + 8 * l16);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                if (u0 + u < n) {  // uniform in the subgroup
+                    float kf[8], vf[8];
+                    Elt<bf16_t>::unpack(kp[u], kf);
+                    Elt<bf16_t>::unpack(vp[u], vf);
+                    float a = 0.0f;
+#pragma unroll
+                    for (int z = 0; z < 8; ++z) a = __builtin_fmaf(q8[z], kf[z], a);
+#pragma unroll
+                    for (int mm = 8; mm >= 1; mm >>= 1) a += __shfl_xor(a, mm, 64);
+                    st.add(A.scale * a, vf);
+                }
+            }
+        }
+    }
+    // unopened pages: mean terms
+#pragma unroll
+    for (int u = 0; u < kCP; ++u) {
+        if (cslot[u] < 0) continue;
+        float vf[8];
+        Elt<bf16_t>::unpack(cpv[u], vf);
+        const int e = cslot[u];
+        st.add(A.scale * __shfl(rl16, seg0 + e, 64) + pln_u[(int64_t)c * PS + ps0 + e], vf);
+    }
+    {
+        uint32_t m = closed;
+        for (int u = 0; u < kCP && m; ++u) m &= m - 1;  // skip the four already done
+        for (; m; m &= m - 1) {
+            const int e = __builtin_ctz(m);
+            float vf[8];
+            load8<bf16_t>(pv_u + ((int64_t)c * PS + ps0 + e) * kD, l16, vf);
+            st.add(A.scale * __shfl(rl16, seg0 + e, 64) + pln_u[(int64_t)c * PS + ps0 + e], vf);
+        }
+    }
+    float* dst = A.part_pg + (rh * A.TG + t) * kPartStride;
+    *reinterpret_cast<float4*>(dst + 8 * l16) = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+    *reinterpret_cast<float4*>(dst + 8 * l16 + 4) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+    if (l16 == 0) { dst[kD] = st.m; dst[kD + 1] = st.l; }
 }
 
 // ---------------------------------------------------------------------------- combine
@@ -889,25 +943,30 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, 
     const int64_t rh = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
     const int d = threadIdx.x & 127;
     if (rh >= nrh) return;
-    float M = -INFINITY;
-    for (int sp = 0; sp < A.nsplit; ++sp) M = fmaxf(M, A.part_fl[sp * A.split_stride + rh * kPartStride + kD]);
-    for (int t = 0; t < A.TG; ++t)
-        if (A.rec[rh * A.TG + t].gid >= 0) M = fmaxf(M, A.part_pg[(rh * A.TG + t) * kPartStride + kD]);
-    float L = 0.0f, O = 0.0f;
-    for (int sp = 0; sp < A.nsplit; ++sp) {
-        const float* pf = A.part_fl + sp * A.split_stride + rh * kPartStride;
-        if (pf[kD] == -INFINITY) continue;
-        const float e = softmax_exp(pf[kD] - M);
-        L = __builtin_fmaf(pf[kD + 1], e, L);
-        O = __builtin_fmaf(pf[d], e, O);
+    // every state's (m, l, o[d]) loaded together: up to 8 flash splits and 16 page slots
+    constexpr int kMax = 8 + kMaxTG;
+    float mm[kMax], ll[kMax], oo[kMax];
+#pragma unroll
+    for (int k = 0; k < kMax; ++k) {
+        mm[k] = -INFINITY;
+        const float* pp = nullptr;
+        if (k < 8) {
+            if (k < A.nsplit) pp = A.part_fl + k * A.split_stride + rh * kPartStride;
+        } else if (k - 8 < A.TG && A.selg[rh * A.TG + (k - 8)] >= 0) {
+            pp = A.part_pg + (rh * A.TG + (k - 8)) * kPartStride;
+        }
+        if (pp) { mm[k] = pp[kD]; ll[k] = pp[kD + 1]; oo[k] = pp[d]; }
     }
-    for (int t = 0; t < A.TG; ++t) {
-        if (A.rec[rh * A.TG + t].gid < 0) continue;
-        const float* pp = A.part_pg + (rh * A.TG + t) * kPartStride;
-        if (pp[kD] == -INFINITY) continue;
-        const float e = softmax_exp(pp[kD] - M);
-        L = __builtin_fmaf(pp[kD + 1], e, L);
-        O = __builtin_fmaf(pp[d], e, O);
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMax; ++k) M = fmaxf(M, mm[k]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMax; ++k) {
+        if (mm[k] == -INFINITY) continue;
+        const float e = softmax_exp(mm[k] - M);
+        L = __builtin_fmaf(ll[k], e, L);
+        O = __builtin_fmaf(oo[k], e, O);
     }
     A.out[rh * kD + d] = O / L;
 }
@@ -1083,6 +1142,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.q = S.q; G.nq = rows; G.pos0 = S.pos0; G.Hq = Hq; G.Hkv = Hkv; G.scale = params->scale;
             G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
             G.rec = S.rec;
+            G.selg = S.selg;
             G.plist = reinterpret_cast<int32_t*>(w + P.off_plist);
             G.poff = reinterpret_cast<int32_t*>(w + P.off_poff);
             G.part_fl = F.part;
