@@ -391,6 +391,8 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
     # query chunk k attends (its keys are in the cache; no attend reads it before k+1).
     side = torch.cuda.Stream(device=dev)
     main = torch.cuda.current_stream(dev)
+    STAGES = ["cand", "select", "flash", "bucket", "pages", "combine"]  # kernels of one call
+    NE = len(STAGES) + 1
 
     def run(evs=None):
         built = {}
@@ -404,7 +406,7 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
                     built[c].record(side)
             if k - nwin >= 0:
                 main.wait_event(built[k - nwin])
-            keep = lod.trace_events(evs[6 * k: 6 * k + 6]) if evs else None
+            keep = lod.trace_events(evs[NE * k: NE * k + NE]) if evs else None
             lod.attend_prefill(cfg, idx, K, V, Q[:, C * k: C * (k + 1)], C * k, ws=ws,
                                out=out[:, C * k: C * (k + 1)])
             if evs:
@@ -413,16 +415,15 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
 
     run()  # warm-up pass (builds every chunk once; the timed pass rebuilds them)
     torch.cuda.synchronize()
-    ev = hip.create(6 * nq)
+    ev = hip.create(NE * nq)
     t0, t1 = hip.create(2)
     hip.record(t0, stream)
     run(ev)
     hip.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = hip.ms(t0, t1)
-    names = ["select", "flash", "bucket", "pages", "combine"]
-    per = {n: sum(hip.ms(ev[6 * k + i], ev[6 * k + i + 1]) for k in range(nq)) for i, n in enumerate(names)}
-    attend_ms = sum(hip.ms(ev[6 * k], ev[6 * k + 5]) for k in range(nq))
+    per = {n: sum(hip.ms(ev[NE * k + i], ev[NE * k + i + 1]) for k in range(nq)) for i, n in enumerate(STAGES)}
+    attend_ms = sum(hip.ms(ev[NE * k], ev[NE * k + NE - 1]) for k in range(nq))
     hip.destroy(ev + [t0, t1])
     log(f"prefill {T}: {total_ms:.1f} ms chunked ({attend_ms:.1f} ms in attention calls)")
 

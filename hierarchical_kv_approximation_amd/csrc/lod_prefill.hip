@@ -355,27 +355,38 @@ struct SelArgs {
     const char* index;
     lod_index_layout_t L;
     int max_chunks, G, W, TG, TP;
+    int nsplit;           // candidate sweeps per tile of columns, each over 1/nsplit of the centroids
+    float* ltop;          // [cols][nsplit][kMaxTG] per sweep: its TG largest lower bounds, descending
+    int32_t* lcnt;        // [cols][nsplit] per sweep: candidates found (may exceed kSplitCap)
+    uint2* lent;          // [cols][nsplit][kSplitCap] per sweep: (group id, upper bound bits)
     int32_t* sel_groups;  // nullable API output [B][nq][Hq][TG], rank order
     int32_t* sel_pages;   // nullable API output [B][nq][Hq][TG][max(TP,1)]
     int32_t* selg;        // [B][nq][Hq][TG] opened groups in ascending id order (-1 pad)
     PairRec* rec;         // [B][nq][Hq][TG] in ascending group order (as selg)
 };
 
-constexpr int kCandCap = 2 * kMaxTG;  // candidates kept per column; beyond: exhaustive path
+constexpr int kCandCap = 2 * kMaxTG;   // candidates kept per column; beyond: exhaustive path
+constexpr int kSplitCap = 2 * kMaxTG;  // candidates kept per column and sweep
 
-struct SelSmem {
+// Grid slot -> (tile of columns, split, KV head).  Workgroups are handed to the eight XCDs
+// in turn by linear id, so the KV head varies fastest: with eight KV heads each XCD (and
+// its L2) serves the centroids of one head.
+struct SelSlot {
+    int tile, split, kvh;
+};
+__device__ __forceinline__ SelSlot sel_slot(int Hkv, int nsplit) {
+    const int j = blockIdx.x + gridDim.x * blockIdx.y;
+    const int rest = j / Hkv;
+    return {rest / nsplit, rest % nsplit, j - rest * Hkv};
+}
+
+struct CandSmem {
     alignas(16) bf16_t kt[2][kFlashKeys][kD];  // double-buffered centroid tiles
     alignas(16) float gkn_t[2][kFlashKeys];
     alignas(16) float gln_t[2][kFlashKeys];
     float qn[kFlashRowHeads];
     float T[kFlashRowHeads];
     int cnt[kFlashRowHeads];
-    int32_t cg[kFlashRowHeads][kCandCap];
-    float cs[kFlashRowHeads][kCandCap];
-    int32_t sel[kFlashRowHeads][kMaxTG];  // rank order
-    int nsel[kFlashRowHeads];
-    uint64_t red[4];
-    int any_overflow;
 };
 
 // Canonical ranking chain q . kbar (fp32 fma in index order) for bf16 rows.
@@ -409,12 +420,22 @@ __device__ __forceinline__ void stage_rows_swizzled(bf16_t (*kt)[kD], const bf16
     }
 }
 
+// Candidate sweep of one split of the centroid tiles for 128 (row, head) columns.
+//
+// Group selection opens the TG groups with the largest q . kbar (ties to the lower id)
+// under the canonical chain.  The MFMA score S of a group is within
+// E = kErrC |q| |kbar| of that chain, so with T the TG-th largest lower bound S - E over
+// the groups, the groups with S + E >= T contain the exact top TG.  Each split finds the
+// TG largest lower bounds and the groups with S + E at or above its own TG-th largest
+// (a local threshold that is never above the global one).  The select step takes the
+// global threshold from the splits' top lists and keeps the listed groups at or above it.
 template <int HG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void prefill_select_kernel(SelArgs A) {
-    __shared__ SelSmem s;
+void prefill_cand_kernel(SelArgs A) {
+    __shared__ CandSmem s;
     constexpr int QT = kFlashRowHeads / HG;
-    const int tile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
+    const SelSlot slot = sel_slot(A.Hkv, A.nsplit);
+    const int tile = slot.tile, split = slot.split, kvh = slot.kvh, b = blockIdx.z, bs = A.seq + b;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int r0 = tile * QT;
     const int nrows = min(QT, A.nq - r0);
@@ -422,7 +443,6 @@ void prefill_select_kernel(SelArgs A) {
     const int nb = nbuilt_prefill(A.pos0 + r0, A.W);
     const int ng = nb * A.G;
     const int TG = A.TG;
-    const int TPW = A.TP > 0 ? A.TP : 1;
     const int64_t gbase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.G;
     const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
     const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
@@ -430,6 +450,13 @@ void prefill_select_kernel(SelArgs A) {
     auto qrow = [&](int n) {  // column n -> its query row (clamped into the tile)
         const int rl = min(n / HG, nrows - 1);
         return A.q + (((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG) * kD;
+    };
+    // column n -> (list slot of this split), -1 for columns past the last row
+    auto list_at = [&](int n) -> int64_t {
+        const int rl = n / HG;
+        if (rl >= nrows) return -1;
+        const int64_t col = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG;
+        return col * A.nsplit + split;
     };
 
     // Q^T operands of this lane's two columns, |q| per column
@@ -453,7 +480,6 @@ void prefill_select_kernel(SelArgs A) {
         s.qn[tid] = sqrtf(ss) * 1.0001f;
         s.cnt[tid] = 0;
     }
-    if (tid == 0) s.any_overflow = 0;
     __syncthreads();
     const float qn[2] = {s.qn[16 * (2 * w) + (l & 15)], s.qn[16 * (2 * w + 1) + (l & 15)]};
 
@@ -473,13 +499,16 @@ void prefill_select_kernel(SelArgs A) {
             }
         }
     };
-    // Centroid tiles of 64 groups stream through two LDS buffers: the loads of tile t+1
-    // (keys, ln n and norm bounds, all straight to LDS) are in flight while tile t is
-    // used.  Each wave waits for its own older loads (vmcnt: the 4, or 6 in wave 0,
-    // instructions of the newer tile may stay outstanding), then a barrier publishes.
+    // This split's centroid tiles [t0, t1) of 64 groups stream through two LDS buffers:
+    // the loads of tile t+1 (keys, ln n and norm bounds, all straight to LDS) are in
+    // flight while tile t is used.  Each wave waits for its own older loads (vmcnt: the
+    // 4, or 6 in wave 0, instructions of the newer tile may stay outstanding), then a
+    // barrier publishes.
     const int ntile = (ng + kFlashKeys - 1) / kFlashKeys;
+    const int t0 = (int)((int64_t)ntile * split / A.nsplit);
+    const int t1 = (int)((int64_t)ntile * (split + 1) / A.nsplit);
     auto issue = [&](int t) {
-        const int buf = t & 1, g0 = t * kFlashKeys, nk = min(kFlashKeys, ng - g0);
+        const int buf = (t - t0) & 1, g0 = t * kFlashKeys, nk = min(kFlashKeys, ng - g0);
         stage_rows_swizzled(s.kt[buf], gk + (int64_t)g0 * kD, nk);
         if (w == 0) {
             const int g = g0 + min(l, nk - 1);
@@ -488,7 +517,7 @@ void prefill_select_kernel(SelArgs A) {
         }
     };
     auto await_tile = [&](int t) {
-        if (t + 1 < ntile) {
+        if (t + 1 < t1) {
             if (w == 0) __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt <= 6
             else __builtin_amdgcn_s_waitcnt(0xF74);         // vmcnt <= 4
         } else {
@@ -496,13 +525,13 @@ void prefill_select_kernel(SelArgs A) {
         }
         __syncthreads();
     };
-    // sweep over the centroid tiles; body(t, buf, nk, S) sees the MFMA scores
+    // sweep over the split's tiles; body(t, buf, nk, S) sees the MFMA scores
     auto sweep = [&](auto&& body) {
-        if (ntile > 0) issue(0);
-        for (int t = 0; t < ntile; ++t) {
-            if (t + 1 < ntile) issue(t + 1);
+        if (t0 < t1) issue(t0);
+        for (int t = t0; t < t1; ++t) {
+            if (t + 1 < t1) issue(t + 1);
             await_tile(t);
-            const int buf = t & 1;
+            const int buf = (t - t0) & 1;
             f32x4_t S[4][2];
             tile_scores(S, buf);
             body(t, buf, min(kFlashKeys, ng - t * kFlashKeys), S);
@@ -510,7 +539,7 @@ void prefill_select_kernel(SelArgs A) {
         }
     };
 
-    // pass A: per column, the k-th largest lower bound S - E (lane-local top-16 lists)
+    // pass A: per column, the TG largest lower bounds S - E (lane-local top-16 lists)
     float lst[2][kMaxTG];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -537,35 +566,43 @@ void prefill_select_kernel(SelArgs A) {
                 }
             }
     });
-    // merge the four lanes of each column: T = TG-th largest with multiplicity
+    // merge the four lanes of each column: the TG largest with multiplicity, descending;
+    // the local threshold is the TG-th (-inf when the split has fewer valid groups)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
+        const int n = 16 * (2 * w + cb) + (l & 15);
+        const int64_t at = list_at(n);
+        float* top = (at >= 0 && (l >> 4) == 0) ? A.ltop + at * kMaxTG : nullptr;
         int taken = 0;
         float T = -INFINITY;
-        for (int round = 0; round < TG; ++round) {
+        for (int round = 0; round < TG && taken < TG; ++round) {
             float h = lst[cb][0];
             float m = fmaxf(h, __shfl_xor(h, 16, 64));
             m = fmaxf(m, __shfl_xor(m, 32, 64));
-            if (m == -INFINITY) { T = -INFINITY; taken = TG; }
             const int mine = (h == m && m != -INFINITY) ? 1 : 0;
             int c = mine + __shfl_xor(mine, 16, 64);
             c += __shfl_xor(c, 32, 64);
-            if (taken < TG) {
-                taken += c;
-                if (taken >= TG) T = m;
-                if (mine) {
+            if (m == -INFINITY) break;  // uniform over the column's four lanes
+            const int upto = min(taken + c, TG);
+            if (top)
+                for (int e = taken; e < upto; ++e) top[e] = m;
+            taken = upto;
+            if (taken >= TG) T = m;
+            if (mine) {
 #pragma unroll
-                    for (int e = 0; e < kMaxTG - 1; ++e) lst[cb][e] = lst[cb][e + 1];
-                    lst[cb][kMaxTG - 1] = -INFINITY;
-                }
+                for (int e = 0; e < kMaxTG - 1; ++e) lst[cb][e] = lst[cb][e + 1];
+                lst[cb][kMaxTG - 1] = -INFINITY;
             }
         }
-        if ((l >> 4) == 0) s.T[16 * (2 * w + cb) + (l & 15)] = T;
+        if (top)
+            for (int e = taken; e < TG; ++e) top[e] = -INFINITY;
+        if ((l >> 4) == 0) s.T[n] = T;
     }
     __syncthreads();
 
-    // pass B: candidates S + E >= T
+    // pass B: this split's candidates S + E >= T
     const float T2[2] = {s.T[16 * (2 * w) + (l & 15)], s.T[16 * (2 * w + 1) + (l & 15)]};
+    const int64_t lat[2] = {list_at(16 * (2 * w) + (l & 15)), list_at(16 * (2 * w + 1) + (l & 15))};
     sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
         const int g0 = t * kFlashKeys;
 #pragma unroll
@@ -580,11 +617,127 @@ void prefill_select_kernel(SelArgs A) {
                     if (valid && ub >= T2[cb]) {
                         const int n = 16 * (2 * w + cb) + (l & 15);
                         const int at = atomicAdd(&s.cnt[n], 1);
-                        if (at < kCandCap) s.cg[n][at] = g0 + key;
+                        if (at < kSplitCap && lat[cb] >= 0)
+                            A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ub));
                     }
                 }
             }
     });
+    if (tid < kFlashRowHeads) {
+        const int64_t at = list_at(tid);
+        if (at >= 0) A.lcnt[at] = s.cnt[tid];
+    }
+}
+
+struct SelSmem {
+    float T[kFlashRowHeads];
+    int cnt[kFlashRowHeads];
+    int32_t cg[kFlashRowHeads][kCandCap];
+    float cs[kFlashRowHeads][kCandCap];
+    int32_t sel[kFlashRowHeads][kMaxTG];  // rank order
+    int nsel[kFlashRowHeads];
+    uint64_t red[4];
+    int any_overflow;
+};
+
+// Selection of 128 (row, head) columns from the candidate lists of the sweeps: global
+// threshold, candidates, exact top TG under the canonical chain, then page ranking of
+// every opened group.
+template <int HG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void prefill_select_kernel(SelArgs A) {
+    __shared__ SelSmem s;
+    constexpr int QT = kFlashRowHeads / HG;
+    const SelSlot slot = sel_slot(A.Hkv, 1);
+    const int tile = slot.tile, kvh = slot.kvh, b = blockIdx.z, bs = A.seq + b;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int r0 = tile * QT;
+    const int nrows = min(QT, A.nq - r0);
+    const int hq0 = kvh * HG;
+    const int nb = nbuilt_prefill(A.pos0 + r0, A.W);
+    const int ng = nb * A.G;
+    const int TG = A.TG;
+    const int TPW = A.TP > 0 ? A.TP : 1;
+    const int64_t gbase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.G;
+    const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
+    const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
+    auto qrow = [&](int n) {  // column n -> its query row (clamped into the tile)
+        const int rl = min(n / HG, nrows - 1);
+        return A.q + (((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG) * kD;
+    };
+    auto col_of = [&](int n) { return ((int64_t)b * A.nq + r0 + n / HG) * A.Hq + hq0 + n % HG; };
+
+    // global threshold per column: the TG-th largest of the splits' top lists (they hold
+    // the TG largest lower bounds of every split, hence those of all groups)
+    if (tid < kFlashRowHeads) {
+        const int n = tid;
+        float T = -INFINITY;
+        int over = 0;
+        if (n / HG < nrows) {
+            const int64_t c0 = col_of(n) * A.nsplit;
+            float top[kMaxTG];
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) top[e] = -INFINITY;
+            for (int sp = 0; sp < A.nsplit; ++sp) {
+                over |= A.lcnt[c0 + sp] > kSplitCap;
+                const float4* src = reinterpret_cast<const float4*>(A.ltop + (c0 + sp) * kMaxTG);
+                float v[kMaxTG];
+#pragma unroll
+                for (int i = 0; i < kMaxTG / 4; ++i) {
+                    const float4 f = 4 * i < TG ? src[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+                }
+#pragma unroll
+                for (int i = 0; i < kMaxTG; ++i) {
+                    float x = i < TG ? v[i] : -INFINITY;
+                    if (x > top[kMaxTG - 1]) {
+#pragma unroll
+                        for (int e = 0; e < kMaxTG; ++e) {
+                            const float hi = fmaxf(top[e], x), lo = fminf(top[e], x);
+                            top[e] = hi;
+                            x = lo;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e)
+                if (e == TG - 1) T = top[e];
+        }
+        s.T[n] = T;
+        s.cnt[n] = over ? kCandCap + 1 : 0;  // an overflowed split forces the exhaustive path
+    }
+    if (tid == 0) s.any_overflow = 0;
+    __syncthreads();
+    // candidates: listed groups with upper bound >= the global threshold (two threads per
+    // column, alternate splits)
+    {
+        const int n = tid & (kFlashRowHeads - 1);
+        if (n / HG < nrows) {
+            const int64_t c0 = col_of(n) * A.nsplit;
+            const float T = s.T[n];
+            for (int sp = tid >> 7; sp < A.nsplit; sp += 2) {
+                const int c = min(A.lcnt[c0 + sp], kSplitCap);
+                const uint4* src = reinterpret_cast<const uint4*>(A.lent + (c0 + sp) * kSplitCap);
+                uint4 e[kSplitCap / 2];
+#pragma unroll
+                for (int i = 0; i < kSplitCap / 2; ++i)
+                    if (2 * i < c) e[i] = src[i];
+#pragma unroll
+                for (int i = 0; i < kSplitCap / 2; ++i) {
+                    if (2 * i < c && __uint_as_float(e[i].y) >= T) {
+                        const int at = atomicAdd(&s.cnt[n], 1);
+                        if (at < kCandCap) s.cg[n][at] = (int32_t)e[i].x;
+                    }
+                    if (2 * i + 1 < c && __uint_as_float(e[i].w) >= T) {
+                        const int at = atomicAdd(&s.cnt[n], 1);
+                        if (at < kCandCap) s.cg[n][at] = (int32_t)e[i].z;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
 
     // canonical chains for the candidates
     for (int x = tid; x < kFlashRowHeads * kCandCap; x += kThreads) {
@@ -982,8 +1135,9 @@ constexpr int kPrefillBatchRows = 2048;
 
 struct PrefillPlan {
     int rows;    // rows per batch (<= n_q, multiple of kChunk unless n_q is smaller)
-    int nsplit;  // flash workgroups per (tile, KV head): enough workgroups for small batches
-    size_t off_selg, off_rec, off_pfl, off_ppg, off_plist, off_poff, bytes;
+    int nsplit;  // candidate sweeps and flash workgroups per (tile, KV head): enough
+                 // workgroups for small batches
+    size_t off_selg, off_rec, off_pfl, off_ppg, off_plist, off_poff, off_ltop, off_lcnt, off_lent, bytes;
 };
 
 // Workspace of one batch of rows of one sequence (sequences run one after another).
@@ -1004,6 +1158,9 @@ static PrefillPlan plan_prefill(const lod_params* p, int n_q) {
     P.off_ppg = o; o = align256(o + rh * TG * kPartStride * 4);
     P.off_plist = o; o = align256(o + units * kChunk * HG * TG * 4);
     P.off_poff = o; o = align256(o + units * 2 * 4);
+    P.off_ltop = o; o = align256(o + (size_t)P.nsplit * rh * kMaxTG * 4);
+    P.off_lcnt = o; o = align256(o + (size_t)P.nsplit * rh * 4);
+    P.off_lent = o; o = align256(o + (size_t)P.nsplit * rh * kSplitCap * 8);
     P.bytes = o;
     return P;
 }
@@ -1014,19 +1171,22 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     constexpr int QT = kFlashRowHeads / HG;
     const int ntiles = (S.nq + QT - 1) / QT;
     trace_point(0, st);
-    hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles, S.Hkv, batch), dim3(kThreads), 0, st, S);
+    hipLaunchKernelGGL((prefill_cand_kernel<HG>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads), 0,
+                       st, S);
     trace_point(1, st);
-    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0, st, F);
+    hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
     trace_point(2, st);
-    hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0, st, F);
     trace_point(3, st);
+    hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
+    trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
     hipLaunchKernelGGL((prefill_pages_kernel<HG>), dim3((maxpairs + kPairsPerWG - 1) / kPairsPerWG,
                        nunits_q * S.Hkv * batch), dim3(kThreads), 0, st, P);
-    trace_point(4, st);
+    trace_point(5, st);
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + 1) / 2)), dim3(kThreads), 0, st, P, nrh);
-    trace_point(5, st);
+    trace_point(6, st);
 }
 
 }  // namespace lodi
@@ -1126,6 +1286,10 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             S.sel_pages = sel_pages ? sel_pages + row0 * Hq * TG * TPW : nullptr;
             S.selg = reinterpret_cast<int32_t*>(w + P.off_selg);
             S.rec = reinterpret_cast<PairRec*>(w + P.off_rec);
+            S.nsplit = P.nsplit;
+            S.ltop = reinterpret_cast<float*>(w + P.off_ltop);
+            S.lcnt = reinterpret_cast<int32_t*>(w + P.off_lcnt);
+            S.lent = reinterpret_cast<uint2*>(w + P.off_lent);
             S.seq = b;
             FlashArgs F{};
             F.k = reinterpret_cast<const bf16_t*>(kv.k);

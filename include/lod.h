@@ -218,9 +218,9 @@ int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_
  * Instrumentation (profiling only; results are unchanged).  While `events` is non-null,
  * every later lod_attend_decode / lod_attend_prefill call made from the same host thread
  * records events[0] on its stream before its first kernel and events[1 + k] after its
- * k-th kernel (decode: k = 0 scan, 1 open-and-combine; bf16 prefill: k = 0 select,
- * 1 flash, 2 bucket, 3 pages, 4 combine, recorded again for every batch of rows, so
- * the last batch's times remain).  `events` points to n_events
+ * k-th kernel (decode: k = 0 scan, 1 open-and-combine; bf16 prefill: k = 0 candidate
+ * sweep, 1 select, 2 flash, 3 bucket, 4 pages, 5 combine, recorded again for every batch
+ * of rows, so the last batch's times remain).  `events` points to n_events
  * hipEvent_t handles created by the caller, who reads them with hipEventElapsedTime;
  * kernels beyond n_events - 1 record nothing.  Pass NULL to stop.  Not for captured graphs.
  */
