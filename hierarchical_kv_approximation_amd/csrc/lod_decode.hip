@@ -24,6 +24,7 @@
 //  3. combine grid (query heads, batch).  Log-sum-exp merge of every partial state.
 // Partial states are (o[d] = sum w v, m, l) relative to their own max m.
 #include "lod_device.h"
+#include "lod_mfma.h"
 
 namespace lodi {
 
@@ -416,12 +417,13 @@ constexpr int kOpenCand = 128;  // canonical re-scoring candidates kept per head
 constexpr int kPartLds = 40;    // scan partial states per head copied to LDS (bf16 path)
 constexpr int kPartLdsFloats = (kPartLds * (kPartStride / 4) + 63) / 64 * 64 * 4;
 constexpr int kMetaMax = 320;   // int16 entries of one chunk's meta row (>= meta_stride)
+constexpr int kMetaRows = 2 * kMaxTG;  // meta rows in LDS: candidates prefetched when this few
 constexpr int kGPW = kMaxTG / 4;             // opened groups per wave (at most)
 constexpr int kItemsPerWave = kGPW * kChunk; // exact rows of a wave's groups (two-tier bound)
 
 template <typename T>
 struct OpenSmem {
-    alignas(16) int16_t meta[kMaxTG][kMetaMax];  // meta row of each opened group's chunk
+    alignas(16) int16_t meta[kMetaRows][kMetaMax];  // meta rows: prefetched candidates' or opened groups'
     float qs[kD];
     uint64_t sel[kMaxTG];
     int nsel;
@@ -435,9 +437,8 @@ struct OpenSmem {
     float scan_m, scan_l;      // merged state of the scan workgroups' partials
     float scan_o[kD];
     // selection from MFMA scores (bf16 path)
-    float wl[4][kMaxTG];       // per wave: its TG largest lower bounds
-    float thr;                 // TG-th largest lower bound of the head
-    int ncand, over;
+    alignas(16) float wl[4][4];  // per wave: its largest lower bounds (at most 4)
+    int ncand;
     int32_t cg[kOpenCand];     // candidates: group id, canonical score, MFMA score, ln n
     float cs[kOpenCand];
     float cS[kOpenCand], cL[kOpenCand];
@@ -488,6 +489,35 @@ __device__ __forceinline__ void open_merge_scan(OpenSmem<T>& s, const float* par
 // page rankings (one lane per (group, page), 16-lane segmented top-k), then the item
 // lists, so the dependent global round trips are few.  Every 16-lane subgroup then
 // streams items with its loads batched into its online-softmax state st.
+// Block update of a 16-lane online softmax with up to OB terms (logit lam[x], -inf: none;
+// value: 8 elements of this lane packed in vp[x]): one rescale to the new maximum, then
+// the weighted values.
+template <typename T, int OB, int U>
+__device__ __forceinline__ void open_block_add(Online& st, const float* lam, const u32x4_t (*vp)[U]) {
+    constexpr int P16 = Elt<T>::kPer16;
+    float mb = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < OB; ++x) mb = fmaxf(mb, lam[x]);
+    if (mb == -INFINITY) return;
+    const float mn = fmaxf(st.m, mb);
+    const float a = softmax_exp(st.m - mn);  // st.m = -inf -> 0
+    st.l *= a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] *= a;
+#pragma unroll
+    for (int x = 0; x < OB; ++x) {
+        if (lam[x] == -INFINITY) continue;  // no term: its value registers were not loaded
+        const float w = softmax_exp(lam[x] - mn);
+        float vf[8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) Elt<T>::unpack(vp[x][u], vf + u * P16);
+        st.l += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.o[e] = __builtin_fmaf(w, vf[e], st.o[e]);
+    }
+    st.m = mn;
+}
+
 template <typename T, int OB>
 __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int seq, int kvh, int64_t head,
                            const float* q8, Online& st) {
@@ -600,7 +630,7 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
     const int nex = s.nex[wave];
     constexpr int P16 = Elt<T>::kPer16, U = 8 / P16;  // 16-byte pieces per 8 elements
     for (int base = 0; base < nex; base += 4 * OB) {
-        uint4 kp[OB][U], vp[OB][U];  // rows kept packed until used
+        u32x4_t kp[OB][U], vp[OB][U];  // rows kept packed until used
 #pragma unroll
         for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
@@ -608,48 +638,51 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
                 const int pos = s.ex[wave][it];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    kp[x][u] = *reinterpret_cast<const uint4*>(kb + (int64_t)pos * A.st + 8 * l16 + u * P16);
-                    vp[x][u] = *reinterpret_cast<const uint4*>(vb + (int64_t)pos * A.st + 8 * l16 + u * P16);
+                    kp[x][u] = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)pos * A.st + 8 * l16 + u * P16);
+                    vp[x][u] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)pos * A.st + 8 * l16 + u * P16);
                 }
             }
         }
+        // block update of the subgroup's online softmax: dot products and their
+        // reductions side by side, one rescale, then the weighted values
+        float lam[OB];
 #pragma unroll
         for (int x = 0; x < OB; ++x) {
-            const int it = base + sgw + 4 * x;
-            if (it < nex) {
-                float kf[8], vf[8];
+            float kf[8];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    Elt<T>::unpack(kp[x][u], kf + u * P16);
-                    Elt<T>::unpack(vp[x][u], vf + u * P16);
-                }
-                float a = 0.0f;
+            for (int u = 0; u < U; ++u) Elt<T>::unpack(kp[x][u], kf + u * P16);
+            float a = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
-#pragma unroll
-                for (int m = 8; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-                st.add(A.scale * a, vf);
-            }
+            for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
+            lam[x] = a;
         }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+            for (int x = 0; x < OB; ++x) lam[x] += __shfl_xor(lam[x], m, 64);
+#pragma unroll
+        for (int x = 0; x < OB; ++x) lam[x] = base + sgw + 4 * x < nex ? A.scale * lam[x] : -INFINITY;
+        open_block_add<T, OB, U>(st, lam, vp);
     }
     const int ncp = s.ncp[wave];
     for (int base = 0; base < ncp; base += 4 * OB) {
-        float vf[OB][8];
+        u32x4_t vp[OB][U];
+        float lam[OB];
 #pragma unroll
         for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
+            lam[x] = -INFINITY;
             if (it < ncp) {
                 const int k = s.cp[wave][it] >> 8, e = s.cp[wave][it] & 255, i = wave + 4 * k;
                 const uint32_t gid = key_id(s.sel[i]);
                 const int c = gid / A.G, ps0 = mrowp(i)[gid % A.G];
-                load8<T>(pv_u + ((int64_t)c * PS + ps0 + e) * kD, l16, vf[x]);
+                const T* row = pv_u + ((int64_t)c * PS + ps0 + e) * kD + 8 * l16;
+#pragma unroll
+                for (int u = 0; u < U; ++u) vp[x][u] = *reinterpret_cast<const u32x4_t*>(row + u * P16);
+                lam[x] = s.cl[wave][it];
             }
         }
-#pragma unroll
-        for (int x = 0; x < OB; ++x) {
-            const int it = base + sgw + 4 * x;
-            if (it < ncp) st.add(s.cl[wave][it], vf[x]);
-        }
+        open_block_add<T, OB, U>(st, lam, vp);
     }
 }
 
@@ -789,9 +822,6 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
 // {g : S_g + E_g >= T}, T being the k-th largest S_g - E_g, and only those candidates
 // are re-scored with the canonical chain.  Selection stays bit-exact; logits of the
 // coarse terms use S.
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMRows = 128;     // rows per chunk of the MFMA kernels
 constexpr int kWinRows = 128;   // window rows per window workgroup (MFMA path)
@@ -1187,50 +1217,85 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         for (int u = 0; u < SPT; ++u)
             if (ln[u] != -INFINITY) mx = fmaxf(mx, sv[u] - eq * kn[u]);
     }
-    // 1b. each wave: its TG largest maxima (with multiplicity)
+    // 1b. each wave: its R largest maxima (with multiplicity), R = min(TG, 4).  Any TG of
+    //     them are maxima of distinct threads, so the TG-th largest of the 4R values is
+    //     again a lower bound of the TG-th largest over all groups.
+    const int R = TG < 4 ? TG : 4;
     {
         int taken = 0;
-        for (int round = 0; round < TG && taken < TG; ++round) {
+        for (int round = 0; round < R && taken < R; ++round) {
             const float m = wave_max_f32(mx, 64);
             if (m == -INFINITY) break;
             const bool mine = mx == m;
             const int c = __popcll(__ballot(mine));
             if (lane == 0)
-                for (int x = 0; x < c && taken + x < TG; ++x) s.wl[wave][taken + x] = m;
+                for (int x = 0; x < c && taken + x < R; ++x) s.wl[wave][taken + x] = m;
             taken += c;
             if (mine) mx = -INFINITY;
         }
         if (lane == 0)
-            for (int x = taken; x < TG; ++x) s.wl[wave][x] = -INFINITY;
+            for (int x = taken < R ? taken : R; x < 4; ++x) s.wl[wave][x] = -INFINITY;
     }
-    if (tid == 0) { s.ncand = 0; s.over = 0; s.meta_ready = 0; }
+    if (tid == 0) { s.ncand = 0; s.meta_ready = 0; }
     __syncthreads();
-    // 1c. T = the TG-th largest over the four lists (-inf if fewer than TG groups)
-    if (wave == 0) {
-        const int nv = 4 * TG;
-        const float v = lane < nv ? s.wl[lane / TG][lane % TG] : -INFINITY;
-        int cge = 0;
-        for (int x = 0; x < nv; ++x) cge += s.wl[x / TG][x % TG] >= v;
-        const float T = wave_max_f32((v != -INFINITY && cge >= TG) ? v : -INFINITY, 64);
-        if (lane == 0) s.thr = T;
-    }
-    __syncthreads();
-    // 1d. candidates: S + E >= T (a single block of groups is still in registers)
+    // 1c. every thread: T = the TG-th largest of the 16 list entries (sorting network;
+    //     -inf when fewer than TG are finite)
+    float T;
     {
-        const float T = s.thr;
-        for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
-            if (ng > SPT * kThreads) load_scores(g0);
+        float v[16];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            const float4 f = *reinterpret_cast<const float4*>(&s.wl[w4][0]);
+            v[4 * w4] = f.x; v[4 * w4 + 1] = f.y; v[4 * w4 + 2] = f.z; v[4 * w4 + 3] = f.w;
+        }
+        // bitonic sort, descending
+#pragma unroll
+        for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int x = i ^ j;
+                    if (x > i) {
+                        const bool desc = (i & k) == 0;
+                        const float hi = fmaxf(v[i], v[x]), lo = fminf(v[i], v[x]);
+                        v[i] = desc ? hi : lo;
+                        v[x] = desc ? lo : hi;
+                    }
+                }
+        T = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (e == TG - 1) T = v[e];
+    }
+    // 1d. candidates: S + E >= T (a single block of groups is still in registers); one
+    //     LDS atomic per wave, positions from a wave prefix sum of the per-thread counts
+    for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
+        if (ng > SPT * kThreads) load_scores(g0);
+        uint32_t cm = 0;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u)
+            if (ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T) cm |= 1u << u;
+        const int cnt = __popc(cm);
+        int incl = cnt;
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) {
+            const int o = __shfl_up(incl, sh, 64);
+            if (lane >= sh) incl += o;
+        }
+        int base = 0;
+        if (lane == 63 && incl > 0) base = atomicAdd(&s.ncand, incl);
+        base = __shfl(base, 63, 64) + incl - cnt;
+        if (cm) {
 #pragma unroll
             for (int u = 0; u < SPT; ++u) {
-                const int g = g0 + tid + kThreads * u;
-                const bool c = ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T;
-                const uint64_t mk = __ballot(c);
-                int base = 0;
-                if (lane == 0 && mk) base = atomicAdd(&s.ncand, __popcll(mk));
-                base = __shfl(base, 0, 64);
-                if (c) {
-                    const int at = base + __popcll(mk & ((1ull << lane) - 1ull));
-                    if (at < kOpenCand) { s.cg[at] = g; s.cS[at] = sv[u]; s.cL[at] = ln[u]; }
+                if (cm & (1u << u)) {
+                    if (base < kOpenCand) {
+                        s.cg[base] = g0 + tid + kThreads * u;
+                        s.cS[base] = sv[u];
+                        s.cL[base] = ln[u];
+                    }
+                    ++base;
                 }
             }
         }
@@ -1238,9 +1303,12 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     __syncthreads();
     const int ncand = s.ncand;
     if (ncand <= kOpenCand) {
-        // the opened groups are among the candidates: with at most kMaxTG of them, their
-        // meta rows go to LDS now, overlapping the canonical re-scoring
-        if (ncand <= kMaxTG) {
+        // the opened groups are among the candidates: with at most kMetaRows of them,
+        // their meta rows go to LDS now (row x: candidate x), overlapping the canonical
+        // re-scoring; otherwise the page step loads the opened groups' rows (row i: the
+        // group of rank i)
+        const bool prefetch = ncand <= kMetaRows;
+        if (prefetch) {
             const int ms16 = A.L.meta_stride / 8;
             const int npiece = ncand * ms16;
             int16_t* mflat = &s.meta[0][0];
@@ -1275,13 +1343,13 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
             for (int y = 0; y < ncand; ++y) rank += rank_key(s.cs[y], (uint32_t)s.cg[y]) > key;
             if (rank < TG) {
                 s.sel[rank] = key;
-                s.mrow[rank] = x;
+                s.mrow[rank] = prefetch ? x : rank;
                 s.sub_lam[rank] = A.scale * s.cS[x] + s.cL[x];
             }
         }
         if (tid == 0) {
             s.nsel = ncand < TG ? ncand : TG;
-            s.meta_ready = ncand <= kMaxTG;
+            s.meta_ready = prefetch;
         }
     } else {
         // exhaustive: canonical score of every non-empty group, workgroup-wide top-TG
@@ -1336,11 +1404,12 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     const int nsel = s.nsel;
     if (A.sel_groups && tid < TG) A.sel_groups[head * TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
     // the opened groups' mean values (loads in flight during the page work)
-    float vsub[kMaxTG];
+    // (raw bits: converted where used, so nothing waits for them before then)
+    uint32_t vsub[kMaxTG];
     if (tid < kD) {
 #pragma unroll
         for (int i = 0; i < kMaxTG; ++i)
-            vsub[i] = i < nsel ? bf16_bits_to_f32(gv[(int64_t)key_id(s.sel[i]) * kD + tid]) : 0.0f;
+            vsub[i] = i < nsel ? gv[(int64_t)key_id(s.sel[i]) * kD + tid] : 0u;
     }
 
     Online st;
@@ -1349,43 +1418,50 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     open_stash(s, st);
     if (part_in_lds) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (part_in_lds && tid < kD) {
-        float M = -INFINITY, L = 0.0f, O = 0.0f;
-        for (int k = 0; k < nscan; ++k) {
-            const float* pp = &s.plds[k * kPartStride];
-            const float mk = pp[kD];
-            if (mk == -INFINITY) continue;
-            const float mn = fmaxf(M, mk);
-            const float a = softmax_exp(M - mn), e = softmax_exp(mk - mn);
-            L = __builtin_fmaf(pp[kD + 1], e, L * a);
-            O = __builtin_fmaf(pp[tid], e, O * a);
-            M = mn;
-        }
-        s.scan_o[tid] = O;
-        if (tid == 0) { s.scan_m = M; s.scan_l = L; }
-    }
-    if (part_in_lds) __syncthreads();
     // out = scan state - opened groups' coarse terms (the very logits the scan used) +
-    // the exact terms of the opened groups
+    // the exact terms of the opened groups.  Thread tid < kD takes dimension tid; the
+    // scan state comes from the partials in LDS (maximum first, then the sums), or from
+    // the merge of waves 2-3.
     if (tid < kD) {
-        float M = s.scan_m;
+        float SM, SL, SO;
+        if (part_in_lds) {
+            SM = -INFINITY;
+            for (int k = 0; k < nscan; ++k) SM = fmaxf(SM, s.plds[k * kPartStride + kD]);
+            SL = 0.0f;
+            SO = 0.0f;
+            if (SM != -INFINITY) {
+#pragma unroll 4
+                for (int k = 0; k < nscan; ++k) {
+                    const float* pp = &s.plds[k * kPartStride];
+                    const float e = pp[kD] == -INFINITY ? 0.0f : softmax_exp(pp[kD] - SM);
+                    SL = __builtin_fmaf(pp[kD + 1], e, SL);
+                    SO = __builtin_fmaf(pp[tid], e, SO);
+                }
+            }
+        } else {
+            SM = s.scan_m;
+            SL = s.scan_l;
+            SO = s.scan_o[tid];
+        }
+        float M = SM;
+#pragma unroll
         for (int k = 0; k < 16; ++k) M = fmaxf(M, s.sm[k]);
         float L = 0.0f, O = 0.0f;
-        if (s.scan_m != -INFINITY) {
-            const float e = softmax_exp(s.scan_m - M);
-            L = s.scan_l * e;
-            O = s.scan_o[tid] * e;
+        if (SM != -INFINITY) {
+            const float e = softmax_exp(SM - M);
+            L = SL * e;
+            O = SO * e;
 #pragma unroll
             for (int i = 0; i < kMaxTG; ++i) {
                 if (i >= nsel) break;
                 const float w = softmax_exp(s.sub_lam[i] - M);
                 L -= w;
-                O = __builtin_fmaf(-w, vsub[i], O);
+                O = __builtin_fmaf(-w, bf16_bits_to_f32(vsub[i]), O);
             }
         }
+#pragma unroll
         for (int k = 0; k < 16; ++k) {
-            if (s.sm[k] == -INFINITY) continue;
-            const float e = softmax_exp(s.sm[k] - M);
+            const float e = s.sm[k] == -INFINITY ? 0.0f : softmax_exp(s.sm[k] - M);
             L = __builtin_fmaf(s.sl[k], e, L);
             O = __builtin_fmaf(s.so[k][tid], e, O);
         }

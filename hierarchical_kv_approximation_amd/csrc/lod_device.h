@@ -9,6 +9,7 @@
 namespace lodi {
 
 typedef uint16_t bf16_t;  // bfloat16 bits
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16 raw bytes
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -33,12 +34,22 @@ template <> struct Elt<float> {
         o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
         o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
     }
+    __device__ static __forceinline__ void unpack(const u32x4_t& u, float* o) {
+        o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+        o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+    }
 };
 template <> struct Elt<bf16_t> {
     static constexpr int kPer16 = 8;
     __device__ static __forceinline__ float to_f32(bf16_t x) { return bf16_bits_to_f32(x); }
     __device__ static __forceinline__ bf16_t store_round(float x) { return f32_to_bf16_rne(x); }
     __device__ static __forceinline__ void unpack(const uint4& u, float* o) {
+        o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+        o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+        o[4] = __uint_as_float(u.z << 16); o[5] = __uint_as_float(u.z & 0xffff0000u);
+        o[6] = __uint_as_float(u.w << 16); o[7] = __uint_as_float(u.w & 0xffff0000u);
+    }
+    __device__ static __forceinline__ void unpack(const u32x4_t& u, float* o) {
         o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
         o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
         o[4] = __uint_as_float(u.z << 16); o[5] = __uint_as_float(u.z & 0xffff0000u);

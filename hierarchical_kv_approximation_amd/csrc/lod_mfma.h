@@ -1,4 +1,4 @@
-// lod_mfma.h -- MFMA operand types and small helpers shared by the prefill kernels.
+// lod_mfma.h -- MFMA operand types and small helpers shared by the MFMA kernels.
 //
 // v_mfma_f32_16x16x32_bf16 lane layout on gfx950 (checked on the device):
 //   A (16 x 32): lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
