@@ -414,7 +414,7 @@ __device__ __forceinline__ void wave_sync() {
 
 constexpr int kOpenBatch = 4;   // items per subgroup whose loads are issued together
 constexpr int kOpenCand = 128;  // canonical re-scoring candidates kept per head
-constexpr int kPartLds = 40;    // scan partial states per head copied to LDS (bf16 path)
+constexpr int kPartLds = kScanMaxSlots;  // scan partial states per head copied to LDS (bf16 path)
 constexpr int kPartLdsFloats = (kPartLds * (kPartStride / 4) + 63) / 64 * 64 * 4;
 constexpr int kMetaMax = 320;   // int16 entries of one chunk's meta row (>= meta_stride)
 constexpr int kMetaRows = 2 * kMaxTG;  // meta rows in LDS: candidates prefetched when this few
@@ -824,7 +824,6 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
 // coarse terms use S.
 
 constexpr int kMRows = 128;     // rows per chunk of the MFMA kernels
-constexpr int kWinRows = 128;   // window rows per window workgroup (MFMA path)
 
 template <int HG>
 struct MSmem {
@@ -1007,69 +1006,6 @@ __device__ void mfma_exact_rows(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* 
     }
 }
 
-// Coarse terms of n groups (tiles of kMRows): MFMA scores S (written to sdst, row h at
-// sdst + h * sstride), logits scale * S + ln n (empty groups: none), online softmax and
-// PV into o.
-template <int HG>
-__device__ void mfma_scan_groups(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* gk, const bf16_t* gv,
-                                   const float* gln, int n, float scale, float* sdst, int64_t sstride,
-                                   float (*o)[4]) {
-    constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int hq = tid / (32 * RPH);
-    for (int c0 = 0; c0 < n; c0 += kMRows) {
-        const int nt = min(kMRows, n - c0);
-        if (tid < nt) s.lnn[tid] = gln[c0 + tid];
-        auto krow = [&](int r) { return gk + (int64_t)(c0 + r) * kD; };
-        auto vrow = [&](int r) { return gv + (int64_t)(c0 + r) * kD; };
-        mfma_issue_v<HG>(s, vrow, nt);
-        mfma_scores<HG>(s.sc, qa, krow, nt);
-        __syncthreads();
-        for (int x = tid; x < HG * nt; x += kThreads) {
-            const int h = x / nt, r = x % nt;
-            sdst[(int64_t)h * sstride + c0 + r] = s.sc[h][r];
-        }
-        for (int h = w; h < HG; h += 4) {
-            float lam[kMRows / 64], mx = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < kMRows / 64; ++k) {
-                const int r = l + 64 * k;
-                // the same expression the open kernel uses for the opened groups it subtracts
-                lam[k] = (r < nt && s.lnn[r] != -INFINITY) ? scale * s.sc[h][r] + s.lnn[r] : -INFINITY;
-                mx = fmaxf(mx, lam[k]);
-            }
-            mx = wave_max_f32(mx, 64);
-            const float mold = s.mrun[h];
-            const float mn = fmaxf(mold, mx);
-            float ls = 0.0f;
-#pragma unroll
-            for (int k = 0; k < kMRows / 64; ++k) {
-                const int r = l + 64 * k;
-                const float wgt = lam[k] == -INFINITY ? 0.0f : softmax_exp(lam[k] - mn);
-                if (r < nt) s.wT[r][h] = wgt;
-                ls += wgt;
-            }
-            ls = wave_sum_f32(ls, 64);
-            if (l == 0) {
-                const float a = mold == -INFINITY ? 0.0f : softmax_exp(mold - mn);
-                s.alpha[h] = a;
-                s.lrun[h] = s.lrun[h] * a + ls;
-                s.mrun[h] = mn;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float a = (4 * hq + i < HG) ? s.alpha[4 * hq + i] : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[i][e] *= a;
-        }
-        mfma_wait_lds();
-        mfma_pv<HG>(s, nt, o);
-        __syncthreads();
-    }
-}
-
 template <int HG>
 __device__ __forceinline__ void mfma_init(MSmem<HG>& s, float (*o)[4]) {
     const int tid = threadIdx.x;
@@ -1081,61 +1017,241 @@ __device__ __forceinline__ void mfma_init(MSmem<HG>& s, float (*o)[4]) {
         for (int e = 0; e < 4; ++e) o[i][e] = 0.0f;
 }
 
-// Decode launch 1 (bf16): per (sequence, KV head), a slice of group summaries
-// (MFMA scores written out for the selection; coarse softmax over every non-empty
-// group) or an exact window tile (tile 0 also takes the sinks).
+// ---------------------------------------------------------------------------- scan (bf16)
+
+// The scan of a (sequence, KV head) unit walks one list of 64-row tiles: the group
+// summaries of every summarised chunk (coarse rows, logit scale * S + ln n), then the
+// exact rows of the sinks and the block window (logit scale * S).  The unit's
+// workgroups take equal runs of that list.  A tile's key and value rows are read with
+// flat 16-byte loads (consecutive lanes, consecutive bytes) into registers one tile
+// ahead, then written to LDS: keys row-major with their 16-byte chunks XOR-swizzled by
+// row, values transposed (dimension-major) in 8-row blocks XOR-swizzled by dimension, so
+// that both MFMA operand reads are 16-byte and spread over the banks.  Scores S = q K^T
+// and the value sums O^T = V^T P^T run on MFMA; P enters as bf16 hi + lo.
+constexpr int kSTile = kScanTile;                      // rows per scan tile
+constexpr int kSPieces = kSTile * kD / 8 / kThreads;   // 16-byte pieces per thread and row kind
+constexpr int kSWStride = kSTile + 8;                  // bf16 per head row of the weights
+
 template <int HG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+struct MScanSmem {
+    alignas(16) bf16_t kl[kSTile][kD];   // key rows (swizzled chunks)
+    alignas(16) bf16_t vt[kD][kSTile];   // value columns: vt[d][8 * (b ^ (d / 8 % 8)) + j] = V[8b + j][d]
+    alignas(16) bf16_t wh[16][kSWStride];  // softmax weights [head][row], bf16 hi (heads >= HG: 0)
+    alignas(16) bf16_t wl[16][kSWStride];  // and lo parts
+    float bias[kSTile];                  // ln n of a coarse tile's groups, 0 for exact rows
+    float sc[HG][kSTile];                // MFMA scores of the tile
+    float mrun[HG], lrun[HG], alpha[16];
+};
+
+// Rows of one unit: coarse tiles first, then the exact rows (list index x is position x
+// for the sinks, w0 + x - ns after them).
+struct ScanSrc {
+    const bf16_t* gk;
+    const bf16_t* gv;
+    const float* gln;
+    int ng;
+    const bf16_t* kb;
+    const bf16_t* vb;
+    int64_t st;
+    int ns, w0, nex;
+};
+
+// One tile in registers: pieces tid + kThreads * i (row piece / 16, chunk piece % 16) of
+// its key and value rows (rows past the tile repeat its last row), and the bias of row tid.
+struct ScanRegs {
+    u32x4_t k[kSPieces], v[kSPieces];
+    float bias;
+};
+
+__device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t, int ntc) {
+    const int tid = threadIdx.x;
+    if (t < ntc) {
+        const int r0 = t * kSTile, n = min(kSTile, S.ng - r0);
+#pragma unroll
+        for (int i = 0; i < kSPieces; ++i) {
+            const int pc = tid + kThreads * i, row = min(pc >> 4, n - 1);
+            const int64_t off = (int64_t)(r0 + row) * kD + 8 * (pc & 15);
+            R.k[i] = *reinterpret_cast<const u32x4_t*>(S.gk + off);
+            R.v[i] = *reinterpret_cast<const u32x4_t*>(S.gv + off);
+        }
+        R.bias = tid < kSTile ? S.gln[r0 + min(tid, n - 1)] : 0.0f;
+    } else {
+        const int x0 = (t - ntc) * kSTile, n = min(kSTile, S.nex - x0);
+#pragma unroll
+        for (int i = 0; i < kSPieces; ++i) {
+            const int pc = tid + kThreads * i, x = x0 + min(pc >> 4, n - 1);
+            const int pos = x < S.ns ? x : S.w0 + (x - S.ns);
+            const int64_t off = (int64_t)pos * S.st + 8 * (pc & 15);
+            R.k[i] = *reinterpret_cast<const u32x4_t*>(S.kb + off);
+            R.v[i] = *reinterpret_cast<const u32x4_t*>(S.vb + off);
+        }
+        R.bias = 0.0f;
+    }
+}
+
+template <int HG>
+__device__ __forceinline__ void scan_stage(MScanSmem<HG>& s, const ScanRegs& R) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kSPieces; ++i) {
+        const int pc = tid + kThreads * i, row = pc >> 4, c = pc & 15;
+        *reinterpret_cast<u32x4_t*>(&s.kl[row][8 * (c ^ (row & 15))]) = R.k[i];
+        // value piece: dims 8c .. 8c+7 of row `row` go down column positions of vt
+        const int pos = 8 * ((row >> 3) ^ (c & 7)) + (row & 7);
+        const uint32_t w4[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s.vt[8 * c + 2 * e][pos] = (bf16_t)(w4[e] & 0xffffu);
+            s.vt[8 * c + 2 * e + 1][pos] = (bf16_t)(w4[e] >> 16);
+        }
+    }
+    if (tid < kSTile) s.bias[tid] = R.bias;
+}
+
+// MFMA scores of the staged tile: wave w takes rows 16w .. 16w+15 (query heads are the A
+// rows, rows >= HG zero).  Coarse tiles also write them to sdst (row h at h * sstride).
+template <int HG>
+__device__ __forceinline__ void scan_scores(MScanSmem<HG>& s, const bf16x8_t* qa, int n, bool coarse,
+                                            float* sdst, int64_t sstride) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int row = 16 * w + (l & 15);
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
+        const bf16x8_t kbv = *reinterpret_cast<const bf16x8_t*>(&s.kl[row][8 * chunk]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kbv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * (l >> 4) + r;
+        if (h < HG) {
+            s.sc[h][row] = acc[r];
+            if (coarse && row < n) sdst[(int64_t)h * sstride + row] = acc[r];
+        }
+    }
+}
+
+// O^T += V^T P^T over the staged tile: wave w takes dims 32w .. 32w+31 (two 16-row MFMA
+// blocks); lane l holds o[mb][i] = O^T[32w + 16mb + 4(l/16) + i][head l%16].
+template <int HG>
+__device__ __forceinline__ void scan_pv(const MScanSmem<HG>& s, f32x4_t* o) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int kb = 0; kb < kSTile / 32; ++kb) {
+        const int rb = 4 * kb + (l >> 4);  // 8-row block of this lane's operand
+        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&s.wh[l & 15][8 * rb]);
+        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&s.wl[l & 15][8 * rb]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int d = 32 * w + 16 * mb + (l & 15);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.vt[d][8 * (rb ^ ((d >> 3) & 7))]);
+            o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, o[mb], 0, 0, 0);
+            o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, o[mb], 0, 0, 0);
+        }
+    }
+}
+
+// Decode launch 1 (bf16): workgroup x of a (sequence, KV head) unit scans tiles
+// [x * nt / nslice, (x + 1) * nt / nslice) of the unit's tile list: MFMA scores (written
+// out for the selection on coarse tiles), online softmax and PV, then its partial state.
+template <int HG>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void decode_scan_mfma_kernel(DecodeArgs A) {
-    __shared__ MSmem<HG> s;
+    __shared__ MScanSmem<HG> s;
     const int kvh = blockIdx.y, b = blockIdx.z;  // b: query row
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     int seq, p;
     row_info(A, b, seq, p);
     const int nb = nbuilt(p, A.W);
-    const int ng = nb * A.G;
     const int64_t unit = (int64_t)seq * A.Hkv + kvh;
+    const int64_t gbase = unit * A.max_chunks * A.G;
+    ScanSrc S;
+    S.gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
+    S.gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
+    S.gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
+    S.ng = nb * A.G;
+    S.kb = reinterpret_cast<const bf16_t*>(A.k) + seq * A.sb + kvh * A.sh;
+    S.vb = reinterpret_cast<const bf16_t*>(A.v) + seq * A.sb + kvh * A.sh;
+    S.st = A.st;
+    S.ns = min(A.n_sink, nb * kChunk);
+    S.w0 = nb * kChunk;
+    S.nex = S.ns + (p + 1 - S.w0);
+    const int ntc = (S.ng + kSTile - 1) / kSTile;
+    const int nt = ntc + (S.nex + kSTile - 1) / kSTile;
+    const int t0 = (int)((int64_t)nt * blockIdx.x / A.nslice);
+    const int t1 = (int)((int64_t)nt * (blockIdx.x + 1) / A.nslice);
     const int hq0 = kvh * HG;
     float* part0 = A.part + ((int64_t)(b * A.Hq + hq0) * A.nslot + blockIdx.x) * kPartStride;
     const int64_t head_stride = (int64_t)A.nslot * kPartStride;
+    float* sdst = A.score + ((int64_t)b * A.Hq + hq0) * A.score_stride;
     const bf16_t* q0 = reinterpret_cast<const bf16_t*>(A.q) + ((int64_t)b * A.Hq + hq0) * kD;
 
-    float o[4][4];
-    mfma_init<HG>(s, o);
+    if (tid < HG) { s.mrun[tid] = -INFINITY; s.lrun[tid] = 0.0f; }
+    if (tid < 16) s.alpha[tid] = 0.0f;
+    // weight rows of the heads past HG stay zero
+    for (int x = tid; x < 16 * kSWStride; x += kThreads) {
+        (&s.wh[0][0])[x] = 0;
+        (&s.wl[0][0])[x] = 0;
+    }
+    f32x4_t o[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
     bf16x8_t qa[4];
     mfma_load_q<HG>(q0, qa);
-    __syncthreads();
+    ScanRegs R;
+    if (t0 < t1) scan_fetch(R, S, t0, ntc);
 
-    if ((int)blockIdx.x >= A.nslice) {
-        // ---------------- window tile (block 0 also takes the sinks)
-        const int wb = blockIdx.x - A.nslice;
-        const int r0 = nb * kChunk + wb * kWinRows;
-        const int nwr = max(0, min(r0 + kWinRows, p + 1) - r0);
-        const int ns = wb == 0 ? min(A.n_sink, nb * kChunk) : 0;
+    for (int t = t0; t < t1; ++t) {
+        const bool coarse = t < ntc;
+        const int r0 = coarse ? t * kSTile : (t - ntc) * kSTile;
+        const int n = min(kSTile, (coarse ? S.ng : S.nex) - r0);
+        scan_stage(s, R);  // the last tile's PV is done (barrier at the end of the loop)
         __syncthreads();
-        if (nwr + ns > 0) {
-            const bf16_t* kb = reinterpret_cast<const bf16_t*>(A.k) + seq * A.sb + kvh * A.sh;
-            const bf16_t* vb = reinterpret_cast<const bf16_t*>(A.v) + seq * A.sb + kvh * A.sh;
-            mfma_exact_rows<HG>(s, qa, kb, vb, A.st, ns, r0, ns + nwr, A.scale, o);
+        scan_scores<HG>(s, qa, n, coarse, sdst + r0, A.score_stride);
+        if (t + 1 < t1) scan_fetch(R, S, t + 1, ntc);  // in flight through this tile
+        __syncthreads();
+        for (int h = w; h < HG; h += 4) {
+            // coarse: the same expression the open kernel uses for the groups it subtracts
+            const float bb = s.bias[l];
+            const float lam = (l < n && bb != -INFINITY) ? A.scale * s.sc[h][l] + bb : -INFINITY;
+            const float mx = wave_max_f32(lam, 64);
+            const float mold = s.mrun[h];
+            const float mn = fmaxf(mold, mx);
+            const float wgt = lam == -INFINITY ? 0.0f : softmax_exp(lam - mn);
+            __bf16 hi, lo;
+            split_bf16(wgt, hi, lo);
+            s.wh[h][l] = __builtin_bit_cast(bf16_t, hi);
+            s.wl[h][l] = __builtin_bit_cast(bf16_t, lo);
+            const float ls = wave_sum_f32(wgt, 64);
+            if (l == 0) {
+                const float a = mold == -INFINITY ? 0.0f : softmax_exp(mold - mn);
+                s.alpha[h] = a;
+                s.lrun[h] = s.lrun[h] * a + ls;
+                s.mrun[h] = mn;
+            }
         }
-        mfma_write_partial<HG>(s, o, part0, head_stride);
-        return;
-    }
-
-    // ---------------- slice of group summaries: MFMA scores (written out for the
-    // selection) and the coarse softmax over every non-empty group of the slice
-    const int g0 = blockIdx.x * A.slice;
-    const int n = min(A.slice, ng - g0);
-    if (n > 0) {
-        const int64_t gbase = unit * A.max_chunks * A.G + g0;
-        mfma_scan_groups<HG>(s, qa, reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD,
-                               reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD,
-                               reinterpret_cast<const float*>(A.index + A.L.gln) + gbase, n, A.scale,
-                               A.score + ((int64_t)b * A.Hq + hq0) * A.score_stride + g0, A.score_stride, o);
-    } else {
+        __syncthreads();
+        const float a = s.alpha[l & 15];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[mb][i] *= a;
+        scan_pv<HG>(s, o);
         __syncthreads();
     }
-    mfma_write_partial<HG>(s, o, part0, head_stride);
+
+    // partial state (o, m, l) of every head
+    const int h = l & 15;
+    if (h < HG) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                part0[(int64_t)h * head_stride + 32 * w + 16 * mb + 4 * (l >> 4) + i] = o[mb][i];
+    }
+    if (tid < HG) {
+        part0[(int64_t)tid * head_stride + kD] = s.mrun[tid];
+        part0[(int64_t)tid * head_stride + kD + 1] = s.lrun[tid];
+    }
 }
 
 // ---------------------------------------------------------------------------- open (bf16)

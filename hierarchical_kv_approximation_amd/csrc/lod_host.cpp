@@ -54,15 +54,17 @@ DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len) 
     const int64_t ng = (int64_t)nb * p->groups_per_chunk;
     const int64_t units = (int64_t)batch * p->n_kv_heads;
     if (p->kv_dtype == LOD_BF16) {
-        // MFMA path: window workgroups take 128-row tiles (sinks in the first); a slice
-        // workgroup streams tiles of 128 groups.  Aim for about 768 workgroups (three per
-        // CU) over the whole batch.
-        P.nwin = (int)ceil_div(p->window, 128);
-        int64_t want = ceil_div(768, units) - P.nwin;
-        if (want < 1) want = 1;
-        int64_t slice = ceil_div(ng > 0 ? ng : 1, want);
-        slice = ceil_div(slice, 2 * kTile) * 2 * kTile;
-        P.slice = (int)slice;
+        // MFMA path: the scan workgroups of a unit share its list of 64-row tiles (group
+        // summaries, then sinks and window).  About 1024 workgroups (four per CU) over the
+        // batch, no more than the unit has tiles, at most kScanMaxSlots per unit.
+        const int64_t ntiles = ceil_div(ng, kScanTile) + ceil_div((int64_t)p->n_sink + p->window, kScanTile);
+        int64_t per = ceil_div(1024, units);
+        if (per > ntiles) per = ntiles;
+        if (per > kScanMaxSlots) per = kScanMaxSlots;
+        if (per < 1) per = 1;
+        P.slice = kScanTile;
+        P.nslice = (int)per;
+        P.nwin = 0;
     } else {
         // VALU path: about 512 slice workgroups of up to 256 groups, then a sinks
         // workgroup and 64-row window tiles
@@ -74,7 +76,7 @@ DecodePlan plan_decode(const lod_params* p, int32_t batch, int32_t max_seq_len) 
         P.slice = (int)slice;
         P.nwin = 1 + (int)ceil_div(p->window, kTile);
     }
-    P.nslice = ng > 0 ? (int)ceil_div(ng, P.slice) : 0;
+    if (p->kv_dtype != LOD_BF16) P.nslice = ng > 0 ? (int)ceil_div(ng, P.slice) : 0;
     P.nslot = P.nslice + P.nwin;
     const size_t heads = (size_t)batch * p->n_q_heads;
     P.off_part = 0;

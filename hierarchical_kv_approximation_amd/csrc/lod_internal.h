@@ -20,6 +20,8 @@ constexpr int kMaxTG = 16;     // opened groups per query
 constexpr int kThreads = 256;  // threads per workgroup of every kernel
 constexpr int kTile = 64;      // rows per LDS tile in the decode kernels
 constexpr int kPartStride = kD + 4;  // floats per partial softmax state: o[d], m, l, pad
+constexpr int kScanTile = 64;        // rows per tile of the bf16 decode scan
+constexpr int kScanMaxSlots = 40;    // bf16 decode scan workgroups per (sequence, KV head), at most
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -43,9 +45,9 @@ lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_c
 
 // Decode launch plan, a pure function of (params, batch, max_seq_len).
 struct DecodePlan {
-    int slice;      // groups per slice workgroup (multiple of kTile)
-    int nslice;     // slice workgroups per (sequence, KV head)
-    int nwin;       // window workgroups per (sequence, KV head): sinks + window tiles
+    int slice;      // fp32: groups per slice workgroup (multiple of kTile); bf16: kScanTile
+    int nslice;     // fp32: slice workgroups per (sequence, KV head); bf16: scan workgroups
+    int nwin;       // fp32: window workgroups per (sequence, KV head); bf16: 0
     int nslot;      // partial softmax states per (sequence, query head)
     int score_stride;  // bf16: stored MFMA scores per (sequence, query head)
     size_t off_part, off_cand, off_score, bytes;
