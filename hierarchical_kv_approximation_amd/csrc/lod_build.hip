@@ -486,6 +486,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     T* gv = reinterpret_cast<T*>(A.index + A.L.gv) + gbase * kD;
     float* gln = reinterpret_cast<float*>(A.index + A.L.gln) + gbase;
     float* gkn = reinterpret_cast<float*>(A.index + A.L.gkn) + gbase;
+    int32_t* gpage = reinterpret_cast<int32_t*>(A.index + A.L.gpage) + gbase;
     T* pk = reinterpret_cast<T*>(A.index + A.L.pk) + pbase * kD;
     T* pv = reinterpret_cast<T*>(A.index + A.L.pv) + pbase * kD;
     float* pln = reinterpret_cast<float*>(A.index + A.L.pln) + pbase;
@@ -506,7 +507,10 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
         const int j = e / kD, t = e % kD;
         store_elt(&gk[e], s.cnt[j] > 0 ? s.mu[j][t] : 0.0f);
     }
-    if (tid < G) gln[tid] = s.cnt[tid] > 0 ? logf((float)s.cnt[tid]) : -INFINITY;
+    if (tid < G) {
+        gln[tid] = s.cnt[tid] > 0 ? logf((float)s.cnt[tid]) : -INFINITY;
+        gpage[tid] = s.gpg[tid] | ((s.gpg[tid + 1] - s.gpg[tid]) << 16);
+    }
     // Norm bound of every stored mean key (the storage-rounded value), rounded up
     // generously; it only widens the error bound that MFMA ranking scores are checked
     // against.

@@ -418,6 +418,7 @@ constexpr int kPartLds = kScanMaxSlots;  // scan partial states per head copied 
 constexpr int kPartLdsFloats = (kPartLds * (kPartStride / 4) + 63) / 64 * 64 * 4;
 constexpr int kMetaMax = 320;   // int16 entries of one chunk's meta row (>= meta_stride)
 constexpr int kMetaRows = 2 * kMaxTG;  // meta rows in LDS: candidates prefetched when this few
+constexpr int kSpecPages = 16 * kMetaRows;  // candidate pages scored ahead (at most 16 per group)
 constexpr int kGPW = kMaxTG / 4;             // opened groups per wave (at most)
 constexpr int kItemsPerWave = kGPW * kChunk; // exact rows of a wave's groups (two-tier bound)
 
@@ -439,9 +440,13 @@ struct OpenSmem {
     // selection from MFMA scores (bf16 path)
     alignas(16) float wl[4][4];  // per wave: its largest lower bounds (at most 4)
     int ncand;
-    int32_t cg[kOpenCand];     // candidates: group id, canonical score, MFMA score, ln n
-    float cs[kOpenCand];
+    int32_t cg[kOpenCand];     // candidates: group id, canonical score, MFMA score, ln n,
+    float cs[kOpenCand];       // page range (first slot | count << 16), first entry in pr
     float cS[kOpenCand], cL[kOpenCand];
+    int32_t cP[kOpenCand], cpo[kOpenCand + 1];
+    float pr[kSpecPages];      // canonical scores and ln n of the candidates' pages (when
+    float pl[kSpecPages];      // scored ahead of the group ranking: pscore_ready)
+    int pscore_ready;
     int mrow[kMaxTG];          // meta row (in s.meta) of opened group i
     int meta_ready;            // meta rows were prefetched (bf16 path)
     uint64_t red[4];
@@ -562,7 +567,10 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
             npg = mrowp(i)[j + 1] - ps0;
         }
         float r = 0.0f;
-        if (A.TP > 0 && e < npg) {
+        if (s.pscore_ready) {
+            // scored ahead: candidate mrow[i], page e (item 16 * mrow[i] + e)
+            if (e < npg) r = s.pr[16 * s.mrow[i] + e];
+        } else if (A.TP > 0 && e < npg) {
             const T* row = pk_u + ((int64_t)c * PS + ps0 + e) * kD;
             constexpr int P16 = Elt<T>::kPer16;
             uint4 u[kD / P16];
@@ -576,7 +584,8 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
                 for (int t = 0; t < P16; ++t) r = __builtin_fmaf(s.qs[x * P16 + t], f[t], r);
             }
         }
-        const float lnp = e < npg ? pln_u[(int64_t)c * PS + ps0 + e] : -INFINITY;
+        const float lnp = e < npg ? (s.pscore_ready ? s.pl[16 * s.mrow[i] + e] : pln_u[(int64_t)c * PS + ps0 + e])
+                                  : -INFINITY;
         int rank = (A.TP == 0 && e < npg) ? 0 : -1;
         if (A.TP > 0) {
             uint64_t key = e < npg ? rank_key(r, (uint32_t)e) : 0;
@@ -751,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
         if (lane == 0) s.nsel = round;
     }
     if (tid < kMaxTG) s.mrow[tid] = tid;
-    if (tid == 0) s.meta_ready = 0;
+    if (tid == 0) { s.meta_ready = 0; s.pscore_ready = 0; }
     __syncthreads();
     const int nsel = s.nsel;
     const uint64_t kth = nsel == A.TG ? s.sel[A.TG - 1] : 0;
@@ -1039,7 +1048,7 @@ struct MScanSmem {
     alignas(16) bf16_t wh[16][kSWStride];  // softmax weights [head][row], bf16 hi (heads >= HG: 0)
     alignas(16) bf16_t wl[16][kSWStride];  // and lo parts
     float bias[kSTile];                  // ln n of a coarse tile's groups, 0 for exact rows
-    float sc[HG][kSTile];                // MFMA scores of the tile
+    alignas(16) float sc[HG][kSTile];    // MFMA scores of the tile
     float mrun[HG], lrun[HG], alpha[16];
 };
 
@@ -1108,11 +1117,10 @@ __device__ __forceinline__ void scan_stage(MScanSmem<HG>& s, const ScanRegs& R) 
     if (tid < kSTile) s.bias[tid] = R.bias;
 }
 
-// MFMA scores of the staged tile: wave w takes rows 16w .. 16w+15 (query heads are the A
-// rows, rows >= HG zero).  Coarse tiles also write them to sdst (row h at h * sstride).
+// MFMA scores of the staged tile into s.sc: wave w takes rows 16w .. 16w+15 (query heads
+// are the A rows, rows >= HG zero).
 template <int HG>
-__device__ __forceinline__ void scan_scores(MScanSmem<HG>& s, const bf16x8_t* qa, int n, bool coarse,
-                                            float* sdst, int64_t sstride) {
+__device__ __forceinline__ void scan_scores(MScanSmem<HG>& s, const bf16x8_t* qa) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int row = 16 * w + (l & 15);
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1125,10 +1133,7 @@ __device__ __forceinline__ void scan_scores(MScanSmem<HG>& s, const bf16x8_t* qa
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int h = 4 * (l >> 4) + r;
-        if (h < HG) {
-            s.sc[h][row] = acc[r];
-            if (coarse && row < n) sdst[(int64_t)h * sstride + row] = acc[r];
-        }
+        if (h < HG) s.sc[h][row] = acc[r];
     }
 }
 
@@ -1206,9 +1211,16 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
         const int n = min(kSTile, (coarse ? S.ng : S.nex) - r0);
         scan_stage(s, R);  // the last tile's PV is done (barrier at the end of the loop)
         __syncthreads();
-        scan_scores<HG>(s, qa, n, coarse, sdst + r0, A.score_stride);
+        scan_scores<HG>(s, qa);
         if (t + 1 < t1) scan_fetch(R, S, t + 1, ntc);  // in flight through this tile
         __syncthreads();
+        // coarse tiles: the scores go out for the selection, a 256-byte row per head
+        // (rows past the tile's groups are never read; the rows stay inside score_stride)
+        if (coarse && tid < 16 * HG) {
+            const int h = tid >> 4, j = tid & 15;
+            *reinterpret_cast<float4*>(sdst + (int64_t)h * A.score_stride + r0 + 4 * j) =
+                *reinterpret_cast<const float4*>(&s.sc[h][4 * j]);
+        }
         for (int h = w; h < HG; h += 4) {
             // coarse: the same expression the open kernel uses for the groups it subtracts
             const float bb = s.bias[l];
@@ -1283,9 +1295,12 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     const float* S = A.score + head * A.score_stride;
     const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + unit * A.max_chunks * A.G;
     const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
+    const int32_t* gpage = reinterpret_cast<const int32_t*>(A.index + A.L.gpage) + unit * A.max_chunks * A.G;
     const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + unit * A.max_chunks * A.G * kD;
     const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
     const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + unit * A.max_chunks * A.L.meta_stride;
+    const bf16_t* pk_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pk) + unit * A.max_chunks * A.L.page_slots * kD;
+    const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + unit * A.max_chunks * A.L.page_slots;
 
     // loads of the first round trip, issued together: q, the scores, the bounds' inputs
     float q8[8];
@@ -1293,12 +1308,13 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     const float qv = tid < kD ? bf16_bits_to_f32(qp[tid]) : 0.0f;
     constexpr int SPT = 16;  // groups per thread per round
     float sv[SPT], kn[SPT], ln[SPT];
+    int32_t gp[SPT];
     auto load_scores = [&](int g0) {
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int g = g0 + tid + kThreads * u;
             ln[u] = -INFINITY;
-            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; ln[u] = gln[g]; }
+            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; ln[u] = gln[g]; gp[u] = gpage[g]; }
         }
     };
     if (ng > 0) load_scores(0);
@@ -1352,7 +1368,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         if (lane == 0)
             for (int x = taken < R ? taken : R; x < 4; ++x) s.wl[wave][x] = -INFINITY;
     }
-    if (tid == 0) { s.ncand = 0; s.meta_ready = 0; }
+    if (tid == 0) { s.ncand = 0; s.meta_ready = 0; s.pscore_ready = 0; }
     __syncthreads();
     // 1c. every thread: T = the TG-th largest of the 16 list entries (sorting network;
     //     -inf when fewer than TG are finite)
@@ -1385,35 +1401,33 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
             if (e == TG - 1) T = v[e];
     }
     // 1d. candidates: S + E >= T (a single block of groups is still in registers); one
-    //     LDS atomic per wave, positions from a wave prefix sum of the per-thread counts
+    //     LDS atomic per wave, positions from the ballots of the wave (by u, then lane)
     for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
         if (ng > SPT * kThreads) load_scores(g0);
-        uint32_t cm = 0;
+        uint64_t mk[SPT];
+        int wtot = 0;
 #pragma unroll
-        for (int u = 0; u < SPT; ++u)
-            if (ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T) cm |= 1u << u;
-        const int cnt = __popc(cm);
-        int incl = cnt;
-#pragma unroll
-        for (int sh = 1; sh < 64; sh <<= 1) {
-            const int o = __shfl_up(incl, sh, 64);
-            if (lane >= sh) incl += o;
+        for (int u = 0; u < SPT; ++u) {
+            mk[u] = __ballot(ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T);
+            wtot += __popcll(mk[u]);
         }
+        if (wtot == 0) continue;  // uniform over the wave
         int base = 0;
-        if (lane == 63 && incl > 0) base = atomicAdd(&s.ncand, incl);
-        base = __shfl(base, 63, 64) + incl - cnt;
-        if (cm) {
+        if (lane == 0) base = atomicAdd(&s.ncand, wtot);
+        base = __shfl(base, 0, 64);
+        const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-            for (int u = 0; u < SPT; ++u) {
-                if (cm & (1u << u)) {
-                    if (base < kOpenCand) {
-                        s.cg[base] = g0 + tid + kThreads * u;
-                        s.cS[base] = sv[u];
-                        s.cL[base] = ln[u];
-                    }
-                    ++base;
+        for (int u = 0; u < SPT; ++u) {
+            if ((mk[u] >> lane) & 1ull) {
+                const int at = base + __popcll(mk[u] & below);
+                if (at < kOpenCand) {
+                    s.cg[at] = g0 + tid + kThreads * u;
+                    s.cS[at] = sv[u];
+                    s.cL[at] = ln[u];
+                    s.cP[at] = gp[u];
                 }
             }
+            base += __popcll(mk[u]);
         }
     }
     __syncthreads();
@@ -1435,6 +1449,33 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
                 const int x = pc / ms16, e = pc % ms16;
                 __builtin_amdgcn_global_load_lds(meta_u + (int64_t)(s.cg[x] / A.G) * A.L.meta_stride + 8 * e,
                                                  mflat + 512 * i, 16, 0, 0);
+            }
+            // canonical scores of every candidate's pages, ahead of the group ranking (the
+            // page step then only ranks them): item f = (candidate f / 16, page f % 16) on
+            // the threads of waves 1-3; the group chains below run on wave 0
+            if (tid >= 64) {
+                for (int f = tid - 64; f < ncand * 16; f += kThreads - 64) {
+                    const int x = f >> 4, e = f & 15;
+                    const int cp = s.cP[x], npg = cp >> 16;
+                    if (e < npg) {
+                        const int64_t slot = (int64_t)(s.cg[x] / A.G) * A.L.page_slots + (cp & 0xffff) + e;
+                        const bf16_t* row = pk_u + slot * kD;
+                        uint4 u[16];
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) u[c] = *reinterpret_cast<const uint4*>(row + 8 * c);
+                        const float lnp = pln_u[slot];
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < 16; ++c) {
+                            float fv[8];
+                            Elt<bf16_t>::unpack(u[c], fv);
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) acc = __builtin_fmaf(s.qs[8 * c + t], fv[t], acc);
+                        }
+                        s.pr[f] = acc;
+                        s.pl[f] = lnp;
+                    }
+                }
             }
         }
         for (int x = tid; x < ncand; x += kThreads) {
@@ -1466,6 +1507,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         if (tid == 0) {
             s.nsel = ncand < TG ? ncand : TG;
             s.meta_ready = prefetch;
+            s.pscore_ready = prefetch;
         }
     } else {
         // exhaustive: canonical score of every non-empty group, workgroup-wide top-TG

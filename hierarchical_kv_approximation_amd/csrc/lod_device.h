@@ -99,6 +99,17 @@ __device__ __forceinline__ float wave_sum_f32(float v, int width) {
     return v;
 }
 
+// Workgroup barrier over LDS traffic only: each wave waits for its own LDS operations
+// (lgkmcnt 0), not for its vector memory operations, so loads of a later tile (also
+// global -> LDS loads, whose completion the caller awaits with an explicit vmcnt wait
+// before the barrier) stay in flight.  __syncthreads would wait for all of them.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 // exp(x) for x <= 0 (softmax weights); exp(-inf) = 0.
 __device__ __forceinline__ float softmax_exp(float x) { return __expf(x); }
 

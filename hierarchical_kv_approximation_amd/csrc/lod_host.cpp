@@ -37,6 +37,7 @@ lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_c
     L.gv = o;     o = align256(o + U * NC * G * d * E);
     L.gln = o;    o = align256(o + U * NC * G * 4);
     L.gkn = o;    o = align256(o + U * NC * G * 4);
+    L.gpage = o;  o = align256(o + U * NC * G * 4);
     L.pk = o;     o = align256(o + U * NC * PS * d * E);
     L.pv = o;     o = align256(o + U * NC * PS * d * E);
     L.pln = o;    o = align256(o + U * NC * PS * 4);

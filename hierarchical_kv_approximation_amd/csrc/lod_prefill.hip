@@ -425,11 +425,13 @@ __device__ __forceinline__ void stage_rows_swizzled(bf16_t (*kt)[kD], const bf16
 // Group selection opens the TG groups with the largest q . kbar (ties to the lower id)
 // under the canonical chain.  The MFMA score S of a group is within
 // E = kErrC |q| |kbar| of that chain, so with T the TG-th largest lower bound S - E over
-// the groups, the groups with S + E >= T contain the exact top TG.  Each split finds the
-// TG largest lower bounds and the groups with S + E at or above its own TG-th largest
-// (a local threshold that is never above the global one).  The select step takes the
-// global threshold from the splits' top lists and keeps the listed groups at or above it.
-template <int HG>
+// the groups, the groups with S + E >= T contain the exact top TG; so does any T below
+// that one.  Each split keeps, per column, the R largest lower bounds seen by each of the
+// column's four lanes (4R >= TG values of distinct groups), lists the TG largest of
+// those, and collects the groups with S + E at or above the TG-th (a lower bound of the
+// split's TG-th largest, never above the global one).  The select step takes the global
+// threshold from the splits' top lists and keeps the listed groups at or above it.
+template <int HG, int R>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_cand_kernel(SelArgs A) {
     __shared__ CandSmem s;
@@ -523,7 +525,7 @@ void prefill_cand_kernel(SelArgs A) {
         } else {
             __builtin_amdgcn_s_waitcnt(0);
         }
-        __syncthreads();
+        lds_barrier();
     };
     // sweep over the split's tiles; body(t, buf, nk, S) sees the MFMA scores
     auto sweep = [&](auto&& body) {
@@ -535,16 +537,17 @@ void prefill_cand_kernel(SelArgs A) {
             f32x4_t S[4][2];
             tile_scores(S, buf);
             body(t, buf, min(kFlashKeys, ng - t * kFlashKeys), S);
-            __syncthreads();
+            lds_barrier();  // the buffer is free for tile t + 2
         }
     };
 
-    // pass A: per column, the TG largest lower bounds S - E (lane-local top-16 lists)
-    float lst[2][kMaxTG];
+    // pass A: per column, the largest lower bounds S - E (lane-local top-R lists, kept
+    // sorted by a branch-free insertion of every element)
+    float lst[2][R];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int e = 0; e < kMaxTG; ++e) lst[cb][e] = -INFINITY;
+        for (int e = 0; e < R; ++e) lst[cb][e] = -INFINITY;
     sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -552,16 +555,15 @@ void prefill_cand_kernel(SelArgs A) {
             for (int r = 0; r < 4; ++r) {
                 const int key = 16 * kb + 4 * (l >> 4) + r;
                 const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
+                const float gn = s.gkn_t[buf][key];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    float x = S[kb][cb][r] - kErrC * qn[cb] * s.gkn_t[buf][key];
-                    if (valid && x > lst[cb][kMaxTG - 1]) {
+                    float x = valid ? S[kb][cb][r] - kErrC * qn[cb] * gn : -INFINITY;
 #pragma unroll
-                        for (int e = 0; e < kMaxTG; ++e) {
-                            const float hi = fmaxf(lst[cb][e], x), lo = fminf(lst[cb][e], x);
-                            lst[cb][e] = hi;
-                            x = lo;
-                        }
+                    for (int e = 0; e < R; ++e) {
+                        const float hi = fmaxf(lst[cb][e], x), lo = fminf(lst[cb][e], x);
+                        lst[cb][e] = hi;
+                        x = lo;
                     }
                 }
             }
@@ -590,8 +592,8 @@ void prefill_cand_kernel(SelArgs A) {
             if (taken >= TG) T = m;
             if (mine) {
 #pragma unroll
-                for (int e = 0; e < kMaxTG - 1; ++e) lst[cb][e] = lst[cb][e + 1];
-                lst[cb][kMaxTG - 1] = -INFINITY;
+                for (int e = 0; e < R - 1; ++e) lst[cb][e] = lst[cb][e + 1];
+                lst[cb][R - 1] = -INFINITY;
             }
         }
         if (top)
@@ -605,23 +607,40 @@ void prefill_cand_kernel(SelArgs A) {
     const int64_t lat[2] = {list_at(16 * (2 * w) + (l & 15)), list_at(16 * (2 * w + 1) + (l & 15))};
     sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
         const int g0 = t * kFlashKeys;
+        // this lane's candidates of the tile as bit masks (bit 4 kb + r), upper bounds kept
+        uint32_t m[2] = {0u, 0u};
+        float ubv[2][16];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = 16 * kb + 4 * (l >> 4) + r;
                 const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
+                const float gn = s.gkn_t[buf][key];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    const float ub = S[kb][cb][r] + kErrC * qn[cb] * s.gkn_t[buf][key];
-                    if (valid && ub >= T2[cb]) {
-                        const int n = 16 * (2 * w + cb) + (l & 15);
-                        const int at = atomicAdd(&s.cnt[n], 1);
-                        if (at < kSplitCap && lat[cb] >= 0)
-                            A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ub));
-                    }
+                    const float ub = S[kb][cb][r] + kErrC * qn[cb] * gn;
+                    ubv[cb][4 * kb + r] = ub;
+                    m[cb] |= (valid && ub >= T2[cb]) ? (1u << (4 * kb + r)) : 0u;
                 }
             }
+        // one LDS atomic per lane and column, then the entries
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            if (m[cb] == 0u) continue;
+            const int n = 16 * (2 * w + cb) + (l & 15);
+            int at = atomicAdd(&s.cnt[n], __popc(m[cb]));
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                if ((m[cb] >> b) & 1u) {
+                    if (at < kSplitCap && lat[cb] >= 0) {
+                        const int key = 16 * (b >> 2) + 4 * (l >> 4) + (b & 3);
+                        A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ubv[cb][b]));
+                    }
+                    ++at;
+                }
+            }
+        }
     });
     if (tid < kFlashRowHeads) {
         const int64_t at = list_at(tid);
@@ -1171,8 +1190,13 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     constexpr int QT = kFlashRowHeads / HG;
     const int ntiles = (S.nq + QT - 1) / QT;
     trace_point(0, st);
-    hipLaunchKernelGGL((prefill_cand_kernel<HG>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads), 0,
-                       st, S);
+    // lane lists of 4 (8 for more than 8 opened groups): 16 (32) values per column
+    if (S.TG <= 8)
+        hipLaunchKernelGGL((prefill_cand_kernel<HG, 4>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads),
+                           0, st, S);
+    else
+        hipLaunchKernelGGL((prefill_cand_kernel<HG, 8>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads),
+                           0, st, S);
     trace_point(1, st);
     hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
     trace_point(2, st);

@@ -42,7 +42,7 @@ class Index(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("gk", "gv", "gln", "gkn", "pk", "pv", "pln", "meta", "assign", "total")] + \
+                ("gk", "gv", "gln", "gkn", "gpage", "pk", "pv", "pln", "meta", "assign", "total")] + \
         [("page_slots", ctypes.c_int32), ("meta_stride", ctypes.c_int32)]
 
 
@@ -184,6 +184,7 @@ class LodIndex:
             "gv": view(L.gv, U * NC * G * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, G, d)),
             "gln": view(L.gln, U * NC * G, torch.float32, (self.batch, cfg.n_kv_heads, NC, G)),
             "gkn": view(L.gkn, U * NC * G, torch.float32, (self.batch, cfg.n_kv_heads, NC, G)),
+            "gpage": view(L.gpage, U * NC * G, torch.int32, (self.batch, cfg.n_kv_heads, NC, G)),
             "pk": view(L.pk, U * NC * PS * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, PS, d)),
             "pv": view(L.pv, U * NC * PS * d, cfg.dtype, (self.batch, cfg.n_kv_heads, NC, PS, d)),
             "pln": view(L.pln, U * NC * PS, torch.float32, (self.batch, cfg.n_kv_heads, NC, PS)),

@@ -101,6 +101,7 @@ typedef struct {
  *   gk, gv   [U][NC*G][d]  E     group mean key / value (storage-rounded)
  *   gln      [U][NC*G]     f32   ln(key count), -inf for an empty group
  *   gkn      [U][NC*G]     f32   upper bound of the Euclidean norm of the stored mean key
+ *   gpage    [U][NC*G]     i32   first page slot of the group | its page count << 16
  *   pk, pv   [U][NC*PS][d] E     page mean key / value
  *   pln      [U][NC*PS]    f32   ln(key count), -inf for an unused page slot
  *   meta     [U][NC][meta_stride] int16: gpg[G+1] first page slot of each group,
@@ -109,7 +110,7 @@ typedef struct {
  *   assign   [U][NC][C]    int8  group of every chunk-local position, -1 for sinks
  */
 typedef struct {
-    size_t gk, gv, gln, gkn, pk, pv, pln, meta, assign, total;
+    size_t gk, gv, gln, gkn, gpage, pk, pv, pln, meta, assign, total;
     int32_t page_slots;
     int32_t meta_stride; /* int16 entries per chunk in `meta` */
 } lod_index_layout_t;

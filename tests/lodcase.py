@@ -87,6 +87,9 @@ def compare_index(index: lod.LodIndex, oidx: dict, b, h, n_chunks):
         "k-means assignments differ"
     gpg, counts, mem = gpu_pages(index, b, h, n_chunks)
     G = index.cfg.groups
+    gpage = a["gpage"][b, h, :n_chunks].cpu().numpy().astype(np.int64)
+    assert np.array_equal(gpage & 0xffff, gpg[:, :G]) and np.array_equal(gpage >> 16, np.diff(gpg, axis=1)), \
+        "group page ranges differ from the meta rows" 
     gcount = np.array([[counts[c, gpg[c, j]:gpg[c, j + 1]].sum() for j in range(G)]
                        for c in range(n_chunks)], dtype=np.int64).reshape(n_chunks, G)
     assert np.array_equal(gcount, oidx["gcount"])

@@ -35,7 +35,7 @@ def test_index_layout_is_aligned_and_disjoint():
     assert lod.lib().lod_index_layout(_p(cfg), 4, 128, ctypes.byref(L)) == 0
     U, NC, G, PS, d = 4 * 8, 128, 8, 16 + 8, 128
     sizes = {"gk": U * NC * G * d * 2, "gv": U * NC * G * d * 2, "gln": U * NC * G * 4,
-             "gkn": U * NC * G * 4,
+             "gkn": U * NC * G * 4, "gpage": U * NC * G * 4,
              "pk": U * NC * PS * d * 2, "pv": U * NC * PS * d * 2, "pln": U * NC * PS * 4,
              "meta": U * NC * L.meta_stride * 2, "assign": U * NC * 256}
     spans = sorted((getattr(L, k), getattr(L, k) + v) for k, v in sizes.items())
