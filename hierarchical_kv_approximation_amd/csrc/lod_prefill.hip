@@ -363,6 +363,7 @@ struct SelArgs {
     int32_t* sel_pages;   // nullable API output [B][nq][Hq][TG][max(TP,1)]
     int32_t* selg;        // [B][nq][Hq][TG] opened groups in ascending id order (-1 pad)
     PairRec* rec;         // [B][nq][Hq][TG] in ascending group order (as selg)
+    float* part_pg;       // [B][nq][Hq][TG] page partial states: m = -inf written for empty slots
 };
 
 constexpr int kCandCap = 2 * kMaxTG;   // candidates kept per column; beyond: exhaustive path
@@ -904,6 +905,7 @@ void prefill_select_kernel(SelArgs A) {
             for (int e = 0; e < s.nsel[n]; ++e) pos += s.sel[n][e] < R.gid;
         }
         A.rec[rh * TG + pos] = R;
+        if (R.gid < 0) A.part_pg[(rh * TG + pos) * kPartStride + kD] = -INFINITY;  // no pages kernel pair
         if (A.sel_pages)
             for (int k = 0; k < TPW; ++k)
                 A.sel_pages[(rh * TG + t) * TPW + k] =
@@ -957,31 +959,50 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
     };
     for (int g = tid; g < ng; g += kThreads) cnt[g] = 0;
     __syncthreads();
-    for (int x = tid; x < npairs; x += kThreads) {
-        const int g = pair_gid(x);
-        if (g >= 0) atomicAdd(&cnt[g], 1);
+    // group ids of 8 pairs per thread loaded together, then counted
+    constexpr int U = 8;
+    for (int x0 = tid; x0 < npairs; x0 += U * kThreads) {
+        int g[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) g[u] = x0 + u * kThreads < npairs ? pair_gid(x0 + u * kThreads) : -1;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (g[u] >= 0) atomicAdd(&cnt[g[u]], 1);
     }
     __syncthreads();
-    // exclusive scan of the counts: contiguous ranges per thread, then one thread scans
-    __shared__ int part[kThreads];
+    // exclusive scan of the counts: contiguous ranges per thread, then the 256 range sums
+    // by wave prefix sums and the waves' totals
     const int per = (ng + kThreads - 1) / kThreads;
     const int g0 = tid * per, g1 = min(ng, g0 + per);
     int sum = 0;
     for (int g = g0; g < g1; ++g) sum += cnt[g];
-    part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int x = 0; x < kThreads; ++x) { const int v = part[x]; part[x] = acc; acc += v; }
-        A.poff[unit * 2] = acc;
+    __shared__ int wsum[kThreads / 64];
+    const int lane = tid & 63, wv = tid >> 6;
+    int incl = sum;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+        const int o = __shfl_up(incl, sh, 64);
+        if (lane >= sh) incl += o;
     }
+    if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    int acc = part[tid];
+    int before = 0, total = 0;
+#pragma unroll
+    for (int x = 0; x < kThreads / 64; ++x) {
+        before += x < wv ? wsum[x] : 0;
+        total += wsum[x];
+    }
+    if (tid == 0) A.poff[unit * 2] = total;
+    int acc = before + incl - sum;
     for (int g = g0; g < g1; ++g) { const int v = cnt[g]; cnt[g] = acc; acc += v; }
     __syncthreads();
-    for (int x = tid; x < npairs; x += kThreads) {
-        const int g = pair_gid(x);
-        if (g >= 0) list[atomicAdd(&cnt[g], 1)] = x;
+    for (int x0 = tid; x0 < npairs; x0 += U * kThreads) {
+        int g[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) g[u] = x0 + u * kThreads < npairs ? pair_gid(x0 + u * kThreads) : -1;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (g[u] >= 0) list[atomicAdd(&cnt[g[u]], 1)] = x0 + u * kThreads;
     }
 }
 
@@ -1124,8 +1145,8 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, 
         const float* pp = nullptr;
         if (k < 8) {
             if (k < A.nsplit) pp = A.part_fl + k * A.split_stride + rh * kPartStride;
-        } else if (k - 8 < A.TG && A.selg[rh * A.TG + (k - 8)] >= 0) {
-            pp = A.part_pg + (rh * A.TG + (k - 8)) * kPartStride;
+        } else if (k - 8 < A.TG) {
+            pp = A.part_pg + (rh * A.TG + (k - 8)) * kPartStride;  // empty slots hold m = -inf
         }
         if (pp) { mm[k] = pp[kD]; ll[k] = pp[kD + 1]; oo[k] = pp[d]; }
     }
@@ -1310,6 +1331,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             S.sel_pages = sel_pages ? sel_pages + row0 * Hq * TG * TPW : nullptr;
             S.selg = reinterpret_cast<int32_t*>(w + P.off_selg);
             S.rec = reinterpret_cast<PairRec*>(w + P.off_rec);
+            S.part_pg = reinterpret_cast<float*>(w + P.off_ppg);
             S.nsplit = P.nsplit;
             S.ltop = reinterpret_cast<float*>(w + P.off_ltop);
             S.lcnt = reinterpret_cast<int32_t*>(w + P.off_lcnt);
