@@ -24,16 +24,13 @@ __device__ __forceinline__ bf16x8_t zero_bf16x8() {
     return z;
 }
 
-// bf16 bits of an fp32 value, round-to-nearest-even, as the MFMA element type.
-__device__ __forceinline__ __bf16 to_bf16(float x) {
-    return __builtin_bit_cast(__bf16, f32_to_bf16_rne(x));
-}
+// fp32 -> bf16, round to nearest even (one hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
 // Split x into bf16 hi + lo with x - hi - lo below 2^-16 |x| (for PV operands).
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
-    const bf16_t h = f32_to_bf16_rne(x);
-    hi = __builtin_bit_cast(__bf16, h);
-    lo = to_bf16(x - bf16_bits_to_f32(h));
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
 }
 
 constexpr int kFlashRowHeads = 128;  // query rows x heads per prefill workgroup

@@ -175,15 +175,8 @@ __device__ __forceinline__ void flash_tile(FlashSmem<HG>& s, FlashState<HG>& F, 
             const bf16_t* vr = &s.vT[16 * db + (l & 15)][32 * st + 4 * (l >> 4)];
             const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
             const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 16);
-            bf16x8_t a;
-            a[0] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.x & 0xffffu));
-            a[1] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.x >> 16));
-            a[2] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.y & 0xffffu));
-            a[3] = __builtin_bit_cast(__bf16, (bf16_t)(lo4.y >> 16));
-            a[4] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.x & 0xffffu));
-            a[5] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.x >> 16));
-            a[6] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.y & 0xffffu));
-            a[7] = __builtin_bit_cast(__bf16, (bf16_t)(hi4.y >> 16));
+            const u32x4_t raw = {lo4.x, lo4.y, hi4.x, hi4.y};  // keys 8 (l/16) .. +7 of the step
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, raw);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 F.O[cb][db] = mfma16(a, ph[cb], F.O[cb][db]);
