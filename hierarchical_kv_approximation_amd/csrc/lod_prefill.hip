@@ -601,9 +601,8 @@ void prefill_cand_kernel(SelArgs A) {
     const int64_t lat[2] = {list_at(16 * (2 * w) + (l & 15)), list_at(16 * (2 * w + 1) + (l & 15))};
     sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
         const int g0 = t * kFlashKeys;
-        // this lane's candidates of the tile as bit masks (bit 4 kb + r), upper bounds kept
+        // this lane's candidates of the tile as bit masks (bit 4 kb + r)
         uint32_t m[2] = {0u, 0u};
-        float ubv[2][16];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -614,7 +613,6 @@ void prefill_cand_kernel(SelArgs A) {
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
                     const float ub = S[kb][cb][r] + kErrC * qn[cb] * gn;
-                    ubv[cb][4 * kb + r] = ub;
                     m[cb] |= (valid && ub >= T2[cb]) ? (1u << (4 * kb + r)) : 0u;
                 }
             }
@@ -629,7 +627,8 @@ void prefill_cand_kernel(SelArgs A) {
                 if ((m[cb] >> b) & 1u) {
                     if (at < kSplitCap && lat[cb] >= 0) {
                         const int key = 16 * (b >> 2) + 4 * (l >> 4) + (b & 3);
-                        A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ubv[cb][b]));
+                        const float ub = S[b >> 2][cb][b & 3] + kErrC * qn[cb] * s.gkn_t[buf][key];
+                        A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ub));
                     }
                     ++at;
                 }
@@ -645,8 +644,11 @@ void prefill_cand_kernel(SelArgs A) {
 struct SelSmem {
     float T[kFlashRowHeads];
     int cnt[kFlashRowHeads];
-    int32_t cg[kFlashRowHeads][kCandCap];
-    float cs[kFlashRowHeads][kCandCap];
+    int32_t cg[kFlashRowHeads][kCandCap];  // candidates: group id, upper bound of the canonical
+    float cub[kFlashRowHeads][kCandCap];   // score (then the score itself where computed),
+    float clb[kFlashRowHeads][kCandCap];   // lower bound, class (0 surely not opened, 1
+    uint8_t cls[kFlashRowHeads][kCandCap]; // needs the chain, 2 surely opened)
+    float qn[kFlashRowHeads];              // |q| per column, rounded up
     int32_t sel[kFlashRowHeads][kMaxTG];  // rank order
     int nsel[kFlashRowHeads];
     uint64_t red[4];
@@ -719,11 +721,23 @@ void prefill_select_kernel(SelArgs A) {
         }
         s.T[n] = T;
         s.cnt[n] = over ? kCandCap + 1 : 0;  // an overflowed split forces the exhaustive path
+        // |q| rounded up, computed as the sweep computed it
+        const bf16_t* qr = qrow(n);
+        float ss = 0.0f;
+        for (int c = 0; c < 16; ++c) {
+            float f[8];
+            Elt<bf16_t>::unpack(*reinterpret_cast<const uint4*>(qr + 8 * c), f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+        }
+        s.qn[n] = sqrtf(ss) * 1.0001f;
     }
     if (tid == 0) s.any_overflow = 0;
     __syncthreads();
     // candidates: listed groups with upper bound >= the global threshold (two threads per
-    // column, alternate splits)
+    // column, alternate splits), with lower bounds ub - 2E (E = kErrC |q| |kbar| as the
+    // sweep computed it, from the stored norm bound)
+    const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + gbase;
     {
         const int n = tid & (kFlashRowHeads - 1);
         if (n / HG < nrows) {
@@ -736,15 +750,26 @@ void prefill_select_kernel(SelArgs A) {
 #pragma unroll
                 for (int i = 0; i < kSplitCap / 2; ++i)
                     if (2 * i < c) e[i] = src[i];
+                const float e2 = 2.0f * kErrC * s.qn[n];
 #pragma unroll
                 for (int i = 0; i < kSplitCap / 2; ++i) {
                     if (2 * i < c && __uint_as_float(e[i].y) >= T) {
                         const int at = atomicAdd(&s.cnt[n], 1);
-                        if (at < kCandCap) s.cg[n][at] = (int32_t)e[i].x;
+                        if (at < kCandCap) {
+                            const float ub = __uint_as_float(e[i].y);
+                            s.cg[n][at] = (int32_t)e[i].x;
+                            s.cub[n][at] = ub;
+                            s.clb[n][at] = ub - e2 * gkn[e[i].x];
+                        }
                     }
                     if (2 * i + 1 < c && __uint_as_float(e[i].w) >= T) {
                         const int at = atomicAdd(&s.cnt[n], 1);
-                        if (at < kCandCap) s.cg[n][at] = (int32_t)e[i].z;
+                        if (at < kCandCap) {
+                            const float ub = __uint_as_float(e[i].w);
+                            s.cg[n][at] = (int32_t)e[i].z;
+                            s.cub[n][at] = ub;
+                            s.clb[n][at] = ub - e2 * gkn[e[i].z];
+                        }
                     }
                 }
             }
@@ -752,10 +777,53 @@ void prefill_select_kernel(SelArgs A) {
     }
     __syncthreads();
 
-    // canonical chains for the candidates
+    // certification: a candidate is surely opened when fewer than TG others can reach its
+    // lower bound (the TG-th largest upper bound of the others is below it), surely not
+    // when TG others are above its upper bound (the TG-th largest lower bound is above
+    // it); only the rest need the canonical chain (all of them when the rank order is an
+    // output).  Needs the TG and TG+1 largest upper bounds and the TG largest lower bounds.
+    if (tid < kFlashRowHeads) {
+        const int n = tid, c = s.cnt[n];
+        if (c <= kCandCap) {
+            float tu[kMaxTG + 1], tl[kMaxTG];
+#pragma unroll
+            for (int e = 0; e <= kMaxTG; ++e) tu[e] = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) tl[e] = -INFINITY;
+            for (int at = 0; at < c; ++at) {
+                float u = s.cub[n][at], v = s.clb[n][at];
+#pragma unroll
+                for (int e = 0; e <= kMaxTG; ++e) {
+                    const float hi = fmaxf(tu[e], u), lo = fminf(tu[e], u);
+                    tu[e] = hi;
+                    u = lo;
+                }
+#pragma unroll
+                for (int e = 0; e < kMaxTG; ++e) {
+                    const float hi = fmaxf(tl[e], v), lo = fminf(tl[e], v);
+                    tl[e] = hi;
+                    v = lo;
+                }
+            }
+            float uT = -INFINITY, uT1 = -INFINITY, lT = -INFINITY;  // TG-th, TG+1-th largest ub; TG-th lb
+#pragma unroll
+            for (int e = 0; e <= kMaxTG; ++e) {
+                if (e == TG - 1) { uT = tu[e]; lT = e < kMaxTG ? tl[e] : -INFINITY; }
+                if (e == TG) uT1 = tu[e];
+            }
+            for (int at = 0; at < c; ++at) {
+                const float lb = s.clb[n][at], ub = s.cub[n][at];
+                const float others = ub >= uT ? uT1 : uT;  // TG-th largest ub of the others
+                s.cls[n][at] = (!A.sel_groups && lb > others) ? 2 : (lT > ub ? 0 : 1);
+            }
+        }
+    }
+    __syncthreads();
+    // canonical chains for the candidates that need them (the score replaces the bound)
     for (int x = tid; x < kFlashRowHeads * kCandCap; x += kThreads) {
         const int n = x / kCandCap, at = x % kCandCap;
-        if (at < min(s.cnt[n], kCandCap)) s.cs[n][at] = canonical_dot_bf16(qrow(n), gk + (int64_t)s.cg[n][at] * kD);
+        if (at < min(s.cnt[n], kCandCap) && s.cls[n][at] == 1)
+            s.cub[n][at] = canonical_dot_bf16(qrow(n), gk + (int64_t)s.cg[n][at] * kD);
     }
     __syncthreads();
     // exact top-TG per column among its candidates (columns that overflowed: below)
@@ -769,7 +837,12 @@ void prefill_select_kernel(SelArgs A) {
 #pragma unroll
             for (int e = 0; e < kMaxTG; ++e) top[e] = 0;
             for (int at = 0; at < c; ++at) {
-                uint64_t x = rank_key(s.cs[n][at], (uint32_t)s.cg[n][at]);
+                // ranking key: surely opened above every score (ties to the lower id),
+                // surely not 0 (never opened), else the canonical score
+                const uint32_t id = (uint32_t)s.cg[n][at];
+                const int cl = s.cls[n][at];
+                uint64_t x = cl == 2 ? ((0xffffffffull << 32) | (0xffffffffu - id))
+                                     : (cl == 0 ? 0ull : rank_key(s.cub[n][at], id));
 #pragma unroll
                 for (int e = 0; e < kMaxTG; ++e) {
                     const uint64_t hi = top[e] > x ? top[e] : x, lo = top[e] > x ? x : top[e];
@@ -777,7 +850,9 @@ void prefill_select_kernel(SelArgs A) {
                     x = lo;
                 }
             }
-            const int k = min(c, TG);
+            int k = 0;  // surely-out candidates (key 0) are never opened
+#pragma unroll
+            for (int e = 0; e < kMaxTG; ++e) k += (e < TG && top[e] != 0) ? 1 : 0;
             for (int e = 0; e < kMaxTG; ++e)
                 if (e < TG) s.sel[n][e] = e < k ? (int)key_id(top[e]) : -1;
             s.nsel[n] = k;
@@ -863,7 +938,8 @@ void prefill_select_kernel(SelArgs A) {
             const int ps0 = gpg[j], npg = gpg[j + 1] - ps0;
             R.ps0 = (int16_t)ps0;
             R.npg = (int16_t)npg;
-            if (A.TP == 0) {
+            if (A.TP == 0 || (npg <= A.TP && !A.sel_pages)) {
+                // every page opened: no ranking, and no unopened page needs a logit
                 R.open = npg >= 32 ? 0xffffffffu : ((1u << npg) - 1u);
             } else {
                 uint64_t key[kPage];

@@ -48,7 +48,11 @@ def _prefill_and_compare(case, Q, q_start, rows, check_dense=False):
     bit-exact, outputs within tolerance.  Returns (worst error, GPU outputs)."""
     g, o = case.gcfg, case.ocfg
     out, sg, sp = lod.attend_prefill(g, case.index, case.Kd, case.Vd, Q.cuda(), q_start, want_selection=True)
+    # without the selection outputs the kernels only certify which groups and pages open
+    # (no rank order): the same groups and pages open, so the outputs agree bit for bit
+    out_plain = lod.attend_prefill(g, case.index, case.Kd, case.Vd, Q.cuda(), q_start)
     torch.cuda.synchronize()
+    assert torch.equal(out, out_plain), float((out - out_plain).abs().max())
     out, sg, sp = out.cpu().numpy(), sg.cpu().numpy(), sp.cpu().numpy()
     hpg = g.n_q_heads // g.n_kv_heads
     st, oidx = case.oracle_index(sorted({(b, h // hpg) for b, _, h in rows}))
