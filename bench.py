@@ -590,7 +590,7 @@ def cpu_baseline(cfg, Ly, seq_len, seconds):
         orc.decode(ocfg, st, idx, Q, [seq_len], threads=threads)
         n += 1
         el = time.time() - t
-        if el >= seconds or n >= 64:
+        if el >= seconds or n >= 4096:
             break
     return {"value": round(n / el, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} decode token(s) of one sequence (all 64 query heads) at position {p}, "
