@@ -110,6 +110,13 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
+// Order this wave's earlier LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // exp(x) for x <= 0 (softmax weights); exp(-inf) = 0.
 __device__ __forceinline__ float softmax_exp(float x) { return __expf(x); }
 

@@ -1000,7 +1000,7 @@ struct PagesArgs {
     int max_chunks, G, W, TG;
     const PairRec* rec;     // [B][nq][Hq][TG], slot t holds the group selg[t]
     const int32_t* selg;    // [B][nq][Hq][TG] opened groups, ascending (-1 padding)
-    int32_t* plist;         // [units][kChunk * HG * TG] pair indices sorted by group
+    int2* plist;            // [units][kChunk * HG * TG] (pair index, group) sorted by group
     int32_t* poff;          // [units][2]: number of pairs with a group, (unused)
     float* part_fl;         // [nsplit][B][nq][Hq] flash partial states
     int nsplit;
@@ -1021,7 +1021,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
     const int ng = nb * A.G;
     const int npairs = nrows * HG * A.TG;
     const int64_t unit = ((int64_t)b * A.Hkv + kvh) * A.units_per_seq_kv + qc;
-    int32_t* list = A.plist + unit * (kChunk * HG * A.TG);
+    int2* list = A.plist + unit * (kChunk * HG * A.TG);
     auto pair_gid = [&](int x) {
         const int t = x % A.TG, h = (x / A.TG) % HG, rl = x / (A.TG * HG);
         return A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t];
@@ -1071,20 +1071,25 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
         for (int u = 0; u < U; ++u) g[u] = x0 + u * kThreads < npairs ? pair_gid(x0 + u * kThreads) : -1;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (g[u] >= 0) list[atomicAdd(&cnt[g[u]], 1)] = x0 + u * kThreads;
+            if (g[u] >= 0) list[atomicAdd(&cnt[g[u]], 1)] = make_int2(x0 + u * kThreads, g[u]);
     }
 }
 
 // ---------------------------------------------------------------------------- pages
 
 constexpr int kPairsPerWG = 16;  // one (row, head, slot) pair per 16-lane subgroup
+constexpr int kPagesMeta = 320;  // int16 entries of a chunk's meta row held in LDS (>= meta_stride)
 
 // One workgroup per 16 consecutive pairs of a unit's group-sorted list; each 16-lane
 // subgroup runs one pair: exact rows of its opened pages and the mean terms of the
 // unopened pages of its group, one online softmax, written as the pair's partial state.
 // Pairs of the same group run side by side, so their rows come from the same cache lines.
+// A pair's loads form three dependent steps: its list entry (pair and group); the query,
+// its record and the whole meta row of the group's chunk (to LDS); then the rows of the
+// opened pages (batches of 8, kept packed) with the unopened pages' means.
 template <int HG>
 __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
+    __shared__ alignas(16) int16_t mrow[kPairsPerWG][kPagesMeta];
     const int blk = blockIdx.x, unit_local = blockIdx.y;
     const int qc = unit_local % A.units_per_seq_kv;
     const int kvh = (unit_local / A.units_per_seq_kv) % A.Hkv;
@@ -1094,7 +1099,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     const int npairs = A.poff[unit * 2];
     const int r0 = qc * kChunk;
     const int PS = A.L.page_slots;
-    const int32_t* list = A.plist + unit * (kChunk * HG * A.TG);
+    const int2* list = A.plist + unit * (kChunk * HG * A.TG);
     const int bs = A.seq + b;
     const int64_t ubase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks;
     const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + ubase * A.L.meta_stride;
@@ -1103,93 +1108,115 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     const bf16_t* kc = A.k + bs * A.sb + kvh * A.sh;
     const bf16_t* vc = A.v + bs * A.sb + kvh * A.sh;
 
-    // one pair per 16-lane subgroup; its dependent loads are few and wide: the record,
-    // then the page starts, the opened pages' member positions and the first unopened
-    // pages' means together, then the rows in batches of 16 (kept packed)
     const int x = blk * kPairsPerWG + sg;
     if (x >= npairs) return;  // uniform in the subgroup
     const int seg0 = (tid & 63) & ~15;
-    const int pi = list[x];
+    const int2 le = list[x];
+    const int pi = le.x, gid = le.y;
     const int t = pi % A.TG, h = (pi / A.TG) % HG, rl = pi / (A.TG * HG);
     const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h;
+    const int c = gid / A.G, j = gid % A.G;
+    // step 2: query, record, meta row
     float q8[8];
     load8<bf16_t>(A.q + rh * kD, l16, q8);
     const PairRec* R = A.rec + rh * A.TG + t;
-    const int gid = R->gid, ps0 = R->ps0, npg = R->npg;
     const uint32_t open = R->open;
     const float rl16 = R->r[l16];  // lane e: score of page e
-    const int c = gid / A.G;
-    const int16_t* pst = meta_u + (int64_t)c * A.L.meta_stride + (A.G + 1);
-    const int16_t* perm = pst + (PS + 1);
-    const int pstv = l16 <= npg ? pst[ps0 + l16] : 0;  // lane e: first member of page e
-    // unopened pages: the first four means in flight now
-    constexpr int kCP = 4;
-    const uint32_t closed = ~open & ((npg >= 32 ? 0xffffffffu : (1u << npg) - 1u));
-    uint4 cpv[kCP];
-    int cslot[kCP];
     {
-        uint32_t m = closed;
-#pragma unroll
-        for (int u = 0; u < kCP; ++u) {
-            cslot[u] = m ? __builtin_ctz(m) : -1;
-            if (m) {
-                m &= m - 1;
-                cpv[u] = *reinterpret_cast<const uint4*>(pv_u + ((int64_t)c * PS + ps0 + cslot[u]) * kD + 8 * l16);
-            }
-        }
+        // 16-byte pieces l16, l16 + 16, l16 + 32 of the row (a meta row has 36 to 40)
+        const int ms16 = A.L.meta_stride / 8;
+        const uint4* src = reinterpret_cast<const uint4*>(meta_u + (int64_t)c * A.L.meta_stride);
+        const uint4 m0 = src[l16], m1 = src[l16 + 16], m2 = src[min(l16 + 32, ms16 - 1)];
+        *reinterpret_cast<uint4*>(&mrow[sg][8 * l16]) = m0;
+        *reinterpret_cast<uint4*>(&mrow[sg][8 * (l16 + 16)]) = m1;
+        if (l16 + 32 < ms16) *reinterpret_cast<uint4*>(&mrow[sg][8 * (l16 + 32)]) = m2;
     }
+    wave_sync_lds();
+    const int16_t* gpg = &mrow[sg][0];
+    const int16_t* pst = gpg + (A.G + 1);
+    const int16_t* perm = pst + (PS + 1);
+    const int ps0 = gpg[j], npg = gpg[j + 1] - ps0;
+    const uint32_t pmask = npg >= 32 ? 0xffffffffu : (1u << npg) - 1u;
+    const uint32_t opened = open & pmask, closed = ~open & pmask;
+    // step 3: ln n of the unopened pages, the opened rows; then the unopened pages' means
+    // (rare: a group's pages beyond the top ones)
+    const float pln16 = (closed >> l16) & 1u ? pln_u[(int64_t)c * PS + ps0 + l16] : 0.0f;  // lane e: page e
+    // opened rows in page order: row u of the pair is member u - start(e) of opened page e
+    int nrow = 0;
+    for (uint32_t m = opened; m; m &= m - 1) {
+        const int e = __builtin_ctz(m);
+        nrow += pst[ps0 + e + 1] - pst[ps0 + e];
+    }
+    auto row_pos = [&](int u) {  // position of opened row u (u < nrow)
+        int base = 0;
+        for (uint32_t m = opened; m; m &= m - 1) {
+            const int e = __builtin_ctz(m);
+            const int x0 = pst[ps0 + e], n = pst[ps0 + e + 1] - x0;
+            if (u < base + n) return c * kChunk + perm[x0 + u - base];
+            base += n;
+        }
+        return 0;
+    };
     Online st;
     st.init();
-    // opened pages, one at a time: lane u < n holds the position of the page's row u
-    for (uint32_t m = open & ((npg >= 32 ? 0xffffffffu : (1u << npg) - 1u)); m; m &= m - 1) {
-        const int e = __builtin_ctz(m);
-        const int x0 = __shfl(pstv, seg0 + e, 64), x1 = __shfl(pstv, seg0 + e + 1, 64);
-        const int n = x1 - x0;
-        const int pos = l16 < n ? c * kChunk + perm[x0 + l16] : 0;
-        constexpr int RB = 8;  // rows in flight per batch (kept packed)
-        for (int u0 = 0; u0 < n; u0 += RB) {
-            uint4 kp[RB], vp[RB];
+    constexpr int RB = 12;  // rows in flight per batch (kept packed): most pairs need one batch
+    for (int u0 = 0; u0 < nrow; u0 += RB) {
+        const int pos = l16 < RB && u0 + l16 < nrow ? row_pos(u0 + l16) : 0;  // lane u: row u0 + u
+        uint4 kp[RB], vp[RB];
 #pragma unroll
-            for (int u = 0; u < RB; ++u) {
-                const int pu = __shfl(pos, seg0 + ((u0 + u) & 15), 64);
-                if (u0 + u < n) {
-                    kp[u] = *reinterpret_cast<const uint4*>(kc + (int64_t)pu * A.st + 8 * l16);
-                    vp[u] = *reinterpret_cast<const uint4*>(vc + (int64_t)pu * A.st + 8 * l16);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < RB; ++u) {
-                if (u0 + u < n) {  // uniform in the subgroup
-                    float kf[8], vf[8];
-                    Elt<bf16_t>::unpack(kp[u], kf);
-                    Elt<bf16_t>::unpack(vp[u], vf);
-                    float a = 0.0f;
-#pragma unroll
-                    for (int z = 0; z < 8; ++z) a = __builtin_fmaf(q8[z], kf[z], a);
-#pragma unroll
-                    for (int mm = 8; mm >= 1; mm >>= 1) a += __shfl_xor(a, mm, 64);
-                    st.add(A.scale * a, vf);
-                }
+        for (int u = 0; u < RB; ++u) {
+            const int pu = __shfl(pos, seg0 + u, 64);
+            if (u0 + u < nrow) {
+                kp[u] = *reinterpret_cast<const uint4*>(kc + (int64_t)pu * A.st + 8 * l16);
+                vp[u] = *reinterpret_cast<const uint4*>(vc + (int64_t)pu * A.st + 8 * l16);
             }
         }
+        // block update: dot products and their reductions side by side, one rescale
+        float lam[RB];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            float kf[8];
+            Elt<bf16_t>::unpack(kp[u], kf);
+            float a = 0.0f;
+#pragma unroll
+            for (int z = 0; z < 8; ++z) a = __builtin_fmaf(q8[z], kf[z], a);
+            lam[u] = a;
+        }
+#pragma unroll
+        for (int mm = 8; mm >= 1; mm >>= 1)
+#pragma unroll
+            for (int u = 0; u < RB; ++u) lam[u] += __shfl_xor(lam[u], mm, 64);
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            lam[u] = u0 + u < nrow ? A.scale * lam[u] : -INFINITY;
+            mb = fmaxf(mb, lam[u]);
+        }
+        const float mn = fmaxf(st.m, mb);
+        const float al = softmax_exp(st.m - mn);  // st.m = -inf -> 0
+        st.l *= al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.o[e] *= al;
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+            if (lam[u] == -INFINITY) continue;  // no row: its registers were not loaded
+            const float wgt = softmax_exp(lam[u] - mn);
+            float vf[8];
+            Elt<bf16_t>::unpack(vp[u], vf);
+            st.l += wgt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[e] = __builtin_fmaf(wgt, vf[e], st.o[e]);
+        }
+        st.m = mn;
     }
     // unopened pages: mean terms
-#pragma unroll
-    for (int u = 0; u < kCP; ++u) {
-        if (cslot[u] < 0) continue;
-        float vf[8];
-        Elt<bf16_t>::unpack(cpv[u], vf);
-        const int e = cslot[u];
-        st.add(A.scale * __shfl(rl16, seg0 + e, 64) + pln_u[(int64_t)c * PS + ps0 + e], vf);
-    }
     {
         uint32_t m = closed;
-        for (int u = 0; u < kCP && m; ++u) m &= m - 1;  // skip the four already done
         for (; m; m &= m - 1) {
             const int e = __builtin_ctz(m);
             float vf[8];
             load8<bf16_t>(pv_u + ((int64_t)c * PS + ps0 + e) * kD, l16, vf);
-            st.add(A.scale * __shfl(rl16, seg0 + e, 64) + pln_u[(int64_t)c * PS + ps0 + e], vf);
+            st.add(A.scale * __shfl(rl16, seg0 + e, 64) + __shfl(pln16, seg0 + e, 64), vf);
         }
     }
     float* dst = A.part_pg + (rh * A.TG + t) * kPartStride;
@@ -1265,7 +1292,7 @@ static PrefillPlan plan_prefill(const lod_params* p, int n_q) {
     P.off_rec = o; o = align256(o + rh * TG * sizeof(PairRec));
     P.off_pfl = o; o = align256(o + (size_t)P.nsplit * rh * kPartStride * 4);
     P.off_ppg = o; o = align256(o + rh * TG * kPartStride * 4);
-    P.off_plist = o; o = align256(o + units * kChunk * HG * TG * 4);
+    P.off_plist = o; o = align256(o + units * kChunk * HG * TG * 8);
     P.off_poff = o; o = align256(o + units * 2 * 4);
     P.off_ltop = o; o = align256(o + (size_t)P.nsplit * rh * kMaxTG * 4);
     P.off_lcnt = o; o = align256(o + (size_t)P.nsplit * rh * 4);
@@ -1422,7 +1449,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
             G.rec = S.rec;
             G.selg = S.selg;
-            G.plist = reinterpret_cast<int32_t*>(w + P.off_plist);
+            G.plist = reinterpret_cast<int2*>(w + P.off_plist);
             G.poff = reinterpret_cast<int32_t*>(w + P.off_poff);
             G.part_fl = F.part;
             G.nsplit = F.nsplit;
