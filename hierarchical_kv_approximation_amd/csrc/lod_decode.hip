@@ -590,25 +590,22 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         if (A.TP > 0) {
             uint64_t key = e < npg ? rank_key(r, (uint32_t)e) : 0;
             const int nopen = npg < A.TP ? npg : A.TP;  // uniform within the 16-lane segment
-            for (int t = 0; t < A.TP; ++t) {          // uniform trip count for the shuffles
-                uint64_t m = key;
-#pragma unroll
-                for (int sh = 8; sh >= 1; sh >>= 1) {
-                    const uint64_t o = shfl_xor_u64(m, sh);
-                    m = o > m ? o : m;
-                }
+            for (int t = 0; t < A.TP; ++t) {          // uniform trip count for the row reductions
+                const uint64_t m = row16_max_u64(key);
                 if (t < nopen && key == m && m != 0) { rank = t; key = 0; }
             }
         }
         // sel_pages: lane t of the segment writes the slot of rank t
-        const int seg0 = lane & ~15;
-        int slot_of_rank = -1;
-        for (int x = 0; x < 16; ++x) {
-            const int rk = __shfl(rank, seg0 + x, 64);
-            if (A.TP > 0 && rk == e) slot_of_rank = ps0 + x;
+        if (A.sel_pages) {
+            const int seg0 = lane & ~15;
+            int slot_of_rank = -1;
+            for (int x = 0; x < 16; ++x) {
+                const int rk = __shfl(rank, seg0 + x, 64);
+                if (A.TP > 0 && rk == e) slot_of_rank = ps0 + x;
+            }
+            if (k < ngw && i < A.TG && e < TPW)
+                A.sel_pages[(head * A.TG + i) * TPW + e] = i < nsel ? slot_of_rank : -1;
         }
-        if (A.sel_pages && k < ngw && i < A.TG && e < TPW)
-            A.sel_pages[(head * A.TG + i) * TPW + e] = i < nsel ? slot_of_rank : -1;
         // item lists: unopened pages (coarse) and exact rows of opened pages
         const bool coarse = e < npg && rank < 0;
         const uint64_t cm = __ballot(coarse);
@@ -622,15 +619,13 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         const int16_t* pst = mrowp(i < kMaxTG ? i : 0) + (A.G + 1);
         const int16_t* perm = pst + (PS + 1);
         const int cnt = (e < npg && rank >= 0) ? pst[ps0 + e + 1] - pst[ps0 + e] : 0;
-        int off = cnt;  // inclusive prefix over the wave's lanes
-#pragma unroll
-        for (int sh = 1; sh < 64; sh <<= 1) {
-            const int o = __shfl_up(off, sh, 64);
-            if (lane >= sh) off += o;
-        }
-        const int total = __shfl(off, 63, 64);
+        int off = wave_incl_scan_i32(cnt);  // inclusive prefix over the wave's lanes
+        const int total = __builtin_amdgcn_readlane(off, 63);
         off -= cnt;
-        for (int x = 0; x < cnt; ++x) s.ex[wave][off + x] = c * kChunk + perm[pst[ps0 + e] + x];
+        const int p0 = (e < npg && rank >= 0) ? pst[ps0 + e] : 0;
+#pragma unroll
+        for (int x = 0; x < kPage; ++x)  // a page holds at most kPage rows
+            if (x < cnt) s.ex[wave][off + x] = c * kChunk + perm[p0 + x];
         if (lane == 0) s.nex[wave] = total;
     }
     wave_sync();
@@ -666,9 +661,7 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
             lam[x] = a;
         }
 #pragma unroll
-        for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-            for (int x = 0; x < OB; ++x) lam[x] += __shfl_xor(lam[x], m, 64);
+        for (int x = 0; x < OB; ++x) lam[x] = row16_sum_f32(lam[x]);
 #pragma unroll
         for (int x = 0; x < OB; ++x) lam[x] = base + sgw + 4 * x < nex ? A.scale * lam[x] : -INFINITY;
         open_block_add<T, OB, U>(st, lam, vp);
@@ -1040,6 +1033,7 @@ __device__ __forceinline__ void mfma_init(MSmem<HG>& s, float (*o)[4]) {
 constexpr int kSTile = kScanTile;                      // rows per scan tile
 constexpr int kSPieces = kSTile * kD / 8 / kThreads;   // 16-byte pieces per thread and row kind
 constexpr int kSWStride = kSTile + 8;                  // bf16 per head row of the weights
+static_assert(kSPieces == 4, "the scan stage packs four rows per thread");
 
 template <int HG>
 struct MScanSmem {
@@ -1065,21 +1059,23 @@ struct ScanSrc {
     int ns, w0, nex;
 };
 
-// One tile in registers: pieces tid + kThreads * i (row piece / 16, chunk piece % 16) of
-// its key and value rows (rows past the tile repeat its last row), and the bias of row tid.
+// One tile in registers: thread tid holds the 16-byte chunk c = tid % 16 of rows
+// 4g .. 4g+3, g = tid / 16, of its key and value rows (rows past the tile repeat its last
+// row), and the bias of row tid.  Four rows per thread let the value transpose go to LDS
+// as 8-byte words (four rows of one dimension).
 struct ScanRegs {
     u32x4_t k[kSPieces], v[kSPieces];
     float bias;
 };
 
 __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t, int ntc) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, c = tid & 15, g = tid >> 4;
     if (t < ntc) {
         const int r0 = t * kSTile, n = min(kSTile, S.ng - r0);
 #pragma unroll
         for (int i = 0; i < kSPieces; ++i) {
-            const int pc = tid + kThreads * i, row = min(pc >> 4, n - 1);
-            const int64_t off = (int64_t)(r0 + row) * kD + 8 * (pc & 15);
+            const int row = min(4 * g + i, n - 1);
+            const int64_t off = (int64_t)(r0 + row) * kD + 8 * c;
             R.k[i] = *reinterpret_cast<const u32x4_t*>(S.gk + off);
             R.v[i] = *reinterpret_cast<const u32x4_t*>(S.gv + off);
         }
@@ -1088,9 +1084,9 @@ __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t,
         const int x0 = (t - ntc) * kSTile, n = min(kSTile, S.nex - x0);
 #pragma unroll
         for (int i = 0; i < kSPieces; ++i) {
-            const int pc = tid + kThreads * i, x = x0 + min(pc >> 4, n - 1);
+            const int x = x0 + min(4 * g + i, n - 1);
             const int pos = x < S.ns ? x : S.w0 + (x - S.ns);
-            const int64_t off = (int64_t)pos * S.st + 8 * (pc & 15);
+            const int64_t off = (int64_t)pos * S.st + 8 * c;
             R.k[i] = *reinterpret_cast<const u32x4_t*>(S.kb + off);
             R.v[i] = *reinterpret_cast<const u32x4_t*>(S.vb + off);
         }
@@ -1098,21 +1094,28 @@ __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t,
     }
 }
 
+// Keys row-major with 16-byte chunks swizzled by row; values transposed, one 8-byte
+// write per dimension holding rows 4g .. 4g+3 (packed from the four row registers).
 template <int HG>
 __device__ __forceinline__ void scan_stage(MScanSmem<HG>& s, const ScanRegs& R) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, c = tid & 15, g = tid >> 4;
 #pragma unroll
     for (int i = 0; i < kSPieces; ++i) {
-        const int pc = tid + kThreads * i, row = pc >> 4, c = pc & 15;
+        const int row = 4 * g + i;
         *reinterpret_cast<u32x4_t*>(&s.kl[row][8 * (c ^ (row & 15))]) = R.k[i];
-        // value piece: dims 8c .. 8c+7 of row `row` go down column positions of vt
-        const int pos = 8 * ((row >> 3) ^ (c & 7)) + (row & 7);
-        const uint32_t w4[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+    }
+    // rows 4g .. 4g+3 sit at column positions 8 * ((g / 2) ^ (d / 8 % 8)) + 4 * (g % 2) + i
+    const int pos = 8 * ((g >> 1) ^ (c & 7)) + 4 * (g & 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s.vt[8 * c + 2 * e][pos] = (bf16_t)(w4[e] & 0xffffu);
-            s.vt[8 * c + 2 * e + 1][pos] = (bf16_t)(w4[e] >> 16);
-        }
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t a0 = R.v[0][m], a1 = R.v[1][m], a2 = R.v[2][m], a3 = R.v[3][m];
+        uint2 lo, hi;  // dimension 8c + 2m (low halves) and 8c + 2m + 1 (high halves)
+        lo.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+        *reinterpret_cast<uint2*>(&s.vt[8 * c + 2 * m][pos]) = lo;
+        *reinterpret_cast<uint2*>(&s.vt[8 * c + 2 * m + 1][pos]) = hi;
     }
     if (tid < kSTile) s.bias[tid] = R.bias;
 }
@@ -1335,7 +1338,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     float qn = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qn = __builtin_fmaf(q8[e], q8[e], qn);
-    qn = sqrtf(wave_sum_f32(qn, 16)) * 1.0001f;
+    qn = sqrtf(row16_sum_f32(qn)) * 1.0001f;
     const float eq = kErrC * qn;
     if (!part_in_lds) open_merge_scan(s, part, nscan);
 
@@ -1400,26 +1403,15 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         for (int e = 0; e < 16; ++e)
             if (e == TG - 1) T = v[e];
     }
-    // 1d. candidates: S + E >= T (a single block of groups is still in registers); one
-    //     LDS atomic per wave, positions from the ballots of the wave (by u, then lane)
+    // 1d. candidates: S + E >= T (a single block of groups is still in registers).  They
+    //     are few, so each takes its slot with an LDS atomic; the order of the slots does
+    //     not matter (ranking compares keys).
     for (int g0 = 0; g0 < ng; g0 += SPT * kThreads) {
         if (ng > SPT * kThreads) load_scores(g0);
-        uint64_t mk[SPT];
-        int wtot = 0;
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
-            mk[u] = __ballot(ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T);
-            wtot += __popcll(mk[u]);
-        }
-        if (wtot == 0) continue;  // uniform over the wave
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&s.ncand, wtot);
-        base = __shfl(base, 0, 64);
-        const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            if ((mk[u] >> lane) & 1ull) {
-                const int at = base + __popcll(mk[u] & below);
+            if (ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T) {
+                const int at = atomicAdd(&s.ncand, 1);
                 if (at < kOpenCand) {
                     s.cg[at] = g0 + tid + kThreads * u;
                     s.cS[at] = sv[u];
@@ -1427,7 +1419,6 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
                     s.cP[at] = gp[u];
                 }
             }
-            base += __popcll(mk[u]);
         }
     }
     __syncthreads();

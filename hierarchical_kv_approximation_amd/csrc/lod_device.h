@@ -99,6 +99,53 @@ __device__ __forceinline__ float wave_sum_f32(float v, int width) {
     return v;
 }
 
+// Reductions over each aligned group of 16 lanes (a DPP row): rotations by 8, 4, 2 and 1
+// lanes within the row.  Each step pairs lanes symmetrically, so every lane of the row
+// ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float row16_sum_f32(float v) {
+    v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));  // row_ror:8
+    v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));  // row_ror:4
+    v += __uint_as_float(dpp_u32<0x122>(__float_as_uint(v)));  // row_ror:2
+    v += __uint_as_float(dpp_u32<0x121>(__float_as_uint(v)));  // row_ror:1
+    return v;
+}
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+#define LODI_ROW_MAX_STEP(CTRL)                                                              \
+    {                                                                                     \
+        const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) |         \
+                           dpp_u32<CTRL>((uint32_t)v);                                    \
+        v = o > v ? o : v;                                                                \
+    }
+    LODI_ROW_MAX_STEP(0x128)
+    LODI_ROW_MAX_STEP(0x124)
+    LODI_ROW_MAX_STEP(0x122)
+    LODI_ROW_MAX_STEP(0x121)
+#undef LODI_ROW_MAX_STEP
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes: a zero-filled shift scan inside each 16-lane
+// row (DPP row_shr 1, 2, 4, 8), then the totals of the lower rows (read from lanes 15,
+// 31, 47).  Every lane of the wave must execute it.
+template <int CTRL>
+__device__ __forceinline__ int dpp_shr_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+    v += dpp_shr_i32<0x111>(v);
+    v += dpp_shr_i32<0x112>(v);
+    v += dpp_shr_i32<0x114>(v);
+    v += dpp_shr_i32<0x118>(v);
+    const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+              t2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = (int)(__lane_id() >> 4);
+    return v + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
+}
+
 // Workgroup barrier over LDS traffic only: each wave waits for its own LDS operations
 // (lgkmcnt 0), not for its vector memory operations, so loads of a later tile (also
 // global -> LDS loads, whose completion the caller awaits with an explicit vmcnt wait
