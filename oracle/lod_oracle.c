@@ -27,6 +27,13 @@
  *                 floor(p/C) exactly (its own causally);
  *   coarse term = logit scale*q.kbar + ln n with value vbar (n identical copies).
  * All softmax arithmetic is fp64.
+ *
+ * Sparsity ablation (drop_remainder = 1): the same selection, but the softmax holds
+ * only the exact keys.  This is the token-removing alternative that the post's "The
+ * Main Idea" section contrasts LoD with, and the attention of "Coarse Semantic Blocks
+ * for Efficient Training-Free Sparse Attention" (readsearch.ai listing, abstract): a
+ * query scores the centroids of key blocks and attends to the original keys of the
+ * blocks it selects (with top_pages = 0, every key of an opened group).
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,6 +58,7 @@ typedef struct {
     int32_t iters;      /* k-means rounds (10) */
     int32_t bf16_store; /* 1: summaries are rounded to bfloat16 */
     double scale;       /* softmax scale, 1/sqrt(d) */
+    int32_t drop_remainder; /* 1: no coarse terms (sparsity ablation) */
 } orc_params;
 
 /* Page slots per chunk: at most C/P full pages plus one partial page per group. */
@@ -389,7 +397,7 @@ int32_t orc_attend(const orc_params* P, const float* q, int32_t p, int32_t n_chu
             vals[nt++] = V + (size_t)x * d;
             ++n_ex;
         }
-        for (int32_t g = 0; g < ng; ++g) {
+        for (int32_t g = 0; g < ng && !P->drop_remainder; ++g) {
             if (gcount[g] <= 0) continue;
             if (!opened[g]) {
                 lam[nt] = P->scale * dot64(q, gk + (size_t)g * d, d) + log((double)gcount[g]);

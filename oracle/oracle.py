@@ -46,7 +46,8 @@ class _Params(ctypes.Structure):
                 ("groups", ctypes.c_int32), ("top_groups", ctypes.c_int32),
                 ("top_pages", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("iters", ctypes.c_int32),
-                ("bf16_store", ctypes.c_int32), ("scale", ctypes.c_double)]
+                ("bf16_store", ctypes.c_int32), ("scale", ctypes.c_double),
+                ("drop_remainder", ctypes.c_int32)]
 
 
 _lib = None
@@ -105,12 +106,13 @@ class Config:
     iters: int = 10
     bf16: bool = False
     scale: float | None = None
+    drop_remainder: bool = False  # sparsity ablation: exact keys only, no coarse terms
 
     def params(self) -> _Params:
         sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
         return _Params(self.d, self.chunk, self.page, self.groups, self.top_groups,
                        self.top_pages, self.window, self.n_sink, self.iters,
-                       1 if self.bf16 else 0, sc)
+                       1 if self.bf16 else 0, sc, 1 if self.drop_remainder else 0)
 
     @property
     def page_slots(self) -> int:

@@ -6,6 +6,7 @@ closed forms, a hand-worked example (tests/golden), an independent library (torc
 bfloat16 cast, scikit-learn's Lloyd k-means, numpy dense softmax), invariants, or brute
 force over tiny inputs.
 """
+import dataclasses
 import json
 import math
 import os
@@ -488,3 +489,60 @@ def test_error_grows_with_cluster_spread_and_two_tier_is_closer():
         assert mean_err[(0.1, tier)] < mean_err[(1.0, tier)], mean_err
     for sigma in (0.1, 1.0):
         assert mean_err[(sigma, "two")] <= mean_err[(sigma, "three")], mean_err
+
+
+# --------------------------------------------------------------------------- sparsity ablation
+
+def _exact_positions(cfg, idx, p, r):
+    """Sinks, the block window and the members of the pages the selection opened."""
+    C, G, PS = cfg.chunk, cfg.groups, cfg.page_slots
+    nb = cfg.built_chunks(p)
+    exact = set(range(min(cfg.n_sink, p + 1))) | set(range(nb * C, p + 1))
+    for i, g in enumerate(g for g in r["sel_groups"].tolist() if g >= 0):
+        c, j = divmod(g, G)
+        slots = [sl for sl in range(PS) if idx["pgroup"][c, sl] == j]
+        chosen = slots if cfg.top_pages == 0 else [s for s in r["sel_pages"][i].tolist() if s >= 0]
+        for sl in chosen:
+            exact |= set(idx["pmem"][c, sl, : idx["pcount"][c, sl]].tolist())
+    return sorted(exact)
+
+
+@pytest.mark.parametrize("top_pages", [2, 0])
+def test_sparsity_ablation_is_softmax_over_the_exact_keys(top_pages):
+    """Dropping the coarse remainder (the token-removing alternative of "The Main Idea";
+    with top_pages = 0 the block attention of "Coarse Semantic Blocks") keeps LoD's
+    selection and leaves a plain softmax over the exact keys only; the remainder can only
+    add mass."""
+    lod = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=3, top_pages=top_pages,
+                     window=128, n_sink=2)
+    sparse = dataclasses.replace(lod, drop_remainder=True)
+    K, V, cen, _ = _mixture(1024, 16, 6, n_centres=8, sigma=0.5)
+    idx = orc.build_stream(lod, K, V, 16)
+    rng = np.random.default_rng(8)
+    for p in [0, 5, 63, 64, 127, 128, 200, 511, 777, 1023]:
+        q = (cen[rng.integers(0, 8)] + 0.3 * rng.standard_normal(16)).astype(np.float32)
+        r = orc.attend(sparse, idx, K, V, q, p)
+        r_lod = orc.attend(lod, idx, K, V, q, p)
+        assert r["sel_groups"].tolist() == r_lod["sel_groups"].tolist()
+        assert r["sel_pages"].tolist() == r_lod["sel_pages"].tolist()
+        ex = _exact_positions(lod, idx, p, r)
+        lam = lod.params().scale * (K[ex].astype(np.float64) @ q.astype(np.float64))
+        w = np.exp(lam - lam.max())
+        ref = (w[:, None] * V[ex].astype(np.float64)).sum(0) / w.sum()
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12)
+        assert r["n_terms"].tolist() == [len(ex), 0, 0]
+        assert abs(r["log_mass"] - (lam.max() + math.log(w.sum()))) < 1e-10
+        assert r["log_mass"] <= r_lod["log_mass"] + 1e-12
+
+
+def test_sparsity_ablation_opening_everything_is_dense():
+    """With every group and page open there is no remainder to drop: dense attention."""
+    cfg = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=10**6, top_pages=0,
+                     window=64, n_sink=3, drop_remainder=True)
+    K, V, cen, _ = _mixture(1000, 16, 11)
+    idx = orc.build_stream(cfg, K, V, 15)
+    rng = np.random.default_rng(13)
+    for p in [0, 3, 64, 500, 999]:
+        q = rng.standard_normal(16).astype(np.float32)
+        r = orc.attend(cfg, idx, K, V, q, p)
+        assert np.allclose(r["out"], _dense_np(K, V, q, p, cfg.params().scale)[0], rtol=0, atol=1e-12)
