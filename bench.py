@@ -280,6 +280,28 @@ def main():
                  "achieved_GBs": round(dense_bytes / dms / 1e6, 1),
                  "lod_speedup_vs_dense": round(dms / ms_per_step, 2)}
 
+    # sparsity ablation on the same inputs: the same selection, the coarse remainder
+    # dropped (the scan reads the mean keys for the scores but no mean values)
+    import dataclasses
+    scfg = dataclasses.replace(cfg, drop_remainder=True)
+    for k in range(min(W, 4)):
+        Ly = layers[k % L]
+        lod.attend_decode(scfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[npos - 1], max_len, ws=ws, out=out)
+    torch.cuda.synchronize()
+    s0e, s1e = hip.create(2)
+    hip.record(s0e, stream)
+    for k in range(K):
+        Ly = layers[k % L]
+        lod.attend_decode(scfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[k // L], max_len, ws=ws, out=out)
+    hip.record(s1e, stream)
+    torch.cuda.synchronize()
+    sms = hip.ms(s0e, s1e) / K
+    hip.destroy([s0e, s1e])
+    sparse = {"what": "same selection, coarse remainder dropped (exact keys only)",
+              "ms_per_call": round(sms, 5), "tok_per_s": round(B * 1000.0 / sms, 1),
+              "time_vs_lod": round(sms / ms_per_step, 3)}
+    log(f"sparsity ablation: {sms * 1000:.1f} us/call")
+
     # CPU oracle on a bounded sample: sequence 0 of layer 0, all 64 heads, one token
     cpu = None
     if not args.no_cpu:
@@ -344,6 +366,7 @@ def main():
             "call_achieved_GBs": round(bytes_call / (call_avg * 1e-3) / 1e9, 1),
             "call_frac_hbm": round(bytes_call / (call_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "dense_decode": dense,
+            "sparsity_ablation": sparse,
             "setup_s": round(setup_s, 1),
         },
         "prefill": prefill,
@@ -493,10 +516,13 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
 
 def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, samples=96):
     """After a T-token prompt, 256 decode steps of one sequence (batch 1) with one chunk
-    build at the boundary, for three-tier and two-tier LoD; keys whose 32 clusters have
-    sigma spread over 0.1 .. 1.0 and queries matched to a cluster.  Reports decode time
-    per token for both, and the error of the LoD output against the dense oracle (fp64)
-    on sampled (step, head) pairs, binned by the sigma of the query's cluster."""
+    build at the boundary, for three-tier and two-tier LoD and for the sparsity ablation
+    (the same selection without the coarse remainder; and block-sparse attention with
+    larger blocks and a larger budget: 4 groups of 64 keys per chunk, 16 opened whole);
+    keys whose 32 clusters have sigma spread over 0.1 .. 1.0 and queries matched to a
+    cluster.  Reports decode time per token for each, and the error of its output against
+    the dense oracle (fp64) on sampled (step, head) pairs, binned by the sigma of the
+    query's cluster."""
     import dataclasses
 
     import numpy as np
@@ -507,15 +533,22 @@ def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, s
     sig = torch.linspace(0.1, 1.0, 32)
     K, V, cen, _ = synth.clustered_kv(1, T + steps, 8, 128, sigma=sig, seed=seed + 777, device=dev)
     Q, z = synth.queries(1, 64, cen, n_rows=steps, sigma=sig, seed=seed + 778, return_centres=True)
-    idx = lod.LodIndex.allocate(cfg, 1, T + steps, device=dev)
     nb0 = (T - 1) // C - cfg.window // C + 1  # chunks the prompt's last row sees
-    # every chunk the decode steps see; the timed region rebuilds the boundary chunk
-    lod.build_chunk(cfg, idx, K, V, 0, nb0 + 1)
+    variants = (("three_tier", dataclasses.replace(cfg)),
+                ("two_tier", dataclasses.replace(cfg, top_pages=0)),
+                ("sparse_three_tier", dataclasses.replace(cfg, drop_remainder=True)),
+                ("sparse_blocks_G4_top16", dataclasses.replace(cfg, groups=4, top_groups=16, top_pages=0,
+                                                               drop_remainder=True)))
+    indexes = {}
+    for G in sorted({c.groups for _, c in variants}):
+        # every chunk the decode steps see; the timed region rebuilds the boundary chunk
+        indexes[G] = lod.LodIndex.allocate(dataclasses.replace(cfg, groups=G), 1, T + steps, device=dev)
+        lod.build_chunk(dataclasses.replace(cfg, groups=G), indexes[G], K, V, 0, nb0 + 1)
     torch.cuda.synchronize()
     res = {}
     outs = {}
-    for name, TP in (("three_tier", cfg.top_pages), ("two_tier", 0)):
-        c = dataclasses.replace(cfg, top_pages=TP)
+    for name, c in variants:
+        idx = indexes[c.groups]
         ws = torch.empty(lod.decode_ws_bytes(c, 1, T + steps), dtype=torch.uint8, device=dev)
         lens = torch.arange(T + 1, T + steps + 1, dtype=torch.int32, device=dev).view(steps, 1)
         out = torch.empty(steps, 64, 128, dtype=torch.float32, device=dev)
@@ -562,7 +595,7 @@ def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, s
                          "mean_max_abs_err": round(float(np.mean(errs)), 5) if errs else None,
                          "max_abs_err": round(float(np.max(errs)), 5) if errs else None})
         res[name]["error_vs_dense_oracle_by_sigma"] = bins
-    del K, V, Q, idx
+    del K, V, Q, indexes
     log("sigma sweep: " + ", ".join(f"{n} {r['decode_us_per_token']} us/token" for n, r in res.items()))
     return {"workload": f"one sequence, {T}-token prompt then {steps} decode steps with one chunk build, "
                         "GQA 64/8, bf16; 32 key clusters with sigma 0.1..1.0, matched queries",

@@ -49,6 +49,7 @@ struct DecodeArgs {
     int score_stride;
     int Hq, Hkv, G, TG, TP, W, n_sink;
     float scale;
+    int drop;  // 1: no coarse remainder (sparsity ablation)
     int slice, nslice, nwin, nslot;
     // query rows: with seq_lens, row r is sequence r at position seq_lens[r]-1 (decode);
     // without, row r is sequence seq0 + r / rows_per_seq at position pos0 + r % rows_per_seq
@@ -351,7 +352,11 @@ __global__ __launch_bounds__(kThreads) void decode_scan_kernel(DecodeArgs A) {
         __syncthreads();
         for (int e = threadIdx.x; e < HG * A.TG; e += kThreads)
             cand[(e / A.TG) * cand_head_stride + e % A.TG] = s.ckey[e / A.TG][e % A.TG];
-        // 3. coarse softmax partial over the remaining groups
+        // 3. coarse softmax partial over the remaining groups (none without the remainder)
+        if (A.drop) {
+            write_partial<HG>(s, R, o, m_run, l_run, part0, head_stride);
+            return;
+        }
         float mx = -INFINITY;
         for (int r = R.li; r < cnt; r += TPH) mx = fmaxf(mx, s.lam[R.h][r]);
         mx = head_allreduce<HG, true>(mx, s.red);
@@ -523,7 +528,9 @@ __device__ __forceinline__ void open_block_add(Online& st, const float* lam, con
     st.m = mn;
 }
 
-template <typename T, int OB>
+// DROP: no coarse remainder, so unopened pages add no terms (a run-time flag on the fp32
+// path, DROP_RT; a compile-time one on the bf16 path).
+template <typename T, int OB, bool DROP_RT = true, bool DROP = false>
 __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int seq, int kvh, int64_t head,
                            const float* q8, Online& st) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -666,7 +673,7 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         for (int x = 0; x < OB; ++x) lam[x] = base + sgw + 4 * x < nex ? A.scale * lam[x] : -INFINITY;
         open_block_add<T, OB, U>(st, lam, vp);
     }
-    const int ncp = s.ncp[wave];
+    const int ncp = (DROP || (DROP_RT && A.drop)) ? 0 : s.ncp[wave];  // unopened pages: coarse terms
     for (int base = 0; base < ncp; base += 4 * OB) {
         u32x4_t vp[OB][U];
         float lam[OB];
@@ -764,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
     open_pages<T, kOpenBatch>(A, s, nsel, seq, kvh, head, q8, st);
 
     // add back the coarse terms of candidates that lost the global ranking
-    if (kth != 0) {
+    if (kth != 0 && !A.drop) {
         const T* gv = reinterpret_cast<const T*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
         const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + unit * A.max_chunks * A.G;
         constexpr int AB = 2 * kOpenBatch;
@@ -1068,6 +1075,8 @@ struct ScanRegs {
     float bias;
 };
 
+// DROP (no coarse remainder): coarse tiles only give scores, so their values are not read.
+template <bool DROP>
 __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t, int ntc) {
     const int tid = threadIdx.x, c = tid & 15, g = tid >> 4;
     if (t < ntc) {
@@ -1077,7 +1086,7 @@ __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t,
             const int row = min(4 * g + i, n - 1);
             const int64_t off = (int64_t)(r0 + row) * kD + 8 * c;
             R.k[i] = *reinterpret_cast<const u32x4_t*>(S.gk + off);
-            R.v[i] = *reinterpret_cast<const u32x4_t*>(S.gv + off);
+            if (!DROP) R.v[i] = *reinterpret_cast<const u32x4_t*>(S.gv + off);
         }
         R.bias = tid < kSTile ? S.gln[r0 + min(tid, n - 1)] : 0.0f;
     } else {
@@ -1163,7 +1172,7 @@ __device__ __forceinline__ void scan_pv(const MScanSmem<HG>& s, f32x4_t* o) {
 // Decode launch 1 (bf16): workgroup x of a (sequence, KV head) unit scans tiles
 // [x * nt / nslice, (x + 1) * nt / nslice) of the unit's tile list: MFMA scores (written
 // out for the selection on coarse tiles), online softmax and PV, then its partial state.
-template <int HG>
+template <int HG, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void decode_scan_mfma_kernel(DecodeArgs A) {
     __shared__ MScanSmem<HG> s;
@@ -1206,7 +1215,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     bf16x8_t qa[4];
     mfma_load_q<HG>(q0, qa);
     ScanRegs R;
-    if (t0 < t1) scan_fetch(R, S, t0, ntc);
+    if (t0 < t1) scan_fetch<DROP>(R, S, t0, ntc);
 
     for (int t = t0; t < t1; ++t) {
         const bool coarse = t < ntc;
@@ -1215,7 +1224,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
         scan_stage(s, R);  // the last tile's PV is done (barrier at the end of the loop)
         __syncthreads();
         scan_scores<HG>(s, qa);
-        if (t + 1 < t1) scan_fetch(R, S, t + 1, ntc);  // in flight through this tile
+        if (t + 1 < t1) scan_fetch<DROP>(R, S, t + 1, ntc);  // in flight through this tile
         __syncthreads();
         // coarse tiles: the scores go out for the selection, a 256-byte row per head
         // (rows past the tile's groups are never read; the rows stay inside score_stride)
@@ -1224,7 +1233,9 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
             *reinterpret_cast<float4*>(sdst + (int64_t)h * A.score_stride + r0 + 4 * j) =
                 *reinterpret_cast<const float4*>(&s.sc[h][4 * j]);
         }
-        for (int h = w; h < HG; h += 4) {
+        // without the remainder a coarse tile only yields scores
+        const bool accumulate = !(DROP && coarse);
+        for (int h = w; h < (accumulate ? HG : 0); h += 4) {
             // coarse: the same expression the open kernel uses for the groups it subtracts
             const float bb = s.bias[l];
             const float lam = (l < n && bb != -INFINITY) ? A.scale * s.sc[h][l] + bb : -INFINITY;
@@ -1245,12 +1256,14 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
             }
         }
         __syncthreads();
-        const float a = s.alpha[l & 15];
+        if (accumulate) {
+            const float a = s.alpha[l & 15];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[mb][i] *= a;
-        scan_pv<HG>(s, o);
+                for (int i = 0; i < 4; ++i) o[mb][i] *= a;
+            scan_pv<HG>(s, o);
+        }
         __syncthreads();
     }
 
@@ -1282,6 +1295,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
 // same logits, are subtracted in the final merge.  The subtracted mass never exceeds
 // the scan's, and the exact terms of the opened pages carry at least the same order of
 // mass, so fp32 cancellation stays near 1e-6 of the output scale.
+template <bool DROP>
 __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b, int hq) {
     const int HG = A.Hq / A.Hkv;
     const int kvh = hq / HG;
@@ -1558,12 +1572,12 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     if (tid < kD) {
 #pragma unroll
         for (int i = 0; i < kMaxTG; ++i)
-            vsub[i] = i < nsel ? gv[(int64_t)key_id(s.sel[i]) * kD + tid] : 0u;
+            vsub[i] = (i < nsel && !DROP) ? gv[(int64_t)key_id(s.sel[i]) * kD + tid] : 0u;
     }
 
     Online st;
     st.init();
-    open_pages<bf16_t, 2 * kOpenBatch>(A, s, nsel, seq, kvh, head, q8, st);
+    open_pages<bf16_t, 2 * kOpenBatch, false, DROP>(A, s, nsel, seq, kvh, head, q8, st);
     open_stash(s, st);
     if (part_in_lds) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1602,7 +1616,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
             O = SO * e;
 #pragma unroll
             for (int i = 0; i < kMaxTG; ++i) {
-                if (i >= nsel) break;
+                if (i >= nsel || DROP) break;  // no remainder: nothing was summed
                 const float w = softmax_exp(s.sub_lam[i] - M);
                 L -= w;
                 O = __builtin_fmaf(-w, bf16_bits_to_f32(vsub[i]), O);
@@ -1621,10 +1635,11 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
 // Decode launch 2 (bf16): one workgroup per (sequence, query head) runs the open step and
 // the final merge.  Consecutive workgroups take different KV heads, so the query heads
 // of one KV head share an XCD (workgroups are dealt to the 8 XCDs round robin).
+template <bool DROP>
 __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A) {
     __shared__ OpenSmem<bf16_t> s;
     const int j = blockIdx.x;
-    decode_open_role(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
+    decode_open_role<DROP>(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
 }
 
 
@@ -1734,10 +1749,19 @@ static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
     trace_point(0, st);
     if constexpr (sizeof(T) == 2) {
         if (A.nslice + A.nwin > 0)
-            hipLaunchKernelGGL((decode_scan_mfma_kernel<HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
-                               dim3(kThreads), 0, st, A);
+        {
+            if (A.drop)
+                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, true>), dim3(A.nslice + A.nwin, A.Hkv, rows),
+                                   dim3(kThreads), 0, st, A);
+            else
+                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, false>), dim3(A.nslice + A.nwin, A.Hkv, rows),
+                                   dim3(kThreads), 0, st, A);
+        }
         trace_point(1, st);
-        hipLaunchKernelGGL(decode_open_mfma_kernel, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+        if (A.drop)
+            hipLaunchKernelGGL(decode_open_mfma_kernel<true>, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+        else
+            hipLaunchKernelGGL(decode_open_mfma_kernel<false>, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
         trace_point(2, st);
     } else {
         if (A.nslice + A.nwin > 0)
@@ -1814,7 +1838,7 @@ static void fill_decode_args(DecodeArgs& A, const lod_params* params, const lod_
     A.score_stride = P.score_stride;
     A.Hq = params->n_q_heads; A.Hkv = params->n_kv_heads; A.G = params->groups_per_chunk;
     A.TG = params->top_groups; A.TP = params->top_pages; A.W = params->window;
-    A.n_sink = params->n_sink; A.scale = params->scale;
+    A.n_sink = params->n_sink; A.scale = params->scale; A.drop = params->drop_remainder;
     A.slice = P.slice; A.nslice = P.nslice; A.nwin = P.nwin; A.nslot = P.nslot;
     A.seq0 = 0; A.rows_per_seq = 1; A.pos0 = 0;
 }

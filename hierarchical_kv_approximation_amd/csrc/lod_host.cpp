@@ -16,6 +16,7 @@ int check_params(const lod_params* p) {
     if (p->window % p->chunk_size != 0) return LOD_ERR_ARG;
     if (p->n_sink >= p->chunk_size) return LOD_ERR_ARG;
     if (!(p->scale > 0.0f) || !isfinite(p->scale)) return LOD_ERR_ARG;
+    if (p->drop_remainder != 0 && p->drop_remainder != 1) return LOD_ERR_ARG;
     if (p->kv_dtype != LOD_F32 && p->kv_dtype != LOD_BF16) return LOD_ERR_UNSUPPORTED;
     if (p->head_dim != kD || p->chunk_size != kChunk || p->page_size != kPage)
         return LOD_ERR_UNSUPPORTED;

@@ -47,6 +47,7 @@ struct FlashArgs {
     const char* index;
     lod_index_layout_t L;
     int max_chunks, G, W, n_sink, TG;
+    int drop;             // LoD: 1 = no coarse remainder (sparsity ablation)
     const int32_t* selg;  // [B][nq][Hq][TG] opened groups sorted ascending, -1 padding
     float* part;          // LoD: [nsplit][B][nq][Hq] partial states (o[d], m, l)
     int nsplit;           // LoD: workgroups sharing one tile's key list
@@ -246,7 +247,7 @@ void prefill_flash_kernel(FlashArgs A) {
         const int ng = nb * A.G;
         const int ns = min(A.n_sink, nb * kChunk);
         const int w0 = nb * kChunk;
-        const int ct = (ng + kFlashKeys - 1) / kFlashKeys;
+        const int ct = A.drop ? 0 : (ng + kFlashKeys - 1) / kFlashKeys;  // no remainder: no centroids
         const int st = (ns + kFlashKeys - 1) / kFlashKeys;
         const int wt = p_last >= w0 ? (p_last - w0) / kFlashKeys + 1 : 0;
         const int nt = ct + st + wt;
@@ -998,6 +999,7 @@ struct PagesArgs {
     const char* index;
     lod_index_layout_t L;
     int max_chunks, G, W, TG;
+    int drop;               // 1: no coarse remainder (unopened pages add nothing)
     const PairRec* rec;     // [B][nq][Hq][TG], slot t holds the group selg[t]
     const int32_t* selg;    // [B][nq][Hq][TG] opened groups, ascending (-1 padding)
     int2* plist;            // [units][kChunk * HG * TG] (pair index, group) sorted by group
@@ -1137,7 +1139,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     const int16_t* perm = pst + (PS + 1);
     const int ps0 = gpg[j], npg = gpg[j + 1] - ps0;
     const uint32_t pmask = npg >= 32 ? 0xffffffffu : (1u << npg) - 1u;
-    const uint32_t opened = open & pmask, closed = ~open & pmask;
+    const uint32_t opened = open & pmask, closed = A.drop ? 0u : ~open & pmask;
     // step 3: ln n of the unopened pages, the opened rows; then the unopened pages' means
     // (rare: a group's pages beyond the top ones)
     const float pln16 = (closed >> l16) & 1u ? pln_u[(int64_t)c * PS + ps0 + l16] : 0.0f;  // lane e: page e
@@ -1439,7 +1441,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             F.seq = b; F.sb = kv.stride_b; F.st = kv.stride_t; F.sh = kv.stride_h;
             F.q = S.q; F.nq = rows; F.pos0 = S.pos0; F.Hq = Hq; F.Hkv = Hkv; F.scale = params->scale;
             F.index = S.index; F.L = L; F.max_chunks = S.max_chunks; F.G = S.G; F.W = S.W;
-            F.n_sink = params->n_sink; F.TG = TG; F.selg = S.selg;
+            F.n_sink = params->n_sink; F.TG = TG; F.selg = S.selg; F.drop = params->drop_remainder;
             F.part = reinterpret_cast<float*>(w + P.off_pfl);
             F.nsplit = P.nsplit;
             F.split_stride = (int64_t)P.rows * Hq * kPartStride;
@@ -1447,6 +1449,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.k = F.k; G.v = F.v; G.seq = b; G.sb = F.sb; G.st = F.st; G.sh = F.sh;
             G.q = S.q; G.nq = rows; G.pos0 = S.pos0; G.Hq = Hq; G.Hkv = Hkv; G.scale = params->scale;
             G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
+            G.drop = params->drop_remainder;
             G.rec = S.rec;
             G.selg = S.selg;
             G.plist = reinterpret_cast<int2*>(w + P.off_plist);

@@ -27,7 +27,7 @@ class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "head_dim", "n_q_heads", "n_kv_heads", "chunk_size", "page_size", "groups_per_chunk",
         "top_groups", "top_pages", "window", "n_sink", "kmeans_iters", "kv_dtype")] + \
-        [("scale", ctypes.c_float)]
+        [("scale", ctypes.c_float), ("drop_remainder", ctypes.c_int32)]
 
 
 class KV(ctypes.Structure):
@@ -115,13 +115,14 @@ class Config:
     chunk_size: int = 256
     page_size: int = 16
     scale: float | None = None
+    drop_remainder: bool = False  # sparsity ablation: the same selection, exact keys only
 
     def params(self) -> Params:
         sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
         dt = {torch.float32: LOD_F32, torch.bfloat16: LOD_BF16}.get(self.dtype, 99)
         return Params(self.head_dim, self.n_q_heads, self.n_kv_heads, self.chunk_size,
                       self.page_size, self.groups, self.top_groups, self.top_pages, self.window,
-                      self.n_sink, self.kmeans_iters, dt, sc)
+                      self.n_sink, self.kmeans_iters, dt, sc, 1 if self.drop_remainder else 0)
 
     @property
     def page_slots(self) -> int:

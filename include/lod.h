@@ -58,7 +58,14 @@ enum { LOD_F32 = 0, LOD_BF16 = 1 };
  * 1 <= groups_per_chunk <= 16; 1 <= top_groups <= 16; 0 <= top_pages <= 16
  * (0 = two-tier: every page of an opened group is exact); window a positive multiple
  * of chunk_size; 0 <= n_sink < chunk_size; kmeans_iters >= 1;
- * n_q_heads = g * n_kv_heads with g in {1, 2, 4, 8}.
+ * n_q_heads = g * n_kv_heads with g in {1, 2, 4, 8}; drop_remainder 0 or 1.
+ *
+ * drop_remainder = 1 is the token-removing alternative that the post's "The Main Idea"
+ * section contrasts LoD with: groups and pages are selected exactly as in LoD, but the
+ * softmax holds only the exact keys (opened pages, block window, sinks).  With
+ * top_pages = 0 it is block-sparse attention in the manner of "Coarse Semantic Blocks
+ * for Efficient Training-Free Sparse Attention" (abstract): a query scores block
+ * centroids and attends to the original keys of the blocks it selects.
  */
 typedef struct {
     int32_t head_dim;
@@ -74,6 +81,8 @@ typedef struct {
     int32_t kmeans_iters;     /* Lloyd rounds per chunk (10) */
     int32_t kv_dtype;         /* LOD_F32 or LOD_BF16 */
     float scale;              /* softmax scale, normally 1/sqrt(head_dim) */
+    int32_t drop_remainder;   /* 0: LoD (coarse remainder in the softmax); 1: sparsity
+                                 ablation: the same selection, exact keys only */
 } lod_params;
 
 /* Strided view of the caller's KV cache (see the conventions above). */

@@ -13,11 +13,11 @@ from oracle import oracle as orc
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-3}
 
 
-def configs(dtype, Hq, Hkv, G, TG=8, TP=2, W=512, S=4, iters=10):
+def configs(dtype, Hq, Hkv, G, TG=8, TP=2, W=512, S=4, iters=10, drop=False):
     gcfg = lod.Config(n_q_heads=Hq, n_kv_heads=Hkv, groups=G, top_groups=TG, top_pages=TP,
-                      window=W, n_sink=S, kmeans_iters=iters, dtype=dtype)
+                      window=W, n_sink=S, kmeans_iters=iters, dtype=dtype, drop_remainder=drop)
     ocfg = orc.Config(d=128, groups=G, top_groups=TG, top_pages=TP, window=W, n_sink=S, iters=iters,
-                      bf16=(dtype == torch.bfloat16))
+                      bf16=(dtype == torch.bfloat16), drop_remainder=drop)
     return gcfg, ocfg
 
 
