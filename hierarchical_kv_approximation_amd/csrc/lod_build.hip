@@ -26,6 +26,8 @@ struct BuildArgs {
     const void* k;
     const void* v;
     int64_t sb, st, sh;
+    const int32_t* btab;  // paged view: block table [batch][maxb], else null
+    int bshift, maxb;
     char* index;  // lod_index.mem
     lod_index_layout_t L;
     int max_chunks;
@@ -83,12 +85,13 @@ __device__ __forceinline__ float xat(const BuildSmem<T, GMAX>& s, int i, int t) 
 
 // Load the chunk's members (positions >= n_sink) of K or V into LDS.
 template <typename T, int GMAX>
-__device__ void load_members(BuildSmem<T, GMAX>& s, const T* base, int64_t st, int first_off, int m) {
+__device__ void load_members(BuildSmem<T, GMAX>& s, const BuildArgs& A, const T* base, int b, int t0, int first_off,
+                             int m) {
     constexpr int P16 = Elt<T>::kPer16;
     constexpr int CPR = kD / P16;  // 16-byte chunks per row
     for (int c = threadIdx.x; c < m * CPR; c += kThreads) {
         const int i = c / CPR, col = c % CPR;
-        const T* src = base + (int64_t)(first_off + i) * st + col * P16;
+        const T* src = base + kv_row_rt(A, b, t0 + first_off + i) + col * P16;
         *reinterpret_cast<uint4*>(&s.x[i][xcol<T>(i, col * P16)]) = *reinterpret_cast<const uint4*>(src);
     }
 }
@@ -395,10 +398,12 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     const int PS = A.L.page_slots;
     const int64_t unit = (int64_t)b * A.n_kv_heads + h;
 
-    const T* kbase = reinterpret_cast<const T*>(A.k) + b * A.sb + h * A.sh + (int64_t)c * kChunk * A.st;
-    const T* vbase = reinterpret_cast<const T*>(A.v) + b * A.sb + h * A.sh + (int64_t)c * kChunk * A.st;
+    // head h of the cache; rows through kv_row_rt (positions c * kChunk + ...)
+    const T* kbase = reinterpret_cast<const T*>(A.k) + h * A.sh;
+    const T* vbase = reinterpret_cast<const T*>(A.v) + h * A.sh;
+    const int t0 = c * kChunk;
 
-    load_members(s, kbase, A.st, first_off, m);
+    load_members(s, A, kbase, b, t0, first_off, m);
     if (tid == 0) s.nunc = 0;
     __syncthreads();
 
@@ -535,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int cidx = tid + kThreads * k, i = cidx / CPR, col = cidx % CPR;
-        vreg[k] = i < m ? *reinterpret_cast<const uint4*>(vbase + (int64_t)(first_off + i) * A.st + col * P16)
+        vreg[k] = i < m ? *reinterpret_cast<const uint4*>(vbase + kv_row_rt(A, b, t0 + first_off + i) + col * P16)
                         : make_uint4(0, 0, 0, 0);
     }
     // Page means of keys (group means of keys are already in s.mu).
@@ -581,14 +586,14 @@ extern "C" int lod_build_chunk(const lod_params* params, const lod_index* index,
         return LOD_ERR_ARG;
     if (batch != index->batch || chunk_begin + (int64_t)n_chunks > index->max_chunks)
         return LOD_ERR_ARG;
-    if (kv.stride_t <= 0 || kv.stride_h < 0 || kv.stride_b < 0) return LOD_ERR_ARG;
-    const int per16 = params->kv_dtype == LOD_BF16 ? 8 : 4;
-    if ((kv.stride_t | kv.stride_h | kv.stride_b) % per16 != 0) return LOD_ERR_ARG;
+    if ((rc = check_kv_view(params, kv, (chunk_begin + (int64_t)n_chunks) * params->chunk_size)) != LOD_OK)
+        return rc;
     lod_index_layout_t L = make_layout(params, index->batch, index->max_chunks);
     if (index->bytes < L.total) return LOD_ERR_WORKSPACE;
     if (n_chunks == 0) return LOD_OK;
     BuildArgs A;
-    A.k = kv.k; A.v = kv.v; A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    A.k = kv.k; A.v = kv.v;
+    set_kv_map(A, kv);
     A.index = reinterpret_cast<char*>(index->mem);
     A.L = L;
     A.max_chunks = index->max_chunks;

@@ -34,6 +34,8 @@ struct DecodeArgs {
     const void* k;
     const void* v;
     int64_t sb, st, sh;
+    const int32_t* btab;  // paged view: block table [batch][maxb], else null
+    int bshift, maxb;
     const char* index;
     lod_index_layout_t L;
     int max_chunks;
@@ -62,6 +64,8 @@ struct DenseArgs {
     const void* k;
     const void* v;
     int64_t sb, st, sh;
+    const int32_t* btab;  // paged view: block table [batch][maxb], else null
+    int bshift, maxb;
     const void* q;
     const int32_t* seq_lens;
     int max_seq_len;
@@ -91,20 +95,25 @@ __device__ __forceinline__ void row_info(const DecodeArgs& A, int row, int& seq,
     }
 }
 
-// Stage n rows (row stride in elements) into an fp32 LDS tile.
-template <typename T>
-__device__ __forceinline__ void stage_rows(float (*dst)[kKS], const T* base, int64_t stride, int n) {
+// Stage n rows (row r at row(r)) into an fp32 LDS tile.
+template <typename T, typename RowPtr>
+__device__ __forceinline__ void stage_rows_at(float (*dst)[kKS], RowPtr row, int n) {
     constexpr int P16 = Elt<T>::kPer16;
     constexpr int CPR = kD / P16;
     for (int c = threadIdx.x; c < n * CPR; c += kThreads) {
         const int r = c / CPR, col = c % CPR;
-        const uint4 u = *reinterpret_cast<const uint4*>(base + (int64_t)r * stride + col * P16);
+        const uint4 u = *reinterpret_cast<const uint4*>(row(r) + col * P16);
         float f[P16];
         Elt<T>::unpack(u, f);
 #pragma unroll
         for (int e = 0; e < P16; e += 4)
             *reinterpret_cast<float4*>(&dst[r][col * P16 + e]) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
     }
+}
+// Stage n rows of a strided array (row stride in elements).
+template <typename T>
+__device__ __forceinline__ void stage_rows(float (*dst)[kKS], const T* base, int64_t stride, int n) {
+    stage_rows_at<T>(dst, [&](int r) { return base + (int64_t)r * stride; }, n);
 }
 
 // Reduction over the kThreads/HG threads of one head (max or sum), result in all of them.
@@ -226,15 +235,15 @@ __device__ void write_partial(ScanSmem<HG>& s, const Roles<HG>& R, float* o, flo
 }
 
 // Exact rows [r0, r1) of one (sequence, KV head) with online softmax across tiles.
-template <typename T, int HG>
-__device__ void exact_rows(ScanSmem<HG>& s, const Roles<HG>& R, const float* qr, const T* kb,
-                           const T* vb, int64_t st, int r0, int r1, float scale, float& m_run,
-                           float& l_run, float* o) {
+// Row x of K / V: krow(x), vrow(x) (cache positions).
+template <typename T, int HG, typename KRow, typename VRow>
+__device__ void exact_rows(ScanSmem<HG>& s, const Roles<HG>& R, const float* qr, KRow krow, VRow vrow,
+                           int r0, int r1, float scale, float& m_run, float& l_run, float* o) {
     constexpr int TPH = Roles<HG>::TPH, RP = Roles<HG>::RP;
     for (int base = r0; base < r1; base += kTile) {
         const int n = min(kTile, r1 - base);
-        stage_rows<T>(s.tk, kb + (int64_t)base * st, st, n);
-        stage_rows<T>(s.tv, vb + (int64_t)base * st, st, n);
+        stage_rows_at<T>(s.tk, [&](int r) { return krow(base + r); }, n);
+        stage_rows_at<T>(s.tv, [&](int r) { return vrow(base + r); }, n);
         __syncthreads();
         score_tile<HG>(s.tk, n, qr, s.lam[R.h], R.li);
         float mx = -INFINITY;
@@ -401,9 +410,10 @@ __global__ __launch_bounds__(kThreads) void decode_scan_kernel(DecodeArgs A) {
         r1 = min(r0 + kTile, p + 1);
     }
     if (r1 > r0) {
-        const T* kb = reinterpret_cast<const T*>(A.k) + seq * A.sb + kvh * A.sh;
-        const T* vb = reinterpret_cast<const T*>(A.v) + seq * A.sb + kvh * A.sh;
-        exact_rows<T, HG>(s, R, qr, kb, vb, A.st, r0, r1, A.scale, m_run, l_run, o);
+        const T* kh = reinterpret_cast<const T*>(A.k) + kvh * A.sh;
+        const T* vh = reinterpret_cast<const T*>(A.v) + kvh * A.sh;
+        exact_rows<T, HG>(s, R, qr, [&](int x) { return kh + kv_row_rt(A, seq, x); },
+                          [&](int x) { return vh + kv_row_rt(A, seq, x); }, r0, r1, A.scale, m_run, l_run, o);
     }
     write_partial<HG>(s, R, o, m_run, l_run, part0, head_stride);
 }
@@ -530,7 +540,7 @@ __device__ __forceinline__ void open_block_add(Online& st, const float* lam, con
 
 // DROP: no coarse remainder, so unopened pages add no terms (a run-time flag on the fp32
 // path, DROP_RT; a compile-time one on the bf16 path).
-template <typename T, int OB, bool DROP_RT = true, bool DROP = false>
+template <typename T, int OB, bool PAGED, bool DROP_RT = true, bool DROP = false>
 __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int seq, int kvh, int64_t head,
                            const float* q8, Online& st) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -538,8 +548,9 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
     const int64_t unit = (int64_t)seq * A.Hkv + kvh;
     const int PS = A.L.page_slots;
     const int TPW = A.TP > 0 ? A.TP : 1;
-    const T* kb = reinterpret_cast<const T*>(A.k) + seq * A.sb + kvh * A.sh;
-    const T* vb = reinterpret_cast<const T*>(A.v) + seq * A.sb + kvh * A.sh;
+    // head kvh of sequence seq; the row of a position adds kv_pos
+    const T* kh = reinterpret_cast<const T*>(A.k) + kvh * A.sh + kv_seq<PAGED>(A, seq);
+    const T* vh = reinterpret_cast<const T*>(A.v) + kvh * A.sh + kv_seq<PAGED>(A, seq);
     const T* pk_u = reinterpret_cast<const T*>(A.index + A.L.pk) + unit * A.max_chunks * PS * kD;
     const T* pv_u = reinterpret_cast<const T*>(A.index + A.L.pv) + unit * A.max_chunks * PS * kD;
     const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + unit * A.max_chunks * PS;
@@ -646,11 +657,11 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         for (int x = 0; x < OB; ++x) {
             const int it = base + sgw + 4 * x;
             if (it < nex) {
-                const int pos = s.ex[wave][it];
+                const int64_t ro = kv_pos<PAGED>(A, seq, s.ex[wave][it]);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    kp[x][u] = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)pos * A.st + 8 * l16 + u * P16);
-                    vp[x][u] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)pos * A.st + 8 * l16 + u * P16);
+                    kp[x][u] = *reinterpret_cast<const u32x4_t*>(kh + ro + 8 * l16 + u * P16);
+                    vp[x][u] = *reinterpret_cast<const u32x4_t*>(vh + ro + 8 * l16 + u * P16);
                 }
             }
         }
@@ -708,7 +719,7 @@ __device__ __forceinline__ void open_stash(OpenSmem<T>& s, const Online& st) {
 // candidates are merged into the global top-k, the opened groups are attended through
 // their pages, losing candidates are added back as coarse terms, and the state is
 // merged with the scan workgroups' partial states into the final output.
-template <typename T>
+template <typename T, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
     __shared__ OpenSmem<T> s;
     const int hq = blockIdx.x, b = blockIdx.y;
@@ -768,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void decode_open_kernel(DecodeArgs A) {
 
     Online st;
     st.init();
-    open_pages<T, kOpenBatch>(A, s, nsel, seq, kvh, head, q8, st);
+    open_pages<T, kOpenBatch, PAGED>(A, s, nsel, seq, kvh, head, q8, st);
 
     // add back the coarse terms of candidates that lost the global ranking
     if (kth != 0 && !A.drop) {
@@ -961,17 +972,17 @@ __device__ void mfma_write_partial(MSmem<HG>& s, float (*o)[4], float* dst_head0
 
 // Exact rows (window, sinks, dense): online softmax over chunks of up to 256 rows.
 // Row r of the list is position pos(r) = r < ns ? r : base + (r - ns).
-template <int HG>
+template <int HG, typename RowOff>
 __device__ void mfma_exact_rows(MSmem<HG>& s, const bf16x8_t* qa, const bf16_t* kb, const bf16_t* vb,
-                                int64_t st, int ns, int base, int nrows, float scale, float (*o)[4]) {
+                                RowOff roff, int ns, int base, int nrows, float scale, float (*o)[4]) {
     constexpr int HQ = (HG + 3) / 4, RPH = 8 / HQ;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int hq = tid / (32 * RPH);
     for (int c0 = 0; c0 < nrows; c0 += kMRows) {
         const int n = min(kMRows, nrows - c0);
         auto pos = [&](int r) { const int x = c0 + r; return x < ns ? x : base + (x - ns); };
-        auto krow = [&](int r) { return kb + (int64_t)pos(r) * st; };
-        auto vrow = [&](int r) { return vb + (int64_t)pos(r) * st; };
+        auto krow = [&](int r) { return kb + roff(pos(r)); };
+        auto vrow = [&](int r) { return vb + roff(pos(r)); };
         mfma_issue_v<HG>(s, vrow, n);
         mfma_scores<HG>(s.sc, qa, krow, n);
         __syncthreads();
@@ -1060,9 +1071,11 @@ struct ScanSrc {
     const bf16_t* gv;
     const float* gln;
     int ng;
-    const bf16_t* kb;
+    const bf16_t* kb;  // head kvh of sequence seq; row of position x: kb + kv_pos(*this, seq, x)
     const bf16_t* vb;
-    int64_t st;
+    int64_t sb, st;
+    const int32_t* btab;
+    int bshift, maxb, seq;
     int ns, w0, nex;
 };
 
@@ -1076,7 +1089,7 @@ struct ScanRegs {
 };
 
 // DROP (no coarse remainder): coarse tiles only give scores, so their values are not read.
-template <bool DROP>
+template <bool DROP, bool PAGED>
 __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t, int ntc) {
     const int tid = threadIdx.x, c = tid & 15, g = tid >> 4;
     if (t < ntc) {
@@ -1095,7 +1108,7 @@ __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t,
         for (int i = 0; i < kSPieces; ++i) {
             const int x = x0 + min(4 * g + i, n - 1);
             const int pos = x < S.ns ? x : S.w0 + (x - S.ns);
-            const int64_t off = (int64_t)pos * S.st + 8 * c;
+            const int64_t off = kv_pos<PAGED>(S, S.seq, pos) + 8 * c;
             R.k[i] = *reinterpret_cast<const u32x4_t*>(S.kb + off);
             R.v[i] = *reinterpret_cast<const u32x4_t*>(S.vb + off);
         }
@@ -1172,7 +1185,7 @@ __device__ __forceinline__ void scan_pv(const MScanSmem<HG>& s, f32x4_t* o) {
 // Decode launch 1 (bf16): workgroup x of a (sequence, KV head) unit scans tiles
 // [x * nt / nslice, (x + 1) * nt / nslice) of the unit's tile list: MFMA scores (written
 // out for the selection on coarse tiles), online softmax and PV, then its partial state.
-template <int HG, bool DROP>
+template <int HG, bool DROP, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void decode_scan_mfma_kernel(DecodeArgs A) {
     __shared__ MScanSmem<HG> s;
@@ -1188,9 +1201,9 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     S.gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
     S.gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
     S.ng = nb * A.G;
-    S.kb = reinterpret_cast<const bf16_t*>(A.k) + seq * A.sb + kvh * A.sh;
-    S.vb = reinterpret_cast<const bf16_t*>(A.v) + seq * A.sb + kvh * A.sh;
-    S.st = A.st;
+    S.kb = reinterpret_cast<const bf16_t*>(A.k) + kvh * A.sh + kv_seq<PAGED>(A, seq);
+    S.vb = reinterpret_cast<const bf16_t*>(A.v) + kvh * A.sh + kv_seq<PAGED>(A, seq);
+    S.sb = A.sb; S.st = A.st; S.btab = A.btab; S.bshift = A.bshift; S.maxb = A.maxb; S.seq = seq;
     S.ns = min(A.n_sink, nb * kChunk);
     S.w0 = nb * kChunk;
     S.nex = S.ns + (p + 1 - S.w0);
@@ -1215,7 +1228,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     bf16x8_t qa[4];
     mfma_load_q<HG>(q0, qa);
     ScanRegs R;
-    if (t0 < t1) scan_fetch<DROP>(R, S, t0, ntc);
+    if (t0 < t1) scan_fetch<DROP, PAGED>(R, S, t0, ntc);
 
     for (int t = t0; t < t1; ++t) {
         const bool coarse = t < ntc;
@@ -1224,7 +1237,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
         scan_stage(s, R);  // the last tile's PV is done (barrier at the end of the loop)
         __syncthreads();
         scan_scores<HG>(s, qa);
-        if (t + 1 < t1) scan_fetch<DROP>(R, S, t + 1, ntc);  // in flight through this tile
+        if (t + 1 < t1) scan_fetch<DROP, PAGED>(R, S, t + 1, ntc);  // in flight through this tile
         __syncthreads();
         // coarse tiles: the scores go out for the selection, a 256-byte row per head
         // (rows past the tile's groups are never read; the rows stay inside score_stride)
@@ -1295,7 +1308,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
 // same logits, are subtracted in the final merge.  The subtracted mass never exceeds
 // the scan's, and the exact terms of the opened pages carry at least the same order of
 // mass, so fp32 cancellation stays near 1e-6 of the output scale.
-template <bool DROP>
+template <bool DROP, bool PAGED>
 __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b, int hq) {
     const int HG = A.Hq / A.Hkv;
     const int kvh = hq / HG;
@@ -1577,7 +1590,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
 
     Online st;
     st.init();
-    open_pages<bf16_t, 2 * kOpenBatch, false, DROP>(A, s, nsel, seq, kvh, head, q8, st);
+    open_pages<bf16_t, 2 * kOpenBatch, PAGED, false, DROP>(A, s, nsel, seq, kvh, head, q8, st);
     open_stash(s, st);
     if (part_in_lds) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1635,16 +1648,16 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
 // Decode launch 2 (bf16): one workgroup per (sequence, query head) runs the open step and
 // the final merge.  Consecutive workgroups take different KV heads, so the query heads
 // of one KV head share an XCD (workgroups are dealt to the 8 XCDs round robin).
-template <bool DROP>
+template <bool DROP, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A) {
     __shared__ OpenSmem<bf16_t> s;
     const int j = blockIdx.x;
-    decode_open_role<DROP>(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
+    decode_open_role<DROP, PAGED>(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
 }
 
 
 // Dense decode (bf16): split workgroups over rows, MFMA scores, online softmax.
-template <int HG>
+template <int HG, bool PAGED>
 __global__ __launch_bounds__(kThreads) void dense_decode_mfma_kernel(DenseArgs A) {
     __shared__ MSmem<HG> s;
     const int kvh = blockIdx.y, b = blockIdx.z;  // b: query row
@@ -1666,9 +1679,10 @@ __global__ __launch_bounds__(kThreads) void dense_decode_mfma_kernel(DenseArgs A
     const int r0 = blockIdx.x * A.rows_per_wg;
     const int r1 = min(r0 + A.rows_per_wg, p + 1);
     if (r1 > r0) {
-        const bf16_t* kb = reinterpret_cast<const bf16_t*>(A.k) + seq * A.sb + kvh * A.sh;
-        const bf16_t* vb = reinterpret_cast<const bf16_t*>(A.v) + seq * A.sb + kvh * A.sh;
-        mfma_exact_rows<HG>(s, qa, kb, vb, A.st, 0, r0, r1 - r0, A.scale, o);
+        const bf16_t* kh = reinterpret_cast<const bf16_t*>(A.k) + kvh * A.sh + kv_seq<PAGED>(A, seq);
+        const bf16_t* vh = reinterpret_cast<const bf16_t*>(A.v) + kvh * A.sh + kv_seq<PAGED>(A, seq);
+        mfma_exact_rows<HG>(s, qa, kh, vh, [&](int x) { return kv_pos<PAGED>(A, seq, x); }, 0, r0, r1 - r0,
+                            A.scale, o);
     }
     if (A.out) {
         mfma_write_partial<HG>(s, o, A.out + ((int64_t)b * A.Hq + hq0) * kD, kD, true);
@@ -1723,9 +1737,10 @@ __global__ __launch_bounds__(kThreads) void dense_decode_kernel(DenseArgs A) {
     const int r0 = blockIdx.x * A.rows_per_wg;
     const int r1 = min(r0 + A.rows_per_wg, p + 1);
     if (r1 > r0) {
-        const T* kb = reinterpret_cast<const T*>(A.k) + seq * A.sb + kvh * A.sh;
-        const T* vb = reinterpret_cast<const T*>(A.v) + seq * A.sb + kvh * A.sh;
-        exact_rows<T, HG>(s, R, qr, kb, vb, A.st, r0, r1, A.scale, m_run, l_run, o);
+        const T* kh = reinterpret_cast<const T*>(A.k) + kvh * A.sh;
+        const T* vh = reinterpret_cast<const T*>(A.v) + kvh * A.sh;
+        exact_rows<T, HG>(s, R, qr, [&](int x) { return kh + kv_row_rt(A, seq, x); },
+                          [&](int x) { return vh + kv_row_rt(A, seq, x); }, r0, r1, A.scale, m_run, l_run, o);
     }
     if (A.out) {  // one split per row: write the normalised output directly
         write_partial<HG>(s, R, o, m_run, l_run, A.out + ((int64_t)b * A.Hq + hq0) * kD, kD, true);
@@ -1737,51 +1752,57 @@ __global__ __launch_bounds__(kThreads) void dense_decode_kernel(DenseArgs A) {
 
 // ---------------------------------------------------------------------------- host side
 
-int check_kv_view(const lod_params* p, const lod_kv& kv) {
-    if (!kv.k || !kv.v || kv.stride_t <= 0 || kv.stride_h < 0 || kv.stride_b < 0) return LOD_ERR_ARG;
-    const int per16 = p->kv_dtype == LOD_BF16 ? 8 : 4;
-    if ((kv.stride_t | kv.stride_h | kv.stride_b) % per16 != 0) return LOD_ERR_ARG;
-    return LOD_OK;
-}
 
-template <typename T, int HG>
-static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
+template <typename T, int HG, bool PAGED>
+static void launch_decode_view(const DecodeArgs& A, int rows, hipStream_t st) {
     trace_point(0, st);
     if constexpr (sizeof(T) == 2) {
-        if (A.nslice + A.nwin > 0)
-        {
+        if (A.nslice + A.nwin > 0) {
             if (A.drop)
-                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, true>), dim3(A.nslice + A.nwin, A.Hkv, rows),
+                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, true, PAGED>), dim3(A.nslice + A.nwin, A.Hkv, rows),
                                    dim3(kThreads), 0, st, A);
             else
-                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, false>), dim3(A.nslice + A.nwin, A.Hkv, rows),
+                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, false, PAGED>), dim3(A.nslice + A.nwin, A.Hkv, rows),
                                    dim3(kThreads), 0, st, A);
         }
         trace_point(1, st);
         if (A.drop)
-            hipLaunchKernelGGL(decode_open_mfma_kernel<true>, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+            hipLaunchKernelGGL((decode_open_mfma_kernel<true, PAGED>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
         else
-            hipLaunchKernelGGL(decode_open_mfma_kernel<false>, dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+            hipLaunchKernelGGL((decode_open_mfma_kernel<false, PAGED>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
         trace_point(2, st);
     } else {
         if (A.nslice + A.nwin > 0)
             hipLaunchKernelGGL((decode_scan_kernel<T, HG>), dim3(A.nslice + A.nwin, A.Hkv, rows),
                                dim3(kThreads), 0, st, A);
         trace_point(1, st);
-        hipLaunchKernelGGL((decode_open_kernel<T>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+        hipLaunchKernelGGL((decode_open_kernel<T, PAGED>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
         trace_point(2, st);
     }
+}
+
+template <typename T, int HG>
+static int launch_decode(const DecodeArgs& A, int rows, hipStream_t st) {
+    if (A.btab)
+        launch_decode_view<T, HG, true>(A, rows, st);
+    else
+        launch_decode_view<T, HG, false>(A, rows, st);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
 
 template <typename T, int HG>
 static int launch_dense(const DenseArgs& A, float* out, int rows, hipStream_t st) {
-    if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((dense_decode_mfma_kernel<HG>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
-                           st, A);
-    else
+    if constexpr (sizeof(T) == 2) {
+        if (A.btab)
+            hipLaunchKernelGGL((dense_decode_mfma_kernel<HG, true>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
+                               st, A);
+        else
+            hipLaunchKernelGGL((dense_decode_mfma_kernel<HG, false>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
+                               st, A);
+    } else {
         hipLaunchKernelGGL((dense_decode_kernel<T, HG>), dim3(A.nsplit, A.Hkv, rows), dim3(kThreads), 0,
                            st, A);
+    }
     if (!A.out)
         hipLaunchKernelGGL(combine_kernel, dim3(A.Hq, rows), dim3(kD), 0, st, (const float*)A.part,
                            A.nsplit, out, A.Hq);
@@ -1828,7 +1849,8 @@ static int dispatch_dense(const lod_params* params, const DenseArgs& A, float* o
 static void fill_decode_args(DecodeArgs& A, const lod_params* params, const lod_index* index,
                              const lod_index_layout_t& L, const lod_kv& kv, const DecodePlan& P,
                              void* ws) {
-    A.k = kv.k; A.v = kv.v; A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    A.k = kv.k; A.v = kv.v;
+    set_kv_map(A, kv);
     A.index = reinterpret_cast<const char*>(index->mem);
     A.L = L;
     A.max_chunks = index->max_chunks;
@@ -1858,7 +1880,7 @@ extern "C" int lod_attend_decode(const lod_params* params, const lod_index* inde
     if (rc != LOD_OK) return rc;
     if (!index || !index->mem || !q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0)
         return LOD_ERR_ARG;
-    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
+    if ((rc = check_kv_view(params, kv, max_seq_len)) != LOD_OK) return rc;
     if (batch != index->batch) return LOD_ERR_ARG;
     if (built_chunks(params, (int64_t)max_seq_len - 1) > index->max_chunks) return LOD_ERR_ARG;
     const lod_index_layout_t L = make_layout(params, index->batch, index->max_chunks);
@@ -1919,11 +1941,12 @@ extern "C" int lod_dense_decode(const lod_params* params, lod_kv kv, const void*
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
-    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
+    if ((rc = check_kv_view(params, kv, max_seq_len)) != LOD_OK) return rc;
     const DensePlan P = plan_dense(params, batch, max_seq_len);
     if (!ws || ws_bytes < P.bytes) return LOD_ERR_WORKSPACE;
     DenseArgs A;
-    A.k = kv.k; A.v = kv.v; A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    A.k = kv.k; A.v = kv.v;
+    set_kv_map(A, kv);
     A.q = q; A.seq_lens = seq_lens; A.max_seq_len = max_seq_len;
     A.part = reinterpret_cast<float*>(ws);
     A.out = nullptr;
@@ -1939,7 +1962,8 @@ int lodi::dense_prefill_valu(const lod_params* params, lod_kv kv, const void* q,
     int rc = LOD_OK;
     const int64_t end = (int64_t)q_start + n_q;
     DenseArgs A;
-    A.k = kv.k; A.v = kv.v; A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    A.k = kv.k; A.v = kv.v;
+    set_kv_map(A, kv);
     A.seq_lens = nullptr; A.max_seq_len = (int32_t)end;
     A.part = nullptr;
     A.Hq = params->n_q_heads; A.Hkv = params->n_kv_heads;

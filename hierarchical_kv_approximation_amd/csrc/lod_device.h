@@ -146,6 +146,35 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
     return v + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
 }
 
+// Element offset of KV row (sequence b, position t) for head 0, for any argument block
+// with fields sb, st (strides), btab (block table or null), bshift (log2 block size) and
+// maxb (block-table row length), split as kv_seq(b) + kv_pos(b, t).  PAGED: position t
+// sits in block btab[b][t >> bshift] at row t & (block size - 1), and kv_seq is 0;
+// strided: sequence b starts at b * sb (kv_seq, loop invariant) and t adds t * st.
+template <bool PAGED, typename Args>
+__device__ __forceinline__ int64_t kv_seq(const Args& A, int b) {
+    if constexpr (PAGED) return 0;
+    else return (int64_t)b * A.sb;
+}
+template <bool PAGED, typename Args>
+__device__ __forceinline__ int64_t kv_pos(const Args& A, int b, int t) {
+    if constexpr (PAGED) {
+        const int64_t blk = A.btab[(int64_t)b * A.maxb + (t >> A.bshift)];
+        return blk * A.sb + (int64_t)(t & ((1 << A.bshift) - 1)) * A.st;
+    } else {
+        return (int64_t)t * A.st;
+    }
+}
+template <bool PAGED, typename Args>
+__device__ __forceinline__ int64_t kv_row(const Args& A, int b, int t) {
+    return kv_seq<PAGED>(A, b) + kv_pos<PAGED>(A, b, t);
+}
+// The same with the view chosen at run time (kernels off the hot path).
+template <typename Args>
+__device__ __forceinline__ int64_t kv_row_rt(const Args& A, int b, int t) {
+    return A.btab ? kv_row<true>(A, b, t) : kv_row<false>(A, b, t);
+}
+
 // Workgroup barrier over LDS traffic only: each wave waits for its own LDS operations
 // (lgkmcnt 0), not for its vector memory operations, so loads of a later tile (also
 // global -> LDS loads, whose completion the caller awaits with an explicit vmcnt wait

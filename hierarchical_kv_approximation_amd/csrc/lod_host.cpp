@@ -27,6 +27,18 @@ int check_params(const lod_params* p) {
     return LOD_OK;
 }
 
+int check_kv_view(const lod_params* p, const lod_kv& kv, int64_t positions) {
+    if (!kv.k || !kv.v || kv.stride_t <= 0 || kv.stride_h < 0 || kv.stride_b < 0) return LOD_ERR_ARG;
+    const int per16 = p->kv_dtype == LOD_BF16 ? 8 : 4;
+    if ((kv.stride_t | kv.stride_h | kv.stride_b) % per16 != 0) return LOD_ERR_ARG;
+    if (kv.block_table) {
+        const int32_t bs = kv.block_size;
+        if (bs < 1 || bs > 65536 || (bs & (bs - 1)) != 0) return LOD_ERR_ARG;
+        if (kv.max_blocks <= 0 || (int64_t)kv.max_blocks * bs < positions) return LOD_ERR_ARG;
+    }
+    return LOD_OK;
+}
+
 lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_chunks) {
     lod_index_layout_t L{};
     const size_t U = (size_t)batch * p->n_kv_heads;

@@ -61,8 +61,22 @@ struct DensePlan {
 };
 DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len);
 
-// Checks of a KV view shared by the entry points (host).
-int check_kv_view(const lod_params* p, const lod_kv& kv);
+// Checks of a KV view shared by the entry points (host): strides, alignment, and for a
+// paged view the block size and that the table rows cover `positions` positions.
+int check_kv_view(const lod_params* p, const lod_kv& kv, int64_t positions);
+inline int log2_exact(int32_t x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+// Copy a KV view into a kernel argument block (fields sb, st, sh, btab, bshift, maxb).
+template <typename Args>
+inline void set_kv_map(Args& A, const lod_kv& kv) {
+    A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    A.btab = kv.block_table;
+    A.bshift = kv.block_table ? log2_exact(kv.block_size) : 0;
+    A.maxb = kv.block_table ? kv.max_blocks : 0;
+}
 // LoD prefill row by row through the decode kernels (fp32 caches).
 int prefill_rows_ws_bytes(const lod_params* params, int32_t n_q, int32_t max_tokens, size_t* bytes);
 int prefill_rows(const lod_params* params, const lod_index* index, lod_kv kv, const void* q,

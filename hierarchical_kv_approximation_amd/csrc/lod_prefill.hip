@@ -37,6 +37,8 @@ struct FlashArgs {
     const bf16_t* k;
     const bf16_t* v;
     int64_t sb, st, sh;
+    const int32_t* btab;  // paged view: block table [batch][maxb], else null
+    int bshift, maxb;
     const bf16_t* q;  // rows of this launch: [B][nq][Hq][d]
     int seq;          // sequence of grid slice z = 0 (index and cache)
     int nq;           // rows per sequence in this launch
@@ -190,7 +192,7 @@ __device__ __forceinline__ void flash_tile(FlashSmem<HG>& s, FlashState<HG>& F, 
 
 // Workgroup: 128 (row, head) columns = (128 / HG) query rows x HG heads of one KV head.
 // Column n = row * HG + head; wave w owns column blocks 2w and 2w+1.
-template <int HG>
+template <int HG, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_flash_kernel(FlashArgs A) {
     __shared__ FlashSmem<HG> s;
@@ -227,8 +229,9 @@ void prefill_flash_kernel(FlashArgs A) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) F.O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
     }
-    const bf16_t* kc = A.k + bs * A.sb + kvh * A.sh;
-    const bf16_t* vc = A.v + bs * A.sb + kvh * A.sh;
+    // head kvh of sequence bs; the row of position x adds kv_pos(A, bs, x)
+    const bf16_t* kc = A.k + kvh * A.sh + kv_seq<PAGED>(A, bs);
+    const bf16_t* vc = A.v + kvh * A.sh + kv_seq<PAGED>(A, bs);
     uint64_t noex[2] = {0, 0};
 
     if (A.index == nullptr) {
@@ -236,8 +239,8 @@ void prefill_flash_kernel(FlashArgs A) {
         for (int k0 = 0; k0 <= p_last; k0 += kFlashKeys) {
             const int nk = min(kFlashKeys, p_last + 1 - k0);
             flash_tile<HG>(
-                s, F, qb, nk, [&](int r) { return kc + (int64_t)(k0 + r) * A.st; },
-                [&](int r) { return vc + (int64_t)(k0 + r) * A.st; }, [&](int) { return 0.0f; },
+                s, F, qb, nk, [&](int r) { return kc + kv_pos<PAGED>(A, bs, k0 + r); },
+                [&](int r) { return vc + kv_pos<PAGED>(A, bs, k0 + r); }, [&](int) { return 0.0f; },
                 [&](int r) { return k0 + r; }, prow, noex, A.scale);
         }
     } else {
@@ -270,9 +273,9 @@ void prefill_flash_kernel(FlashArgs A) {
             const bool coarse = t < ct, sink = !coarse && t < ct + st;
             const int k0 = coarse ? t * kFlashKeys : (sink ? (t - ct) * kFlashKeys : w0 + (t - ct - st) * kFlashKeys);
             const int nk = coarse ? min(kFlashKeys, ng - k0) : (sink ? min(kFlashKeys, ns - k0) : min(kFlashKeys, p_last + 1 - k0));
-            const bf16_t* kt = coarse ? gk + (int64_t)k0 * kD : kc + (int64_t)k0 * A.st;
-            const bf16_t* vt = coarse ? gv + (int64_t)k0 * kD : vc + (int64_t)k0 * A.st;
-            const int64_t rs = coarse ? kD : A.st;
+            const bf16_t* kt = coarse ? gk + (int64_t)k0 * kD : kc;  // coarse: index rows; else cache rows
+            const bf16_t* vt = coarse ? gv + (int64_t)k0 * kD : vc;
+            auto roff = [&](int r) { return coarse ? (int64_t)r * kD : kv_pos<PAGED>(A, bs, k0 + r); };
             uint64_t ex[2] = {0, 0};
             if (coarse) {
 #pragma unroll
@@ -287,7 +290,7 @@ void prefill_flash_kernel(FlashArgs A) {
                 }
             }
             flash_tile<HG>(
-                s, F, qb, nk, [&](int r) { return kt + (int64_t)r * rs; }, [&](int r) { return vt + (int64_t)r * rs; },
+                s, F, qb, nk, [&](int r) { return kt + roff(r); }, [&](int r) { return vt + roff(r); },
                 [&](int r) { return coarse ? gln[k0 + r] : 0.0f; }, [&](int r) { return coarse ? INT_MIN : k0 + r; },
                 prow, ex, A.scale);
         }
@@ -992,6 +995,8 @@ struct PagesArgs {
     const bf16_t* k;
     const bf16_t* v;
     int64_t sb, st, sh;
+    const int32_t* btab;  // paged view: block table [batch][maxb], else null
+    int bshift, maxb;
     const bf16_t* q;
     int seq;                // sequence of grid slice z = 0 (index and cache)
     int nq, pos0, Hq, Hkv;
@@ -1089,7 +1094,7 @@ constexpr int kPagesMeta = 320;  // int16 entries of a chunk's meta row held in 
 // A pair's loads form three dependent steps: its list entry (pair and group); the query,
 // its record and the whole meta row of the group's chunk (to LDS); then the rows of the
 // opened pages (batches of 8, kept packed) with the unopened pages' means.
-template <int HG>
+template <int HG, bool PAGED>
 __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     __shared__ alignas(16) int16_t mrow[kPairsPerWG][kPagesMeta];
     const int blk = blockIdx.x, unit_local = blockIdx.y;
@@ -1107,8 +1112,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + ubase * A.L.meta_stride;
     const bf16_t* pv_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pv) + ubase * PS * kD;
     const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + ubase * PS;
-    const bf16_t* kc = A.k + bs * A.sb + kvh * A.sh;
-    const bf16_t* vc = A.v + bs * A.sb + kvh * A.sh;
+    // head kvh of sequence bs; the row of position x adds kv_pos(A, bs, x)
+    const bf16_t* kc = A.k + kvh * A.sh + kv_seq<PAGED>(A, bs);
+    const bf16_t* vc = A.v + kvh * A.sh + kv_seq<PAGED>(A, bs);
 
     const int x = blk * kPairsPerWG + sg;
     if (x >= npairs) return;  // uniform in the subgroup
@@ -1169,8 +1175,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
         for (int u = 0; u < RB; ++u) {
             const int pu = __shfl(pos, seg0 + u, 64);
             if (u0 + u < nrow) {
-                kp[u] = *reinterpret_cast<const uint4*>(kc + (int64_t)pu * A.st + 8 * l16);
-                vp[u] = *reinterpret_cast<const uint4*>(vc + (int64_t)pu * A.st + 8 * l16);
+                const int64_t ro = kv_pos<PAGED>(A, bs, pu);
+                kp[u] = *reinterpret_cast<const uint4*>(kc + ro + 8 * l16);
+                vp[u] = *reinterpret_cast<const uint4*>(vc + ro + 8 * l16);
             }
         }
         // block update: dot products and their reductions side by side, one rescale
@@ -1319,13 +1326,21 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     trace_point(1, st);
     hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
     trace_point(2, st);
-    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0, st, F);
+    if (F.btab)
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
+                           st, F);
+    else
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
+                           st, F);
     trace_point(3, st);
     hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
     trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
-    hipLaunchKernelGGL((prefill_pages_kernel<HG>), dim3((maxpairs + kPairsPerWG - 1) / kPairsPerWG,
-                       nunits_q * S.Hkv * batch), dim3(kThreads), 0, st, P);
+    const dim3 pgrid((maxpairs + kPairsPerWG - 1) / kPairsPerWG, nunits_q * S.Hkv * batch);
+    if (P.btab)
+        hipLaunchKernelGGL((prefill_pages_kernel<HG, true>), pgrid, dim3(kThreads), 0, st, P);
+    else
+        hipLaunchKernelGGL((prefill_pages_kernel<HG, false>), pgrid, dim3(kThreads), 0, st, P);
     trace_point(5, st);
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + 1) / 2)), dim3(kThreads), 0, st, P, nrh);
@@ -1339,8 +1354,12 @@ namespace lodi {
 template <int HG>
 static void launch_flash(const FlashArgs& A, int batch, hipStream_t st) {
     constexpr int QT = kFlashRowHeads / HG;
-    hipLaunchKernelGGL((prefill_flash_kernel<HG>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kThreads),
-                       0, st, A);
+    if (A.btab)
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kThreads),
+                           0, st, A);
+    else
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kThreads),
+                           0, st, A);
 }
 
 static int dispatch_flash(const FlashArgs& A, int batch, hipStream_t st) {
@@ -1362,14 +1381,14 @@ extern "C" int lod_dense_prefill(const lod_params* params, lod_kv kv, const void
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
-    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
+    if ((rc = check_kv_view(params, kv, (int64_t)q_start + n_q)) != LOD_OK) return rc;
     if ((int64_t)q_start + n_q > INT32_MAX) return LOD_ERR_ARG;
     if (params->kv_dtype != LOD_BF16)
         return dense_prefill_valu(params, kv, q, q_start, n_q, batch, out, stream);
     FlashArgs A{};
     A.k = reinterpret_cast<const bf16_t*>(kv.k);
     A.v = reinterpret_cast<const bf16_t*>(kv.v);
-    A.sb = kv.stride_b; A.st = kv.stride_t; A.sh = kv.stride_h;
+    set_kv_map(A, kv);
     A.q = reinterpret_cast<const bf16_t*>(q);
     A.nq = n_q; A.pos0 = q_start;
     A.Hq = params->n_q_heads; A.Hkv = params->n_kv_heads; A.scale = params->scale;
@@ -1396,7 +1415,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
     if (rc != LOD_OK) return rc;
     if (!index || !index->mem || !q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
     if (q_start % params->chunk_size != 0) return LOD_ERR_ARG;
-    if ((rc = check_kv_view(params, kv)) != LOD_OK) return rc;
+    if ((rc = check_kv_view(params, kv, (int64_t)q_start + n_q)) != LOD_OK) return rc;
     if (batch != index->batch) return LOD_ERR_ARG;
     const int64_t end = (int64_t)q_start + n_q;
     if (end > INT32_MAX || built_chunks(params, end - 1) > index->max_chunks) return LOD_ERR_ARG;
@@ -1438,7 +1457,8 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             FlashArgs F{};
             F.k = reinterpret_cast<const bf16_t*>(kv.k);
             F.v = reinterpret_cast<const bf16_t*>(kv.v);
-            F.seq = b; F.sb = kv.stride_b; F.st = kv.stride_t; F.sh = kv.stride_h;
+            F.seq = b;
+            set_kv_map(F, kv);
             F.q = S.q; F.nq = rows; F.pos0 = S.pos0; F.Hq = Hq; F.Hkv = Hkv; F.scale = params->scale;
             F.index = S.index; F.L = L; F.max_chunks = S.max_chunks; F.G = S.G; F.W = S.W;
             F.n_sink = params->n_sink; F.TG = TG; F.selg = S.selg; F.drop = params->drop_remainder;
@@ -1446,7 +1466,8 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             F.nsplit = P.nsplit;
             F.split_stride = (int64_t)P.rows * Hq * kPartStride;
             PagesArgs G{};
-            G.k = F.k; G.v = F.v; G.seq = b; G.sb = F.sb; G.st = F.st; G.sh = F.sh;
+            G.k = F.k; G.v = F.v; G.seq = b;
+            set_kv_map(G, kv);
             G.q = S.q; G.nq = rows; G.pos0 = S.pos0; G.Hq = Hq; G.Hkv = Hkv; G.scale = params->scale;
             G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
             G.drop = params->drop_remainder;

@@ -32,7 +32,9 @@ class Params(ctypes.Structure):
 
 class KV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
-                ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+                ("stride_t", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32)]
 
 
 class Index(ctypes.Structure):
@@ -137,11 +139,21 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def kv_view(K: torch.Tensor, V: torch.Tensor) -> KV:
-    """[B][T][Hkv][d] (any strides, last dim contiguous) -> the library's KV view."""
+def kv_view(K: torch.Tensor, V: torch.Tensor, block_table: torch.Tensor | None = None) -> KV:
+    """The library's KV view.  Strided: K, V are [B][T][Hkv][d] (any strides, last dim
+    contiguous).  Paged: K, V are [num_blocks][block_size][Hkv][d] caches and block_table
+    [B][max_blocks] (device int32) names the block of every block_size positions."""
     assert K.shape == V.shape and K.stride() == V.stride() and K.dtype == V.dtype
     assert K.stride(3) == 1
-    return KV(K.data_ptr(), V.data_ptr(), K.stride(0), K.stride(1), K.stride(2))
+    if block_table is None:
+        return KV(K.data_ptr(), V.data_ptr(), K.stride(0), K.stride(1), K.stride(2), None, 0, 0)
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.dim() == 2
+    return KV(K.data_ptr(), V.data_ptr(), K.stride(0), K.stride(1), K.stride(2), block_table.data_ptr(),
+              K.shape[1], block_table.shape[1])
+
+
+def _batch(K, block_table):
+    return K.shape[0] if block_table is None else block_table.shape[0]
 
 
 @dataclass
@@ -197,9 +209,10 @@ class LodIndex:
 
 
 def build_chunk(cfg: Config, index: LodIndex, K, V, chunk_begin: int, n_chunks: int,
-                assign_in: torch.Tensor | None = None, want_assign: bool = False):
+                assign_in: torch.Tensor | None = None, want_assign: bool = False,
+                block_table: torch.Tensor | None = None):
     """lod_build_chunk over chunks [chunk_begin, chunk_begin + n_chunks) of every sequence."""
-    B = K.shape[0]
+    B = _batch(K, block_table)
     aout = None
     if want_assign:
         aout = torch.empty(B, cfg.n_kv_heads, n_chunks, cfg.chunk_size, dtype=torch.int32, device=K.device)
@@ -207,7 +220,7 @@ def build_chunk(cfg: Config, index: LodIndex, K, V, chunk_begin: int, n_chunks: 
         assign_in = assign_in.to(device=K.device, dtype=torch.int32).contiguous()
     idx = index.c()
     _check("lod_build_chunk", lib().lod_build_chunk(ctypes.byref(cfg.params()), ctypes.byref(idx),
-                                                    kv_view(K, V), B, chunk_begin, n_chunks,
+                                                    kv_view(K, V, block_table), B, chunk_begin, n_chunks,
                                                     _ptr(assign_in), _ptr(aout), _stream()))
     return aout
 
@@ -221,7 +234,7 @@ def decode_ws_bytes(cfg: Config, batch: int, max_seq_len: int) -> int:
 
 def attend_decode(cfg: Config, index: LodIndex, K, V, q, seq_lens: torch.Tensor, max_seq_len: int,
                   want_selection: bool = False, ws: torch.Tensor | None = None,
-                  out: torch.Tensor | None = None):
+                  out: torch.Tensor | None = None, block_table: torch.Tensor | None = None):
     """lod_attend_decode; q [B][Hq][d]; seq_lens device int32 [B].  Returns out (fp32) or
     (out, sel_groups, sel_pages)."""
     B = q.shape[0]
@@ -237,7 +250,7 @@ def attend_decode(cfg: Config, index: LodIndex, K, V, q, seq_lens: torch.Tensor,
         ws = torch.empty(decode_ws_bytes(cfg, B, max_seq_len), dtype=torch.uint8, device=dev)
     idx = index.c()
     _check("lod_attend_decode", lib().lod_attend_decode(
-        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V), _ptr(q), _ptr(seq_lens), B,
+        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V, block_table), _ptr(q), _ptr(seq_lens), B,
         max_seq_len, _ptr(out), _ptr(sg), _ptr(sp), _ptr(ws), ws.numel(), _stream()))
     return (out, sg, sp) if want_selection else out
 
@@ -250,7 +263,8 @@ def prefill_ws_bytes(cfg: Config, batch: int, n_q: int, max_tokens: int) -> int:
 
 
 def attend_prefill(cfg: Config, index: LodIndex, K, V, q, q_start: int, want_selection: bool = False,
-                   ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
+                   ws: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   block_table: torch.Tensor | None = None):
     """lod_attend_prefill; q [B][n_q][Hq][d] holds rows q_start .. q_start+n_q-1."""
     B, nq = q.shape[0], q.shape[1]
     dev = q.device
@@ -265,7 +279,7 @@ def attend_prefill(cfg: Config, index: LodIndex, K, V, q, q_start: int, want_sel
         ws = torch.empty(max(1, prefill_ws_bytes(cfg, B, nq, q_start + nq)), dtype=torch.uint8, device=dev)
     idx = index.c()
     _check("lod_attend_prefill", lib().lod_attend_prefill(
-        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V), _ptr(q), q_start, nq, B,
+        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V, block_table), _ptr(q), q_start, nq, B,
         _ptr(out), _ptr(sg), _ptr(sp), _ptr(ws), ws.numel(), _stream()))
     return (out, sg, sp) if want_selection else out
 
@@ -278,24 +292,26 @@ def dense_decode_ws_bytes(cfg: Config, batch: int, max_seq_len: int) -> int:
 
 
 def dense_decode(cfg: Config, K, V, q, seq_lens: torch.Tensor, max_seq_len: int,
-                 ws: torch.Tensor | None = None, out: torch.Tensor | None = None):
+                 ws: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 block_table: torch.Tensor | None = None):
     B = q.shape[0]
     if out is None:
         out = torch.empty(B, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
     if ws is None:
         ws = torch.empty(dense_decode_ws_bytes(cfg, B, max_seq_len), dtype=torch.uint8, device=q.device)
     _check("lod_dense_decode", lib().lod_dense_decode(
-        ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), _ptr(seq_lens), B, max_seq_len,
+        ctypes.byref(cfg.params()), kv_view(K, V, block_table), _ptr(q), _ptr(seq_lens), B, max_seq_len,
         _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 
 
-def dense_prefill(cfg: Config, K, V, q, q_start: int, out: torch.Tensor | None = None):
+def dense_prefill(cfg: Config, K, V, q, q_start: int, out: torch.Tensor | None = None,
+                  block_table: torch.Tensor | None = None):
     B, nq = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty(B, nq, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
     _check("lod_dense_prefill", lib().lod_dense_prefill(
-        ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), q_start, nq, B, _ptr(out), _stream()))
+        ctypes.byref(cfg.params()), kv_view(K, V, block_table), _ptr(q), q_start, nq, B, _ptr(out), _stream()))
     return out
 
 

@@ -28,7 +28,8 @@
  *   - Calls are reentrant.  Calls that share output, index or workspace buffers must
  *     be ordered by the caller (same stream or events).
  *   - KV cache: element (b, t, h, i) of K is at k[b*stride_b + t*stride_t + h*stride_h + i]
- *     (strides in elements, last dimension contiguous, 16-byte aligned rows).
+ *     (strides in elements, last dimension contiguous, 16-byte aligned rows), or found
+ *     through a block table (lod_kv below).
  *     Queries have the cache's element type; outputs are fp32.
  */
 #ifndef LOD_H
@@ -85,11 +86,28 @@ typedef struct {
                                  ablation: the same selection, exact keys only */
 } lod_params;
 
-/* Strided view of the caller's KV cache (see the conventions above). */
+/*
+ * View of the caller's KV cache.
+ *   Strided (block_table == NULL): element (b, t, h, i) of K is at
+ *     k[b*stride_b + t*stride_t + h*stride_h + i].
+ *   Paged (block_table != NULL), the block-table layout of a vLLM-style serving engine:
+ *     position t of sequence b lives in cache block blk = block_table[b*max_blocks +
+ *     t/block_size], and element (b, t, h, i) of K is at
+ *     k[blk*stride_b + (t % block_size)*stride_t + h*stride_h + i]
+ *     (stride_b is then the stride between blocks).  block_size is a power of two in
+ *     [1, 65536]; max_blocks must cover every position a call reads (checked on the
+ *     host); the block ids themselves are device data and are not checked: each must
+ *     name a block inside the caller's K and V buffers.
+ * The paged view is a boundary change only: every call computes the same results as
+ * with a strided copy of the same cache.
+ */
 typedef struct {
     const void* k;
     const void* v;
     int64_t stride_b, stride_t, stride_h;
+    const int32_t* block_table; /* DEVICE [batch][max_blocks] int32, or NULL (strided) */
+    int32_t block_size;         /* positions per cache block (paged view) */
+    int32_t max_blocks;         /* row length of block_table (paged view) */
 } lod_kv;
 
 /* The multi-resolution view: one caller-allocated device buffer of `bytes` bytes,

@@ -125,6 +125,32 @@ def test_bad_buffers_rejected():
     assert L.lod_dense_decode(_p(cfg), kv, FAKE, FAKE, 1, 8192, FAKE, FAKE, 8, None) == lod.LOD_ERR_WORKSPACE
 
 
+def test_paged_view_checks():
+    """A block-table view needs a power-of-two block size and table rows that cover every
+    position the call reads; anything else is rejected before launch."""
+    cfg = lod.Config(n_q_heads=8, n_kv_heads=1)
+    L = lod.lib()
+    n = ctypes.c_size_t()
+    assert L.lod_index_bytes(_p(cfg), 1, 8192, ctypes.byref(n)) == 0
+    idx = lod.Index(FAKE.value, n.value, 1, 32)
+    E = lod.LOD_ERR_ARG
+
+    def paged(bs, maxb):
+        return lod.KV(FAKE.value, FAKE.value, bs * 1024, 1024, 128, FAKE.value, bs, maxb)
+
+    for bad in (paged(24, 4096), paged(0, 4096), paged(1 << 17, 1)):
+        assert L.lod_build_chunk(_p(cfg), ctypes.byref(idx), bad, 1, 0, 1, None, None, None) == E
+    # chunks 0..3 read 1024 positions: 63 blocks of 16 are too few
+    assert L.lod_build_chunk(_p(cfg), ctypes.byref(idx), paged(16, 63), 1, 0, 4, None, None, None) == E
+    # decode reads positions up to max_seq_len - 1, prefill up to q_start + n_q - 1
+    assert L.lod_attend_decode(_p(cfg), ctypes.byref(idx), paged(16, 511), FAKE, FAKE, 1, 8192, FAKE,
+                               None, None, FAKE, 1 << 40, None) == E
+    assert L.lod_attend_prefill(_p(cfg), ctypes.byref(idx), paged(32, 39), FAKE, 1024, 256, 1, FAKE, None,
+                                None, FAKE, 1 << 40, None) == E
+    assert L.lod_dense_decode(_p(cfg), paged(16, 100), FAKE, FAKE, 1, 8192, FAKE, FAKE, 1 << 40, None) == E
+    assert L.lod_dense_prefill(_p(cfg), paged(64, 3), FAKE, 0, 256, 1, FAKE, None) == E
+
+
 def test_product_path_refuses_to_run_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lod, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(lod, "_lib", None)
