@@ -155,6 +155,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--prefill-ctx", type=int, default=131072)
     ap.add_argument("--no-sweep", action="store_true", help="skip the sigma sweep of the approximation error")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV-view decode timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -209,9 +210,8 @@ def main():
         lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[0], max_len, ws=ws, out=out)
     torch.cuda.synchronize()
 
-    # timed region
-    NE = 3  # trace events per call: before the scan, after the scan, after the open step
-    ev = hip.create(NE * K)
+    # timed region: the decode calls back to back, with the chunk builds the boundary
+    # needs; nothing else is recorded on the stream (events only around the builds)
     bev = hip.create(2 * L)
     t0, t1 = hip.create(2)
     nbuilt = 0
@@ -225,20 +225,30 @@ def main():
             hip.record(bev[2 * nbuilt + 1], stream)
             Ly["built"] = True
             nbuilt += 1
-        keep = lod.trace_events(ev[NE * k: NE * k + NE])
         lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[pi], max_len, ws=ws, out=out)
-        lod.trace_events(None)
-        del keep
     hip.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = hip.ms(t0, t1)
+    build_ms = [hip.ms(bev[2 * i], bev[2 * i + 1]) for i in range(nbuilt)]
+    hip.destroy(bev + [t0, t1])
+    ms_per_step = total_ms / K
+    log(f"timed {K} steps: {ms_per_step * 1000:.1f} us/step")
+
+    # the same calls again with the library's trace events (before the scan, after the
+    # scan, after the open step) for the per-kernel times; events add a little time
+    NE = 3
+    ev = hip.create(NE * K)
+    for k in range(K):
+        Ly = layers[k % L]
+        keep = lod.trace_events(ev[NE * k: NE * k + NE])
+        lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[k // L], max_len, ws=ws, out=out)
+        lod.trace_events(None)
+        del keep
+    torch.cuda.synchronize()
     scan_ms = [hip.ms(ev[NE * k], ev[NE * k + 1]) for k in range(K)]
     open_ms = [hip.ms(ev[NE * k + 1], ev[NE * k + 2]) for k in range(K)]
     call_ms = [hip.ms(ev[NE * k], ev[NE * k + 2]) for k in range(K)]
-    build_ms = [hip.ms(bev[2 * i], bev[2 * i + 1]) for i in range(nbuilt)]
-    hip.destroy(ev + bev + [t0, t1])
-    ms_per_step = total_ms / K
-    log(f"timed {K} steps: {ms_per_step * 1000:.1f} us/step")
+    hip.destroy(ev)
 
     # algorithmic bytes at the last timed position (selection from one extra call)
     Ly = layers[(K - 1) % L]
@@ -280,27 +290,63 @@ def main():
                  "achieved_GBs": round(dense_bytes / dms / 1e6, 1),
                  "lod_speedup_vs_dense": round(dms / ms_per_step, 2)}
 
+    # reference for the variants below: the same LoD calls back to back, no trace events,
+    # no builds (every layer is already built past the boundary)
+    def time_calls(c, paged_view=False):
+        for k in range(min(W, 4)):
+            Ly = layers[k % L]
+            lod.attend_decode(c, Ly["index"], Ly["Kp" if paged_view else "K"], Ly["Vp" if paged_view else "V"],
+                              Ly["q"], seq[npos - 1], max_len, ws=ws, out=out,
+                              block_table=Ly["table"] if paged_view else None)
+        torch.cuda.synchronize()
+        a0, a1 = hip.create(2)
+        hip.record(a0, stream)
+        for k in range(K):
+            Ly = layers[k % L]
+            lod.attend_decode(c, Ly["index"], Ly["Kp" if paged_view else "K"], Ly["Vp" if paged_view else "V"],
+                              Ly["q"], seq[k // L], max_len, ws=ws, out=out,
+                              block_table=Ly["table"] if paged_view else None)
+        hip.record(a1, stream)
+        torch.cuda.synchronize()
+        r = hip.ms(a0, a1) / K
+        hip.destroy([a0, a1])
+        return r
+    ref_ms = time_calls(cfg)
+
     # sparsity ablation on the same inputs: the same selection, the coarse remainder
     # dropped (the scan reads the mean keys for the scores but no mean values)
     import dataclasses
     scfg = dataclasses.replace(cfg, drop_remainder=True)
-    for k in range(min(W, 4)):
-        Ly = layers[k % L]
-        lod.attend_decode(scfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[npos - 1], max_len, ws=ws, out=out)
-    torch.cuda.synchronize()
-    s0e, s1e = hip.create(2)
-    hip.record(s0e, stream)
-    for k in range(K):
-        Ly = layers[k % L]
-        lod.attend_decode(scfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[k // L], max_len, ws=ws, out=out)
-    hip.record(s1e, stream)
-    torch.cuda.synchronize()
-    sms = hip.ms(s0e, s1e) / K
-    hip.destroy([s0e, s1e])
+    sms = time_calls(scfg)
     sparse = {"what": "same selection, coarse remainder dropped (exact keys only)",
               "ms_per_call": round(sms, 5), "tok_per_s": round(B * 1000.0 / sms, 1),
-              "time_vs_lod": round(sms / ms_per_step, 3)}
+              "time_vs_lod": round(sms / ref_ms, 3), "lod_reference_ms_per_call": round(ref_ms, 5)}
     log(f"sparsity ablation: {sms * 1000:.1f} us/call")
+
+    # paged KV view: each layer's cache scattered over a pool of 16-position blocks in a
+    # seeded random order (a serving engine's block table); same index, same positions
+    paged = None
+    if not args.no_paged:
+        import numpy as np
+        bsz = 16
+        nbl = cap // bsz
+        for li, Ly in enumerate(layers):
+            perm = np.random.default_rng(args.seed + 31 * li).permutation(B * nbl).astype(np.int32)
+            table = torch.from_numpy(perm).view(B, nbl).to(dev)
+            pool_shape = (B * nbl, bsz) + tuple(Ly["K"].shape[2:])
+            Ly["Kp"] = torch.empty(pool_shape, dtype=Ly["K"].dtype, device=dev)
+            Ly["Vp"] = torch.empty_like(Ly["Kp"])
+            Ly["Kp"][table.view(-1).long()] = Ly["K"].reshape(pool_shape)
+            Ly["Vp"][table.view(-1).long()] = Ly["V"].reshape(pool_shape)
+            Ly["table"] = table
+        pms = time_calls(cfg, paged_view=True)
+        for Ly in layers:
+            del Ly["Kp"], Ly["Vp"], Ly["table"]
+        paged = {"what": "the same decode calls with each cache in a pool of 16-position blocks "
+                         "(random block order, block table)",
+                 "ms_per_call": round(pms, 5), "tok_per_s": round(B * 1000.0 / pms, 1),
+                 "time_vs_strided": round(pms / ref_ms, 3), "strided_reference_ms_per_call": round(ref_ms, 5)}
+        log(f"paged KV view: {pms * 1000:.1f} us/call")
 
     # CPU oracle on a bounded sample: sequence 0 of layer 0, all 64 heads, one token
     cpu = None
@@ -357,16 +403,18 @@ def main():
         },
         "cpu_baseline": cpu,
         "extra": {
-            "lod_call_us": round(call_avg * 1000, 2),
+            "step_us": round(ms_per_step * 1000, 2),
+            "lod_call_us_with_trace_events": round(call_avg * 1000, 2),
             "scan_us": round(scan_avg * 1000, 2),
             "open_us": round(open_avg * 1000, 2),
             "open_algorithmic_bytes": bytes_open,
             "build_one_chunk_batch_us": [round(x * 1000, 1) for x in build_ms],
             "algorithmic_bytes_per_call": bytes_call,
-            "call_achieved_GBs": round(bytes_call / (call_avg * 1e-3) / 1e9, 1),
-            "call_frac_hbm": round(bytes_call / (call_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "call_achieved_GBs": round(bytes_call / (ms_per_step * 1e-3) / 1e9, 1),
+            "call_frac_hbm": round(bytes_call / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "dense_decode": dense,
             "sparsity_ablation": sparse,
+            "paged_kv_view": paged,
             "setup_s": round(setup_s, 1),
         },
         "prefill": prefill,
