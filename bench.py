@@ -75,9 +75,12 @@ def profiled_traffic(name):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != rec["source_sha256_16"]:
-            return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:  # the kernel's file and every header it includes
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec["sources_sha256_16"]:
+        return None
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
@@ -486,17 +489,22 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
 
     run()  # warm-up pass (builds every chunk once; the timed pass rebuilds them)
     torch.cuda.synchronize()
-    ev = hip.create(NE * nq)
     t0, t1 = hip.create(2)
     hip.record(t0, stream)
-    run(ev)
+    run()
     hip.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = hip.ms(t0, t1)
+    hip.destroy([t0, t1])
+    # the same pass with the library's trace events around every kernel, for the stage
+    # times (the events add a little time of their own)
+    ev = hip.create(NE * nq)
+    run(ev)
+    torch.cuda.synchronize()
     per = {n: sum(hip.ms(ev[NE * k + i], ev[NE * k + i + 1]) for k in range(nq)) for i, n in enumerate(STAGES)}
     attend_ms = sum(hip.ms(ev[NE * k], ev[NE * k + NE - 1]) for k in range(nq))
-    hip.destroy(ev + [t0, t1])
-    log(f"prefill {T}: {total_ms:.1f} ms chunked ({attend_ms:.1f} ms in attention calls)")
+    hip.destroy(ev)
+    log(f"prefill {T}: {total_ms:.1f} ms chunked ({attend_ms:.1f} ms in attention calls, traced pass)")
 
     cnt = idx.arrays()["gln"][0, :, : nq].cpu().numpy()  # [Hkv][chunks][G]
     nonempty = np.isfinite(cnt).sum(axis=2).mean(axis=0)  # per chunk, mean over KV heads
