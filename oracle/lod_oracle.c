@@ -34,6 +34,14 @@
  * for Efficient Training-Free Sparse Attention" (readsearch.ai listing, abstract): a
  * query scores the centroids of key blocks and attends to the original keys of the
  * blocks it selects (with top_pages = 0, every key of an opened group).
+ *
+ * Three-tier INT4 (int4_pages = 1), from the post's "Additional Benefits" section:
+ * because a group holds similar keys, the clustered rows are stored compressed as
+ * 4-bit codes, and only the pages a query opens are decoded.  Reading: every clustered
+ * key (value) row is stored as its residual from its group's stored mean key (value),
+ * with one scale per row, s = max_t |r_t| / 7, and codes rint(r_t / s) clamped to
+ * [-8, 7] (all 0 when s = 0); a decoded element is fma(s, code, mean).  Members of
+ * opened pages enter the softmax decoded; sinks and the window stay exact.
  */
 #include <math.h>
 #include <stdint.h>
@@ -59,6 +67,7 @@ typedef struct {
     int32_t bf16_store; /* 1: summaries are rounded to bfloat16 */
     double scale;       /* softmax scale, 1/sqrt(d) */
     int32_t drop_remainder; /* 1: no coarse terms (sparsity ablation) */
+    int32_t int4_pages;     /* 1: opened pages decoded from 4-bit codes (three-tier INT4) */
 } orc_params;
 
 /* Page slots per chunk: at most C/P full pages plus one partial page per group. */
@@ -270,6 +279,55 @@ int32_t orc_build(const orc_params* P, const float* K, const float* V, int32_t n
     return rc;
 }
 
+/* 4-bit code of one row: residual from the group mean, scale max|r|/7, rint, clamp. */
+static void encode_row(const float* x, const float* mean, int32_t d, int8_t* code, float* scale) {
+    float mx = 0.0f;
+    for (int32_t t = 0; t < d; ++t) {
+        const float r = x[t] - mean[t];
+        const float a = r < 0.0f ? -r : r;
+        if (a > mx) mx = a;
+    }
+    const float s = mx / 7.0f;
+    *scale = s;
+    for (int32_t t = 0; t < d; ++t) {
+        if (s == 0.0f) { code[t] = 0; continue; }
+        float c = rintf((x[t] - mean[t]) / s);
+        if (c < -8.0f) c = -8.0f;
+        if (c > 7.0f) c = 7.0f;
+        code[t] = (int8_t)c;
+    }
+}
+
+/*
+ * Three-tier INT4 storage of chunks [0, n_chunks) built by orc_build: for every
+ * chunk-local position with a group, codes [C][d] and a scale [C] for K and V (the
+ * residual from the group's stored mean key / value); sinks get zero codes and scale.
+ */
+int32_t orc_encode_int4(const orc_params* P, const float* K, const float* V, int32_t n_chunks,
+                        const int32_t* assign, const float* gk, const float* gv, int8_t* qk,
+                        int8_t* qv, float* qks, float* qvs) {
+    if (!P || !K || !V || !assign || !gk || !gv || !qk || !qv || !qks || !qvs || n_chunks < 0)
+        return ORC_ERR_ARG;
+    const int32_t C = P->chunk, G = P->groups, d = P->d;
+    for (int32_t c = 0; c < n_chunks; ++c)
+        for (int32_t off = 0; off < C; ++off) {
+            const size_t row = (size_t)c * C + off;
+            const int32_t j = assign[row];
+            if (j < 0) {
+                memset(qk + row * d, 0, (size_t)d);
+                memset(qv + row * d, 0, (size_t)d);
+                qks[row] = 0.0f;
+                qvs[row] = 0.0f;
+                continue;
+            }
+            if (j >= G) return ORC_ERR_ARG;
+            const size_t p = (size_t)c * C + off;
+            encode_row(K + p * d, gk + ((size_t)c * G + j) * d, d, qk + row * d, qks + row);
+            encode_row(V + p * d, gv + ((size_t)c * G + j) * d, d, qv + row * d, qvs + row);
+        }
+    return ORC_OK;
+}
+
 /* Number of chunks summarised for a query at position p (block-granular window). */
 int32_t orc_built_chunks(const orc_params* P, int32_t p) {
     int32_t nb = p / P->chunk - P->window / P->chunk + 1;
@@ -304,9 +362,11 @@ int32_t orc_attend(const orc_params* P, const float* q, int32_t p, int32_t n_chu
                    const int32_t* gcount, const float* gk, const float* gv,
                    const int32_t* pgroup, const int32_t* pcount, const int32_t* pmem,
                    const float* pk, const float* pv, const float* K, const float* V,
+                   const int8_t* qk, const int8_t* qv, const float* qks, const float* qvs,
                    double* out, int32_t* sel_groups, int32_t* sel_pages, double* log_mass,
                    int32_t* n_terms) {
     if (!P || !q || !K || !V || !out || p < 0) return ORC_ERR_ARG;
+    if (P->int4_pages && (!qk || !qv || !qks || !qvs)) return ORC_ERR_ARG;
     const int32_t C = P->chunk, Pg = P->page, G = P->groups, d = P->d, s = P->n_sink;
     const int32_t PS = orc_page_slots(P);
     const int32_t TG = P->top_groups, TP = P->top_pages;
@@ -318,11 +378,12 @@ int32_t orc_attend(const orc_params* P, const float* q, int32_t p, int32_t n_chu
     ranked* el = (ranked*)malloc(sizeof(ranked) * (size_t)(ng > 0 ? ng : 1));
     uint8_t* opened = (uint8_t*)calloc((size_t)(ng > 0 ? ng : 1), 1);
     uint8_t* exact = (uint8_t*)calloc((size_t)p + 1, 1);
+    int32_t* xgroup = (int32_t*)calloc((size_t)p + 1, sizeof(int32_t)); /* opened-page member: group + 1 */
     uint8_t* popen = (uint8_t*)calloc((size_t)(nb > 0 ? nb : 1) * PS, 1);
     double* lam = NULL;
     const float** vals = NULL;
-    if (!el || !opened || !exact || !popen) {
-        free(el); free(opened); free(exact); free(popen);
+    if (!el || !opened || !exact || !popen || !xgroup) {
+        free(el); free(opened); free(exact); free(popen); free(xgroup);
         return ORC_ERR_NOMEM;
     }
     int32_t rc = ORC_OK;
@@ -377,12 +438,21 @@ int32_t orc_attend(const orc_params* P, const float* q, int32_t p, int32_t n_chu
                     if (x < 0 || x > p) { rc = ORC_ERR_ARG; break; }
                     dup |= exact[x];
                     exact[x] = 1;
+                    xgroup[x] = c * G + pgroup[(size_t)c * PS + sl] + 1;
                 }
             }
         if (dup && rc == ORC_OK) rc = ORC_ERR_DOUBLE_COUNT;
     }
 
     /* 4. gather all terms (logit, value row) and take one fp64 softmax */
+    /* decoded rows of opened-page members (three-tier INT4) */
+    float* dec = NULL;
+    int32_t ndec = 0;
+    if (rc == ORC_OK && P->int4_pages) {
+        for (int32_t x = 0; x <= p; ++x) ndec += xgroup[x] != 0;
+        dec = (float*)malloc(sizeof(float) * (size_t)(ndec > 0 ? ndec : 1) * 2 * d);
+        if (!dec) rc = ORC_ERR_NOMEM;
+    }
     if (rc == ORC_OK) {
         const int32_t maxt = (p + 1) + ng + nb * PS;
         lam = (double*)malloc(sizeof(double) * (size_t)maxt);
@@ -390,11 +460,25 @@ int32_t orc_attend(const orc_params* P, const float* q, int32_t p, int32_t n_chu
         if (!lam || !vals) rc = ORC_ERR_NOMEM;
     }
     if (rc == ORC_OK) {
-        int32_t nt = 0, n_ex = 0, n_cg = 0, n_cp = 0;
+        int32_t nt = 0, n_ex = 0, n_cg = 0, n_cp = 0, k4 = 0;
         for (int32_t x = 0; x <= p; ++x) {
             if (!exact[x]) continue;
-            lam[nt] = P->scale * dot64(q, K + (size_t)x * d, d);
-            vals[nt++] = V + (size_t)x * d;
+            const float* kx = K + (size_t)x * d;
+            const float* vx = V + (size_t)x * d;
+            if (P->int4_pages && xgroup[x]) {
+                const int32_t g = xgroup[x] - 1;
+                float* kd = dec + (size_t)k4 * 2 * d;
+                float* vd = kd + d;
+                for (int32_t t = 0; t < d; ++t) {
+                    kd[t] = fmaf(qks[x], (float)qk[(size_t)x * d + t], gk[(size_t)g * d + t]);
+                    vd[t] = fmaf(qvs[x], (float)qv[(size_t)x * d + t], gv[(size_t)g * d + t]);
+                }
+                kx = kd;
+                vx = vd;
+                ++k4;
+            }
+            lam[nt] = P->scale * dot64(q, kx, d);
+            vals[nt++] = vx;
             ++n_ex;
         }
         for (int32_t g = 0; g < ng && !P->drop_remainder; ++g) {
@@ -427,7 +511,7 @@ int32_t orc_attend(const orc_params* P, const float* q, int32_t p, int32_t n_chu
         if (log_mass) *log_mass = M + log(Z);
         if (n_terms) { n_terms[0] = n_ex; n_terms[1] = n_cg; n_terms[2] = n_cp; }
     }
-    free(el); free(opened); free(exact); free(popen); free(lam); free(vals);
+    free(el); free(opened); free(exact); free(popen); free(xgroup); free(dec); free(lam); free(vals);
     return rc;
 }
 

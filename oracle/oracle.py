@@ -47,7 +47,7 @@ class _Params(ctypes.Structure):
                 ("top_pages", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("iters", ctypes.c_int32),
                 ("bf16_store", ctypes.c_int32), ("scale", ctypes.c_double),
-                ("drop_remainder", ctypes.c_int32)]
+                ("drop_remainder", ctypes.c_int32), ("int4_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -77,9 +77,13 @@ def _L():
         lib.orc_build.argtypes = [pp, f32p, f32p, ctypes.c_int32, i32p, i32p, i32p, f32p, f32p,
                                   i32p, i32p, i32p, f32p, f32p]
         lib.orc_attend.restype = ctypes.c_int32
+        i8p = P(ctypes.c_int8)
         lib.orc_attend.argtypes = [pp, f32p, ctypes.c_int32, ctypes.c_int32, i32p, f32p, f32p,
-                                   i32p, i32p, i32p, f32p, f32p, f32p, f32p, f64p, i32p, i32p,
-                                   f64p, i32p]
+                                   i32p, i32p, i32p, f32p, f32p, f32p, f32p, i8p, i8p, f32p, f32p,
+                                   f64p, i32p, i32p, f64p, i32p]
+        lib.orc_encode_int4.restype = ctypes.c_int32
+        lib.orc_encode_int4.argtypes = [pp, f32p, f32p, ctypes.c_int32, i32p, f32p, f32p, i8p, i8p,
+                                        f32p, f32p]
         lib.orc_dense.restype = ctypes.c_int32
         lib.orc_dense.argtypes = [pp, f32p, ctypes.c_int32, f32p, f32p, f64p, f64p]
         _lib = lib
@@ -107,12 +111,14 @@ class Config:
     bf16: bool = False
     scale: float | None = None
     drop_remainder: bool = False  # sparsity ablation: exact keys only, no coarse terms
+    int4_pages: bool = False      # three-tier INT4: opened pages decoded from 4-bit codes
 
     def params(self) -> _Params:
         sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.d)
         return _Params(self.d, self.chunk, self.page, self.groups, self.top_groups,
                        self.top_pages, self.window, self.n_sink, self.iters,
-                       1 if self.bf16 else 0, sc, 1 if self.drop_remainder else 0)
+                       1 if self.bf16 else 0, sc, 1 if self.drop_remainder else 0,
+                       1 if self.int4_pages else 0)
 
     @property
     def page_slots(self) -> int:
@@ -178,6 +184,17 @@ def build_stream(cfg: Config, K, V, n_chunks: int, assign_in=None) -> dict:
     if rc != ORC_OK:
         raise RuntimeError(f"orc_build failed: {rc}")
     idx["n_chunks"] = n_chunks
+    if cfg.int4_pages:
+        idx["qk"] = np.empty((n_chunks, C, d), np.int8)
+        idx["qv"] = np.empty((n_chunks, C, d), np.int8)
+        idx["qks"] = np.empty((n_chunks, C), np.float32)
+        idx["qvs"] = np.empty((n_chunks, C), np.float32)
+        i8 = ctypes.c_int8
+        rc = _L().orc_encode_int4(ctypes.byref(prm), _p(K, f32), _p(V, f32), n_chunks, _p(idx["assign"], i32),
+                                  _p(idx["gk"], f32), _p(idx["gv"], f32), _p(idx["qk"], i8), _p(idx["qv"], i8),
+                                  _p(idx["qks"], f32), _p(idx["qvs"], f32))
+        if rc != ORC_OK:
+            raise RuntimeError(f"orc_encode_int4 failed: {rc}")
     return idx
 
 
@@ -193,12 +210,15 @@ def attend(cfg: Config, idx: dict, K, V, q, p: int):
     lm = np.zeros(1, np.float64)
     nt = np.zeros(3, np.int32)
     prm = cfg.params()
-    i32, f32, f64 = ctypes.c_int32, ctypes.c_float, ctypes.c_double
+    i32, f32, f64, i8 = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_int8
+    if cfg.int4_pages and "qk" not in idx:
+        raise ValueError("the index was built without INT4 codes")
     rc = _L().orc_attend(ctypes.byref(prm), _p(q, f32), p, idx["n_chunks"], _p(idx["gcount"], i32),
                          _p(idx["gk"], f32), _p(idx["gv"], f32), _p(idx["pgroup"], i32),
                          _p(idx["pcount"], i32), _p(idx["pmem"], i32), _p(idx["pk"], f32),
-                         _p(idx["pv"], f32), _p(K, f32), _p(V, f32), _p(out, f64), _p(sg, i32),
-                         _p(sp, i32), _p(lm, f64), _p(nt, i32))
+                         _p(idx["pv"], f32), _p(K, f32), _p(V, f32), _p(idx.get("qk"), i8),
+                         _p(idx.get("qv"), i8), _p(idx.get("qks"), f32), _p(idx.get("qvs"), f32),
+                         _p(out, f64), _p(sg, i32), _p(sp, i32), _p(lm, f64), _p(nt, i32))
     if rc != ORC_OK:
         raise RuntimeError(f"orc_attend failed: {rc}")
     return {"out": out, "sel_groups": sg, "sel_pages": sp.reshape(TG, TPW),

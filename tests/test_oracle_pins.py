@@ -546,3 +546,109 @@ def test_sparsity_ablation_opening_everything_is_dense():
         q = rng.standard_normal(16).astype(np.float32)
         r = orc.attend(cfg, idx, K, V, q, p)
         assert np.allclose(r["out"], _dense_np(K, V, q, p, cfg.params().scale)[0], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- three-tier INT4
+
+def _int4_case(seed, sigma=0.5, n=16):
+    cfg = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=3, top_pages=2, window=128,
+                     n_sink=2, bf16=True, int4_pages=True)
+    K, V, cen, _ = _mixture(n * 64 + 64, 16, seed, n_centres=8, sigma=sigma, round_bf16=True)
+    return cfg, K, V, cen, orc.build_stream(cfg, K, V, n)
+
+
+def test_int4_codes_reconstruct_within_half_a_step():
+    """Each clustered row decodes to within half a quantisation step of itself, codes
+    stay in [-8, 7], the largest residual takes code +-7, and sinks carry no code."""
+    cfg, K, V, cen, idx = _int4_case(81)
+    C = cfg.chunk
+    for X, mean, code, scale in ((K, idx["gk"], idx["qk"], idx["qks"]), (V, idx["gv"], idx["qv"], idx["qvs"])):
+        for c in range(idx["n_chunks"]):
+            for off in range(C):
+                j = idx["assign"][c, off]
+                if j < 0:
+                    assert scale[c, off] == 0 and not code[c, off].any()
+                    continue
+                x = X[c * C + off].astype(np.float64)
+                m = mean[c, j].astype(np.float64)
+                s = float(scale[c, off])
+                q = code[c, off].astype(np.int64)
+                assert q.min() >= -8 and q.max() <= 7
+                dec = m + s * q
+                assert np.all(np.abs(dec - x) <= s / 2 * (1 + 1e-6) + 1e-30)
+                if s > 0:
+                    assert np.abs(q).max() == 7
+                else:
+                    assert np.array_equal(x, m)
+
+
+def test_int4_rows_equal_to_their_group_mean_are_exact():
+    """Groups whose keys and values are all identical are stored losslessly, so INT4
+    changes nothing: the output equals the bf16 three-tier output bit for bit."""
+    rng = np.random.default_rng(82)
+    d, C = 16, 64
+    cen_k = rng.standard_normal((4, d)).astype(np.float32)
+    cen_v = rng.standard_normal((4, d)).astype(np.float32)
+    z = np.repeat(np.arange(4), C // 4)  # four runs of 16: strided seeds find each centre
+    K = np.concatenate([cen_k[z]] * 17)
+    V = np.concatenate([cen_v[z]] * 17)
+    K = torch.from_numpy(K).to(torch.bfloat16).float().numpy()
+    V = torch.from_numpy(V).to(torch.bfloat16).float().numpy()
+    base = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=2, top_pages=2, window=128,
+                      n_sink=0, bf16=True)
+    q4 = dataclasses.replace(base, int4_pages=True)
+    idx = orc.build_stream(q4, K, V, 16)
+    assert not idx["qks"].any() and not idx["qvs"].any()
+    for p in [300, 700, 1087]:
+        q = rng.standard_normal(16).astype(np.float32)
+        a = orc.attend(base, idx, K, V, q, p)
+        b = orc.attend(q4, idx, K, V, q, p)
+        assert np.array_equal(a["out"], b["out"])
+
+
+def test_int4_attention_is_softmax_over_the_decoded_rows():
+    """With INT4 pages the output is the softmax over the exact set in which members of
+    opened pages are replaced by their decoded rows (decoded here in fp64 and rounded
+    once to fp32), plus the unchanged coarse remainder."""
+    cfg, K, V, cen, idx = _int4_case(83)
+    C, G, PS = cfg.chunk, cfg.groups, cfg.page_slots
+    rng = np.random.default_rng(84)
+    for p in [200, 511, 777, 1087]:
+        q = (cen[rng.integers(0, 8)] + 0.3 * rng.standard_normal(16)).astype(np.float32)
+        r = orc.attend(cfg, idx, K, V, q, p)
+        nb = cfg.built_chunks(p)
+        keys, vals = {}, {}
+        for x in range(min(cfg.n_sink, p + 1)):
+            keys[x], vals[x] = K[x], V[x]
+        for x in range(nb * C, p + 1):
+            keys[x], vals[x] = K[x], V[x]
+        sel = [g for g in r["sel_groups"].tolist() if g >= 0]
+        opened = set()
+        for i, g in enumerate(sel):
+            c, j = divmod(g, G)
+            for sl in [s for s in r["sel_pages"][i].tolist() if s >= 0]:
+                opened.add((c, sl))
+                for x in idx["pmem"][c, sl, : idx["pcount"][c, sl]].tolist():
+                    o = x - c * C
+                    for src, mean, code, sc in ((keys, idx["gk"], idx["qk"], idx["qks"]),
+                                                (vals, idx["gv"], idx["qv"], idx["qvs"])):
+                        dec = (np.float64(sc[c, o]) * code[c, o].astype(np.float64) +
+                               mean[c, j].astype(np.float64)).astype(np.float32)
+                        src[x] = dec
+        terms = [(cfg.params().scale * float(keys[x].astype(np.float64) @ q.astype(np.float64)),
+                  vals[x].astype(np.float64)) for x in sorted(keys)]
+        for c in range(nb):
+            for j in range(G):
+                n = int(idx["gcount"][c, j])
+                if n == 0:
+                    continue
+                if c * G + j not in sel:
+                    terms.append((cfg.params().scale * float(idx["gk"][c, j].astype(np.float64) @ q) + math.log(n),
+                                  idx["gv"][c, j].astype(np.float64)))
+                else:
+                    for sl in range(PS):
+                        if idx["pgroup"][c, sl] == j and (c, sl) not in opened:
+                            terms.append((cfg.params().scale * float(idx["pk"][c, sl].astype(np.float64) @ q)
+                                          + math.log(int(idx["pcount"][c, sl])), idx["pv"][c, sl].astype(np.float64)))
+        ref, _ = _softmax_terms(terms)
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12)
