@@ -33,6 +33,7 @@ struct BuildArgs {
     int max_chunks;
     int chunk_begin, n_chunks;
     int n_kv_heads, G, n_sink, iters;
+    int int4;  // three-tier INT4: store 4-bit codes of every clustered row
     const int32_t* assign_in;
     int32_t* assign_out;
 };
@@ -386,6 +387,56 @@ __device__ void summaries(BuildSmem<T, GMAX>& s, int G, int PS, T* pdst, bool gr
     }
 }
 
+// Three-tier INT4 codes of the chunk's rows (bf16 keys or values in s.x, their group
+// means in s.mu): member i (thread i) stores the residual from its group's stored mean
+// (the mean rounded to bf16) as 128 4-bit codes at chunk-local position first_off + i,
+// with scale max|r| / 7 and codes rint(r / scale) clamped to [-8, 7] (0 when the scale
+// is 0); element 2j sits in the low nibble of byte j.  Sink positions get zero codes
+// and scale.  This follows the page's note that centroid groups let clustered rows be
+// stored at INT4 and decoded only for opened pages (section "Additional Benefits").
+template <int GMAX>
+__device__ void encode_rows_int4(const BuildSmem<bf16_t, GMAX>& s, int m, int first_off, uint8_t* q4,
+                                 float* q4s) {
+    const int tid = threadIdx.x;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    if (tid < first_off) {
+#pragma unroll
+        for (int u = 0; u < kD / 32; ++u) reinterpret_cast<uint4*>(q4 + (int64_t)tid * (kD / 2))[u] = zero;
+        q4s[tid] = 0.0f;
+    }
+    if (tid >= m) return;
+    const int i = tid, j = s.a[i];
+    // residual of elements 8c .. 8c+7 (LDS reads; recomputed in the second pass)
+    auto resid8 = [&](int c, float* r) {
+        float f[8];
+        Elt<bf16_t>::unpack(*reinterpret_cast<const uint4*>(&s.x[i][8 * (c ^ (i & 15))]), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            r[e] = f[e] - Elt<bf16_t>::to_f32(Elt<bf16_t>::store_round(s.mu[j][8 * c + e]));
+    };
+    float mx = 0.0f;
+    for (int c = 0; c < kD / 8; ++c) {
+        float r[8];
+        resid8(c, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(r[e]));
+    }
+    const float sc = mx / 7.0f;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(q4 + (int64_t)(first_off + i) * (kD / 2));
+    for (int c = 0; c < kD / 8; ++c) {
+        float r[8];
+        resid8(c, r);
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q = sc == 0.0f ? 0.0f : fminf(fmaxf(rintf(r[e] / sc), -8.0f), 7.0f);
+            v |= ((uint32_t)(int)q & 0xfu) << (4 * e);
+        }
+        dst[c] = v;
+    }
+    q4s[first_off + i] = sc;
+}
+
 template <typename T, int GMAX>
 __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     __shared__ BuildSmem<T, GMAX> s;
@@ -545,6 +596,12 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     }
     // Page means of keys (group means of keys are already in s.mu).
     summaries(s, G, PS, pk, false);
+    const int64_t qrow = ((int64_t)unit * A.max_chunks + c) * kChunk;  // first code row of the chunk
+    if constexpr (sizeof(T) == 2) {
+        if (A.int4)
+            encode_rows_int4(s, m, first_off, reinterpret_cast<uint8_t*>(A.index + A.L.q4k) + qrow * (kD / 2),
+                             reinterpret_cast<float*>(A.index + A.L.q4ks) + qrow);
+    }
     if (tid < PS) {
         const int n = s.pst[tid + 1] - s.pst[tid];
         pln[tid] = n > 0 ? logf((float)n) : -INFINITY;
@@ -560,6 +617,11 @@ __global__ __launch_bounds__(kThreads) void build_chunk_kernel(BuildArgs A) {
     __syncthreads();
     summaries(s, G, PS, pv, true);
     __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+        if (A.int4)
+            encode_rows_int4(s, m, first_off, reinterpret_cast<uint8_t*>(A.index + A.L.q4v) + qrow * (kD / 2),
+                             reinterpret_cast<float*>(A.index + A.L.q4vs) + qrow);
+    }
     for (int e = tid; e < G * kD; e += kThreads) {
         const int j = e / kD, t = e % kD;
         store_elt(&gv[e], s.cnt[j] > 0 ? s.mu[j][t] : 0.0f);
@@ -600,6 +662,7 @@ extern "C" int lod_build_chunk(const lod_params* params, const lod_index* index,
     A.chunk_begin = chunk_begin; A.n_chunks = n_chunks;
     A.n_kv_heads = params->n_kv_heads; A.G = params->groups_per_chunk;
     A.n_sink = params->n_sink; A.iters = params->kmeans_iters;
+    A.int4 = params->int4_pages;
     A.assign_in = assign_in; A.assign_out = assign_out;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int G = A.G;

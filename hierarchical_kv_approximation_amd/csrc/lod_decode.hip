@@ -52,6 +52,7 @@ struct DecodeArgs {
     int Hq, Hkv, G, TG, TP, W, n_sink;
     float scale;
     int drop;  // 1: no coarse remainder (sparsity ablation)
+    int q4;    // 1: opened pages decoded from the index's 4-bit codes (three-tier INT4)
     int slice, nslice, nwin, nslot;
     // query rows: with seq_lens, row r is sequence r at position seq_lens[r]-1 (decode);
     // without, row r is sequence seq0 + r / rows_per_seq at position pos0 + r % rows_per_seq
@@ -540,7 +541,9 @@ __device__ __forceinline__ void open_block_add(Online& st, const float* lam, con
 
 // DROP: no coarse remainder, so unopened pages add no terms (a run-time flag on the fp32
 // path, DROP_RT; a compile-time one on the bf16 path).
-template <typename T, int OB, bool PAGED, bool DROP_RT = true, bool DROP = false>
+// Q4 (bf16 only): the opened pages' rows are decoded from the index's 4-bit codes
+// (fma(scale, code, group mean)) instead of read from the cache.
+template <typename T, int OB, bool PAGED, bool DROP_RT = true, bool DROP = false, bool Q4 = false>
 __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int seq, int kvh, int64_t head,
                            const float* q8, Online& st) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -643,7 +646,7 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         const int p0 = (e < npg && rank >= 0) ? pst[ps0 + e] : 0;
 #pragma unroll
         for (int x = 0; x < kPage; ++x)  // a page holds at most kPage rows
-            if (x < cnt) s.ex[wave][off + x] = c * kChunk + perm[p0 + x];
+            if (x < cnt) s.ex[wave][off + x] = (c * kChunk + perm[p0 + x]) | (Q4 ? k << 24 : 0);
         if (lane == 0) s.nex[wave] = total;
     }
     wave_sync();
@@ -651,38 +654,118 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
     // exact rows of the wave's groups, then its coarse pages (subgroup sgw takes sgw, sgw+4, ...)
     const int nex = s.nex[wave];
     constexpr int P16 = Elt<T>::kPer16, U = 8 / P16;  // 16-byte pieces per 8 elements
-    for (int base = 0; base < nex; base += 4 * OB) {
-        u32x4_t kp[OB][U], vp[OB][U];  // rows kept packed until used
+    if constexpr (Q4) {
+        // entries: position | group slot << 24; the slots' mean rows stay in registers
+        const int64_t qrow0 = unit * A.max_chunks * kChunk;
+        const uint8_t* q4k = reinterpret_cast<const uint8_t*>(A.index + A.L.q4k) + qrow0 * (kD / 2);
+        const uint8_t* q4v = reinterpret_cast<const uint8_t*>(A.index + A.L.q4v) + qrow0 * (kD / 2);
+        const float* q4ks = reinterpret_cast<const float*>(A.index + A.L.q4ks) + qrow0;
+        const float* q4vs = reinterpret_cast<const float*>(A.index + A.L.q4vs) + qrow0;
+        const bf16_t* gk_u = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + unit * A.max_chunks * A.G * kD;
+        const bf16_t* gv_u = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + unit * A.max_chunks * A.G * kD;
+        u32x4_t mk[kGPW], mv[kGPW];
 #pragma unroll
-        for (int x = 0; x < OB; ++x) {
-            const int it = base + sgw + 4 * x;
-            if (it < nex) {
-                const int64_t ro = kv_pos<PAGED>(A, seq, s.ex[wave][it]);
+        for (int k = 0; k < kGPW; ++k) {
+            const int i = wave + 4 * k;
+            const int64_t g = (k < ngw && i < nsel) ? (int64_t)key_id(s.sel[i]) : 0;
+            mk[k] = *reinterpret_cast<const u32x4_t*>(gk_u + g * kD + 8 * l16);
+            mv[k] = *reinterpret_cast<const u32x4_t*>(gv_u + g * kD + 8 * l16);
+        }
+        auto pick = [&](const u32x4_t* m, int k) {
+            return k == 0 ? m[0] : (k == 1 ? m[1] : (k == 2 ? m[2] : m[3]));
+        };
+        auto decode8 = [&](uint32_t code, float sc, const u32x4_t& mean, float* f) {
+            float mf[8];
+            Elt<bf16_t>::unpack(mean, mf);
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    kp[x][u] = *reinterpret_cast<const u32x4_t*>(kh + ro + 8 * l16 + u * P16);
-                    vp[x][u] = *reinterpret_cast<const u32x4_t*>(vh + ro + 8 * l16 + u * P16);
+            for (int e = 0; e < 8; ++e) {
+                const int q = (int)((code >> (4 * e)) & 0xfu);
+                f[e] = __builtin_fmaf(sc, (float)((q ^ 8) - 8), mf[e]);
+            }
+        };
+        for (int base = 0; base < nex; base += 4 * OB) {
+            uint32_t kc[OB], vc[OB];
+            float ks[OB], vs[OB];
+            int slot[OB];
+#pragma unroll
+            for (int x = 0; x < OB; ++x) {
+                const int it = base + sgw + 4 * x;
+                const int ent = it < nex ? s.ex[wave][it] : 0;
+                const int64_t pos = ent & 0xffffff;
+                slot[x] = ent >> 24;
+                kc[x] = *reinterpret_cast<const uint32_t*>(q4k + pos * (kD / 2) + 4 * l16);
+                vc[x] = *reinterpret_cast<const uint32_t*>(q4v + pos * (kD / 2) + 4 * l16);
+                ks[x] = q4ks[pos];
+                vs[x] = q4vs[pos];
+            }
+            float lam[OB];
+#pragma unroll
+            for (int x = 0; x < OB; ++x) {
+                float kf[8];
+                decode8(kc[x], ks[x], pick(mk, slot[x]), kf);
+                float a = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
+                lam[x] = row16_sum_f32(a);
+            }
+            float mb = -INFINITY;
+#pragma unroll
+            for (int x = 0; x < OB; ++x) {
+                lam[x] = base + sgw + 4 * x < nex ? A.scale * lam[x] : -INFINITY;
+                mb = fmaxf(mb, lam[x]);
+            }
+            if (mb == -INFINITY) continue;
+            const float mn = fmaxf(st.m, mb);
+            const float a = softmax_exp(st.m - mn);
+            st.l *= a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[e] *= a;
+#pragma unroll
+            for (int x = 0; x < OB; ++x) {
+                if (lam[x] == -INFINITY) continue;
+                const float w = softmax_exp(lam[x] - mn);
+                float vf[8];
+                decode8(vc[x], vs[x], pick(mv, slot[x]), vf);
+                st.l += w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st.o[e] = __builtin_fmaf(w, vf[e], st.o[e]);
+            }
+            st.m = mn;
+        }
+    } else {
+        for (int base = 0; base < nex; base += 4 * OB) {
+            u32x4_t kp[OB][U], vp[OB][U];  // rows kept packed until used
+#pragma unroll
+            for (int x = 0; x < OB; ++x) {
+                const int it = base + sgw + 4 * x;
+                if (it < nex) {
+                    const int64_t ro = kv_pos<PAGED>(A, seq, s.ex[wave][it]);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        kp[x][u] = *reinterpret_cast<const u32x4_t*>(kh + ro + 8 * l16 + u * P16);
+                        vp[x][u] = *reinterpret_cast<const u32x4_t*>(vh + ro + 8 * l16 + u * P16);
+                    }
                 }
             }
+            // block update of the subgroup's online softmax: dot products and their
+            // reductions side by side, one rescale, then the weighted values
+            float lam[OB];
+#pragma unroll
+            for (int x = 0; x < OB; ++x) {
+                float kf[8];
+#pragma unroll
+                for (int u = 0; u < U; ++u) Elt<T>::unpack(kp[x][u], kf + u * P16);
+                float a = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
+                lam[x] = a;
+            }
+#pragma unroll
+            for (int x = 0; x < OB; ++x) lam[x] = row16_sum_f32(lam[x]);
+#pragma unroll
+            for (int x = 0; x < OB; ++x) lam[x] = base + sgw + 4 * x < nex ? A.scale * lam[x] : -INFINITY;
+            open_block_add<T, OB, U>(st, lam, vp);
         }
-        // block update of the subgroup's online softmax: dot products and their
-        // reductions side by side, one rescale, then the weighted values
-        float lam[OB];
-#pragma unroll
-        for (int x = 0; x < OB; ++x) {
-            float kf[8];
-#pragma unroll
-            for (int u = 0; u < U; ++u) Elt<T>::unpack(kp[x][u], kf + u * P16);
-            float a = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = __builtin_fmaf(q8[e], kf[e], a);
-            lam[x] = a;
-        }
-#pragma unroll
-        for (int x = 0; x < OB; ++x) lam[x] = row16_sum_f32(lam[x]);
-#pragma unroll
-        for (int x = 0; x < OB; ++x) lam[x] = base + sgw + 4 * x < nex ? A.scale * lam[x] : -INFINITY;
-        open_block_add<T, OB, U>(st, lam, vp);
     }
     const int ncp = (DROP || (DROP_RT && A.drop)) ? 0 : s.ncp[wave];  // unopened pages: coarse terms
     for (int base = 0; base < ncp; base += 4 * OB) {
@@ -1308,7 +1391,7 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
 // same logits, are subtracted in the final merge.  The subtracted mass never exceeds
 // the scan's, and the exact terms of the opened pages carry at least the same order of
 // mass, so fp32 cancellation stays near 1e-6 of the output scale.
-template <bool DROP, bool PAGED>
+template <bool DROP, bool PAGED, bool Q4>
 __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b, int hq) {
     const int HG = A.Hq / A.Hkv;
     const int kvh = hq / HG;
@@ -1590,7 +1673,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
 
     Online st;
     st.init();
-    open_pages<bf16_t, 2 * kOpenBatch, PAGED, false, DROP>(A, s, nsel, seq, kvh, head, q8, st);
+    open_pages<bf16_t, 2 * kOpenBatch, PAGED, false, DROP, Q4>(A, s, nsel, seq, kvh, head, q8, st);
     open_stash(s, st);
     if (part_in_lds) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1648,11 +1731,11 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
 // Decode launch 2 (bf16): one workgroup per (sequence, query head) runs the open step and
 // the final merge.  Consecutive workgroups take different KV heads, so the query heads
 // of one KV head share an XCD (workgroups are dealt to the 8 XCDs round robin).
-template <bool DROP, bool PAGED>
+template <bool DROP, bool PAGED, bool Q4>
 __global__ __launch_bounds__(kThreads) void decode_open_mfma_kernel(DecodeArgs A) {
     __shared__ OpenSmem<bf16_t> s;
     const int j = blockIdx.x;
-    decode_open_role<DROP, PAGED>(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
+    decode_open_role<DROP, PAGED, Q4>(A, s, blockIdx.y, (j % A.Hkv) * (A.Hq / A.Hkv) + j / A.Hkv);
 }
 
 
@@ -1766,10 +1849,16 @@ static void launch_decode_view(const DecodeArgs& A, int rows, hipStream_t st) {
                                    dim3(kThreads), 0, st, A);
         }
         trace_point(1, st);
-        if (A.drop)
-            hipLaunchKernelGGL((decode_open_mfma_kernel<true, PAGED>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+        // with INT4 pages the open step reads no cache rows, so the view does not matter
+        const dim3 og(A.Hq, rows);
+        if (A.q4 && A.drop)
+            hipLaunchKernelGGL((decode_open_mfma_kernel<true, false, true>), og, dim3(kThreads), 0, st, A);
+        else if (A.q4)
+            hipLaunchKernelGGL((decode_open_mfma_kernel<false, false, true>), og, dim3(kThreads), 0, st, A);
+        else if (A.drop)
+            hipLaunchKernelGGL((decode_open_mfma_kernel<true, PAGED, false>), og, dim3(kThreads), 0, st, A);
         else
-            hipLaunchKernelGGL((decode_open_mfma_kernel<false, PAGED>), dim3(A.Hq, rows), dim3(kThreads), 0, st, A);
+            hipLaunchKernelGGL((decode_open_mfma_kernel<false, PAGED, false>), og, dim3(kThreads), 0, st, A);
         trace_point(2, st);
     } else {
         if (A.nslice + A.nwin > 0)
@@ -1861,6 +1950,7 @@ static void fill_decode_args(DecodeArgs& A, const lod_params* params, const lod_
     A.Hq = params->n_q_heads; A.Hkv = params->n_kv_heads; A.G = params->groups_per_chunk;
     A.TG = params->top_groups; A.TP = params->top_pages; A.W = params->window;
     A.n_sink = params->n_sink; A.scale = params->scale; A.drop = params->drop_remainder;
+    A.q4 = params->int4_pages;
     A.slice = P.slice; A.nslice = P.nslice; A.nwin = P.nwin; A.nslot = P.nslot;
     A.seq0 = 0; A.rows_per_seq = 1; A.pos0 = 0;
 }

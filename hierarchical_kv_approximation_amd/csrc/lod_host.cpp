@@ -17,7 +17,9 @@ int check_params(const lod_params* p) {
     if (p->n_sink >= p->chunk_size) return LOD_ERR_ARG;
     if (!(p->scale > 0.0f) || !isfinite(p->scale)) return LOD_ERR_ARG;
     if (p->drop_remainder != 0 && p->drop_remainder != 1) return LOD_ERR_ARG;
+    if (p->int4_pages != 0 && p->int4_pages != 1) return LOD_ERR_ARG;
     if (p->kv_dtype != LOD_F32 && p->kv_dtype != LOD_BF16) return LOD_ERR_UNSUPPORTED;
+    if (p->int4_pages && p->kv_dtype != LOD_BF16) return LOD_ERR_UNSUPPORTED;
     if (p->head_dim != kD || p->chunk_size != kChunk || p->page_size != kPage)
         return LOD_ERR_UNSUPPORTED;
     if (p->groups_per_chunk > kMaxG || p->top_groups > kMaxTG || p->top_pages > kPage)
@@ -56,6 +58,11 @@ lod_index_layout_t make_layout(const lod_params* p, int32_t batch, int32_t max_c
     L.pln = o;    o = align256(o + U * NC * PS * 4);
     L.meta = o;   o = align256(o + U * NC * meta_stride(p) * 2);
     L.assign = o; o = align256(o + U * NC * p->chunk_size);
+    const size_t Q = p->int4_pages ? U * NC * p->chunk_size : 0;  // rows with 4-bit codes
+    L.q4k = o;    o = align256(o + Q * d / 2);
+    L.q4v = o;    o = align256(o + Q * d / 2);
+    L.q4ks = o;   o = align256(o + Q * 4);
+    L.q4vs = o;   o = align256(o + Q * 4);
     L.total = o;
     L.page_slots = (int32_t)PS;
     L.meta_stride = meta_stride(p);

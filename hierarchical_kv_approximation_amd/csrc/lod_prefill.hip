@@ -1005,6 +1005,7 @@ struct PagesArgs {
     lod_index_layout_t L;
     int max_chunks, G, W, TG;
     int drop;               // 1: no coarse remainder (unopened pages add nothing)
+    int q4;                 // 1: opened rows decoded from the index's 4-bit codes
     const PairRec* rec;     // [B][nq][Hq][TG], slot t holds the group selg[t]
     const int32_t* selg;    // [B][nq][Hq][TG] opened groups, ascending (-1 padding)
     int2* plist;            // [units][kChunk * HG * TG] (pair index, group) sorted by group
@@ -1094,7 +1095,9 @@ constexpr int kPagesMeta = 320;  // int16 entries of a chunk's meta row held in 
 // A pair's loads form three dependent steps: its list entry (pair and group); the query,
 // its record and the whole meta row of the group's chunk (to LDS); then the rows of the
 // opened pages (batches of 8, kept packed) with the unopened pages' means.
-template <int HG, bool PAGED>
+// Q4: the opened rows are decoded from the index's 4-bit codes (fma(scale, code, group
+// mean)), so no cache row is read.
+template <int HG, bool PAGED, bool Q4>
 __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     __shared__ alignas(16) int16_t mrow[kPairsPerWG][kPagesMeta];
     const int blk = blockIdx.x, unit_local = blockIdx.y;
@@ -1167,17 +1170,44 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     };
     Online st;
     st.init();
+    // INT4: the group's mean rows (this lane's 8 elements) and the unit's code rows
+    const int64_t qrow0 = ubase * kChunk;
+    uint4 mk = make_uint4(0, 0, 0, 0), mv = mk;
+    if constexpr (Q4) {
+        const int64_t g = ubase * A.G + gid;
+        mk = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + g * kD + 8 * l16);
+        mv = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + g * kD + 8 * l16);
+    }
+    auto decode8 = [&](uint32_t code, float sc, const uint4& mean, float* f) {
+        float mf[8];
+        Elt<bf16_t>::unpack(mean, mf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int q = (int)((code >> (4 * e)) & 0xfu);
+            f[e] = __builtin_fmaf(sc, (float)((q ^ 8) - 8), mf[e]);
+        }
+    };
     constexpr int RB = 12;  // rows in flight per batch (kept packed): most pairs need one batch
     for (int u0 = 0; u0 < nrow; u0 += RB) {
         const int pos = l16 < RB && u0 + l16 < nrow ? row_pos(u0 + l16) : 0;  // lane u: row u0 + u
-        uint4 kp[RB], vp[RB];
+        uint4 kp[RB], vp[RB];      // bf16 rows (packed)
+        uint32_t kq[RB], vq[RB];   // INT4: codes of this lane's 8 elements
+        float ks[RB], vs[RB];      // INT4: row scales
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
             const int pu = __shfl(pos, seg0 + u, 64);
             if (u0 + u < nrow) {
-                const int64_t ro = kv_pos<PAGED>(A, bs, pu);
-                kp[u] = *reinterpret_cast<const uint4*>(kc + ro + 8 * l16);
-                vp[u] = *reinterpret_cast<const uint4*>(vc + ro + 8 * l16);
+                if constexpr (Q4) {
+                    const int64_t row = qrow0 + pu;
+                    kq[u] = *reinterpret_cast<const uint32_t*>(A.index + A.L.q4k + row * (kD / 2) + 4 * l16);
+                    vq[u] = *reinterpret_cast<const uint32_t*>(A.index + A.L.q4v + row * (kD / 2) + 4 * l16);
+                    ks[u] = reinterpret_cast<const float*>(A.index + A.L.q4ks)[row];
+                    vs[u] = reinterpret_cast<const float*>(A.index + A.L.q4vs)[row];
+                } else {
+                    const int64_t ro = kv_pos<PAGED>(A, bs, pu);
+                    kp[u] = *reinterpret_cast<const uint4*>(kc + ro + 8 * l16);
+                    vp[u] = *reinterpret_cast<const uint4*>(vc + ro + 8 * l16);
+                }
             }
         }
         // block update: dot products and their reductions side by side, one rescale
@@ -1185,16 +1215,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
             float kf[8];
-            Elt<bf16_t>::unpack(kp[u], kf);
+            if constexpr (Q4)
+                decode8(kq[u], ks[u], mk, kf);
+            else
+                Elt<bf16_t>::unpack(kp[u], kf);
             float a = 0.0f;
 #pragma unroll
             for (int z = 0; z < 8; ++z) a = __builtin_fmaf(q8[z], kf[z], a);
             lam[u] = a;
         }
 #pragma unroll
-        for (int mm = 8; mm >= 1; mm >>= 1)
-#pragma unroll
-            for (int u = 0; u < RB; ++u) lam[u] += __shfl_xor(lam[u], mm, 64);
+        for (int u = 0; u < RB; ++u) lam[u] = row16_sum_f32(lam[u]);
         float mb = -INFINITY;
 #pragma unroll
         for (int u = 0; u < RB; ++u) {
@@ -1211,7 +1242,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
             if (lam[u] == -INFINITY) continue;  // no row: its registers were not loaded
             const float wgt = softmax_exp(lam[u] - mn);
             float vf[8];
-            Elt<bf16_t>::unpack(vp[u], vf);
+            if constexpr (Q4)
+                decode8(vq[u], vs[u], mv, vf);
+            else
+                Elt<bf16_t>::unpack(vp[u], vf);
             st.l += wgt;
 #pragma unroll
             for (int e = 0; e < 8; ++e) st.o[e] = __builtin_fmaf(wgt, vf[e], st.o[e]);
@@ -1337,10 +1371,12 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
     const dim3 pgrid((maxpairs + kPairsPerWG - 1) / kPairsPerWG, nunits_q * S.Hkv * batch);
-    if (P.btab)
-        hipLaunchKernelGGL((prefill_pages_kernel<HG, true>), pgrid, dim3(kThreads), 0, st, P);
+    if (P.q4)  // decoded from the index: the cache view does not matter
+        hipLaunchKernelGGL((prefill_pages_kernel<HG, false, true>), pgrid, dim3(kThreads), 0, st, P);
+    else if (P.btab)
+        hipLaunchKernelGGL((prefill_pages_kernel<HG, true, false>), pgrid, dim3(kThreads), 0, st, P);
     else
-        hipLaunchKernelGGL((prefill_pages_kernel<HG, false>), pgrid, dim3(kThreads), 0, st, P);
+        hipLaunchKernelGGL((prefill_pages_kernel<HG, false, false>), pgrid, dim3(kThreads), 0, st, P);
     trace_point(5, st);
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + 1) / 2)), dim3(kThreads), 0, st, P, nrh);
@@ -1471,6 +1507,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.q = S.q; G.nq = rows; G.pos0 = S.pos0; G.Hq = Hq; G.Hkv = Hkv; G.scale = params->scale;
             G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
             G.drop = params->drop_remainder;
+            G.q4 = params->int4_pages;
             G.rec = S.rec;
             G.selg = S.selg;
             G.plist = reinterpret_cast<int2*>(w + P.off_plist);

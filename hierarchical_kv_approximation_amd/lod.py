@@ -27,7 +27,7 @@ class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "head_dim", "n_q_heads", "n_kv_heads", "chunk_size", "page_size", "groups_per_chunk",
         "top_groups", "top_pages", "window", "n_sink", "kmeans_iters", "kv_dtype")] + \
-        [("scale", ctypes.c_float), ("drop_remainder", ctypes.c_int32)]
+        [("scale", ctypes.c_float), ("drop_remainder", ctypes.c_int32), ("int4_pages", ctypes.c_int32)]
 
 
 class KV(ctypes.Structure):
@@ -44,7 +44,8 @@ class Index(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("gk", "gv", "gln", "gkn", "gpage", "pk", "pv", "pln", "meta", "assign", "total")] + \
+                ("gk", "gv", "gln", "gkn", "gpage", "pk", "pv", "pln", "meta", "assign", "q4k", "q4v",
+                 "q4ks", "q4vs", "total")] + \
         [("page_slots", ctypes.c_int32), ("meta_stride", ctypes.c_int32)]
 
 
@@ -118,13 +119,15 @@ class Config:
     page_size: int = 16
     scale: float | None = None
     drop_remainder: bool = False  # sparsity ablation: the same selection, exact keys only
+    int4_pages: bool = False      # three-tier INT4: opened pages decoded from 4-bit codes
 
     def params(self) -> Params:
         sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
         dt = {torch.float32: LOD_F32, torch.bfloat16: LOD_BF16}.get(self.dtype, 99)
         return Params(self.head_dim, self.n_q_heads, self.n_kv_heads, self.chunk_size,
                       self.page_size, self.groups, self.top_groups, self.top_pages, self.window,
-                      self.n_sink, self.kmeans_iters, dt, sc, 1 if self.drop_remainder else 0)
+                      self.n_sink, self.kmeans_iters, dt, sc, 1 if self.drop_remainder else 0,
+                      1 if self.int4_pages else 0)
 
     @property
     def page_slots(self) -> int:
@@ -205,6 +208,14 @@ class LodIndex:
                          (self.batch, cfg.n_kv_heads, NC, L.meta_stride)),
             "assign": view(L.assign, U * NC * cfg.chunk_size, torch.int8,
                            (self.batch, cfg.n_kv_heads, NC, cfg.chunk_size)),
+            **({"q4k": view(L.q4k, U * NC * cfg.chunk_size * d // 2, torch.uint8,
+                            (self.batch, cfg.n_kv_heads, NC, cfg.chunk_size, d // 2)),
+                "q4v": view(L.q4v, U * NC * cfg.chunk_size * d // 2, torch.uint8,
+                            (self.batch, cfg.n_kv_heads, NC, cfg.chunk_size, d // 2)),
+                "q4ks": view(L.q4ks, U * NC * cfg.chunk_size, torch.float32,
+                             (self.batch, cfg.n_kv_heads, NC, cfg.chunk_size)),
+                "q4vs": view(L.q4vs, U * NC * cfg.chunk_size, torch.float32,
+                             (self.batch, cfg.n_kv_heads, NC, cfg.chunk_size))} if cfg.int4_pages else {}),
         } if es else None
 
 

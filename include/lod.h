@@ -59,7 +59,17 @@ enum { LOD_F32 = 0, LOD_BF16 = 1 };
  * 1 <= groups_per_chunk <= 16; 1 <= top_groups <= 16; 0 <= top_pages <= 16
  * (0 = two-tier: every page of an opened group is exact); window a positive multiple
  * of chunk_size; 0 <= n_sink < chunk_size; kmeans_iters >= 1;
- * n_q_heads = g * n_kv_heads with g in {1, 2, 4, 8}; drop_remainder 0 or 1.
+ * n_q_heads = g * n_kv_heads with g in {1, 2, 4, 8}; drop_remainder 0 or 1; int4_pages 0
+ * or 1 (1 needs kv_dtype LOD_BF16).
+ *
+ * int4_pages = 1 follows the post's "Additional Benefits" section (centroids keep
+ * similar keys together, so the cache compresses to INT4, and in three-tier mode only
+ * the selected pages are decompressed).  Reading: every clustered key (value) row is
+ * stored as its residual r from its group's stored mean key (value), one fp32 scale per
+ * row s = max_t |r_t| / 7, and codes rint(r_t / s) clamped to [-8, 7] (0 when s = 0);
+ * a decoded element is fma(s, code, mean).  Members of opened pages enter the softmax
+ * decoded; sinks and the block window are read from the cache.  Once a chunk is built,
+ * its clustered rows are never read from the cache again.
  *
  * drop_remainder = 1 is the token-removing alternative that the post's "The Main Idea"
  * section contrasts LoD with: groups and pages are selected exactly as in LoD, but the
@@ -84,6 +94,10 @@ typedef struct {
     float scale;              /* softmax scale, normally 1/sqrt(head_dim) */
     int32_t drop_remainder;   /* 0: LoD (coarse remainder in the softmax); 1: sparsity
                                  ablation: the same selection, exact keys only */
+    int32_t int4_pages;       /* 0: exact rows of opened pages from the KV cache; 1: three-
+                                 tier INT4: the build stores every clustered row as 4-bit
+                                 codes in the index and opened pages are decoded from them
+                                 (bf16 caches only) */
 } lod_params;
 
 /*
@@ -135,9 +149,12 @@ typedef struct {
  *            pst[PS+1] first perm entry of each page slot, perm[C] chunk-local offsets
  *            of the clustered keys ordered by (group, position)
  *   assign   [U][NC][C]    int8  group of every chunk-local position, -1 for sinks
+ *   q4k, q4v [U][NC][C][d/2] uint8 (int4_pages only, else empty) 4-bit codes of every
+ *            chunk-local row, two's complement, element 2j in the low nibble of byte j
+ *   q4ks, q4vs [U][NC][C]  f32   their scales (0 for sinks)
  */
 typedef struct {
-    size_t gk, gv, gln, gkn, gpage, pk, pv, pln, meta, assign, total;
+    size_t gk, gv, gln, gkn, gpage, pk, pv, pln, meta, assign, q4k, q4v, q4ks, q4vs, total;
     int32_t page_slots;
     int32_t meta_stride; /* int16 entries per chunk in `meta` */
 } lod_index_layout_t;

@@ -29,8 +29,9 @@ def test_status_strings():
         assert L.lod_status_string(code)
 
 
-def test_index_layout_is_aligned_and_disjoint():
-    cfg = lod.Config()
+@pytest.mark.parametrize("int4", [False, True])
+def test_index_layout_is_aligned_and_disjoint(int4):
+    cfg = lod.Config(int4_pages=int4)
     L = lod.Layout()
     assert lod.lib().lod_index_layout(_p(cfg), 4, 128, ctypes.byref(L)) == 0
     U, NC, G, PS, d = 4 * 8, 128, 8, 16 + 8, 128
@@ -38,6 +39,9 @@ def test_index_layout_is_aligned_and_disjoint():
              "gkn": U * NC * G * 4, "gpage": U * NC * G * 4,
              "pk": U * NC * PS * d * 2, "pv": U * NC * PS * d * 2, "pln": U * NC * PS * 4,
              "meta": U * NC * L.meta_stride * 2, "assign": U * NC * 256}
+    if int4:
+        sizes.update({"q4k": U * NC * 256 * d // 2, "q4v": U * NC * 256 * d // 2,
+                      "q4ks": U * NC * 256 * 4, "q4vs": U * NC * 256 * 4})
     spans = sorted((getattr(L, k), getattr(L, k) + v) for k, v in sizes.items())
     for (a0, a1), (b0, _) in zip(spans, spans[1:]):
         assert a1 <= b0
@@ -89,6 +93,19 @@ def test_bad_params_rejected_by_every_entry_point(field, value, status):
                                 FAKE, 1 << 40, None) == status
     assert L.lod_dense_decode(_p(cfg), kv, FAKE, FAKE, 1, 4096, FAKE, FAKE, 1 << 40, None) == status
     assert L.lod_dense_prefill(_p(cfg), kv, FAKE, 0, 256, 1, FAKE, None) == status
+
+
+def test_int4_flag_values():
+    """int4_pages is 0 or 1, and INT4 pages need bf16 caches."""
+    L = lod.lib()
+    n = ctypes.c_size_t()
+    p = lod.Config().params()
+    p.int4_pages = 2
+    assert L.lod_index_bytes(ctypes.byref(p), 1, 4096, ctypes.byref(n)) == lod.LOD_ERR_ARG
+    p = lod.Config(dtype=torch.float32, int4_pages=True).params()
+    assert L.lod_index_bytes(ctypes.byref(p), 1, 4096, ctypes.byref(n)) == lod.LOD_ERR_UNSUPPORTED
+    p = lod.Config(int4_pages=True).params()
+    assert L.lod_index_bytes(ctypes.byref(p), 1, 4096, ctypes.byref(n)) == lod.LOD_OK
 
 
 def test_bad_buffers_rejected():
