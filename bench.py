@@ -159,6 +159,7 @@ def main():
     ap.add_argument("--prefill-ctx", type=int, default=131072)
     ap.add_argument("--no-sweep", action="store_true", help="skip the sigma sweep of the approximation error")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV-view decode timing")
+    ap.add_argument("--no-int4", action="store_true", help="skip the INT4-pages decode timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -295,10 +296,10 @@ def main():
 
     # reference for the variants below: the same LoD calls back to back, no trace events,
     # no builds (every layer is already built past the boundary)
-    def time_calls(c, paged_view=False):
+    def time_calls(c, paged_view=False, index="index"):
         for k in range(min(W, 4)):
             Ly = layers[k % L]
-            lod.attend_decode(c, Ly["index"], Ly["Kp" if paged_view else "K"], Ly["Vp" if paged_view else "V"],
+            lod.attend_decode(c, Ly[index], Ly["Kp" if paged_view else "K"], Ly["Vp" if paged_view else "V"],
                               Ly["q"], seq[npos - 1], max_len, ws=ws, out=out,
                               block_table=Ly["table"] if paged_view else None)
         torch.cuda.synchronize()
@@ -306,7 +307,7 @@ def main():
         hip.record(a0, stream)
         for k in range(K):
             Ly = layers[k % L]
-            lod.attend_decode(c, Ly["index"], Ly["Kp" if paged_view else "K"], Ly["Vp" if paged_view else "V"],
+            lod.attend_decode(c, Ly[index], Ly["Kp" if paged_view else "K"], Ly["Vp" if paged_view else "V"],
                               Ly["q"], seq[k // L], max_len, ws=ws, out=out,
                               block_table=Ly["table"] if paged_view else None)
         hip.record(a1, stream)
@@ -325,6 +326,26 @@ def main():
               "ms_per_call": round(sms, 5), "tok_per_s": round(B * 1000.0 / sms, 1),
               "time_vs_lod": round(sms / ref_ms, 3), "lod_reference_ms_per_call": round(ref_ms, 5)}
     log(f"sparsity ablation: {sms * 1000:.1f} us/call")
+
+    # three-tier INT4: indexes built with 4-bit codes of every clustered row; the open
+    # step decodes the opened pages from them instead of reading the cache
+    int4 = None
+    if not args.no_int4:
+        qcfg = dataclasses.replace(cfg, int4_pages=True)
+        for Ly in layers:
+            Ly["index4"] = lod.LodIndex.allocate(qcfg, B, cap, device=dev)
+            lod.build_chunk(qcfg, Ly["index4"], Ly["K"], Ly["V"], 0, build_chunk + 1)
+        qms = time_calls(qcfg, index="index4")
+        code_bytes = sum(int(Ly["index4"].mem.numel()) for Ly in layers) // L - sum(
+            int(Ly["index"].mem.numel()) for Ly in layers) // L
+        for Ly in layers:
+            del Ly["index4"]
+        int4 = {"what": "the same decode calls with opened pages decoded from 4-bit codes in the index",
+                "ms_per_call": round(qms, 5), "tok_per_s": round(B * 1000.0 / qms, 1),
+                "time_vs_bf16_pages": round(qms / ref_ms, 3),
+                "code_bytes_per_layer": code_bytes,
+                "cache_bytes_per_layer_bf16": int(layers[0]["K"].numel() * 2 * 2)}
+        log(f"INT4 pages: {qms * 1000:.1f} us/call")
 
     # paged KV view: each layer's cache scattered over a pool of 16-position blocks in a
     # seeded random order (a serving engine's block table); same index, same positions
@@ -418,6 +439,7 @@ def main():
             "dense_decode": dense,
             "sparsity_ablation": sparse,
             "paged_kv_view": paged,
+            "int4_pages": int4,
             "setup_s": round(setup_s, 1),
         },
         "prefill": prefill,
@@ -594,17 +616,19 @@ def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, s
                 ("two_tier", dataclasses.replace(cfg, top_pages=0)),
                 ("sparse_three_tier", dataclasses.replace(cfg, drop_remainder=True)),
                 ("sparse_blocks_G4_top16", dataclasses.replace(cfg, groups=4, top_groups=16, top_pages=0,
-                                                               drop_remainder=True)))
+                                                               drop_remainder=True)),
+                ("int4_three_tier", dataclasses.replace(cfg, int4_pages=True)))
     indexes = {}
-    for G in sorted({c.groups for _, c in variants}):
+    for G, q4 in sorted({(c.groups, c.int4_pages) for _, c in variants}):
         # every chunk the decode steps see; the timed region rebuilds the boundary chunk
-        indexes[G] = lod.LodIndex.allocate(dataclasses.replace(cfg, groups=G), 1, T + steps, device=dev)
-        lod.build_chunk(dataclasses.replace(cfg, groups=G), indexes[G], K, V, 0, nb0 + 1)
+        ic = dataclasses.replace(cfg, groups=G, int4_pages=q4)
+        indexes[(G, q4)] = lod.LodIndex.allocate(ic, 1, T + steps, device=dev)
+        lod.build_chunk(ic, indexes[(G, q4)], K, V, 0, nb0 + 1)
     torch.cuda.synchronize()
     res = {}
     outs = {}
     for name, c in variants:
-        idx = indexes[c.groups]
+        idx = indexes[(c.groups, c.int4_pages)]
         ws = torch.empty(lod.decode_ws_bytes(c, 1, T + steps), dtype=torch.uint8, device=dev)
         lens = torch.arange(T + 1, T + steps + 1, dtype=torch.int32, device=dev).view(steps, 1)
         out = torch.empty(steps, 64, 128, dtype=torch.float32, device=dev)
