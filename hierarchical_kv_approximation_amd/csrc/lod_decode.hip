@@ -1272,7 +1272,7 @@ template <int HG, bool DROP, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void decode_scan_mfma_kernel(DecodeArgs A) {
     __shared__ MScanSmem<HG> s;
-    const int kvh = blockIdx.y, b = blockIdx.z;  // b: query row
+    const int kvh = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;  // b: query row
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     int seq, p;
     row_info(A, b, seq, p);
@@ -1292,10 +1292,10 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     S.nex = S.ns + (p + 1 - S.w0);
     const int ntc = (S.ng + kSTile - 1) / kSTile;
     const int nt = ntc + (S.nex + kSTile - 1) / kSTile;
-    const int t0 = (int)((int64_t)nt * blockIdx.x / A.nslice);
-    const int t1 = (int)((int64_t)nt * (blockIdx.x + 1) / A.nslice);
+    const int t0 = (int)((int64_t)nt * slice / A.nslice);
+    const int t1 = (int)((int64_t)nt * (slice + 1) / A.nslice);
     const int hq0 = kvh * HG;
-    float* part0 = A.part + ((int64_t)(b * A.Hq + hq0) * A.nslot + blockIdx.x) * kPartStride;
+    float* part0 = A.part + ((int64_t)(b * A.Hq + hq0) * A.nslot + slice) * kPartStride;
     const int64_t head_stride = (int64_t)A.nslot * kPartStride;
     float* sdst = A.score + ((int64_t)b * A.Hq + hq0) * A.score_stride;
     const bf16_t* q0 = reinterpret_cast<const bf16_t*>(A.q) + ((int64_t)b * A.Hq + hq0) * kD;
@@ -1841,12 +1841,15 @@ static void launch_decode_view(const DecodeArgs& A, int rows, hipStream_t st) {
     trace_point(0, st);
     if constexpr (sizeof(T) == 2) {
         if (A.nslice + A.nwin > 0) {
+            // KV head fastest, then the row, then the slice: a unit's workgroups share
+            // an XCD (workgroups go to the 8 XCDs round robin), the one the open step's
+            // workgroups of that KV head use, and slices of one unit reach a CU at
+            // different times, so no unit as a whole starts last
+            const dim3 sg(A.Hkv, rows, A.nslice + A.nwin);
             if (A.drop)
-                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, true, PAGED>), dim3(A.nslice + A.nwin, A.Hkv, rows),
-                                   dim3(kThreads), 0, st, A);
+                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, true, PAGED>), sg, dim3(kThreads), 0, st, A);
             else
-                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, false, PAGED>), dim3(A.nslice + A.nwin, A.Hkv, rows),
-                                   dim3(kThreads), 0, st, A);
+                hipLaunchKernelGGL((decode_scan_mfma_kernel<HG, false, PAGED>), sg, dim3(kThreads), 0, st, A);
         }
         trace_point(1, st);
         // with INT4 pages the open step reads no cache rows, so the view does not matter
