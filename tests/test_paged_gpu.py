@@ -86,3 +86,26 @@ def test_paged_view_with_sparsity_ablation():
     sl = torch.tensor([T, 3001], dtype=torch.int32, device="cuda")
     assert torch.equal(lod.attend_decode(g, case.index, case.Kd, case.Vd, q, sl, T),
                        lod.attend_decode(g, case.index, Kp, Vp, q, sl, T, block_table=table))
+
+
+def test_paged_view_with_int4_pages():
+    """INT4 pages read no cache rows in the open step; the window and sinks still come
+    through the block table: paged and strided agree bit for bit."""
+    g = lod.Config(n_q_heads=16, n_kv_heads=2, groups=8, dtype=torch.bfloat16, int4_pages=True)
+    from oracle import oracle as orc
+    o = orc.Config(d=128, groups=8, bf16=True, int4_pages=True)
+    B, T = 2, 4096
+    case = Case(g, o, B, T, seed=78)
+    case.build_gpu()
+    Kp, Vp, table = _paged(case.Kd, case.Vd, 16, seed=79)
+    idx = lod.LodIndex.allocate(g, B, T, device="cuda")
+    lod.build_chunk(g, idx, Kp, Vp, 0, T // 256, block_table=table)
+    q = case.queries(seed=80).cuda()
+    sl = torch.tensor([T, 3333], dtype=torch.int32, device="cuda")
+    Q = case.queries(seed=81, n_rows=256).cuda()
+    torch.cuda.synchronize()
+    assert torch.equal(idx.mem, case.index.mem)
+    assert torch.equal(lod.attend_decode(g, case.index, case.Kd, case.Vd, q, sl, T),
+                       lod.attend_decode(g, idx, Kp, Vp, q, sl, T, block_table=table))
+    assert torch.equal(lod.attend_prefill(g, case.index, case.Kd, case.Vd, Q, T - 256),
+                       lod.attend_prefill(g, idx, Kp, Vp, Q, T - 256, block_table=table))
