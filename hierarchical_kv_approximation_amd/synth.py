@@ -94,3 +94,53 @@ def queries(B: int, Hq: int, centres: torch.Tensor, *, n_rows: int | None = None
     if n_rows is None:
         q, z = q[:, 0], z[:, 0]
     return (q, z) if return_centres else q
+
+
+def video_qkv(B: int, frames: int, height: int, width: int, Hq: int, Hkv: int, d: int = 128, *,
+              region=(8, 8, 8), n_centres: int = 32, sigma: float = 0.3, seed: int = 0,
+              kind: str = "matched", dtype=torch.bfloat16, device="cpu", zero_variance_block=None):
+    """Video tokens on a frames x height x width grid (raster order, T tokens).
+
+    Returns (Q [B][T][Hq][d], K, V [B][T][Hkv][d]) in ``dtype``.  The grid is tiled by
+    ``region`` boxes (clipped at the edges); every box of every (sequence, KV head)
+    draws one of ``n_centres`` N(0, I_d) centres, and its keys are that centre plus
+    sigma * N(0, I_d): nearby tokens look alike, as in video.  "matched" queries are
+    the centre of their own box plus the same noise; "diffuse" queries are N(0, I_d).
+    Values are N(0, I_d).  With ``zero_variance_block`` = (bf, bh, bw) every such
+    block's keys are one centre rounded to bfloat16 with no noise."""
+    gen = _gen(seed, device)
+    T = frames * height * width
+    g = Hq // Hkv
+    assert Hq % Hkv == 0
+    f = torch.arange(frames, device=device)[:, None, None]
+    y = torch.arange(height, device=device)[None, :, None]
+    x = torch.arange(width, device=device)[None, None, :]
+    box = region if zero_variance_block is None else zero_variance_block
+    ny, nx = -(-height // box[1]), -(-width // box[2])
+    rid = ((f // box[0]) * ny + y // box[1]) * nx + x // box[2]
+    rid = rid.reshape(T)
+    nreg = int(rid.max()) + 1
+    centres = torch.randn(B, Hkv, n_centres, d, generator=gen, device=device)
+    if zero_variance_block is not None:
+        centres = centres.to(torch.bfloat16).float()
+    z = torch.randint(0, n_centres, (B, Hkv, nreg), generator=gen, device=device)
+    K = torch.empty(B, T, Hkv, d, dtype=dtype, device=device)
+    V = torch.empty(B, T, Hkv, d, dtype=dtype, device=device)
+    Q = torch.empty(B, T, Hq, d, dtype=dtype, device=device)
+    for b in range(B):
+        for h in range(Hkv):
+            mu = centres[b, h][z[b, h][rid]]  # [T][d]
+            if zero_variance_block is None:
+                K[b, :, h] = (mu + sigma * torch.randn(T, d, generator=gen, device=device)).to(dtype)
+            else:
+                K[b, :, h] = mu.to(dtype)
+            V[b, :, h] = torch.randn(T, d, generator=gen, device=device).to(dtype)
+            for j in range(g):
+                if kind == "matched":
+                    q = mu + sigma * torch.randn(T, d, generator=gen, device=device)
+                elif kind == "diffuse":
+                    q = torch.randn(T, d, generator=gen, device=device)
+                else:
+                    raise ValueError(f"unknown query kind {kind!r}")
+                Q[b, :, h * g + j] = q.to(dtype)
+    return Q, K, V

@@ -23,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lod_oracle.c")
+_SRC_VIDEO = os.path.join(_HERE, "video_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblod_oracle.so")
 
 ORC_OK = 0
@@ -35,7 +36,7 @@ def build_library(force: bool = True) -> str:
     """Compile the oracle with gcc: no fast-math, no fp contraction."""
     if force or not os.path.exists(_LIB_PATH):
         cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+               "-fno-fast-math", "-o", _LIB_PATH + ".tmp", _SRC, _SRC_VIDEO, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
     return _LIB_PATH
