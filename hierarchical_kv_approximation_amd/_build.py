@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblod.so")
 
-SOURCES = ["lod_host.cpp", "lod_build.hip", "lod_decode.hip", "lod_prefill.hip"]
+SOURCES = ["lod_host.cpp", "lod_build.hip", "lod_decode.hip", "lod_prefill.hip", "lod_video.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -49,6 +49,17 @@ class Layout(ctypes.Structure):
         [("page_slots", ctypes.c_int32), ("meta_stride", ctypes.c_int32)]
 
 
+class VideoParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "head_dim", "n_q_heads", "n_kv_heads", "frames", "height", "width", "block_f", "block_h",
+        "block_w", "top_blocks", "kv_dtype", "drop_remainder")] + [("scale", ctypes.c_float)]
+
+
+class VideoLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("kbar", "vbar", "lnn", "qbar", "sel", "total")] + \
+        [("n_blocks", ctypes.c_int32)]
+
+
 class LodError(RuntimeError):
     def __init__(self, fn, status):
         super().__init__(f"{fn} failed: {lib().lod_status_string(status).decode()}")
@@ -81,10 +92,16 @@ def lib():
         L.lod_dense_decode.argtypes = [pp, KV, vp, vp, i32, i32, vp, vp, sz, vp]
         L.lod_dense_prefill.argtypes = [pp, KV, vp, i32, i32, i32, vp, vp]
         L.lod_trace_events.argtypes = [P(vp), i32]
+        vpp = P(VideoParams)
+        L.lod_video_layout.argtypes = [vpp, i32, P(VideoLayout)]
+        L.lod_video_ws_bytes.argtypes = [vpp, i32, P(sz)]
+        L.lod_video_attend.argtypes = [vpp, KV, vp, i32, vp, vp, vp, sz, vp]
+        L.lod_video_dense.argtypes = [vpp, KV, vp, i32, vp, vp]
         for fn in ("lod_index_bytes", "lod_index_layout", "lod_build_chunk", "lod_decode_ws_bytes",
                    "lod_attend_decode", "lod_prefill_ws_bytes", "lod_attend_prefill",
                    "lod_dense_decode_ws_bytes", "lod_dense_decode", "lod_dense_prefill",
-                   "lod_trace_events"):
+                   "lod_trace_events", "lod_video_layout", "lod_video_ws_bytes", "lod_video_attend",
+                   "lod_video_dense"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -334,3 +351,99 @@ def trace_events(events):
     arr = (ctypes.c_void_p * len(events))(*events)
     _check("lod_trace_events", lib().lod_trace_events(arr, len(events)))
     return arr  # caller keeps it alive while tracing
+
+
+# ---------------------------------------------------------------------------- video LoD
+
+@dataclass
+class VideoConfig:
+    """Video LoD: a frames x height x width token grid cut into 4x4x4 blocks, each query
+    block opening its top c = 16 key blocks."""
+    frames: int = 8
+    height: int = 8
+    width: int = 8
+    n_q_heads: int = 8
+    n_kv_heads: int = 8
+    block: tuple = (4, 4, 4)
+    top_blocks: int = 16
+    dtype: torch.dtype = torch.bfloat16
+    head_dim: int = 128
+    scale: float | None = None
+    drop_remainder: bool = False
+
+    def params(self) -> VideoParams:
+        sc = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+        dt = {torch.float32: LOD_F32, torch.bfloat16: LOD_BF16}.get(self.dtype, 99)
+        return VideoParams(self.head_dim, self.n_q_heads, self.n_kv_heads, self.frames, self.height,
+                           self.width, *self.block, self.top_blocks, dt, 1 if self.drop_remainder else 0, sc)
+
+    @property
+    def n_tokens(self) -> int:
+        return self.frames * self.height * self.width
+
+
+def video_layout(cfg: VideoConfig, batch: int) -> VideoLayout:
+    L = VideoLayout()
+    _check("lod_video_layout", lib().lod_video_layout(ctypes.byref(cfg.params()), batch, ctypes.byref(L)))
+    return L
+
+
+def video_ws_bytes(cfg: VideoConfig, batch: int) -> int:
+    n = ctypes.c_size_t()
+    _check("lod_video_ws_bytes", lib().lod_video_ws_bytes(ctypes.byref(cfg.params()), batch, ctypes.byref(n)))
+    return n.value
+
+
+def video_arrays(cfg: VideoConfig, ws: torch.Tensor, batch: int) -> dict:
+    """Views of the summaries and choice that lod_video_attend left in `ws`."""
+    L = video_layout(cfg, batch)
+    nb, d = L.n_blocks, cfg.head_dim
+
+    def view(off, n, dt):
+        es = torch.tensor([], dtype=dt).element_size()
+        return ws[off:off + n * es].view(dt)
+    return {
+        "kbar": view(L.kbar, batch * cfg.n_kv_heads * nb * d, torch.bfloat16).view(batch, cfg.n_kv_heads, nb, d),
+        "vbar": view(L.vbar, batch * cfg.n_kv_heads * nb * d, torch.bfloat16).view(batch, cfg.n_kv_heads, nb, d),
+        "lnn": view(L.lnn, nb, torch.float32),
+        "qbar": view(L.qbar, batch * cfg.n_q_heads * nb * d, torch.float32).view(batch, cfg.n_q_heads, nb, d),
+        "sel": view(L.sel, batch * cfg.n_q_heads * nb * cfg.top_blocks, torch.int32).view(
+            batch, cfg.n_q_heads, nb, cfg.top_blocks),
+    }
+
+
+def _video_shapes(cfg: VideoConfig, K, V, q):
+    B, T = q.shape[0], cfg.n_tokens
+    assert q.is_contiguous() and tuple(q.shape) == (B, T, cfg.n_q_heads, cfg.head_dim)
+    assert K.shape[0] == B and tuple(K.shape[1:]) == (T, cfg.n_kv_heads, cfg.head_dim)
+    assert q.dtype == K.dtype == V.dtype
+    return B
+
+
+def attend_video(cfg: VideoConfig, K, V, q, want_selection: bool = False, ws: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None):
+    """Video LoD attention.  q [B][T][Hq][d], K, V [B][T][Hkv][d] (bf16, T = frames*height*
+    width in raster order).  Returns (out [B][T][Hq][d] fp32, sel [B][Hq][NB][c] or None)."""
+    B = _video_shapes(cfg, K, V, q)
+    if out is None:
+        out = torch.empty(B, cfg.n_tokens, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(video_ws_bytes(cfg, B), dtype=torch.uint8, device=q.device)
+    sel = None
+    if want_selection:
+        nb = video_layout(cfg, B).n_blocks
+        sel = torch.empty(B, cfg.n_q_heads, nb, cfg.top_blocks, dtype=torch.int32, device=q.device)
+    _check("lod_video_attend", lib().lod_video_attend(
+        ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), B, _ptr(out), _ptr(sel), _ptr(ws), ws.numel(),
+        _stream()))
+    return out, sel
+
+
+def dense_video(cfg: VideoConfig, K, V, q, out: torch.Tensor | None = None):
+    """Dense bidirectional attention over the whole grid (the baseline), same layout."""
+    B = _video_shapes(cfg, K, V, q)
+    if out is None:
+        out = torch.empty(B, cfg.n_tokens, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+    _check("lod_video_dense", lib().lod_video_dense(
+        ctypes.byref(cfg.params()), kv_view(K, V), _ptr(q), B, _ptr(out), _stream()))
+    return out

@@ -260,6 +260,84 @@ int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_
                       int32_t n_q, int32_t batch, float* out, void* stream);
 
 /*
+ * Video LoD ("Level of Detail Attention", section "Video LoD"): the method carried over
+ * to video, whose tokens are local in space and time, with queries and keys/values
+ * handled in 4x4x4 blocks of the token grid and c = 16.  The section names only the
+ * block shape and c; the rest follows the text method ("How It Works") read this way:
+ *   - tokens sit on a frames x height x width grid, token t = (f*height + y)*width + x;
+ *     attention is bidirectional (every query sees every key; no window, no sinks);
+ *   - the grid is cut into block_f x block_h x block_w blocks, clipped at the far
+ *     edges; block ids run in raster order of the block coordinates, a block's members
+ *     in ascending token order.  A block plays the part of a group: it keeps its mean
+ *     key and value (fp32 sums in member order, correctly rounded divide, rounded to
+ *     nearest even to bf16) and ln(n) of its token count n;
+ *   - the queries of a block share one choice: their mean query (the same fp32 mean,
+ *     not rounded) scores every key block with the unscaled fp32 fma chain over the
+ *     head dimension in index order, and the top_blocks best (score descending, then
+ *     lower block id) open;
+ *   - each query's softmax holds scale*q.k for every member of the opened blocks and,
+ *     for every other block, one term scale*q.kbar + ln(n) with value vbar (its mean
+ *     key and value repeated n times); drop_remainder = 1 leaves those terms out.
+ * Supported: head_dim 128, kv_dtype LOD_BF16, block volume <= 64, 1 <= top_blocks <= 64,
+ * at most 15360 blocks, n_q_heads a multiple of n_kv_heads (query head h reads KV head
+ * h / (n_q_heads / n_kv_heads)); anything else valid returns LOD_ERR_UNSUPPORTED.
+ */
+typedef struct {
+    int32_t head_dim;
+    int32_t n_q_heads, n_kv_heads;
+    int32_t frames, height, width;        /* token grid */
+    int32_t block_f, block_h, block_w;    /* block extents along frames, rows, columns */
+    int32_t top_blocks;                   /* c: key blocks each query block opens */
+    int32_t kv_dtype;                     /* element type of q, K and V (LOD_BF16) */
+    int32_t drop_remainder;               /* 0 or 1 (sparsity ablation) */
+    float scale;                          /* softmax scale, usually 1/sqrt(head_dim) */
+} lod_video_params;
+
+/*
+ * Byte offsets of the arrays in the workspace of lod_video_attend (NB blocks, d =
+ * head_dim, B = batch); every array is 256-byte aligned.  They hold the last call's
+ * summaries and choice, so tests can read them back:
+ *   kbar, vbar  [B][n_kv_heads][NB][d] bf16   block mean key / value
+ *   lnn         [NB]                   f32    ln(token count) of each block
+ *   qbar        [B][n_q_heads][NB][d]  f32    block mean query
+ *   sel         [B][n_q_heads][NB][top_blocks] int32  opened key blocks of each query
+ *               block, ascending, -1 padding when NB < top_blocks
+ */
+typedef struct {
+    size_t kbar, vbar, lnn, qbar, sel, total;
+    int32_t n_blocks;
+} lod_video_layout_t;
+
+/* Host-only: workspace layout of lod_video_attend for `batch` sequences. */
+int lod_video_layout(const lod_video_params* params, int32_t batch, lod_video_layout_t* layout);
+
+/* Host-only: workspace bytes of lod_video_attend (layout.total). */
+int lod_video_ws_bytes(const lod_video_params* params, int32_t batch, size_t* bytes);
+
+/*
+ * Video LoD attention of every token of `batch` token grids: summaries, choice and
+ * softmax as described above, in one call.
+ *   kv          strided view of K and V (block_table must be NULL: LOD_ERR_UNSUPPORTED
+ *               otherwise); position t of the view is token t of the grid
+ *   q           [batch][T][n_q_heads][head_dim] bf16, T = frames*height*width,
+ *               16-byte aligned
+ *   out         [batch][T][n_q_heads][head_dim] fp32
+ *   sel_blocks  nullable [batch][n_q_heads][NB][top_blocks] int32: a copy of `sel`
+ *   ws          workspace of at least lod_video_ws_bytes bytes, 16-byte aligned;
+ *               LOD_ERR_WORKSPACE when smaller
+ */
+int lod_video_attend(const lod_video_params* params, lod_kv kv, const void* q, int32_t batch,
+                     float* out, int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense bidirectional softmax attention of every token over all T keys: the baseline
+ * video LoD is measured against.  Same q, kv and out layout as lod_video_attend; uses
+ * the grid, head counts, head_dim, kv_dtype and scale of params.  No workspace.
+ */
+int lod_video_dense(const lod_video_params* params, lod_kv kv, const void* q, int32_t batch,
+                    float* out, void* stream);
+
+/*
  * Instrumentation (profiling only; results are unchanged).  While `events` is non-null,
  * every later lod_attend_decode / lod_attend_prefill call made from the same host thread
  * records events[0] on its stream before its first kernel and events[1 + k] after its
