@@ -185,204 +185,279 @@ __global__ __launch_bounds__(kThreads) void video_select_kernel(VideoArgs A) {
 
 // ---------------------------------------------------------------------------- attend
 
+// A workgroup takes two neighbouring query blocks (raster order) of one query head;
+// wave w serves query block w / 2, columns 32 (w % 2) .. +31 (two 16-column MFMA
+// blocks).  Its key tiles are the union of the two blocks' opened blocks, then the mean
+// keys of all blocks; a wave skips the exact tiles its own block did not open, and the
+// coarse tiles mask its own opened blocks.  K and V tiles are double buffered and
+// loaded straight into LDS; both are row-major with 16-byte chunks XOR-swizzled (K by
+// row & 15, V by 2 (row & 7)), and V^T operands come from transposing LDS reads.
+constexpr int kVideoPair = 2;  // query blocks per attend workgroup
+
 struct VideoSmem {
-    alignas(16) bf16_t kt[kFlashKeys][kD];      // key tile, 16-byte chunks XOR-swizzled
-    alignas(16) bf16_t vT[kD][kFlashKeys + 4];  // value tile, transposed
-    float bias[kFlashKeys];
-    int sel[kVideoMaxTop];
-    uint32_t opened[kVideoMaxBlocks / 32];      // bitmap of the opened key blocks
+    alignas(16) bf16_t kt[2][kFlashKeys][kD];  // key tiles (double buffer)
+    alignas(16) bf16_t vt[2][kFlashKeys][kD];  // value tiles (double buffer)
+    float bias[2][kVideoPair][kFlashKeys];     // [buffer][query block of the pair][key slot]
+    int tl[kVideoPair * kVideoMaxTop];         // exact tiles: block ids, ascending
+    int tmask[kVideoPair * kVideoMaxTop];      // bit q: query block q of the pair opened it
+    int sl[kVideoPair][kVideoMaxTop];          // each block's opened list
+    uint32_t opened[kVideoPair][kVideoMaxBlocks / 32];
+    int slot_off[kVideoSlots];                 // token offset of a member slot from the block origin
+    int slot_ijk[kVideoSlots];                 // its (frame, row, column) offsets, 8 bits each
+    int nex;
 };
 
-struct VideoState {
-    f32x4_t O[8];  // O^T, one 16 x 16 tile per d block
-    float m, l;
-};
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 7); }
 
-// One tile of 64 key slots: rows krow(r), vrow(r) (always readable addresses), bias
-// bias_of(r) (-inf: no key).  Column = this lane's query slot (16 w + l % 16).
-template <typename KRow, typename VRow, typename Bias>
-__device__ __forceinline__ void video_tile(VideoSmem& s, VideoState& F, const bf16x8_t* qf, KRow krow, VRow vrow,
-                                           Bias bias_of, float scale) {
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    for (int i = w; i < kFlashKeys / 4; i += 4) {
-        const int row = 4 * i + (l >> 4);
-        const int cp = l & 15, c = cp ^ (row & 15);
-        __builtin_amdgcn_global_load_lds(krow(row) + 8 * c, &s.kt[4 * i][0], 16, 0, 0);
-    }
-    uint4 vv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + kThreads * i, key = idx & 63, ch = idx >> 6;
-        vv[i] = *reinterpret_cast<const uint4*>(vrow(key) + 8 * ch);
-    }
-    if (tid < kFlashKeys) s.bias[tid] = bias_of(tid);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + kThreads * i, key = idx & 63, ch = idx >> 6;
-        const uint32_t u[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s.vT[8 * ch + 2 * e][key] = (bf16_t)(u[e] & 0xffffu);
-            s.vT[8 * ch + 2 * e + 1][key] = (bf16_t)(u[e] >> 16);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-    // S^T = K Q^T: 4 key blocks of 16 for this wave's 16 columns
-    f32x4_t S[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        S[kb] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int row = 16 * kb + (l & 15);
-            const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
-            S[kb] = mfma16(a, qf[kk], S[kb]);
-        }
-    }
-    // logits and the online softmax (a column's 64 keys live in lanes l, l^16, l^32, l^48)
-    float P[4][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float b = s.bias[16 * kb + 4 * (l >> 4) + r];
-            const float lam = b != -INFINITY ? __builtin_fmaf(scale, S[kb][r], b) : -INFINITY;
-            P[kb][r] = lam;
-            mt = fmaxf(mt, lam);
-        }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(F.m, mt);
-    const float a = F.m == -INFINITY ? 0.0f : softmax_exp(F.m - mn);
-    float ls = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float lam = P[kb][r];
-            const float p = lam == -INFINITY ? 0.0f : softmax_exp(lam - mn);
-            P[kb][r] = p;
-            ls += p;
-        }
-    F.l = __builtin_fmaf(F.l, a, ls);
-    F.m = mn;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) F.O[db] *= a;
-    // O^T += V^T P^T over two 32-key steps; P as bf16 hi + lo
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        bf16x8_t ph, pl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __bf16 h, lo;
-            split_bf16(P[2 * st + j / 4][j % 4], h, lo);
-            ph[j] = h;
-            pl[j] = lo;
-        }
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const bf16_t* vr = &s.vT[16 * db + (l & 15)][32 * st + 4 * (l >> 4)];
-            const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
-            const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 16);
-            const u32x4_t raw = {lo4.x, lo4.y, hi4.x, hi4.y};  // keys 8 (l/16) .. +7 of the step
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, raw);
-            F.O[db] = mfma16(av, ph, F.O[db]);
-            F.O[db] = mfma16(av, pl, F.O[db]);
-        }
-    }
-    __syncthreads();
+// 4 bf16 of a V^T operand: this lane gets V[key0 + r][d0 + lane % 16] for r = 0..3,
+// where the 16 lanes of its group read (row key0 + i / 4, elements d0 + 4 (i % 4) ..).
+__device__ __forceinline__ s16x4_t vt_read(const bf16_t (*vt)[kD], int key0, int d0, int i) {
+    const int row = key0 + (i >> 2);
+    const int e = d0 + 4 * (i & 3);
+    const int chunk = (e >> 3) ^ swz_v(row);
+    const bf16_t* p = &vt[row][8 * chunk + (e & 7)];
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
 }
 
-// grid (NB, Hq, B): the 64 query slots of query block blockIdx.x of query head
-// blockIdx.y.  LoD: the opened blocks' members, then the mean keys of the other blocks
-// with bias ln n.  DENSE: every key of the grid in tiles of 64 consecutive tokens.
 template <bool DENSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void video_attend_kernel(VideoArgs A) {
     __shared__ VideoSmem s;
-    const int qb = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int pair = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
     const int kvh = hq / (A.Hq / A.Hkv);
-    const int qt = video_token(A, qb, 16 * w + (l & 15));
-    bf16x8_t qf[4];
-    {
-        const bf16_t* qr = A.q + (((int64_t)b * A.T + (qt < 0 ? 0 : qt)) * A.Hq + hq) * kD;
+    const int qb0 = kVideoPair * pair;
+    const int nqb = min(kVideoPair, A.NB - qb0);
+    const int qi = w >> 1;  // query block of this wave within the pair
+    const bool on = qi < nqb;
+    const int qb = qb0 + min(qi, nqb - 1);
+
+    if (tid < kVideoSlots) {
+        const int m = tid;
+        const int i = m / (A.bh * A.bw), j = (m / A.bw) % A.bh, k = m % A.bw;
+        s.slot_off[m] = (i * A.H + j) * A.W + k;
+        s.slot_ijk[m] = m < A.bsz ? (i | (j << 8) | (k << 16)) : -1;
+    }
+    // Q^T operands of this lane's two columns
+    bf16x8_t qf[2][4];
+    int qt[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        qt[cb] = on ? video_token(A, qb, 32 * (w & 1) + 16 * cb + li) : -1;
+        const bf16_t* qr = A.q + (((int64_t)b * A.T + (qt[cb] < 0 ? 0 : qt[cb])) * A.Hq + hq) * kD;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            qf[kk] = qt < 0 ? zero_bf16x8() : *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * (l >> 4));
+            qf[cb][kk] = qt[cb] < 0 ? zero_bf16x8() : *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
     }
-    VideoState F;
-    F.m = -INFINITY;
-    F.l = 0.0f;
+    f32x4_t O[2][8];
+    float m_run[2], l_run[2];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) F.O[db] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int cb = 0; cb < 2; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
+    }
     const bf16_t* kc = A.k + (int64_t)b * A.sb + (int64_t)kvh * A.sh;
     const bf16_t* vc = A.v + (int64_t)b * A.sb + (int64_t)kvh * A.sh;
+    const bf16_t* kbr = A.kbar + ((int64_t)b * A.Hkv + kvh) * A.NB * kD;
+    const bf16_t* vbr = A.vbar + ((int64_t)b * A.Hkv + kvh) * A.NB * kD;
 
-    if (DENSE) {
-        for (int k0 = 0; k0 < A.T; k0 += kFlashKeys) {
-            const int nk = min(kFlashKeys, A.T - k0);
-            video_tile(
-                s, F, qf, [&](int r) { return kc + (int64_t)(k0 + min(r, nk - 1)) * A.st; },
-                [&](int r) { return vc + (int64_t)(k0 + min(r, nk - 1)) * A.st; },
-                [&](int r) { return r < nk ? 0.0f : -INFINITY; }, A.scale);
-        }
-    } else {
-        const int32_t* selr = A.sel + (((int64_t)b * A.Hq + hq) * A.NB + qb) * A.c;
-        for (int i = tid; i < (A.NB + 31) / 32; i += kThreads) s.opened[i] = 0;
+    int nex = 0;
+    if (!DENSE) {
+        for (int i = tid; i < kVideoPair * (kVideoMaxBlocks / 32); i += kThreads) (&s.opened[0][0])[i] = 0;
         __syncthreads();
-        if (tid < A.c) {
-            const int j = selr[tid];
-            s.sel[tid] = j;
-            if (j >= 0) atomicOr(&s.opened[j >> 5], 1u << (j & 31));
+        if (tid < kVideoPair * A.c) {
+            const int q = tid / A.c, u = tid % A.c;
+            const int j = q < nqb ? A.sel[(((int64_t)b * A.Hq + hq) * A.NB + qb0 + q) * A.c + u] : -1;
+            s.sl[q][u] = j;
+            if (j >= 0) atomicOr(&s.opened[q][j >> 5], 1u << (j & 31));
         }
         __syncthreads();
-        // exact: the members of each opened block (ascending ids, -1 padding last)
-        for (int u = 0; u < A.c; ++u) {
-            const int j = s.sel[u];
-            if (j < 0) break;
-            const int t0 = video_token(A, j, 0);  // slot 0 always lies in the grid
-            auto tok = [&](int r) {
-                const int t = video_token(A, j, r);
-                return t < 0 ? t0 : t;
+        if (tid == 0) {  // merge the two ascending lists (-1 padding last)
+            int ia = 0, ib = 0, n = 0;
+            const int* sa = s.sl[0];
+            const int* sb2 = s.sl[1];
+            auto len = [&](const int* x) {
+                int c = 0;
+                while (c < A.c && x[c] >= 0) ++c;
+                return c;
             };
-            video_tile(
-                s, F, qf, [&](int r) { return kc + (int64_t)tok(r) * A.st; },
-                [&](int r) { return vc + (int64_t)tok(r) * A.st; },
-                [&](int r) { return video_token(A, j, r) < 0 ? -INFINITY : 0.0f; }, A.scale);
+            const int na = len(sa), nb = nqb > 1 ? len(sb2) : 0;
+            while (ia < na || ib < nb) {
+                int x, mk;
+                if (ib >= nb || (ia < na && sa[ia] < sb2[ib])) { x = sa[ia++]; mk = 1; }
+                else if (ia >= na || sb2[ib] < sa[ia]) { x = sb2[ib++]; mk = 2; }
+                else { x = sa[ia]; ++ia; ++ib; mk = 3; }
+                s.tl[n] = x;
+                s.tmask[n] = mk;
+                ++n;
+            }
+            s.nex = n;
         }
-        // coarse: every other block's mean key and value with bias ln n
-        if (!A.drop) {
-            const bf16_t* kb = A.kbar + ((int64_t)b * A.Hkv + kvh) * A.NB * kD;
-            const bf16_t* vb = A.vbar + ((int64_t)b * A.Hkv + kvh) * A.NB * kD;
-            for (int j0 = 0; j0 < A.NB; j0 += kFlashKeys) {
-                video_tile(
-                    s, F, qf, [&](int r) { return kb + (int64_t)min(j0 + r, A.NB - 1) * kD; },
-                    [&](int r) { return vb + (int64_t)min(j0 + r, A.NB - 1) * kD; },
-                    [&](int r) {
-                        const int j = j0 + r;
-                        return (j < A.NB && !((s.opened[j >> 5] >> (j & 31)) & 1u)) ? A.lnn[j] : -INFINITY;
-                    },
-                    A.scale);
+        __syncthreads();
+        nex = s.nex;
+    }
+    const int ntc = DENSE || A.drop ? 0 : (A.NB + kFlashKeys - 1) / kFlashKeys;
+    const int nt = DENSE ? (A.T + kFlashKeys - 1) / kFlashKeys : nex + ntc;
+
+    // Load tile t into buffer `buf`: K and V rows straight to LDS, and the two bias rows.
+    auto issue = [&](int t, int buf) {
+        const bf16_t* kbase;
+        const bf16_t* vbase;
+        int64_t stride;
+        int origin = 0, lf = 0, lh = 0, lw = 0, blk0 = 0, nk = 0;
+        const int kind = DENSE ? 0 : (t < nex ? 1 : 2);  // 0 dense run, 1 opened block, 2 coarse
+        if (kind == 0) {
+            kbase = kc; vbase = vc; stride = A.st;
+            blk0 = t * kFlashKeys;
+            nk = min(kFlashKeys, A.T - blk0);
+        } else if (kind == 1) {
+            kbase = kc; vbase = vc; stride = A.st;
+            const int j = s.tl[t];
+            const int bfi = j / (A.nby * A.nbx), byi = (j / A.nbx) % A.nby, bxi = j % A.nbx;
+            origin = ((bfi * A.bf) * A.H + byi * A.bh) * A.W + bxi * A.bw;
+            lf = min(A.bf, A.F - bfi * A.bf);
+            lh = min(A.bh, A.H - byi * A.bh);
+            lw = min(A.bw, A.W - bxi * A.bw);
+        } else {
+            kbase = kbr; vbase = vbr; stride = kD;
+            blk0 = (t - nex) * kFlashKeys;
+            nk = min(kFlashKeys, A.NB - blk0);
+        }
+        // row r of the tile -> element offset of its K / V row; valid flag
+        auto row_of = [&](int r, bool& ok) -> int64_t {
+            if (kind == 1) {
+                const int ijk = s.slot_ijk[r];
+                ok = ijk >= 0 && (ijk & 255) < lf && ((ijk >> 8) & 255) < lh && (ijk >> 16) < lw;
+                return (int64_t)(ok ? origin + s.slot_off[r] : origin) * stride;
+            }
+            ok = r < nk;
+            return (int64_t)(blk0 + (ok ? r : nk - 1)) * stride;
+        };
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = w + 4 * ii;
+            const int row = 4 * i + g;
+            bool ok;
+            const int64_t off = row_of(row, ok);
+            __builtin_amdgcn_global_load_lds(kbase + off + 8 * (li ^ swz_k(row)), &s.kt[buf][4 * i][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + off + 8 * (li ^ swz_v(row)), &s.vt[buf][4 * i][0], 16, 0, 0);
+        }
+        if (tid < kVideoPair * kFlashKeys) {
+            const int q = tid >> 6, r = tid & 63;
+            bool ok;
+            (void)row_of(r, ok);
+            float bv = -INFINITY;
+            if (kind == 0) bv = ok ? 0.0f : -INFINITY;
+            else if (kind == 1) bv = ok && ((s.tmask[t] >> q) & 1) ? 0.0f : -INFINITY;
+            else if (ok && !((s.opened[q][(blk0 + r) >> 5] >> ((blk0 + r) & 31)) & 1u)) bv = A.lnn[blk0 + r];
+            s.bias[buf][q][r] = bv;
+        }
+    };
+
+    if (nt > 0) issue(0, 0);
+    for (int t = 0; t < nt; ++t) {
+        const int buf = t & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 < nt) issue(t + 1, buf ^ 1);
+        const bool use = on && (DENSE || t >= nex || ((s.tmask[t] >> qi) & 1));
+        if (!use) continue;
+        // S^T = K Q^T: 4 key blocks x 2 column blocks
+        f32x4_t S[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
+            S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int row = 16 * kb + li;
+                const int chunk = (4 * kk + g) ^ swz_k(row);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[buf][row][8 * chunk]);
+                S[kb][0] = mfma16(a, qf[0][kk], S[kb][0]);
+                S[kb][1] = mfma16(a, qf[1][kk], S[kb][1]);
+            }
+        }
+        // logits and the online softmax (a column's 64 keys live in lanes l, l^16, l^32, l^48)
+        const float* bias = s.bias[buf][qi];
+        float P[4][2][4];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float bv = bias[16 * kb + 4 * g + r];
+                    const float lam = bv != -INFINITY ? __builtin_fmaf(A.scale, S[kb][cb][r], bv) : -INFINITY;
+                    P[kb][cb][r] = lam;
+                    mt = fmaxf(mt, lam);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mn = fmaxf(m_run[cb], mt);
+            const float a = m_run[cb] == -INFINITY ? 0.0f : softmax_exp(m_run[cb] - mn);
+            float ls = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float lam = P[kb][cb][r];
+                    const float p = lam == -INFINITY ? 0.0f : softmax_exp(lam - mn);
+                    P[kb][cb][r] = p;
+                    ls += p;
+                }
+            l_run[cb] = __builtin_fmaf(l_run[cb], a, ls);
+            m_run[cb] = mn;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) O[cb][db] *= a;
+        }
+        // O^T += V^T P^T over two 32-key steps.  MFMA k index e of lane group g is key
+        // 32 st + 16 (e / 4) + 4 g + e % 4 on both operands; P as bf16 hi + lo.
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8_t ph[2], pl[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    __bf16 h, lo;
+                    split_bf16(P[2 * st + j / 4][cb][j % 4], h, lo);
+                    ph[cb][j] = h;
+                    pl[cb][j] = lo;
+                }
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const s16x4_t v0 = vt_read(s.vt[buf], 32 * st + 4 * g, 16 * db, li);
+                const s16x4_t v1 = vt_read(s.vt[buf], 32 * st + 16 + 4 * g, 16 * db, li);
+                const s16x4_t both[2] = {v0, v1};
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    O[cb][db] = mfma16(av, ph[cb], O[cb][db]);
+                    O[cb][db] = mfma16(av, pl[cb], O[cb][db]);
+                }
             }
         }
     }
-    // column total (the 4 lanes of a column hold partial sums), then write
-    float lt = F.l;
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (qt < 0) return;
-    float* dst = A.out + (((int64_t)b * A.T + qt) * A.Hq + hq) * kD;
-    const float inv = 1.0f / lt;
+    // column totals (the 4 lanes of a column hold partial sums), then write
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const f32x4_t o = F.O[db];
-        *reinterpret_cast<float4*>(dst + 16 * db + 4 * (l >> 4)) =
-            make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+    for (int cb = 0; cb < 2; ++cb) {
+        float lt = l_run[cb];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        if (qt[cb] < 0) continue;
+        float* dst = A.out + (((int64_t)b * A.T + qt[cb]) * A.Hq + hq) * kD;
+        const float inv = 1.0f / lt;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const f32x4_t o = O[cb][db];
+            *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+        }
     }
 }
 
@@ -505,7 +580,8 @@ extern "C" int lod_video_attend(const lod_video_params* params, lod_kv kv, const
     if ((size_t)4 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<4>(A, batch, st);
     else if ((size_t)2 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<2>(A, batch, st);
     else launch_video_select<1>(A, batch, st);
-    hipLaunchKernelGGL((video_attend_kernel<false>), dim3(A.NB, A.Hq, batch), dim3(kThreads), 0, st, A);
+    hipLaunchKernelGGL((video_attend_kernel<false>), dim3((unsigned)ceil_div(A.NB, kVideoPair), A.Hq, batch),
+                       dim3(kThreads), 0, st, A);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
 
@@ -518,6 +594,7 @@ extern "C" int lod_video_dense(const lod_video_params* params, lod_kv kv, const 
     if (rc != LOD_OK) return rc;
     VideoArgs A = video_args(params, kv, q, out);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL((video_attend_kernel<true>), dim3(A.NB, A.Hq, batch), dim3(kThreads), 0, st, A);
+    hipLaunchKernelGGL((video_attend_kernel<true>), dim3((unsigned)ceil_div(A.NB, kVideoPair), A.Hq, batch),
+                       dim3(kThreads), 0, st, A);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
