@@ -25,9 +25,9 @@
 namespace lodi {
 
 constexpr int kVideoSlots = 64;          // member slots of a block (volume <= 64)
-constexpr int kVideoMaxBlocks = 15360;   // blocks of a grid, at most
+constexpr int kVideoMaxBlocks = 14336;   // blocks of a grid, at most
 constexpr int kVideoMaxTop = 64;         // opened blocks per query block, at most
-constexpr int kVideoScoreLds = 61440;    // bytes of select scores per workgroup, at most
+constexpr int kVideoScoreLds = 57344;    // bytes of select scores per workgroup (with the static arrays, under 64 KB)
 constexpr uint32_t kTakenBits = 0x7fffffffu;  // marks a chosen score (a NaN no chain makes)
 
 struct VideoArgs {
@@ -60,24 +60,26 @@ __device__ __forceinline__ int video_token(const VideoArgs& A, int blk, int m) {
 
 // ---------------------------------------------------------------------------- summary
 
-// grid (NB, Hkv + Hq, B).  y < Hkv: mean key and value of KV head y; else the mean
-// query of query head y - Hkv.  Rows are staged with 16-byte loads, then thread
-// (tensor, column) sums its column over the members in slot order, which is ascending
-// token order.
+// grid (Hkv + ceil(Hq / 2), NB, B): unit x < Hkv averages the keys and values of KV
+// head x; a later unit averages the queries of two query heads.  Units of one block run
+// next to each other, so neighbouring workgroups read neighbouring rows.  Rows are
+// staged with 16-byte loads, then thread (tensor, column) sums its column over the
+// members in slot order, which is ascending token order.
 __global__ __launch_bounds__(kThreads) void video_summary_kernel(VideoArgs A) {
     __shared__ alignas(16) bf16_t rows[2][kVideoSlots][kD];
     __shared__ int tok[kVideoSlots];
-    const int blk = blockIdx.x, hh = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const bool isq = hh >= A.Hkv;
+    const int u = blockIdx.x, blk = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const bool isq = u >= A.Hkv;
+    const int h0 = isq ? 2 * (u - A.Hkv) : u;          // first head of the unit
+    const int ntens = isq ? min(2, A.Hq - h0) : 2;      // tensors of the unit
     if (tid < kVideoSlots) tok[tid] = video_token(A, blk, tid);
     __syncthreads();
-    const int ntens = isq ? 1 : 2;
     for (int i = tid; i < ntens * kVideoSlots * (kD / 8); i += kThreads) {
         const int tsr = i / (kVideoSlots * (kD / 8)), m = (i / (kD / 8)) % kVideoSlots, ch = i % (kD / 8);
         const int t = tok[m];
         if (t < 0) continue;
-        const bf16_t* src = isq ? A.q + (((int64_t)b * A.T + t) * A.Hq + (hh - A.Hkv)) * kD
-                                : (tsr ? A.v : A.k) + (int64_t)b * A.sb + (int64_t)t * A.st + (int64_t)hh * A.sh;
+        const bf16_t* src = isq ? A.q + (((int64_t)b * A.T + t) * A.Hq + h0 + tsr) * kD
+                                : (tsr ? A.v : A.k) + (int64_t)b * A.sb + (int64_t)t * A.st + (int64_t)h0 * A.sh;
         *reinterpret_cast<uint4*>(&rows[tsr][m][8 * ch]) = *reinterpret_cast<const uint4*>(src + 8 * ch);
     }
     __syncthreads();
@@ -92,18 +94,18 @@ __global__ __launch_bounds__(kThreads) void video_summary_kernel(VideoArgs A) {
     }
     const float mean = s / (float)n;  // every block holds its slot 0
     if (isq) {
-        A.qbar[(((int64_t)b * A.Hq + (hh - A.Hkv)) * A.NB + blk) * kD + col] = mean;
+        A.qbar[(((int64_t)b * A.Hq + h0 + tsr) * A.NB + blk) * kD + col] = mean;
     } else {
         bf16_t* dst = tsr ? A.vbar : A.kbar;
-        dst[(((int64_t)b * A.Hkv + hh) * A.NB + blk) * kD + col] = f32_to_bf16_rne(mean);
-        if (b == 0 && hh == 0 && tid == 0) A.lnn[blk] = logf((float)n);
+        dst[(((int64_t)b * A.Hkv + h0) * A.NB + blk) * kD + col] = f32_to_bf16_rne(mean);
+        if (b == 0 && u == 0 && tid == 0) A.lnn[blk] = logf((float)n);
     }
 }
 
 // ---------------------------------------------------------------------------- select
 
 // grid (ceil(NB / QPW), Hq, B), dynamic LDS QPW * NB floats.  Query blocks
-// QPW*x .. QPW*x + QPW-1; wave w < QPW ranks the scores of query block QPW*x + w.
+// QPW*x .. QPW*x + QPW-1 share every mean key the workgroup loads.
 template <int QPW>
 __global__ __launch_bounds__(kThreads) void video_select_kernel(VideoArgs A) {
     extern __shared__ float sc[];  // [QPW][NB]
@@ -140,46 +142,49 @@ __global__ __launch_bounds__(kThreads) void video_select_kernel(VideoArgs A) {
         for (int qi = 0; qi < QPW; ++qi) sc[qi * A.NB + j] = acc[qi];
     }
     __syncthreads();
-    if (w >= QPW) return;
-    const int qb = qb0 + w;
-    if (qb >= A.NB) return;
-    float* s = sc + w * A.NB;
+    // wave w ranks query blocks QPW*x + w, + w + 4, ...: each lane keeps the best key of
+    // its entries j = l, l + 64, ...; the wave takes the best of all lanes k times, and
+    // the owner of each winner marks it and rescans
     const int k = min(A.c, A.NB);
-    // each lane keeps the best key of its entries j = l, l + 64, ...; the wave takes the
-    // best of all lanes k times, and the owner of each winner marks it and rescans
-    auto best_of = [&]() {
-        uint64_t bk = 0;
-        for (int j = l; j < A.NB; j += 64) {
-            const float x = s[j];
-            if (__float_as_uint(x) == kTakenBits) continue;
-            const uint64_t key = rank_key(x, (uint32_t)j);
-            bk = key > bk ? key : bk;
+    for (int qq = w; qq < QPW; qq += 4) {
+        const int qb = qb0 + qq;
+        if (qb >= A.NB) break;
+        float* s = sc + qq * A.NB;
+        auto best_of = [&]() {
+            uint64_t bk = 0;
+            for (int j = l; j < A.NB; j += 64) {
+                const float x = s[j];
+                if (__float_as_uint(x) == kTakenBits) continue;
+                const uint64_t key = rank_key(x, (uint32_t)j);
+                bk = key > bk ? key : bk;
+            }
+            return bk;
+        };
+        uint64_t mine = best_of();
+        int wsel = -1;
+        for (int r = 0; r < k; ++r) {
+            const uint64_t top = wave_max_u64(mine);
+            const int j = (int)key_id(top);
+            if (l == r) wsel = j;
+            if ((j & 63) == l) {
+                s[j] = __uint_as_float(kTakenBits);
+                mine = best_of();
+            }
         }
-        return bk;
-    };
-    uint64_t mine = best_of();
-    int wsel = -1;
-    for (int r = 0; r < k; ++r) {
-        const uint64_t top = wave_max_u64(mine);
-        const int j = (int)key_id(top);
-        if (l == r) wsel = j;
-        if ((j & 63) == l) {
-            s[j] = __uint_as_float(kTakenBits);
-            mine = best_of();
+        win[w][l] = wsel;
+        wave_sync_lds();
+        if (l < A.c) {
+            const int64_t o = (((int64_t)b * A.Hq + hq) * A.NB + qb) * A.c;
+            int pos = l, val = -1;
+            if (l < k) {
+                pos = 0;
+                for (int i = 0; i < k; ++i) pos += win[w][i] < wsel;
+                val = wsel;
+            }
+            A.sel[o + pos] = val;
+            if (A.sel_out) A.sel_out[o + pos] = val;
         }
-    }
-    win[w][l] = wsel;
-    wave_sync_lds();
-    if (l < A.c) {
-        const int64_t o = (((int64_t)b * A.Hq + hq) * A.NB + qb) * A.c;
-        int pos = l, val = -1;
-        if (l < k) {
-            pos = 0;
-            for (int i = 0; i < k; ++i) pos += win[w][i] < wsel;
-            val = wsel;
-        }
-        A.sel[o + pos] = val;
-        if (A.sel_out) A.sel_out[o + pos] = val;
+        wave_sync_lds();  // win[w] is rewritten by the next query block
     }
 }
 
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void video_select_kernel(VideoArgs A) {
 // loaded straight into LDS; both are row-major with 16-byte chunks XOR-swizzled (K by
 // row & 15, V by 2 (row & 7)), and V^T operands come from transposing LDS reads.
 constexpr int kVideoPair = 2;  // query blocks per attend workgroup
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct VideoSmem {
     alignas(16) bf16_t kt[2][kFlashKeys][kD];  // key tiles (double buffer)
@@ -202,8 +208,7 @@ struct VideoSmem {
     int tmask[kVideoPair * kVideoMaxTop];      // bit q: query block q of the pair opened it
     int sl[kVideoPair][kVideoMaxTop];          // each block's opened list
     uint32_t opened[kVideoPair][kVideoMaxBlocks / 32];
-    int slot_off[kVideoSlots];                 // token offset of a member slot from the block origin
-    int slot_ijk[kVideoSlots];                 // its (frame, row, column) offsets, 8 bits each
+    int tdesc[kVideoPair * kVideoMaxTop][2];   // exact tiles: block origin token, clipped extents
     int nex;
 };
 
@@ -235,11 +240,18 @@ void video_attend_kernel(VideoArgs A) {
     const bool on = qi < nqb;
     const int qb = qb0 + min(qi, nqb - 1);
 
-    if (tid < kVideoSlots) {
-        const int m = tid;
+    // member slots of the tile rows this thread loads (rows 4 (w + 4 ii) + g) and of its
+    // bias entry (row l): token offset from the block origin and (frame, row, column)
+    // offsets; a slot beyond the block volume gets offsets no block reaches
+    int soff[5], si[5], sj[5], sk[5];
+#pragma unroll
+    for (int ii = 0; ii < 5; ++ii) {
+        const int m = ii < 4 ? 4 * (w + 4 * ii) + g : l;
         const int i = m / (A.bh * A.bw), j = (m / A.bw) % A.bh, k = m % A.bw;
-        s.slot_off[m] = (i * A.H + j) * A.W + k;
-        s.slot_ijk[m] = m < A.bsz ? (i | (j << 8) | (k << 16)) : -1;
+        soff[ii] = (i * A.H + j) * A.W + k;
+        si[ii] = m < A.bsz ? i : 1 << 20;
+        sj[ii] = j;
+        sk[ii] = k;
     }
     // Q^T operands of this lane's two columns
     bf16x8_t qf[2][4];
@@ -265,6 +277,7 @@ void video_attend_kernel(VideoArgs A) {
     const bf16_t* vc = A.v + (int64_t)b * A.sb + (int64_t)kvh * A.sh;
     const bf16_t* kbr = A.kbar + ((int64_t)b * A.Hkv + kvh) * A.NB * kD;
     const bf16_t* vbr = A.vbar + ((int64_t)b * A.Hkv + kvh) * A.NB * kD;
+    const float sc2 = A.scale * kLog2e;  // logits in log2 units: exp2 weights
 
     int nex = 0;
     if (!DENSE) {
@@ -300,61 +313,61 @@ void video_attend_kernel(VideoArgs A) {
         }
         __syncthreads();
         nex = s.nex;
+        if (tid < nex) {  // origin token and clipped extents of each opened block
+            const int j = s.tl[tid];
+            const int bfi = j / (A.nby * A.nbx), byi = (j / A.nbx) % A.nby, bxi = j % A.nbx;
+            s.tdesc[tid][0] = ((bfi * A.bf) * A.H + byi * A.bh) * A.W + bxi * A.bw;
+            s.tdesc[tid][1] = min(A.bf, A.F - bfi * A.bf) | (min(A.bh, A.H - byi * A.bh) << 8) |
+                              (min(A.bw, A.W - bxi * A.bw) << 16);
+        }
+        __syncthreads();
     }
     const int ntc = DENSE || A.drop ? 0 : (A.NB + kFlashKeys - 1) / kFlashKeys;
     const int nt = DENSE ? (A.T + kFlashKeys - 1) / kFlashKeys : nex + ntc;
 
     // Load tile t into buffer `buf`: K and V rows straight to LDS, and the two bias rows.
     auto issue = [&](int t, int buf) {
-        const bf16_t* kbase;
-        const bf16_t* vbase;
-        int64_t stride;
-        int origin = 0, lf = 0, lh = 0, lw = 0, blk0 = 0, nk = 0;
         const int kind = DENSE ? 0 : (t < nex ? 1 : 2);  // 0 dense run, 1 opened block, 2 coarse
-        if (kind == 0) {
-            kbase = kc; vbase = vc; stride = A.st;
-            blk0 = t * kFlashKeys;
-            nk = min(kFlashKeys, A.T - blk0);
-        } else if (kind == 1) {
-            kbase = kc; vbase = vc; stride = A.st;
-            const int j = s.tl[t];
-            const int bfi = j / (A.nby * A.nbx), byi = (j / A.nbx) % A.nby, bxi = j % A.nbx;
-            origin = ((bfi * A.bf) * A.H + byi * A.bh) * A.W + bxi * A.bw;
-            lf = min(A.bf, A.F - bfi * A.bf);
-            lh = min(A.bh, A.H - byi * A.bh);
-            lw = min(A.bw, A.W - bxi * A.bw);
+        const bf16_t* kbase = kind == 2 ? kbr : kc;
+        const bf16_t* vbase = kind == 2 ? vbr : vc;
+        const int64_t stride = kind == 2 ? (int64_t)kD : A.st;
+        int origin = 0, lf = 0, lh = 0, lw = 0, first = 0, nk = 0;
+        if (kind == 1) {
+            origin = s.tdesc[t][0];
+            const int ext = s.tdesc[t][1];
+            lf = ext & 255;
+            lh = (ext >> 8) & 255;
+            lw = ext >> 16;
         } else {
-            kbase = kbr; vbase = vbr; stride = kD;
-            blk0 = (t - nex) * kFlashKeys;
-            nk = min(kFlashKeys, A.NB - blk0);
+            first = kind == 0 ? t * kFlashKeys : (t - nex) * kFlashKeys;
+            nk = min(kFlashKeys, (kind == 0 ? A.T : A.NB) - first);
         }
-        // row r of the tile -> element offset of its K / V row; valid flag
-        auto row_of = [&](int r, bool& ok) -> int64_t {
+        // slot ii of this thread -> row index (token or block) and whether it holds a key
+        auto row_of = [&](int ii, int r, bool& ok) -> int {
             if (kind == 1) {
-                const int ijk = s.slot_ijk[r];
-                ok = ijk >= 0 && (ijk & 255) < lf && ((ijk >> 8) & 255) < lh && (ijk >> 16) < lw;
-                return (int64_t)(ok ? origin + s.slot_off[r] : origin) * stride;
+                ok = si[ii] < lf && sj[ii] < lh && sk[ii] < lw;
+                return origin + (ok ? soff[ii] : 0);
             }
             ok = r < nk;
-            return (int64_t)(blk0 + (ok ? r : nk - 1)) * stride;
+            return first + (ok ? r : nk - 1);
         };
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int i = w + 4 * ii;
             const int row = 4 * i + g;
             bool ok;
-            const int64_t off = row_of(row, ok);
+            const int64_t off = (int64_t)row_of(ii, row, ok) * stride;
             __builtin_amdgcn_global_load_lds(kbase + off + 8 * (li ^ swz_k(row)), &s.kt[buf][4 * i][0], 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vbase + off + 8 * (li ^ swz_v(row)), &s.vt[buf][4 * i][0], 16, 0, 0);
         }
         if (tid < kVideoPair * kFlashKeys) {
-            const int q = tid >> 6, r = tid & 63;
+            const int q = tid >> 6, r = l;
             bool ok;
-            (void)row_of(r, ok);
-            float bv = -INFINITY;
+            const int x = row_of(4, r, ok);
+            float bv = -INFINITY;  // in log2 units, like the scaled logits
             if (kind == 0) bv = ok ? 0.0f : -INFINITY;
             else if (kind == 1) bv = ok && ((s.tmask[t] >> q) & 1) ? 0.0f : -INFINITY;
-            else if (ok && !((s.opened[q][(blk0 + r) >> 5] >> ((blk0 + r) & 31)) & 1u)) bv = A.lnn[blk0 + r];
+            else if (ok && !((s.opened[q][x >> 5] >> (x & 31)) & 1u)) bv = A.lnn[x] * kLog2e;
             s.bias[buf][q][r] = bv;
         }
     };
@@ -382,7 +395,11 @@ void video_attend_kernel(VideoArgs A) {
                 S[kb][1] = mfma16(a, qf[1][kk], S[kb][1]);
             }
         }
-        // logits and the online softmax (a column's 64 keys live in lanes l, l^16, l^32, l^48)
+        // logits in log2 units and the online softmax (a column's 64 keys live in lanes
+        // l, l^16, l^32, l^48).  A masked key has bias -inf, so its logit is -inf and its
+        // weight exp2(-inf) = 0.  The first tile a wave computes always holds a key of its
+        // own (an opened block's slot 0, or a dense run), so the running maximum is finite
+        // from then on and no difference below is -inf - (-inf).
         const float* bias = s.bias[buf][qi];
         float P[4][2][4];
 #pragma unroll
@@ -392,29 +409,29 @@ void video_attend_kernel(VideoArgs A) {
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float bv = bias[16 * kb + 4 * g + r];
-                    const float lam = bv != -INFINITY ? __builtin_fmaf(A.scale, S[kb][cb][r], bv) : -INFINITY;
+                    const float lam = __builtin_fmaf(sc2, S[kb][cb][r], bias[16 * kb + 4 * g + r]);
                     P[kb][cb][r] = lam;
                     mt = fmaxf(mt, lam);
                 }
             mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
             const float mn = fmaxf(m_run[cb], mt);
-            const float a = m_run[cb] == -INFINITY ? 0.0f : softmax_exp(m_run[cb] - mn);
+            const float a = __builtin_amdgcn_exp2f(m_run[cb] - mn);  // 0 on the first tile
             float ls = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float lam = P[kb][cb][r];
-                    const float p = lam == -INFINITY ? 0.0f : softmax_exp(lam - mn);
+                    const float p = __builtin_amdgcn_exp2f(P[kb][cb][r] - mn);
                     P[kb][cb][r] = p;
                     ls += p;
                 }
             l_run[cb] = __builtin_fmaf(l_run[cb], a, ls);
             m_run[cb] = mn;
+            if (__any(a != 1.0f)) {  // the maximum moved for some column of the wave
 #pragma unroll
-            for (int db = 0; db < 8; ++db) O[cb][db] *= a;
+                for (int db = 0; db < 8; ++db) O[cb][db] *= a;
+            }
         }
         // O^T += V^T P^T over two 32-key steps.  MFMA k index e of lane group g is key
         // 32 st + 16 (e / 4) + 4 g + e % 4 on both operands; P as bf16 hi + lo.
@@ -575,9 +592,10 @@ extern "C" int lod_video_attend(const lod_video_params* params, lod_kv kv, const
     A.sel = reinterpret_cast<int32_t*>(base + L.sel);
     A.sel_out = sel_blocks;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(video_summary_kernel, dim3(A.NB, A.Hkv + A.Hq, batch), dim3(kThreads), 0, st, A);
+    hipLaunchKernelGGL(video_summary_kernel, dim3(A.Hkv + (A.Hq + 1) / 2, A.NB, batch), dim3(kThreads), 0, st, A);
     // as many query blocks per select workgroup as the score buffer allows
-    if ((size_t)4 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<4>(A, batch, st);
+    if ((size_t)8 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<8>(A, batch, st);
+    else if ((size_t)4 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<4>(A, batch, st);
     else if ((size_t)2 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<2>(A, batch, st);
     else launch_video_select<1>(A, batch, st);
     hipLaunchKernelGGL((video_attend_kernel<false>), dim3((unsigned)ceil_div(A.NB, kVideoPair), A.Hq, batch),

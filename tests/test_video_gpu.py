@@ -145,3 +145,21 @@ def test_video_full_size_sampled():
             assert np.array_equal(sel[0, h, j], r["sel"][0, 0, j]), (h, j)
             tok = vo.members(o, j)
             assert np.abs(out[0, tok, h] - r["out"][0, tok, 0]).max() <= TOL, (h, j)
+
+
+@pytest.mark.parametrize("nby,nbx", [(40, 50), (50, 80), (80, 100)])
+def test_video_large_grids_sampled(nby, nbx):
+    """2000, 4000 and 8000 blocks: the choice is made with 4, 2 and 1 query blocks per
+    select workgroup (the score buffer bounds it); sampled pairs against the oracle."""
+    F, H, W = 4, 4 * nby, 4 * nbx
+    g, o = _cfgs(F, H, W, 1, 1, 16)
+    print(f"video large grid={F}x{H}x{W}", flush=True)
+    Q, K, V = synth.video_qkv(1, F, H, W, 1, 1, seed=137, device="cuda")
+    out, sel, _ = _run(g, Q, K, V)
+    nb = o.n_blocks
+    blocks = [0, nb // 2 + 1, nb - 1]
+    r = vo.forward(o, *_np(Q.cpu(), K.cpu(), V.cpu()), pairs=[(0, 0, j) for j in blocks])
+    for j in blocks:
+        assert np.array_equal(sel[0, 0, j], r["sel"][0, 0, j]), j
+        tok = vo.members(o, j)
+        assert np.abs(out[0, tok, 0] - r["out"][0, tok, 0]).max() <= TOL, j
