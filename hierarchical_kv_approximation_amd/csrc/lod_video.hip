@@ -25,9 +25,10 @@
 namespace lodi {
 
 constexpr int kVideoSlots = 64;          // member slots of a block (volume <= 64)
-constexpr int kVideoMaxBlocks = 14336;   // blocks of a grid, at most
+constexpr int kVideoMaxBlocks = 13312;   // blocks of a grid, at most
 constexpr int kVideoMaxTop = 64;         // opened blocks per query block, at most
-constexpr int kVideoScoreLds = 57344;    // bytes of select scores per workgroup (with the static arrays, under 64 KB)
+constexpr int kVideoScoreLds = 53248;    // bytes of select scores per workgroup (with the static arrays, under 64 KB)
+constexpr int kVideoCand = 128;          // top-c candidates a select wave ranks exactly
 constexpr uint32_t kTakenBits = 0x7fffffffu;  // marks a chosen score (a NaN no chain makes)
 
 struct VideoArgs {
@@ -60,44 +61,60 @@ __device__ __forceinline__ int video_token(const VideoArgs& A, int blk, int m) {
 
 // ---------------------------------------------------------------------------- summary
 
-// grid (Hkv + ceil(Hq / 2), NB, B): unit x < Hkv averages the keys and values of KV
-// head x; a later unit averages the queries of two query heads.  Units of one block run
-// next to each other, so neighbouring workgroups read neighbouring rows.  Rows are
-// staged with 16-byte loads, then thread (tensor, column) sums its column over the
-// members in slot order, which is ascending token order.
+// grid (ceil(Hkv / 8) + ceil(Hq / 16), NB, B).  Thread (tensor slot tt = tid / 16,
+// column group cg = tid % 16) owns columns 8 cg .. 8 cg + 7 of one tensor of block
+// blockIdx.y: a unit x < ceil(Hkv / 8) covers the keys (even tt) and values (odd tt) of
+// KV heads 8 x + tt / 2; a later unit the queries of 16 query heads.  The thread reads
+// the block's rows 16 at a time with 16-byte loads and adds each column in member
+// order, which is ascending token order.
 __global__ __launch_bounds__(kThreads) void video_summary_kernel(VideoArgs A) {
-    __shared__ alignas(16) bf16_t rows[2][kVideoSlots][kD];
     __shared__ int tok[kVideoSlots];
     const int u = blockIdx.x, blk = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const bool isq = u >= A.Hkv;
-    const int h0 = isq ? 2 * (u - A.Hkv) : u;          // first head of the unit
-    const int ntens = isq ? min(2, A.Hq - h0) : 2;      // tensors of the unit
+    const int cg = tid & 15, tt = tid >> 4;
+    const int nku = (A.Hkv + 7) / 8;
+    const bool isq = u >= nku;
+    const int head = isq ? 16 * (u - nku) + tt : 8 * u + (tt >> 1);
+    const bool valid = head < (isq ? A.Hq : A.Hkv);
+    const bf16_t* base = isq ? A.q + ((int64_t)b * A.T * A.Hq + head) * kD + 8 * cg
+                             : ((tt & 1) ? A.v : A.k) + (int64_t)b * A.sb + (int64_t)head * A.sh + 8 * cg;
+    const int64_t ts = isq ? (int64_t)A.Hq * kD : A.st;  // elements between tokens
     if (tid < kVideoSlots) tok[tid] = video_token(A, blk, tid);
     __syncthreads();
-    for (int i = tid; i < ntens * kVideoSlots * (kD / 8); i += kThreads) {
-        const int tsr = i / (kVideoSlots * (kD / 8)), m = (i / (kD / 8)) % kVideoSlots, ch = i % (kD / 8);
-        const int t = tok[m];
-        if (t < 0) continue;
-        const bf16_t* src = isq ? A.q + (((int64_t)b * A.T + t) * A.Hq + h0 + tsr) * kD
-                                : (tsr ? A.v : A.k) + (int64_t)b * A.sb + (int64_t)t * A.st + (int64_t)h0 * A.sh;
-        *reinterpret_cast<uint4*>(&rows[tsr][m][8 * ch]) = *reinterpret_cast<const uint4*>(src + 8 * ch);
-    }
-    __syncthreads();
-    const int tsr = tid / kD, col = tid % kD;
-    if (tsr >= ntens) return;
-    float s = 0.0f;
+    if (!valid) return;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     int n = 0;
-    for (int m = 0; m < A.bsz; ++m) {
-        if (tok[m] < 0) continue;
-        s = s + bf16_bits_to_f32(rows[tsr][m][col]);
-        ++n;
+    for (int rb = 0; rb < A.bsz; rb += 16) {
+        uint4 x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = rb + i < kVideoSlots ? tok[rb + i] : -1;
+            x[i] = t >= 0 ? *reinterpret_cast<const uint4*>(base + (int64_t)t * ts) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (rb + i >= kVideoSlots || tok[rb + i] < 0) continue;
+            const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = acc[e] + bf16_bits_to_f32((wd[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            ++n;
+        }
     }
-    const float mean = s / (float)n;  // every block holds its slot 0
+    float mean[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mean[e] = acc[e] / (float)n;  // every block holds its slot 0
     if (isq) {
-        A.qbar[(((int64_t)b * A.Hq + h0 + tsr) * A.NB + blk) * kD + col] = mean;
+        float* dst = A.qbar + (((int64_t)b * A.Hq + head) * A.NB + blk) * kD + 8 * cg;
+        *reinterpret_cast<float4*>(dst) = make_float4(mean[0], mean[1], mean[2], mean[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(mean[4], mean[5], mean[6], mean[7]);
     } else {
-        bf16_t* dst = tsr ? A.vbar : A.kbar;
-        dst[(((int64_t)b * A.Hkv + h0) * A.NB + blk) * kD + col] = f32_to_bf16_rne(mean);
+        bf16_t* dst = ((tt & 1) ? A.vbar : A.kbar) + (((int64_t)b * A.Hkv + head) * A.NB + blk) * kD + 8 * cg;
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = (uint32_t)f32_to_bf16_rne(mean[2 * e]) | ((uint32_t)f32_to_bf16_rne(mean[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         if (b == 0 && u == 0 && tid == 0) A.lnn[blk] = logf((float)n);
     }
 }
@@ -111,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void video_select_kernel(VideoArgs A) {
     extern __shared__ float sc[];  // [QPW][NB]
     __shared__ alignas(16) float qs[QPW][kD];
     __shared__ int win[4][kVideoMaxTop];
+    __shared__ uint64_t ckey[4][kVideoCand];
     const int hq = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int qb0 = blockIdx.x * QPW;
     const int kvh = hq / (A.Hq / A.Hkv);
@@ -142,49 +160,86 @@ __global__ __launch_bounds__(kThreads) void video_select_kernel(VideoArgs A) {
         for (int qi = 0; qi < QPW; ++qi) sc[qi * A.NB + j] = acc[qi];
     }
     __syncthreads();
-    // wave w ranks query blocks QPW*x + w, + w + 4, ...: each lane keeps the best key of
-    // its entries j = l, l + 64, ...; the wave takes the best of all lanes k times, and
-    // the owner of each winner marks it and rescans
+    // Wave w ranks query blocks QPW*x + w, + w + 4, ...  The k-th largest of the 64 lane
+    // maxima (lane l holds entries l, l + 64, ...) is at most the k-th largest key, so
+    // every winner is among the keys at or above it; those candidates are compacted and
+    // ranked exactly.  More than kVideoCand candidates (the best keys crowd into a few
+    // lanes) fall back to k rounds of a wave-wide maximum with rescans.
     const int k = min(A.c, A.NB);
     for (int qq = w; qq < QPW; qq += 4) {
         const int qb = qb0 + qq;
         if (qb >= A.NB) break;
         float* s = sc + qq * A.NB;
-        auto best_of = [&]() {
-            uint64_t bk = 0;
-            for (int j = l; j < A.NB; j += 64) {
-                const float x = s[j];
-                if (__float_as_uint(x) == kTakenBits) continue;
-                const uint64_t key = rank_key(x, (uint32_t)j);
-                bk = key > bk ? key : bk;
-            }
-            return bk;
-        };
-        uint64_t mine = best_of();
-        int wsel = -1;
-        for (int r = 0; r < k; ++r) {
-            const uint64_t top = wave_max_u64(mine);
-            const int j = (int)key_id(top);
-            if (l == r) wsel = j;
-            if ((j & 63) == l) {
-                s[j] = __uint_as_float(kTakenBits);
-                mine = best_of();
-            }
+        const int64_t o = (((int64_t)b * A.Hq + hq) * A.NB + qb) * A.c;
+        uint64_t lm = 0;
+        for (int j = l; j < A.NB; j += 64) {
+            const uint64_t key = rank_key(s[j], (uint32_t)j);
+            lm = key > lm ? key : lm;
         }
-        win[w][l] = wsel;
+        // k rounds over the lane maxima (keys are distinct, so one lane leaves per round);
+        // at least k lanes hold entries, so tau is a real key
+        uint64_t cur = lm, tau = 0;
+        for (int r = 0; r < k; ++r) {
+            tau = wave_max_u64(cur);
+            if (cur == tau) cur = 0;
+        }
+        int ncand = 0;
+        for (int j0 = 0; j0 < A.NB; j0 += 64) {
+            const int j = j0 + l;
+            const uint64_t key = j < A.NB ? rank_key(s[j], (uint32_t)j) : 0;
+            const bool in = key >= tau;
+            const uint64_t bal = __ballot(in);
+            const int pos = ncand + __popcll(bal & ((1ull << l) - 1ull));
+            if (in && pos < kVideoCand) ckey[w][pos] = key;
+            ncand += __popcll(bal);
+        }
         wave_sync_lds();
+        if (ncand <= kVideoCand) {
+            // rank of each candidate among all candidates; winners store their id by rank
+            for (int i = l; i < ncand; i += 64) {
+                const uint64_t mine = ckey[w][i];
+                int rank = 0;
+                for (int j = 0; j < ncand; ++j) rank += ckey[w][j] > mine;
+                if (rank < k) win[w][rank] = (int)key_id(mine);
+            }
+        } else {
+            uint64_t best = 0;
+            auto best_of = [&]() {
+                uint64_t bk = 0;
+                for (int j = l; j < A.NB; j += 64) {
+                    const float x = s[j];
+                    if (__float_as_uint(x) == kTakenBits) continue;
+                    const uint64_t key = rank_key(x, (uint32_t)j);
+                    bk = key > bk ? key : bk;
+                }
+                return bk;
+            };
+            best = best_of();
+            int wsel = -1;
+            for (int r = 0; r < k; ++r) {
+                const uint64_t top = wave_max_u64(best);
+                const int j = (int)key_id(top);
+                if (l == r) wsel = j;
+                if ((j & 63) == l) {
+                    s[j] = __uint_as_float(kTakenBits);
+                    best = best_of();
+                }
+            }
+            if (l < k) win[w][l] = wsel;
+        }
+        wave_sync_lds();
+        // the k winners in ascending id order, -1 padding up to c
         if (l < A.c) {
-            const int64_t o = (((int64_t)b * A.Hq + hq) * A.NB + qb) * A.c;
             int pos = l, val = -1;
             if (l < k) {
+                val = win[w][l];
                 pos = 0;
-                for (int i = 0; i < k; ++i) pos += win[w][i] < wsel;
-                val = wsel;
+                for (int i = 0; i < k; ++i) pos += win[w][i] < val;
             }
             A.sel[o + pos] = val;
             if (A.sel_out) A.sel_out[o + pos] = val;
         }
-        wave_sync_lds();  // win[w] is rewritten by the next query block
+        wave_sync_lds();  // win[w] and ckey[w] are rewritten by the next query block
     }
 }
 
@@ -216,6 +271,8 @@ __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return 2 * (row & 7); }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // 4 bf16 of a V^T operand: this lane gets V[key0 + r][d0 + lane % 16] for r = 0..3,
 // where the 16 lanes of its group read (row key0 + i / 4, elements d0 + 4 (i % 4) ..).
@@ -441,11 +498,15 @@ void video_attend_kernel(VideoArgs A) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    __bf16 h, lo;
-                    split_bf16(P[2 * st + j / 4][cb][j % 4], h, lo);
-                    ph[cb][j] = h;
-                    pl[cb][j] = lo;
+                for (int j = 0; j < 8; j += 2) {  // two at a time: one packed conversion each
+                    const f32x2_t x = {P[2 * st + j / 4][cb][j % 4], P[2 * st + j / 4][cb][j % 4 + 1]};
+                    const bf16x2_t h = __builtin_convertvector(x, bf16x2_t);
+                    const f32x2_t r = x - __builtin_convertvector(h, f32x2_t);
+                    const bf16x2_t lo = __builtin_convertvector(r, bf16x2_t);
+                    ph[cb][j] = h[0];
+                    ph[cb][j + 1] = h[1];
+                    pl[cb][j] = lo[0];
+                    pl[cb][j + 1] = lo[1];
                 }
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
@@ -592,7 +653,8 @@ extern "C" int lod_video_attend(const lod_video_params* params, lod_kv kv, const
     A.sel = reinterpret_cast<int32_t*>(base + L.sel);
     A.sel_out = sel_blocks;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(video_summary_kernel, dim3(A.Hkv + (A.Hq + 1) / 2, A.NB, batch), dim3(kThreads), 0, st, A);
+    hipLaunchKernelGGL(video_summary_kernel, dim3((A.Hkv + 7) / 8 + (A.Hq + 15) / 16, A.NB, batch), dim3(kThreads), 0,
+                       st, A);
     // as many query blocks per select workgroup as the score buffer allows
     if ((size_t)8 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<8>(A, batch, st);
     else if ((size_t)4 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<4>(A, batch, st);

@@ -279,7 +279,7 @@ int lod_dense_prefill(const lod_params* params, lod_kv kv, const void* q, int32_
  *     for every other block, one term scale*q.kbar + ln(n) with value vbar (its mean
  *     key and value repeated n times); drop_remainder = 1 leaves those terms out.
  * Supported: head_dim 128, kv_dtype LOD_BF16, block volume <= 64, 1 <= top_blocks <= 64,
- * at most 14336 blocks, n_q_heads a multiple of n_kv_heads (query head h reads KV head
+ * at most 13312 blocks, n_q_heads a multiple of n_kv_heads (query head h reads KV head
  * h / (n_q_heads / n_kv_heads)); anything else valid returns LOD_ERR_UNSUPPORTED.
  */
 typedef struct {

@@ -52,7 +52,7 @@ def test_video_layout_is_aligned_disjoint_and_sized(batch):
     ("top_blocks", 65, lod.LOD_ERR_UNSUPPORTED),
     ("n_q_heads", 12, lod.LOD_ERR_ARG),
     ("frames", 0, lod.LOD_ERR_ARG),
-    ("frames", 16000, lod.LOD_ERR_UNSUPPORTED),  # 4000 * 2 * 2 = 16000 blocks > 14336
+    ("frames", 16000, lod.LOD_ERR_UNSUPPORTED),  # 4000 * 2 * 2 = 16000 blocks > 13312
     ("scale", 0.0, lod.LOD_ERR_ARG),
     ("drop_remainder", 2, lod.LOD_ERR_ARG),
 ])
