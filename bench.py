@@ -19,6 +19,7 @@ step of the method) at its real rate of once per 256 tokens.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import math
@@ -160,6 +161,10 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the sigma sweep of the approximation error")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV-view decode timing")
     ap.add_argument("--no-int4", action="store_true", help="skip the INT4-pages decode timing")
+    ap.add_argument("--no-video", action="store_true", help="skip the video LoD measurement")
+    ap.add_argument("--only-video", action="store_true",
+                    help="measure video LoD only and print its JSON object (for profiling)")
+    ap.add_argument("--video-calls", type=int, default=20)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,6 +178,13 @@ def main():
     from hierarchical_kv_approximation_amd import lod, synth
 
     dev = torch.device("cuda:0")
+    if args.only_video:
+        hip = HipEvents()
+        v = bench_video(torch, lod, synth, hip, torch.cuda.current_stream().cuda_stream, args.seed,
+                        calls=args.video_calls, dense=not args.no_dense, cpu=not args.no_cpu,
+                        cpu_seconds=args.cpu_seconds)
+        print(json.dumps({"video": v}), flush=True)
+        return
     B, T, L = args.batch, args.ctx, args.layers
     K, W = max(2, args.steps), max(0, args.warmup)
     cfg = lod.Config(n_q_heads=64, n_kv_heads=8, groups=8, top_groups=8, top_pages=2, window=512,
@@ -393,6 +405,12 @@ def main():
     if not args.no_prefill:
         prefill = bench_prefill(torch, lod, synth, cfg, hip, stream, args.prefill_ctx, args.seed,
                                 dense=not args.no_dense)
+        torch.cuda.empty_cache()
+
+    video = None
+    if not args.no_video:
+        video = bench_video(torch, lod, synth, hip, stream, args.seed, calls=args.video_calls,
+                            dense=not args.no_dense, cpu=not args.no_cpu, cpu_seconds=min(args.cpu_seconds, 10.0))
 
     line = {
         "metric": METRIC,
@@ -444,6 +462,7 @@ def main():
         },
         "prefill": prefill,
         "sigma_sweep": sweep,
+        "video": video,
     }
     print(json.dumps(line), flush=True)
 
@@ -680,6 +699,153 @@ def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, s
     return {"workload": f"one sequence, {T}-token prompt then {steps} decode steps with one chunk build, "
                         "GQA 64/8, bf16; 32 key clusters with sigma 0.1..1.0, matched queries",
             **res, "samples": samples}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def video_flops(torch, sel, counts, d, drop):
+    """Algorithmic flops of one video LoD call: 4 d per (query, softmax term), i.e. the
+    QK and PV products over the opened blocks' members and one term per other block."""
+    opened = sel >= 0
+    cnt = counts.to(sel.device)
+    exact = (cnt[sel.clamp(min=0).long()] * opened).sum(-1)          # [B][Hq][NB]
+    terms = exact + (0 if drop else (cnt.numel() - opened.sum(-1)))
+    return int(4 * d * (terms.double() * cnt.double()[None, None, :]).sum().item())
+
+
+def bench_video(torch, lod, synth, hip, stream, seed, calls=20, dense=True, cpu=True, cpu_seconds=10.0):
+    """Video LoD on a 20 x 48 x 80 token grid (76800 tokens), 40 query and KV heads,
+    head_dim 128, bf16, 4x4x4 blocks, c = 16: one lod_video_attend call per step, rotating
+    over two input copies (2 x 2.36 GB, beyond the Infinity Cache)."""
+    F, H, W, Hh, c, d = 20, 48, 80, 40, 16, 128
+    dev = torch.device("cuda:0")
+    g = lod.VideoConfig(frames=F, height=H, width=W, n_q_heads=Hh, n_kv_heads=Hh, top_blocks=c)
+    T = F * H * W
+    log(f"video LoD: grid {F}x{H}x{W}, {Hh} heads ...")
+    data = [synth.video_qkv(1, F, H, W, Hh, Hh, seed=seed + 1000 + 17 * i, device=dev) for i in range(2)]
+    ws = torch.empty(lod.video_ws_bytes(g, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(1, T, Hh, d, dtype=torch.float32, device=dev)
+
+    def run(cfg, i, o=out):
+        Q, K, V = data[i % 2]
+        lod.attend_video(cfg, K, V, Q, ws=ws, out=o)
+
+    for i in range(4):
+        run(g, i)
+    torch.cuda.synchronize()
+    e = hip.create(2)
+    hip.record(e[0], stream)
+    for i in range(calls):
+        run(g, i)
+    hip.record(e[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e[0], e[1]) / calls
+    hip.destroy(e)
+    # per-kernel split from the library's trace events (a separate pass)
+    n_tr = 6
+    evs = hip.create(4 * n_tr)
+    keep = []
+    for i in range(n_tr):
+        keep.append(lod.trace_events(evs[4 * i:4 * i + 4]))
+        run(g, i)
+    lod.trace_events(None)
+    torch.cuda.synchronize()
+    seg = [[hip.ms(evs[4 * i + k], evs[4 * i + k + 1]) for k in range(3)] for i in range(n_tr)]
+    hip.destroy(evs)
+    summ_ms, sel_ms, att_ms = (sum(x[k] for x in seg) / n_tr for k in range(3))
+    # algorithmic work from the choice the call made (copy 0)
+    _, sel = lod.attend_video(g, data[0][1], data[0][2], data[0][0], ws=ws, out=out, want_selection=True)
+    counts = torch.exp(lod.video_arrays(g, ws, 1)["lnn"]).round().to(torch.int64)
+    flops = video_flops(torch, sel, counts, d, False)
+    lod_out = out.clone()
+    qkv_bytes = 3 * T * Hh * d * 2
+    res = {
+        "workload": f"video LoD, one attention layer per call: {F}x{H}x{W} token grid ({T} tokens), "
+                    f"batch 1, {Hh} query / {Hh} KV heads, head_dim {d}, bf16, 4x4x4 blocks, top {c} blocks",
+        "ms_per_call": round(ms, 4),
+        "tok_per_s": round(T * 1000.0 / ms, 1),
+        "kernel_ms": {"summaries": round(summ_ms, 4), "choice": round(sel_ms, 4), "attention": round(att_ms, 4)},
+        "algorithmic_tflop_per_call": round(flops / 1e12, 4),
+        "summaries_GBs": round(qkv_bytes / (summ_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "video_attend_kernel", "unit": "TFLOP/s",
+                     "achieved": round(flops / (att_ms * 1e-3) / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "frac": round(flops / (att_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops},
+    }
+    # the ablation: same choice, no coarse terms
+    gd = dataclasses.replace(g, drop_remainder=True)
+    e = hip.create(2)
+    hip.record(e[0], stream)
+    for i in range(calls):
+        run(gd, i)
+    hip.record(e[1], stream)
+    torch.cuda.synchronize()
+    drop_ms = hip.ms(e[0], e[1]) / calls
+    hip.destroy(e)
+    abl = torch.empty_like(out)
+    run(gd, 0, abl)
+    res["sparsity_ablation"] = {"ms_per_call": round(drop_ms, 4), "time_vs_lod": round(drop_ms / ms, 3)}
+    if dense:
+        Q, K, V = data[0]
+        dout = torch.empty_like(out)
+        lod.dense_video(g, K, V, Q, out=dout)
+        torch.cuda.synchronize()
+        e = hip.create(2)
+        hip.record(e[0], stream)
+        lod.dense_video(g, K, V, Q, out=dout)
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        dms = hip.ms(e[0], e[1])
+        hip.destroy(e)
+        dflops = 4 * d * T * T * Hh
+        err = (lod_out - dout).abs()
+        aerr = (abl - dout).abs()
+        res["dense"] = {"ms_per_call": round(dms, 3), "speedup_lod_vs_dense": round(dms / ms, 2),
+                        "tflops": round(dflops / (dms * 1e-3) / 1e12, 1),
+                        "frac_mfma": round(dflops / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "lod_err_vs_dense": {"max_abs": round(float(err.max()), 5), "mean_abs": round(float(err.mean()), 6)},
+                        "ablation_err_vs_dense": {"max_abs": round(float(aerr.max()), 5),
+                                                  "mean_abs": round(float(aerr.mean()), 6)},
+                        "mean_abs_dense_output": round(float(dout.abs().mean()), 5)}
+        del dout
+        log(f"video dense: {dms:.1f} ms/call")
+    log(f"video LoD: {ms:.3f} ms/call (summaries {summ_ms:.3f}, choice {sel_ms:.3f}, attention {att_ms:.3f})")
+    if cpu:
+        res["cpu_baseline"] = video_cpu_baseline(data[0], F, H, W, c, cpu_seconds)
+        log(f"video CPU oracle: {res['cpu_baseline']['value']} tok/s")
+    del data, ws, out, lod_out, abl
+    torch.cuda.empty_cache()
+    return res
+
+
+def video_cpu_baseline(qkv, F, H, W, c, seconds):
+    """The video oracle, as it stands, on sampled query blocks of one head: summaries of
+    the head's blocks, then choice and softmax block by block until `seconds` pass;
+    scaled to tokens of the whole grid per second over all heads."""
+    import numpy as np
+
+    from oracle import video as vo
+    threads = cpu_threads()
+    Q, K, V = (x[:, :, 0:1].float().cpu().numpy() for x in qkv)
+    Hh = qkv[0].shape[2]
+    o = vo.VideoConfig(d=128, frames=F, height=H, width=W, top_blocks=c, bf16=True)
+    nb = o.n_blocks
+    order = np.random.default_rng(7).permutation(nb)
+    t = time.time()
+    vo.forward(o, Q, K, V, pairs=[], threads=threads)  # the head's summaries
+    t_sum = time.time() - t
+    done, t1 = 0, time.time()
+    while done < nb and time.time() - t1 < seconds:
+        step = min(2 * threads, nb - done)
+        vo.forward(o, Q, K, V, pairs=[(0, 0, int(j)) for j in order[done:done + step]], threads=threads)
+        done += step
+    el = time.time() - t1 - t_sum * (done // (2 * threads) + (done % (2 * threads) > 0))
+    per_block = max(el, 1e-9) / done
+    head_s = t_sum + per_block * nb
+    return {"value": round(F * H * W / (head_s * Hh), 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {nb} query blocks of head 0 (each call re-summarises the head, "
+                      f"{t_sum:.2f} s, subtracted), scaled to the full grid and {Hh} heads; {threads} threads"}
 
 
 def cpu_baseline(cfg, Ly, seq_len, seconds):

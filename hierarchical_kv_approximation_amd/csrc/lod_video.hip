@@ -653,15 +653,19 @@ extern "C" int lod_video_attend(const lod_video_params* params, lod_kv kv, const
     A.sel = reinterpret_cast<int32_t*>(base + L.sel);
     A.sel_out = sel_blocks;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    trace_point(0, st);
     hipLaunchKernelGGL(video_summary_kernel, dim3((A.Hkv + 7) / 8 + (A.Hq + 15) / 16, A.NB, batch), dim3(kThreads), 0,
                        st, A);
+    trace_point(1, st);
     // as many query blocks per select workgroup as the score buffer allows
     if ((size_t)8 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<8>(A, batch, st);
     else if ((size_t)4 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<4>(A, batch, st);
     else if ((size_t)2 * A.NB * sizeof(float) <= (size_t)kVideoScoreLds) launch_video_select<2>(A, batch, st);
     else launch_video_select<1>(A, batch, st);
+    trace_point(2, st);
     hipLaunchKernelGGL((video_attend_kernel<false>), dim3((unsigned)ceil_div(A.NB, kVideoPair), A.Hq, batch),
                        dim3(kThreads), 0, st, A);
+    trace_point(3, st);
     return hipGetLastError() == hipSuccess ? LOD_OK : LOD_ERR_HIP;
 }
 

@@ -339,11 +339,13 @@ int lod_video_dense(const lod_video_params* params, lod_kv kv, const void* q, in
 
 /*
  * Instrumentation (profiling only; results are unchanged).  While `events` is non-null,
- * every later lod_attend_decode / lod_attend_prefill call made from the same host thread
+ * every later lod_attend_decode / lod_attend_prefill / lod_video_attend call made from the
+ * same host thread
  * records events[0] on its stream before its first kernel and events[1 + k] after its
  * k-th kernel (decode: k = 0 scan, 1 open-and-combine; bf16 prefill: k = 0 candidate
  * sweep, 1 select, 2 flash, 3 bucket, 4 pages, 5 combine, recorded again for every batch
- * of rows, so the last batch's times remain).  `events` points to n_events
+ * of rows, so the last batch's times remain; lod_video_attend: k = 0 summaries, 1 choice,
+ * 2 attention).  `events` points to n_events
  * hipEvent_t handles created by the caller, who reads them with hipEventElapsedTime;
  * kernels beyond n_events - 1 record nothing.  Pass NULL to stop.  Not for captured graphs.
  */

@@ -163,3 +163,31 @@ def test_video_large_grids_sampled(nby, nbx):
         assert np.array_equal(sel[0, 0, j], r["sel"][0, 0, j]), j
         tok = vo.members(o, j)
         assert np.abs(out[0, tok, 0] - r["out"][0, tok, 0]).max() <= TOL, j
+
+
+def test_video_select_fallback_when_winners_crowd_one_lane():
+    """8192 blocks: every block whose id is a multiple of 64 (one lane's entries in the
+    select wave) has identical keys along the queries' direction, so more than 128 keys
+    tie at the top and the selection takes its fallback path; ties go to the lower ids."""
+    F, H, W = 4, 256, 512
+    g, o = _cfgs(F, H, W, 1, 1, 16)
+    T = F * H * W
+    gen = torch.Generator().manual_seed(139)
+    u = torch.randn(128, generator=gen)
+    t = torch.arange(T)
+    f, y, x = t // (H * W), (t // W) % H, t % W
+    blk = ((f // 4) * (H // 4) + y // 4) * (W // 4) + x // 4
+    K = 0.1 * torch.randn(1, T, 1, 128, generator=gen)
+    K[0, blk % 64 == 0, 0] = u
+    Q = (u + 0.05 * torch.randn(1, T, 1, 128, generator=gen)).to(torch.bfloat16)
+    K = K.to(torch.bfloat16)
+    V = torch.randn(1, T, 1, 128, generator=gen).to(torch.bfloat16)
+    out, sel, _ = _run(g, Q, K, V)
+    nb = o.n_blocks
+    blocks = [0, 4097, nb - 1]
+    r = vo.forward(o, *_np(Q, K, V), pairs=[(0, 0, j) for j in blocks])
+    for j in blocks:
+        assert list(sel[0, 0, j]) == list(range(0, 1024, 64)), j
+        assert np.array_equal(sel[0, 0, j], r["sel"][0, 0, j]), j
+        tok = vo.members(o, j)
+        assert np.abs(out[0, tok, 0] - r["out"][0, tok, 0]).max() <= TOL, j
