@@ -1973,6 +1973,7 @@ extern "C" int lod_attend_decode(const lod_params* params, const lod_index* inde
     if (rc != LOD_OK) return rc;
     if (!index || !index->mem || !q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0)
         return LOD_ERR_ARG;
+    if (!aligned16(q) || !aligned16(out)) return LOD_ERR_ARG;
     if ((rc = check_kv_view(params, kv, max_seq_len)) != LOD_OK) return rc;
     if (batch != index->batch) return LOD_ERR_ARG;
     if (built_chunks(params, (int64_t)max_seq_len - 1) > index->max_chunks) return LOD_ERR_ARG;
@@ -2034,6 +2035,7 @@ extern "C" int lod_dense_decode(const lod_params* params, lod_kv kv, const void*
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
+    if (!aligned16(q) || !aligned16(out)) return LOD_ERR_ARG;
     if ((rc = check_kv_view(params, kv, max_seq_len)) != LOD_OK) return rc;
     const DensePlan P = plan_dense(params, batch, max_seq_len);
     if (!ws || ws_bytes < P.bytes) return LOD_ERR_WORKSPACE;

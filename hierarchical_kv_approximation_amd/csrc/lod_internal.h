@@ -64,6 +64,7 @@ DensePlan plan_dense(const lod_params* p, int32_t batch, int32_t max_seq_len);
 // Checks of a KV view shared by the entry points (host): strides, alignment, and for a
 // paged view the block size and that the table rows cover `positions` positions.
 int check_kv_view(const lod_params* p, const lod_kv& kv, int64_t positions);
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline int log2_exact(int32_t x) {
     int s = 0;
     while ((1 << s) < x) ++s;

@@ -1272,12 +1272,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
 
 // out = merge of the flash partial and the page partials of every opened slot.
 __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, int64_t nrh) {
-    const int64_t rh = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
-    const int d = threadIdx.x & 127;
+    // 32 threads per (row, head), 4 output elements each: 8 (row, head) per workgroup
+    const int64_t rh = (int64_t)blockIdx.x * (kThreads / 32) + (threadIdx.x >> 5);
+    const int d4 = 4 * (threadIdx.x & 31);
     if (rh >= nrh) return;
-    // every state's (m, l, o[d]) loaded together: up to 8 flash splits and 16 page slots
+    // every state's (m, l, o[d4 .. d4+3]) loaded together: up to 8 flash splits and 16 page slots
     constexpr int kMax = 8 + kMaxTG;
-    float mm[kMax], ll[kMax], oo[kMax];
+    float mm[kMax], ll[kMax];
+    float4 oo[kMax];
 #pragma unroll
     for (int k = 0; k < kMax; ++k) {
         mm[k] = -INFINITY;
@@ -1287,20 +1289,28 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, 
         } else if (k - 8 < A.TG) {
             pp = A.part_pg + (rh * A.TG + (k - 8)) * kPartStride;  // empty slots hold m = -inf
         }
-        if (pp) { mm[k] = pp[kD]; ll[k] = pp[kD + 1]; oo[k] = pp[d]; }
+        if (pp) {
+            const float2 ml = *reinterpret_cast<const float2*>(pp + kD);
+            mm[k] = ml.x;
+            ll[k] = ml.y;
+            oo[k] = *reinterpret_cast<const float4*>(pp + d4);
+        }
     }
     float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kMax; ++k) M = fmaxf(M, mm[k]);
-    float L = 0.0f, O = 0.0f;
+    float L = 0.0f, O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
 #pragma unroll
     for (int k = 0; k < kMax; ++k) {
         if (mm[k] == -INFINITY) continue;
         const float e = softmax_exp(mm[k] - M);
         L = __builtin_fmaf(ll[k], e, L);
-        O = __builtin_fmaf(oo[k], e, O);
+        O0 = __builtin_fmaf(oo[k].x, e, O0);
+        O1 = __builtin_fmaf(oo[k].y, e, O1);
+        O2 = __builtin_fmaf(oo[k].z, e, O2);
+        O3 = __builtin_fmaf(oo[k].w, e, O3);
     }
-    A.out[rh * kD + d] = O / L;
+    *reinterpret_cast<float4*>(A.out + rh * kD + d4) = make_float4(O0 / L, O1 / L, O2 / L, O3 / L);
 }
 
 }  // namespace lodi
@@ -1379,7 +1389,8 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
         hipLaunchKernelGGL((prefill_pages_kernel<HG, false, false>), pgrid, dim3(kThreads), 0, st, P);
     trace_point(5, st);
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
-    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + 1) / 2)), dim3(kThreads), 0, st, P, nrh);
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + kThreads / 32 - 1) / (kThreads / 32))),
+                       dim3(kThreads), 0, st, P, nrh);
     trace_point(6, st);
 }
 
@@ -1417,6 +1428,7 @@ extern "C" int lod_dense_prefill(const lod_params* params, lod_kv kv, const void
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
+    if (!aligned16(q) || !aligned16(out)) return LOD_ERR_ARG;
     if ((rc = check_kv_view(params, kv, (int64_t)q_start + n_q)) != LOD_OK) return rc;
     if ((int64_t)q_start + n_q > INT32_MAX) return LOD_ERR_ARG;
     if (params->kv_dtype != LOD_BF16)
@@ -1450,6 +1462,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!index || !index->mem || !q || !out || batch <= 0 || n_q <= 0 || q_start < 0) return LOD_ERR_ARG;
+    if (!aligned16(q) || !aligned16(out)) return LOD_ERR_ARG;
     if (q_start % params->chunk_size != 0) return LOD_ERR_ARG;
     if ((rc = check_kv_view(params, kv, (int64_t)q_start + n_q)) != LOD_OK) return rc;
     if (batch != index->batch) return LOD_ERR_ARG;

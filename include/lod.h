@@ -30,7 +30,8 @@
  *   - KV cache: element (b, t, h, i) of K is at k[b*stride_b + t*stride_t + h*stride_h + i]
  *     (strides in elements, last dimension contiguous, 16-byte aligned rows), or found
  *     through a block table (lod_kv below).
- *     Queries have the cache's element type; outputs are fp32.
+ *     Queries have the cache's element type; outputs are fp32.  q and out are 16-byte
+ *     aligned (LOD_ERR_ARG otherwise).
  */
 #ifndef LOD_H
 #define LOD_H

@@ -173,3 +173,23 @@ def test_product_path_refuses_to_run_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lod, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         lod.lib()
+
+
+def test_misaligned_q_or_out_rejected():
+    """Queries and outputs are read and written 16 bytes at a time: both must be 16-byte
+    aligned, else every entry point returns LOD_ERR_ARG before enqueuing anything."""
+    cfg = lod.Config(n_q_heads=8, n_kv_heads=1)
+    L = lod.lib()
+    n = ctypes.c_size_t()
+    assert L.lod_index_bytes(_p(cfg), 1, 8192, ctypes.byref(n)) == 0
+    idx = lod.Index(FAKE.value, n.value, 1, 32)
+    kv = lod.KV(FAKE.value, FAKE.value, 0, 1024, 128)
+    odd = ctypes.c_void_p(0x10004)
+    E = lod.LOD_ERR_ARG
+    for qq, oo in ((odd, FAKE), (FAKE, odd)):
+        assert L.lod_attend_decode(_p(cfg), ctypes.byref(idx), kv, qq, FAKE, 1, 8192, oo, None, None,
+                                   FAKE, 1 << 40, None) == E
+        assert L.lod_attend_prefill(_p(cfg), ctypes.byref(idx), kv, qq, 0, 256, 1, oo, None, None,
+                                    FAKE, 1 << 40, None) == E
+        assert L.lod_dense_decode(_p(cfg), kv, qq, FAKE, 1, 8192, oo, FAKE, 1 << 40, None) == E
+        assert L.lod_dense_prefill(_p(cfg), kv, qq, 0, 256, 1, oo, None) == E
