@@ -57,137 +57,61 @@ struct FlashArgs {
     float* out;           // dense: normalised output [B][nq][Hq][d]
 };
 
+// K and V tiles are double buffered and loaded straight into LDS; both are row-major
+// with 16-byte chunks XOR-swizzled (K by row & 15, V by 2 (row & 7), so the 16 rows a
+// transposing read touches fall on distinct banks); V^T operands come from gfx950's
+// transposing LDS read.  Logits are kept in log2 units (exp2 weights); a partial
+// state's maximum is written back in natural units.
 template <int HG>
 struct FlashSmem {
-    alignas(16) bf16_t kt[kFlashKeys][kD];          // key tile, 16-byte chunks XOR-swizzled
-    alignas(16) bf16_t vT[kD][kFlashKeys + 4];      // value tile, transposed
-    float bias[kFlashKeys];
-    int kpos[kFlashKeys];                           // key position for the causal test
-    int32_t sel[kFlashRowHeads][kMaxTG];            // opened groups per column (LoD)
+    alignas(16) bf16_t kt[2][kFlashKeys][kD];  // key tiles (double buffer)
+    alignas(16) bf16_t vt[2][kFlashKeys][kD];  // value tiles (double buffer)
+    float bias[2][kFlashKeys];                 // log2 units; -inf: not a key
+    int kpos[2][kFlashKeys];                   // key position for the causal test (INT_MIN: none)
+    int32_t sel[kFlashRowHeads][kMaxTG];       // opened groups per column (LoD)
 };
 
-// One tile of nk keys: rows krow(k), vrow(k), bias bias_of(k) (-inf: not a key), causal
-// position pos_of(k) (INT_MIN: no causal test).
-template <int HG>
-struct FlashState {
-    f32x4_t O[2][8];  // O^T tiles: [column block][d block]
-    float m[2], l[2];
-};
+constexpr float kFlashLog2e = 1.4426950408889634f;
+constexpr float kFlashLn2 = 0.6931471805599453f;
 
-template <int HG, typename KRow, typename VRow, typename Bias, typename Pos>
-__device__ __forceinline__ void flash_tile(FlashSmem<HG>& s, FlashState<HG>& F, const bf16x8_t (*qb)[4],
-                                           int nk, KRow krow, VRow vrow, Bias bias_of, Pos pos_of,
-                                           const int* prow, const uint64_t* excl, float scale) {
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    // stage keys (direct to LDS, swizzled) and values (transposed)
-    for (int i = w; i < kFlashKeys / 4; i += 4) {
-        int row = 4 * i + (l >> 4);
-        const int cp = l & 15, c = cp ^ (row & 15);
-        const int rr = row < nk ? row : nk - 1;
-        __builtin_amdgcn_global_load_lds(krow(rr) + 8 * c, &s.kt[4 * i][0], 16, 0, 0);
-    }
-    uint4 vv[4];
+__device__ __forceinline__ int fswz_k(int row) { return row & 15; }
+__device__ __forceinline__ int fswz_v(int row) { return 2 * (row & 7); }
+
+typedef short fs16x4_t __attribute__((ext_vector_type(4)));
+typedef float ff32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 fbf16x2_t __attribute__((ext_vector_type(2)));
+
+// 4 bf16 of a V^T operand: this lane gets V[key0 + r][d0 + lane % 16] for r = 0..3,
+// where the 16 lanes of its group read (row key0 + i / 4, elements d0 + 4 (i % 4) ..).
+__device__ __forceinline__ fs16x4_t flash_vt_read(const bf16_t (*vt)[kD], int key0, int d0, int i) {
+    const int row = key0 + (i >> 2);
+    const int e = d0 + 4 * (i & 3);
+    const int chunk = (e >> 3) ^ fswz_v(row);
+    const bf16_t* p = &vt[row][8 * chunk + (e & 7)];
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) fs16x4_t*)(p));
+}
+
+// Load key tile (coarse, k0, nk) into buffer buf: the K and V rows straight into LDS (a
+// wave's 64 lanes fill four rows per instruction; rows past nk repeat the last key) and
+// the tile's bias (log2 units) and causal positions.  kb, vb: the rows' base (index
+// summaries for a coarse tile, else the cache of this head and sequence).
+template <int HG, bool PAGED>
+__device__ __forceinline__ void flash_issue(FlashSmem<HG>& s, const FlashArgs& A, int buf, int coarse, int k0, int nk,
+                                            const bf16_t* kb, const bf16_t* vb, const float* gln, int bs) {
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + kThreads * i, key = idx & 63, ch = idx >> 6;
-        const int kr = key < nk ? key : nk - 1;
-        vv[i] = *reinterpret_cast<const uint4*>(vrow(kr) + 8 * ch);
+    for (int ii = 0; ii < 4; ++ii) {
+        const int i = w + 4 * ii;
+        const int row = 4 * i + g;
+        const int rr = row < nk ? row : nk - 1;
+        const int64_t off = coarse ? (int64_t)(k0 + rr) * kD : kv_pos<PAGED>(A, bs, k0 + rr);
+        __builtin_amdgcn_global_load_lds(kb + off + 8 * (li ^ fswz_k(row)), &s.kt[buf][4 * i][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + off + 8 * (li ^ fswz_v(row)), &s.vt[buf][4 * i][0], 16, 0, 0);
     }
     if (tid < kFlashKeys) {
-        s.bias[tid] = tid < nk ? bias_of(tid) : -INFINITY;
-        s.kpos[tid] = tid < nk ? pos_of(tid) : INT_MIN;
+        s.bias[buf][tid] = tid < nk ? (coarse ? gln[k0 + tid] * kFlashLog2e : 0.0f) : -INFINITY;
+        s.kpos[buf][tid] = tid < nk && !coarse ? k0 + tid : INT_MIN;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + kThreads * i, key = idx & 63, ch = idx >> 6;
-        const uint32_t u[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s.vT[8 * ch + 2 * e][key] = (bf16_t)(u[e] & 0xffffu);
-            s.vT[8 * ch + 2 * e + 1][key] = (bf16_t)(u[e] >> 16);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // S^T = K Q^T for 4 key blocks x 2 column blocks
-    f32x4_t S[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
-        S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int row = 16 * kb + (l & 15);
-            const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
-            S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
-            S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
-        }
-    }
-    // logits, masks, online softmax (a column's 64 keys live in lanes l, l^16, l^32, l^48)
-    float P[4][2][4];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = 16 * kb + 4 * (l >> 4) + r;
-                const float b = s.bias[key];
-                const bool ok = b != -INFINITY && s.kpos[key] <= prow[cb] && !((excl[cb] >> key) & 1ull);
-                const float lam = ok ? __builtin_fmaf(scale, S[kb][cb][r], b) : -INFINITY;
-                P[kb][cb][r] = lam;
-                mt = fmaxf(mt, lam);
-            }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float mn = fmaxf(F.m[cb], mt);
-        const float a = F.m[cb] == -INFINITY ? 0.0f : softmax_exp(F.m[cb] - mn);
-        float ls = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float lam = P[kb][cb][r];
-                const float p = lam == -INFINITY ? 0.0f : softmax_exp(lam - mn);
-                P[kb][cb][r] = p;
-                ls += p;
-            }
-        F.l[cb] = __builtin_fmaf(F.l[cb], a, ls);
-        F.m[cb] = mn;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) F.O[cb][db] *= a;
-    }
-    // O^T += V^T P^T over two 32-key steps; P as bf16 hi + lo
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        bf16x8_t ph[2], pl[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                __bf16 h, lo;
-                split_bf16(P[2 * st + j / 4][cb][j % 4], h, lo);
-                ph[cb][j] = h;
-                pl[cb][j] = lo;
-            }
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const bf16_t* vr = &s.vT[16 * db + (l & 15)][32 * st + 4 * (l >> 4)];
-            const uint2 lo4 = *reinterpret_cast<const uint2*>(vr);
-            const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + 16);
-            const u32x4_t raw = {lo4.x, lo4.y, hi4.x, hi4.y};  // keys 8 (l/16) .. +7 of the step
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, raw);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                F.O[cb][db] = mfma16(a, ph[cb], F.O[cb][db]);
-                F.O[cb][db] = mfma16(a, pl[cb], F.O[cb][db]);
-            }
-        }
-    }
-    __syncthreads();
 }
 
 // Workgroup: 128 (row, head) columns = (128 / HG) query rows x HG heads of one KV head.
@@ -200,11 +124,12 @@ void prefill_flash_kernel(FlashArgs A) {
     const int nsplit = A.index ? A.nsplit : 1;
     const int tile = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
     const int kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
     const int r0 = tile * QT;
     const int nrows = min(QT, A.nq - r0);
     const int p_first = A.pos0 + r0, p_last = A.pos0 + r0 + nrows - 1;
     const int hq0 = kvh * HG;
+    const float sc2 = A.scale * kFlashLog2e;
 
     // Q^T operands for this lane's two columns, row positions, per-column masks
     bf16x8_t qb[2][4];
@@ -212,53 +137,53 @@ void prefill_flash_kernel(FlashArgs A) {
     int colrow[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-        const int n = 16 * (2 * w + cb) + (l & 15);
+        const int n = 16 * (2 * w + cb) + li;
         const int rl = n / HG, h = n % HG;
         colrow[cb] = rl;
         prow[cb] = rl < nrows ? A.pos0 + r0 + rl : INT_MIN;  // INT_MIN: no key passes
         const bf16_t* qr = A.q + (((int64_t)b * A.nq + r0 + min(rl, nrows - 1)) * A.Hq + hq0 + h) * kD;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * (l >> 4));
+            qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
     }
-    FlashState<HG> F;
+    f32x4_t O[2][8];
+    float m_run[2], l_run[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-        F.m[cb] = -INFINITY;
-        F.l[cb] = 0.0f;
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.0f;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) F.O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int db = 0; db < 8; ++db) O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
     }
     // head kvh of sequence bs; the row of position x adds kv_pos(A, bs, x)
     const bf16_t* kc = A.k + kvh * A.sh + kv_seq<PAGED>(A, bs);
     const bf16_t* vc = A.v + kvh * A.sh + kv_seq<PAGED>(A, bs);
-    uint64_t noex[2] = {0, 0};
 
+    // Key tiles.  Dense causal: keys [0, p_last] in tiles of 64.  LoD: coarse centroids
+    // (bias ln n, each column's opened groups masked), then the sinks, then the causal
+    // block window [nb*C, p]; split `split` of `nsplit` takes an equal share of the list.
+    int ct = 0, st = 0, ng = 0, ns = 0, w0 = 0, nt, t0 = 0, t1;
+    const bf16_t* gk = nullptr;
+    const bf16_t* gv = nullptr;
+    const float* gln = nullptr;
     if (A.index == nullptr) {
-        // dense causal: keys [0, p_last]
-        for (int k0 = 0; k0 <= p_last; k0 += kFlashKeys) {
-            const int nk = min(kFlashKeys, p_last + 1 - k0);
-            flash_tile<HG>(
-                s, F, qb, nk, [&](int r) { return kc + kv_pos<PAGED>(A, bs, k0 + r); },
-                [&](int r) { return vc + kv_pos<PAGED>(A, bs, k0 + r); }, [&](int) { return 0.0f; },
-                [&](int r) { return k0 + r; }, prow, noex, A.scale);
-        }
+        nt = (p_last + kFlashKeys) / kFlashKeys;
+        t1 = nt;
     } else {
-        // key tiles: coarse centroids, then the sinks, then the causal block window
-        // [nb*C, p]; split `split` of `nsplit` takes an equal share of the list
         const int nb = nbuilt_prefill(p_first, A.W);
-        const int ng = nb * A.G;
-        const int ns = min(A.n_sink, nb * kChunk);
-        const int w0 = nb * kChunk;
-        const int ct = A.drop ? 0 : (ng + kFlashKeys - 1) / kFlashKeys;  // no remainder: no centroids
-        const int st = (ns + kFlashKeys - 1) / kFlashKeys;
+        ng = nb * A.G;
+        ns = min(A.n_sink, nb * kChunk);
+        w0 = nb * kChunk;
+        ct = A.drop ? 0 : (ng + kFlashKeys - 1) / kFlashKeys;  // no remainder: no centroids
+        st = (ns + kFlashKeys - 1) / kFlashKeys;
         const int wt = p_last >= w0 ? (p_last - w0) / kFlashKeys + 1 : 0;
-        const int nt = ct + st + wt;
-        const int t0 = split * nt / nsplit, t1 = (split + 1) * nt / nsplit;
+        nt = ct + st + wt;
+        t0 = split * nt / nsplit;
+        t1 = (split + 1) * nt / nsplit;
         const int64_t gbase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.G;
-        const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
-        const bf16_t* gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
-        const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
+        gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
+        gv = reinterpret_cast<const bf16_t*>(A.index + A.L.gv) + gbase * kD;
+        gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
         if (t0 < ct) {
             // opened groups of the tile's columns (left out of the coarse terms)
             for (int x = tid; x < kFlashRowHeads * A.TG; x += kThreads) {
@@ -268,43 +193,151 @@ void prefill_flash_kernel(FlashArgs A) {
             }
             __syncthreads();
         }
-        for (int t = t0; t < t1; ++t) {
-            // one tile description for all three kinds keeps a single flash_tile body
-            const bool coarse = t < ct, sink = !coarse && t < ct + st;
-            const int k0 = coarse ? t * kFlashKeys : (sink ? (t - ct) * kFlashKeys : w0 + (t - ct - st) * kFlashKeys);
-            const int nk = coarse ? min(kFlashKeys, ng - k0) : (sink ? min(kFlashKeys, ns - k0) : min(kFlashKeys, p_last + 1 - k0));
-            const bf16_t* kt = coarse ? gk + (int64_t)k0 * kD : kc;  // coarse: index rows; else cache rows
-            const bf16_t* vt = coarse ? gv + (int64_t)k0 * kD : vc;
-            auto roff = [&](int r) { return coarse ? (int64_t)r * kD : kv_pos<PAGED>(A, bs, k0 + r); };
-            uint64_t ex[2] = {0, 0};
-            if (coarse) {
+    }
+    // tile t: kind (0 coarse, 1 sinks / window / dense run), first key, key count
+    auto tile_of = [&](int t, int& coarse, int& k0, int& nk) {
+        if (A.index == nullptr) {
+            coarse = 0;
+            k0 = t * kFlashKeys;
+            nk = min(kFlashKeys, p_last + 1 - k0);
+        } else if (t < ct) {
+            coarse = 1;
+            k0 = t * kFlashKeys;
+            nk = min(kFlashKeys, ng - k0);
+        } else if (t < ct + st) {
+            coarse = 0;
+            k0 = (t - ct) * kFlashKeys;
+            nk = min(kFlashKeys, ns - k0);
+        } else {
+            coarse = 0;
+            k0 = w0 + (t - ct - st) * kFlashKeys;
+            nk = min(kFlashKeys, p_last + 1 - k0);
+        }
+    };
+    if (t0 < t1) {
+        int coarse, k0, nk;
+        tile_of(t0, coarse, k0, nk);
+        flash_issue<HG, PAGED>(s, A, 0, coarse, k0, nk, coarse ? gk : kc, coarse ? gv : vc, gln, bs);
+    }
+    for (int t = t0; t < t1; ++t) {
+        const int buf = (t - t0) & 1;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        int coarse, k0, nk;
+        if (t + 1 < t1) {
+            tile_of(t + 1, coarse, k0, nk);
+            flash_issue<HG, PAGED>(s, A, buf ^ 1, coarse, k0, nk, coarse ? gk : kc, coarse ? gv : vc, gln, bs);
+        }
+        tile_of(t, coarse, k0, nk);
+        // excluded keys of this lane's columns: their opened groups inside a coarse tile
+        uint64_t ex[2] = {0, 0};
+        if (coarse) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int n = 16 * (2 * w + cb) + li;
+                uint64_t msk = 0;
+                for (int u = 0; u < A.TG; ++u) {
+                    const int gg = s.sel[n][u] - k0;
+                    if (gg >= 0 && gg < kFlashKeys) msk |= 1ull << gg;
+                }
+                ex[cb] = msk;
+            }
+        }
+        // S^T = K Q^T for 4 key blocks x 2 column blocks
+        f32x4_t S[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
+            S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int row = 16 * kb + li;
+                const int chunk = (4 * kk + g) ^ fswz_k(row);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[buf][row][8 * chunk]);
+                S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
+                S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
+            }
+        }
+        // logits (log2 units), masks, online softmax (a column's 64 keys live in lanes
+        // l, l^16, l^32, l^48).  A column may see no key in a tile (all masked): its
+        // maximum then stays -inf and the guards below keep every weight 0.
+        float P[4][2][4];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 16 * kb + 4 * g + r;
+                    const bool ok = s.kpos[buf][key] <= prow[cb] && !((ex[cb] >> key) & 1ull);
+                    const float lam = ok ? __builtin_fmaf(sc2, S[kb][cb][r], s.bias[buf][key]) : -INFINITY;
+                    P[kb][cb][r] = lam;
+                    mt = fmaxf(mt, lam);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mn = fmaxf(m_run[cb], mt);
+            const float a = m_run[cb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[cb] - mn);
+            const float ms = mn == -INFINITY ? 0.0f : mn;
+            float ls = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(P[kb][cb][r] - ms);  // exp2(-inf) = 0
+                    P[kb][cb][r] = p;
+                    ls += p;
+                }
+            l_run[cb] = __builtin_fmaf(l_run[cb], a, ls);
+            m_run[cb] = mn;
+            if (__any(a != 1.0f)) {  // the maximum moved for some column of the wave
+#pragma unroll
+                for (int db = 0; db < 8; ++db) O[cb][db] *= a;
+            }
+        }
+        // O^T += V^T P^T over two 32-key steps.  MFMA k index e of lane group g is key
+        // 32 st + 16 (e / 4) + 4 g + e % 4 on both operands; P as bf16 hi + lo.
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            bf16x8_t ph[2], pl[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {  // two at a time: one packed conversion each
+                    const ff32x2_t x = {P[2 * sp + j / 4][cb][j % 4], P[2 * sp + j / 4][cb][j % 4 + 1]};
+                    const fbf16x2_t h = __builtin_convertvector(x, fbf16x2_t);
+                    const ff32x2_t r = x - __builtin_convertvector(h, ff32x2_t);
+                    const fbf16x2_t lo = __builtin_convertvector(r, fbf16x2_t);
+                    ph[cb][j] = h[0];
+                    ph[cb][j + 1] = h[1];
+                    pl[cb][j] = lo[0];
+                    pl[cb][j + 1] = lo[1];
+                }
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const fs16x4_t v0 = flash_vt_read(s.vt[buf], 32 * sp + 4 * g, 16 * db, li);
+                const fs16x4_t v1 = flash_vt_read(s.vt[buf], 32 * sp + 16 + 4 * g, 16 * db, li);
+                const fs16x4_t both[2] = {v0, v1};
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    const int n = 16 * (2 * w + cb) + (l & 15);
-                    uint64_t msk = 0;
-                    for (int u = 0; u < A.TG; ++u) {
-                        const int g = s.sel[n][u] - k0;
-                        if (g >= 0 && g < kFlashKeys) msk |= 1ull << g;
-                    }
-                    ex[cb] = msk;
+                    O[cb][db] = mfma16(av, ph[cb], O[cb][db]);
+                    O[cb][db] = mfma16(av, pl[cb], O[cb][db]);
                 }
             }
-            flash_tile<HG>(
-                s, F, qb, nk, [&](int r) { return kt + roff(r); }, [&](int r) { return vt + roff(r); },
-                [&](int r) { return coarse ? gln[k0 + r] : 0.0f; }, [&](int r) { return coarse ? INT_MIN : k0 + r; },
-                prow, ex, A.scale);
         }
     }
 
     // column totals (the 4 lanes of a column hold partial sums), then write
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-        float lt = F.l[cb];
+        float lt = l_run[cb];
         lt += __shfl_xor(lt, 16, 64);
         lt += __shfl_xor(lt, 32, 64);
         const int rl = colrow[cb];
         if (rl >= nrows) continue;
-        const int n = 16 * (2 * w + cb) + (l & 15);
+        const int n = 16 * (2 * w + cb) + li;
         const int h = n % HG;
         const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h;
         if (A.index == nullptr) {
@@ -312,19 +345,19 @@ void prefill_flash_kernel(FlashArgs A) {
             const float inv = 1.0f / lt;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const f32x4_t o = F.O[cb][db];
-                *reinterpret_cast<float4*>(dst + 16 * db + 4 * (l >> 4)) =
+                const f32x4_t o = O[cb][db];
+                *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) =
                     make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
             }
         } else {
             float* dst = A.part + split * A.split_stride + rh * kPartStride;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const f32x4_t o = F.O[cb][db];
-                *reinterpret_cast<float4*>(dst + 16 * db + 4 * (l >> 4)) = make_float4(o[0], o[1], o[2], o[3]);
+                const f32x4_t o = O[cb][db];
+                *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
             }
-            if ((l >> 4) == 0) {
-                dst[kD] = F.m[cb];
+            if (g == 0) {
+                dst[kD] = m_run[cb] == -INFINITY ? -INFINITY : m_run[cb] * kFlashLn2;  // natural units
                 dst[kD + 1] = lt;
             }
         }
