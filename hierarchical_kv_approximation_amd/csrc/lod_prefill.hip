@@ -1023,6 +1023,8 @@ void prefill_select_kernel(SelArgs A) {
 // A unit is (sequence, KV head, 256-row query chunk of the launch); its pairs are
 // (row, head, slot) with pair index (row_in_chunk * HG + head) * TG + slot.
 constexpr int kMaxBucketGroups = 16384;  // summarised groups per KV head a prefill supports
+constexpr int kBucketThreads = 1024;     // threads of a bucket workgroup
+constexpr int kBucketPer = kChunk * 8 * kMaxTG / kBucketThreads;  // pairs per bucket thread, at most
 
 struct PagesArgs {
     const bf16_t* k;
@@ -1052,8 +1054,9 @@ struct PagesArgs {
 };
 
 template <int HG>
-__global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
+__global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArgs A) {
     __shared__ int cnt[kMaxBucketGroups];
+    __shared__ int wsum[kBucketThreads / 64];
     const int qc = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int r0 = qc * kChunk;
@@ -1063,30 +1066,31 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
     const int npairs = nrows * HG * A.TG;
     const int64_t unit = ((int64_t)b * A.Hkv + kvh) * A.units_per_seq_kv + qc;
     int2* list = A.plist + unit * (kChunk * HG * A.TG);
-    auto pair_gid = [&](int x) {
-        const int t = x % A.TG, h = (x / A.TG) % HG, rl = x / (A.TG * HG);
-        return A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t];
-    };
-    for (int g = tid; g < ng; g += kThreads) cnt[g] = 0;
-    __syncthreads();
-    // group ids of 8 pairs per thread loaded together, then counted
-    constexpr int U = 8;
-    for (int x0 = tid; x0 < npairs; x0 += U * kThreads) {
-        int g[U];
+    for (int g = tid; g < ng; g += kBucketThreads) cnt[g] = 0;
+    // the group id of every pair this thread owns (pairs tid, tid + 1024, ...), loaded
+    // together and kept for both passes
+    int gid[kBucketPer];
 #pragma unroll
-        for (int u = 0; u < U; ++u) g[u] = x0 + u * kThreads < npairs ? pair_gid(x0 + u * kThreads) : -1;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (g[u] >= 0) atomicAdd(&cnt[g[u]], 1);
+    for (int u = 0; u < kBucketPer; ++u) {
+        const int x = tid + u * kBucketThreads;
+        if (x < npairs) {
+            const int t = x % A.TG, h = (x / A.TG) % HG, rl = x / (A.TG * HG);
+            gid[u] = A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t];
+        } else {
+            gid[u] = -1;
+        }
     }
     __syncthreads();
-    // exclusive scan of the counts: contiguous ranges per thread, then the 256 range sums
-    // by wave prefix sums and the waves' totals
-    const int per = (ng + kThreads - 1) / kThreads;
+#pragma unroll
+    for (int u = 0; u < kBucketPer; ++u)
+        if (gid[u] >= 0) atomicAdd(&cnt[gid[u]], 1);
+    __syncthreads();
+    // exclusive scan of the counts: contiguous ranges per thread, then the range sums by
+    // wave prefix sums and the waves' totals
+    const int per = (ng + kBucketThreads - 1) / kBucketThreads;
     const int g0 = tid * per, g1 = min(ng, g0 + per);
     int sum = 0;
     for (int g = g0; g < g1; ++g) sum += cnt[g];
-    __shared__ int wsum[kThreads / 64];
     const int lane = tid & 63, wv = tid >> 6;
     int incl = sum;
 #pragma unroll
@@ -1098,7 +1102,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
-    for (int x = 0; x < kThreads / 64; ++x) {
+    for (int x = 0; x < kBucketThreads / 64; ++x) {
         before += x < wv ? wsum[x] : 0;
         total += wsum[x];
     }
@@ -1106,14 +1110,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bucket_kernel(PagesArgs A) {
     int acc = before + incl - sum;
     for (int g = g0; g < g1; ++g) { const int v = cnt[g]; cnt[g] = acc; acc += v; }
     __syncthreads();
-    for (int x0 = tid; x0 < npairs; x0 += U * kThreads) {
-        int g[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) g[u] = x0 + u * kThreads < npairs ? pair_gid(x0 + u * kThreads) : -1;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (g[u] >= 0) list[atomicAdd(&cnt[g[u]], 1)] = make_int2(x0 + u * kThreads, g[u]);
-    }
+    for (int u = 0; u < kBucketPer; ++u)
+        if (gid[u] >= 0) list[atomicAdd(&cnt[gid[u]], 1)] = make_int2(tid + u * kBucketThreads, gid[u]);
 }
 
 // ---------------------------------------------------------------------------- pages
@@ -1410,7 +1409,7 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
         hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
                            st, F);
     trace_point(3, st);
-    hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kThreads), 0, st, P);
+    hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kBucketThreads), 0, st, P);
     trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
     const dim3 pgrid((maxpairs + kPairsPerWG - 1) / kPairsPerWG, nunits_q * S.Hkv * batch);
