@@ -1386,9 +1386,41 @@ static PrefillPlan plan_prefill(const lod_params* p, int n_q) {
     return P;
 }
 
+// A second stream on the caller's device, with two events, per host thread: the flash
+// kernel runs on it beside the bucket and pages kernels (all three need only the
+// selection), forked after the selection and joined before the combine.  Created by the
+// thread's first prefill call on that device and kept until the thread ends.
+struct PrefillSide {
+    hipStream_t st;
+    hipEvent_t fork, join;
+};
+static int prefill_side(hipStream_t caller, PrefillSide& out) {
+    constexpr int kMaxDev = 64;
+    static thread_local PrefillSide cache[kMaxDev] = {};
+    int dev = 0;
+    if (caller ? hipStreamGetDevice(caller, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return LOD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDev) return LOD_ERR_HIP;
+    PrefillSide& c = cache[dev];
+    if (!c.st) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return LOD_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return LOD_ERR_HIP;
+        PrefillSide n{};
+        hipError_t e = hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return LOD_ERR_HIP;
+        c = n;
+    }
+    out = c;
+    return LOD_OK;
+}
+
 template <int HG>
-static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const PagesArgs& P, int batch,
-                                 int nunits_q, hipStream_t st) {
+static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const PagesArgs& P, int batch,
+                                int nunits_q, hipStream_t st, const PrefillSide& side) {
     constexpr int QT = kFlashRowHeads / HG;
     const int ntiles = (S.nq + QT - 1) / QT;
     trace_point(0, st);
@@ -1402,13 +1434,17 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     trace_point(1, st);
     hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
     trace_point(2, st);
+    // fork: the flash kernel on the side stream, bucket and pages on the caller's
+    if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(side.st, side.fork, 0) != hipSuccess)
+        return LOD_ERR_HIP;
     if (F.btab)
         hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
-                           st, F);
+                           side.st, F);
     else
         hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
-                           st, F);
-    trace_point(3, st);
+                           side.st, F);
+    trace_point(3, side.st);
+    if (hipEventRecord(side.join, side.st) != hipSuccess) return LOD_ERR_HIP;
     hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kBucketThreads), 0, st, P);
     trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
@@ -1420,10 +1456,12 @@ static void launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Pag
     else
         hipLaunchKernelGGL((prefill_pages_kernel<HG, false, false>), pgrid, dim3(kThreads), 0, st, P);
     trace_point(5, st);
+    if (hipStreamWaitEvent(st, side.join, 0) != hipSuccess) return LOD_ERR_HIP;  // join
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + kThreads / 32 - 1) / (kThreads / 32))),
                        dim3(kThreads), 0, st, P, nrh);
     trace_point(6, st);
+    return LOD_OK;
 }
 
 }  // namespace lodi
@@ -1513,6 +1551,8 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
     const int Hq = params->n_q_heads, Hkv = params->n_kv_heads, HG = Hq / Hkv, TG = params->top_groups;
     const int TPW = params->top_pages > 0 ? params->top_pages : 1;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    PrefillSide side;
+    if ((rc = prefill_side(st, side)) != LOD_OK) return rc;
     for (int r0 = 0; r0 < n_q; r0 += P.rows) {
         const int rows = (n_q - r0) < P.rows ? (n_q - r0) : P.rows;
         const int nunits_q = (rows + kChunk - 1) / kChunk;
@@ -1564,11 +1604,12 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.out = out + row0 * Hq * kD;
             G.units_per_seq_kv = nunits_q;
             switch (HG) {
-                case 1: launch_prefill_batch<1>(S, F, G, 1, nunits_q, st); break;
-                case 2: launch_prefill_batch<2>(S, F, G, 1, nunits_q, st); break;
-                case 4: launch_prefill_batch<4>(S, F, G, 1, nunits_q, st); break;
-                default: launch_prefill_batch<8>(S, F, G, 1, nunits_q, st); break;
+                case 1: rc = launch_prefill_batch<1>(S, F, G, 1, nunits_q, st, side); break;
+                case 2: rc = launch_prefill_batch<2>(S, F, G, 1, nunits_q, st, side); break;
+                case 4: rc = launch_prefill_batch<4>(S, F, G, 1, nunits_q, st, side); break;
+                default: rc = launch_prefill_batch<8>(S, F, G, 1, nunits_q, st, side); break;
             }
+            if (rc != LOD_OK) return rc;
         }
         if (hipGetLastError() != hipSuccess) return LOD_ERR_HIP;
     }

@@ -18,7 +18,10 @@
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
  *     buffer; the library never allocates device memory and keeps no state apart from
- *     the optional trace events of lod_trace_events.
+ *     the optional trace events of lod_trace_events and, per host thread and device, one
+ *     extra stream with two events that the first bf16 lod_attend_prefill call creates
+ *     (the call runs one of its kernels there, ordered after the caller's earlier work
+ *     and before its later work by those events, so the stream-ordering contract holds).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work;
  *     they return before the GPU finishes.  Device faults surface at the caller's next
  *     synchronisation of that stream.
@@ -344,7 +347,9 @@ int lod_video_dense(const lod_video_params* params, lod_kv kv, const void* q, in
  * same host thread
  * records events[0] on its stream before its first kernel and events[1 + k] after its
  * k-th kernel (decode: k = 0 scan, 1 open-and-combine; bf16 prefill: k = 0 candidate
- * sweep, 1 select, 2 flash, 3 bucket, 4 pages, 5 combine, recorded again for every batch
+ * sweep, 1 select, 2 flash (recorded on the call's second stream: flash runs beside
+ * bucket and pages, so events[4] follows events[2], not events[3]), 3 bucket, 4 pages,
+ * 5 combine, recorded again for every batch
  * of rows, so the last batch's times remain; lod_video_attend: k = 0 summaries, 1 choice,
  * 2 attention).  `events` points to n_events
  * hipEvent_t handles created by the caller, who reads them with hipEventElapsedTime;
