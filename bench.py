@@ -162,6 +162,7 @@ def main():
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-KV-view decode timing")
     ap.add_argument("--no-int4", action="store_true", help="skip the INT4-pages decode timing")
     ap.add_argument("--no-video", action="store_true", help="skip the video LoD measurement")
+    ap.add_argument("--no-batch1", action="store_true", help="skip the batch-1 decode measurement")
     ap.add_argument("--only-video", action="store_true",
                     help="measure video LoD only and print its JSON object (for profiling)")
     ap.add_argument("--video-calls", type=int, default=20)
@@ -396,6 +397,11 @@ def main():
     del layers, ws
     torch.cuda.empty_cache()
 
+    batch1 = None
+    if not args.no_batch1:
+        batch1 = bench_batch1(torch, lod, synth, cfg, hip, stream, T, args.seed, dense=not args.no_dense)
+        torch.cuda.empty_cache()
+
     sweep = None
     if not args.no_sweep:
         sweep = bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, args.prefill_ctx, args.seed)
@@ -458,6 +464,7 @@ def main():
             "sparsity_ablation": sparse,
             "paged_kv_view": paged,
             "int4_pages": int4,
+            "batch1": batch1,
             "setup_s": round(setup_s, 1),
         },
         "prefill": prefill,
@@ -714,6 +721,91 @@ def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, s
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_batch1(torch, lod, synth, cfg, hip, stream, T, seed, layers=8, reps=32, dense=True):
+    """Decode at batch 1 and context T on `layers` layer copies: back-to-back calls
+    rotating over the copies, and the same 8 calls captured in one HIP graph and replayed
+    (launch costs hidden, as a model's decode step would run them); dense decode on the
+    same copies.  The position sits just after a chunk boundary's build (no build inside)."""
+    dev = torch.device("cuda:0")
+    C = cfg.chunk_size
+    nb = max(0, (T - 1) // C - cfg.window // C + 1)
+    Ls = []
+    for li in range(layers):
+        K, V, cen, _ = synth.clustered_kv(1, T, cfg.n_kv_heads, cfg.head_dim, seed=seed + 301 + 7 * li, device=dev)
+        q = synth.queries(1, cfg.n_q_heads, cen, seed=seed + 302 + 7 * li)
+        idx = lod.LodIndex.allocate(cfg, 1, T, device=dev)
+        lod.build_chunk(cfg, idx, K, V, 0, nb)
+        Ls.append((K, V, q, idx))
+        del cen
+    seq = torch.tensor([T], dtype=torch.int32, device=dev)
+    ws = torch.empty(lod.decode_ws_bytes(cfg, 1, T), dtype=torch.uint8, device=dev)
+    out = torch.empty(1, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+
+    def step(i):
+        K, V, q, idx = Ls[i % layers]
+        lod.attend_decode(cfg, idx, K, V, q, seq, T, ws=ws, out=out)
+
+    def timed(fn, n):
+        e = hip.create(2)
+        hip.record(e[0], stream)
+        fn(n)
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(e[0], e[1])
+        hip.destroy(e)
+        return ms
+
+    for i in range(2 * layers):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = timed(lambda n: [step(i) for i in range(n)], layers * reps) / (layers * reps)
+    # one graph of `layers` calls (one per layer copy), replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(layers):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(layers):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    stream_now = torch.cuda.current_stream().cuda_stream
+    e = hip.create(2)
+    hip.record(e[0], stream_now)
+    for _ in range(reps):
+        g.replay()
+    hip.record(e[1], stream_now)
+    torch.cuda.synchronize()
+    graph_ms = hip.ms(e[0], e[1]) / (layers * reps)
+    hip.destroy(e)
+    del g
+    res = {"what": f"batch 1 at context {T}, {layers} layer copies; eager back-to-back calls and a graph of "
+                   f"{layers} calls (one per copy) replayed {reps} times",
+           "us_per_call": round(eager_ms * 1000, 2), "us_per_call_graph": round(graph_ms * 1000, 2),
+           "tok_per_s_graph": round(1000.0 / graph_ms, 1)}
+    if dense:
+        wsd = torch.empty(lod.dense_decode_ws_bytes(cfg, 1, T), dtype=torch.uint8, device=dev)
+        outd = torch.empty_like(out)
+
+        def dstep(n):
+            for i in range(n):
+                K, V, q, _ = Ls[i % layers]
+                lod.dense_decode(cfg, K, V, q, seq, T, ws=wsd, out=outd)
+        dstep(layers)
+        torch.cuda.synchronize()
+        dms = timed(dstep, 2 * layers) / (2 * layers)
+        res["dense_us_per_call"] = round(dms * 1000, 2)
+        res["lod_speedup_vs_dense"] = round(dms / graph_ms, 2)
+        res["lod_speedup_vs_dense_eager"] = round(dms / eager_ms, 2)
+    log(f"batch 1: {res['us_per_call']} us/call eager, {res['us_per_call_graph']} us/call in a graph")
+    del Ls, ws, out
+    return res
 
 
 def video_flops(torch, sel, counts, d, drop):
