@@ -623,6 +623,8 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
         "roofline": {"bound": "mfma", "kernel": "prefill_flash_kernel (coarse + sinks + window)",
                      "achieved": round(flash_tfs, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(flash_tfs / 2500.0, 4),
+                     "note": "the kernel runs on a second stream beside bucket + pages: its interval "
+                             "includes the time it shares the GPU with them",
                      "algorithmic_flops": int(flash_flops), "launches": nq,
                      "avg_launch_us": round(per["flash"] / nq * 1000, 2)},
         "select_algorithmic_flops": int(select_flops),

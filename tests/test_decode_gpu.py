@@ -204,3 +204,15 @@ def test_c3_full_size_128k_batch8_sampled():
     q = case.queries(seed=22)
     heads = [(b, kvh * 8 + i) for b, kvh in keys for i in range(8)]
     _decode_and_compare(case, (st, oidx), [131072] * 8, q, check_heads=heads)
+
+
+@pytest.mark.parametrize("T", [65536, 131072])
+def test_batch1_long_context_one_kv_head(T):
+    """One sequence with one KV head at 64K and 128K: the scan splits the unit into its
+    largest number of workgroups (40), whose partial states the open step merges."""
+    g, o = configs(torch.bfloat16, 8, 1, G=8, W=512, S=4)
+    case = Case(g, o, 1, T, seed=23, gen_device="cuda")
+    case.build_gpu()
+    keys = [(0, 0)]
+    st, oidx = case.oracle_index(keys)
+    _decode_and_compare(case, (st, oidx), [T], case.queries(seed=24))
