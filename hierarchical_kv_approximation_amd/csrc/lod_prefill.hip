@@ -890,6 +890,7 @@ void prefill_select_kernel(SelArgs A) {
             int k = 0;  // surely-out candidates (key 0) are never opened
 #pragma unroll
             for (int e = 0; e < kMaxTG; ++e) k += (e < TG && top[e] != 0) ? 1 : 0;
+#pragma unroll
             for (int e = 0; e < kMaxTG; ++e)
                 if (e < TG) s.sel[n][e] = e < k ? (int)key_id(top[e]) : -1;
             s.nsel[n] = k;
@@ -979,7 +980,8 @@ void prefill_select_kernel(SelArgs A) {
                 // every page opened: no ranking, and no unopened page needs a logit
                 R.open = npg >= 32 ? 0xffffffffu : ((1u << npg) - 1u);
             } else {
-                uint64_t key[kPage];
+                uint64_t key[kPage];  // every index below is static: the record stays in registers
+#pragma unroll
                 for (int e = 0; e < kPage; ++e) {
                     key[e] = 0;
                     if (e < npg) {
@@ -988,7 +990,9 @@ void prefill_select_kernel(SelArgs A) {
                     }
                 }
                 const int nopen = min(npg, A.TP);
-                for (int k = 0; k < nopen; ++k) {
+#pragma unroll
+                for (int k = 0; k < kPage; ++k) {
+                    if (k >= nopen) break;
                     // largest remaining key (register-resident: static indices only)
                     uint64_t bk = 0;
                     int best = 0;
@@ -1012,10 +1016,13 @@ void prefill_select_kernel(SelArgs A) {
         }
         A.rec[rh * TG + pos] = R;
         if (R.gid < 0) A.part_pg[(rh * TG + pos) * kPartStride + kD] = -INFINITY;  // no pages kernel pair
-        if (A.sel_pages)
-            for (int k = 0; k < TPW; ++k)
-                A.sel_pages[(rh * TG + t) * TPW + k] =
-                    (A.TP > 0 && R.gid >= 0 && k < kPage && slot_rank[k] >= 0) ? R.ps0 + slot_rank[k] : -1;
+        if (A.sel_pages) {
+#pragma unroll
+            for (int k = 0; k < kPage; ++k)
+                if (k < TPW)
+                    A.sel_pages[(rh * TG + t) * TPW + k] =
+                        (A.TP > 0 && R.gid >= 0 && slot_rank[k] >= 0) ? R.ps0 + slot_rank[k] : -1;
+        }
     }
 }
 // ---------------------------------------------------------------------------- bucket
