@@ -579,7 +579,7 @@ void prefill_cand_kernel(SelArgs A) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < R; ++e) lst[cb][e] = -INFINITY;
-    sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
+    sweep([&](int, int buf, int nk, f32x4_t (*S)[2]) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -992,18 +992,19 @@ void prefill_select_kernel(SelArgs A) {
                 const int nopen = min(npg, A.TP);
 #pragma unroll
                 for (int k = 0; k < kPage; ++k) {
-                    if (k >= nopen) break;
-                    // largest remaining key (register-resident: static indices only)
-                    uint64_t bk = 0;
-                    int best = 0;
+                    if (k < nopen) {
+                        // largest remaining key (register-resident: static indices only)
+                        uint64_t bk = 0;
+                        int best = 0;
 #pragma unroll
-                    for (int e = 0; e < kPage; ++e)
-                        if (key[e] > bk) { bk = key[e]; best = e; }
+                        for (int e = 0; e < kPage; ++e)
+                            if (key[e] > bk) { bk = key[e]; best = e; }
 #pragma unroll
-                    for (int e = 0; e < kPage; ++e)
-                        if (e == best) key[e] = 0;
-                    slot_rank[k] = best;
-                    R.open |= 1u << best;
+                        for (int e = 0; e < kPage; ++e)
+                            if (e == best) key[e] = 0;
+                        slot_rank[k] = best;
+                        R.open |= 1u << best;
+                    }
                 }
             }
         }
