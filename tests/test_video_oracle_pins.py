@@ -215,3 +215,31 @@ def test_query_heads_use_their_kv_head_and_choose_independently():
         assert np.array_equal(one["sel"][0, 0], r["sel"][0, h])
         assert np.array_equal(one["out"][0, :, 0], r["out"][0, :, h])
     assert not np.array_equal(r["sel"][0, 0], r["sel"][0, 1])
+
+
+def test_hand_worked_example():
+    """tests/golden/video_worked_example.json: a 1x2x4 grid with 1x2x2 blocks, d = 2, c = 1,
+    worked by hand from the definitions (block means, a tied score going to the lower
+    block id, LoD and dense outputs in closed form)."""
+    import json
+    import os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "video_worked_example.json")))
+    gr = fx["grid"]
+    cfg = vo.VideoConfig(d=gr["d"], frames=gr["frames"], height=gr["height"], width=gr["width"],
+                         block=tuple(gr["block"]), top_blocks=gr["top_blocks"], scale=gr["scale"], bf16=False)
+    K = np.array(fx["K"], np.float32)[None, :, None, :]
+    V = np.array(fx["V"], np.float32)[None, :, None, :]
+    Q = np.array(fx["Q"], np.float32)[None, :, None, :]
+    r = vo.forward(cfg, Q, K, V, dense=True)
+    ex = fx["expected"]
+    assert np.array_equal(r["kbar"][0, 0], np.array(ex["kbar"], np.float32))
+    assert np.array_equal(r["vbar"][0, 0], np.array(ex["vbar"], np.float32))
+    assert np.array_equal(r["qbar"][0, 0], np.array(ex["qbar"], np.float32))
+    assert list(r["count"]) == ex["count"]
+    assert r["sel"][0, 0].tolist() == ex["sel"]
+    for t in (0, 1, 4, 5):
+        assert np.allclose(r["out"][0, t, 0], ex["lod_block0_query"]["value"], rtol=0, atol=1e-12)
+        assert np.allclose(r["dense"][0, t, 0], ex["dense_block0_query"]["value"], rtol=0, atol=1e-12)
+    for t in (2, 3, 6, 7):
+        assert np.allclose(r["out"][0, t, 0], ex["lod_block1_query"]["value"], rtol=0, atol=1e-12)
+        assert np.allclose(r["dense"][0, t, 0], ex["dense_block1_query"]["value"], rtol=0, atol=1e-12)
