@@ -678,29 +678,33 @@ void prefill_cand_kernel(SelArgs A) {
     }
 }
 
+constexpr int kSelCols = 64;  // (row, head) columns per select workgroup: half a column tile
+
+template <int NC>
 struct SelSmem {
-    float T[kFlashRowHeads];
-    int cnt[kFlashRowHeads];
-    int32_t cg[kFlashRowHeads][kCandCap];  // candidates: group id, upper bound of the canonical
-    float cub[kFlashRowHeads][kCandCap];   // score (then the score itself where computed),
-    float clb[kFlashRowHeads][kCandCap];   // lower bound, class (0 surely not opened, 1
-    uint8_t cls[kFlashRowHeads][kCandCap]; // needs the chain, 2 surely opened)
-    float qn[kFlashRowHeads];              // |q| per column, rounded up
-    int32_t sel[kFlashRowHeads][kMaxTG];  // rank order
-    int nsel[kFlashRowHeads];
+    float T[NC];
+    int cnt[NC];
+    int32_t cg[NC][kCandCap];  // candidates: group id, upper bound of the canonical
+    float cub[NC][kCandCap];   // score (then the score itself where computed),
+    float clb[NC][kCandCap];   // lower bound, class (0 surely not opened, 1
+    uint8_t cls[NC][kCandCap]; // needs the chain, 2 surely opened)
+    float qn[NC];              // |q| per column, rounded up
+    int32_t sel[NC][kMaxTG];   // rank order
+    int nsel[NC];
     uint64_t red[4];
     int any_overflow;
 };
 
-// Selection of 128 (row, head) columns from the candidate lists of the sweeps: global
-// threshold, candidates, exact top TG under the canonical chain, then page ranking of
-// every opened group.
-template <int HG>
+// Selection of NC (row, head) columns -- columns c0 .. c0 + NC - 1 of a 128-column tile
+// -- from the candidate lists of the sweeps: global threshold, candidates, exact top TG
+// under the canonical chain, then page ranking of every opened group.
+template <int HG, int NC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_select_kernel(SelArgs A) {
-    __shared__ SelSmem s;
+    __shared__ SelSmem<NC> s;
     constexpr int QT = kFlashRowHeads / HG;
-    const SelSlot slot = sel_slot(A.Hkv, 1);
+    const SelSlot slot = sel_slot(A.Hkv, kFlashRowHeads / NC);  // split field: the column group
+    const int c0 = slot.split * NC;
     const int tile = slot.tile, kvh = slot.kvh, b = blockIdx.z, bs = A.seq + b;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int r0 = tile * QT;
@@ -714,18 +718,18 @@ void prefill_select_kernel(SelArgs A) {
     const bf16_t* gk = reinterpret_cast<const bf16_t*>(A.index + A.L.gk) + gbase * kD;
     const float* gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
     auto qrow = [&](int n) {  // column n -> its query row (clamped into the tile)
-        const int rl = min(n / HG, nrows - 1);
-        return A.q + (((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG) * kD;
+        const int rl = min((c0 + n) / HG, nrows - 1);
+        return A.q + (((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + (c0 + n) % HG) * kD;
     };
-    auto col_of = [&](int n) { return ((int64_t)b * A.nq + r0 + n / HG) * A.Hq + hq0 + n % HG; };
+    auto col_of = [&](int n) { return ((int64_t)b * A.nq + r0 + (c0 + n) / HG) * A.Hq + hq0 + (c0 + n) % HG; };
 
     // global threshold per column: the TG-th largest of the splits' top lists (they hold
     // the TG largest lower bounds of every split, hence those of all groups)
-    if (tid < kFlashRowHeads) {
+    if (tid < NC) {
         const int n = tid;
         float T = -INFINITY;
         int over = 0;
-        if (n / HG < nrows) {
+        if ((c0 + n) / HG < nrows) {
             const int64_t c0 = col_of(n) * A.nsplit;
             float top[kMaxTG];
 #pragma unroll
@@ -776,11 +780,11 @@ void prefill_select_kernel(SelArgs A) {
     // sweep computed it, from the stored norm bound)
     const float* gkn = reinterpret_cast<const float*>(A.index + A.L.gkn) + gbase;
     {
-        const int n = tid & (kFlashRowHeads - 1);
-        if (n / HG < nrows) {
+        const int n = tid & (NC - 1);
+        if ((c0 + n) / HG < nrows) {
             const int64_t c0 = col_of(n) * A.nsplit;
             const float T = s.T[n];
-            for (int sp = tid >> 7; sp < A.nsplit; sp += 2) {
+            for (int sp = tid / NC; sp < A.nsplit; sp += kThreads / NC) {
                 const int c = min(A.lcnt[c0 + sp], kSplitCap);
                 const uint4* src = reinterpret_cast<const uint4*>(A.lent + (c0 + sp) * kSplitCap);
                 uint4 e[kSplitCap / 2];
@@ -819,7 +823,7 @@ void prefill_select_kernel(SelArgs A) {
     // when TG others are above its upper bound (the TG-th largest lower bound is above
     // it); only the rest need the canonical chain (all of them when the rank order is an
     // output).  Needs the TG and TG+1 largest upper bounds and the TG largest lower bounds.
-    if (tid < kFlashRowHeads) {
+    if (tid < NC) {
         const int n = tid, c = s.cnt[n];
         if (c <= kCandCap) {
             float tu[kMaxTG + 1], tl[kMaxTG];
@@ -857,14 +861,14 @@ void prefill_select_kernel(SelArgs A) {
     }
     __syncthreads();
     // canonical chains for the candidates that need them (the score replaces the bound)
-    for (int x = tid; x < kFlashRowHeads * kCandCap; x += kThreads) {
+    for (int x = tid; x < NC * kCandCap; x += kThreads) {
         const int n = x / kCandCap, at = x % kCandCap;
         if (at < min(s.cnt[n], kCandCap) && s.cls[n][at] == 1)
             s.cub[n][at] = canonical_dot_bf16(qrow(n), gk + (int64_t)s.cg[n][at] * kD);
     }
     __syncthreads();
     // exact top-TG per column among its candidates (columns that overflowed: below)
-    if (tid < kFlashRowHeads) {
+    if (tid < NC) {
         const int n = tid, c = s.cnt[n];
         if (c > kCandCap) {
             atomicOr(&s.any_overflow, 1);
@@ -900,7 +904,7 @@ void prefill_select_kernel(SelArgs A) {
     // exhaustive path for columns with more candidates than kept: canonical scores of
     // every eligible group, workgroup-wide top-TG
     if (s.any_overflow) {
-        for (int n = 0; n < kFlashRowHeads; ++n) {
+        for (int n = 0; n < NC; ++n) {
             if (s.nsel[n] >= 0) continue;  // uniform: read from LDS after a barrier
             uint64_t top[kMaxTG];
 #pragma unroll
@@ -941,11 +945,11 @@ void prefill_select_kernel(SelArgs A) {
     }
 
     // outputs: opened groups (rank order and ascending), then the pages of each
-    for (int x = tid; x < kFlashRowHeads * TG; x += kThreads) {
+    for (int x = tid; x < NC * TG; x += kThreads) {
         const int n = x / TG, t = x % TG;
-        const int rl = n / HG;
+        const int rl = (c0 + n) / HG;
         if (rl >= nrows) continue;
-        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG;
+        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + (c0 + n) % HG;
         if (A.sel_groups) A.sel_groups[rh * TG + t] = s.sel[n][t];
         // ascending copy: the t-th smallest id among the selected
         const int gt = s.sel[n][t];
@@ -958,11 +962,11 @@ void prefill_select_kernel(SelArgs A) {
                             ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.L.meta_stride;
     const bf16_t* pk_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pk) +
                          ((int64_t)bs * A.Hkv + kvh) * A.max_chunks * A.L.page_slots * kD;
-    for (int x = tid; x < kFlashRowHeads * TG; x += kThreads) {
+    for (int x = tid; x < NC * TG; x += kThreads) {
         const int n = x / TG, t = x % TG;
-        const int rl = n / HG;
+        const int rl = (c0 + n) / HG;
         if (rl >= nrows) continue;
-        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + n % HG;
+        const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + (c0 + n) % HG;
         PairRec R;
         R.gid = s.sel[n][t];
         R.ps0 = R.npg = 0;
@@ -1440,7 +1444,8 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
         hipLaunchKernelGGL((prefill_cand_kernel<HG, 8>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads),
                            0, st, S);
     trace_point(1, st);
-    hipLaunchKernelGGL((prefill_select_kernel<HG>), dim3(ntiles * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
+    hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols>), dim3(ntiles * (kFlashRowHeads / kSelCols) * S.Hkv, 1, batch),
+                       dim3(kThreads), 0, st, S);
     trace_point(2, st);
     // fork: the flash kernel on the side stream, bucket and pages on the caller's
     if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(side.st, side.fork, 0) != hipSuccess)
