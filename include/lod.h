@@ -174,9 +174,9 @@ int lod_index_layout(const lod_params* params, int32_t batch, int32_t max_chunks
                      lod_index_layout_t* layout);
 
 /*
- * Build chunks [chunk_begin, chunk_begin + n_chunks) of every sequence and KV head
- * ("after every chunk of 256 tokens, similar keys are grouped into centroid clusters.
- * Within each cluster, keys are divided into pages of 16 keys" -- How It Works).
+ * Build chunks [chunk_begin, chunk_begin + n_chunks) of every sequence and KV head:
+ * the step of "How It Works" in which each completed 256-token chunk has its keys
+ * clustered into centroid groups and every group cut into pages of 16 keys.
  * Clustering: Lloyd's k-means on the chunk's non-sink keys (positions >= n_sink) in
  * fp32, seeds mu_j = x[floor(j*m/G)] for m members, kmeans_iters rounds of (assign to
  * the nearest centroid by the fp32 fma chain of squared differences in index order,

@@ -10,6 +10,7 @@ from hierarchical_kv_approximation_amd import lod
 from oracle import oracle as orc
 
 from lodcase import TOL, Case, compare_index, configs
+from lodcase import decode_and_compare as _decode_and_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -18,30 +19,6 @@ pytestmark = pytest.mark.gpu
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def _decode_and_compare(case, keys_oidx, seq, q, check_heads=None):
-    """GPU decode at seq_lens=seq vs the oracle on every (b, h) (or check_heads)."""
-    g, o = case.gcfg, case.ocfg
-    st, oidx = keys_oidx
-    dev = case.Kd.device
-    sl = torch.tensor(seq, dtype=torch.int32, device=dev)
-    out, sg, sp = lod.attend_decode(g, case.index, case.Kd, case.Vd, q.to(dev), sl, max(seq),
-                                    want_selection=True)
-    torch.cuda.synchronize()
-    out, sg, sp = out.cpu().numpy(), sg.cpu().numpy(), sp.cpu().numpy()
-    qf = q.float().cpu().numpy()
-    hpg = g.n_q_heads // g.n_kv_heads
-    heads = check_heads or [(b, h) for b in range(case.B) for h in range(g.n_q_heads)]
-    worst = 0.0
-    for b, h in heads:
-        kv = (b, h // hpg)
-        r = orc.attend(o, oidx[kv], *st[kv], qf[b, h], seq[b] - 1)
-        assert np.array_equal(sg[b, h], r["sel_groups"]), (b, h, sg[b, h], r["sel_groups"])
-        assert np.array_equal(sp[b, h], r["sel_pages"]), (b, h)
-        worst = max(worst, float(np.max(np.abs(out[b, h] - r["out"]))))
-    assert worst <= TOL[g.dtype], worst
-    return worst
 
 
 # ------------------------------------------------------------------ fp32, one head, 4096 keys
@@ -216,3 +193,60 @@ def test_batch1_long_context_one_kv_head(T):
     keys = [(0, 0)]
     st, oidx = case.oracle_index(keys)
     _decode_and_compare(case, (st, oidx), [T], case.queries(seed=24))
+
+
+# ------------------------------------------------------------------ ties: every selection path
+
+def _near_ties(case, oidx, q, T, margin=0.05):
+    """Per query head, how many eligible groups score within `margin` of the 8th best
+    (numpy fp64 dots of the oracle's stored mean keys): a lower bound on the candidates
+    the open step must re-score canonically."""
+    g = case.gcfg
+    nb = case.ocfg.built_chunks(T - 1)
+    qf = q.float().cpu().numpy()
+    counts = []
+    for h in range(g.n_q_heads):
+        idx = oidx[(0, h // (g.n_q_heads // g.n_kv_heads))]
+        ok = idx["gcount"][:nb].reshape(-1) > 0
+        s = (idx["gk"][:nb].reshape(-1, 128)[ok].astype(np.float64) @ qf[0, h].astype(np.float64))
+        kth = np.sort(s)[::-1][g.top_groups - 1]
+        counts.append(int(np.sum(s >= kth - margin)))
+    return counts
+
+
+@pytest.mark.parametrize("T,lo,hi", [
+    (4096, 9, 32),         # 14 tied groups: candidates' meta rows prefetched
+    (16384, 33, 128),      # 62 tied groups: pages scored after the ranking
+    (40960, 129, 10**9),   # 158 tied groups: every group ranked canonically
+])
+def test_bf16_ties_reach_every_selection_path(T, lo, hi):
+    """GQA 64/8, bf16, zero variance: every chunk holds the same four centres in runs of
+    64, so the top score of a query is shared by one group of EVERY summarised chunk.
+    The number of tied candidates grows with the context and crosses both limits of the
+    open step's selection (32 candidates with prefetched meta rows, 128 re-scored
+    candidates).  Ties go to the lower group id, so the opened groups are the top
+    centre's groups in the first 8 chunks; outputs equal the oracle and, with zero
+    variance, dense attention."""
+    g, o = configs(torch.bfloat16, 64, 8, G=8, W=512, S=4)
+    case = Case(g, o, 1, T, seed=27, zero_variance=True, n_centres=4, gen_device="cuda")
+    case.build_gpu()
+    keys = [(0, h) for h in range(8)]
+    st, oidx = case.oracle_index(keys)
+    for kv in keys:
+        compare_index(case.index, oidx[kv], 0, kv[1], case.nchunks)
+    q = case.queries(seed=28)
+    ties = _near_ties(case, oidx, q, T)
+    assert all(lo <= c <= hi for c in ties), ties
+    _decode_and_compare(case, (st, oidx), [T], q)
+    sl = torch.tensor([T], dtype=torch.int32, device="cuda")
+    out, sg, _ = lod.attend_decode(g, case.index, case.Kd, case.Vd, q.cuda(), sl, T, want_selection=True)
+    torch.cuda.synchronize()
+    sg, out = sg.cpu().numpy(), out.cpu().numpy()
+    qf = q.float().cpu().numpy()
+    for h in range(64):
+        # one opened group per chunk 0..7, all holding the same mean key
+        assert [x // 8 for x in sg[0, h]] == list(range(8)), sg[0, h]
+        idx = oidx[(0, h // 8)]
+        assert len({idx["gk"][x // 8, x % 8].tobytes() for x in sg[0, h]}) == 1
+        ref, _ = orc.dense(o, *st[(0, h // 8)], qf[0, h], T - 1)
+        assert np.max(np.abs(out[0, h] - ref)) <= TOL[torch.bfloat16]

@@ -12,8 +12,9 @@ from hierarchical_kv_approximation_amd import lod
 from oracle import oracle as orc
 
 from lodcase import TOL, Case
-from test_decode_gpu import _decode_and_compare
-from test_prefill_gpu import _prefill_and_compare, _sample_rows
+from lodcase import decode_and_compare as _decode_and_compare
+from lodcase import prefill_and_compare as _prefill_and_compare
+from lodcase import sample_rows as _sample_rows
 
 pytestmark = pytest.mark.gpu
 

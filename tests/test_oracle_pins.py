@@ -335,6 +335,48 @@ def test_ties_break_to_lower_id():
     assert r["sel_pages"].tolist() == [[0]]
 
 
+def test_dense_reference_against_closed_forms_and_scipy():
+    """The dense causal reference (orc_dense) that the GPU dense kernels and every
+    LoD-equals-dense check rest on: softmax attention of one query over rows [0, p].
+    Pinned without its own formula: one row gives that row's value; identical keys give
+    the plain mean of the first p+1 values (an off-by-one in the causal bound fails);
+    a key far along q takes all the weight (a wrong sign or scale fails); rows past p
+    never matter; random cases match scipy's softmax in fp64."""
+    from scipy.special import logsumexp, softmax
+    cfg = orc.Config(d=128)
+    sc = cfg.params().scale
+    rng = np.random.default_rng(90)
+    K = rng.standard_normal((300, 128)).astype(np.float32)
+    V = rng.standard_normal((300, 128)).astype(np.float32)
+    q = rng.standard_normal(128).astype(np.float32)
+    out, lm = orc.dense(cfg, K, V, q, 0)
+    assert np.array_equal(out, V[0].astype(np.float64))
+    assert abs(lm - sc * float(K[0].astype(np.float64) @ q.astype(np.float64))) < 1e-12
+    # identical keys: uniform weights over the p + 1 visible rows
+    Ks = np.repeat(K[:1], 300, axis=0)
+    for p in (1, 17, 299):
+        out, lm = orc.dense(cfg, Ks, V, q, p)
+        assert np.allclose(out, V[: p + 1].astype(np.float64).mean(0), rtol=0, atol=1e-13)
+        lam0 = sc * float(K[0].astype(np.float64) @ q.astype(np.float64))
+        assert abs(lm - (lam0 + math.log(p + 1))) < 1e-12
+    # one key 40 q-lengths along q dominates: its value is the output
+    Kp = K.copy()
+    Kp[123] = 40.0 * q / np.linalg.norm(q) * math.sqrt(128)
+    out, _ = orc.dense(cfg, Kp, V, q, 250)
+    assert np.max(np.abs(out - V[123])) < 1e-9
+    # causality: rows after p are never read
+    K2, V2 = K.copy(), V.copy()
+    K2[151:], V2[151:] = 1e4, np.nan
+    assert np.array_equal(orc.dense(cfg, K2, V2, q, 150)[0], orc.dense(cfg, K, V, q, 150)[0])
+    # random cases against scipy (fp64 logits of the fp32 inputs)
+    for p in (5, 64, 299):
+        lam = sc * (K[: p + 1].astype(np.float64) @ q.astype(np.float64))
+        ref = softmax(lam) @ V[: p + 1].astype(np.float64)
+        out, lm = orc.dense(cfg, K, V, q, p)
+        assert np.max(np.abs(out - ref)) < 1e-12
+        assert abs(lm - logsumexp(lam)) < 1e-12
+
+
 def test_open_everything_equals_dense():
     """Opening every group and every page leaves nothing coarse: dense causal attention."""
     cfg = orc.Config(d=16, chunk=64, page=4, groups=4, top_groups=10**6, top_pages=0,
@@ -364,8 +406,9 @@ def test_no_summarised_chunks_gives_dense_causal():
 
 @pytest.mark.parametrize("bf16", [False, True])
 def test_zero_variance_groups_give_full_attention(bf16):
-    """'When the groups have zero variance, this ends up being equivalent to full
-    attention': chunks of four identical-key runs, strided seeds land on each run."""
+    """Groups whose keys are all identical make LoD equal to full attention (the
+    invariant stated at the end of "How It Works"): chunks of four identical-key runs,
+    strided seeds land on each run."""
     from hierarchical_kv_approximation_amd import synth
     K, V, cen, _ = synth.clustered_kv(1, 4096, 1, 128, seed=14, zero_variance=True,
                                       dtype=torch.bfloat16 if bf16 else torch.float32)
@@ -390,7 +433,8 @@ def test_zero_variance_groups_give_full_attention(bf16):
 
 
 def test_coarse_mass_is_conservative_jensen():
-    """'As variance increases, it becomes a conservative estimate of attention mass':
+    """With spread inside a group the coarse term under-counts the group's attention
+    mass ("How It Works", last paragraph; Jensen's inequality):
     n exp(q.kbar) <= sum exp(q.k_i) for every group and page, and the total mass of the
     LoD softmax never exceeds the dense one (fp32 summaries; a small rounding slack)."""
     cfg = orc.Config(d=128, groups=8, window=512, n_sink=4)
