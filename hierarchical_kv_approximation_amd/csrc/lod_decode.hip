@@ -23,6 +23,8 @@
 //             back the coarse terms of candidates that lost the global ranking.
 //  3. combine grid (query heads, batch).  Log-sum-exp merge of every partial state.
 // Partial states are (o[d] = sum w v, m, l) relative to their own max m.
+#include <mutex>
+
 #include "lod_device.h"
 #include "lod_mfma.h"
 
@@ -1986,6 +1988,47 @@ extern "C" int lod_attend_decode(const lod_params* params, const lod_index* inde
     A.q = q; A.seq_lens = seq_lens; A.max_seq_len = max_seq_len;
     A.out = out; A.sel_groups = sel_groups; A.sel_pages = sel_pages;
     return dispatch_decode(params, A, batch, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Workspace of lod_attend_decode_noalloc: a fixed device array, one copy per device
+// (loaded with the library's code object and held until the process ends).  In host code
+// the symbol is only a stand-in: its device address for the current device comes from
+// hipGetSymbolAddress, taken once per device and kept in noalloc_ws[].
+static __device__ __align__(256) unsigned char scratch[LOD_NOALLOC_WS_BYTES];
+
+namespace lodi {
+constexpr int kNoallocDevices = 64;
+static std::mutex noalloc_mu;
+static void* noalloc_ws[kNoallocDevices];
+
+// Device address of `scratch` on the current device (looked up on first use).
+static int noalloc_workspace(void** ws) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LOD_ERR_HIP;
+    if (dev >= kNoallocDevices) return LOD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_ws[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LOD_ERR_HIP;
+        noalloc_ws[dev] = p;
+    }
+    *ws = noalloc_ws[dev];
+    return LOD_OK;
+}
+}  // namespace lodi
+
+extern "C" int lod_attend_decode_noalloc(const lod_params* params, const lod_index* index, lod_kv kv,
+                                         const void* q, const int32_t* seq_lens, int32_t batch,
+                                         int32_t max_seq_len, float* out, int32_t* sel_groups,
+                                         int32_t* sel_pages, void* stream) {
+    int rc = check_params(params);
+    if (rc != LOD_OK) return rc;
+    if (batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
+    if (plan_decode(params, batch, max_seq_len).bytes > (size_t)LOD_NOALLOC_WS_BYTES) return LOD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((rc = noalloc_workspace(&ws)) != LOD_OK) return rc;
+    return lod_attend_decode(params, index, kv, q, seq_lens, batch, max_seq_len, out, sel_groups, sel_pages,
+                             ws, (size_t)LOD_NOALLOC_WS_BYTES, stream);
 }
 
 // Row-by-row prefill (fp32 caches): each group of up to kPrefillRows rows runs as that

@@ -86,6 +86,7 @@ def lib():
         L.lod_build_chunk.argtypes = [pp, P(Index), KV, i32, i32, i32, vp, vp, vp]
         L.lod_decode_ws_bytes.argtypes = [pp, i32, i32, P(sz)]
         L.lod_attend_decode.argtypes = [pp, P(Index), KV, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.lod_attend_decode_noalloc.argtypes = [pp, P(Index), KV, vp, vp, i32, i32, vp, vp, vp, vp]
         L.lod_prefill_ws_bytes.argtypes = [pp, i32, i32, i32, P(sz)]
         L.lod_attend_prefill.argtypes = [pp, P(Index), KV, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.lod_dense_decode_ws_bytes.argtypes = [pp, i32, i32, P(sz)]
@@ -98,7 +99,7 @@ def lib():
         L.lod_video_attend.argtypes = [vpp, KV, vp, i32, vp, vp, vp, sz, vp]
         L.lod_video_dense.argtypes = [vpp, KV, vp, i32, vp, vp]
         for fn in ("lod_index_bytes", "lod_index_layout", "lod_build_chunk", "lod_decode_ws_bytes",
-                   "lod_attend_decode", "lod_prefill_ws_bytes", "lod_attend_prefill",
+                   "lod_attend_decode", "lod_attend_decode_noalloc", "lod_prefill_ws_bytes", "lod_attend_prefill",
                    "lod_dense_decode_ws_bytes", "lod_dense_decode", "lod_dense_prefill",
                    "lod_trace_events", "lod_video_layout", "lod_video_ws_bytes", "lod_video_attend",
                    "lod_video_dense"):
@@ -281,6 +282,33 @@ def attend_decode(cfg: Config, index: LodIndex, K, V, q, seq_lens: torch.Tensor,
         ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V, block_table), _ptr(q), _ptr(seq_lens), B,
         max_seq_len, _ptr(out), _ptr(sg), _ptr(sp), _ptr(ws), ws.numel(), _stream()))
     return (out, sg, sp) if want_selection else out
+
+
+NOALLOC_WS_BYTES = 32 << 20  # LOD_NOALLOC_WS_BYTES of include/lod.h
+
+
+def attend_decode_noalloc(cfg: Config, index: LodIndex, K, V, q, seq_lens: torch.Tensor, max_seq_len: int,
+                          want_selection: bool = False, out: torch.Tensor | None = None,
+                          sel: tuple | None = None, block_table: torch.Tensor | None = None):
+    """lod_attend_decode_noalloc: lod_attend_decode with the library's fixed device
+    workspace.  Pass `out` (and `sel` = (sel_groups, sel_pages)) to allocate nothing here
+    either.  Returns out or (out, sel_groups, sel_pages)."""
+    B = q.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+    sg = sp = None
+    if sel is not None:
+        sg, sp = sel
+    elif want_selection:
+        sg = torch.empty(B, cfg.n_q_heads, cfg.top_groups, dtype=torch.int32, device=dev)
+        sp = torch.empty(B, cfg.n_q_heads, cfg.top_groups, max(cfg.top_pages, 1), dtype=torch.int32,
+                         device=dev)
+    idx = index.c()
+    _check("lod_attend_decode_noalloc", lib().lod_attend_decode_noalloc(
+        ctypes.byref(cfg.params()), ctypes.byref(idx), kv_view(K, V, block_table), _ptr(q), _ptr(seq_lens), B,
+        max_seq_len, _ptr(out), _ptr(sg), _ptr(sp), _stream()))
+    return (out, sg, sp) if (want_selection or sel is not None) else out
 
 
 def prefill_ws_bytes(cfg: Config, batch: int, n_q: int, max_tokens: int) -> int:

@@ -224,6 +224,28 @@ int lod_attend_decode(const lod_params* params, const lod_index* index, lod_kv k
                       int32_t max_seq_len, float* out, int32_t* sel_groups,
                       int32_t* sel_pages, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * lod_attend_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments and results are those of lod_attend_decode; the
+ * workspace is a fixed device array of LOD_NOALLOC_WS_BYTES bytes inside the library,
+ * one per device, loaded with the library's code and kept until the process ends.
+ *   - The call allocates nothing and calls no allocating routine.  The array's address
+ *     on the current device is looked up once per device (hipGetSymbolAddress) on the
+ *     first call there; `stream` must belong to the current device.
+ *   - LOD_ERR_WORKSPACE when lod_decode_ws_bytes(params, batch, max_seq_len) exceeds
+ *     LOD_NOALLOC_WS_BYTES (32 MiB: e.g. batch 16 at 128K context, or batch 8 at 256K,
+ *     with 64/8 heads); nothing is enqueued then.
+ *   - Every call on one device shares that device's array and leaves its last contents
+ *     there (no kernel reads workspace it has not written in the same call).  Calls that
+ *     may overlap on one device race on it: order them (one stream, or events).
+ */
+#define LOD_NOALLOC_WS_BYTES (32u << 20)
+int lod_attend_decode_noalloc(const lod_params* params, const lod_index* index, lod_kv kv,
+                              const void* q, const int32_t* seq_lens, int32_t batch,
+                              int32_t max_seq_len, float* out, int32_t* sel_groups,
+                              int32_t* sel_pages, void* stream);
+
 /* Host-only: workspace bytes for lod_attend_prefill. */
 int lod_prefill_ws_bytes(const lod_params* params, int32_t batch, int32_t n_q,
                          int32_t max_tokens, size_t* bytes);
