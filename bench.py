@@ -8,13 +8,14 @@ context 131072; groups of a 256-token chunk = 8, pages of 16, top 8 groups, top 
 pages, block window 512, 4 sinks.  Keys from a 32-centre Gaussian mixture (sigma 0.3),
 values N(0, 1), queries matched to the mixture (all seeded, synthetic).
 
-A step is one lod_attend_decode call: one decode token for every sequence of the batch
-through one attention layer.  Steps rotate over `--layers` independent layer copies
-(cache + index) so the 256 MB Infinity Cache cannot serve a layer's reads from the
-previous step.  Positions advance by one every `--layers` steps; by default each layer
-decodes 256 positions that straddle a chunk boundary, so the timed region includes the
-one lod_build_chunk call per layer that the boundary requires (the build-during-decode
-step of the method) at its real rate of once per 256 tokens.
+A step is one lod_attend_decode call -- one decode token for every sequence of the batch
+through one attention layer -- plus its share of the chunk builds the method needs while
+decoding: each layer builds one chunk (every sequence and KV head in one lod_build_chunk
+call) per 256 positions, so a step is charged 1/256 of that call, timed on its own.
+Steps rotate over `--layers` independent layer copies (cache + index) so the 256 MB
+Infinity Cache cannot serve a layer's reads from the previous step.  The timed positions
+start at a chunk boundary (the first query of a chunk, which needs the chunk that has
+just left the block window).
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
 
     def create(self, n):
         out = []
@@ -56,6 +58,10 @@ class HipEvents:
 
     def record(self, ev, stream):
         assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def wait(self, stream, ev):
+        """Make `stream` wait for event `ev` (hipStreamWaitEvent)."""
+        assert self.hip.hipStreamWaitEvent(stream, ev, 0) == 0
 
     def ms(self, a, b):
         t = ctypes.c_float()
@@ -95,6 +101,47 @@ def cpu_threads() -> int:
     except AttributeError:
         n = os.cpu_count() or 1
     return max(1, min(16, n))
+
+
+def host_info() -> dict:
+    """The benchmark machine's host CPU (the oracle's baseline runs there)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable,
+            "oracle_threads": cpu_threads()}
+
+
+def copy_bandwidth(torch, hip, stream, nbytes=1 << 30, reps=10):
+    """Measured HBM rate of a plain device-to-device copy (the practical ceiling that the
+    kernels' fractions are also quoted against): bytes read + written per second."""
+    x = torch.ones(nbytes // 4, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e = hip.create(2)
+    hip.record(e[0], stream)
+    for _ in range(reps):
+        y.copy_(x)
+    hip.record(e[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e[0], e[1]) / reps
+    hip.destroy(e)
+    del x, y
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"what": f"device-to-device copy of {nbytes >> 20} MiB, read + write bytes per second",
+            "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def algorithmic_decode_bytes(cfg, index, sel_g, sel_p, seq_lens, elt):
@@ -166,6 +213,10 @@ def main():
     ap.add_argument("--only-video", action="store_true",
                     help="measure video LoD only and print its JSON object (for profiling)")
     ap.add_argument("--video-calls", type=int, default=20)
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the 4K fp32 and 32K batch-4 decode cases and the 32K prefill")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run the chunked 128K prefill only and print its JSON object (for profiling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -186,6 +237,14 @@ def main():
                         cpu_seconds=args.cpu_seconds)
         print(json.dumps({"video": v}), flush=True)
         return
+    if args.only_prefill:
+        hip = HipEvents()
+        cfg = lod.Config(n_q_heads=64, n_kv_heads=8, groups=8, top_groups=8, top_pages=2, window=512,
+                         n_sink=4, dtype=torch.bfloat16)
+        pr = bench_prefill(torch, lod, synth, cfg, hip, torch.cuda.current_stream().cuda_stream,
+                           args.prefill_ctx, args.seed, dense=False, cpu=False, one_call=False)
+        print(json.dumps({"prefill": pr}), flush=True)
+        return
     B, T, L = args.batch, args.ctx, args.layers
     K, W = max(2, args.steps), max(0, args.warmup)
     cfg = lod.Config(n_q_heads=64, n_kv_heads=8, groups=8, top_groups=8, top_pages=2, window=512,
@@ -194,13 +253,16 @@ def main():
     elt = 2
     assert T % C == 0
     npos = (K + L - 1) // L
-    # first query position sits just below a chunk boundary so the timed steps cross it
+    # the timed positions start at a chunk boundary: the first query of chunk T/C needs
+    # chunk T/C - W/C summarised (it has just left the block window), and every later
+    # position of the run needs no other build while it stays inside that chunk
     boundary = T  # first query position of chunk T/C
-    s0 = boundary + 1 - max(1, npos // 2)  # seq_len of the first timed position
-    cap = T + C
-    nb0 = max(0, (s0 - 1) // C - cfg.window // C + 1)  # chunks built before the run
-    build_chunk = boundary // C - cfg.window // C  # chunk that the boundary requires
+    s0 = boundary + 1  # seq_len of the first timed position
+    cap = T + C * ((npos + C - 1) // C)
     max_len = s0 + npos - 1
+    nb0 = max(0, (s0 - 1) // C - cfg.window // C)  # chunks built before the boundary
+    build_chunk = boundary // C - cfg.window // C  # chunk that the boundary requires
+    nb_end = max(0, (max_len - 1) // C - cfg.window // C + 1)  # chunks the last position needs
 
     t_setup = time.time()
     layers = []
@@ -209,7 +271,7 @@ def main():
         q = synth.queries(B, 64, cen, seed=args.seed + 7 + 101 * li)
         index = lod.LodIndex.allocate(cfg, B, cap, device=dev)
         lod.build_chunk(cfg, index, Kc, Vc, 0, nb0)
-        layers.append({"K": Kc, "V": Vc, "q": q, "index": index, "built": False})
+        layers.append({"K": Kc, "V": Vc, "q": q, "index": index})
         del cen
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -221,35 +283,41 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     hip = HipEvents()
 
-    # warm-up: below the boundary, no build
+    # the build the boundary needs, one per layer (every sequence and KV head of the layer
+    # in one call), timed alone; a decode step is charged 1/256 of one: each layer builds
+    # one chunk per 256 of its positions
+    bev = hip.create(2 * L)
+    for li, Ly in enumerate(layers):
+        hip.record(bev[2 * li], stream)
+        lod.build_chunk(cfg, Ly["index"], Ly["K"], Ly["V"], build_chunk, 1)
+        hip.record(bev[2 * li + 1], stream)
+        if nb_end > build_chunk + 1:  # runs longer than one chunk per layer: untimed
+            lod.build_chunk(cfg, Ly["index"], Ly["K"], Ly["V"], build_chunk + 1, nb_end - build_chunk - 1)
+    torch.cuda.synchronize()
+    build_ms = [hip.ms(bev[2 * i], bev[2 * i + 1]) for i in range(L)]
+    hip.destroy(bev)
+    build_charge_ms = sum(build_ms) / L / C
+
+    # warm-up at the first position
     for k in range(W):
         Ly = layers[k % L]
         lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[0], max_len, ws=ws, out=out)
     torch.cuda.synchronize()
 
-    # timed region: the decode calls back to back, with the chunk builds the boundary
-    # needs; nothing else is recorded on the stream (events only around the builds)
-    bev = hip.create(2 * L)
+    # timed region: the decode calls back to back, nothing else on the stream
     t0, t1 = hip.create(2)
-    nbuilt = 0
     hip.record(t0, stream)
     for k in range(K):
-        li, pi = k % L, k // L
-        Ly = layers[li]
-        if s0 + pi - 1 >= boundary and not Ly["built"]:
-            hip.record(bev[2 * nbuilt], stream)
-            lod.build_chunk(cfg, Ly["index"], Ly["K"], Ly["V"], build_chunk, 1)
-            hip.record(bev[2 * nbuilt + 1], stream)
-            Ly["built"] = True
-            nbuilt += 1
-        lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[pi], max_len, ws=ws, out=out)
+        Ly = layers[k % L]
+        lod.attend_decode(cfg, Ly["index"], Ly["K"], Ly["V"], Ly["q"], seq[k // L], max_len, ws=ws, out=out)
     hip.record(t1, stream)
     torch.cuda.synchronize()
     total_ms = hip.ms(t0, t1)
-    build_ms = [hip.ms(bev[2 * i], bev[2 * i + 1]) for i in range(nbuilt)]
-    hip.destroy(bev + [t0, t1])
-    ms_per_step = total_ms / K
-    log(f"timed {K} steps: {ms_per_step * 1000:.1f} us/step")
+    hip.destroy([t0, t1])
+    decode_ms_per_step = total_ms / K
+    ms_per_step = decode_ms_per_step + build_charge_ms
+    log(f"timed {K} steps: {decode_ms_per_step * 1000:.1f} us/step + {build_charge_ms * 1000:.2f} us/step "
+        f"of chunk builds (one {sum(build_ms) / L * 1000:.0f} us build per layer per {C} positions)")
 
     # the same calls again with the library's trace events (before the scan, after the
     # scan, after the open step) for the per-kernel times; events add a little time
@@ -347,7 +415,7 @@ def main():
         qcfg = dataclasses.replace(cfg, int4_pages=True)
         for Ly in layers:
             Ly["index4"] = lod.LodIndex.allocate(qcfg, B, cap, device=dev)
-            lod.build_chunk(qcfg, Ly["index4"], Ly["K"], Ly["V"], 0, build_chunk + 1)
+            lod.build_chunk(qcfg, Ly["index4"], Ly["K"], Ly["V"], 0, max(nb_end, build_chunk + 1))
         qms = time_calls(qcfg, index="index4")
         code_bytes = sum(int(Ly["index4"].mem.numel()) for Ly in layers) // L - sum(
             int(Ly["index"].mem.numel()) for Ly in layers) // L
@@ -386,16 +454,25 @@ def main():
         log(f"paged KV view: {pms * 1000:.1f} us/call")
 
     # CPU oracle on a bounded sample: sequence 0 of layer 0, all 64 heads, one token
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu:
         log("CPU oracle baseline ...")
-        cpu = cpu_baseline(cfg, layers[0], s0, args.cpu_seconds)
-        log(f"CPU oracle: {cpu['value']} tok/s on {cpu['cores']} threads")
+        cpu, cpu1 = cpu_baseline(cfg, layers[0], s0, args.cpu_seconds, min(5.0, args.cpu_seconds))
+        log(f"CPU oracle: {cpu['value']} tok/s on {cpu['cores']} threads, {cpu1['value']} tok/s on one")
 
     for Ly in layers:
         del Ly["K"], Ly["V"], Ly["index"]
     del layers, ws
     torch.cuda.empty_cache()
+
+    copy_bw = copy_bandwidth(torch, hip, stream)
+    log(f"copy bandwidth: {copy_bw['GBs']} GB/s")
+
+    small = None
+    if not args.no_small:
+        small = {"c1_decode_fp32_4k": bench_c1(torch, lod, synth, hip, stream, cpu=not args.no_cpu),
+                 "c2_decode_bf16_32k_b4": bench_c2(torch, lod, synth, hip, stream, cpu=not args.no_cpu)}
+        torch.cuda.empty_cache()
 
     batch1 = None
     if not args.no_batch1:
@@ -407,11 +484,15 @@ def main():
         sweep = bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, args.prefill_ctx, args.seed)
         torch.cuda.empty_cache()
 
-    prefill = None
+    prefill = prefill32 = None
     if not args.no_prefill:
         prefill = bench_prefill(torch, lod, synth, cfg, hip, stream, args.prefill_ctx, args.seed,
-                                dense=not args.no_dense)
+                                dense=not args.no_dense, cpu=not args.no_cpu)
         torch.cuda.empty_cache()
+        if not args.no_small:
+            prefill32 = bench_prefill(torch, lod, synth, cfg, hip, stream, 32768, args.seed,
+                                      dense=not args.no_dense, cpu=False)
+            torch.cuda.empty_cache()
 
     video = None
     if not args.no_video:
@@ -436,7 +517,10 @@ def main():
                         "GQA 64/8, head_dim 128, bf16 KV, 8 groups per 256-token chunk, pages of 16, "
                         "top 8 groups / top 2 pages, block window 512, 4 sinks",
             "batch": B, "context": T, "layers_rotated": L,
-            "positions": [s0 - 1, max_len - 1], "chunk_builds_in_timed_region": nbuilt,
+            "positions": [s0 - 1, max_len - 1],
+            "step": "one lod_attend_decode call (one token of every sequence through one layer) plus "
+                    "1/256 of that layer's lod_build_chunk call (each layer builds one chunk per 256 "
+                    "positions); the calls are timed back to back, the build alone",
         },
         "roofline": {
             "bound": "hbm",
@@ -452,6 +536,8 @@ def main():
         "cpu_baseline": cpu,
         "extra": {
             "step_us": round(ms_per_step * 1000, 2),
+            "decode_call_us": round(decode_ms_per_step * 1000, 2),
+            "build_charge_us_per_step": round(build_charge_ms * 1000, 3),
             "lod_call_us_with_trace_events": round(call_avg * 1000, 2),
             "scan_us": round(scan_avg * 1000, 2),
             "open_us": round(open_avg * 1000, 2),
@@ -465,9 +551,17 @@ def main():
             "paged_kv_view": paged,
             "int4_pages": int4,
             "batch1": batch1,
+            "cpu_baseline_one_core": cpu1,
+            "host": host_info(),
+            "copy_bandwidth": copy_bw,
+            "scan_frac_of_copy_bandwidth": round(dom[2] / (dom[1] * 1e-3) / 1e9 / copy_bw["GBs"], 4),
+            "call_frac_of_copy_bandwidth": round(bytes_call / (ms_per_step * 1e-3) / 1e9 / copy_bw["GBs"], 4),
+            "seeds": {"headline": args.seed, "c1_c2": [0, 1, 2]},
+            **(small or {}),
             "setup_s": round(setup_s, 1),
         },
         "prefill": prefill,
+        "prefill_32k_c4": prefill32,
         "sigma_sweep": sweep,
         "video": video,
     }
@@ -492,7 +586,7 @@ def prefill_flops(cfg, index, T, G_nonempty):
     return flash, select
 
 
-def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
+def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True, cpu=True, one_call=True):
     """Chunked causal prefill of one sequence of T tokens: for every 256-row query chunk,
     the chunk that leaves the window is built and the chunk's rows attend.  Builds run on
     a side stream one step ahead (overlapping the previous chunk's attention), as a
@@ -571,16 +665,18 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
     flash_tfs = flash_flops / (per["flash"] * 1e-3) / 1e12
 
     # one call over every row with the index prebuilt
-    wsb = torch.empty(lod.prefill_ws_bytes(cfg, 1, T, T), dtype=torch.uint8, device=dev)
-    lod.attend_prefill(cfg, idx, K, V, Q, 0, ws=wsb, out=out)
-    a0, a1 = hip.create(2)
-    hip.record(a0, stream)
-    lod.attend_prefill(cfg, idx, K, V, Q, 0, ws=wsb, out=out)
-    hip.record(a1, stream)
-    torch.cuda.synchronize()
-    one_shot_ms = hip.ms(a0, a1)
-    hip.destroy([a0, a1])
-    del wsb
+    one_shot_ms = None
+    if one_call:
+        wsb = torch.empty(lod.prefill_ws_bytes(cfg, 1, T, T), dtype=torch.uint8, device=dev)
+        lod.attend_prefill(cfg, idx, K, V, Q, 0, ws=wsb, out=out)
+        a0, a1 = hip.create(2)
+        hip.record(a0, stream)
+        lod.attend_prefill(cfg, idx, K, V, Q, 0, ws=wsb, out=out)
+        hip.record(a1, stream)
+        torch.cuda.synchronize()
+        one_shot_ms = hip.ms(a0, a1)
+        hip.destroy([a0, a1])
+        del wsb
 
     dense_rep = None
     if dense:
@@ -609,17 +705,19 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
                      "achieved_TFLOPs": round(dflops / (sample_ms * 1e-3) / 1e12, 1),
                      "lod_speedup_vs_dense": round(est_ms / total_ms, 2)}
         log(f"dense prefill estimate: {est_ms:.0f} ms")
+    cpu_rep = prefill_cpu_baseline(cfg, K, V, Q, T, seed) if cpu else None
     del K, V, Q, out, ws, idx
     torch.cuda.empty_cache()
     return {
         "workload": f"chunked causal prefill of {T} tokens, batch 1, GQA 64/8, bf16, 256-row query "
                     "chunks; the chunk leaving the window is built one step ahead on a side stream",
+        "cpu_baseline": cpu_rep,
         "tok_per_s": round(T * 1000.0 / total_ms, 1),
         "ms": round(total_ms, 2),
         "attention_calls_ms": round(attend_ms, 2),
         "kernel_ms": {n: round(v, 2) for n, v in per.items()},
         "kernel_ms_note": "flash runs on a second stream beside bucket + pages",
-        "one_call_prebuilt_index_ms": round(one_shot_ms, 2),
+        "one_call_prebuilt_index_ms": None if one_shot_ms is None else round(one_shot_ms, 2),
         "roofline": {"bound": "mfma", "kernel": "prefill_flash_kernel (coarse + sinks + window)",
                      "achieved": round(flash_tfs, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(flash_tfs / 2500.0, 4),
@@ -632,94 +730,194 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True):
     }
 
 
+def prefill_cpu_baseline(cfg, K, V, Q, T, seed):
+    """The oracle, as it stands, on a bounded sample of the same chunked prefill: the
+    build of a seeded sample of chunk-heads, LoD attention of seeded (row, head) pairs
+    spread over the sequence, and dense attention of fewer such pairs.  Each part is
+    scaled to the whole prefill (every chunk-head built once; every row with all query
+    heads); the rate is tokens of the prompt per second.  The extrapolation is stated."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as orc
+    threads = cpu_threads()
+    host = host_info()
+    C, Hq, Hkv = cfg.chunk_size, cfg.n_q_heads, cfg.n_kv_heads
+    ocfg = orc.Config(d=128, groups=cfg.groups, top_groups=cfg.top_groups, top_pages=cfg.top_pages,
+                      window=cfg.window, n_sink=cfg.n_sink, bf16=True)
+    rng = np.random.default_rng(seed + 4242)
+    kvh = int(rng.integers(0, Hkv))
+    Kh = K[0, :, kvh].float().cpu().numpy().copy()
+    Vh = V[0, :, kvh].float().cpu().numpy().copy()
+    nchunks = T // C - cfg.window // C  # chunks the chunked flow builds
+    # build: every chunk of one KV head (parallel over chunks, each chunk built alone)
+    t = time.time()
+    idx = orc.build_stream(ocfg, Kh, Vh, nchunks)
+    build_s = time.time() - t  # one thread, nchunks chunk-heads
+    build_total = build_s * Hkv / threads
+    # LoD rows: seeded positions, the sampled KV head's query heads
+    n_lod = 8 * threads
+    pos = np.sort(rng.integers(0, T, n_lod))
+    heads = kvh * (Hq // Hkv) + rng.integers(0, Hq // Hkv, n_lod)
+    Qs = Q[0, torch_index(pos), torch_index(heads)].float().cpu().numpy()
+
+    def lod_one(i):
+        return orc.attend(ocfg, idx, Kh, Vh, Qs[i], int(pos[i]))["out"]
+    t = time.time()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lod_one, range(n_lod)))
+    lod_s = time.time() - t
+    # per-pair cost grows with the summarised groups: the sample spans the sequence
+    lod_total = lod_s / n_lod * T * Hq
+    # dense rows: cost linear in the position, so the mean over uniform positions scales
+    n_dense = 2 * threads
+    dpos = rng.integers(0, T, n_dense)
+    Qd = Q[0, torch_index(dpos), torch_index(heads[:n_dense])].float().cpu().numpy()
+
+    def dense_one(i):
+        return orc.dense(ocfg, Kh, Vh, Qd[i], int(dpos[i]))[0]
+    t = time.time()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(dense_one, range(n_dense)))
+    dense_s = time.time() - t
+    dense_total = dense_s / n_dense * (T / 2) / max(1.0, float(np.mean(dpos))) * T * Hq
+    lod_rate = T / (build_total + lod_total)
+    return {"value": round(lod_rate, 2), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"LoD oracle: build of {nchunks} chunks of one KV head ({build_s:.1f} s on one thread), "
+                      f"{n_lod} (row, head) pairs at seeded positions ({lod_s:.1f} s on {threads} threads); "
+                      f"extrapolated to all {Hkv} KV heads and {T} rows x {Hq} heads "
+                      f"({build_total + lod_total:.0f} s); {host['nproc']}-CPU host ({host['cpu_model']})",
+            "dense_oracle_tok_per_s": round(T / dense_total, 3),
+            "dense_sample": f"{n_dense} (row, head) pairs at seeded positions ({dense_s:.1f} s on {threads} threads), "
+                            f"scaled by position to all rows and heads ({dense_total:.0f} s, an extrapolation)"}
+
+
+def torch_index(a):
+    import torch
+    return torch.as_tensor(a, dtype=torch.long)
+
+
 def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, samples=96):
-    """After a T-token prompt, 256 decode steps of one sequence (batch 1) with one chunk
-    build at the boundary, for three-tier and two-tier LoD and for the sparsity ablation
-    (the same selection without the coarse remainder; and block-sparse attention with
-    larger blocks and a larger budget: 4 groups of 64 keys per chunk, 16 opened whole);
-    keys whose 32 clusters have sigma spread over 0.1 .. 1.0 and queries matched to a
-    cluster.  Reports decode time per token for each, and the error of its output against
-    the dense oracle (fp64) on sampled (step, head) pairs, binned by the sigma of the
-    query's cluster."""
+    """A T-token prompt through the chunked LoD prefill (before each 256-row query chunk,
+    the chunk leaving the window is built), then 256 decode steps of the same sequence
+    (batch 1) with the one chunk build they need.  Variants: three-tier and two-tier
+    LoD with 8 groups per chunk (about 32 keys, i.e. two pages, per group: top 2 pages
+    opens every page, so the tiers coincide) and with 4 groups per chunk (about 64 keys,
+    four pages: top 2 opens half, so the tiers differ); the sparsity ablation with the
+    three-tier selection; block-sparse attention with larger blocks and a larger budget
+    (4 groups per chunk, 16 opened whole, no remainder); three-tier INT4.  Keys come
+    from 32 clusters whose sigma is spread over 0.1 .. 1.0, queries are matched to a
+    cluster.  Reports the prefill and decode time of each variant and the error of its
+    outputs against the dense oracle (fp64) on sampled (row, head) pairs of the prompt
+    and sampled (step, head) pairs of the decode, binned by the sigma of the query's
+    cluster."""
     import dataclasses
+    from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
 
     from oracle import oracle as orc
     dev = torch.device("cuda:0")
     C = cfg.chunk_size
+    nwin = cfg.window // C
     sig = torch.linspace(0.1, 1.0, 32)
     K, V, cen, _ = synth.clustered_kv(1, T + steps, 8, 128, sigma=sig, seed=seed + 777, device=dev)
-    Q, z = synth.queries(1, 64, cen, n_rows=steps, sigma=sig, seed=seed + 778, return_centres=True)
-    nb0 = (T - 1) // C - cfg.window // C + 1  # chunks the prompt's last row sees
+    Qd, zd = synth.queries(1, 64, cen, n_rows=steps, sigma=sig, seed=seed + 778, return_centres=True)
+    Qp, zp = synth.queries(1, 64, cen, n_rows=T, sigma=sig, seed=seed + 780, return_centres=True)
+    nb0 = (T - 1) // C - nwin + 1  # chunks the prompt's last row sees
     variants = (("three_tier", dataclasses.replace(cfg)),
                 ("two_tier", dataclasses.replace(cfg, top_pages=0)),
+                ("three_tier_G4", dataclasses.replace(cfg, groups=4)),
+                ("two_tier_G4", dataclasses.replace(cfg, groups=4, top_pages=0)),
                 ("sparse_three_tier", dataclasses.replace(cfg, drop_remainder=True)),
                 ("sparse_blocks_G4_top16", dataclasses.replace(cfg, groups=4, top_groups=16, top_pages=0,
                                                                drop_remainder=True)),
                 ("int4_three_tier", dataclasses.replace(cfg, int4_pages=True)))
-    indexes = {}
-    for G, q4 in sorted({(c.groups, c.int4_pages) for _, c in variants}):
-        # every chunk the decode steps see; the timed region rebuilds the boundary chunk
-        ic = dataclasses.replace(cfg, groups=G, int4_pages=q4)
-        indexes[(G, q4)] = lod.LodIndex.allocate(ic, 1, T + steps, device=dev)
-        lod.build_chunk(ic, indexes[(G, q4)], K, V, 0, nb0 + 1)
-    torch.cuda.synchronize()
-    res = {}
-    outs = {}
+    rng = np.random.default_rng(seed + 779)
+    pick_d = [(int(k), int(h)) for k, h in zip(rng.integers(0, steps, samples), rng.integers(0, 64, samples))]
+    pick_p = [(int(r), int(h)) for r, h in zip(rng.integers(0, T, samples), rng.integers(0, 64, samples))]
+    pr_t = torch.tensor([r for r, _ in pick_p], device=dev)
+    ph_t = torch.tensor([h for _, h in pick_p], device=dev)
+    outp = torch.empty(1, T, 64, 128, dtype=torch.float32, device=dev)
+    lens = torch.arange(T + 1, T + steps + 1, dtype=torch.int32, device=dev).view(steps, 1)
+    res, outs_d, outs_p = {}, {}, {}
     for name, c in variants:
-        idx = indexes[(c.groups, c.int4_pages)]
+        idx = lod.LodIndex.allocate(c, 1, T + steps, device=dev)
         ws = torch.empty(lod.decode_ws_bytes(c, 1, T + steps), dtype=torch.uint8, device=dev)
-        lens = torch.arange(T + 1, T + steps + 1, dtype=torch.int32, device=dev).view(steps, 1)
+        ws_p = torch.empty(lod.prefill_ws_bytes(c, 1, C, T + steps), dtype=torch.uint8, device=dev)
         out = torch.empty(steps, 64, 128, dtype=torch.float32, device=dev)
-        # warm-up, then the timed pass; the first step needs the chunk leaving the window
-        lod.attend_decode(c, idx, K, V, Q[:, 0], lens[0], T + steps, ws=ws, out=out[0:1])
-        e0, e1 = hip.create(2)
-        hip.record(e0, stream)
+        torch.cuda.synchronize()
+        e = hip.create(4)
+        hip.record(e[0], stream)
+        for k in range(T // C):
+            if k - nwin >= 0:
+                lod.build_chunk(c, idx, K, V, k - nwin, 1)
+            lod.attend_prefill(c, idx, K, V, Qp[:, C * k: C * (k + 1)], C * k, ws=ws_p,
+                               out=outp[:, C * k: C * (k + 1)])
+        hip.record(e[1], stream)
+        hip.record(e[2], stream)
         lod.build_chunk(c, idx, K, V, nb0, 1)
         for k in range(steps):
-            lod.attend_decode(c, idx, K, V, Q[:, k], lens[k], T + steps, ws=ws, out=out[k:k + 1])
-        hip.record(e1, stream)
+            lod.attend_decode(c, idx, K, V, Qd[:, k], lens[k], T + steps, ws=ws, out=out[k:k + 1])
+        hip.record(e[3], stream)
         torch.cuda.synchronize()
-        ms = hip.ms(e0, e1)
-        hip.destroy([e0, e1])
-        outs[name] = out.cpu().numpy()
-        res[name] = {"decode_us_per_token": round(ms * 1000 / steps, 2), "tok_per_s": round(steps * 1000 / ms, 1)}
-        del ws
-    # dense oracle on sampled (step, head) pairs
-    rng = np.random.default_rng(seed + 779)
-    pick = [(int(k), int(h)) for k, h in zip(rng.integers(0, steps, samples), rng.integers(0, 64, samples))]
-    ocfg = orc.Config(d=128, groups=cfg.groups, top_groups=cfg.top_groups, top_pages=cfg.top_pages,
-                      window=cfg.window, n_sink=cfg.n_sink, bf16=True)
+        pms, dms = hip.ms(e[0], e[1]), hip.ms(e[2], e[3])
+        hip.destroy(e)
+        outs_d[name] = out.cpu().numpy()
+        outs_p[name] = outp[0, pr_t, ph_t].cpu().numpy()
+        res[name] = {"prefill_ms": round(pms, 2), "prefill_tok_per_s": round(T * 1000 / pms, 1),
+                     "decode_us_per_token": round(dms * 1000 / steps, 2),
+                     "decode_tok_per_s": round(steps * 1000 / dms, 1)}
+        del ws, ws_p, idx, out
+    del outp
+    # dense oracle on the sampled pairs (one reference for every variant)
+    ocfg = orc.Config(d=128, bf16=True)
     Kh = K[0].float().cpu().numpy()
     Vh = V[0].float().cpu().numpy()
-    Qh = Q[0].float().cpu().numpy()
-    zh = z[0].cpu().numpy()
-    streams = {h: (np.ascontiguousarray(Kh[:, h]), np.ascontiguousarray(Vh[:, h])) for h in {hq // 8 for _, hq in pick}}
-    from concurrent.futures import ThreadPoolExecutor
+    Qdh = Qd[0].float().cpu().numpy()
+    Qph = Qp[0, pr_t, ph_t].float().cpu().numpy()
+    zdh, zph = zd[0].cpu().numpy(), zp[0, pr_t, ph_t].cpu().numpy()
+    heads = {h // 8 for _, h in pick_d + pick_p}
+    streams = {h: (np.ascontiguousarray(Kh[:, h]), np.ascontiguousarray(Vh[:, h])) for h in heads}
 
-    def one(kh):
-        k, h = kh
-        Ks, Vs = streams[h // 8]
-        return kh, orc.dense(ocfg, Ks, Vs, Qh[k, h], T + k)[0]
+    def one(job):
+        kind, i = job
+        if kind == "d":
+            k, h = pick_d[i]
+            return job, orc.dense(ocfg, *streams[h // 8], Qdh[k, h], T + k)[0]
+        r, h = pick_p[i]
+        return job, orc.dense(ocfg, *streams[h // 8], Qph[i], r)[0]
+    jobs = [("d", i) for i in range(samples)] + [("p", i) for i in range(samples)]
     with ThreadPoolExecutor(cpu_threads()) as ex:
-        ref = dict(ex.map(one, pick))
+        ref = dict(ex.map(one, jobs))
     edges = np.linspace(0.1, 1.0, 5)
     sig_np = sig.numpy()
-    for name in res:
+
+    def binned(err_sig):
         bins = []
         for i in range(4):
-            errs = [float(np.max(np.abs(outs[name][k, h] - ref[(k, h)]))) for k, h in pick
-                    if edges[i] <= sig_np[zh[k, h]] < edges[i + 1] + (1e-9 if i == 3 else 0.0)]
+            errs = [e_ for e_, sg_ in err_sig if edges[i] <= sg_ < edges[i + 1] + (1e-9 if i == 3 else 0.0)]
             bins.append({"sigma": [round(float(edges[i]), 3), round(float(edges[i + 1]), 3)], "n": len(errs),
                          "mean_max_abs_err": round(float(np.mean(errs)), 5) if errs else None,
                          "max_abs_err": round(float(np.max(errs)), 5) if errs else None})
-        res[name]["error_vs_dense_oracle_by_sigma"] = bins
-    del K, V, Q, indexes
-    log("sigma sweep: " + ", ".join(f"{n} {r['decode_us_per_token']} us/token" for n, r in res.items()))
-    return {"workload": f"one sequence, {T}-token prompt then {steps} decode steps with one chunk build, "
-                        "GQA 64/8, bf16; 32 key clusters with sigma 0.1..1.0, matched queries",
-            **res, "samples": samples}
+        return bins
+    for name in res:
+        ed = [(float(np.max(np.abs(outs_d[name][k, h] - ref[("d", i)]))), sig_np[zdh[k, h]])
+              for i, (k, h) in enumerate(pick_d)]
+        ep = [(float(np.max(np.abs(outs_p[name][i] - ref[("p", i)]))), sig_np[zph[i]])
+              for i in range(samples)]
+        res[name]["decode_error_vs_dense_oracle_by_sigma"] = binned(ed)
+        res[name]["prefill_error_vs_dense_oracle_by_sigma"] = binned(ep)
+    tiers = {f"G{G}": {"decode_max_abs_diff": round(float(np.max(np.abs(outs_d[a] - outs_d[b]))), 6),
+                       "prefill_max_abs_diff": round(float(np.max(np.abs(outs_p[a] - outs_p[b]))), 6)}
+             for G, a, b in ((8, "three_tier", "two_tier"), (4, "three_tier_G4", "two_tier_G4"))}
+    del K, V, Qd, Qp
+    log("sigma sweep: " + ", ".join(f"{n} {r['prefill_ms']} ms + {r['decode_us_per_token']} us/token"
+                                    for n, r in res.items()))
+    return {"workload": f"one sequence: {T}-token prompt through the chunked LoD prefill, then {steps} decode "
+                        "steps with one chunk build; GQA 64/8, bf16; 32 key clusters with sigma 0.1..1.0, "
+                        "matched queries",
+            **res, "three_vs_two_tier_difference": tiers, "samples": {"prefill_rows": samples, "decode_steps": samples}}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -808,6 +1006,154 @@ def bench_batch1(torch, lod, synth, cfg, hip, stream, T, seed, layers=8, reps=32
     log(f"batch 1: {res['us_per_call']} us/call eager, {res['us_per_call_graph']} us/call in a graph")
     del Ls, ws, out
     return res
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def bench_c1(torch, lod, synth, hip, stream, seeds=(0, 1, 2), calls=200, cpu=True):
+    """The 4K fp32 decode case: one query head over one KV head, 4096 keys, 4 groups per
+    chunk, top 8 groups / top 2 pages, window 256, 1 sink; per seed the latency of one
+    call (median of `calls` calls, each between its own events) and of back-to-back
+    calls, and the output's distance from the oracle (fp64)."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    dev = torch.device("cuda:0")
+    T = 4096
+    cfg = lod.Config(n_q_heads=1, n_kv_heads=1, groups=4, top_groups=8, top_pages=2, window=256, n_sink=1,
+                     dtype=torch.float32)
+    ocfg = orc.Config(d=128, groups=4, top_groups=8, top_pages=2, window=256, n_sink=1, bf16=False)
+    res = []
+    for seed in seeds:
+        K, V, cen, _ = synth.clustered_kv(1, T, 1, 128, seed=seed, dtype=torch.float32, device=dev)
+        q = synth.queries(1, 1, cen, seed=seed + 1, dtype=torch.float32)
+        idx = lod.LodIndex.allocate(cfg, 1, T, device=dev)
+        nb = ocfg.built_chunks(T - 1)
+        lod.build_chunk(cfg, idx, K, V, 0, nb)
+        sl = torch.tensor([T], dtype=torch.int32, device=dev)
+        ws = torch.empty(lod.decode_ws_bytes(cfg, 1, T), dtype=torch.uint8, device=dev)
+        out = torch.empty(1, 1, 128, dtype=torch.float32, device=dev)
+        for _ in range(10):
+            lod.attend_decode(cfg, idx, K, V, q, sl, T, ws=ws, out=out)
+        torch.cuda.synchronize()
+        ev = hip.create(2 * calls)
+        for i in range(calls):
+            hip.record(ev[2 * i], stream)
+            lod.attend_decode(cfg, idx, K, V, q, sl, T, ws=ws, out=out)
+            hip.record(ev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        single = _median([hip.ms(ev[2 * i], ev[2 * i + 1]) for i in range(calls)])
+        hip.destroy(ev)
+        e = hip.create(2)
+        hip.record(e[0], stream)
+        for _ in range(calls):
+            lod.attend_decode(cfg, idx, K, V, q, sl, T, ws=ws, out=out)
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        b2b = hip.ms(e[0], e[1]) / calls
+        hip.destroy(e)
+        r = {"seed": seed, "us_per_call_single": round(single * 1000, 2), "us_per_call_back_to_back": round(b2b * 1000, 2)}
+        if cpu:
+            o, sg, _ = lod.attend_decode(cfg, idx, K, V, q, sl, T, want_selection=True)
+            Kh, Vh = K[0, :, 0].cpu().numpy().copy(), V[0, :, 0].cpu().numpy().copy()
+            oidx = orc.build_stream(ocfg, Kh, Vh, nb)
+            ref = orc.attend(ocfg, oidx, Kh, Vh, q[0, 0].cpu().numpy(), T - 1)
+            r["max_abs_err_vs_oracle"] = float(np.max(np.abs(o[0, 0].cpu().numpy() - ref["out"])))
+            r["selection_equal"] = bool(np.array_equal(sg[0, 0].cpu().numpy(), ref["sel_groups"]))
+        res.append(r)
+        del K, V, idx, ws
+    log("4K fp32 decode: " + ", ".join(f"{r['us_per_call_single']} us" for r in res))
+    return {"workload": "LoD decode, fp32, 1 query / 1 KV head, head_dim 128, 4096-token context, 4 groups per "
+                        "256-token chunk, pages of 16, top 8 groups / top 2 pages, window 256, 1 sink",
+            "per_seed": res}
+
+
+def bench_c2(torch, lod, synth, hip, stream, seeds=(0, 1, 2), layers=4, calls=256, cpu=True):
+    """The 32K decode case: bf16, GQA 64/8, batch 4, 32768-token context, 8 groups per
+    chunk, top 8 / top 2, window 512, 4 sinks.  Per seed, calls rotate over `layers`
+    layer copies (1.07 GB, beyond the Infinity Cache) at the last position; tok/s, the
+    call's algorithmic bytes over its time against 8 TB/s, the scan and open times from
+    a traced pass, and sampled heads against the oracle."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    dev = torch.device("cuda:0")
+    B, T = 4, 32768
+    cfg = lod.Config(n_q_heads=64, n_kv_heads=8, groups=8, top_groups=8, top_pages=2, window=512, n_sink=4,
+                     dtype=torch.bfloat16)
+    ocfg = orc.Config(d=128, groups=8, top_groups=8, top_pages=2, window=512, n_sink=4, bf16=True)
+    nb = ocfg.built_chunks(T - 1)
+    res = []
+    for seed in seeds:
+        Ls = []
+        for li in range(layers):
+            K, V, cen, _ = synth.clustered_kv(B, T, 8, 128, seed=1000 * seed + 11 * li + 5, device=dev)
+            q = synth.queries(B, 64, cen, seed=1000 * seed + 11 * li + 6)
+            idx = lod.LodIndex.allocate(cfg, B, T, device=dev)
+            lod.build_chunk(cfg, idx, K, V, 0, nb)
+            Ls.append((K, V, q, idx))
+        sl = torch.full((B,), T, dtype=torch.int32, device=dev)
+        ws = torch.empty(lod.decode_ws_bytes(cfg, B, T), dtype=torch.uint8, device=dev)
+        out = torch.empty(B, 64, 128, dtype=torch.float32, device=dev)
+
+        def call(i):
+            K, V, q, idx = Ls[i % layers]
+            lod.attend_decode(cfg, idx, K, V, q, sl, T, ws=ws, out=out)
+        for i in range(2 * layers):
+            call(i)
+        torch.cuda.synchronize()
+        e = hip.create(2)
+        hip.record(e[0], stream)
+        for i in range(calls):
+            call(i)
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(e[0], e[1]) / calls
+        hip.destroy(e)
+        NE = 3
+        ev = hip.create(NE * 32)
+        for i in range(32):
+            keep = lod.trace_events(ev[NE * i: NE * i + NE])
+            call(i)
+            lod.trace_events(None)
+            del keep
+        torch.cuda.synchronize()
+        scan = sum(hip.ms(ev[NE * i], ev[NE * i + 1]) for i in range(32)) / 32
+        opn = sum(hip.ms(ev[NE * i + 1], ev[NE * i + 2]) for i in range(32)) / 32
+        hip.destroy(ev)
+        K, V, q, idx = Ls[0]
+        o, sg, sp = lod.attend_decode(cfg, idx, K, V, q, sl, T, want_selection=True)
+        torch.cuda.synchronize()
+        total, scores, coarse, opened = algorithmic_decode_bytes(cfg, idx, sg, sp, [T] * B, 2)
+        r = {"seed": seed, "us_per_call": round(ms * 1000, 2), "tok_per_s": round(B * 1000.0 / ms, 1),
+             "scan_us_traced": round(scan * 1000, 2), "open_us_traced": round(opn * 1000, 2),
+             "algorithmic_bytes_per_call": total,
+             "call_frac_hbm": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "scan_frac_hbm": round((scores + coarse) / (scan * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if cpu:
+            keys = [(0, 0), (B - 1, 7)]
+            st = {kv: (K[kv[0], :, kv[1]].float().cpu().numpy().copy(), V[kv[0], :, kv[1]].float().cpu().numpy().copy())
+                  for kv in keys}
+            oidx = orc.build_all(ocfg, st, nb, threads=cpu_threads())
+            qf, of, sgf = q.float().cpu().numpy(), o.cpu().numpy(), sg.cpu().numpy()
+            err, same = 0.0, True
+            for b, kvh in keys:
+                for h in range(8 * kvh, 8 * kvh + 8):
+                    ref = orc.attend(ocfg, oidx[(b, kvh)], *st[(b, kvh)], qf[b, h], T - 1)
+                    err = max(err, float(np.max(np.abs(of[b, h] - ref["out"]))))
+                    same = same and bool(np.array_equal(sgf[b, h], ref["sel_groups"]))
+            r["sampled_heads_vs_oracle"] = {"heads": 16, "max_abs_err": err, "selection_equal": same}
+        res.append(r)
+        del Ls, ws, out
+        torch.cuda.empty_cache()
+    log("32K batch-4 decode: " + ", ".join(f"{r['us_per_call']} us" for r in res))
+    return {"workload": "LoD decode, bf16, GQA 64/8, head_dim 128, batch 4, 32768-token context, 8 groups per "
+                        "256-token chunk, pages of 16, top 8 groups / top 2 pages, window 512, 4 sinks; "
+                        f"{layers} layer copies rotated",
+            "per_seed": res}
 
 
 def video_flops(torch, sel, counts, d, drop):
@@ -954,8 +1300,10 @@ def video_cpu_baseline(qkv, F, H, W, c, seconds):
                       f"{t_sum:.2f} s, subtracted), scaled to the full grid and {Hh} heads; {threads} threads"}
 
 
-def cpu_baseline(cfg, Ly, seq_len, seconds):
-    """The oracle, as it stands, on one sequence's decode token (all 64 query heads)."""
+def cpu_baseline(cfg, Ly, seq_len, seconds, seconds_one_core=5.0):
+    """The oracle, as it stands, on one sequence's decode token (all 64 query heads), on
+    every usable host core (up to 16 threads) and on one core.  The index is built
+    once beforehand (not timed).  Returns (all cores, one core)."""
     import numpy as np
 
     from oracle import oracle as orc
@@ -969,17 +1317,22 @@ def cpu_baseline(cfg, Ly, seq_len, seconds):
     nb = ocfg.built_chunks(p)
     idx = orc.build_all(ocfg, st, nb, threads=threads)  # index build: not timed
     Q = Ly["q"][0:1].float().cpu().numpy()
-    t = time.time()
-    n = 0
-    while True:
-        orc.decode(ocfg, st, idx, Q, [seq_len], threads=threads)
-        n += 1
-        el = time.time() - t
-        if el >= seconds or n >= 4096:
-            break
-    return {"value": round(n / el, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode token(s) of one sequence (all 64 query heads) at position {p}, "
-                      f"index prebuilt (not timed); {el:.1f} s wall on {threads} threads"}
+    host = host_info()
+
+    def timed(th, budget):
+        t = time.time()
+        n = 0
+        while True:
+            orc.decode(ocfg, st, idx, Q, [seq_len], threads=th)
+            n += 1
+            el = time.time() - t
+            if el >= budget or n >= 4096:
+                break
+        return {"value": round(n / el, 3), "unit": "tok/s", "cores": th, "kind": "oracle",
+                "sample": f"{n} decode token(s) of one sequence (all 64 query heads) at position {p}, "
+                          f"index prebuilt (not timed); {el:.1f} s wall on {th} thread(s) of a "
+                          f"{host['nproc']}-CPU host ({host['cpu_model']})"}
+    return timed(threads, seconds), timed(1, seconds_one_core)
 
 
 if __name__ == "__main__":

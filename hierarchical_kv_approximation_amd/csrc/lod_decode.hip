@@ -460,7 +460,7 @@ struct OpenSmem {
     int ncand;
     int32_t cg[kOpenCand];     // candidates: group id, canonical score, MFMA score, ln n,
     float cs[kOpenCand];       // page range (first slot | count << 16), first entry in pr
-    float cS[kOpenCand], cL[kOpenCand];
+    float cS[kOpenCand];
     int32_t cP[kOpenCand], cpo[kOpenCand + 1];
     float pr[kSpecPages];      // canonical scores and ln n of the candidates' pages (when
     float pl[kSpecPages];      // scored ahead of the group ranking: pscore_ready)
@@ -468,7 +468,8 @@ struct OpenSmem {
     int mrow[kMaxTG];          // meta row (in s.meta) of opened group i
     int meta_ready;            // meta rows were prefetched (bf16 path)
     uint64_t red[4];
-    float sub_lam[kMaxTG];     // opened groups' coarse logits in the scan (subtracted)
+    float sub_S[kMaxTG];       // opened groups' MFMA scores in the scan
+    float sub_lam[kMaxTG];     // and their coarse logits there (subtracted)
     alignas(16) float plds[kPartLdsFloats];  // the scan partial states (bf16 path), when they fit
 };
 
@@ -1164,6 +1165,23 @@ struct ScanSrc {
     int ns, w0, nex;
 };
 
+// Tile t of a unit's list: coarse tiles (group summaries) first, then exact tiles (sinks
+// and window rows); up to kSTile rows of one kind, starting at row r0 of its list.  (A
+// split by 16-row blocks, balancing bytes across a unit's workgroups, was slower: the
+// partial tiles add iterations, and an iteration's latency, not its bytes, sets the pace
+// of a workgroup.)
+struct ScanTile {
+    int coarse, r0, n;
+};
+
+__device__ __forceinline__ ScanTile scan_tile(int t, int ntc, int ng, int nex) {
+    ScanTile T;
+    T.coarse = t < ntc;
+    T.r0 = (T.coarse ? t : t - ntc) * kSTile;
+    T.n = min(kSTile, (T.coarse ? ng : nex) - T.r0);
+    return T;
+}
+
 // One tile in registers: thread tid holds the 16-byte chunk c = tid % 16 of rows
 // 4g .. 4g+3, g = tid / 16, of its key and value rows (rows past the tile repeat its last
 // row), and the bias of row tid.  Four rows per thread let the value transpose go to LDS
@@ -1175,10 +1193,10 @@ struct ScanRegs {
 
 // DROP (no coarse remainder): coarse tiles only give scores, so their values are not read.
 template <bool DROP, bool PAGED>
-__device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t, int ntc) {
+__device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, const ScanTile& T) {
     const int tid = threadIdx.x, c = tid & 15, g = tid >> 4;
-    if (t < ntc) {
-        const int r0 = t * kSTile, n = min(kSTile, S.ng - r0);
+    if (T.coarse) {
+        const int r0 = T.r0, n = T.n;
 #pragma unroll
         for (int i = 0; i < kSPieces; ++i) {
             const int row = min(4 * g + i, n - 1);
@@ -1188,7 +1206,7 @@ __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, int t,
         }
         R.bias = tid < kSTile ? S.gln[r0 + min(tid, n - 1)] : 0.0f;
     } else {
-        const int x0 = (t - ntc) * kSTile, n = min(kSTile, S.nex - x0);
+        const int x0 = T.r0, n = T.n;
 #pragma unroll
         for (int i = 0; i < kSPieces; ++i) {
             const int x = x0 + min(4 * g + i, n - 1);
@@ -1313,23 +1331,29 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     bf16x8_t qa[4];
     mfma_load_q<HG>(q0, qa);
     ScanRegs R;
-    if (t0 < t1) scan_fetch<DROP, PAGED>(R, S, t0, ntc);
+    if (t0 < t1) scan_fetch<DROP, PAGED>(R, S, scan_tile(t0, ntc, S.ng, S.nex));
 
     for (int t = t0; t < t1; ++t) {
-        const bool coarse = t < ntc;
-        const int r0 = coarse ? t * kSTile : (t - ntc) * kSTile;
-        const int n = min(kSTile, (coarse ? S.ng : S.nex) - r0);
+        const ScanTile cur = scan_tile(t, ntc, S.ng, S.nex);
+        const bool coarse = cur.coarse;
+        const int r0 = cur.r0, n = cur.n;
         scan_stage(s, R);  // the last tile's PV is done (barrier at the end of the loop)
         __syncthreads();
         scan_scores<HG>(s, qa);
-        if (t + 1 < t1) scan_fetch<DROP, PAGED>(R, S, t + 1, ntc);  // in flight through this tile
+        if (t + 1 < t1) scan_fetch<DROP, PAGED>(R, S, scan_tile(t + 1, ntc, S.ng, S.nex));  // in flight
         __syncthreads();
-        // coarse tiles: the scores go out for the selection, a 256-byte row per head
-        // (rows past the tile's groups are never read; the rows stay inside score_stride)
-        if (coarse && tid < 16 * HG) {
+        // coarse tiles: the scores go out for the selection, one float4 per head and four
+        // groups, -inf for an empty group (only the last tile of the unit's groups is
+        // partial; its last float4 may pass the end: those rows lie inside score_stride
+        // and are never read)
+        if (coarse && tid < 16 * HG && 4 * (tid & 15) < n) {
             const int h = tid >> 4, j = tid & 15;
-            *reinterpret_cast<float4*>(sdst + (int64_t)h * A.score_stride + r0 + 4 * j) =
-                *reinterpret_cast<const float4*>(&s.sc[h][4 * j]);
+            float4 v = *reinterpret_cast<const float4*>(&s.sc[h][4 * j]);
+            if (s.bias[4 * j] == -INFINITY) v.x = -INFINITY;
+            if (s.bias[4 * j + 1] == -INFINITY) v.y = -INFINITY;
+            if (s.bias[4 * j + 2] == -INFINITY) v.z = -INFINITY;
+            if (s.bias[4 * j + 3] == -INFINITY) v.w = -INFINITY;
+            *reinterpret_cast<float4*>(sdst + (int64_t)h * A.score_stride + r0 + 4 * j) = v;
         }
         // without the remainder a coarse tile only yields scores
         const bool accumulate = !(DROP && coarse);
@@ -1422,14 +1446,15 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
     load8<bf16_t>(qp, l16, q8);
     const float qv = tid < kD ? bf16_bits_to_f32(qp[tid]) : 0.0f;
     constexpr int SPT = 16;  // groups per thread per round
-    float sv[SPT], kn[SPT], ln[SPT];
+    // the scan stored -inf as the score of an empty group: only non-empty ones compete
+    float sv[SPT], kn[SPT];
     int32_t gp[SPT];
     auto load_scores = [&](int g0) {
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int g = g0 + tid + kThreads * u;
-            ln[u] = -INFINITY;
-            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; ln[u] = gln[g]; gp[u] = gpage[g]; }
+            sv[u] = -INFINITY;
+            if (g < ng) { sv[u] = S[g]; kn[u] = gkn[g]; gp[u] = gpage[g]; }
         }
     };
     if (ng > 0) load_scores(0);
@@ -1462,7 +1487,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         if (g0 > 0) load_scores(g0);
 #pragma unroll
         for (int u = 0; u < SPT; ++u)
-            if (ln[u] != -INFINITY) mx = fmaxf(mx, sv[u] - eq * kn[u]);
+            if (sv[u] != -INFINITY) mx = fmaxf(mx, sv[u] - eq * kn[u]);
     }
     // 1b. each wave: its R largest maxima (with multiplicity), R = min(TG, 4).  Any TG of
     //     them are maxima of distinct threads, so the TG-th largest of the 4R values is
@@ -1522,12 +1547,11 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         if (ng > SPT * kThreads) load_scores(g0);
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
-            if (ln[u] != -INFINITY && sv[u] + eq * kn[u] >= T) {
+            if (sv[u] != -INFINITY && sv[u] + eq * kn[u] >= T) {
                 const int at = atomicAdd(&s.ncand, 1);
                 if (at < kOpenCand) {
                     s.cg[at] = g0 + tid + kThreads * u;
                     s.cS[at] = sv[u];
-                    s.cL[at] = ln[u];
                     s.cP[at] = gp[u];
                 }
             }
@@ -1604,7 +1628,7 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
             if (rank < TG) {
                 s.sel[rank] = key;
                 s.mrow[rank] = prefetch ? x : rank;
-                s.sub_lam[rank] = A.scale * s.cS[x] + s.cL[x];
+                s.sub_S[rank] = s.cS[x];
             }
         }
         if (tid == 0) {
@@ -1657,14 +1681,14 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         __syncthreads();
         if (tid < k) {
             const uint32_t g = key_id(s.sel[tid]);
-            s.sub_lam[tid] = A.scale * S[g] + gln[g];
+            s.sub_S[tid] = S[g];
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // prefetched meta rows (global -> LDS) of this wave
     __syncthreads();
     const int nsel = s.nsel;
     if (A.sel_groups && tid < TG) A.sel_groups[head * TG + tid] = tid < nsel ? (int)key_id(s.sel[tid]) : -1;
-    // the opened groups' mean values (loads in flight during the page work)
+    // the opened groups' mean values and ln n (loads in flight during the page work)
     // (raw bits: converted where used, so nothing waits for them before then)
     uint32_t vsub[kMaxTG];
     if (tid < kD) {
@@ -1672,11 +1696,14 @@ __device__ void decode_open_role(const DecodeArgs& A, OpenSmem<bf16_t>& s, int b
         for (int i = 0; i < kMaxTG; ++i)
             vsub[i] = (i < nsel && !DROP) ? gv[(int64_t)key_id(s.sel[i]) * kD + tid] : 0u;
     }
+    const float lsub = (tid < nsel && !DROP) ? gln[key_id(s.sel[tid < kMaxTG ? tid : 0])] : 0.0f;
 
     Online st;
     st.init();
     open_pages<bf16_t, 2 * kOpenBatch, PAGED, false, DROP, Q4>(A, s, nsel, seq, kvh, head, q8, st);
     open_stash(s, st);
+    // the opened groups' coarse logits in the scan, by the scan's own arithmetic
+    if (tid < nsel) s.sub_lam[tid] = A.scale * s.sub_S[tid] + lsub;
     if (part_in_lds) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // out = scan state - opened groups' coarse terms (the very logits the scan used) +
