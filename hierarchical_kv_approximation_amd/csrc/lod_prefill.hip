@@ -1053,6 +1053,7 @@ struct PagesArgs {
     int max_chunks, G, W, TG;
     int drop;               // 1: no coarse remainder (unopened pages add nothing)
     int q4;                 // 1: opened rows decoded from the index's 4-bit codes
+    int tp;                 // pages opened per opened group (0: two-tier, every page)
     const PairRec* rec;     // [B][nq][Hq][TG], slot t holds the group selg[t]
     const int32_t* selg;    // [B][nq][Hq][TG] opened groups, ascending (-1 padding)
     int2* plist;            // [units][kChunk * HG * TG] (pair index, group) sorted by group
@@ -1312,6 +1313,374 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
     if (l16 == 0) { dst[kD] = st.m; dst[kD + 1] = st.l; }
 }
 
+// ---------------------------------------------------------------------------- group pages (MFMA)
+
+// The opened groups' pages on MFMA, group by group.  A workgroup takes kGroupPairs
+// consecutive pairs of its unit's group-sorted list (one MFMA column each); the pairs
+// form runs of equal group.  Up to kGroupRuns runs at a time share one key list: the
+// members of each run's group in page order (K/V rows from the cache) and, when some pair
+// leaves a page of the group unopened (more pages than top_pages, and a remainder), the
+// group's page summaries (mean key and value, bias ln n).  A column sees a row of its own
+// run: a member row when the row's page is opened for the pair, a summary row when it is
+// not.  So each group's rows are read once per workgroup, not once per pair, and most
+// workgroups need one key tile.  S^T = K Q^T and O^T = V^T P^T run as in the flash kernel
+// (keys as MFMA rows, P from registers as bf16 hi + lo); each column's online softmax is
+// written as the pair's partial state.
+// Which runs share a workgroup depends on the order in which the bucket step filled the
+// list, so a pair's result must not depend on its neighbours: a run's rows start at a
+// 32-row boundary of a tile (the same positions of every 32-key MFMA sum wherever the run
+// lands), a run never straddles tiles unless it has more than 64 rows (then it starts a
+// tile of its own), and the rows of other runs enter only as exact zeros.
+constexpr int kGroupThreads = 128;                  // two waves
+constexpr int kGroupWaves = kGroupThreads / 64;
+constexpr int kGroupPairs = 32 * kGroupWaves;       // pairs (MFMA columns) per workgroup
+constexpr int kGroupRuns = 4;                       // runs sharing a key list (meta rows in LDS)
+constexpr int kSumRow = 0x100;                      // flag of a summary row in GroupSmem::rpage
+
+struct GroupSmem {
+    alignas(16) bf16_t kt[kFlashKeys][kD];  // key tile
+    alignas(16) bf16_t vt[kFlashKeys][kD];
+    float bias[kFlashKeys];                 // log2 units; -inf: no row
+    int rpage[kFlashKeys];                  // run << 16 | page of the row in its group (| kSumRow); -1: none
+    int rsrc[kFlashKeys];                   // member: cache position; summary: unit page slot
+    alignas(16) int16_t meta[kGroupRuns][kPagesMeta];  // meta rows of the batch's runs
+    int2 ent[kGroupPairs];                  // (pair index, group) of the workgroup's pairs
+    uint32_t open[kGroupPairs];             // opened-page mask of each pair
+    int seg[kGroupPairs + 1];               // run starts (offsets into ent), then the end
+    int runof[kGroupPairs];                 // run of each pair
+    int rtile[kGroupRuns], roff[kGroupRuns], rn[kGroupRuns];  // placement of the batch's runs
+    int ntile;                              // key tiles of the batch
+    int firstrow, tilerows;                 // the tile's first row, 1 + its last row
+    int nseg;
+};
+
+template <int HG, bool PAGED>
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void prefill_group_kernel(PagesArgs A) {
+    __shared__ GroupSmem s;
+    const int unit_local = blockIdx.y;
+    const int qc = unit_local % A.units_per_seq_kv;
+    const int kvh = (unit_local / A.units_per_seq_kv) % A.Hkv;
+    const int b = unit_local / (A.units_per_seq_kv * A.Hkv);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+    const int64_t unit = unit_local;
+    const int npairs = A.poff[unit * 2];
+    const int x0 = blockIdx.x * kGroupPairs;
+    if (x0 >= npairs) return;  // uniform in the workgroup
+    const int np = min(kGroupPairs, npairs - x0);
+    const int r0 = qc * kChunk;
+    const int PS = A.L.page_slots;
+    const int ms16 = A.L.meta_stride / 8;  // 16-byte pieces of a meta row
+    const int2* list = A.plist + unit * (kChunk * HG * A.TG);
+    const int bs = A.seq + b;
+    const int64_t ubase = ((int64_t)bs * A.Hkv + kvh) * A.max_chunks;
+    const int16_t* meta_u = reinterpret_cast<const int16_t*>(A.index + A.L.meta) + ubase * A.L.meta_stride;
+    const bf16_t* pk_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pk) + ubase * PS * kD;
+    const bf16_t* pv_u = reinterpret_cast<const bf16_t*>(A.index + A.L.pv) + ubase * PS * kD;
+    const float* pln_u = reinterpret_cast<const float*>(A.index + A.L.pln) + ubase * PS;
+    const bf16_t* kc = A.k + kvh * A.sh + kv_seq<PAGED>(A, bs);
+    const bf16_t* vc = A.v + kvh * A.sh + kv_seq<PAGED>(A, bs);
+    const float sc2 = A.scale * kFlashLog2e;
+    auto pair_rh = [&](int pi, int& t) {
+        t = pi % A.TG;
+        const int h = (pi / A.TG) % HG, rl = pi / (A.TG * HG);
+        return ((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h;
+    };
+    auto load_metas = [&](int sb, int nrun) {  // meta rows of runs sb .. sb+nrun-1 -> slots 0..
+        for (int x = tid; x < nrun * ms16; x += kGroupThreads) {
+            const int k = x / ms16, e = x % ms16;
+            const int c = s.ent[s.seg[sb + k]].y / A.G;
+            *reinterpret_cast<uint4*>(&s.meta[k][8 * e]) =
+                *reinterpret_cast<const uint4*>(meta_u + (int64_t)c * A.L.meta_stride + 8 * e);
+        }
+    };
+
+    // the workgroup's pairs and the runs of equal group (wave 0: one pair per lane)
+    if (w == 0) {
+        const int2 e = l < np ? list[x0 + l] : make_int2(0, -1);
+        s.ent[l] = e;
+        const int prev = __shfl_up(e.y, 1, 64);
+        const bool start = l < np && (l == 0 || e.y != prev);
+        const uint64_t m = __ballot(start);
+        const int below = __popcll(m & ((1ull << l) - 1ull));
+        if (start) s.seg[below] = l;
+        s.runof[l] = start ? below : below - 1;  // the run this pair belongs to
+        if (l == 0) {
+            s.nseg = __popcll(m);
+            s.seg[__popcll(m)] = np;
+        }
+    }
+    __syncthreads();
+    const int nseg = s.nseg;
+    // the pairs' opened-page masks and the first runs' meta rows, in one round trip; the
+    // query operands of this lane's two columns are in flight meanwhile
+    if (tid < kGroupPairs) {
+        uint32_t op = 0;
+        if (tid < np) {
+            int t;
+            const int64_t rh = pair_rh(s.ent[tid].x, t);
+            op = A.rec[rh * A.TG + t].open;
+        }
+        s.open[tid] = op;
+    }
+    load_metas(0, min(nseg, kGroupRuns));
+    bf16x8_t qb[2][4];
+    bool cvalid[2];
+    int64_t crh[2];
+    int ct[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n = 16 * (2 * w + cb) + li;
+        cvalid[cb] = n < np;
+        crh[cb] = pair_rh(s.ent[cvalid[cb] ? n : 0].x, ct[cb]);
+        const bf16_t* qr = A.q + crh[cb] * kD;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
+    }
+    __syncthreads();
+    int crun[2];
+    uint32_t copen[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n = 16 * (2 * w + cb) + li;
+        crun[cb] = cvalid[cb] ? s.runof[n] : -1;
+        copen[cb] = cvalid[cb] ? s.open[n] : 0u;
+    }
+
+    for (int sb = 0; sb < nseg; sb += kGroupRuns) {  // batches of runs
+        const int nrun = min(kGroupRuns, nseg - sb);
+        if (sb > 0) {  // runs past the first batch (every use of the slots has ended)
+            load_metas(sb, nrun);
+            __syncthreads();
+        }
+        // rows of the batch's runs: members, then summaries if some pair of the run leaves
+        // a page unopened (more pages than top_pages, and a remainder); placed in key tiles
+        // at 32-row boundaries
+        if (tid == 0) {
+            int tile = 0, off = 0;
+            for (int k = 0; k < nrun; ++k) {
+                const int16_t* gpg = s.meta[k];
+                const int16_t* pst = gpg + (A.G + 1);
+                const int j = s.ent[s.seg[sb + k]].y % A.G;
+                const int ps0 = gpg[j], npg = gpg[j + 1] - ps0;
+                const bool sums = A.tp > 0 && npg > A.tp && !A.drop;
+                const int n = pst[ps0 + npg] - pst[ps0] + (sums ? npg : 0);
+                s.rn[k] = n;
+                if (n > kFlashKeys) {  // its own tiles
+                    if (off > 0) { ++tile; off = 0; }
+                    s.rtile[k] = tile;
+                    s.roff[k] = 0;
+                    tile += (n + kFlashKeys - 1) / kFlashKeys;
+                } else {
+                    const int need = (n + 31) & ~31;
+                    if (off + need > kFlashKeys) { ++tile; off = 0; }
+                    s.rtile[k] = tile;
+                    s.roff[k] = off;
+                    off += need;
+                    if (off == kFlashKeys) { ++tile; off = 0; }
+                }
+            }
+            s.ntile = tile + (off > 0 ? 1 : 0);
+        }
+        __syncthreads();
+        const int ntile = s.ntile;
+        f32x4_t O[2][8];
+        float m_run[2], l_run[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            m_run[cb] = -INFINITY;
+            l_run[cb] = 0.0f;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        // columns of this batch (run sb + k is k here); a wave with none only helps load
+        int cbat[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) cbat[cb] = (crun[cb] >= sb && crun[cb] < sb + nrun) ? crun[cb] - sb : -1;
+        const bool active = __any(cbat[0] >= 0 || cbat[1] >= 0);
+        for (int kt = 0; kt < ntile; ++kt) {
+            // the tile's rows: run k's members (cache position, page) then its summaries
+            // (unit page slot, page | flag); -1: no row
+            if (tid < kFlashKeys) {
+                int k = -1, u = 0;
+                for (int x = 0; x < nrun; ++x) {
+                    const int o = (kt - s.rtile[x]) * kFlashKeys + tid - s.roff[x];
+                    if (kt >= s.rtile[x] && o >= 0 && o < s.rn[x]) { k = x; u = o; }
+                }
+                int src = 0, pg = -1;
+                float bias = -INFINITY;
+                if (k >= 0) {
+                    const int16_t* gpg = s.meta[k];
+                    const int16_t* pst = gpg + (A.G + 1);
+                    const int16_t* perm = pst + (PS + 1);
+                    const int gid = s.ent[s.seg[sb + k]].y;
+                    const int c = gid / A.G, j = gid % A.G;
+                    const int ps0 = gpg[j], npg = gpg[j + 1] - ps0;
+                    const int m0 = pst[ps0], nmem = pst[ps0 + npg] - m0;
+                    if (u < nmem) {
+                        const int x = m0 + u;
+                        int e = 0;
+                        while (e + 1 < npg && pst[ps0 + e + 1] <= x) ++e;
+                        src = c * kChunk + perm[x];
+                        pg = (k << 16) | e;
+                        bias = 0.0f;
+                    } else {
+                        const int e = u - nmem;
+                        src = c * PS + ps0 + e;
+                        pg = (k << 16) | kSumRow | e;
+                        bias = pln_u[src] * kFlashLog2e;
+                    }
+                }
+                s.rsrc[tid] = src;
+                s.rpage[tid] = pg;
+                s.bias[tid] = bias;
+                if (tid == 0) {  // the rows the tile spans
+                    int first = kFlashKeys, last = 0;
+                    for (int x = 0; x < nrun; ++x) {
+                        const int o = (kt - s.rtile[x]) * kFlashKeys;  // rows of run x before this tile
+                        if (kt < s.rtile[x] || o >= s.rn[x] + s.roff[x]) continue;
+                        const int lo = kt == s.rtile[x] ? s.roff[x] : 0;
+                        first = min(first, lo);
+                        last = max(last, min(kFlashKeys, s.roff[x] + s.rn[x] - o));
+                    }
+                    s.firstrow = first;
+                    s.tilerows = last;
+                }
+            }
+            __syncthreads();
+            const int nk = s.tilerows;
+            // K and V rows straight into LDS (a wave's 64 lanes fill four rows per
+            // instruction; a slot without a row loads the tile's first row, a valid
+            // address, and is masked)
+#pragma unroll
+            for (int ii = 0; ii < kFlashKeys / 4 / kGroupWaves; ++ii) {
+                const int i = w + kGroupWaves * ii;
+                const int row = 4 * i + g;
+                const int rr = s.rpage[row] >= 0 ? row : s.firstrow;
+                const int src = s.rsrc[rr];
+                const bool sum = (s.rpage[rr] & kSumRow) != 0;
+                const bf16_t* ks = sum ? pk_u + (int64_t)src * kD : kc + kv_pos<PAGED>(A, bs, src);
+                const bf16_t* vs = sum ? pv_u + (int64_t)src * kD : vc + kv_pos<PAGED>(A, bs, src);
+                __builtin_amdgcn_global_load_lds(ks + 8 * (li ^ fswz_k(row)), &s.kt[4 * i][0], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vs + 8 * (li ^ fswz_v(row)), &s.vt[4 * i][0], 16, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (active) {
+                const int nkb = (nk + 15) / 16;
+                f32x4_t S[4][2];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if (kb < nkb) {
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const int row = 16 * kb + li;
+                            const int chunk = (4 * kk + g) ^ fswz_k(row);
+                            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
+                            S[kb][0] = mfma16(av, qb[0][kk], S[kb][0]);
+                            S[kb][1] = mfma16(av, qb[1][kk], S[kb][1]);
+                        }
+                    }
+                }
+                // logits (log2 units) of the column's own run under its page mask, online
+                // softmax (a column's keys live in lanes l, l^16, l^32, l^48)
+                float P[4][2][4];
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    float mt = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = 16 * kb + 4 * g + r;
+                            const int pg = s.rpage[key];
+                            const bool mine = pg >= 0 && (pg >> 16) == cbat[cb];
+                            const bool opened = ((copen[cb] >> (pg & 31)) & 1u) != 0;
+                            const bool ok = mine && ((pg & kSumRow) ? !opened : opened);
+                            const float lam = ok ? __builtin_fmaf(sc2, S[kb][cb][r], s.bias[key]) : -INFINITY;
+                            P[kb][cb][r] = lam;
+                            mt = fmaxf(mt, lam);
+                        }
+                    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+                    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                    const float mn = fmaxf(m_run[cb], mt);
+                    const float al = m_run[cb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[cb] - mn);
+                    const float ms = mn == -INFINITY ? 0.0f : mn;
+                    float ls = 0.0f;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float pw = __builtin_amdgcn_exp2f(P[kb][cb][r] - ms);  // exp2(-inf) = 0
+                            P[kb][cb][r] = pw;
+                            ls += pw;
+                        }
+                    l_run[cb] = __builtin_fmaf(l_run[cb], al, ls);
+                    m_run[cb] = mn;
+                    if (__any(al != 1.0f)) {
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) O[cb][db] *= al;
+                    }
+                }
+                // O^T += V^T P^T over the tile's 32-key steps (P as bf16 hi + lo)
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    if (32 * sp >= nk) break;
+                    bf16x8_t ph[2], pl[2];
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                        for (int jj = 0; jj < 8; jj += 2) {
+                            const ff32x2_t xv = {P[2 * sp + jj / 4][cb][jj % 4], P[2 * sp + jj / 4][cb][jj % 4 + 1]};
+                            const fbf16x2_t h = __builtin_convertvector(xv, fbf16x2_t);
+                            const ff32x2_t rv = xv - __builtin_convertvector(h, ff32x2_t);
+                            const fbf16x2_t lo = __builtin_convertvector(rv, fbf16x2_t);
+                            ph[cb][jj] = h[0];
+                            ph[cb][jj + 1] = h[1];
+                            pl[cb][jj] = lo[0];
+                            pl[cb][jj + 1] = lo[1];
+                        }
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) {
+                        const fs16x4_t v0 = flash_vt_read(s.vt, 32 * sp + 4 * g, 16 * db, li);
+                        const fs16x4_t v1 = flash_vt_read(s.vt, 32 * sp + 16 + 4 * g, 16 * db, li);
+                        const fs16x4_t both[2] = {v0, v1};
+                        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb) {
+                            O[cb][db] = mfma16(av, ph[cb], O[cb][db]);
+                            O[cb][db] = mfma16(av, pl[cb], O[cb][db]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();  // the tile's rows are consumed before the next tile or batch
+        }
+        // the batch's columns: partial states (o, m in natural units, l)
+        if (active) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                float lt = l_run[cb];
+                lt += __shfl_xor(lt, 16, 64);
+                lt += __shfl_xor(lt, 32, 64);
+                if (cbat[cb] < 0) continue;
+                float* dst = A.part_pg + (crh[cb] * A.TG + ct[cb]) * kPartStride;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const f32x4_t o = O[cb][db];
+                    *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+                if (g == 0) {
+                    dst[kD] = m_run[cb] == -INFINITY ? -INFINITY : m_run[cb] * kFlashLn2;
+                    dst[kD + 1] = lt;
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------- combine
 
 // out = merge of the flash partial and the page partials of every opened slot.
@@ -1398,41 +1767,9 @@ static PrefillPlan plan_prefill(const lod_params* p, int n_q) {
     return P;
 }
 
-// A second stream on the caller's device, with two events, per host thread: the flash
-// kernel runs on it beside the bucket and pages kernels (all three need only the
-// selection), forked after the selection and joined before the combine.  Created by the
-// thread's first prefill call on that device and kept until the thread ends.
-struct PrefillSide {
-    hipStream_t st;
-    hipEvent_t fork, join;
-};
-static int prefill_side(hipStream_t caller, PrefillSide& out) {
-    constexpr int kMaxDev = 64;
-    static thread_local PrefillSide cache[kMaxDev] = {};
-    int dev = 0;
-    if (caller ? hipStreamGetDevice(caller, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
-        return LOD_ERR_HIP;
-    if (dev < 0 || dev >= kMaxDev) return LOD_ERR_HIP;
-    PrefillSide& c = cache[dev];
-    if (!c.st) {
-        int cur = 0;
-        if (hipGetDevice(&cur) != hipSuccess) return LOD_ERR_HIP;
-        if (cur != dev && hipSetDevice(dev) != hipSuccess) return LOD_ERR_HIP;
-        PrefillSide n{};
-        hipError_t e = hipStreamCreateWithFlags(&n.st, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
-        if (cur != dev) (void)hipSetDevice(cur);
-        if (e != hipSuccess) return LOD_ERR_HIP;
-        c = n;
-    }
-    out = c;
-    return LOD_OK;
-}
-
 template <int HG>
 static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const PagesArgs& P, int batch,
-                                int nunits_q, hipStream_t st, const PrefillSide& side) {
+                                int nunits_q, hipStream_t st) {
     constexpr int QT = kFlashRowHeads / HG;
     const int ntiles = (S.nq + QT - 1) / QT;
     trace_point(0, st);
@@ -1447,29 +1784,25 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
     hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols>), dim3(ntiles * (kFlashRowHeads / kSelCols) * S.Hkv, 1, batch),
                        dim3(kThreads), 0, st, S);
     trace_point(2, st);
-    // fork: the flash kernel on the side stream, bucket and pages on the caller's
-    if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(side.st, side.fork, 0) != hipSuccess)
-        return LOD_ERR_HIP;
     if (F.btab)
         hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
-                           side.st, F);
+                           st, F);
     else
         hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
-                           side.st, F);
-    trace_point(3, side.st);
-    if (hipEventRecord(side.join, side.st) != hipSuccess) return LOD_ERR_HIP;
+                           st, F);
+    trace_point(3, st);
     hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kBucketThreads), 0, st, P);
     trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
     const dim3 pgrid((maxpairs + kPairsPerWG - 1) / kPairsPerWG, nunits_q * S.Hkv * batch);
-    if (P.q4)  // decoded from the index: the cache view does not matter
+    const dim3 ggrid((maxpairs + kGroupPairs - 1) / kGroupPairs, nunits_q * S.Hkv * batch);
+    if (P.q4)  // decoded from the index (not bf16 rows): the VALU kernel; the view does not matter
         hipLaunchKernelGGL((prefill_pages_kernel<HG, false, true>), pgrid, dim3(kThreads), 0, st, P);
     else if (P.btab)
-        hipLaunchKernelGGL((prefill_pages_kernel<HG, true, false>), pgrid, dim3(kThreads), 0, st, P);
+        hipLaunchKernelGGL((prefill_group_kernel<HG, true>), ggrid, dim3(kGroupThreads), 0, st, P);
     else
-        hipLaunchKernelGGL((prefill_pages_kernel<HG, false, false>), pgrid, dim3(kThreads), 0, st, P);
+        hipLaunchKernelGGL((prefill_group_kernel<HG, false>), ggrid, dim3(kGroupThreads), 0, st, P);
     trace_point(5, st);
-    if (hipStreamWaitEvent(st, side.join, 0) != hipSuccess) return LOD_ERR_HIP;  // join
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + kThreads / 32 - 1) / (kThreads / 32))),
                        dim3(kThreads), 0, st, P, nrh);
@@ -1564,8 +1897,6 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
     const int Hq = params->n_q_heads, Hkv = params->n_kv_heads, HG = Hq / Hkv, TG = params->top_groups;
     const int TPW = params->top_pages > 0 ? params->top_pages : 1;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    PrefillSide side;
-    if ((rc = prefill_side(st, side)) != LOD_OK) return rc;
     for (int r0 = 0; r0 < n_q; r0 += P.rows) {
         const int rows = (n_q - r0) < P.rows ? (n_q - r0) : P.rows;
         const int nunits_q = (rows + kChunk - 1) / kChunk;
@@ -1606,6 +1937,7 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.index = S.index; G.L = L; G.max_chunks = S.max_chunks; G.G = S.G; G.W = S.W; G.TG = TG;
             G.drop = params->drop_remainder;
             G.q4 = params->int4_pages;
+            G.tp = params->top_pages;
             G.rec = S.rec;
             G.selg = S.selg;
             G.plist = reinterpret_cast<int2*>(w + P.off_plist);
@@ -1617,10 +1949,10 @@ extern "C" int lod_attend_prefill(const lod_params* params, const lod_index* ind
             G.out = out + row0 * Hq * kD;
             G.units_per_seq_kv = nunits_q;
             switch (HG) {
-                case 1: rc = launch_prefill_batch<1>(S, F, G, 1, nunits_q, st, side); break;
-                case 2: rc = launch_prefill_batch<2>(S, F, G, 1, nunits_q, st, side); break;
-                case 4: rc = launch_prefill_batch<4>(S, F, G, 1, nunits_q, st, side); break;
-                default: rc = launch_prefill_batch<8>(S, F, G, 1, nunits_q, st, side); break;
+                case 1: rc = launch_prefill_batch<1>(S, F, G, 1, nunits_q, st); break;
+                case 2: rc = launch_prefill_batch<2>(S, F, G, 1, nunits_q, st); break;
+                case 4: rc = launch_prefill_batch<4>(S, F, G, 1, nunits_q, st); break;
+                default: rc = launch_prefill_batch<8>(S, F, G, 1, nunits_q, st); break;
             }
             if (rc != LOD_OK) return rc;
         }
