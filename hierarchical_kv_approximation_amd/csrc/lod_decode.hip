@@ -1994,10 +1994,11 @@ constexpr int kPrefillRows = 256;
 
 using namespace lodi;
 
-extern "C" int lod_attend_decode(const lod_params* params, const lod_index* index, lod_kv kv,
-                                 const void* q, const int32_t* seq_lens, int32_t batch,
-                                 int32_t max_seq_len, float* out, int32_t* sel_groups,
-                                 int32_t* sel_pages, void* ws, size_t ws_bytes, void* stream) {
+namespace lodi {
+// Every check of a decode call except its workspace (host only, nothing enqueued).
+static int check_decode_args(const lod_params* params, const lod_index* index, const lod_kv& kv,
+                             const void* q, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                             const float* out) {
     int rc = check_params(params);
     if (rc != LOD_OK) return rc;
     if (!index || !index->mem || !q || !seq_lens || !out || batch <= 0 || max_seq_len <= 0)
@@ -2006,8 +2007,18 @@ extern "C" int lod_attend_decode(const lod_params* params, const lod_index* inde
     if ((rc = check_kv_view(params, kv, max_seq_len)) != LOD_OK) return rc;
     if (batch != index->batch) return LOD_ERR_ARG;
     if (built_chunks(params, (int64_t)max_seq_len - 1) > index->max_chunks) return LOD_ERR_ARG;
+    if (index->bytes < make_layout(params, index->batch, index->max_chunks).total) return LOD_ERR_WORKSPACE;
+    return LOD_OK;
+}
+}  // namespace lodi
+
+extern "C" int lod_attend_decode(const lod_params* params, const lod_index* index, lod_kv kv,
+                                 const void* q, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_seq_len, float* out, int32_t* sel_groups,
+                                 int32_t* sel_pages, void* ws, size_t ws_bytes, void* stream) {
+    const int rc = check_decode_args(params, index, kv, q, seq_lens, batch, max_seq_len, out);
+    if (rc != LOD_OK) return rc;
     const lod_index_layout_t L = make_layout(params, index->batch, index->max_chunks);
-    if (index->bytes < L.total) return LOD_ERR_WORKSPACE;
     const DecodePlan P = plan_decode(params, batch, max_seq_len);
     if (!ws || ws_bytes < P.bytes) return LOD_ERR_WORKSPACE;
     DecodeArgs A;
@@ -2048,9 +2059,8 @@ extern "C" int lod_attend_decode_noalloc(const lod_params* params, const lod_ind
                                          const void* q, const int32_t* seq_lens, int32_t batch,
                                          int32_t max_seq_len, float* out, int32_t* sel_groups,
                                          int32_t* sel_pages, void* stream) {
-    int rc = check_params(params);
+    int rc = check_decode_args(params, index, kv, q, seq_lens, batch, max_seq_len, out);
     if (rc != LOD_OK) return rc;
-    if (batch <= 0 || max_seq_len <= 0) return LOD_ERR_ARG;
     if (plan_decode(params, batch, max_seq_len).bytes > (size_t)LOD_NOALLOC_WS_BYTES) return LOD_ERR_WORKSPACE;
     void* ws = nullptr;
     if ((rc = noalloc_workspace(&ws)) != LOD_OK) return rc;

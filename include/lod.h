@@ -18,13 +18,12 @@
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns every
  *     buffer; the library never allocates device memory and keeps no state apart from
- *     the optional trace events of lod_trace_events and, per host thread and device, one
- *     extra stream with two events that the first bf16 lod_attend_prefill call creates
- *     (the call runs one of its kernels there, ordered after the caller's earlier work
- *     and before its later work by those events, so the stream-ordering contract holds).
- *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work;
- *     they return before the GPU finishes.  Device faults surface at the caller's next
- *     synchronisation of that stream.
+ *     the optional trace events of lod_trace_events (and the fixed workspace of
+ *     lod_attend_decode_noalloc).  It creates no stream or event.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue kernels
+ *     on that stream (no memset, copy or host synchronisation), so they can be captured
+ *     in a HIP graph; they return before the GPU finishes.  Device faults surface at the
+ *     caller's next synchronisation of that stream.
  *   - Arguments are validated on the host before anything is enqueued: a bad argument
  *     returns LOD_ERR_ARG (or LOD_ERR_UNSUPPORTED / LOD_ERR_WORKSPACE) and enqueues
  *     nothing.  A failed launch returns LOD_ERR_HIP.  No exception crosses the ABI.
@@ -233,9 +232,10 @@ int lod_attend_decode(const lod_params* params, const lod_index* index, lod_kv k
  *   - The call allocates nothing and calls no allocating routine.  The array's address
  *     on the current device is looked up once per device (hipGetSymbolAddress) on the
  *     first call there; `stream` must belong to the current device.
- *   - LOD_ERR_WORKSPACE when lod_decode_ws_bytes(params, batch, max_seq_len) exceeds
- *     LOD_NOALLOC_WS_BYTES (32 MiB: e.g. batch 16 at 128K context, or batch 8 at 256K,
- *     with 64/8 heads); nothing is enqueued then.
+ *   - Arguments are checked as by lod_attend_decode; then LOD_ERR_WORKSPACE when
+ *     lod_decode_ws_bytes(params, batch, max_seq_len) exceeds LOD_NOALLOC_WS_BYTES
+ *     (32 MiB: e.g. batch 16 at 128K context, or batch 8 at 256K, with 64/8 heads);
+ *     nothing is enqueued then.
  *   - Every call on one device shares that device's array and leaves its last contents
  *     there (no kernel reads workspace it has not written in the same call).  Calls that
  *     may overlap on one device race on it: order them (one stream, or events).
@@ -259,6 +259,9 @@ int lod_prefill_ws_bytes(const lod_params* params, int32_t batch, int32_t n_q,
  *   out         [batch][n_q][n_q_heads][head_dim] fp32
  *   sel_groups  nullable [batch][n_q][n_q_heads][top_groups]
  *   sel_pages   nullable [batch][n_q][n_q_heads][top_groups][max(top_pages,1)]
+ * Limit (bf16 caches): the rows of one call may see at most 16384 summarised groups per
+ * KV head (512K tokens at 8 groups per chunk, 256K at 16): LOD_ERR_UNSUPPORTED beyond
+ * that, before anything is enqueued.  fp32 caches have no such limit.
  */
 int lod_attend_prefill(const lod_params* params, const lod_index* index, lod_kv kv,
                        const void* q, int32_t q_start, int32_t n_q, int32_t batch, float* out,
@@ -369,9 +372,7 @@ int lod_video_dense(const lod_video_params* params, lod_kv kv, const void* q, in
  * same host thread
  * records events[0] on its stream before its first kernel and events[1 + k] after its
  * k-th kernel (decode: k = 0 scan, 1 open-and-combine; bf16 prefill: k = 0 candidate
- * sweep, 1 select, 2 flash (recorded on the call's second stream: flash runs beside
- * bucket and pages, so events[4] follows events[2], not events[3]), 3 bucket, 4 pages,
- * 5 combine, recorded again for every batch
+ * sweep, 1 select, 2 flash, 3 bucket, 4 pages, 5 combine, recorded again for every batch
  * of rows, so the last batch's times remain; lod_video_attend: k = 0 summaries, 1 choice,
  * 2 attention).  `events` points to n_events
  * hipEvent_t handles created by the caller, who reads them with hipEventElapsedTime;

@@ -89,6 +89,8 @@ def test_bad_params_rejected_by_every_entry_point(field, value, status):
     assert L.lod_build_chunk(_p(cfg), ctypes.byref(idx), kv, 1, 0, 1, None, None, None) == status
     assert L.lod_attend_decode(_p(cfg), ctypes.byref(idx), kv, FAKE, FAKE, 1, 4096, FAKE, None, None,
                                FAKE, 1 << 40, None) == status
+    assert L.lod_attend_decode_noalloc(_p(cfg), ctypes.byref(idx), kv, FAKE, FAKE, 1, 4096, FAKE, None, None,
+                                       None) == status
     assert L.lod_attend_prefill(_p(cfg), ctypes.byref(idx), kv, FAKE, 0, 256, 1, FAKE, None, None,
                                 FAKE, 1 << 40, None) == status
     assert L.lod_dense_decode(_p(cfg), kv, FAKE, FAKE, 1, 4096, FAKE, FAKE, 1 << 40, None) == status
@@ -136,6 +138,17 @@ def test_bad_buffers_rejected():
                                None, 1 << 40, None) == lod.LOD_ERR_WORKSPACE
     assert L.lod_attend_decode(_p(cfg), ctypes.byref(good), kv, FAKE, None, 1, 8192, FAKE, None, None,
                                FAKE, 1 << 40, None) == E
+    # the fixed-workspace decode: the same argument checks, then its size limit
+    assert L.lod_attend_decode_noalloc(_p(cfg), ctypes.byref(good), kv, FAKE, FAKE, 1, 9000 + 512, FAKE,
+                                       None, None, None) == E
+    assert L.lod_attend_decode_noalloc(_p(cfg), ctypes.byref(lod.Index(FAKE.value, n.value, 2, 32)), kv, FAKE,
+                                       FAKE, 1, 8192, FAKE, None, None, None) == E
+    big = lod.Config(n_q_heads=64, n_kv_heads=8)
+    nb = ctypes.c_size_t()
+    assert L.lod_index_bytes(_p(big), 64, 131072, ctypes.byref(nb)) == 0
+    assert lod.decode_ws_bytes(big, 64, 131072) > lod.NOALLOC_WS_BYTES
+    assert L.lod_attend_decode_noalloc(_p(big), ctypes.byref(lod.Index(FAKE.value, nb.value, 64, 512)), kv, FAKE,
+                                       FAKE, 64, 131072, FAKE, None, None, None) == lod.LOD_ERR_WORKSPACE
     # prefill: q_start not on a chunk boundary
     assert L.lod_attend_prefill(_p(cfg), ctypes.byref(good), kv, FAKE, 100, 256, 1, FAKE, None, None,
                                 FAKE, 1 << 40, None) == E

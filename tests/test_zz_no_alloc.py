@@ -48,6 +48,9 @@ def test_noalloc_decode_equals_workspace_decode_twice_second_smaller():
 
 
 def test_noalloc_decode_refuses_requests_above_the_fixed_size():
+    """Batch 64 at 128K needs more than the fixed workspace: refused with
+    LOD_ERR_WORKSPACE before anything is enqueued (the index descriptor claims the
+    size such a call needs; the refusal comes before any of it is read)."""
     g, o = configs(torch.bfloat16, 64, 8, G=8)
     case = Case(g, o, 1, 1024, seed=117, gen_device="cuda")
     B, T = 64, 131072  # lod_decode_ws_bytes > LOD_NOALLOC_WS_BYTES
@@ -55,8 +58,10 @@ def test_noalloc_decode_refuses_requests_above_the_fixed_size():
     q = torch.zeros(B, 64, 128, dtype=torch.bfloat16, device="cuda")
     sl = torch.full((B,), T, dtype=torch.int32, device="cuda")
     out = torch.full((B, 64, 128), 7.0, device="cuda")
-    with pytest.raises(lod.LodError) as e:
-        lod.attend_decode_noalloc(g, case.index, case.Kd, case.Vd, q, sl, T, out=out)
-    assert e.value.status == lod.LOD_ERR_WORKSPACE
+    idx = lod.Index(case.index.mem.data_ptr(), 1 << 40, B, T // 256)
+    kv = lod.kv_view(case.Kd, case.Vd)
+    rc = lod.lib().lod_attend_decode_noalloc(g.params(), idx, kv, lod._ptr(q), lod._ptr(sl), B, T, lod._ptr(out),
+                                             None, None, lod._stream())
+    assert rc == lod.LOD_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
