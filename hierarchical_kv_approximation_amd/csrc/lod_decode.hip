@@ -6,22 +6,21 @@
 // enters the same softmax as count-weighted means ("Level of Detail Attention", How It
 // Works).
 //
-// Three launches per call, all on the caller's stream:
-//  1. scan    grid (slices + window tiles, KV heads, batch).  A slice workgroup streams
-//             a contiguous run of group summaries (mean keys, then mean values) of one
-//             (sequence, KV head) through LDS for all g query heads of that KV head.
-//             Ranking scores are the canonical fp32 fma chain (one lane per (group,
-//             head), query in registers).  Each head's local top-k groups become
-//             candidates and are left out of the slice's coarse softmax partial; every
-//             other non-empty group adds exp(scale*r + ln n) * vbar.  Every global top-k
-//             group is in its slice's local top-k, so one pass over the summaries
-//             suffices.  Window workgroups do exact tiles of the block window and the
-//             sinks.
-//  2. open    grid (top_groups, query heads, batch).  Merges the candidates into the
-//             global top-k, scores the pages of opened group i, opens the top pages,
-//             attends their rows exactly, adds unopened pages as coarse terms, and adds
-//             back the coarse terms of candidates that lost the global ranking.
-//  3. combine grid (query heads, batch).  Log-sum-exp merge of every partial state.
+// bf16 caches: two launches per call, on the caller's stream.
+//  1. scan    grid (KV heads, batch, scan workgroups per unit).  A unit is a (sequence,
+//             KV head); its workgroups stream equal runs of its 64-row tiles (the group
+//             summaries of every summarised chunk, then the sinks and the block window)
+//             through LDS for all query heads of the KV head: MFMA scores (written out
+//             for the selection), online softmax over every group (coarse, logit
+//             scale*S + ln n) and exact row, MFMA value sums, one partial state each.
+//  2. open    grid (query heads, batch).  Exact top groups from the stored scores and
+//             their error bounds (only candidates near the cut run the canonical chain),
+//             top pages, the opened pages' rows exactly and the unopened pages' means,
+//             then the merge of the scan's partials, from which the opened groups' coarse
+//             terms are subtracted with the very logits the scan used.
+// fp32 caches (VALU): slice workgroups with canonical chains keep each slice's local top
+// groups out of their coarse partial and an open step adds back those that lose the
+// global ranking; the dense baseline and row-by-row prefill reuse these kernels.
 // Partial states are (o[d] = sum w v, m, l) relative to their own max m.
 #include <mutex>
 

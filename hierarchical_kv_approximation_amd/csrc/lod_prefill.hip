@@ -13,10 +13,13 @@
 //            chain and ranked exactly; then the pages of the opened groups are ranked.
 //   flash    per tile: one online softmax over the coarse centroids (bias ln n, the
 //            row's opened groups masked out), the sinks and the causal block window.
-//   pages    per (query chunk, KV head, group block): the opened groups' pages, shared
-//            by every (row, head) that opened them: exact rows of opened pages, mean
-//            terms of unopened pages.
+//   bucket   per (query chunk, KV head): the (row, head, opened slot) pairs sorted by
+//            opened group.
+//   pages    per run of pairs that opened the same group (MFMA): the group's members and
+//            page summaries are one key tile shared by those pairs, each pair a column
+//            with its page mask: exact rows of opened pages, mean terms of unopened ones.
 //   combine  per (row, head): log-sum-exp merge of the flash and page partial states.
+// Every kernel of a call runs on the caller's stream, one after another.
 //
 // The flash kernel keeps keys as MFMA rows and (row, head) pairs as MFMA columns
 // (S^T = K Q^T), so a lane holds one column of P and the PV product O^T = V^T P^T takes
