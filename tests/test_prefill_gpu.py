@@ -60,6 +60,23 @@ def test_lod_prefill_parity(dtype, hq, hkv, q_start, nq, G, TG, TP):
     _prefill_and_compare(case, Q, q_start, rows)
 
 
+@pytest.mark.parametrize("G,TG,TP,kind", [
+    (2, 4, 2, "matched"),     # groups of about 128 keys: runs of more than 64 rows, summaries
+    (2, 2, 1, "diffuse"),     # one opened page of eight: mostly summary terms
+    (16, 16, 2, "diffuse"),   # small groups, many distinct ones: more than 4 runs per workgroup
+])
+def test_lod_prefill_group_kernel_paths(G, TG, TP, kind):
+    """The opened pages' MFMA kernel on its rarer paths: groups whose members and page
+    summaries need several key tiles, pairs that leave most pages of a group unopened,
+    and workgroups whose pairs span many groups (meta rows loaded beyond the first
+    four runs)."""
+    g, o = configs(torch.bfloat16, 16, 2, G=G, TG=TG, TP=TP)
+    case = Case(g, o, 1, 4096, seed=56)
+    case.build_gpu()
+    Q = case.queries(seed=57, n_rows=768, kind=kind)
+    _prefill_and_compare(case, Q, 3328, _sample_rows(1, 768, 16, 100, 58))
+
+
 def test_lod_prefill_diffuse_queries():
     g, o = configs(torch.bfloat16, 16, 2, G=8)
     case = Case(g, o, 1, 4096, seed=44)
