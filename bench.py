@@ -23,7 +23,6 @@ import argparse
 import dataclasses
 import ctypes
 import json
-import math
 import os
 import sys
 import time
@@ -400,7 +399,6 @@ def main():
 
     # sparsity ablation on the same inputs: the same selection, the coarse remainder
     # dropped (the scan reads the mean keys for the scores but no mean values)
-    import dataclasses
     scfg = dataclasses.replace(cfg, drop_remainder=True)
     sms = time_calls(scfg)
     sparse = {"what": "same selection, coarse remainder dropped (exact keys only)",
@@ -805,7 +803,6 @@ def bench_sigma_sweep(torch, lod, synth, cfg, hip, stream, T, seed, steps=256, s
     outputs against the dense oracle (fp64) on sampled (row, head) pairs of the prompt
     and sampled (step, head) pairs of the decode, binned by the sigma of the query's
     cluster."""
-    import dataclasses
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
