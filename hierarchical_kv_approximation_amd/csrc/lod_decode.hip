@@ -1311,8 +1311,15 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
     S.nex = S.ns + (p + 1 - S.w0);
     const int ntc = (S.ng + kSTile - 1) / kSTile;
     const int nt = ntc + (S.nex + kSTile - 1) / kSTile;
-    const int t0 = (int)((int64_t)nt * slice / A.nslice);
-    const int t1 = (int)((int64_t)nt * (slice + 1) / A.nslice);
+    // The slice is the slowest grid dimension, so on a CU the workgroups of lower slices
+    // are the older ones, and the oldest waves issue first: the youngest workgroups of a
+    // CU run last, much of the time alone.  So the older slices take the larger shares
+    // (one tile more when the tiles do not divide evenly) and the end of the list (the
+    // window's exact tiles, read from the cache with a stride, are the slowest), and the
+    // youngest the first coarse tiles.
+    const int tq = nt / A.nslice, tr = nt % A.nslice;
+    const int t1 = nt - (slice * tq + min(slice, tr));
+    const int t0 = t1 - (tq + (slice < tr ? 1 : 0));
     const int hq0 = kvh * HG;
     float* part0 = A.part + ((int64_t)(b * A.Hq + hq0) * A.nslot + slice) * kPartStride;
     const int64_t head_stride = (int64_t)A.nslot * kPartStride;
