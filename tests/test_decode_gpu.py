@@ -183,6 +183,21 @@ def test_c3_full_size_128k_batch8_sampled():
     _decode_and_compare(case, (st, oidx), [131072] * 8, q, check_heads=heads)
 
 
+def test_many_tiles_per_scan_workgroup():
+    """Batch 8 with 32 query and 32 KV heads at 64K: 256 (sequence, KV head) units, so
+    each is scanned by only 4 workgroups over its 41 tiles, and a workgroup covers more
+    than the 8 tiles whose ln n it holds at once (it loads the next 8 mid-scan).  Two
+    units checked against the oracle, rows at different lengths."""
+    g, o = configs(torch.bfloat16, 32, 32, G=8, W=512, S=4)
+    case = Case(g, o, 8, 65536, seed=25, gen_device="cuda")
+    case.build_gpu()
+    keys = [(0, 0), (5, 31)]
+    st, oidx = case.oracle_index(keys)
+    seq = [65536, 60001, 65536, 65536, 65536, 64500, 65536, 65536]
+    heads = [(0, 0), (5, 31)]
+    _decode_and_compare(case, (st, oidx), seq, case.queries(seed=26), check_heads=heads)
+
+
 @pytest.mark.parametrize("T", [65536, 131072])
 def test_batch1_long_context_one_kv_head(T):
     """One sequence with one KV head at 64K and 128K: the scan splits the unit into its
@@ -249,4 +264,45 @@ def test_bf16_ties_reach_every_selection_path(T, lo, hi):
         idx = oidx[(0, h // 8)]
         assert len({idx["gk"][x // 8, x % 8].tobytes() for x in sg[0, h]}) == 1
         ref, _ = orc.dense(o, *st[(0, h // 8)], qf[0, h], T - 1)
+        assert np.max(np.abs(out[0, h] - ref)) <= TOL[torch.bfloat16]
+
+
+
+def test_bf16_every_group_tied_exactly():
+    """GQA 8/1, bf16: every key agrees with every other on its first 64 coordinates, the
+    last 64 take one of 8 values per 32-key run, and the queries are zero on the last 64,
+    so every non-empty group of every chunk ties exactly, in the canonical chain and in
+    the MFMA scores alike: far more candidates than the open step re-scores, so it ranks
+    every group canonically.  Ties go to the lower id, so the first chunk's groups open;
+    selections equal the oracle's, outputs equal the oracle and dense attention."""
+    T, Hq, Hkv = 49152, 8, 1
+    g, o = configs(torch.bfloat16, Hq, Hkv, G=8, W=512, S=4)
+    case = Case(g, o, 1, T, seed=61, gen_device="cuda")
+    gen = torch.Generator().manual_seed(62)
+    base = torch.randn(Hkv, 64, generator=gen).to(torch.bfloat16)
+    cen = torch.randn(Hkv, 8, 64, generator=gen).to(torch.bfloat16)
+    run = (torch.arange(T) % 256) // 32
+    K = torch.empty(1, T, Hkv, 128, dtype=torch.bfloat16)
+    K[0, :, :, :64] = base[None]
+    K[0, :, :, 64:] = cen[:, run].permute(1, 0, 2)
+    case.K, case.Kd = K, K.cuda()
+    case.V = case.V.cpu()
+    case._streams = {}
+    case.build_gpu()
+    st, oidx = case.oracle_index([(0, 0)])
+    compare_index(case.index, oidx[(0, 0)], 0, 0, case.nchunks)
+    q = torch.randn(1, Hq, 128, generator=gen).to(torch.bfloat16)
+    q[..., 64:] = 0
+    _decode_and_compare(case, (st, oidx), [T], q)
+    sl = torch.tensor([T], dtype=torch.int32, device="cuda")
+    out, sg, _ = lod.attend_decode(g, case.index, case.Kd, case.Vd, q.cuda(), sl, T, want_selection=True)
+    torch.cuda.synchronize()
+    gcount = oidx[(0, 0)]["gcount"].reshape(-1)
+    assert int((gcount > 0).sum()) > 128
+    nonempty = [x for x in range(gcount.size) if gcount[x] > 0][:8]
+    qf = q.float().numpy()
+    sg, out = sg.cpu().numpy(), out.cpu().numpy()
+    for h in range(Hq):
+        assert list(sg[0, h]) == nonempty, sg[0, h]
+        ref, _ = orc.dense(o, *st[(0, 0)], qf[0, h], T - 1)
         assert np.max(np.abs(out[0, h] - ref)) <= TOL[torch.bfloat16]
