@@ -35,5 +35,7 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
 
 constexpr int kFlashRowHeads = 128;  // query rows x heads per prefill workgroup
 constexpr int kFlashKeys = 64;       // keys per LDS tile
+constexpr int kFlashWaves = 8;       // waves of a prefill flash workgroup (one 16-column block each)
+constexpr int kFlashThreads = 64 * kFlashWaves;
 
 }  // namespace lodi

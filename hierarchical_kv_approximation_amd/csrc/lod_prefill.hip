@@ -69,7 +69,7 @@ template <int HG>
 struct FlashSmem {
     alignas(16) bf16_t kt[2][kFlashKeys][kD];  // key tiles (double buffer)
     alignas(16) bf16_t vt[2][kFlashKeys][kD];  // value tiles (double buffer)
-    float bias[2][kFlashKeys];                 // log2 units; -inf: not a key
+    alignas(16) float bias[2][kFlashKeys];     // log2 units; -inf: not a key
     int kpos[2][kFlashKeys];                   // key position for the causal test (INT_MIN: none)
     int32_t sel[kFlashRowHeads][kMaxTG];       // opened groups per column (LoD)
 };
@@ -103,8 +103,8 @@ __device__ __forceinline__ void flash_issue(FlashSmem<HG>& s, const FlashArgs& A
                                             const bf16_t* kb, const bf16_t* vb, const float* gln, int bs) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        const int i = w + 4 * ii;
+    for (int ii = 0; ii < kFlashKeys / 4 / kFlashWaves; ++ii) {
+        const int i = w + kFlashWaves * ii;
         const int row = 4 * i + g;
         const int rr = row < nk ? row : nk - 1;
         const int64_t off = coarse ? (int64_t)(k0 + rr) * kD : kv_pos<PAGED>(A, bs, k0 + rr);
@@ -117,16 +117,24 @@ __device__ __forceinline__ void flash_issue(FlashSmem<HG>& s, const FlashArgs& A
     }
 }
 
-// Workgroup: 128 (row, head) columns = (128 / HG) query rows x HG heads of one KV head.
-// Column n = row * HG + head; wave w owns column blocks 2w and 2w+1.
+// Workgroup: 128 (row, head) columns = (128 / HG) query rows x HG heads of one KV head,
+// in 8 waves.  Column n = row * HG + head; wave w owns column block w (columns 16w ..
+// 16w+15), so a wave's registers stay under 128 and four waves share each SIMD: with
+// two column blocks per wave (4 waves, 232 registers) only two did, and the softmax and
+// conversion chains left the matrix cores idle four fifths of the time.
 template <int HG, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(kFlashThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void prefill_flash_kernel(FlashArgs A) {
     __shared__ FlashSmem<HG> s;
     constexpr int QT = kFlashRowHeads / HG;
     const int nsplit = A.index ? A.nsplit : 1;
-    const int tile = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
-    const int kvh = blockIdx.y, b = blockIdx.z, bs = A.seq + b;
+    // KV head fastest in the workgroup order: workgroups go to the 8 XCDs round robin, so
+    // each XCD's L2 serves the key tiles of one KV head (with the tile fastest, every
+    // XCD streamed every head's centroids)
+    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const int kvh = lin % A.Hkv, tx = lin / A.Hkv;
+    const int tile = tx / nsplit, split = tx % nsplit;
+    const int b = blockIdx.z, bs = A.seq + b;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
     const int r0 = tile * QT;
     const int nrows = min(QT, A.nq - r0);
@@ -134,30 +142,22 @@ void prefill_flash_kernel(FlashArgs A) {
     const int hq0 = kvh * HG;
     const float sc2 = A.scale * kFlashLog2e;
 
-    // Q^T operands for this lane's two columns, row positions, per-column masks
-    bf16x8_t qb[2][4];
-    int prow[2];
-    int colrow[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int n = 16 * (2 * w + cb) + li;
+    // Q^T operands for this lane's column, its row position
+    bf16x8_t qb[4];
+    int prow, colrow;
+    {
+        const int n = 16 * w + li;
         const int rl = n / HG, h = n % HG;
-        colrow[cb] = rl;
-        prow[cb] = rl < nrows ? A.pos0 + r0 + rl : INT_MIN;  // INT_MIN: no key passes
+        colrow = rl;
+        prow = rl < nrows ? A.pos0 + r0 + rl : INT_MIN;  // INT_MIN: no key passes
         const bf16_t* qr = A.q + (((int64_t)b * A.nq + r0 + min(rl, nrows - 1)) * A.Hq + hq0 + h) * kD;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
+        for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
     }
-    f32x4_t O[2][8];
-    float m_run[2], l_run[2];
+    f32x4_t O[8];
+    float m_run = -INFINITY, l_run = 0.0f;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        m_run[cb] = -INFINITY;
-        l_run[cb] = 0.0f;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    for (int db = 0; db < 8; ++db) O[db] = {0.0f, 0.0f, 0.0f, 0.0f};
     // head kvh of sequence bs; the row of position x adds kv_pos(A, bs, x)
     const bf16_t* kc = A.k + kvh * A.sh + kv_seq<PAGED>(A, bs);
     const bf16_t* vc = A.v + kvh * A.sh + kv_seq<PAGED>(A, bs);
@@ -189,7 +189,7 @@ void prefill_flash_kernel(FlashArgs A) {
         gln = reinterpret_cast<const float*>(A.index + A.L.gln) + gbase;
         if (t0 < ct) {
             // opened groups of the tile's columns (left out of the coarse terms)
-            for (int x = tid; x < kFlashRowHeads * A.TG; x += kThreads) {
+            for (int x = tid; x < kFlashRowHeads * A.TG; x += kFlashThreads) {
                 const int n = x / A.TG, t = x % A.TG;
                 const int rl = n / HG, h = n % HG;
                 s.sel[n][t] = rl < nrows ? A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h) * A.TG + t] : -1;
@@ -232,115 +232,111 @@ void prefill_flash_kernel(FlashArgs A) {
             flash_issue<HG, PAGED>(s, A, buf ^ 1, coarse, k0, nk, coarse ? gk : kc, coarse ? gv : vc, gln, bs);
         }
         tile_of(t, coarse, k0, nk);
-        // excluded keys of this lane's columns: their opened groups inside a coarse tile
-        uint64_t ex[2] = {0, 0};
+        // excluded keys of this lane's column: its opened groups inside a coarse tile
+        uint64_t ex = 0;
         if (coarse) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                const int n = 16 * (2 * w + cb) + li;
-                uint64_t msk = 0;
-                for (int u = 0; u < A.TG; ++u) {
-                    const int gg = s.sel[n][u] - k0;
-                    if (gg >= 0 && gg < kFlashKeys) msk |= 1ull << gg;
-                }
-                ex[cb] = msk;
+            const int n = 16 * w + li;
+            for (int u = 0; u < A.TG; ++u) {
+                const int gg = s.sel[n][u] - k0;
+                if (gg >= 0 && gg < kFlashKeys) ex |= 1ull << gg;
             }
         }
-        // S^T = K Q^T for 4 key blocks x 2 column blocks
-        f32x4_t S[4][2];
+        // S^T = K Q^T for 4 key blocks.  LDS addresses are formed here from one lane value
+        // that the compiler cannot see through, so they are not hoisted out of the loop
+        // into registers of their own (a key row 16 kb + li holds chunk 4 kk + g at
+        // position (4 kk + g) ^ li)
+        int lo_ = li;
+        asm volatile("" : "+v"(lo_));
+        const bf16_t* ktb = &s.kt[buf][0][0] + lo_ * kD;
+        f32x4_t S[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
-            S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+            S[kb] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int row = 16 * kb + li;
-                const int chunk = (4 * kk + g) ^ fswz_k(row);
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[buf][row][8 * chunk]);
-                S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
-                S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktb + 16 * kb * kD + 8 * ((4 * kk + g) ^ lo_));
+                S[kb] = mfma16(a, qb[kk], S[kb]);
             }
         }
         // logits (log2 units), masks, online softmax (a column's 64 keys live in lanes
         // l, l^16, l^32, l^48).  A column may see no key in a tile (all masked): its
         // maximum then stays -inf and the guards below keep every weight 0.
-        float P[4][2][4];
+        float P[4][4];
+        float mt = -INFINITY;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            float mt = -INFINITY;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 16 * kb + 4 * g + r;
-                    const bool ok = s.kpos[buf][key] <= prow[cb] && !((ex[cb] >> key) & 1ull);
-                    const float lam = ok ? __builtin_fmaf(sc2, S[kb][cb][r], s.bias[buf][key]) : -INFINITY;
-                    P[kb][cb][r] = lam;
-                    mt = fmaxf(mt, lam);
-                }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float mn = fmaxf(m_run[cb], mt);
-            const float a = m_run[cb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[cb] - mn);
-            const float ms = mn == -INFINITY ? 0.0f : mn;
-            float ls = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(P[kb][cb][r] - ms);  // exp2(-inf) = 0
-                    P[kb][cb][r] = p;
-                    ls += p;
-                }
-            l_run[cb] = __builtin_fmaf(l_run[cb], a, ls);
-            m_run[cb] = mn;
-            if (__any(a != 1.0f)) {  // the maximum moved for some column of the wave
-#pragma unroll
-                for (int db = 0; db < 8; ++db) O[cb][db] *= a;
+            for (int r = 0; r < 4; ++r) {
+                const int key = 16 * kb + 4 * g + r;
+                const bool ok = s.kpos[buf][key] <= prow && !((ex >> key) & 1ull);
+                const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], s.bias[buf][key]) : -INFINITY;
+                P[kb][r] = lam;
+                mt = fmaxf(mt, lam);
             }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(m_run, mt);
+        const float a = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
+        const float ms = mn == -INFINITY ? 0.0f : mn;
+        float ls = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(P[kb][r] - ms);  // exp2(-inf) = 0
+                P[kb][r] = p;
+                ls += p;
+            }
+        l_run = __builtin_fmaf(l_run, a, ls);
+        m_run = mn;
+        if (__any(a != 1.0f)) {  // the maximum moved for some column of the wave
+#pragma unroll
+            for (int db = 0; db < 8; ++db) O[db] *= a;
         }
         // O^T += V^T P^T over two 32-key steps.  MFMA k index e of lane group g is key
         // 32 st + 16 (e / 4) + 4 g + e % 4 on both operands; P as bf16 hi + lo.
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-            bf16x8_t ph[2], pl[2];
+            bf16x8_t ph, pl;
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int j = 0; j < 8; j += 2) {  // two at a time: one packed conversion each
-                    const ff32x2_t x = {P[2 * sp + j / 4][cb][j % 4], P[2 * sp + j / 4][cb][j % 4 + 1]};
-                    const fbf16x2_t h = __builtin_convertvector(x, fbf16x2_t);
-                    const ff32x2_t r = x - __builtin_convertvector(h, ff32x2_t);
-                    const fbf16x2_t lo = __builtin_convertvector(r, fbf16x2_t);
-                    ph[cb][j] = h[0];
-                    ph[cb][j + 1] = h[1];
-                    pl[cb][j] = lo[0];
-                    pl[cb][j + 1] = lo[1];
-                }
+            for (int j = 0; j < 8; j += 2) {  // two at a time: one packed conversion each
+                const ff32x2_t x = {P[2 * sp + j / 4][j % 4], P[2 * sp + j / 4][j % 4 + 1]};
+                const fbf16x2_t h = __builtin_convertvector(x, fbf16x2_t);
+                const ff32x2_t r = x - __builtin_convertvector(h, ff32x2_t);
+                const fbf16x2_t lo = __builtin_convertvector(r, fbf16x2_t);
+                ph[j] = h[0];
+                ph[j + 1] = h[1];
+                pl[j] = lo[0];
+                pl[j + 1] = lo[1];
+            }
+            // V^T operands (flash_vt_read's addresses, formed here as for K): row
+            // 32 sp + 4 g + li / 4 (and 16 rows on), elements 16 db + 4 (li % 4) .. at chunk
+            // (2 db + (li / 2) % 2) ^ 2 ((4 g + li / 4) % 8)
+            int vs_ = 2 * ((4 * g + (li >> 2)) & 7);
+            asm volatile("" : "+v"(vs_));
+            const bf16_t* vtb = &s.vt[buf][0][0] + (32 * sp + 4 * g + (li >> 2)) * kD + 4 * (li & 1);
+            const int vx = (li >> 1) & 1;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const fs16x4_t v0 = flash_vt_read(s.vt[buf], 32 * sp + 4 * g, 16 * db, li);
-                const fs16x4_t v1 = flash_vt_read(s.vt[buf], 32 * sp + 16 + 4 * g, 16 * db, li);
+                const bf16_t* p0 = vtb + 8 * (((2 * db) ^ vs_) + vx);
+                typedef __attribute__((address_space(3))) fs16x4_t lds_fs16x4_t;
+                const fs16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_fs16x4_t*)(p0));
+                const fs16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_fs16x4_t*)(p0 + 16 * kD));
                 const fs16x4_t both[2] = {v0, v1};
                 const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    O[cb][db] = mfma16(av, ph[cb], O[cb][db]);
-                    O[cb][db] = mfma16(av, pl[cb], O[cb][db]);
-                }
+                O[db] = mfma16(av, ph, O[db]);
+                O[db] = mfma16(av, pl, O[db]);
             }
         }
     }
 
-    // column totals (the 4 lanes of a column hold partial sums), then write
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        float lt = l_run[cb];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
-        const int rl = colrow[cb];
-        if (rl >= nrows) continue;
-        const int n = 16 * (2 * w + cb) + li;
+    // column total (the 4 lanes of a column hold partial sums), then write
+    float lt = l_run;
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const int rl = colrow;
+    if (rl < nrows) {
+        const int n = 16 * w + li;
         const int h = n % HG;
         const int64_t rh = ((int64_t)b * A.nq + r0 + rl) * A.Hq + hq0 + h;
         if (A.index == nullptr) {
@@ -348,7 +344,7 @@ void prefill_flash_kernel(FlashArgs A) {
             const float inv = 1.0f / lt;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const f32x4_t o = O[cb][db];
+                const f32x4_t o = O[db];
                 *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) =
                     make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
             }
@@ -356,11 +352,11 @@ void prefill_flash_kernel(FlashArgs A) {
             float* dst = A.part + split * A.split_stride + rh * kPartStride;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const f32x4_t o = O[cb][db];
+                const f32x4_t o = O[db];
                 *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
             }
             if (g == 0) {
-                dst[kD] = m_run[cb] == -INFINITY ? -INFINITY : m_run[cb] * kFlashLn2;  // natural units
+                dst[kD] = m_run == -INFINITY ? -INFINITY : m_run * kFlashLn2;  // natural units
                 dst[kD + 1] = lt;
             }
         }
@@ -1788,10 +1784,10 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
                        dim3(kThreads), 0, st, S);
     trace_point(2, st);
     if (F.btab)
-        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
                            st, F);
     else
-        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kThreads), 0,
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
                            st, F);
     trace_point(3, st);
     hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kBucketThreads), 0, st, P);
@@ -1821,10 +1817,10 @@ template <int HG>
 static void launch_flash(const FlashArgs& A, int batch, hipStream_t st) {
     constexpr int QT = kFlashRowHeads / HG;
     if (A.btab)
-        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kThreads),
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kFlashThreads),
                            0, st, A);
     else
-        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kThreads),
+        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3((A.nq + QT - 1) / QT, A.Hkv, batch), dim3(kFlashThreads),
                            0, st, A);
 }
 
