@@ -1683,23 +1683,28 @@ void prefill_group_kernel(PagesArgs A) {
 // ---------------------------------------------------------------------------- combine
 
 // out = merge of the flash partial and the page partials of every opened slot.
+// KM: the most states a call has (flash splits + page slots), so that the registers
+// holding them in flight are no more than needed (with room for 24 states the kernel ran
+// at two waves per SIMD).
+template <int KM>
 __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, int64_t nrh) {
     // 32 threads per (row, head), 4 output elements each: 8 (row, head) per workgroup
     const int64_t rh = (int64_t)blockIdx.x * (kThreads / 32) + (threadIdx.x >> 5);
     const int d4 = 4 * (threadIdx.x & 31);
     if (rh >= nrh) return;
-    // every state's (m, l, o[d4 .. d4+3]) loaded together: up to 8 flash splits and 16 page slots
-    constexpr int kMax = 8 + kMaxTG;
+    // every state's (m, l, o[d4 .. d4+3]) loaded together: the flash splits, then the
+    // page slots
+    constexpr int kMax = KM;
     float mm[kMax], ll[kMax];
     float4 oo[kMax];
 #pragma unroll
     for (int k = 0; k < kMax; ++k) {
         mm[k] = -INFINITY;
         const float* pp = nullptr;
-        if (k < 8) {
-            if (k < A.nsplit) pp = A.part_fl + k * A.split_stride + rh * kPartStride;
-        } else if (k - 8 < A.TG) {
-            pp = A.part_pg + (rh * A.TG + (k - 8)) * kPartStride;  // empty slots hold m = -inf
+        if (k < A.nsplit) {
+            pp = A.part_fl + k * A.split_stride + rh * kPartStride;
+        } else if (k - A.nsplit < A.TG) {
+            pp = A.part_pg + (rh * A.TG + (k - A.nsplit)) * kPartStride;  // empty slots hold m = -inf
         }
         if (pp) {
             const float2 ml = *reinterpret_cast<const float2*>(pp + kD);
@@ -1803,8 +1808,16 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
         hipLaunchKernelGGL((prefill_group_kernel<HG, false>), ggrid, dim3(kGroupThreads), 0, st, P);
     trace_point(5, st);
     const int64_t nrh = (int64_t)batch * S.nq * S.Hq;
-    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((nrh + kThreads / 32 - 1) / (kThreads / 32))),
-                       dim3(kThreads), 0, st, P, nrh);
+    const dim3 cgrid((unsigned)((nrh + kThreads / 32 - 1) / (kThreads / 32)));
+    const int nstates = P.nsplit + P.TG;
+    if (nstates <= 9)
+        hipLaunchKernelGGL((prefill_combine_kernel<9>), cgrid, dim3(kThreads), 0, st, P, nrh);
+    else if (nstates <= 12)
+        hipLaunchKernelGGL((prefill_combine_kernel<12>), cgrid, dim3(kThreads), 0, st, P, nrh);
+    else if (nstates <= 16)
+        hipLaunchKernelGGL((prefill_combine_kernel<16>), cgrid, dim3(kThreads), 0, st, P, nrh);
+    else
+        hipLaunchKernelGGL((prefill_combine_kernel<8 + kMaxTG>), cgrid, dim3(kThreads), 0, st, P, nrh);
     trace_point(6, st);
     return LOD_OK;
 }
