@@ -1324,15 +1324,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pages_kernel(PagesArgs A) {
 // not.  So each group's rows are read once per workgroup, not once per pair, and most
 // workgroups need one key tile.  S^T = K Q^T and O^T = V^T P^T run as in the flash kernel
 // (keys as MFMA rows, P from registers as bf16 hi + lo); each column's online softmax is
-// written as the pair's partial state.
+// written as the pair's partial state.  Four waves of one 16-column block each: 121
+// registers, four waves per SIMD (two waves of two blocks each needed 222 registers and
+// ran two per SIMD, 20% slower).
 // Which runs share a workgroup depends on the order in which the bucket step filled the
 // list, so a pair's result must not depend on its neighbours: a run's rows start at a
 // 32-row boundary of a tile (the same positions of every 32-key MFMA sum wherever the run
 // lands), a run never straddles tiles unless it has more than 64 rows (then it starts a
 // tile of its own), and the rows of other runs enter only as exact zeros.
-constexpr int kGroupThreads = 128;                  // two waves
+constexpr int kGroupThreads = 256;                  // four waves, one 16-column block each
 constexpr int kGroupWaves = kGroupThreads / 64;
-constexpr int kGroupPairs = 32 * kGroupWaves;       // pairs (MFMA columns) per workgroup
+constexpr int kGroupPairs = 16 * kGroupWaves;       // pairs (MFMA columns) per workgroup
 constexpr int kGroupRuns = 4;                       // runs sharing a key list (meta rows in LDS)
 constexpr int kSumRow = 0x100;                      // flag of a summary row in GroupSmem::rpage
 
@@ -1354,7 +1356,7 @@ struct GroupSmem {
 };
 
 template <int HG, bool PAGED>
-__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(kGroupThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void prefill_group_kernel(PagesArgs A) {
     __shared__ GroupSmem s;
     const int unit_local = blockIdx.y;
@@ -1423,28 +1425,20 @@ void prefill_group_kernel(PagesArgs A) {
         s.open[tid] = op;
     }
     load_metas(0, min(nseg, kGroupRuns));
-    bf16x8_t qb[2][4];
-    bool cvalid[2];
-    int64_t crh[2];
-    int ct[2];
+    // this lane's column: pair 16 w + li
+    const int ncol = 16 * w + li;
+    const bool cvalid = ncol < np;
+    int ct;
+    const int64_t crh = pair_rh(s.ent[cvalid ? ncol : 0].x, ct);
+    bf16x8_t qb[4];
+    {
+        const bf16_t* qr = A.q + crh * kD;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int n = 16 * (2 * w + cb) + li;
-        cvalid[cb] = n < np;
-        crh[cb] = pair_rh(s.ent[cvalid[cb] ? n : 0].x, ct[cb]);
-        const bf16_t* qr = A.q + crh[cb] * kD;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qb[cb][kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
+        for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
     }
     __syncthreads();
-    int crun[2];
-    uint32_t copen[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int n = 16 * (2 * w + cb) + li;
-        crun[cb] = cvalid[cb] ? s.runof[n] : -1;
-        copen[cb] = cvalid[cb] ? s.open[n] : 0u;
-    }
+    const int crun = cvalid ? s.runof[ncol] : -1;
+    const uint32_t copen = cvalid ? s.open[ncol] : 0u;
 
     for (int sb = 0; sb < nseg; sb += kGroupRuns) {  // batches of runs
         const int nrun = min(kGroupRuns, nseg - sb);
@@ -1483,20 +1477,14 @@ void prefill_group_kernel(PagesArgs A) {
         }
         __syncthreads();
         const int ntile = s.ntile;
-        f32x4_t O[2][8];
-        float m_run[2], l_run[2];
+        f32x4_t O[8];
+        float m_run = -INFINITY, l_run = 0.0f;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            m_run[cb] = -INFINITY;
-            l_run[cb] = 0.0f;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) O[cb][db] = {0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        // columns of this batch (run sb + k is k here); a wave with none only helps load
-        int cbat[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) cbat[cb] = (crun[cb] >= sb && crun[cb] < sb + nrun) ? crun[cb] - sb : -1;
-        const bool active = __any(cbat[0] >= 0 || cbat[1] >= 0);
+        for (int db = 0; db < 8; ++db) O[db] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // the column's run in this batch (run sb + k is k here); a wave with none only
+        // helps load
+        const int cbat = (crun >= sb && crun < sb + nrun) ? crun - sb : -1;
+        const bool active = __any(cbat >= 0);
         for (int kt = 0; kt < ntile; ++kt) {
             // the tile's rows: run k's members (cache position, page) then its summaries
             // (unit page slot, page | flag); -1: no row
@@ -1567,27 +1555,24 @@ void prefill_group_kernel(PagesArgs A) {
             __syncthreads();
             if (active) {
                 const int nkb = (nk + 15) / 16;
-                f32x4_t S[4][2];
+                f32x4_t S[4];
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
-                    S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    S[kb] = {0.0f, 0.0f, 0.0f, 0.0f};
                     if (kb < nkb) {
 #pragma unroll
                         for (int kk = 0; kk < 4; ++kk) {
                             const int row = 16 * kb + li;
                             const int chunk = (4 * kk + g) ^ fswz_k(row);
                             const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&s.kt[row][8 * chunk]);
-                            S[kb][0] = mfma16(av, qb[0][kk], S[kb][0]);
-                            S[kb][1] = mfma16(av, qb[1][kk], S[kb][1]);
+                            S[kb] = mfma16(av, qb[kk], S[kb]);
                         }
                     }
                 }
                 // logits (log2 units) of the column's own run under its page mask, online
                 // softmax (a column's keys live in lanes l, l^16, l^32, l^48)
-                float P[4][2][4];
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
+                float P[4][4];
+                {
                     float mt = -INFINITY;
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb)
@@ -1595,63 +1580,58 @@ void prefill_group_kernel(PagesArgs A) {
                         for (int r = 0; r < 4; ++r) {
                             const int key = 16 * kb + 4 * g + r;
                             const int pg = s.rpage[key];
-                            const bool mine = pg >= 0 && (pg >> 16) == cbat[cb];
-                            const bool opened = ((copen[cb] >> (pg & 31)) & 1u) != 0;
+                            const bool mine = pg >= 0 && (pg >> 16) == cbat;
+                            const bool opened = ((copen >> (pg & 31)) & 1u) != 0;
                             const bool ok = mine && ((pg & kSumRow) ? !opened : opened);
-                            const float lam = ok ? __builtin_fmaf(sc2, S[kb][cb][r], s.bias[key]) : -INFINITY;
-                            P[kb][cb][r] = lam;
+                            const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], s.bias[key]) : -INFINITY;
+                            P[kb][r] = lam;
                             mt = fmaxf(mt, lam);
                         }
                     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
                     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                    const float mn = fmaxf(m_run[cb], mt);
-                    const float al = m_run[cb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[cb] - mn);
+                    const float mn = fmaxf(m_run, mt);
+                    const float al = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
                     const float ms = mn == -INFINITY ? 0.0f : mn;
                     float ls = 0.0f;
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float pw = __builtin_amdgcn_exp2f(P[kb][cb][r] - ms);  // exp2(-inf) = 0
-                            P[kb][cb][r] = pw;
+                            const float pw = __builtin_amdgcn_exp2f(P[kb][r] - ms);  // exp2(-inf) = 0
+                            P[kb][r] = pw;
                             ls += pw;
                         }
-                    l_run[cb] = __builtin_fmaf(l_run[cb], al, ls);
-                    m_run[cb] = mn;
+                    l_run = __builtin_fmaf(l_run, al, ls);
+                    m_run = mn;
                     if (__any(al != 1.0f)) {
 #pragma unroll
-                        for (int db = 0; db < 8; ++db) O[cb][db] *= al;
+                        for (int db = 0; db < 8; ++db) O[db] *= al;
                     }
                 }
                 // O^T += V^T P^T over the tile's 32-key steps (P as bf16 hi + lo)
 #pragma unroll
                 for (int sp = 0; sp < 2; ++sp) {
                     if (32 * sp >= nk) break;
-                    bf16x8_t ph[2], pl[2];
+                    bf16x8_t ph, pl;
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                        for (int jj = 0; jj < 8; jj += 2) {
-                            const ff32x2_t xv = {P[2 * sp + jj / 4][cb][jj % 4], P[2 * sp + jj / 4][cb][jj % 4 + 1]};
-                            const fbf16x2_t h = __builtin_convertvector(xv, fbf16x2_t);
-                            const ff32x2_t rv = xv - __builtin_convertvector(h, ff32x2_t);
-                            const fbf16x2_t lo = __builtin_convertvector(rv, fbf16x2_t);
-                            ph[cb][jj] = h[0];
-                            ph[cb][jj + 1] = h[1];
-                            pl[cb][jj] = lo[0];
-                            pl[cb][jj + 1] = lo[1];
-                        }
+                    for (int jj = 0; jj < 8; jj += 2) {
+                        const ff32x2_t xv = {P[2 * sp + jj / 4][jj % 4], P[2 * sp + jj / 4][jj % 4 + 1]};
+                        const fbf16x2_t h = __builtin_convertvector(xv, fbf16x2_t);
+                        const ff32x2_t rv = xv - __builtin_convertvector(h, ff32x2_t);
+                        const fbf16x2_t lo = __builtin_convertvector(rv, fbf16x2_t);
+                        ph[jj] = h[0];
+                        ph[jj + 1] = h[1];
+                        pl[jj] = lo[0];
+                        pl[jj + 1] = lo[1];
+                    }
 #pragma unroll
                     for (int db = 0; db < 8; ++db) {
                         const fs16x4_t v0 = flash_vt_read(s.vt, 32 * sp + 4 * g, 16 * db, li);
                         const fs16x4_t v1 = flash_vt_read(s.vt, 32 * sp + 16 + 4 * g, 16 * db, li);
                         const fs16x4_t both[2] = {v0, v1};
                         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb) {
-                            O[cb][db] = mfma16(av, ph[cb], O[cb][db]);
-                            O[cb][db] = mfma16(av, pl[cb], O[cb][db]);
-                        }
+                        O[db] = mfma16(av, ph, O[db]);
+                        O[db] = mfma16(av, pl, O[db]);
                     }
                 }
             }
@@ -1659,20 +1639,18 @@ void prefill_group_kernel(PagesArgs A) {
         }
         // the batch's columns: partial states (o, m in natural units, l)
         if (active) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                float lt = l_run[cb];
-                lt += __shfl_xor(lt, 16, 64);
-                lt += __shfl_xor(lt, 32, 64);
-                if (cbat[cb] < 0) continue;
-                float* dst = A.part_pg + (crh[cb] * A.TG + ct[cb]) * kPartStride;
+            float lt = l_run;
+            lt += __shfl_xor(lt, 16, 64);
+            lt += __shfl_xor(lt, 32, 64);
+            if (cbat >= 0) {
+                float* dst = A.part_pg + (crh * A.TG + ct) * kPartStride;
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
-                    const f32x4_t o = O[cb][db];
+                    const f32x4_t o = O[db];
                     *reinterpret_cast<float4*>(dst + 16 * db + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
                 }
                 if (g == 0) {
-                    dst[kD] = m_run[cb] == -INFINITY ? -INFINITY : m_run[cb] * kFlashLn2;
+                    dst[kD] = m_run == -INFINITY ? -INFINITY : m_run * kFlashLn2;
                     dst[kD + 1] = lt;
                 }
             }
