@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--video-calls", type=int, default=20)
     ap.add_argument("--no-small", action="store_true",
                     help="skip the 4K fp32 and 32K batch-4 decode cases and the 32K prefill")
+    ap.add_argument("--prefill-shapes", action="store_true",
+                    help="with --only-prefill: also the 2048-token steps and the whole-prompt prefill")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run the chunked 128K prefill only and print its JSON object (for profiling)")
     args = ap.parse_args()
@@ -241,7 +243,7 @@ def main():
         cfg = lod.Config(n_q_heads=64, n_kv_heads=8, groups=8, top_groups=8, top_pages=2, window=512,
                          n_sink=4, dtype=torch.bfloat16)
         pr = bench_prefill(torch, lod, synth, cfg, hip, torch.cuda.current_stream().cuda_stream,
-                           args.prefill_ctx, args.seed, dense=False, cpu=False, one_call=False)
+                           args.prefill_ctx, args.seed, dense=False, cpu=False, one_call=args.prefill_shapes)
         print(json.dumps({"prefill": pr}), flush=True)
         return
     B, T, L = args.batch, args.ctx, args.layers
@@ -757,6 +759,9 @@ def bench_prefill(torch, lod, synth, cfg, hip, stream, T, seed, dense=True, cpu=
         hip.destroy([d0, d1])
         est_ms = sample_ms * bins / rows
         dflops = sum(4 * 128 * 64 * sum(range(s + 1, s + rows + 1)) for s in starts)
+        for rep_ in (stepped, whole):
+            if rep_ is not None:
+                rep_["lod_speedup_vs_dense"] = round(est_ms / rep_["ms"], 2)
         dense_rep = {"ms_estimated": round(est_ms, 1), "sampled_ms": round(sample_ms, 2),
                      "sample": f"{nblk} blocks of {rows} rows at bin midpoints, scaled by {bins // rows}",
                      "achieved_TFLOPs": round(dflops / (sample_ms * 1e-3) / 1e12, 1),
