@@ -462,7 +462,7 @@ __device__ __forceinline__ void stage_rows_swizzled(bf16_t (*kt)[kD], const bf16
 // split's TG-th largest, never above the global one).  The select step takes the global
 // threshold from the splits' top lists and keeps the listed groups at or above it.
 template <int HG, int R>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void prefill_cand_kernel(SelArgs A) {
     __shared__ CandSmem s;
     constexpr int QT = kFlashRowHeads / HG;
@@ -515,20 +515,21 @@ void prefill_cand_kernel(SelArgs A) {
     __syncthreads();
     const float qn[2] = {s.qn[16 * (2 * w) + (l & 15)], s.qn[16 * (2 * w + 1) + (l & 15)]};
 
-    // MFMA scores S^T of one staged tile for this lane's two columns
-    auto tile_scores = [&](f32x4_t (*S)[2], int buf) {
+    // MFMA scores S^T of key block kb (16 keys) of one staged tile for this lane's two
+    // columns.  LDS addresses are formed here from a lane value the compiler cannot see
+    // through, so none is hoisted into a register of its own (key row 16 kb + l % 16
+    // holds chunk 4 kk + l / 16 at (4 kk + l / 16) ^ (l % 16)).
+    auto block_scores = [&](f32x4_t* S, int buf, int kb) {
+        int lo_ = l & 15;
+        asm volatile("" : "+v"(lo_));
+        const bf16_t* ktb = &s.kt[buf][0][0] + lo_ * kD + 16 * kb * kD;
+        S[0] = {0.0f, 0.0f, 0.0f, 0.0f};
+        S[1] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            S[kb][0] = {0.0f, 0.0f, 0.0f, 0.0f};
-            S[kb][1] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int row = 16 * kb + (l & 15);
-                const int chunk = (4 * kk + (l >> 4)) ^ (row & 15);
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&s.kt[buf][row][8 * chunk]);
-                S[kb][0] = mfma16(a, qb[0][kk], S[kb][0]);
-                S[kb][1] = mfma16(a, qb[1][kk], S[kb][1]);
-            }
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktb + 8 * ((4 * kk + (l >> 4)) ^ lo_));
+            S[0] = mfma16(a, qb[0][kk], S[0]);
+            S[1] = mfma16(a, qb[1][kk], S[1]);
         }
     };
     // This split's centroid tiles [t0, t1) of 64 groups stream through two LDS buffers:
@@ -557,16 +558,21 @@ void prefill_cand_kernel(SelArgs A) {
         }
         lds_barrier();
     };
-    // sweep over the split's tiles; body(t, buf, nk, S) sees the MFMA scores
+    // sweep over the split's tiles; body(t, buf, nk, kb, S) sees the MFMA scores of key
+    // block kb (one block at a time keeps 8 registers of scores live instead of 32)
     auto sweep = [&](auto&& body) {
         if (t0 < t1) issue(t0);
         for (int t = t0; t < t1; ++t) {
             if (t + 1 < t1) issue(t + 1);
             await_tile(t);
             const int buf = (t - t0) & 1;
-            f32x4_t S[4][2];
-            tile_scores(S, buf);
-            body(t, buf, min(kFlashKeys, ng - t * kFlashKeys), S);
+            const int nk = min(kFlashKeys, ng - t * kFlashKeys);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                f32x4_t S[2];
+                block_scores(S, buf, kb);
+                body(t, buf, nk, kb, S);
+            }
             lds_barrier();  // the buffer is free for tile t + 2
         }
     };
@@ -578,9 +584,7 @@ void prefill_cand_kernel(SelArgs A) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < R; ++e) lst[cb][e] = -INFINITY;
-    sweep([&](int, int buf, int nk, f32x4_t (*S)[2]) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+    sweep([&](int, int buf, int nk, int kb, f32x4_t* S) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = 16 * kb + 4 * (l >> 4) + r;
@@ -588,7 +592,7 @@ void prefill_cand_kernel(SelArgs A) {
                 const float gn = s.gkn_t[buf][key];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    float x = valid ? S[kb][cb][r] - kErrC * qn[cb] * gn : -INFINITY;
+                    float x = valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY;
 #pragma unroll
                     for (int e = 0; e < R; ++e) {
                         const float hi = fmaxf(lst[cb][e], x), lo = fminf(lst[cb][e], x);
@@ -635,35 +639,33 @@ void prefill_cand_kernel(SelArgs A) {
     // pass B: this split's candidates S + E >= T
     const float T2[2] = {s.T[16 * (2 * w) + (l & 15)], s.T[16 * (2 * w + 1) + (l & 15)]};
     const int64_t lat[2] = {list_at(16 * (2 * w) + (l & 15)), list_at(16 * (2 * w + 1) + (l & 15))};
-    sweep([&](int t, int buf, int nk, f32x4_t (*S)[2]) {
+    sweep([&](int t, int buf, int nk, int kb, f32x4_t* S) {
         const int g0 = t * kFlashKeys;
-        // this lane's candidates of the tile as bit masks (bit 4 kb + r)
+        // this lane's candidates of key block kb as bit masks (bit r)
         uint32_t m[2] = {0u, 0u};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int r = 0; r < 4; ++r) {
+            const int key = 16 * kb + 4 * (l >> 4) + r;
+            const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
+            const float gn = s.gkn_t[buf][key];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = 16 * kb + 4 * (l >> 4) + r;
-                const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
-                const float gn = s.gkn_t[buf][key];
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const float ub = S[kb][cb][r] + kErrC * qn[cb] * gn;
-                    m[cb] |= (valid && ub >= T2[cb]) ? (1u << (4 * kb + r)) : 0u;
-                }
+            for (int cb = 0; cb < 2; ++cb) {
+                const float ub = S[cb][r] + kErrC * qn[cb] * gn;
+                m[cb] |= (valid && ub >= T2[cb]) ? (1u << r) : 0u;
             }
-        // one LDS atomic per lane and column, then the entries
+        }
+        // one LDS atomic per lane, column and key block with candidates, then the entries
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             if (m[cb] == 0u) continue;
             const int n = 16 * (2 * w + cb) + (l & 15);
             int at = atomicAdd(&s.cnt[n], __popc(m[cb]));
 #pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                if ((m[cb] >> b) & 1u) {
+            for (int r = 0; r < 4; ++r) {
+                if ((m[cb] >> r) & 1u) {
                     if (at < kSplitCap && lat[cb] >= 0) {
-                        const int key = 16 * (b >> 2) + 4 * (l >> 4) + (b & 3);
-                        const float ub = S[b >> 2][cb][b & 3] + kErrC * qn[cb] * s.gkn_t[buf][key];
+                        const int key = 16 * kb + 4 * (l >> 4) + r;
+                        const float ub = S[cb][r] + kErrC * qn[cb] * s.gkn_t[buf][key];
                         A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ub));
                     }
                     ++at;
