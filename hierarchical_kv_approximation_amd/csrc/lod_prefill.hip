@@ -420,21 +420,28 @@ struct CandSmem {
 };
 
 // Canonical ranking chain q . kbar (fp32 fma in index order) for bf16 rows.
+// (Loaded 32 elements at a time, with a compiler barrier between the pieces: loading
+// both rows whole kept 128 registers live and held the select kernel at two waves per
+// SIMD.  The chain's order, and so its result, is unchanged.)
 __device__ __forceinline__ float canonical_dot_bf16(const bf16_t* q, const bf16_t* k) {
-    uint4 qu[16], ku[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        qu[c] = *reinterpret_cast<const uint4*>(q + 8 * c);
-        ku[c] = *reinterpret_cast<const uint4*>(k + 8 * c);
-    }
     float acc = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        float qf[8], kf[8];
-        Elt<bf16_t>::unpack(qu[c], qf);
-        Elt<bf16_t>::unpack(ku[c], kf);
+    for (int p4 = 0; p4 < 4; ++p4) {
+        uint4 qu[4], ku[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[e], kf[e], acc);
+        for (int c = 0; c < 4; ++c) {
+            qu[c] = *reinterpret_cast<const uint4*>(q + 32 * p4 + 8 * c);
+            ku[c] = *reinterpret_cast<const uint4*>(k + 32 * p4 + 8 * c);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float qf[8], kf[8];
+            Elt<bf16_t>::unpack(qu[c], qf);
+            Elt<bf16_t>::unpack(ku[c], kf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[e], kf[e], acc);
+        }
+        asm volatile("" ::: "memory");
     }
     return acc;
 }
@@ -700,7 +707,7 @@ struct SelSmem {
 // -- from the candidate lists of the sweeps: global threshold, candidates, exact top TG
 // under the canonical chain, then page ranking of every opened group.
 template <int HG, int NC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void prefill_select_kernel(SelArgs A) {
     __shared__ SelSmem<NC> s;
     constexpr int QT = kFlashRowHeads / HG;
