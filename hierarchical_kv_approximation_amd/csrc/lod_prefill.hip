@@ -222,6 +222,7 @@ void prefill_flash_kernel(FlashArgs A) {
         tile_of(t0, coarse, k0, nk);
         flash_issue<HG, PAGED>(s, A, 0, coarse, k0, nk, coarse ? gk : kc, coarse ? gv : vc, gln, bs);
     }
+    int eptr = 0;  // next opened group of this lane's column not yet below the tiles
     for (int t = t0; t < t1; ++t) {
         const int buf = (t - t0) & 1;
         __builtin_amdgcn_s_waitcnt(0);
@@ -232,13 +233,16 @@ void prefill_flash_kernel(FlashArgs A) {
             flash_issue<HG, PAGED>(s, A, buf ^ 1, coarse, k0, nk, coarse ? gk : kc, coarse ? gv : vc, gln, bs);
         }
         tile_of(t, coarse, k0, nk);
-        // excluded keys of this lane's column: its opened groups inside a coarse tile
+        // excluded keys of this lane's column: its opened groups inside a coarse tile.  The
+        // column's list is ascending (-1 after the last) and coarse tiles come in key
+        // order, so a pointer that only moves forward visits each opened group once.
         uint64_t ex = 0;
         if (coarse) {
             const int n = 16 * w + li;
-            for (int u = 0; u < A.TG; ++u) {
-                const int gg = s.sel[n][u] - k0;
-                if (gg >= 0 && gg < kFlashKeys) ex |= 1ull << gg;
+            int gsel;
+            while (eptr < A.TG && (gsel = s.sel[n][eptr]) >= 0 && gsel < k0 + kFlashKeys) {
+                if (gsel >= k0) ex |= 1ull << (gsel - k0);
+                ++eptr;
             }
         }
         // S^T = K Q^T for 4 key blocks.  LDS addresses are formed here from one lane value
