@@ -22,6 +22,7 @@ constexpr int kTile = 64;      // rows per LDS tile in the decode kernels
 constexpr int kPartStride = kD + 4;  // floats per partial softmax state: o[d], m, l, pad
 constexpr int kScanTile = 64;        // rows per tile of the bf16 decode scan
 constexpr int kScanMaxSlots = 40;    // bf16 decode scan workgroups per (sequence, KV head), at most
+constexpr int kCUs = 256;            // compute units of the gfx950 part that launch shapes are sized for
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -472,8 +472,8 @@ __device__ __forceinline__ void stage_rows_swizzled(bf16_t (*kt)[kD], const bf16
 // those, and collects the groups with S + E at or above the TG-th (a lower bound of the
 // split's TG-th largest, never above the global one).  The select step takes the global
 // threshold from the splits' top lists and keeps the listed groups at or above it.
-template <int HG, int R>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+template <int HG, int R, bool WT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WT ? 2 : 4, 8)))
 void prefill_cand_kernel(SelArgs A) {
     __shared__ CandSmem s;
     constexpr int QT = kFlashRowHeads / HG;
@@ -527,18 +527,14 @@ void prefill_cand_kernel(SelArgs A) {
     const float qn[2] = {s.qn[16 * (2 * w) + (l & 15)], s.qn[16 * (2 * w + 1) + (l & 15)]};
 
     // MFMA scores S^T of key block kb (16 keys) of one staged tile for this lane's two
-    // columns.  LDS addresses are formed here from a lane value the compiler cannot see
-    // through, so none is hoisted into a register of its own (key row 16 kb + l % 16
-    // holds chunk 4 kk + l / 16 at (4 kk + l / 16) ^ (l % 16)).
-    auto block_scores = [&](f32x4_t* S, int buf, int kb) {
-        int lo_ = l & 15;
-        asm volatile("" : "+v"(lo_));
-        const bf16_t* ktb = &s.kt[buf][0][0] + lo_ * kD + 16 * kb * kD;
+    // columns; ktb: the tile's row l % 16, lo_: l % 16 (key row 16 kb + l % 16 holds
+    // chunk 4 kk + l / 16 at (4 kk + l / 16) ^ (l % 16))
+    auto block_scores = [&](f32x4_t* S, const bf16_t* ktb, int lo_, int kb) {
         S[0] = {0.0f, 0.0f, 0.0f, 0.0f};
         S[1] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktb + 8 * ((4 * kk + (l >> 4)) ^ lo_));
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ktb + 16 * kb * kD + 8 * ((4 * kk + (l >> 4)) ^ lo_));
             S[0] = mfma16(a, qb[0][kk], S[0]);
             S[1] = mfma16(a, qb[1][kk], S[1]);
         }
@@ -570,7 +566,9 @@ void prefill_cand_kernel(SelArgs A) {
         lds_barrier();
     };
     // sweep over the split's tiles; body(t, buf, nk, kb, S) sees the MFMA scores of key
-    // block kb (one block at a time keeps 8 registers of scores live instead of 32)
+    // block kb.  WT: the scores of the whole tile first (more MFMAs in flight per wave,
+    // for launches of few waves per SIMD), else one block at a time (8 registers of
+    // scores live instead of 32: four waves per SIMD)
     auto sweep = [&](auto&& body) {
         if (t0 < t1) issue(t0);
         for (int t = t0; t < t1; ++t) {
@@ -578,11 +576,24 @@ void prefill_cand_kernel(SelArgs A) {
             await_tile(t);
             const int buf = (t - t0) & 1;
             const int nk = min(kFlashKeys, ng - t * kFlashKeys);
+            // LDS addresses formed from a lane value the compiler cannot see through, once
+            // per tile, so none is hoisted out of the loop into a register of its own
+            int lo_ = l & 15;
+            asm volatile("" : "+v"(lo_));
+            const bf16_t* ktb = &s.kt[buf][0][0] + lo_ * kD;
+            if constexpr (WT) {
+                f32x4_t S[4][2];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                f32x4_t S[2];
-                block_scores(S, buf, kb);
-                body(t, buf, nk, kb, S);
+                for (int kb = 0; kb < 4; ++kb) block_scores(S[kb], ktb, lo_, kb);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) body(t, buf, nk, kb, S[kb]);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    f32x4_t S[2];
+                    block_scores(S, ktb, lo_, kb);
+                    body(t, buf, nk, kb, S);
+                }
             }
             lds_barrier();  // the buffer is free for tile t + 2
         }
@@ -1768,16 +1779,26 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
     constexpr int QT = kFlashRowHeads / HG;
     const int ntiles = (S.nq + QT - 1) / QT;
     trace_point(0, st);
-    // lane lists of 4 (8 for more than 8 opened groups): 16 (32) values per column
-    if (S.TG <= 8)
-        hipLaunchKernelGGL((prefill_cand_kernel<HG, 4>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads),
-                           0, st, S);
-    else
-        hipLaunchKernelGGL((prefill_cand_kernel<HG, 8>), dim3(ntiles * S.nsplit * S.Hkv, 1, batch), dim3(kThreads),
-                           0, st, S);
+    // lane lists of 4 (8 for more than 8 opened groups): 16 (32) values per column;
+    // launches of fewer than four workgroups per CU score whole tiles at a time
+    const int64_t ncand = (int64_t)ntiles * S.nsplit * S.Hkv * batch;
+    const dim3 gc(ntiles * S.nsplit * S.Hkv, 1, batch);
+    if (ncand < 4 * kCUs) {
+        if (S.TG <= 8) hipLaunchKernelGGL((prefill_cand_kernel<HG, 4, true>), gc, dim3(kThreads), 0, st, S);
+        else hipLaunchKernelGGL((prefill_cand_kernel<HG, 8, true>), gc, dim3(kThreads), 0, st, S);
+    } else {
+        if (S.TG <= 8) hipLaunchKernelGGL((prefill_cand_kernel<HG, 4, false>), gc, dim3(kThreads), 0, st, S);
+        else hipLaunchKernelGGL((prefill_cand_kernel<HG, 8, false>), gc, dim3(kThreads), 0, st, S);
+    }
     trace_point(1, st);
-    hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols>), dim3(ntiles * (kFlashRowHeads / kSelCols) * S.Hkv, 1, batch),
-                       dim3(kThreads), 0, st, S);
+    // half-size column groups where full ones would leave CUs with less than two
+    // workgroups (the select steps are chains of dependent loads)
+    if ((int64_t)ntiles * (kFlashRowHeads / kSelCols) * S.Hkv * batch < 2 * kCUs)
+        hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols / 2>),
+                           dim3(ntiles * (kFlashRowHeads / (kSelCols / 2)) * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
+    else
+        hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols>), dim3(ntiles * (kFlashRowHeads / kSelCols) * S.Hkv, 1, batch),
+                           dim3(kThreads), 0, st, S);
     trace_point(2, st);
     if (F.btab)
         hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
