@@ -68,6 +68,20 @@ __device__ __forceinline__ uint64_t rank_key(float r, uint32_t id) {
     return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - id);
 }
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
+// Insert x into the descending list t[0..N), which keeps the N largest values seen (with
+// multiplicity).  The new t[e] is the median of the old t[e-1], t[e] and x (x clamped
+// into [t[e], t[e-1]]), so every entry is one independent med3 of old values.
+template <int N>
+__device__ __forceinline__ void insert_desc(float (&t)[N], float x) {
+    float prev = t[0];
+    t[0] = fmaxf(prev, x);
+#pragma unroll
+    for (int e = 1; e < N; ++e) {
+        const float cur = t[e];
+        t[e] = __builtin_amdgcn_fmed3f(prev, cur, x);
+        prev = cur;
+    }
+}
 __device__ __forceinline__ float key_score(uint64_t k) {
     uint32_t u = (uint32_t)(k >> 32);
     u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;

@@ -614,13 +614,7 @@ void prefill_cand_kernel(SelArgs A) {
                 const float gn = s.gkn_t[buf][key];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    float x = valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY;
-#pragma unroll
-                    for (int e = 0; e < R; ++e) {
-                        const float hi = fmaxf(lst[cb][e], x), lo = fminf(lst[cb][e], x);
-                        lst[cb][e] = hi;
-                        x = lo;
-                    }
+                    insert_desc(lst[cb], valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY);
                 }
             }
     });
@@ -707,12 +701,14 @@ template <int NC>
 struct SelSmem {
     float T[NC];
     int cnt[NC];
-    int32_t cg[NC][kCandCap];  // candidates: group id, upper bound of the canonical
-    float cub[NC][kCandCap];   // score (then the score itself where computed),
-    float clb[NC][kCandCap];   // lower bound, class (0 surely not opened, 1
-    uint8_t cls[NC][kCandCap]; // needs the chain, 2 surely opened)
-    float qn[NC];              // |q| per column, rounded up
-    int32_t sel[NC][kMaxTG];   // rank order
+    // per-column rows padded to an odd number of words: lanes that read one column each
+    // hit distinct LDS banks
+    int32_t cg[NC][kCandCap + 1];  // candidates: group id, upper bound of the canonical
+    float cub[NC][kCandCap + 1];   // score (then the score itself where computed),
+    float clb[NC][kCandCap + 1];   // lower bound, class (0 surely not opened, 1
+    uint8_t cls[NC][kCandCap + 4]; // needs the chain, 2 surely opened)
+    float qn[NC];                  // |q| per column, rounded up
+    int32_t sel[NC][kMaxTG + 1];   // rank order
     int nsel[NC];
     uint64_t red[4];
     int any_overflow;
@@ -768,15 +764,8 @@ void prefill_select_kernel(SelArgs A) {
                 }
 #pragma unroll
                 for (int i = 0; i < kMaxTG; ++i) {
-                    float x = i < TG ? v[i] : -INFINITY;
-                    if (x > top[kMaxTG - 1]) {
-#pragma unroll
-                        for (int e = 0; e < kMaxTG; ++e) {
-                            const float hi = fmaxf(top[e], x), lo = fminf(top[e], x);
-                            top[e] = hi;
-                            x = lo;
-                        }
-                    }
+                    const float x = i < TG ? v[i] : -INFINITY;
+                    if (x > top[kMaxTG - 1]) insert_desc(top, x);
                 }
             }
 #pragma unroll
@@ -855,19 +844,8 @@ void prefill_select_kernel(SelArgs A) {
 #pragma unroll
             for (int e = 0; e < kMaxTG; ++e) tl[e] = -INFINITY;
             for (int at = 0; at < c; ++at) {
-                float u = s.cub[n][at], v = s.clb[n][at];
-#pragma unroll
-                for (int e = 0; e <= kMaxTG; ++e) {
-                    const float hi = fmaxf(tu[e], u), lo = fminf(tu[e], u);
-                    tu[e] = hi;
-                    u = lo;
-                }
-#pragma unroll
-                for (int e = 0; e < kMaxTG; ++e) {
-                    const float hi = fmaxf(tl[e], v), lo = fminf(tl[e], v);
-                    tl[e] = hi;
-                    v = lo;
-                }
+                insert_desc(tu, s.cub[n][at]);
+                insert_desc(tl, s.clb[n][at]);
             }
             float uT = -INFINITY, uT1 = -INFINITY, lT = -INFINITY;  // TG-th, TG+1-th largest ub; TG-th lb
 #pragma unroll
@@ -1059,7 +1037,6 @@ void prefill_select_kernel(SelArgs A) {
 // (row, head, slot) with pair index (row_in_chunk * HG + head) * TG + slot.
 constexpr int kMaxBucketGroups = 16384;  // summarised groups per KV head a prefill supports
 constexpr int kBucketThreads = 1024;     // threads of a bucket workgroup
-constexpr int kBucketPer = kChunk * 8 * kMaxTG / kBucketThreads;  // pairs per bucket thread, at most
 
 struct PagesArgs {
     const bf16_t* k;
@@ -1089,9 +1066,12 @@ struct PagesArgs {
     int units_per_seq_kv;   // query chunks in the launch
 };
 
-template <int HG>
+// PER: pair slots per thread, at least kChunk * HG * TG / kBucketThreads.
+template <int HG, int PER>
 __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArgs A) {
-    __shared__ int cnt[kMaxBucketGroups];
+    // + 64 spare counters: slots with no group (or past the last pair) count into the
+    // spare of their lane, so every slot takes its atomic without a branch
+    __shared__ int cnt[kMaxBucketGroups + 64];
     __shared__ int wsum[kBucketThreads / 64];
     const int qc = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
@@ -1103,23 +1083,28 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     const int64_t unit = ((int64_t)b * A.Hkv + kvh) * A.units_per_seq_kv + qc;
     int2* list = A.plist + unit * (kChunk * HG * A.TG);
     for (int g = tid; g < ng; g += kBucketThreads) cnt[g] = 0;
+    const int spare = kMaxBucketGroups + (tid & 63);
     // the group id of every pair this thread owns (pairs tid, tid + 1024, ...), loaded
-    // together and kept for both passes
-    int gid[kBucketPer];
+    // together and kept for both passes.  Pair x = rl * HG * TG + e (e = head * TG + slot)
+    // sits at selg row r0 + rl, entry kvh * HG * TG + e; (rl, e) advances by the
+    // division of 1024 by HG * TG with one carry, so the loop divides nothing.
+    int gid[PER];
+    {
+        const int per_row = HG * A.TG, rs = A.Hq * A.TG;  // pairs of a unit row; selg row stride
+        const int de = kBucketThreads % per_row, doff = kBucketThreads / per_row * rs + de;
+        int e = tid % per_row, off = tid / per_row * rs + e;
+        const int32_t* sg = A.selg + ((int64_t)b * A.nq + r0) * rs + kvh * per_row;
 #pragma unroll
-    for (int u = 0; u < kBucketPer; ++u) {
-        const int x = tid + u * kBucketThreads;
-        if (x < npairs) {
-            const int t = x % A.TG, h = (x / A.TG) % HG, rl = x / (A.TG * HG);
-            gid[u] = A.selg[(((int64_t)b * A.nq + r0 + rl) * A.Hq + kvh * HG + h) * A.TG + t];
-        } else {
-            gid[u] = -1;
+        for (int u = 0; u < PER; ++u) {
+            gid[u] = tid + u * kBucketThreads < npairs ? sg[off] : -1;
+            off += doff;
+            e += de;
+            if (e >= per_row) { e -= per_row; off += rs - per_row; }
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kBucketPer; ++u)
-        if (gid[u] >= 0) atomicAdd(&cnt[gid[u]], 1);
+    for (int u = 0; u < PER; ++u) atomicAdd(&cnt[gid[u] >= 0 ? gid[u] : spare], 1);
     __syncthreads();
     // exclusive scan of the counts: contiguous ranges per thread, then the range sums by
     // wave prefix sums and the waves' totals
@@ -1146,9 +1131,13 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     int acc = before + incl - sum;
     for (int g = g0; g < g1; ++g) { const int v = cnt[g]; cnt[g] = acc; acc += v; }
     __syncthreads();
+    // every slot's LDS atomic first, then the stores (one wait, not one per pair)
+    int at[PER];
 #pragma unroll
-    for (int u = 0; u < kBucketPer; ++u)
-        if (gid[u] >= 0) list[atomicAdd(&cnt[gid[u]], 1)] = make_int2(tid + u * kBucketThreads, gid[u]);
+    for (int u = 0; u < PER; ++u) at[u] = atomicAdd(&cnt[gid[u] >= 0 ? gid[u] : spare], 1);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (gid[u] >= 0) list[at[u]] = make_int2(tid + u * kBucketThreads, gid[u]);
 }
 
 // ---------------------------------------------------------------------------- pages
@@ -1807,7 +1796,14 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
         hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
                            st, F);
     trace_point(3, st);
-    hipLaunchKernelGGL((prefill_bucket_kernel<HG>), dim3(nunits_q, S.Hkv, batch), dim3(kBucketThreads), 0, st, P);
+    {
+        const dim3 gb(nunits_q, S.Hkv, batch);
+        const int per = (kChunk * HG * S.TG + kBucketThreads - 1) / kBucketThreads;
+        if (per <= 4) hipLaunchKernelGGL((prefill_bucket_kernel<HG, 4>), gb, dim3(kBucketThreads), 0, st, P);
+        else if (per <= 8) hipLaunchKernelGGL((prefill_bucket_kernel<HG, 8>), gb, dim3(kBucketThreads), 0, st, P);
+        else if (per <= 16) hipLaunchKernelGGL((prefill_bucket_kernel<HG, 16>), gb, dim3(kBucketThreads), 0, st, P);
+        else hipLaunchKernelGGL((prefill_bucket_kernel<HG, 32>), gb, dim3(kBucketThreads), 0, st, P);
+    }
     trace_point(4, st);
     const int maxpairs = kChunk * HG * S.TG;
     const dim3 pgrid((maxpairs + kPairsPerWG - 1) / kPairsPerWG, nunits_q * S.Hkv * batch);
