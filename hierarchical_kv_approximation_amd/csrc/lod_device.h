@@ -70,17 +70,28 @@ __device__ __forceinline__ uint64_t rank_key(float r, uint32_t id) {
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
 // Insert x into the descending list t[0..N), which keeps the N largest values seen (with
 // multiplicity).  The new t[e] is the median of the old t[e-1], t[e] and x (x clamped
-// into [t[e], t[e-1]]), so every entry is one independent med3 of old values.
+// into [t[e], t[e-1]]), so every entry is one independent med3 of old values; the head
+// is med3(t[0], x, +inf), the larger of the two (no NaN reaches these lists).  x and the
+// +inf pass through empty asm: otherwise the compiler turns the head back into a max
+// with NaN quieting, and branches on x = -inf (an invalid element) to a copy of the list.
+// pinf: +inf, formed by the caller through empty asm (once, outside its loops).
 template <int N>
-__device__ __forceinline__ void insert_desc(float (&t)[N], float x) {
+__device__ __forceinline__ void insert_desc(float (&t)[N], float x, float pinf) {
+    asm volatile("" : "+v"(x));
     float prev = t[0];
-    t[0] = fmaxf(prev, x);
+    t[0] = __builtin_amdgcn_fmed3f(prev, x, pinf);
 #pragma unroll
     for (int e = 1; e < N; ++e) {
         const float cur = t[e];
         t[e] = __builtin_amdgcn_fmed3f(prev, cur, x);
         prev = cur;
     }
+}
+template <int N>
+__device__ __forceinline__ void insert_desc(float (&t)[N], float x) {
+    float pinf = INFINITY;
+    asm volatile("" : "+v"(pinf));
+    insert_desc(t, x, pinf);
 }
 __device__ __forceinline__ float key_score(uint64_t k) {
     uint32_t u = (uint32_t)(k >> 32);

@@ -606,15 +606,22 @@ void prefill_cand_kernel(SelArgs A) {
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int e = 0; e < R; ++e) lst[cb][e] = -INFINITY;
+    float pinf = INFINITY;  // +inf the compiler cannot see (insert_desc's head med3)
+    asm volatile("" : "+v"(pinf));
     sweep([&](int, int buf, int nk, int kb, f32x4_t* S) {
+            // ln n and norm bounds of this lane's four keys (every one of the 64 slots is
+            // staged, so the reads need no branch)
+            const int k4 = 16 * kb + 4 * (l >> 4);
+            const float4 gl4 = *reinterpret_cast<const float4*>(&s.gln_t[buf][k4]);
+            const float4 gn4 = *reinterpret_cast<const float4*>(&s.gkn_t[buf][k4]);
+            const float glr[4] = {gl4.x, gl4.y, gl4.z, gl4.w}, gnr[4] = {gn4.x, gn4.y, gn4.z, gn4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = 16 * kb + 4 * (l >> 4) + r;
-                const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
-                const float gn = s.gkn_t[buf][key];
+                const bool valid = (k4 + r < nk) & (glr[r] != -INFINITY);
+                const float gn = gnr[r];
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) {
-                    insert_desc(lst[cb], valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY);
+                    insert_desc(lst[cb], valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY, pinf);
                 }
             }
     });
@@ -659,15 +666,17 @@ void prefill_cand_kernel(SelArgs A) {
         const int g0 = t * kFlashKeys;
         // this lane's candidates of key block kb as bit masks (bit r)
         uint32_t m[2] = {0u, 0u};
+        const int k4 = 16 * kb + 4 * (l >> 4);
+        const float4 gl4 = *reinterpret_cast<const float4*>(&s.gln_t[buf][k4]);
+        const float4 gn4 = *reinterpret_cast<const float4*>(&s.gkn_t[buf][k4]);
+        const float glr[4] = {gl4.x, gl4.y, gl4.z, gl4.w}, gnr[4] = {gn4.x, gn4.y, gn4.z, gn4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int key = 16 * kb + 4 * (l >> 4) + r;
-            const bool valid = key < nk && s.gln_t[buf][key] != -INFINITY;
-            const float gn = s.gkn_t[buf][key];
+            const bool valid = (k4 + r < nk) & (glr[r] != -INFINITY);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const float ub = S[cb][r] + kErrC * qn[cb] * gn;
-                m[cb] |= (valid && ub >= T2[cb]) ? (1u << r) : 0u;
+                const float ub = S[cb][r] + kErrC * qn[cb] * gnr[r];
+                m[cb] |= (valid & (ub >= T2[cb])) ? (1u << r) : 0u;
             }
         }
         // one LDS atomic per lane, column and key block with candidates, then the entries
@@ -680,9 +689,8 @@ void prefill_cand_kernel(SelArgs A) {
             for (int r = 0; r < 4; ++r) {
                 if ((m[cb] >> r) & 1u) {
                     if (at < kSplitCap && lat[cb] >= 0) {
-                        const int key = 16 * kb + 4 * (l >> 4) + r;
-                        const float ub = S[cb][r] + kErrC * qn[cb] * s.gkn_t[buf][key];
-                        A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + key), __float_as_uint(ub));
+                        const float ub = S[cb][r] + kErrC * qn[cb] * gnr[r];
+                        A.lent[lat[cb] * kSplitCap + at] = make_uint2((uint32_t)(g0 + k4 + r), __float_as_uint(ub));
                     }
                     ++at;
                 }
