@@ -1692,25 +1692,21 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PagesArgs A, 
     const int d4 = 4 * (threadIdx.x & 31);
     if (rh >= nrh) return;
     // every state's (m, l, o[d4 .. d4+3]) loaded together: the flash splits, then the
-    // page slots
+    // page slots.  Slots past the last state load state 0 again and are dropped after the
+    // loads (a load behind a branch would be waited for before the next one issues).
     constexpr int kMax = KM;
+    const int nst = A.nsplit + A.TG;
     float mm[kMax], ll[kMax];
     float4 oo[kMax];
 #pragma unroll
     for (int k = 0; k < kMax; ++k) {
-        mm[k] = -INFINITY;
-        const float* pp = nullptr;
-        if (k < A.nsplit) {
-            pp = A.part_fl + k * A.split_stride + rh * kPartStride;
-        } else if (k - A.nsplit < A.TG) {
-            pp = A.part_pg + (rh * A.TG + (k - A.nsplit)) * kPartStride;  // empty slots hold m = -inf
-        }
-        if (pp) {
-            const float2 ml = *reinterpret_cast<const float2*>(pp + kD);
-            mm[k] = ml.x;
-            ll[k] = ml.y;
-            oo[k] = *reinterpret_cast<const float4*>(pp + d4);
-        }
+        const float* pp = k < A.nsplit ? A.part_fl + k * A.split_stride + rh * kPartStride
+                                       : A.part_pg + (rh * A.TG + (k - A.nsplit)) * kPartStride;  // empty slots hold m = -inf
+        if (k >= nst) pp = A.part_fl + rh * kPartStride;
+        const float2 ml = *reinterpret_cast<const float2*>(pp + kD);
+        mm[k] = k < nst ? ml.x : -INFINITY;
+        ll[k] = ml.y;
+        oo[k] = *reinterpret_cast<const float4*>(pp + d4);
     }
     float M = -INFINITY;
 #pragma unroll
