@@ -1,6 +1,5 @@
-"""The entry points under HIP graph capture: the library enqueues kernels and events only
-(no memsets, copies, allocations or host syncs), and the bf16 prefill forks its flash
-kernel onto a second stream and joins it back with events, which capture follows.  Each
+"""The entry points under HIP graph capture: the library enqueues kernels only, all on the
+caller's stream (no memsets, copies, allocations, host syncs or streams of its own).  Each
 graph is replayed three times with the program's own eager work and synchronizations
 between the replays, and every replay must give bit for bit what the eager call gave:
 no kernel's result depends on the order in which its workgroups run or take list slots."""
@@ -62,7 +61,7 @@ def test_decode_and_prefill_graph_replays_equal_eager():
     ref = lod.attend_decode(cfg, index, K, V, q, seq, T, ws=ws, out=out).clone()
     g = _capture(lambda: lod.attend_decode(cfg, index, K, V, q, seq, T, ws=ws, out=out))
     _replays_match(g, [out], [ref])
-    # bf16 prefill of two 2048-row batches (the flash kernel on the second stream)
+    # bf16 prefill of two 2048-row batches
     nq, q0 = 4096, 4096
     qp = synth.queries(B, 16, cen, seed=73, n_rows=nq)
     wsp = torch.empty(lod.prefill_ws_bytes(cfg, B, nq, q0 + nq), dtype=torch.uint8, device=dev)
