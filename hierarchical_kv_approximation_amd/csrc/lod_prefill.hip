@@ -1362,8 +1362,8 @@ constexpr int kSumRow = 0x100;                      // flag of a summary row in 
 struct GroupSmem {
     alignas(16) bf16_t kt[kFlashKeys][kD];  // key tile
     alignas(16) bf16_t vt[kFlashKeys][kD];
-    float bias[kFlashKeys];                 // log2 units; -inf: no row
-    int rpage[kFlashKeys];                  // run << 16 | page of the row in its group (| kSumRow); -1: none
+    alignas(16) float bias[kFlashKeys];     // log2 units; -inf: no row
+    alignas(16) int rpage[kFlashKeys];      // run << 16 | page of the row in its group (| kSumRow); -1: none
     int rsrc[kFlashKeys];                   // member: cache position; summary: unit page slot
     alignas(16) int16_t meta[kGroupRuns][kPagesMeta];  // meta rows of the batch's runs
     int2 ent[kGroupPairs];                  // (pair index, group) of the workgroup's pairs
@@ -1596,18 +1596,25 @@ void prefill_group_kernel(PagesArgs A) {
                 {
                     float mt = -INFINITY;
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
+                    for (int kb = 0; kb < 4; ++kb) {
+                        // a lane's four keys' tags and biases in one 16-byte read each (every
+                        // slot written) and a branch-free mask
+                        const int k4 = 16 * kb + 4 * g;
+                        const int4 pg4 = *reinterpret_cast<const int4*>(&s.rpage[k4]);
+                        const float4 bi4 = *reinterpret_cast<const float4*>(&s.bias[k4]);
+                        const int pgr[4] = {pg4.x, pg4.y, pg4.z, pg4.w};
+                        const float bir[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const int key = 16 * kb + 4 * g + r;
-                            const int pg = s.rpage[key];
-                            const bool mine = pg >= 0 && (pg >> 16) == cbat;
+                            const int pg = pgr[r];
+                            const bool mine = (pg >= 0) & ((pg >> 16) == cbat);
                             const bool opened = ((copen >> (pg & 31)) & 1u) != 0;
-                            const bool ok = mine && ((pg & kSumRow) ? !opened : opened);
-                            const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], s.bias[key]) : -INFINITY;
+                            const bool ok = mine & (((pg & kSumRow) != 0) != opened);
+                            const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], bir[r]) : -INFINITY;
                             P[kb][r] = lam;
                             mt = fmaxf(mt, lam);
                         }
+                    }
                     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
                     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
                     const float mn = fmaxf(m_run, mt);
