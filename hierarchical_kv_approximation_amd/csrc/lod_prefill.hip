@@ -272,8 +272,12 @@ void prefill_flash_kernel(FlashArgs A) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = 16 * kb + 4 * g + r;
-                const bool ok = s.kpos[buf][key] <= prow && !((ex >> key) & 1ull);
-                const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], s.bias[buf][key]) : -INFINITY;
+                // the bias is read whatever the mask says (through empty asm, so the read
+                // is not sunk into the mask's branch, where each one was waited for alone)
+                float bi = s.bias[buf][key];
+                asm volatile("" : "+v"(bi));
+                const bool ok = (s.kpos[buf][key] <= prow) & !((ex >> key) & 1ull);
+                const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], bi) : -INFINITY;
                 P[kb][r] = lam;
                 mt = fmaxf(mt, lam);
             }
