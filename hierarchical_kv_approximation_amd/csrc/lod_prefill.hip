@@ -1084,6 +1084,11 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     // + 64 spare counters: slots with no group (or past the last pair) count into the
     // spare of their lane, so every slot takes its atomic without a branch
     __shared__ int cnt[kMaxBucketGroups + 64];
+    // up to 16 slots per thread (16384 pairs): the sorted list is assembled in LDS (pair
+    // index and group in 14 bits each) and written out in order, so the global stores are
+    // coalesced instead of scattered one pair at a time
+    constexpr bool kStage = PER <= 16;
+    __shared__ uint32_t stage[kStage ? kBucketThreads * 16 : 1];
     __shared__ int wsum[kBucketThreads / 64];
     const int qc = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
@@ -1147,9 +1152,20 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     int at[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) at[u] = atomicAdd(&cnt[gid[u] >= 0 ? gid[u] : spare], 1);
+    if constexpr (kStage) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-        if (gid[u] >= 0) list[at[u]] = make_int2(tid + u * kBucketThreads, gid[u]);
+        for (int u = 0; u < PER; ++u)
+            if (gid[u] >= 0) stage[at[u]] = (uint32_t)(tid + u * kBucketThreads) | ((uint32_t)gid[u] << 14);
+        __syncthreads();
+        for (int x = tid; x < total; x += kBucketThreads) {
+            const uint32_t v = stage[x];
+            list[x] = make_int2((int)(v & 0x3fffu), (int)(v >> 14));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (gid[u] >= 0) list[at[u]] = make_int2(tid + u * kBucketThreads, gid[u]);
+    }
 }
 
 // ---------------------------------------------------------------------------- pages
