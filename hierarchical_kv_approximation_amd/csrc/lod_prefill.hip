@@ -102,14 +102,22 @@ template <int HG, bool PAGED>
 __device__ __forceinline__ void flash_issue(FlashSmem<HG>& s, const FlashArgs& A, int buf, int coarse, int k0, int nk,
                                             const bf16_t* kb, const bf16_t* vb, const float* gln, int bs) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+    // every row's offset first (a paged view reads its block table), then the loads: a
+    // load whose address waits on a block-table read would wait for the rows before it
+    constexpr int kSteps = kFlashKeys / 4 / kFlashWaves;
+    int64_t off[kSteps];
 #pragma unroll
-    for (int ii = 0; ii < kFlashKeys / 4 / kFlashWaves; ++ii) {
+    for (int ii = 0; ii < kSteps; ++ii) {
+        const int row = 4 * (w + kFlashWaves * ii) + g;
+        const int rr = row < nk ? row : nk - 1;
+        off[ii] = coarse ? (int64_t)(k0 + rr) * kD : kv_pos<PAGED>(A, bs, k0 + rr);
+    }
+#pragma unroll
+    for (int ii = 0; ii < kSteps; ++ii) {
         const int i = w + kFlashWaves * ii;
         const int row = 4 * i + g;
-        const int rr = row < nk ? row : nk - 1;
-        const int64_t off = coarse ? (int64_t)(k0 + rr) * kD : kv_pos<PAGED>(A, bs, k0 + rr);
-        __builtin_amdgcn_global_load_lds(kb + off + 8 * (li ^ fswz_k(row)), &s.kt[buf][4 * i][0], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + off + 8 * (li ^ fswz_v(row)), &s.vt[buf][4 * i][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kb + off[ii] + 8 * (li ^ fswz_k(row)), &s.kt[buf][4 * i][0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + off[ii] + 8 * (li ^ fswz_v(row)), &s.vt[buf][4 * i][0], 16, 0, 0);
     }
     if (tid < kFlashKeys) {
         s.bias[buf][tid] = tid < nk ? (coarse ? gln[k0 + tid] * kFlashLog2e : 0.0f) : -INFINITY;
@@ -1579,18 +1587,28 @@ void prefill_group_kernel(PagesArgs A) {
             const int nk = s.tilerows;
             // K and V rows straight into LDS (a wave's 64 lanes fill four rows per
             // instruction; a slot without a row loads the tile's first row, a valid
-            // address, and is masked)
+            // address, and is masked).  Every row's source is read from LDS before the
+            // first load is issued: an LDS read after a load into LDS is made to wait for
+            // it, which ran the four steps one after another.
+            constexpr int kSteps = kFlashKeys / 4 / kGroupWaves;
+            const bf16_t* ksrc[kSteps];
+            const bf16_t* vsrc[kSteps];
+            const int fr = s.firstrow;
 #pragma unroll
-            for (int ii = 0; ii < kFlashKeys / 4 / kGroupWaves; ++ii) {
-                const int i = w + kGroupWaves * ii;
-                const int row = 4 * i + g;
-                const int rr = s.rpage[row] >= 0 ? row : s.firstrow;
+            for (int ii = 0; ii < kSteps; ++ii) {
+                const int row = 4 * (w + kGroupWaves * ii) + g;
+                const int rr = s.rpage[row] >= 0 ? row : fr;
                 const int src = s.rsrc[rr];
                 const bool sum = (s.rpage[rr] & kSumRow) != 0;
-                const bf16_t* ks = sum ? pk_u + (int64_t)src * kD : kc + kv_pos<PAGED>(A, bs, src);
-                const bf16_t* vs = sum ? pv_u + (int64_t)src * kD : vc + kv_pos<PAGED>(A, bs, src);
-                __builtin_amdgcn_global_load_lds(ks + 8 * (li ^ fswz_k(row)), &s.kt[4 * i][0], 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vs + 8 * (li ^ fswz_v(row)), &s.vt[4 * i][0], 16, 0, 0);
+                ksrc[ii] = sum ? pk_u + (int64_t)src * kD : kc + kv_pos<PAGED>(A, bs, src);
+                vsrc[ii] = sum ? pv_u + (int64_t)src * kD : vc + kv_pos<PAGED>(A, bs, src);
+            }
+#pragma unroll
+            for (int ii = 0; ii < kSteps; ++ii) {
+                const int i = w + kGroupWaves * ii;
+                const int row = 4 * i + g;
+                __builtin_amdgcn_global_load_lds(ksrc[ii] + 8 * (li ^ fswz_k(row)), &s.kt[4 * i][0], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vsrc[ii] + 8 * (li ^ fswz_v(row)), &s.vt[4 * i][0], 16, 0, 0);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -1621,7 +1639,10 @@ void prefill_group_kernel(PagesArgs A) {
                         // slot written) and a branch-free mask
                         const int k4 = 16 * kb + 4 * g;
                         const int4 pg4 = *reinterpret_cast<const int4*>(&s.rpage[k4]);
-                        const float4 bi4 = *reinterpret_cast<const float4*>(&s.bias[k4]);
+                        float4 bi4 = *reinterpret_cast<const float4*>(&s.bias[k4]);
+                        // through empty asm: otherwise the compiler splits the read and sinks
+                        // each part into the mask's branch, where it is waited for alone
+                        asm volatile("" : "+v"(bi4.x), "+v"(bi4.y), "+v"(bi4.z), "+v"(bi4.w));
                         const int pgr[4] = {pg4.x, pg4.y, pg4.z, pg4.w};
                         const float bir[4] = {bi4.x, bi4.y, bi4.z, bi4.w};
 #pragma unroll
