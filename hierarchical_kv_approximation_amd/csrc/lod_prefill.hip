@@ -737,7 +737,8 @@ struct SelSmem {
 // Selection of NC (row, head) columns -- columns c0 .. c0 + NC - 1 of a 128-column tile
 // -- from the candidate lists of the sweeps: global threshold, candidates, exact top TG
 // under the canonical chain, then page ranking of every opened group.
-template <int HG, int NC>
+// TGM: opened groups per column at most (8 or kMaxTG): the sorting networks are sized by it.
+template <int HG, int NC, int TGM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void prefill_select_kernel(SelArgs A) {
     __shared__ SelSmem<NC> s;
@@ -770,26 +771,26 @@ void prefill_select_kernel(SelArgs A) {
         int over = 0;
         if ((c0 + n) / HG < nrows) {
             const int64_t c0 = col_of(n) * A.nsplit;
-            float top[kMaxTG];
+            float top[TGM];
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e) top[e] = -INFINITY;
+            for (int e = 0; e < TGM; ++e) top[e] = -INFINITY;
             for (int sp = 0; sp < A.nsplit; ++sp) {
                 over |= A.lcnt[c0 + sp] > kSplitCap;
                 const float4* src = reinterpret_cast<const float4*>(A.ltop + (c0 + sp) * kMaxTG);
-                float v[kMaxTG];
+                float v[TGM];
 #pragma unroll
-                for (int i = 0; i < kMaxTG / 4; ++i) {
+                for (int i = 0; i < TGM / 4; ++i) {
                     const float4 f = 4 * i < TG ? src[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
                     v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
                 }
 #pragma unroll
-                for (int i = 0; i < kMaxTG; ++i) {
+                for (int i = 0; i < TGM; ++i) {
                     const float x = i < TG ? v[i] : -INFINITY;
-                    if (x > top[kMaxTG - 1]) insert_desc(top, x);
+                    if (x > top[TGM - 1]) insert_desc(top, x);
                 }
             }
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e)
+            for (int e = 0; e < TGM; ++e)
                 if (e == TG - 1) T = top[e];
         }
         s.T[n] = T;
@@ -858,19 +859,19 @@ void prefill_select_kernel(SelArgs A) {
     if (tid < NC) {
         const int n = tid, c = s.cnt[n];
         if (c <= kCandCap) {
-            float tu[kMaxTG + 1], tl[kMaxTG];
+            float tu[TGM + 1], tl[TGM];
 #pragma unroll
-            for (int e = 0; e <= kMaxTG; ++e) tu[e] = -INFINITY;
+            for (int e = 0; e <= TGM; ++e) tu[e] = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e) tl[e] = -INFINITY;
+            for (int e = 0; e < TGM; ++e) tl[e] = -INFINITY;
             for (int at = 0; at < c; ++at) {
                 insert_desc(tu, s.cub[n][at]);
                 insert_desc(tl, s.clb[n][at]);
             }
             float uT = -INFINITY, uT1 = -INFINITY, lT = -INFINITY;  // TG-th, TG+1-th largest ub; TG-th lb
 #pragma unroll
-            for (int e = 0; e <= kMaxTG; ++e) {
-                if (e == TG - 1) { uT = tu[e]; lT = e < kMaxTG ? tl[e] : -INFINITY; }
+            for (int e = 0; e <= TGM; ++e) {
+                if (e == TG - 1) { uT = tu[e]; lT = e < TGM ? tl[e] : -INFINITY; }
                 if (e == TG) uT1 = tu[e];
             }
             for (int at = 0; at < c; ++at) {
@@ -895,9 +896,9 @@ void prefill_select_kernel(SelArgs A) {
             atomicOr(&s.any_overflow, 1);
             s.nsel[n] = -1;
         } else {
-            uint64_t top[kMaxTG];
+            uint64_t top[TGM];
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e) top[e] = 0;
+            for (int e = 0; e < TGM; ++e) top[e] = 0;
             for (int at = 0; at < c; ++at) {
                 // ranking key: surely opened above every score (ties to the lower id),
                 // surely not 0 (never opened), else the canonical score
@@ -906,7 +907,7 @@ void prefill_select_kernel(SelArgs A) {
                 uint64_t x = cl == 2 ? ((0xffffffffull << 32) | (0xffffffffu - id))
                                      : (cl == 0 ? 0ull : rank_key(s.cub[n][at], id));
 #pragma unroll
-                for (int e = 0; e < kMaxTG; ++e) {
+                for (int e = 0; e < TGM; ++e) {
                     const uint64_t hi = top[e] > x ? top[e] : x, lo = top[e] > x ? x : top[e];
                     top[e] = hi;
                     x = lo;
@@ -914,9 +915,9 @@ void prefill_select_kernel(SelArgs A) {
             }
             int k = 0;  // surely-out candidates (key 0) are never opened
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e) k += (e < TG && top[e] != 0) ? 1 : 0;
+            for (int e = 0; e < TGM; ++e) k += (e < TG && top[e] != 0) ? 1 : 0;
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e)
+            for (int e = 0; e < TGM; ++e)
                 if (e < TG) s.sel[n][e] = e < k ? (int)key_id(top[e]) : -1;
             s.nsel[n] = k;
         }
@@ -927,14 +928,14 @@ void prefill_select_kernel(SelArgs A) {
     if (s.any_overflow) {
         for (int n = 0; n < NC; ++n) {
             if (s.nsel[n] >= 0) continue;  // uniform: read from LDS after a barrier
-            uint64_t top[kMaxTG];
+            uint64_t top[TGM];
 #pragma unroll
-            for (int e = 0; e < kMaxTG; ++e) top[e] = 0;
+            for (int e = 0; e < TGM; ++e) top[e] = 0;
             for (int g = tid; g < ng; g += kThreads) {
                 if (gln[g] == -INFINITY) continue;
                 uint64_t x = rank_key(canonical_dot_bf16(qrow(n), gk + (int64_t)g * kD), (uint32_t)g);
 #pragma unroll
-                for (int e = 0; e < kMaxTG; ++e) {
+                for (int e = 0; e < TGM; ++e) {
                     const uint64_t hi = top[e] > x ? top[e] : x, lo = top[e] > x ? x : top[e];
                     top[e] = hi;
                     x = lo;
@@ -952,8 +953,8 @@ void prefill_select_kernel(SelArgs A) {
                 if (tid == 0) s.sel[n][round] = (int)key_id(m);
                 if (top[0] == m) {
 #pragma unroll
-                    for (int e = 0; e < kMaxTG - 1; ++e) top[e] = top[e + 1];
-                    top[kMaxTG - 1] = 0;
+                    for (int e = 0; e < TGM - 1; ++e) top[e] = top[e + 1];
+                    top[TGM - 1] = 0;
                 }
                 ++k;
             }
@@ -1834,12 +1835,18 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
     trace_point(1, st);
     // half-size column groups where full ones would leave CUs with less than two
     // workgroups (the select steps are chains of dependent loads)
-    if ((int64_t)ntiles * (kFlashRowHeads / kSelCols) * S.Hkv * batch < 2 * kCUs)
-        hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols / 2>),
-                           dim3(ntiles * (kFlashRowHeads / (kSelCols / 2)) * S.Hkv, 1, batch), dim3(kThreads), 0, st, S);
-    else
-        hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols>), dim3(ntiles * (kFlashRowHeads / kSelCols) * S.Hkv, 1, batch),
-                           dim3(kThreads), 0, st, S);
+    // (sorting networks of 8 entries when at most 8 groups are opened)
+    {
+        const bool half = (int64_t)ntiles * (kFlashRowHeads / kSelCols) * S.Hkv * batch < 2 * kCUs;
+        const dim3 gs(ntiles * (kFlashRowHeads / (half ? kSelCols / 2 : kSelCols)) * S.Hkv, 1, batch);
+        if (half) {
+            if (S.TG <= 8) hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols / 2, 8>), gs, dim3(kThreads), 0, st, S);
+            else hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols / 2, kMaxTG>), gs, dim3(kThreads), 0, st, S);
+        } else {
+            if (S.TG <= 8) hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols, 8>), gs, dim3(kThreads), 0, st, S);
+            else hipLaunchKernelGGL((prefill_select_kernel<HG, kSelCols, kMaxTG>), gs, dim3(kThreads), 0, st, S);
+        }
+    }
     trace_point(2, st);
     if (F.btab)
         hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
