@@ -48,6 +48,9 @@ def test_dense_prefill_parity(dtype, hq, hkv, q_start, nq):
     (torch.bfloat16, 16, 2, 1536, 512, 8, 8, 3),
     (torch.bfloat16, 16, 2, 1280, 400, 4, 4, 2),
     (torch.bfloat16, 16, 2, 1280, 400, 16, 16, 2),
+    (torch.bfloat16, 64, 8, 2048, 2100, 16, 16, 2),  # 16 opened groups in a 2048-row batch: the
+                                                     # block-at-a-time sweep with 8-entry lane
+                                                     # lists, 64-column select with 16-entry networks
     (torch.float32, 4, 4, 1024, 300, 4, 8, 2),      # fp32 caches: row-by-row path
 ])
 def test_lod_prefill_parity(dtype, hq, hkv, q_start, nq, G, TG, TP):
