@@ -70,7 +70,7 @@ struct FlashSmem {
     alignas(16) bf16_t kt[2][kFlashKeys][kD];  // key tiles (double buffer)
     alignas(16) bf16_t vt[2][kFlashKeys][kD];  // value tiles (double buffer)
     alignas(16) float bias[2][kFlashKeys];     // log2 units; -inf: not a key
-    int kpos[2][kFlashKeys];                   // key position for the causal test (INT_MIN: none)
+    alignas(16) float lnr[2][kFlashKeys];      // ln n of a coarse tile's centroids, as loaded
     int32_t sel[kFlashRowHeads][kMaxTG];       // opened groups per column (LoD)
 };
 
@@ -82,6 +82,7 @@ __device__ __forceinline__ int fswz_v(int row) { return 2 * (row & 7); }
 
 typedef short fs16x4_t __attribute__((ext_vector_type(4)));
 typedef float ff32x2_t __attribute__((ext_vector_type(2)));
+typedef float ff32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 fbf16x2_t __attribute__((ext_vector_type(2)));
 
 // 4 bf16 of a V^T operand: this lane gets V[key0 + r][d0 + lane % 16] for r = 0..3,
@@ -94,10 +95,41 @@ __device__ __forceinline__ fs16x4_t flash_vt_read(const bf16_t (*vt)[kD], int ke
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) fs16x4_t*)(p));
 }
 
+// V^T operands of two 16-dimension blocks: for each, the transposing reads at p (rows
+// r ..) and 16 rows on, as flash_vt_read forms them.  Written as asm, waited for inside the
+// block: the compiler's wait-count pass made the first transposing read of a tile wait for
+// every load in flight into LDS, the next tile's rows in the other buffer included, so the
+// next tile's latency was exposed in every wave before its PV products.
+// OFF: a byte offset added to both addresses.
+template <int OFF>
+__device__ __forceinline__ void flash_vt_read2(const bf16_t* pa, const bf16_t* pb, bf16x8_t& va, bf16x8_t& vb) {
+    typedef __attribute__((address_space(3))) const bf16_t* lds_bf16_ptr;
+    const uint32_t a = (uint32_t)(uintptr_t)(lds_bf16_ptr)pa;
+    const uint32_t b = (uint32_t)(uintptr_t)(lds_bf16_ptr)pb;
+    static_assert(16 * kD * sizeof(bf16_t) == 4096, "offset of the second read below");
+    fs16x4_t a0, a1, b0, b1;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+        : "v"(a), "v"(b), "i"(OFF), "i"(OFF + 4096));
+    const fs16x4_t ha[2] = {a0, a1};
+    const fs16x4_t hb[2] = {b0, b1};
+    va = __builtin_bit_cast(bf16x8_t, ha);
+    vb = __builtin_bit_cast(bf16x8_t, hb);
+}
+
 // Load key tile (coarse, k0, nk) into buffer buf: the K and V rows straight into LDS (a
-// wave's 64 lanes fill four rows per instruction; rows past nk repeat the last key) and
-// the tile's bias (log2 units) and causal positions.  kb, vb: the rows' base (index
-// summaries for a coarse tile, else the cache of this head and sequence).
+// wave's 64 lanes fill four rows per instruction; rows past nk repeat the last key), and
+// for a coarse tile its ln n values, also straight into LDS.  The tile's bias is formed
+// from them by flash_commit after the current tile's work: reading
+// ln n into a register here made wave 0 wait for that load (and for every load issued
+// before it) ahead of its share of the current tile, and the other waves then waited for
+// wave 0 at the next barrier.  kb, vb: the rows' base (index summaries for a coarse
+// tile, else the cache of this head and sequence).
 template <int HG, bool PAGED>
 __device__ __forceinline__ void flash_issue(FlashSmem<HG>& s, const FlashArgs& A, int buf, int coarse, int k0, int nk,
                                             const bf16_t* kb, const bf16_t* vb, const float* gln, int bs) {
@@ -119,9 +151,23 @@ __device__ __forceinline__ void flash_issue(FlashSmem<HG>& s, const FlashArgs& A
         __builtin_amdgcn_global_load_lds(kb + off[ii] + 8 * (li ^ fswz_k(row)), &s.kt[buf][4 * i][0], 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vb + off[ii] + 8 * (li ^ fswz_v(row)), &s.vt[buf][4 * i][0], 16, 0, 0);
     }
-    if (tid < kFlashKeys) {
-        s.bias[buf][tid] = tid < nk ? (coarse ? gln[k0 + tid] * kFlashLog2e : 0.0f) : -INFINITY;
-        s.kpos[buf][tid] = tid < nk && !coarse ? k0 + tid : INT_MIN;
+    // lane l's value lands at lnr[buf][l] (keys past nk repeat the last one)
+    if (tid < kFlashKeys && coarse)
+        __builtin_amdgcn_global_load_lds(gln + k0 + min(l, nk - 1), &s.lnr[buf][0], 4, 0, 0);
+}
+
+// The tile's bias (log2 units; -inf: not a key) into buffer buf, by wave 0 once its loads
+// have landed.
+template <int HG>
+__device__ __forceinline__ void flash_commit(FlashSmem<HG>& s, int buf, int coarse, int nk) {
+    if (threadIdx.x < kFlashKeys) {
+        // the lane index through empty asm: its LDS addresses are formed here, not kept
+        // in registers across the tile loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): ln n in LDS
+        const bool in = tid < nk;
+        s.bias[buf][tid] = in ? (coarse ? s.lnr[buf][tid] * kFlashLog2e : 0.0f) : -INFINITY;
     }
 }
 
@@ -157,7 +203,7 @@ void prefill_flash_kernel(FlashArgs A) {
         const int n = 16 * w + li;
         const int rl = n / HG, h = n % HG;
         colrow = rl;
-        prow = rl < nrows ? A.pos0 + r0 + rl : INT_MIN;  // INT_MIN: no key passes
+        prow = rl < nrows ? A.pos0 + r0 + rl : -1;  // -1: no cache key passes
         const bf16_t* qr = A.q + (((int64_t)b * A.nq + r0 + min(rl, nrows - 1)) * A.Hq + hq0 + h) * kD;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qb[kk] = *reinterpret_cast<const bf16x8_t*>(qr + 32 * kk + 8 * g);
@@ -229,6 +275,7 @@ void prefill_flash_kernel(FlashArgs A) {
         int coarse, k0, nk;
         tile_of(t0, coarse, k0, nk);
         flash_issue<HG, PAGED>(s, A, 0, coarse, k0, nk, coarse ? gk : kc, coarse ? gv : vc, gln, bs);
+        flash_commit<HG>(s, 0, coarse, nk);
     }
     int eptr = 0;  // next opened group of this lane's column not yet below the tiles
     for (int t = t0; t < t1; ++t) {
@@ -244,12 +291,16 @@ void prefill_flash_kernel(FlashArgs A) {
         // excluded keys of this lane's column: its opened groups inside a coarse tile.  The
         // column's list is ascending (-1 after the last) and coarse tiles come in key
         // order, so a pointer that only moves forward visits each opened group once.
-        uint64_t ex = 0;
+        // Only the 16 keys this lane scores are kept: bit 4 kb + r stands for key
+        // 16 kb + 4 g + r, so each test below is against a constant bit (a 64-bit mask
+        // tested at 16 key positions kept 16 shifted 64-bit constants in registers).
+        uint32_t ex = 0;
         if (coarse) {
             const int n = 16 * w + li;
             int gsel;
             while (eptr < A.TG && (gsel = s.sel[n][eptr]) >= 0 && gsel < k0 + kFlashKeys) {
-                if (gsel >= k0) ex |= 1ull << (gsel - k0);
+                const int key = gsel - k0;
+                if (key >= 0 && ((key >> 2) & 3) == g) ex |= 1u << (4 * (key >> 4) + (key & 3));
                 ++eptr;
             }
         }
@@ -272,20 +323,24 @@ void prefill_flash_kernel(FlashArgs A) {
         }
         // logits (log2 units), masks, online softmax (a column's 64 keys live in lanes
         // l, l^16, l^32, l^48).  A column may see no key in a tile (all masked): its
-        // maximum then stays -inf and the guards below keep every weight 0.
+        // maximum then stays -inf and the guards below keep every weight 0.  The lane's
+        // keys 16 kb + 4 g .. 16 kb + 4 g + 3 are consecutive, so their biases come in four
+        // 16-byte reads, issued together and waited for once (through empty asm, so no
+        // read is sunk into the mask's branch, where each was waited for alone).  Causal
+        // test: key k0 + c is visible when c <= prow - k0 (coarse tiles: always).
+        ff32x4_t b4[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) b4[kb] = *reinterpret_cast<const ff32x4_t*>(&s.bias[buf][16 * kb + 4 * g]);
+        asm volatile("" : "+v"(b4[0]), "+v"(b4[1]), "+v"(b4[2]), "+v"(b4[3]));
+        const int dlim = coarse ? kFlashKeys : prow - k0 - 4 * g;
         float P[4][4];
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = 16 * kb + 4 * g + r;
-                // the bias is read whatever the mask says (through empty asm, so the read
-                // is not sunk into the mask's branch, where each one was waited for alone)
-                float bi = s.bias[buf][key];
-                asm volatile("" : "+v"(bi));
-                const bool ok = (s.kpos[buf][key] <= prow) & !((ex >> key) & 1ull);
-                const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], bi) : -INFINITY;
+                const bool ok = (16 * kb + r <= dlim) & !((ex >> (4 * kb + r)) & 1u);
+                const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], b4[kb][r]) : -INFINITY;
                 P[kb][r] = lam;
                 mt = fmaxf(mt, lam);
             }
@@ -328,21 +383,30 @@ void prefill_flash_kernel(FlashArgs A) {
             // V^T operands (flash_vt_read's addresses, formed here as for K): row
             // 32 sp + 4 g + li / 4 (and 16 rows on), elements 16 db + 4 (li % 4) .. at chunk
             // (2 db + (li / 2) % 2) ^ 2 ((4 g + li / 4) % 8)
+            // (row 32 sp + r is row r plus an immediate offset of the reads)
             int vs_ = 2 * ((4 * g + (li >> 2)) & 7);
             asm volatile("" : "+v"(vs_));
-            const bf16_t* vtb = &s.vt[buf][0][0] + (32 * sp + 4 * g + (li >> 2)) * kD + 4 * (li & 1);
+            const bf16_t* vtb = &s.vt[buf][0][0] + (4 * g + (li >> 2)) * kD + 4 * (li & 1);
             const int vx = (li >> 1) & 1;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const bf16_t* p0 = vtb + 8 * (((2 * db) ^ vs_) + vx);
-                typedef __attribute__((address_space(3))) fs16x4_t lds_fs16x4_t;
-                const fs16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_fs16x4_t*)(p0));
-                const fs16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_fs16x4_t*)(p0 + 16 * kD));
-                const fs16x4_t both[2] = {v0, v1};
-                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
+            for (int db = 0; db < 8; db += 2) {
+                bf16x8_t av, bv;
+                const bf16_t* pa = vtb + 8 * (((2 * db) ^ vs_) + vx);
+                const bf16_t* pb = vtb + 8 * (((2 * db + 2) ^ vs_) + vx);
+                if (sp == 0)
+                    flash_vt_read2<0>(pa, pb, av, bv);
+                else
+                    flash_vt_read2<32 * kD * (int)sizeof(bf16_t)>(pa, pb, av, bv);
                 O[db] = mfma16(av, ph, O[db]);
                 O[db] = mfma16(av, pl, O[db]);
+                O[db + 1] = mfma16(bv, ph, O[db + 1]);
+                O[db + 1] = mfma16(bv, pl, O[db + 1]);
             }
+        }
+        // buffer buf ^ 1 held tile t - 1, which every wave finished before this tile's barrier
+        if (t + 1 < t1) {
+            tile_of(t + 1, coarse, k0, nk);
+            flash_commit<HG>(s, buf ^ 1, coarse, nk);
         }
     }
 
