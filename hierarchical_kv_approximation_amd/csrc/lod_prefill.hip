@@ -95,33 +95,6 @@ __device__ __forceinline__ fs16x4_t flash_vt_read(const bf16_t (*vt)[kD], int ke
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) fs16x4_t*)(p));
 }
 
-// V^T operands of two 16-dimension blocks: for each, the transposing reads at p (rows
-// r ..) and 16 rows on, as flash_vt_read forms them.  Written as asm, waited for inside the
-// block: the compiler's wait-count pass made the first transposing read of a tile wait for
-// every load in flight into LDS, the next tile's rows in the other buffer included, so the
-// next tile's latency was exposed in every wave before its PV products.
-// OFF: a byte offset added to both addresses.
-template <int OFF>
-__device__ __forceinline__ void flash_vt_read2(const bf16_t* pa, const bf16_t* pb, bf16x8_t& va, bf16x8_t& vb) {
-    typedef __attribute__((address_space(3))) const bf16_t* lds_bf16_ptr;
-    const uint32_t a = (uint32_t)(uintptr_t)(lds_bf16_ptr)pa;
-    const uint32_t b = (uint32_t)(uintptr_t)(lds_bf16_ptr)pb;
-    static_assert(16 * kD * sizeof(bf16_t) == 4096, "offset of the second read below");
-    fs16x4_t a0, a1, b0, b1;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
-        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
-        : "v"(a), "v"(b), "i"(OFF), "i"(OFF + 4096));
-    const fs16x4_t ha[2] = {a0, a1};
-    const fs16x4_t hb[2] = {b0, b1};
-    va = __builtin_bit_cast(bf16x8_t, ha);
-    vb = __builtin_bit_cast(bf16x8_t, hb);
-}
-
 // Load key tile (coarse, k0, nk) into buffer buf: the K and V rows straight into LDS (a
 // wave's 64 lanes fill four rows per instruction; rows past nk repeat the last key), and
 // for a coarse tile its ln n values, also straight into LDS.  The tile's bias is formed
@@ -326,21 +299,37 @@ void prefill_flash_kernel(FlashArgs A) {
         // maximum then stays -inf and the guards below keep every weight 0.  The lane's
         // keys 16 kb + 4 g .. 16 kb + 4 g + 3 are consecutive, so their biases come in four
         // 16-byte reads, issued together and waited for once (through empty asm, so no
-        // read is sunk into the mask's branch, where each was waited for alone).  Causal
-        // test: key k0 + c is visible when c <= prow - k0 (coarse tiles: always).
+        // read is sunk into the mask's branch, where each was waited for alone).
         ff32x4_t b4[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) b4[kb] = *reinterpret_cast<const ff32x4_t*>(&s.bias[buf][16 * kb + 4 * g]);
         asm volatile("" : "+v"(b4[0]), "+v"(b4[1]), "+v"(b4[2]), "+v"(b4[3]));
-        const int dlim = coarse ? kFlashKeys : prow - k0 - 4 * g;
+        // keep mask: bit 4 kb + r is set when the lane's key 16 kb + 4 g + r counts.  Coarse
+        // tiles: every centroid but the column's opened groups.  Cache tiles: the causal
+        // test, key k0 + c visible when c <= prow - k0.  A key that fails gets the bit
+        // pattern of -inf through a sign-extended bit field and a bitwise select, two
+        // instructions per key.
+        uint32_t vm;
+        if (coarse) {
+            vm = ~ex;
+        } else {
+            const int d = prow - k0 - 4 * g;  // the lane's key 16 kb + r passes when 16 kb + r <= d
+            vm = 0;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int n = min(max(d - 16 * kb + 1, 0), 4);
+                vm |= ((1u << n) - 1u) << (4 * kb);
+            }
+        }
         float P[4][4];
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool ok = (16 * kb + r <= dlim) & !((ex >> (4 * kb + r)) & 1u);
-                const float lam = ok ? __builtin_fmaf(sc2, S[kb][r], b4[kb][r]) : -INFINITY;
+                const int keep = __builtin_amdgcn_sbfe((int)vm, 4 * kb + r, 1);  // 0 or -1
+                const int lb = __float_as_int(__builtin_fmaf(sc2, S[kb][r], b4[kb][r]));
+                const float lam = __int_as_float((lb & keep) | ((int)0xFF800000 & ~keep));  // else -inf
                 P[kb][r] = lam;
                 mt = fmaxf(mt, lam);
             }
@@ -383,24 +372,20 @@ void prefill_flash_kernel(FlashArgs A) {
             // V^T operands (flash_vt_read's addresses, formed here as for K): row
             // 32 sp + 4 g + li / 4 (and 16 rows on), elements 16 db + 4 (li % 4) .. at chunk
             // (2 db + (li / 2) % 2) ^ 2 ((4 g + li / 4) % 8)
-            // (row 32 sp + r is row r plus an immediate offset of the reads)
             int vs_ = 2 * ((4 * g + (li >> 2)) & 7);
             asm volatile("" : "+v"(vs_));
-            const bf16_t* vtb = &s.vt[buf][0][0] + (4 * g + (li >> 2)) * kD + 4 * (li & 1);
+            const bf16_t* vtb = &s.vt[buf][0][0] + (32 * sp + 4 * g + (li >> 2)) * kD + 4 * (li & 1);
             const int vx = (li >> 1) & 1;
 #pragma unroll
-            for (int db = 0; db < 8; db += 2) {
-                bf16x8_t av, bv;
-                const bf16_t* pa = vtb + 8 * (((2 * db) ^ vs_) + vx);
-                const bf16_t* pb = vtb + 8 * (((2 * db + 2) ^ vs_) + vx);
-                if (sp == 0)
-                    flash_vt_read2<0>(pa, pb, av, bv);
-                else
-                    flash_vt_read2<32 * kD * (int)sizeof(bf16_t)>(pa, pb, av, bv);
+            for (int db = 0; db < 8; ++db) {
+                const bf16_t* p0 = vtb + 8 * (((2 * db) ^ vs_) + vx);
+                typedef __attribute__((address_space(3))) fs16x4_t lds_fs16x4_t;
+                const fs16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_fs16x4_t*)(p0));
+                const fs16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_fs16x4_t*)(p0 + 16 * kD));
+                const fs16x4_t both[2] = {v0, v1};
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, both);
                 O[db] = mfma16(av, ph, O[db]);
                 O[db] = mfma16(av, pl, O[db]);
-                O[db + 1] = mfma16(bv, ph, O[db + 1]);
-                O[db + 1] = mfma16(bv, pl, O[db + 1]);
             }
         }
         // buffer buf ^ 1 held tile t - 1, which every wave finished before this tile's barrier
