@@ -528,8 +528,9 @@ __device__ __forceinline__ void stage_rows_swizzled(bf16_t (*kt)[kD], const bf16
 // under the canonical chain.  The MFMA score S of a group is within
 // E = kErrC |q| |kbar| of that chain, so with T the TG-th largest lower bound S - E over
 // the groups, the groups with S + E >= T contain the exact top TG; so does any T below
-// that one.  Each split keeps, per column, the R largest lower bounds seen by each of the
-// column's four lanes (4R >= TG values of distinct groups), lists the TG largest of
+// that one.  Each split keeps, per column, the R largest of the lower bounds' maxima over
+// the 4-key blocks seen by each of the column's four lanes (4R >= TG values of distinct
+// groups), lists the TG largest of
 // those, and collects the groups with S + E at or above the TG-th (a lower bound of the
 // split's TG-th largest, never above the global one).  The select step takes the global
 // threshold from the splits' top lists and keeps the listed groups at or above it.
@@ -660,8 +661,11 @@ void prefill_cand_kernel(SelArgs A) {
         }
     };
 
-    // pass A: per column, the largest lower bounds S - E (lane-local top-R lists, kept
-    // sorted by a branch-free insertion of every element)
+    // pass A: per column, large lower bounds S - E.  Each lane keeps the R largest of its
+    // 4-key blocks' maxima (one insertion per block instead of one per key: the values
+    // are still lower bounds of distinct groups, so the TG-th largest of the four lanes'
+    // lists is still at or below the split's TG-th largest lower bound), in lists kept
+    // sorted by a branch-free insertion.
     float lst[2][R];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -676,15 +680,17 @@ void prefill_cand_kernel(SelArgs A) {
             const float4 gl4 = *reinterpret_cast<const float4*>(&s.gln_t[buf][k4]);
             const float4 gn4 = *reinterpret_cast<const float4*>(&s.gkn_t[buf][k4]);
             const float glr[4] = {gl4.x, gl4.y, gl4.z, gl4.w}, gnr[4] = {gn4.x, gn4.y, gn4.z, gn4.w};
+            float bm[2] = {-INFINITY, -INFINITY};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool valid = (k4 + r < nk) & (glr[r] != -INFINITY);
                 const float gn = gnr[r];
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    insert_desc(lst[cb], valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY, pinf);
-                }
+                for (int cb = 0; cb < 2; ++cb)
+                    bm[cb] = fmaxf(bm[cb], valid ? S[cb][r] - kErrC * qn[cb] * gn : -INFINITY);
             }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) insert_desc(lst[cb], bm[cb], pinf);
     });
     // merge the four lanes of each column: the TG largest with multiplicity, descending;
     // the local threshold is the TG-th (-inf when the split has fewer valid groups)
@@ -931,10 +937,14 @@ void prefill_select_kernel(SelArgs A) {
         }
     }
     __syncthreads();
-    // canonical chains for the candidates that need them (the score replaces the bound)
+    // canonical chains for the candidates that need them (the score replaces the bound).
+    // A column past kCandCap takes the exhaustive path below and skips this: its classes
+    // were never set, and when a split's list overflowed, not even its candidate slots
+    // (their group ids would be whatever LDS held).
     for (int x = tid; x < NC * kCandCap; x += kThreads) {
         const int n = x / kCandCap, at = x % kCandCap;
-        if (at < min(s.cnt[n], kCandCap) && s.cls[n][at] == 1)
+        const int c = s.cnt[n];
+        if (c <= kCandCap && at < c && s.cls[n][at] == 1)
             s.cub[n][at] = canonical_dot_bf16(qrow(n), gk + (int64_t)s.cg[n][at] * kD);
     }
     __syncthreads();
