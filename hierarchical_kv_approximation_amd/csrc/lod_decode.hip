@@ -1344,9 +1344,9 @@ void decode_scan_mfma_kernel(DecodeArgs A) {
         const bool coarse = cur.coarse;
         const int r0 = cur.r0, n = cur.n;
         scan_stage(s, R);  // the last tile's PV is done (barrier at the end of the loop)
+        if (t + 1 < t1) scan_fetch<DROP, PAGED>(R, S, scan_tile(t + 1, ntc, S.ng, S.nex));  // in flight
         __syncthreads();
         scan_scores<HG>(s, qa);
-        if (t + 1 < t1) scan_fetch<DROP, PAGED>(R, S, scan_tile(t + 1, ntc, S.ng, S.nex));  // in flight
         __syncthreads();
         // coarse tiles: the scores go out for the selection, one float4 per head and four
         // groups, -inf for an empty group (only the last tile of the unit's groups is
