@@ -529,7 +529,7 @@ __device__ __forceinline__ void open_block_add(Online& st, const float* lam, con
     for (int e = 0; e < 8; ++e) st.o[e] *= a;
 #pragma unroll
     for (int x = 0; x < OB; ++x) {
-        if (lam[x] == -INFINITY) continue;  // no term: its value registers were not loaded
+        if (lam[x] == -INFINITY) continue;  // no term (its value registers may repeat a row)
         const float w = softmax_exp(lam[x] - mn);
         float vf[8];
 #pragma unroll
@@ -736,19 +736,25 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
         }
     } else {
         for (int base = 0; base < nex; base += 4 * OB) {
+            // every item's row position first, then every row load: items past nex repeat
+            // the last row (masked below), so no load sits behind a branch of its own,
+            // where each item's LDS read was waited for before its loads were issued
+            int ent[OB];
+#pragma unroll
+            for (int x = 0; x < OB; ++x) ent[x] = s.ex[wave][min(base + sgw + 4 * x, nex - 1)];
             u32x4_t kp[OB][U], vp[OB][U];  // rows kept packed until used
 #pragma unroll
             for (int x = 0; x < OB; ++x) {
-                const int it = base + sgw + 4 * x;
-                if (it < nex) {
-                    const int64_t ro = kv_pos<PAGED>(A, seq, s.ex[wave][it]);
+                const int64_t ro = kv_pos<PAGED>(A, seq, ent[x]);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        kp[x][u] = *reinterpret_cast<const u32x4_t*>(kh + ro + 8 * l16 + u * P16);
-                        vp[x][u] = *reinterpret_cast<const u32x4_t*>(vh + ro + 8 * l16 + u * P16);
-                    }
+                for (int u = 0; u < U; ++u) {
+                    kp[x][u] = *reinterpret_cast<const u32x4_t*>(kh + ro + 8 * l16 + u * P16);
+                    vp[x][u] = *reinterpret_cast<const u32x4_t*>(vh + ro + 8 * l16 + u * P16);
                 }
             }
+            // keeps the value loads here, in flight beside the key loads (the compiler
+            // would otherwise sink them to their use, after the dot products)
+            asm volatile("" ::: "memory");
             // block update of the subgroup's online softmax: dot products and their
             // reductions side by side, one rescale, then the weighted values
             float lam[OB];
@@ -771,22 +777,30 @@ __device__ void open_pages(const DecodeArgs& A, OpenSmem<T>& s, int nsel, int se
     }
     const int ncp = (DROP || (DROP_RT && A.drop)) ? 0 : s.ncp[wave];  // unopened pages: coarse terms
     for (int base = 0; base < ncp; base += 4 * OB) {
-        u32x4_t vp[OB][U];
+        // as for the exact rows: the items' LDS entries first (past ncp: the last item,
+        // masked), then every page row load
+        int cpe[OB];
         float lam[OB];
 #pragma unroll
         for (int x = 0; x < OB; ++x) {
-            const int it = base + sgw + 4 * x;
-            lam[x] = -INFINITY;
-            if (it < ncp) {
-                const int k = s.cp[wave][it] >> 8, e = s.cp[wave][it] & 255, i = wave + 4 * k;
-                const uint32_t gid = key_id(s.sel[i]);
-                const int c = gid / A.G, ps0 = mrowp(i)[gid % A.G];
-                const T* row = pv_u + ((int64_t)c * PS + ps0 + e) * kD + 8 * l16;
-#pragma unroll
-                for (int u = 0; u < U; ++u) vp[x][u] = *reinterpret_cast<const u32x4_t*>(row + u * P16);
-                lam[x] = s.cl[wave][it];
-            }
+            const int it = min(base + sgw + 4 * x, ncp - 1);
+            cpe[x] = s.cp[wave][it];
+            lam[x] = base + sgw + 4 * x < ncp ? s.cl[wave][it] : -INFINITY;
         }
+        const T* rows[OB];
+#pragma unroll
+        for (int x = 0; x < OB; ++x) {
+            const int k = cpe[x] >> 8, e = cpe[x] & 255, i = wave + 4 * k;
+            const uint32_t gid = key_id(s.sel[i]);
+            const int c = gid / A.G, ps0 = mrowp(i)[gid % A.G];
+            rows[x] = pv_u + ((int64_t)c * PS + ps0 + e) * kD + 8 * l16;
+        }
+        u32x4_t vp[OB][U];
+#pragma unroll
+        for (int x = 0; x < OB; ++x)
+#pragma unroll
+            for (int u = 0; u < U; ++u) vp[x][u] = *reinterpret_cast<const u32x4_t*>(rows[x] + u * P16);
+        asm volatile("" ::: "memory");  // the loads stay issued together, ahead of their use
         open_block_add<T, OB, U>(st, lam, vp);
     }
 }
