@@ -88,11 +88,13 @@ def test_lod_prefill_diffuse_queries():
     _prefill_and_compare(case, Q, 3072, _sample_rows(1, 1024, 16, 100, 46))
 
 
-def test_lod_prefill_ties_take_the_exhaustive_path():
+@pytest.mark.parametrize("TG", [16, 8])
+def test_lod_prefill_ties_take_the_exhaustive_path(TG):
     """Four centres shared by every chunk and zero variance: dozens of groups tie at the
-    top score, more than the candidate list keeps, so selection falls back to ranking
-    every group canonically.  Zero variance also makes LoD equal dense attention."""
-    g, o = configs(torch.bfloat16, 16, 2, G=8, TG=16)
+    top score, more than a split's candidate list keeps, so selection falls back to
+    ranking every group canonically (for both instantiations of the selection, up to 8 and
+    up to 16 opened groups).  Zero variance also makes LoD equal dense attention."""
+    g, o = configs(torch.bfloat16, 16, 2, G=8, TG=TG)
     case = Case(g, o, 1, 12288, seed=47, zero_variance=True, n_centres=4)
     case.build_gpu()
     Q = case.queries(seed=48, n_rows=512)
