@@ -149,16 +149,14 @@ __device__ __forceinline__ void flash_commit(FlashSmem<HG>& s, int buf, int coar
 // 16w+15), so a wave's registers stay under 128 and four waves share each SIMD: with
 // two column blocks per wave (4 waves, 232 registers) only two did, and the softmax and
 // conversion chains left the matrix cores idle four fifths of the time.
+// lin: the workgroup's index in the (x, y) plane of the flash grid.
 template <int HG, bool PAGED>
-__global__ __launch_bounds__(kFlashThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void prefill_flash_kernel(FlashArgs A) {
-    __shared__ FlashSmem<HG> s;
+__device__ __forceinline__ void flash_body(const FlashArgs& A, FlashSmem<HG>& s, int lin) {
     constexpr int QT = kFlashRowHeads / HG;
     const int nsplit = A.index ? A.nsplit : 1;
     // KV head fastest in the workgroup order: workgroups go to the 8 XCDs round robin, so
     // each XCD's L2 serves the key tiles of one KV head (with the tile fastest, every
     // XCD streamed every head's centroids)
-    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
     const int kvh = lin % A.Hkv, tx = lin / A.Hkv;
     const int tile = tx / nsplit, split = tx % nsplit;
     const int b = blockIdx.z, bs = A.seq + b;
@@ -426,6 +424,13 @@ void prefill_flash_kernel(FlashArgs A) {
             }
         }
     }
+}
+
+template <int HG, bool PAGED>
+__global__ __launch_bounds__(kFlashThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void prefill_flash_kernel(FlashArgs A) {
+    __shared__ FlashSmem<HG> s;
+    flash_body<HG, PAGED>(A, s, blockIdx.x + gridDim.x * blockIdx.y);
 }
 
 }  // namespace lodi
@@ -1146,19 +1151,17 @@ struct PagesArgs {
     int units_per_seq_kv;   // query chunks in the launch
 };
 
-// PER: pair slots per thread, at least kChunk * HG * TG / kBucketThreads.
-template <int HG, int PER>
-__global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArgs A) {
-    // + 64 spare counters: slots with no group (or past the last pair) count into the
-    // spare of their lane, so every slot takes its atomic without a branch
-    __shared__ int cnt[kMaxBucketGroups + 64];
-    // up to 16 slots per thread (16384 pairs): the sorted list is assembled in LDS (pair
-    // index and group in 14 bits each) and written out in order, so the global stores are
-    // coalesced instead of scattered one pair at a time
-    constexpr bool kStage = PER <= 16;
-    __shared__ uint32_t stage[kStage ? kBucketThreads * 16 : 1];
-    __shared__ int wsum[kBucketThreads / 64];
-    const int qc = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+// Counting sort of one unit's (query chunk qc, KV head kvh, sequence b) pairs by opened
+// group, by NT threads.  PER: pair slots per thread, at least kChunk * HG * TG / NT.
+// cnt: kMaxBucketGroups + 64 counters (+ 64 spares: slots with no group, or past the last
+// pair, count into the spare of their lane, so every slot takes its atomic without a
+// branch); wsum: NT / 64 words.  STAGE (up to 16 slots per thread, 16384 pairs): the
+// sorted list is assembled in stage[NT * 16] (pair index and group in 14 bits each) and
+// written out in order, so the global stores are coalesced instead of scattered one pair
+// at a time.
+template <int HG, int PER, int NT, bool STAGE>
+__device__ __forceinline__ void bucket_body(const PagesArgs& A, int qc, int kvh, int b, int* cnt, uint32_t* stage,
+                                            int* wsum) {
     const int tid = threadIdx.x;
     const int r0 = qc * kChunk;
     const int nrows = min(kChunk, A.nq - r0);
@@ -1167,21 +1170,21 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     const int npairs = nrows * HG * A.TG;
     const int64_t unit = ((int64_t)b * A.Hkv + kvh) * A.units_per_seq_kv + qc;
     int2* list = A.plist + unit * (kChunk * HG * A.TG);
-    for (int g = tid; g < ng; g += kBucketThreads) cnt[g] = 0;
+    for (int g = tid; g < ng; g += NT) cnt[g] = 0;
     const int spare = kMaxBucketGroups + (tid & 63);
-    // the group id of every pair this thread owns (pairs tid, tid + 1024, ...), loaded
+    // the group id of every pair this thread owns (pairs tid, tid + NT, ...), loaded
     // together and kept for both passes.  Pair x = rl * HG * TG + e (e = head * TG + slot)
     // sits at selg row r0 + rl, entry kvh * HG * TG + e; (rl, e) advances by the
-    // division of 1024 by HG * TG with one carry, so the loop divides nothing.
+    // division of NT by HG * TG with one carry, so the loop divides nothing.
     int gid[PER];
     {
         const int per_row = HG * A.TG, rs = A.Hq * A.TG;  // pairs of a unit row; selg row stride
-        const int de = kBucketThreads % per_row, doff = kBucketThreads / per_row * rs + de;
+        const int de = NT % per_row, doff = NT / per_row * rs + de;
         int e = tid % per_row, off = tid / per_row * rs + e;
         const int32_t* sg = A.selg + ((int64_t)b * A.nq + r0) * rs + kvh * per_row;
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            gid[u] = tid + u * kBucketThreads < npairs ? sg[off] : -1;
+            gid[u] = tid + u * NT < npairs ? sg[off] : -1;
             off += doff;
             e += de;
             if (e >= per_row) { e -= per_row; off += rs - per_row; }
@@ -1193,7 +1196,7 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     __syncthreads();
     // exclusive scan of the counts: contiguous ranges per thread, then the range sums by
     // wave prefix sums and the waves' totals
-    const int per = (ng + kBucketThreads - 1) / kBucketThreads;
+    const int per = (ng + NT - 1) / NT;
     const int g0 = tid * per, g1 = min(ng, g0 + per);
     int sum = 0;
     for (int g = g0; g < g1; ++g) sum += cnt[g];
@@ -1208,7 +1211,7 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
-    for (int x = 0; x < kBucketThreads / 64; ++x) {
+    for (int x = 0; x < NT / 64; ++x) {
         before += x < wv ? wsum[x] : 0;
         total += wsum[x];
     }
@@ -1220,20 +1223,60 @@ __global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArg
     int at[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) at[u] = atomicAdd(&cnt[gid[u] >= 0 ? gid[u] : spare], 1);
-    if constexpr (kStage) {
+    if constexpr (STAGE) {
 #pragma unroll
         for (int u = 0; u < PER; ++u)
-            if (gid[u] >= 0) stage[at[u]] = (uint32_t)(tid + u * kBucketThreads) | ((uint32_t)gid[u] << 14);
+            if (gid[u] >= 0) stage[at[u]] = (uint32_t)(tid + u * NT) | ((uint32_t)gid[u] << 14);
         __syncthreads();
-        for (int x = tid; x < total; x += kBucketThreads) {
+        for (int x = tid; x < total; x += NT) {
             const uint32_t v = stage[x];
             list[x] = make_int2((int)(v & 0x3fffu), (int)(v >> 14));
         }
     } else {
 #pragma unroll
         for (int u = 0; u < PER; ++u)
-            if (gid[u] >= 0) list[at[u]] = make_int2(tid + u * kBucketThreads, gid[u]);
+            if (gid[u] >= 0) list[at[u]] = make_int2(tid + u * NT, gid[u]);
     }
+}
+
+// PER: pair slots per thread, at least kChunk * HG * TG / kBucketThreads.
+template <int HG, int PER>
+__global__ __launch_bounds__(kBucketThreads) void prefill_bucket_kernel(PagesArgs A) {
+    __shared__ int cnt[kMaxBucketGroups + 64];
+    constexpr bool kStage = PER <= 16;
+    __shared__ uint32_t stage[kStage ? kBucketThreads * 16 : 1];
+    __shared__ int wsum[kBucketThreads / 64];
+    bucket_body<HG, PER, kBucketThreads, kStage>(A, blockIdx.x, blockIdx.y, blockIdx.z, cnt, stage, wsum);
+}
+
+// The flash kernel and the bucket sort in one launch: both need only the selection, so
+// the bucket workgroups (after the nflash flash workgroups, one per query chunk and KV
+// head) take the CUs that the first flash workgroups to end leave, beside the flash
+// tail, instead of running as a launch of their own between the flash kernel and the
+// group kernel, where eight workgroups held the whole GPU for about 10 us per call.  The
+// bucket side sorts with the flash kernel's 512 threads and without staging (its LDS is
+// the flash kernel's, whose 75 KB would not also hold the stage).
+template <int HG>
+union FlashBucketSmem {
+    FlashSmem<HG> f;
+    struct {
+        int cnt[kMaxBucketGroups + 64];
+        int wsum[kFlashThreads / 64];
+    } k;
+};
+
+template <int HG, bool PAGED, int PER>
+__global__ __launch_bounds__(kFlashThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void prefill_flash_bucket_kernel(FlashArgs F, PagesArgs P, int nflash, int nunits_q) {
+    __shared__ FlashBucketSmem<HG> u;
+    const int bx = blockIdx.x;
+    if (bx >= nflash) {  // uniform in the workgroup
+        const int x = bx - nflash;
+        bucket_body<HG, PER, kFlashThreads, false>(P, x % nunits_q, x / nunits_q, blockIdx.z, u.k.cnt, nullptr,
+                                                   u.k.wsum);
+        return;
+    }
+    flash_body<HG, PAGED>(F, u.f, bx);
 }
 
 // ---------------------------------------------------------------------------- pages
@@ -1907,14 +1950,36 @@ static int launch_prefill_batch(const SelArgs& S, const FlashArgs& F, const Page
         }
     }
     trace_point(2, st);
-    if (F.btab)
-        hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
-                           st, F);
-    else
-        hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads), 0,
-                           st, F);
-    trace_point(3, st);
-    {
+    // flash and bucket in one launch when the bucket side's 512 threads hold a unit's pairs
+    // in at most 32 slots each (HG * TG <= 64); else two launches
+    const int per_fused = (kChunk * HG * S.TG + kFlashThreads - 1) / kFlashThreads;
+    if (per_fused <= 32) {
+        const int nflash = ntiles * F.nsplit * S.Hkv;
+        const dim3 gf(nflash + nunits_q * S.Hkv, 1, batch);
+        if (F.btab) {
+            if (per_fused <= 16)
+                hipLaunchKernelGGL((prefill_flash_bucket_kernel<HG, true, 16>), gf, dim3(kFlashThreads), 0, st, F, P, nflash,
+                                   nunits_q);
+            else
+                hipLaunchKernelGGL((prefill_flash_bucket_kernel<HG, true, 32>), gf, dim3(kFlashThreads), 0, st, F, P, nflash,
+                                   nunits_q);
+        } else {
+            if (per_fused <= 16)
+                hipLaunchKernelGGL((prefill_flash_bucket_kernel<HG, false, 16>), gf, dim3(kFlashThreads), 0, st, F, P, nflash,
+                                   nunits_q);
+            else
+                hipLaunchKernelGGL((prefill_flash_bucket_kernel<HG, false, 32>), gf, dim3(kFlashThreads), 0, st, F, P, nflash,
+                                   nunits_q);
+        }
+        trace_point(3, st);
+    } else {
+        if (F.btab)
+            hipLaunchKernelGGL((prefill_flash_kernel<HG, true>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads),
+                               0, st, F);
+        else
+            hipLaunchKernelGGL((prefill_flash_kernel<HG, false>), dim3(ntiles * F.nsplit, S.Hkv, batch), dim3(kFlashThreads),
+                               0, st, F);
+        trace_point(3, st);
         const dim3 gb(nunits_q, S.Hkv, batch);
         const int per = (kChunk * HG * S.TG + kBucketThreads - 1) / kBucketThreads;
         if (per <= 4) hipLaunchKernelGGL((prefill_bucket_kernel<HG, 4>), gb, dim3(kBucketThreads), 0, st, P);
