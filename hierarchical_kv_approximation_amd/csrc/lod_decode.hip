@@ -1214,8 +1214,10 @@ __device__ __forceinline__ void scan_fetch(ScanRegs& R, const ScanSrc& S, const 
         for (int i = 0; i < kSPieces; ++i) {
             const int row = min(4 * g + i, n - 1);
             const int64_t off = (int64_t)(r0 + row) * kD + 8 * c;
-            R.k[i] = *reinterpret_cast<const u32x4_t*>(S.gk + off);
-            if (!DROP) R.v[i] = *reinterpret_cast<const u32x4_t*>(S.gv + off);
+            // read once per call: non-temporal, so that these rows do not push out of
+            // the caches what the open step reads next (meta rows, norms, opened pages)
+            R.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(S.gk + off));
+            if (!DROP) R.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(S.gv + off));
         }
         R.bias = tid < kSTile ? S.gln[r0 + min(tid, n - 1)] : 0.0f;
     } else {
